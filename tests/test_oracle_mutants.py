@@ -1,0 +1,130 @@
+"""Plausible mistakes planted into the oracle (on the CPU) must each make at least
+one pin fail: evidence that the pins constrain every step of the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import infini_ref as o
+from tests.oracle_pins import ALL_PINS
+
+
+def _strict_mask(n):
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return j < i
+
+
+def _scale_model_width(d_key, scale=None):
+    return 1.0 / math.sqrt(2 * d_key)
+
+
+def _elu_without_plus_one(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0.0, x, np.exp(np.minimum(x, 0.0)) - 1.0)
+
+
+def _retrieval_with_raw_query(q, M, z, first):
+    if first:
+        return np.zeros((q.shape[0], M.shape[1]))
+    return (q @ M) / (q @ z)[:, None]
+
+
+def _retrieval_sum_denominator(q, M, z, first):
+    if first:
+        return np.zeros((q.shape[0], M.shape[1]))
+    return (o.sigma(q) @ M) / z.sum()
+
+
+def _linear_without_sigma_in_z(k, v, M, z):
+    return M + o.sigma(k).T @ v, z + k.sum(axis=0)
+
+
+def _linear_transposed(k, v, M, z):
+    return M + (v.T @ o.sigma(k)).T[::-1], z + o.sigma(k).sum(axis=0)
+
+
+def _delta_sign_flipped(k, v, M, z, first):
+    fk = o.sigma(k)
+    return M + fk.T @ (v + o.delta_correction(k, M, z, first)), z + fk.sum(axis=0)
+
+
+def _delta_unnormalised(k, M, z, first):
+    if first:
+        return np.zeros((k.shape[0], M.shape[1]))
+    return o.sigma(k) @ M
+
+
+def _delta_with_new_z(k, v, M, z, first):
+    fk = o.sigma(k)
+    z_new = z + fk.sum(axis=0)
+    return M + fk.T @ (v - o.delta_correction(k, M, z_new, False if not first else True)), z_new
+
+
+def _delta_per_token(k, v, M, z, first):
+    fk = o.sigma(k)
+    M = M.copy()
+    z = z.copy()
+    for t in range(k.shape[0]):
+        den = fk[t] @ z
+        r = (fk[t] @ M) / den if den > 0 else np.zeros(M.shape[1])
+        M += np.outer(fk[t], v[t] - r)
+        z += fk[t]
+    return M, z
+
+
+def _gate_swapped(beta, a_mem, a_dot):
+    g = 1.0 / (1.0 + math.exp(-beta)) if math.isfinite(beta) else (1.0 if beta > 0 else 0.0)
+    return g * a_dot + (1.0 - g) * a_mem
+
+
+def _softmax_over_all_keys(q, k, v, scale):
+    n = q.shape[0]
+    scores = scale * (q @ k.T)
+    p = np.exp(scores - scores.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    p = np.where(o.causal_mask(n), p, 0.0)
+    return p @ v
+
+
+_real_segment_forward = o.segment_forward
+
+
+def _write_before_read(q, k, v, M, z, beta, rule, first, scale):
+    M2, z2 = o.memory_update(k, v, M, z, rule, first)
+    a_mem = o.memory_retrieval(q, M2, z2, False)
+    a_dot = o.local_causal_attention(q, k, v, scale)
+    return o.gate(beta, a_mem, a_dot), M2, z2, a_dot, a_mem
+
+
+MUTANTS = {
+    "mask_excludes_diagonal": ("causal_mask", _strict_mask),
+    "scale_uses_model_width": ("default_scale", _scale_model_width),
+    "sigma_is_plain_elu": ("sigma", _elu_without_plus_one),
+    "retrieval_without_sigma": ("memory_retrieval", _retrieval_with_raw_query),
+    "retrieval_wrong_denominator": ("memory_retrieval", _retrieval_sum_denominator),
+    "z_sums_raw_keys": ("update_linear", _linear_without_sigma_in_z),
+    "linear_binding_rows_permuted": ("update_linear", _linear_transposed),
+    "delta_adds_retrieved_value": ("update_delta", _delta_sign_flipped),
+    "delta_without_normaliser": ("delta_correction", _delta_unnormalised),
+    "delta_reads_updated_z": ("update_delta", _delta_with_new_z),
+    "delta_token_by_token": ("update_delta", _delta_per_token),
+    "gate_weights_swapped": ("gate", _gate_swapped),
+    "softmax_normalised_before_mask": ("local_causal_attention", _softmax_over_all_keys),
+    "memory_written_before_read": ("segment_forward", _write_before_read),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, bad = MUTANTS[name]
+    monkeypatch.setattr(o, attr, bad)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in ALL_PINS:
+            try:
+                pin(o)
+            except Exception:  # noqa: BLE001 - any failure of a pin counts
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
