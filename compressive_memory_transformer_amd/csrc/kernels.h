@@ -1,0 +1,102 @@
+// Internal launcher interface between the C ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infini {
+
+typedef __bf16 bf16;
+
+// ------------------------------------------------------------------ bf16 path
+// Tensors cover S segments of N tokens for each of B*H heads; token t of head
+// bh lives at row bh * L + t, L = S * N.
+struct FaArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const float* beta;     // [H]
+  const bf16* snapM;     // [B*H*S][D][D] bf16 snapshot of M_{s-1}^T (row = d_value)
+  const float* snapz;    // [B*H*S][D]    fp32 snapshot of z_{s-1}
+  bf16* out;
+  int B, H, S, N;
+  int64_t L;
+  int nq;                // ceil(N / 128) query tiles per segment
+  int64_t seg_base;      // segments folded into the state before this call
+  float sc_log2;         // softmax scale * log2(e)
+};
+template <int D> hipError_t launch_fa_fwd(const FaArgs& a, hipStream_t stream);
+
+// Linear rule, phase 1: per-segment contributions C_s^T = V^T sigma(K) (fp32, row =
+// d_value) and c_s = sum_t sigma(K_t).
+struct LinContribArgs {
+  const bf16* k;
+  const bf16* v;
+  float* cM;             // [B*H*S][D][D]
+  float* cz;             // [B*H*S][D]
+  int B, H, S, N;
+  int64_t L;
+};
+template <int D> hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream);
+
+// Linear rule, phase 2: exclusive prefix over segments.  Writes the snapshots
+// read by the fused kernel and leaves M_S, z_S in the state.
+struct LinScanArgs {
+  const float* cM;
+  const float* cz;
+  float* M;              // state [B*H][D][D] (row = d_key), read then overwritten
+  float* z;              // state [B*H][D]
+  bf16* snapM;           // [B*H*S][D][D] (row = d_value)
+  float* snapz;          // [B*H*S][D]
+  int BH, S;
+};
+template <int D> hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream);
+
+// Delta rule: persistent chain over the S segments of each head; each workgroup
+// owns 16 columns (d_value) of M.  Emits the snapshots and updates the state.
+struct DeltaArgs {
+  const bf16* k;
+  const bf16* v;
+  float* M;              // state [B*H][D][D] (row = d_key)
+  float* z;              // state [B*H][D]
+  bf16* snapM;           // [B*H*S][D][D] (row = d_value)
+  float* snapz;          // [B*H*S][D]
+  int BH, S, N;
+  int64_t L;
+  int64_t seg_base;
+};
+template <int D> hipError_t launch_delta_chain(const DeltaArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------ fp32 path
+// One segment per launch; M and z are read as M_{s-1}, z_{s-1}.
+struct F32AttnArgs {
+  const float* q;        // rows of this segment: q + (bh * L + seg_off) * dk
+  const float* k;
+  const float* v;
+  const float* beta;
+  const float* M;        // [BH][dk][dv]
+  const float* z;        // [BH][dk]
+  float* out;
+  int H, BH, N, dk, dv;
+  int64_t L, seg_off;
+  int has_memory;
+  float scale;
+};
+hipError_t launch_f32_attn(const F32AttnArgs& a, hipStream_t stream);
+
+struct F32UpdateArgs {
+  const float* k;
+  const float* v;
+  float* M;
+  float* z;
+  float* U;              // workspace [BH][N][dv] (delta rule)
+  int BH, N, dk, dv;
+  int64_t L, seg_off;
+  int delta, has_memory;
+};
+hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream);
+
+// Zero n floats.
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
+}  // namespace infini

@@ -1,0 +1,208 @@
+"""ctypes binding of libinfini_attn.so (C ABI in include/infini_attn.h).
+
+Argument marshalling only: every step of the segment forward runs in the HIP
+kernels of the library.  The functions below carry the C names without the
+``infini_attn_`` prefix and take device pointers as Python ints (or torch
+tensors, whose ``data_ptr()`` is used).  ``InfiniAttention`` wraps one state
+together with torch-allocated M, z and workspace buffers.
+
+The library is loaded from this package directory; there is no fallback: if it
+has not been built, loading raises ``LibraryNotBuilt``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libinfini_attn.so")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "infini_attn.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+RULE_LINEAR, RULE_DELTA = 0, 1
+F32, BF16 = 0, 1
+RULES = {"linear": RULE_LINEAR, "delta": RULE_DELTA}
+DTYPES = {"f32": F32, "bf16": BF16}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class InfiniError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"infini_attn error {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+class State(ctypes.Structure):
+    """Mirror of infini_attn_state."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("d_key", ctypes.c_int32),
+        ("d_value", ctypes.c_int32),
+        ("segment_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("rule", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("M", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("segments_done", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise LibraryNotBuilt(f"{p} not found: build it with `python -m compressive_memory_transformer_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sp = ctypes.POINTER(State)
+    lib.infini_attn_init_state.argtypes = [sp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.infini_attn_init_state.restype = ctypes.c_int
+    lib.infini_attn_workspace_bytes.argtypes = [sp, i64]
+    lib.infini_attn_workspace_bytes.restype = sz
+    lib.infini_attn_forward_sequence.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    lib.infini_attn_forward_sequence.restype = ctypes.c_int
+    lib.infini_attn_forward_segment.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.infini_attn_forward_segment.restype = ctypes.c_int
+    lib.infini_attn_reset.argtypes = [sp, vp]
+    lib.infini_attn_reset.restype = ctypes.c_int
+    lib.infini_attn_last_error.argtypes = []
+    lib.infini_attn_last_error.restype = ctypes.c_char_p
+    lib.infini_attn_abi_version.argtypes = []
+    lib.infini_attn_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions declared in the C header."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"\b(infini_attn_[a-z_]+)\s*\(", text)))
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check(rc: int) -> int:
+    if rc != OK:
+        raise InfiniError(rc, last_error())
+    return rc
+
+
+def last_error() -> str:
+    return load_library().infini_attn_last_error().decode()
+
+
+def abi_version() -> int:
+    return load_library().infini_attn_abi_version()
+
+
+def init_state(st: State, batch, heads, d_key, d_value, segment_len, dtype, rule, scale, M, z, stream=None,
+               check=True) -> int:
+    rc = load_library().infini_attn_init_state(ctypes.byref(st), batch, heads, d_key, d_value, segment_len, dtype,
+                                               rule, scale, _ptr(M), _ptr(z), stream)
+    return _check(rc) if check else rc
+
+
+def workspace_bytes(st: State, seq_len: int) -> int:
+    return load_library().infini_attn_workspace_bytes(ctypes.byref(st), seq_len)
+
+
+def forward_sequence(st: State, q, k, v, seq_len, beta, out, workspace, ws_bytes, stream=None, check=True) -> int:
+    rc = load_library().infini_attn_forward_sequence(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len,
+                                                     _ptr(beta), _ptr(out), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
+def forward_segment(st: State, q, k, v, beta, out, workspace, ws_bytes, stream=None, check=True) -> int:
+    rc = load_library().infini_attn_forward_segment(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                                    _ptr(out), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
+def reset(st: State, stream=None, check=True) -> int:
+    rc = load_library().infini_attn_reset(ctypes.byref(st), stream)
+    return _check(rc) if check else rc
+
+
+def _stream_handle(torch, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class InfiniAttention:
+    """One Infini-attention state on a GPU with torch-owned buffers.
+
+    Inputs are device tensors [B, H, L, d] of the state's dtype (torch.bfloat16
+    or torch.float32); beta is a device fp32 tensor [H]."""
+
+    def __init__(self, batch, heads, d_key, d_value, segment_len, dtype="bf16", rule="linear", scale=0.0,
+                 device="cuda", stream=None):
+        import torch
+
+        self.torch = torch
+        self.device = torch.device(device)
+        self.dtype_code = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+        self.rule_code = RULES[rule] if isinstance(rule, str) else int(rule)
+        self.M = torch.empty((batch, heads, d_key, d_value), dtype=torch.float32, device=self.device)
+        self.z = torch.empty((batch, heads, d_key), dtype=torch.float32, device=self.device)
+        self.state = State()
+        self._ws = None
+        self._ws_bytes = 0
+        init_state(self.state, batch, heads, d_key, d_value, segment_len, self.dtype_code, self.rule_code,
+                   float(scale), self.M, self.z, _stream_handle(torch, stream))
+
+    @property
+    def torch_dtype(self):
+        return self.torch.bfloat16 if self.dtype_code == BF16 else self.torch.float32
+
+    @property
+    def segments_done(self) -> int:
+        return int(self.state.segments_done)
+
+    def workspace(self, seq_len: int):
+        need = workspace_bytes(self.state, seq_len)
+        if need == 0:
+            raise InfiniError(EINVAL, f"no workspace size for seq_len={seq_len}")
+        if self._ws_bytes < need:
+            raw = self.torch.empty(need + 256, dtype=self.torch.uint8, device=self.device)
+            off = (-raw.data_ptr()) % 256
+            self._ws_raw, self._ws, self._ws_bytes = raw, raw[off:off + need], need
+        return self._ws, self._ws_bytes
+
+    def forward_sequence(self, q, k, v, beta, out=None, stream=None):
+        seq_len = q.shape[2]
+        if out is None:
+            out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
+        ws, nbytes = self.workspace(seq_len)
+        forward_sequence(self.state, q, k, v, seq_len, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
+        return out
+
+    def forward_segment(self, q, k, v, beta, out=None, stream=None):
+        if out is None:
+            out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
+        ws, nbytes = self.workspace(self.state.segment_len)
+        forward_segment(self.state, q, k, v, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
+        return out
+
+    def reset(self, stream=None):
+        reset(self.state, _stream_handle(self.torch, stream))

@@ -1,0 +1,128 @@
+/*
+ * infini_attn.h -- C ABI of the Infini-attention segment forward for AMD MI355X (gfx950).
+ *
+ * The method: "Leave No Context Behind: Efficient Infinite Context Transformers
+ * with Infini-attention" (Munkhdalai, Faruqui, Golovnev; arXiv 2404.07143), as
+ * restated on the pages "精读笔记：Infini-attention" (sections 3.1-3.8),
+ * "忘记遗忘：解锁无限上下文的 Infini-attention" (section 2) and
+ * "第24章 Sparse与Infinite Attention" (sections 24.4-24.5).
+ *
+ * For every (batch b, head h) the sequence is cut into segments of N tokens and
+ * the segments are processed in order.  Segment s of head (b, h) computes
+ *
+ *   A_dot = softmax(scale * Q K^T, causal inside the segment) V        (section 3.1)
+ *   A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1}),  sigma = ELU + 1      (section 3.3)
+ *   A     = g * A_mem + (1 - g) * A_dot,  g = sigmoid(beta_h)           (section 3.5)
+ *
+ * and then updates the compressive state (section 3.4):
+ *
+ *   linear: M_s = M_{s-1} + sigma(K)^T V
+ *   delta : M_s = M_{s-1} + sigma(K)^T (V - sigma(K) M_{s-1} / (sigma(K) z_{s-1}))
+ *   both  : z_s = z_{s-1} + sum_t sigma(K_t)
+ *
+ * Conventions fixed by this library: M_0 = 0, z_0 = 0; in the first segment after
+ * init or reset A_mem = 0 and the delta correction is 0 (so the first delta
+ * update equals the linear one).  "First" is decided by the state's segment
+ * counter.  scale <= 0 selects 1/sqrt(d_key).  The delta correction is
+ * segment-batched: every token of segment s reads M_{s-1}, z_{s-1}.
+ *
+ * Memory and layouts.  Every tensor pointer is a DEVICE pointer to contiguous
+ * row-major memory owned by the caller; the library never allocates, frees or
+ * keeps device memory and holds no global state besides a thread-local error
+ * string and a per-device cache of device properties.
+ *   q, k  : [B, H, L, d_key]   dtype of the state (fp32 or bf16)
+ *   v, out: [B, H, L, d_value] same dtype
+ *   beta  : [H] fp32, one gate logit per head shared over the batch (section 3.5)
+ *   M     : [B, H, d_key, d_value] fp32;  z: [B, H, d_key] fp32
+ * out must not alias q, k, v, M, z or the workspace.
+ *
+ * Supported shapes.  fp32: 1 <= d_key, d_value <= 128, any N >= 1.
+ * bf16 (the fast path): d_key == d_value in {64, 128}, N a positive multiple of 64.
+ * Other shapes return INFINI_EUNSUPPORTED.
+ *
+ * Errors.  Every entry point validates all of its arguments before making any
+ * HIP call; on an error it enqueues nothing, leaves *st unchanged and returns a
+ * negative infini_status; infini_attn_last_error() then describes the problem.
+ * Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
+ * call returns without synchronising; a launch failure returns INFINI_EHIP and a
+ * device fault surfaces at the caller's next synchronisation.
+ *
+ * Threads.  One state must not be used from two threads or two streams at once.
+ * The counter segments_done advances on the host at enqueue time.
+ */
+#ifndef INFINI_ATTN_H
+#define INFINI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INFINI_OK = 0,
+  INFINI_EINVAL = -1,        /* a null pointer, a non-positive or inconsistent size */
+  INFINI_EUNSUPPORTED = -2,  /* a valid shape or dtype this build has no kernel for */
+  INFINI_EWORKSPACE = -3,    /* workspace missing or smaller than infini_attn_workspace_bytes */
+  INFINI_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+} infini_status;
+
+typedef enum { INFINI_RULE_LINEAR = 0, INFINI_RULE_DELTA = 1 } infini_rule;
+typedef enum { INFINI_F32 = 0, INFINI_BF16 = 1 } infini_dtype;
+
+/* Caller-allocated plain struct.  Fill it only through infini_attn_init_state. */
+typedef struct {
+  int32_t batch, heads, d_key, d_value, segment_len; /* B, H, d_key, d_value, N */
+  int32_t dtype;          /* infini_dtype of q, k, v and out */
+  int32_t rule;           /* infini_rule */
+  float scale;            /* softmax scale actually used (1/sqrt(d_key) if given <= 0) */
+  float *M;               /* device fp32 [B, H, d_key, d_value], caller-owned */
+  float *z;               /* device fp32 [B, H, d_key], caller-owned */
+  int64_t segments_done;  /* segments folded into (M, z); 0 => next segment reads an empty memory */
+} infini_attn_state;
+
+/* Validates the configuration, fills *st, zeroes M and z on `stream` and sets the
+ * counter to 0 (the state of a fresh stream: M_0 = 0, z_0 = 0). */
+int infini_attn_init_state(infini_attn_state *st, int32_t batch, int32_t heads,
+                           int32_t d_key, int32_t d_value, int32_t segment_len,
+                           int32_t dtype, int32_t rule, float scale,
+                           float *M, float *z, void *stream);
+
+/* Bytes of device workspace that forward_sequence needs for seq_len tokens
+ * (forward_segment: seq_len = segment_len).  Returns 0 for an invalid state or a
+ * seq_len that is not a positive multiple of the segment length. */
+size_t infini_attn_workspace_bytes(const infini_attn_state *st, int64_t seq_len);
+
+/* Processes the S = seq_len / N segments of every (b, h) in order, starting from
+ * the state's (M, z, segments_done), writes A to out and leaves (M_S, z_S) in the
+ * state; segments_done += S.  q, k, v, out hold seq_len tokens per (b, h).
+ * beta: device fp32 [H].  workspace: device memory of at least
+ * infini_attn_workspace_bytes(st, seq_len) bytes, 256-byte aligned, contents
+ * irrelevant on entry and undefined on return. */
+int infini_attn_forward_sequence(infini_attn_state *st, const void *q, const void *k,
+                                 const void *v, int64_t seq_len, const float *beta,
+                                 void *out, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* One segment: the same as forward_sequence with seq_len = segment_len.  A stream
+ * fed segment by segment gives bitwise the same results as one
+ * forward_sequence call over the whole stream. */
+int infini_attn_forward_segment(infini_attn_state *st, const void *q, const void *k,
+                                const void *v, const float *beta, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* M, z <- 0 on `stream`; segments_done <- 0. */
+int infini_attn_reset(infini_attn_state *st, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *infini_attn_last_error(void);
+
+/* Library ABI version, currently 1. */
+int infini_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFINI_ATTN_H */

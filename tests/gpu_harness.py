@@ -1,0 +1,169 @@
+"""Shared helpers of the GPU parity tests: seeded inputs on the device, library
+calls through the C ABI, and per-(b, h, segment) comparison with the oracle.
+
+Metrics (one value per (b, h, s) tile of the output, and for the final state):
+  fp32 inputs: max|gpu - ref| / max|ref|          (bar 1e-4)
+  bf16 inputs: ||gpu - ref||_F / ||ref||_F        (bar 2e-2)
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+
+from compressive_memory_transformer_amd import infini as ia
+from compressive_memory_transformer_amd import synthetic as syn
+from oracle import infini_ref as ref
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def upload(w: syn.Workload, tensor_id: int, heads=None, segments=None):
+    """Full [B, H, L, d] device tensor of one input (bf16 or fp32)."""
+    torch = torch_mod()
+    arr = syn.full_tensor(w, tensor_id, as_bits=True, heads=heads, segments=segments)
+    if w.dtype == "bf16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(arr)
+    out = t.to("cuda")
+    del arr, t
+    return out
+
+
+def device_inputs(w: syn.Workload, heads=None, segments=None):
+    torch = torch_mod()
+    t0 = time.time()
+    q, k, v = (upload(w, i, heads, segments) for i in (syn.Q_ID, syn.K_ID, syn.V_ID))
+    beta = torch.from_numpy(syn.betas(w)).to("cuda")
+    if heads is not None:
+        beta = beta[list(heads)].contiguous()
+    torch.cuda.synchronize()
+    log(f"  inputs of {w.name} on device in {time.time() - t0:.1f}s")
+    return q, k, v, beta
+
+
+def metric(gpu: np.ndarray, want: np.ndarray, dtype: str) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if dtype == "f32":
+        den = np.abs(want).max()
+        return float(np.abs(gpu - want).max() / den) if den > 0 else float(np.abs(gpu).max())
+    den = np.linalg.norm(want)
+    return float(np.linalg.norm(gpu - want) / den) if den > 0 else float(np.linalg.norm(gpu))
+
+
+def tol(dtype: str) -> float:
+    return F32_TOL if dtype == "f32" else BF16_TOL
+
+
+def to_host(t) -> np.ndarray:
+    torch = torch_mod()
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def run(w: syn.Workload, rule: str, q, k, v, beta, mode: str = "sequence", engine=None, stream=None):
+    """Runs the library over the whole stream; returns (out, engine)."""
+    B, H, L, D = q.shape
+    eng = engine or ia.InfiniAttention(B, H, q.shape[3], v.shape[3], w.segment_len, w.dtype, rule)
+    if mode == "sequence":
+        out = eng.forward_sequence(q, k, v, beta, stream=stream)
+    else:
+        torch = torch_mod()
+        out = torch.empty((B, H, L, v.shape[3]), dtype=q.dtype, device=q.device)
+        N = w.segment_len
+        for s in range(L // N):
+            sl = slice(s * N, (s + 1) * N)
+            o = eng.forward_segment(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(), v[:, :, sl].contiguous(),
+                                    beta, stream=stream)
+            out[:, :, sl] = o
+    return out, eng
+
+
+def oracle_full(w: syn.Workload, rule: str, beta_np=None, heads=None, segments=None, keep_parts=False):
+    hs = list(range(w.heads)) if heads is None else list(heads)
+    q, k, v = (syn.full_tensor(w, i, heads=hs, segments=segments) for i in (0, 1, 2))
+    b = syn.betas(w)[hs] if beta_np is None else beta_np
+    return ref.forward_sequence(q, k, v, b, rule, w.segment_len, keep_parts=keep_parts)
+
+
+def compare_full(w, rule, out, eng, res, label=""):
+    """Per-tile comparison of a full GPU output against a full oracle result."""
+    N = w.segment_len
+    got = to_host(out)
+    worst = 0.0
+    B, H, L, _ = got.shape
+    for b in range(B):
+        for h in range(H):
+            for s in range(L // N):
+                sl = slice(s * N, (s + 1) * N)
+                e = metric(got[b, h, sl], res["A"][b, h, sl], w.dtype)
+                worst = max(worst, e)
+                assert e <= tol(w.dtype), f"{label} tile b={b} h={h} s={s}: error {e:.3e}"
+    eM = metric(to_host(eng.M), res["M"], w.dtype)
+    ez = metric(to_host(eng.z), res["z"], w.dtype)
+    log(f"  {label}: worst tile error {worst:.3e}; final M {eM:.3e}; z {ez:.3e}")
+    assert eM <= tol(w.dtype) and ez <= tol(w.dtype)
+    return worst, eM, ez
+
+
+def oracle_walk(w: syn.Workload, rule: str, b: int, h: int, sample_segments, beta=None):
+    """Memory-only walk of one head through all segments; at each sampled segment
+    the full oracle segment output is produced.  Returns ({s: A_s}, M_S, z_S)."""
+    N, dk, dv = w.segment_len, w.d_key, w.d_value
+    M = np.zeros((dk, dv))
+    z = np.zeros(dk)
+    sc = ref.default_scale(dk)
+    bt = float(syn.betas(w)[h]) if beta is None else float(beta)
+    want = {}
+    samples = set(sample_segments)
+    for s in range(w.segments):
+        k = syn.tile(w, syn.K_ID, b, h, s).astype(np.float64)
+        v = syn.tile(w, syn.V_ID, b, h, s).astype(np.float64)
+        if s in samples:
+            q = syn.tile(w, syn.Q_ID, b, h, s).astype(np.float64)
+            a, M2, z2, _, _ = ref.segment_forward(q, k, v, M, z, bt, rule, s == 0, sc)
+            want[s] = a
+            M, z = M2, z2
+        else:
+            M, z = ref.memory_update(k, v, M, z, rule, s == 0)
+    return want, M, z
+
+
+def compare_sampled(w, rule, out, eng, heads_bh, sample_segments, beta=None, label=""):
+    """Sampled comparison for workloads too large for a full oracle run."""
+    N = w.segment_len
+    worst = 0.0
+    for (b, h) in heads_bh:
+        t0 = time.time()
+        want, M, z = oracle_walk(w, rule, b, h, sample_segments, beta)
+        for s, a in want.items():
+            got = to_host(out[b, h, s * N:(s + 1) * N])
+            e = metric(got, a, w.dtype)
+            worst = max(worst, e)
+            assert e <= tol(w.dtype), f"{label} b={b} h={h} s={s}: error {e:.3e}"
+        eM = metric(to_host(eng.M[b, h]), M, w.dtype)
+        ez = metric(to_host(eng.z[b, h]), z, w.dtype)
+        log(f"  {label} head ({b},{h}): worst sampled tile {worst:.3e}; final M {eM:.3e}; z {ez:.3e} "
+            f"(oracle walk {time.time() - t0:.1f}s)")
+        assert eM <= tol(w.dtype) and ez <= tol(w.dtype)
+    return worst
+
+
+def inf_beta(H, sign):
+    torch = torch_mod()
+    return torch.full((H,), math.inf * sign, dtype=torch.float32, device="cuda")

@@ -1,0 +1,137 @@
+"""The C ABI on the CPU: the library loads, exports every declared function, and
+rejects invalid arguments before any HIP call (no GPU is needed for these)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from compressive_memory_transformer_amd import infini as ia
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(ia.LIB_PATH),
+                                reason="library not built")
+
+FAKE = 1 << 40  # never dereferenced: every call below fails validation first
+
+
+def _state(**over):
+    st = ia.State()
+    vals = dict(batch=1, heads=2, d_key=128, d_value=128, segment_len=2048, dtype=ia.BF16,
+                rule=ia.RULE_LINEAR, scale=0.08838834764831845, M=FAKE, z=FAKE * 2, segments_done=0)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(st, k, v)
+    return st
+
+
+def _snapshot(st):
+    return tuple(getattr(st, f) for f, _ in ia.State._fields_)
+
+
+def test_exports_every_declared_function():
+    lib = ia.load_library()
+    names = ia.header_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert ia.abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(ia.State) == 56
+    assert ia.State.M.offset == 32 and ia.State.segments_done.offset == 48
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 2, 128, 128, 2048, ia.BF16, ia.RULE_LINEAR), ia.EINVAL),
+    ((1, 0, 128, 128, 2048, ia.BF16, ia.RULE_LINEAR), ia.EINVAL),
+    ((1, 2, 128, 128, 0, ia.BF16, ia.RULE_LINEAR), ia.EINVAL),
+    ((1, 2, 128, 128, 2048, 7, ia.RULE_LINEAR), ia.EINVAL),
+    ((1, 2, 128, 128, 2048, ia.BF16, 9), ia.EINVAL),
+    ((1, 2, 96, 96, 2048, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
+    ((1, 2, 128, 64, 2048, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
+    ((1, 2, 128, 128, 2000, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
+    ((1, 2, 256, 32, 64, ia.F32, ia.RULE_LINEAR), ia.EUNSUPPORTED),
+    ((1, 2, 32, 32, 8192, ia.F32, ia.RULE_LINEAR), ia.EUNSUPPORTED),
+])
+def test_init_state_rejects_bad_config(args, code):
+    st = ia.State()
+    before = _snapshot(st)
+    rc = ia.init_state(st, *args, 0.0, FAKE, FAKE * 2, None, check=False)
+    assert rc == code
+    assert ia.last_error()
+    assert _snapshot(st) == before
+
+
+def test_init_state_rejects_null_and_inf():
+    st = ia.State()
+    assert ia.init_state(st, 1, 2, 32, 32, 64, ia.F32, 0, 0.0, None, FAKE, None, check=False) == ia.EINVAL
+    assert ia.init_state(st, 1, 2, 32, 32, 64, ia.F32, 0, float("inf"), FAKE, FAKE * 2, None,
+                         check=False) == ia.EINVAL
+    assert ia.load_library().infini_attn_init_state(None, 1, 2, 32, 32, 64, 0, 0, 0.0, FAKE, FAKE, None) == ia.EINVAL
+
+
+def test_workspace_bytes():
+    st = _state(rule=ia.RULE_LINEAR)
+    S, D, BH = 16, 128, 2
+    want = BH * S * D * D * 2 + BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4
+    assert ia.workspace_bytes(st, S * 2048) == want
+    st = _state(rule=ia.RULE_DELTA)
+    assert ia.workspace_bytes(st, S * 2048) == BH * S * D * D * 2 + BH * S * D * 4
+    assert ia.workspace_bytes(st, 2047) == 0
+    assert ia.workspace_bytes(st, 0) == 0
+    assert ia.workspace_bytes(_state(batch=0), 2048) == 0
+    f32 = _state(dtype=ia.F32, d_key=32, d_value=16, segment_len=64, rule=ia.RULE_DELTA)
+    assert ia.workspace_bytes(f32, 256) == 2 * 64 * 16 * 4
+    assert ia.workspace_bytes(_state(dtype=ia.F32, d_key=32, d_value=32, segment_len=64), 256) == 256
+
+
+@pytest.mark.parametrize("case", ["null_q", "null_beta", "ragged", "zero_len", "small_ws", "null_ws",
+                                  "misaligned", "alias_out", "alias_state", "bad_state", "uninit"])
+def test_forward_rejects_bad_arguments(case):
+    st = _state()
+    L = 2 * 2048
+    need = ia.workspace_bytes(st, L)
+    q, k, v, beta = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7
+    out, ws, nbytes = FAKE * 8, FAKE * 9, need
+    expect = ia.EINVAL
+    if case == "null_q":
+        q = None
+    elif case == "null_beta":
+        beta = None
+    elif case == "ragged":
+        L = 2048 + 64
+    elif case == "zero_len":
+        L = 0
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    elif case == "null_ws":
+        ws, expect = None, ia.EWORKSPACE
+    elif case == "misaligned":
+        q = FAKE * 4 + 2
+    elif case == "alias_out":
+        out = k + 1024
+    elif case == "alias_state":
+        out = st.M - 64
+    elif case == "bad_state":
+        st.d_key = 100
+        expect = ia.EUNSUPPORTED
+    elif case == "uninit":
+        st = ia.State()
+    before = _snapshot(st)
+    rc = ia.forward_sequence(st, q, k, v, L, beta, out, ws, nbytes, None, check=False)
+    assert rc == expect, ia.last_error()
+    assert ia.last_error()
+    assert _snapshot(st) == before
+
+
+def test_segment_and_reset_validate():
+    st = _state()
+    before = _snapshot(st)
+    assert ia.forward_segment(st, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, check=False) == ia.EINVAL
+    assert ia.reset(ia.State(), None, check=False) == ia.EINVAL
+    assert ia.load_library().infini_attn_reset(None, None) == ia.EINVAL
+    assert _snapshot(st) == before
