@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Throughput of the Infini-attention segment forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rule RULE]
+
+One step = one pass of the whole path over one batch of the workload's synthetic
+stream: reset the state, then forward_sequence over all segments of every head
+(memory-state stage + fused attention/retrieval/gate stage), inputs resident in
+HBM.  The timed region is K steps bracketed by device synchronisation.  Prints
+one JSON line with the whole-job tokens/s, the roofline position of the
+dominant kernel (the fused attention kernel, timed live with HIP events around
+its stage on the stream it runs on) and the float64 oracle timed on the host
+cores over a bounded prefix of the same stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
+DOMINANT_SOURCES = ["compressive_memory_transformer_amd/csrc/fa_fwd.hip",
+                    "compressive_memory_transformer_amd/csrc/common.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="layer_32k_linear")
+    p.add_argument("--rule", default=None)
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="budget of the oracle leg (0 disables it)")
+    return p.parse_args()
+
+
+def hip_runtime():
+    """The HIP runtime already mapped into this process (the one torch uses)."""
+    maps = open("/proc/self/maps").read()
+    paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", maps)))
+    return ctypes.CDLL(paths[0] if paths else "libamdhip64.so")
+
+
+class Events:
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev.append(e.value)
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]), ctypes.c_void_p(self.ev[b]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def attention_flops(w, first_segment_global: int = 0) -> int:
+    """Algorithmic FLOPs of one launch of the fused kernel: causal pairs only,
+    2 * d * N (N + 1) per (b, h, segment) for QK^T and PV, plus the retrieval GEMM
+    and its denominator 2 * N * d_k * (d_v + 1) for every segment that reads a
+    non-empty memory."""
+    N, dk, dv = w.segment_len, w.d_key, w.d_value
+    att = 2 * dk * N * (N + 1) // 2 + 2 * dv * N * (N + 1) // 2
+    ret = 2 * N * dk * dv + 2 * N * dk
+    seg_with_memory = sum(1 for s in range(w.segments) if first_segment_global + s > 0)
+    return w.batch * w.heads * (w.segments * att + seg_with_memory * ret)
+
+
+def state_flops(w, rule: str) -> int:
+    N, dk, dv = w.segment_len, w.d_key, w.d_value
+    upd = 2 * N * dk * dv + N * dk
+    if rule == "delta":
+        upd += 2 * N * dk * dv + 2 * N * dk
+    return w.batch * w.heads * w.segments * upd
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in DOMINANT_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, rule: str):
+    """HBM bytes per launch of the fused kernel from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    entry = rec.get("workloads", {}).get(f"{workload}/{rule}")
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, rule: str, budget_s: float):
+    """The float64 oracle on the host over a prefix of the same stream: segments in
+    order, all heads of a segment before the next, until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from compressive_memory_transformer_amd import synthetic as syn
+    from oracle import infini_ref as ref
+
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    sc = ref.default_scale(w.d_key)
+    betas = syn.betas(w)
+    M = {(b, h): np.zeros((w.d_key, w.d_value)) for b in range(w.batch) for h in range(w.heads)}
+    z = {key: np.zeros(w.d_key) for key in M}
+    done = 0
+    spent = 0.0
+    for s in range(w.segments):
+        for (b, h) in M:
+            q, k, v = (syn.tile(w, i, b, h, s).astype(np.float64) for i in (0, 1, 2))
+            t0 = time.perf_counter()
+            _, M[(b, h)], z[(b, h)], _, _ = ref.segment_forward(q, k, v, M[(b, h)], z[(b, h)], float(betas[h]),
+                                                                rule, s == 0, sc)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    tokens = done * w.segment_len / w.heads
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.heads * w.segments} (batch, head, segment) tiles of {w.name}/{rule}, "
+                      f"in stream order, float64 numpy, {spent:.1f}s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
+              "this library has no multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from compressive_memory_transformer_amd import infini as ia
+    from compressive_memory_transformer_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = syn.WORKLOADS[args.workload]
+    rule = args.rule or w.rules[0]
+    ia.load_library()
+
+    def upload(tid):
+        arr = syn.full_tensor(w, tid, as_bits=True)
+        if w.dtype == "bf16":
+            import numpy as np
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(arr).to("cuda")
+
+    q, k, v = (upload(i) for i in (0, 1, 2))
+    beta = torch.from_numpy(syn.betas(w)).to("cuda")
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, w.dtype, rule)
+    out = torch.empty((w.batch, w.heads, w.seq_len, w.d_value), dtype=q.dtype, device="cuda")
+    ws, ws_bytes = eng.workspace(w.seq_len)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    hip = hip_runtime()
+    ev = Events(hip, 3 * args.steps)
+
+    def step(events=None):
+        ia.reset(eng.state, sh)
+        if events is None:
+            ia.forward_sequence(eng.state, q, k, v, w.seq_len, beta, out, ws, ws_bytes, sh)
+        else:
+            ia.forward_sequence_profiled(eng.state, q, k, v, w.seq_len, beta, out, ws, ws_bytes, sh, events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev.ev[3 * i:3 * i + 3])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall = t1 - t0
+    tokens = w.batch * w.seq_len
+    fa_ms = [ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]
+    st_ms = [ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]
+    ev.destroy()
+    fa_avg = sum(fa_ms) / len(fa_ms)
+    st_avg = sum(st_ms) / len(st_ms)
+    fl = attention_flops(w)
+    achieved = fl / (fa_avg * 1e-3) / 1e12
+    step_fl = fl + state_flops(w, rule)
+    traffic = traffic_for(w.name, rule)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, rule, args.cpu_seconds)
+
+    line = {
+        "metric": "Infini-attention fwd tokens/sec on 1 MI355X + % of bf16 MFMA/HBM roofline",
+        "value": tokens * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "segment_len": w.segment_len, "d_key": w.d_key, "d_value": w.d_value, "rule": rule,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": fa_avg},
+        "stages_ms": {"state": st_avg, "attention": fa_avg},
+        "step_tflops": step_fl / (wall / args.steps) / 1e12,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

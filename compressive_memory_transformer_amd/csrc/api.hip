@@ -119,9 +119,18 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(INFINI_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+int record(void* const* events, int i, hipStream_t stream) {
+  if (!events) return INFINI_OK;
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+  return e == hipSuccess ? INFINI_OK : hip_fail(e, "hipEventRecord");
+}
+
 template <int D>
 int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t L, int S,
-             const float* beta, void* out, char* ws, const WsLayout& w, hipStream_t stream) {
+             const float* beta, void* out, char* ws, const WsLayout& w, hipStream_t stream,
+             void* const* events) {
+  int rc;
+  if ((rc = record(events, 0, stream)) != INFINI_OK) return rc;
   using infini::bf16;
   const int B = st->batch, H = st->heads, N = st->segment_len;
   bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
@@ -139,16 +148,20 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
                         B * H, S, N, L, st->segments_done};
     if ((e = infini::launch_delta_chain<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta_chain launch");
   }
+  if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,
                    snapM, snapz, static_cast<bf16*>(out), B, H, S, N, L, (N + 127) / 128,
                    st->segments_done, (float)((double)st->scale * 1.4426950408889634)};
   if ((e = infini::launch_fa_fwd<D>(f, stream)) != hipSuccess) return hip_fail(e, "fa_fwd launch");
-  return INFINI_OK;
+  return record(events, 2, stream);
 }
 
 int run_f32(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t L, int S,
-            const float* beta, void* out, char* ws, const WsLayout& w, hipStream_t stream) {
+            const float* beta, void* out, char* ws, const WsLayout& w, hipStream_t stream,
+            void* const* events) {
   const int BH = st->batch * st->heads, N = st->segment_len;
+  int rc;
+  if ((rc = record(events, 0, stream)) != INFINI_OK) return rc;
   for (int s = 0; s < S; ++s) {
     const int64_t off = (int64_t)s * N;
     const int has_memory = (st->segments_done + s) > 0;
@@ -163,7 +176,8 @@ int run_f32(infini_attn_state* st, const void* q, const void* k, const void* v, 
     e = infini::launch_f32_update(u, stream);
     if (e != hipSuccess) return hip_fail(e, "f32 update launch");
   }
-  return INFINI_OK;
+  if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
+  return record(events, 2, stream);
 }
 
 int zero_state(infini_attn_state* st, float* M, float* z, hipStream_t stream) {
@@ -220,9 +234,9 @@ size_t infini_attn_workspace_bytes(const infini_attn_state* st, int64_t seq_len)
   return w.total;
 }
 
-int infini_attn_forward_sequence(infini_attn_state* st, const void* q, const void* k, const void* v,
-                                 int64_t seq_len, const float* beta, void* out, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+static int forward_impl(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t seq_len,
+                        const float* beta, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* events) {
   int rc = check_state(st);
   if (rc != INFINI_OK) return rc;
   if (!q || !k || !v || !beta || !out) return fail(INFINI_EINVAL, "q, k, v, beta and out must be non-NULL");
@@ -267,14 +281,29 @@ int infini_attn_forward_sequence(infini_attn_state* st, const void* q, const voi
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (st->dtype == INFINI_BF16) {
-    rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm)
-                          : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm);
+    rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events)
+                          : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events);
   } else {
-    rc = run_f32(st, q, k, v, seq_len, S, beta, out, ws, w, strm);
+    rc = run_f32(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events);
   }
   if (rc != INFINI_OK) return rc;
   st->segments_done += S;
   return ok();
+}
+
+int infini_attn_forward_sequence(infini_attn_state* st, const void* q, const void* k, const void* v,
+                                 int64_t seq_len, const float* beta, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return forward_impl(st, q, k, v, seq_len, beta, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int infini_attn_forward_sequence_profiled(infini_attn_state* st, const void* q, const void* k, const void* v,
+                                          int64_t seq_len, const float* beta, void* out, void* workspace,
+                                          size_t workspace_bytes, void* stream, void* const* events,
+                                          int32_t n_events) {
+  if (!events || n_events != 3 || !events[0] || !events[1] || !events[2])
+    return fail(INFINI_EINVAL, "profiled forward needs exactly 3 non-NULL events");
+  return forward_impl(st, q, k, v, seq_len, beta, out, workspace, workspace_bytes, stream, events);
 }
 
 int infini_attn_forward_segment(infini_attn_state* st, const void* q, const void* k, const void* v,

@@ -63,6 +63,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
+    try:
+        # torch ships its own libamdhip64; loading it first makes the library bind to
+        # that same HIP runtime (matched by soname) instead of a second copy.
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         raise LibraryNotBuilt(f"{p} not found: build it with `python -m compressive_memory_transformer_amd.build`")
     lib = ctypes.CDLL(p)
@@ -74,6 +80,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_workspace_bytes.restype = sz
     lib.infini_attn_forward_sequence.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     lib.infini_attn_forward_sequence.restype = ctypes.c_int
+    lib.infini_attn_forward_sequence_profiled.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, sz, vp,
+                                                          ctypes.POINTER(vp), i32]
+    lib.infini_attn_forward_sequence_profiled.restype = ctypes.c_int
     lib.infini_attn_forward_segment.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.infini_attn_forward_segment.restype = ctypes.c_int
     lib.infini_attn_reset.argtypes = [sp, vp]
@@ -129,6 +138,17 @@ def workspace_bytes(st: State, seq_len: int) -> int:
 def forward_sequence(st: State, q, k, v, seq_len, beta, out, workspace, ws_bytes, stream=None, check=True) -> int:
     rc = load_library().infini_attn_forward_sequence(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len,
                                                      _ptr(beta), _ptr(out), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
+def forward_sequence_profiled(st: State, q, k, v, seq_len, beta, out, workspace, ws_bytes, stream, events,
+                              check=True) -> int:
+    """forward_sequence recording the HIP events ``events`` (3 raw hipEvent_t handles)
+    before the state stage, between the stages and after the attention stage."""
+    arr = (ctypes.c_void_p * len(events))(*events)
+    rc = load_library().infini_attn_forward_sequence_profiled(
+        ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len, _ptr(beta), _ptr(out), _ptr(workspace), ws_bytes,
+        stream, arr, len(events))
     return _check(rc) if check else rc
 
 

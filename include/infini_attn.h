@@ -29,7 +29,7 @@
  * Memory and layouts.  Every tensor pointer is a DEVICE pointer to contiguous
  * row-major memory owned by the caller; the library never allocates, frees or
  * keeps device memory and holds no global state besides a thread-local error
- * string and a per-device cache of device properties.
+ * string.
  *   q, k  : [B, H, L, d_key]   dtype of the state (fp32 or bf16)
  *   v, out: [B, H, L, d_value] same dtype
  *   beta  : [H] fp32, one gate logit per head shared over the batch (section 3.5)
@@ -104,6 +104,18 @@ int infini_attn_forward_sequence(infini_attn_state *st, const void *q, const voi
                                  const void *v, int64_t seq_len, const float *beta,
                                  void *out, void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/* forward_sequence that also records caller-created HIP events (hipEvent_t, as
+ * void*) on `stream` at the stage boundaries, for profiling tools:
+ *   events[0] before the first kernel, events[1] after the memory-state stage
+ *   (linear contributions + prefix scan, or the delta chain; for fp32 after the
+ *   last segment's update), events[2] after the fused attention stage.
+ * n_events must be 3 and every event non-NULL; otherwise INFINI_EINVAL.  The
+ * arithmetic and results are those of forward_sequence. */
+int infini_attn_forward_sequence_profiled(infini_attn_state *st, const void *q, const void *k,
+                                          const void *v, int64_t seq_len, const float *beta,
+                                          void *out, void *workspace, size_t workspace_bytes,
+                                          void *stream, void *const *events, int32_t n_events);
 
 /* One segment: the same as forward_sequence with seq_len = segment_len.  A stream
  * fed segment by segment gives bitwise the same results as one

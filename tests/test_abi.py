@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -126,6 +126,15 @@ def test_forward_rejects_bad_arguments(case):
     assert rc == expect, ia.last_error()
     assert ia.last_error()
     assert _snapshot(st) == before
+
+
+def test_profiled_needs_three_events():
+    st = _state()
+    L = 2048
+    need = ia.workspace_bytes(st, L)
+    args = (st, FAKE * 4, FAKE * 5, FAKE * 6, L, FAKE * 7, FAKE * 8, FAKE * 9, need, None)
+    assert ia.forward_sequence_profiled(*args, [FAKE, FAKE], check=False) == ia.EINVAL
+    assert ia.forward_sequence_profiled(*args, [FAKE, None, FAKE], check=False) == ia.EINVAL
 
 
 def test_segment_and_reset_validate():
