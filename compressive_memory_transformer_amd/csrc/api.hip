@@ -83,7 +83,7 @@ int check_state(const infini_attn_state* st) {
 }
 
 struct WsLayout {
-  size_t snapM = 0, snapz = 0, cM = 0, cz = 0, U = 0, total = 0;
+  size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, U = 0, total = 0;
 };
 
 // Workspace regions, each 256-byte aligned.  Returns false on overflow.
@@ -97,6 +97,7 @@ bool workspace_layout(const infini_attn_state* st, int64_t S, WsLayout* w) {
     if (!mul_ok(seg_heads, D * D, &n)) return false;
     w->snapM = off; off = align_up(off + (size_t)n * 2);
     w->snapz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
+    w->snapc = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
     if (st->rule == INFINI_RULE_LINEAR) {
       w->cM = off; off = align_up(off + (size_t)n * 4);
       w->cz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
@@ -135,22 +136,23 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
   const int B = st->batch, H = st->heads, N = st->segment_len;
   bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
   float* snapz = reinterpret_cast<float*>(ws + w.snapz);
+  float* snapc = reinterpret_cast<float*>(ws + w.snapc);
   hipError_t e;
   if (st->rule == INFINI_RULE_LINEAR) {
     infini::LinContribArgs c{static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                              reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
                              B, H, S, N, L};
     if ((e = infini::launch_lin_contrib<D>(c, stream)) != hipSuccess) return hip_fail(e, "lin_contrib launch");
-    infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, B * H, S};
+    infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, snapc, B * H, S};
     if ((e = infini::launch_lin_scan<D>(sarg, stream)) != hipSuccess) return hip_fail(e, "lin_scan launch");
   } else {
     infini::DeltaArgs d{static_cast<const bf16*>(k), static_cast<const bf16*>(v), st->M, st->z, snapM, snapz,
-                        B * H, S, N, L, st->segments_done};
+                        snapc, B * H, S, N, L, st->segments_done};
     if ((e = infini::launch_delta_chain<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta_chain launch");
   }
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,
-                   snapM, snapz, static_cast<bf16*>(out), B, H, S, N, L, (N + 127) / 128,
+                   snapM, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, (N + 127) / 128,
                    st->segments_done, (float)((double)st->scale * 1.4426950408889634)};
   if ((e = infini::launch_fa_fwd<D>(f, stream)) != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return record(events, 2, stream);

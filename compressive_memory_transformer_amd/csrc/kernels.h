@@ -18,6 +18,7 @@ struct FaArgs {
   const float* beta;     // [H]
   const bf16* snapM;     // [B*H*S][D][D] bf16 snapshot of M_{s-1}^T (row = d_value)
   const float* snapz;    // [B*H*S][D]    fp32 snapshot of z_{s-1}
+  const float* snapc;    // [B*H*S][D]    fp32 column sums of M_{s-1} over d_key
   bf16* out;
   int B, H, S, N;
   int64_t L;
@@ -48,6 +49,7 @@ struct LinScanArgs {
   float* z;              // state [B*H][D]
   bf16* snapM;           // [B*H*S][D][D] (row = d_value)
   float* snapz;          // [B*H*S][D]
+  float* snapc;          // [B*H*S][D] column sums of M over d_key
   int BH, S;
 };
 template <int D> hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream);
@@ -61,6 +63,7 @@ struct DeltaArgs {
   float* z;              // state [B*H][D]
   bf16* snapM;           // [B*H*S][D][D] (row = d_value)
   float* snapz;          // [B*H*S][D]
+  float* snapc;          // [B*H*S][D]
   int BH, S, N;
   int64_t L;
   int64_t seg_base;

@@ -129,33 +129,49 @@ void lin_contrib_kernel(LinContribArgs a) {
   }
 }
 
-// Exclusive prefix over segments, one thread per element of M^T (and of z).
+// Exclusive prefix over segments.  One thread per element of M^T; the last
+// workgroup of each head carries z.  Each snapshot also gets the fp32 column sums
+// of M over d_key (row sums of M^T), reduced in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void lin_scan_kernel(LinScanArgs a) {
-  constexpr int E = D * D + D;
-  const int per_head = (E + kThreads - 1) / kThreads;
-  const int bh = blockIdx.x / per_head;
-  const int e = (blockIdx.x % per_head) * kThreads + threadIdx.x;
-  if (e >= E) return;
-  const bool is_m = e < D * D;
-  const int dv = is_m ? e / D : 0, dk = is_m ? e % D : e - D * D;
-  float run = is_m ? a.M[(int64_t)bh * D * D + dk * D + dv] : a.z[(int64_t)bh * D + dk];
+  constexpr int MB = D * D / kThreads;     // workgroups holding M^T per head
+  constexpr int WPR = D / 64;              // waves per row of M^T
+  static_assert(D * D % kThreads == 0 && D % 64 == 0, "shape");
+  __shared__ float red[2][kThreads / 64];
+  const int bh = blockIdx.x / (MB + 1);
+  const int sub = blockIdx.x % (MB + 1);
   const int64_t base = (int64_t)bh * a.S;
+  if (sub == MB) {
+    const int dk = threadIdx.x;
+    if (dk >= D) return;
+    float run = a.z[(int64_t)bh * D + dk];
+    for (int s = 0; s < a.S; ++s) {
+      a.snapz[(base + s) * D + dk] = run;
+      run += a.cz[(base + s) * D + dk];
+    }
+    a.z[(int64_t)bh * D + dk] = run;
+    return;
+  }
+  const int e = sub * kThreads + threadIdx.x;
+  const int dv = e / D, dk = e % D;
+  const int wave = threadIdx.x >> 6;
+  float run = a.M[(int64_t)bh * D * D + dk * D + dv];
   for (int s = 0; s < a.S; ++s) {
     const int64_t sh = base + s;
-    if (is_m) {
-      a.snapM[sh * D * D + e] = f2bf(run);
-      run += a.cM[sh * D * D + e];
-    } else {
-      a.snapz[sh * D + dk] = run;
-      run += a.cz[sh * D + dk];
+    a.snapM[sh * D * D + e] = f2bf(run);
+    const float part = wave_sum(run);
+    if ((threadIdx.x & 63) == 0) red[s & 1][wave] = part;
+    __syncthreads();
+    if (threadIdx.x % D == 0) {
+      float c = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) c += red[s & 1][wave + w];
+      a.snapc[sh * D + dv] = c;
     }
+    run += a.cM[sh * D * D + e];
   }
-  if (is_m)
-    a.M[(int64_t)bh * D * D + dk * D + dv] = run;
-  else
-    a.z[(int64_t)bh * D + dk] = run;
+  a.M[(int64_t)bh * D * D + dk * D + dv] = run;
 }
 
 // ==================================================================== delta
@@ -176,6 +192,7 @@ void delta_chain_kernel(DeltaArgs a) {
   __shared__ float mt[CB][D];         // M^T block (row = column of M), fp32
   __shared__ float zs[D];
   __shared__ float zred[4][D];
+  __shared__ float csum[CB];          // column sums of the M block over d_key (fp32)
   __shared__ __attribute__((aligned(16))) bf16 stage[4][2][STAGE];  // per wave: hi, lo
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -210,6 +227,21 @@ void delta_chain_kernel(DeltaArgs a) {
     }
     if (cb == 0)
       for (int i = t; i < D; i += kThreads) a.snapz[sh * D + i] = zs[i];
+    {
+      // column sums: 16 threads per column, fixed-order reduction
+      const int j = t >> 4, q16 = t & 15;
+      float part = 0.f;
+      for (int i = q16; i < D; i += 16) part += mt[j][i];
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 4);
+      part += __shfl_xor(part, 8);
+      if (q16 == 0) {
+        csum[j] = part;
+        a.snapc[sh * D + cb * CB + j] = part;
+      }
+    }
+    __syncthreads();
 
     // ---- B operand of the read-back: M[dk][col] = mt[col][dk], bf16
     bf16x8 mop[D / 32];
@@ -246,19 +278,21 @@ void delta_chain_kernel(DeltaArgs a) {
           bf16x8 h8, l8;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float f = elu1(bf2f(kx[i]));
+            const float x = bf2f(kx[i]);
+            const float kp = x > 0.f ? x : exp_e(x) - 1.f;   // k' = sigma(k) - 1
+            const float f = kp + 1.f;
             zacc[c][i] += f;
             den = __builtin_fmaf(f, zs[32 * c + 8 * grp + i], den);
             h8[i] = f2bf(f);
             l8[i] = lo_part(f, h8[i]);
+            kop[c][i] = f2bf(kp);
           }
-          kop[c] = h8;
           *(INFINI_LDS bf16x8*)(khs + (16 * h2 + sidx) * P + 32 * c + 8 * grp) = h8;
           *(INFINI_LDS bf16x8*)(kls + (16 * h2 + sidx) * P + 32 * c + 8 * grp) = l8;
         }
         den += __shfl_xor(den, 16);
         den += __shfl_xor(den, 32);
-        // R = sigma(K) M_{s-1}: lane holds R[token 4*grp + r][col sidx]
+        // R = sigma(K) M_{s-1} = colsum(M) + K' M: lane holds (K' M)[token 4*grp + r][col sidx]
         f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
         if (has_memory) {
 #pragma unroll
@@ -269,7 +303,7 @@ void delta_chain_kernel(DeltaArgs a) {
           const int tl = 4 * grp + r;                     // token within the 16-row half
           const float den_t = __shfl(den, tl);
           const float vv = bf2f(vb[(int64_t)(32 * st + 16 * h2 + tl) * D + sidx]);
-          const float u = (has_memory && den_t > 0.f) ? vv - r4[r] / den_t : vv;
+          const float u = (has_memory && den_t > 0.f) ? vv - (csum[sidx] + r4[r]) / den_t : vv;
           uh[h2][r] = f2bf(u);
           ul[h2][r] = lo_part(u, uh[h2][r]);
         }
@@ -346,8 +380,7 @@ hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream) {
-  const int per_head = (D * D + D + kThreads - 1) / kThreads;
-  const int64_t blocks = (int64_t)a.BH * per_head;
+  const int64_t blocks = (int64_t)a.BH * (D * D / kThreads + 1);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(lin_scan_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

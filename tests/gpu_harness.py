@@ -121,9 +121,10 @@ def compare_full(w, rule, out, eng, res, label=""):
     return worst, eM, ez
 
 
-def oracle_walk(w: syn.Workload, rule: str, b: int, h: int, sample_segments, beta=None):
+def oracle_walk(w: syn.Workload, rule: str, b: int, h: int, sample_segments, beta=None, parts=None):
     """Memory-only walk of one head through all segments; at each sampled segment
-    the full oracle segment output is produced.  Returns ({s: A_s}, M_S, z_S)."""
+    the full oracle segment output is produced.  Returns ({s: A_s}, M_S, z_S);
+    with ``parts`` (a dict) also fills parts[s] = (A_dot, A_mem)."""
     N, dk, dv = w.segment_len, w.d_key, w.d_value
     M = np.zeros((dk, dv))
     z = np.zeros(dk)
@@ -136,8 +137,10 @@ def oracle_walk(w: syn.Workload, rule: str, b: int, h: int, sample_segments, bet
         v = syn.tile(w, syn.V_ID, b, h, s).astype(np.float64)
         if s in samples:
             q = syn.tile(w, syn.Q_ID, b, h, s).astype(np.float64)
-            a, M2, z2, _, _ = ref.segment_forward(q, k, v, M, z, bt, rule, s == 0, sc)
+            a, M2, z2, a_dot, a_mem = ref.segment_forward(q, k, v, M, z, bt, rule, s == 0, sc)
             want[s] = a
+            if parts is not None:
+                parts[s] = (a_dot, a_mem)
             M, z = M2, z2
         else:
             M, z = ref.memory_update(k, v, M, z, rule, s == 0)

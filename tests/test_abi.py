@@ -77,10 +77,10 @@ def test_init_state_rejects_null_and_inf():
 def test_workspace_bytes():
     st = _state(rule=ia.RULE_LINEAR)
     S, D, BH = 16, 128, 2
-    want = BH * S * D * D * 2 + BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4
+    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4
     assert ia.workspace_bytes(st, S * 2048) == want
     st = _state(rule=ia.RULE_DELTA)
-    assert ia.workspace_bytes(st, S * 2048) == BH * S * D * D * 2 + BH * S * D * 4
+    assert ia.workspace_bytes(st, S * 2048) == BH * S * D * D * 2 + 2 * BH * S * D * 4
     assert ia.workspace_bytes(st, 2047) == 0
     assert ia.workspace_bytes(st, 0) == 0
     assert ia.workspace_bytes(_state(batch=0), 2048) == 0
