@@ -33,99 +33,121 @@ __device__ __forceinline__ bf16 lo_part(float x, bf16 hi) { return f2bf(x - bf2f
 }  // namespace
 
 // =================================================================== linear
-// One workgroup per (b, h, s).  64-token tiles are staged in LDS as sigma(K)_hi,
-// sigma(K)_lo and V (row-major); the contraction over tokens reads both operands
-// transposed with ds_read_b64_tr_b16.  Output C^T[d_value][d_key] on
-// v_mfma_f32_32x32x16_bf16.
+// One workgroup per (b, h, s, 32-column block of d_key).  sigma(K) of the block
+// is computed once per element (split into bf16 hi + lo) and staged in LDS with
+// V (row-major); the contraction over tokens reads both operands transposed with
+// ds_read_b64_tr_b16.  Output C^T[d_value][d_key block] on
+// v_mfma_f32_32x32x16_bf16, plus c[d_key block] = sum_t sigma(K_t).  The next
+// 64-token tile is prefetched into registers while the current one is used.
 template <int D>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kThreads, 2)
 void lin_contrib_kernel(LinContribArgs a) {
-  constexpr int P = D + 16;
-  constexpr int TPR = D / 8, RPP = kThreads / TPR, PASSES = 64 / RPP;
-  constexpr int NBLK = (D / 32) * (D / 32);
-  constexpr int BPW = (NBLK + 3) / 4;  // output blocks per wave
-  __shared__ __attribute__((aligned(16))) bf16 khi[64 * P];
-  __shared__ __attribute__((aligned(16))) bf16 klo[64 * P];
-  __shared__ __attribute__((aligned(16))) bf16 vt[64 * P];
-  __shared__ float zred[RPP][D];
+  constexpr int KB = 32;               // d_key columns per workgroup
+  constexpr int NKB = D / KB;
+  constexpr int KP = KB + 16;          // sigma(K) tile pitch: 4 rows x 32 B of a tr16 group on distinct banks
+  constexpr int VP = D + 16;           // V tile pitch
+  constexpr int VCH = D / 8;           // 16-byte chunks per V row
+  constexpr int VPT = 64 * VCH / kThreads;
+  constexpr int NDVB = D / 32;         // 32-row blocks of d_value = output blocks
+  constexpr int WPB = 4 / NDVB;        // waves sharing one output block (token-interleaved)
+  __shared__ __attribute__((aligned(16))) bf16 khi[64 * KP];
+  __shared__ __attribute__((aligned(16))) bf16 klo[64 * KP];
+  __shared__ __attribute__((aligned(16))) bf16 vt[64 * VP];
+  __shared__ float zred[64][KB + 1];
 
-  const int sh = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int sh = blk / NKB, dkb = blk % NKB;
   const int bh = sh / a.S, s = sh % a.S;
   const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const bf16* __restrict__ kb = a.k + tok0 * D;
+  const bf16* __restrict__ kb = a.k + tok0 * D + dkb * KB;
   const bf16* __restrict__ vb = a.v + tok0 * D;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int hi = lane >> 5, grp = lane >> 4, sidx = lane & 15, l32 = lane & 31;
-  const int col = (t % TPR) * 8;
+  const int krow = t >> 2, kch = t & 3;            // this thread's 16-byte chunk of the K block
+  const int dvb = wave % NDVB, part = wave / NDVB;
 
+  bf16x8 kx = *reinterpret_cast<const bf16x8*>(kb + (int64_t)krow * D + kch * 8);
+  u32x4 vx[VPT];
+#pragma unroll
+  for (int p = 0; p < VPT; ++p) {
+    const int c = t + kThreads * p;
+    vx[p] = *reinterpret_cast<const u32x4*>(vb + (int64_t)(c / VCH) * D + (c % VCH) * 8);
+  }
   float zp[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) zp[i] = 0.f;
-  f32x16 acc[BPW];
+  f32x16 acc;
 #pragma unroll
-  for (int j = 0; j < BPW; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
   for (int t0 = 0; t0 < a.N; t0 += 64) {
+    bf16x8 h8, l8;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = t / TPR + p * RPP;
-      const bf16x8 kx = *reinterpret_cast<const bf16x8*>(kb + (int64_t)(t0 + row) * D + col);
-      const u32x4 vx = *reinterpret_cast<const u32x4*>(vb + (int64_t)(t0 + row) * D + col);
-      bf16x8 h8, l8;
+    for (int i = 0; i < 8; ++i) {
+      const float f = elu1(bf2f(kx[i]));
+      zp[i] += f;
+      h8[i] = f2bf(f);
+      l8[i] = lo_part(f, h8[i]);
+    }
+    *(INFINI_LDS bf16x8*)(khi + krow * KP + kch * 8) = h8;
+    *(INFINI_LDS bf16x8*)(klo + krow * KP + kch * 8) = l8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float f = elu1(bf2f(kx[i]));
-        zp[i] += f;
-        h8[i] = f2bf(f);
-        l8[i] = lo_part(f, h8[i]);
+    for (int p = 0; p < VPT; ++p) {
+      const int c = t + kThreads * p;
+      *(INFINI_LDS u32x4*)(vt + (c / VCH) * VP + (c % VCH) * 8) = vx[p];
+    }
+    if (t0 + 64 < a.N) {
+      kx = *reinterpret_cast<const bf16x8*>(kb + (int64_t)(t0 + 64 + krow) * D + kch * 8);
+#pragma unroll
+      for (int p = 0; p < VPT; ++p) {
+        const int c = t + kThreads * p;
+        vx[p] = *reinterpret_cast<const u32x4*>(vb + (int64_t)(t0 + 64 + c / VCH) * D + (c % VCH) * 8);
       }
-      *(INFINI_LDS bf16x8*)(khi + row * P + col) = h8;
-      *(INFINI_LDS bf16x8*)(klo + row * P + col) = l8;
-      *(INFINI_LDS u32x4*)(vt + row * P + col) = vx;
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-      const int blk = wave * BPW + j;
-      if (blk < NBLK) {
-        const int dvb = blk / (D / 32), dkb = blk % (D / 32);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int ra = 16 * ks + 8 * hi;
-          const bf16x8 va = lds_operand_tr(vt, P, ra, ra + 4, 32 * dvb + 16 * (grp & 1), sidx);
-          const bf16x8 bh8 = lds_operand_tr(khi, P, ra, ra + 4, 32 * dkb + 16 * (grp & 1), sidx);
-          const bf16x8 bl8 = lds_operand_tr(klo, P, ra, ra + 4, 32 * dkb + 16 * (grp & 1), sidx);
-          acc[j] = mfma32(va, bh8, acc[j]);
-          acc[j] = mfma32(va, bl8, acc[j]);
-        }
-      }
+    for (int ks = part; ks < 4; ks += WPB) {
+      const int ra = 16 * ks + 8 * hi;
+      const bf16x8 va = lds_operand_tr(vt, VP, ra, ra + 4, 32 * dvb + 16 * (grp & 1), sidx);
+      const bf16x8 bh8 = lds_operand_tr(khi, KP, ra, ra + 4, 16 * (grp & 1), sidx);
+      const bf16x8 bl8 = lds_operand_tr(klo, KP, ra, ra + 4, 16 * (grp & 1), sidx);
+      acc = mfma32(va, bh8, acc);
+      acc = mfma32(va, bl8, acc);
     }
     __syncthreads();
   }
 
+  // token-interleaved partials of one block are summed in wave order (D = 64)
+  float* red = reinterpret_cast<float*>(vt);
+  if (WPB > 1) {
+    if (part > 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((part - 1) * NDVB + dvb) * 1024 + r * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (part == 0) {
+#pragma unroll
+      for (int w = 1; w < WPB; ++w)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += red[((w - 1) * NDVB + dvb) * 1024 + r * 64 + lane];
+    }
+  }
   float* __restrict__ cm = a.cM + (int64_t)sh * D * D;
+  if (part == 0) {
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    const int blk = wave * BPW + j;
-    if (blk < NBLK) {
-      const int dvb = blk / (D / 32), dkb = blk % (D / 32);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dv = 32 * dvb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        cm[dv * D + 32 * dkb + l32] = acc[j][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int dv = 32 * dvb + 8 * (r >> 2) + 4 * hi + (r & 3);
+      cm[dv * D + dkb * KB + l32] = acc[r];
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) zred[t / TPR][col + i] = zp[i];
+  for (int i = 0; i < 8; ++i) zred[krow][kch * 8 + i] = zp[i];
   __syncthreads();
-  for (int c = t; c < D; c += kThreads) {
+  if (t < KB) {
     float sum = 0.f;
-    for (int r = 0; r < RPP; ++r) sum += zred[r][c];
-    a.cz[(int64_t)sh * D + c] = sum;
+    for (int r = 0; r < 64; ++r) sum += zred[r][t];
+    a.cz[(int64_t)sh * D + dkb * KB + t] = sum;
   }
 }
 
@@ -372,7 +394,7 @@ void delta_chain_kernel(DeltaArgs a) {
 // ------------------------------------------------------------------ launchers
 template <int D>
 hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.B * a.H * a.S;
+  const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / 32);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
