@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--rule", default=None)
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="budget of the oracle leg (0 disables it)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (3 launches), to calibrate "
+                        "the HBM byte counters of a profiler against a known size")
     return p.parse_args()
 
 
@@ -162,6 +165,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n * 4, "write": n * 4}, "launches": 3}))
+        return
 
     from compressive_memory_transformer_amd import infini as ia
     from compressive_memory_transformer_amd import synthetic as syn

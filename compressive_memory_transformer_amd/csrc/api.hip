@@ -152,7 +152,7 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
   }
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,
-                   snapM, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, (N + 127) / 128,
+                   snapM, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, 0,
                    st->segments_done, (float)((double)st->scale * 1.4426950408889634)};
   if ((e = infini::launch_fa_fwd<D>(f, stream)) != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return record(events, 2, stream);
@@ -276,7 +276,7 @@ static int forward_impl(infini_attn_state* st, const void* q, const void* k, con
       overlaps(workspace, w.total, st->z, z_bytes))
     return fail(INFINI_EWORKSPACE, "workspace must not alias out or the state");
   if (st->dtype == INFINI_BF16) {
-    const int64_t fa_blocks = BH * S64 * (((st->segment_len + 127) / 128 + 1) / 2);
+    const int64_t fa_blocks = infini::fa_fwd_blocks(BH * S64, st->segment_len);
     if (fa_blocks > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
   }
 

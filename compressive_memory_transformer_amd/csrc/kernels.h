@@ -22,11 +22,13 @@ struct FaArgs {
   bf16* out;
   int B, H, S, N;
   int64_t L;
-  int nq;                // ceil(N / 128) query tiles per segment
+  int nq;                // query tiles per segment (set by the launcher)
   int64_t seg_base;      // segments folded into the state before this call
   float sc_log2;         // softmax scale * log2(e)
 };
 template <int D> hipError_t launch_fa_fwd(const FaArgs& a, hipStream_t stream);
+// Workgroups of one fused-kernel launch over seg_heads (b, h, segment) tiles.
+int64_t fa_fwd_blocks(int64_t seg_heads, int N);
 
 // Linear rule, phase 1: per-segment contributions C_s^T = V^T sigma(K) (fp32, row =
 // d_value) and c_s = sum_t sigma(K_t).
