@@ -7,22 +7,37 @@
 // section 3.3; the gate of section 3.5.  The N x N score matrix never leaves
 // registers (chapter-24 page, section 24.1.2).
 //
-// Work decomposition.  One workgroup = 4 waves = one pair of 128-row query tiles
-// of one (b, h, segment): tile w and tile NQ-1-w, so every workgroup does the
-// same amount of causal work.  Each wave owns 32 query rows.  Per 64-key tile:
-//   S^T (64 keys x 32 queries) = K Q^T on v_mfma_f32_32x32x16_bf16, so that each
-//   lane holds one query column and the softmax row statistics are per lane (one
-//   cross-lane exchange with lane l^32 for the other half of the keys);
-//   O^T (D x 32) += V^T P^T, with V^T read from the row-major V tile in LDS by
+// Work decomposition.  One workgroup (4 waves, one per SIMD, one workgroup per
+// CU) handles a pair of 256-row query tiles of one (b, h, segment): tile w and
+// tile NQ-1-w, so that every workgroup does the same causal work.  Each wave
+// owns two 32-row query blocks of a tile, rows 32 w + [0, 32) and 128 + 32 w +
+// [0, 32), so every K or V operand read from LDS feeds two MFMAs.  Per 32-key
+// block of a 128-key tile:
+//   S^T (32 keys x 32 queries) = K Q^T on v_mfma_f32_32x32x16_bf16 for both query
+//   blocks: each lane holds one query column, so the softmax statistics are per
+//   lane (one exchange with lane l^32 holds the rest of a row);
+//   O^T (D x 32) += V^T P^T, with V^T read from the row-major V tile by
 //   ds_read_b64_tr_b16 and P^T taken straight from the S^T accumulators (the key
 //   order inside each 16-key step is permuted identically on both operands).
-// K and V tiles stream from HBM straight into LDS (buffer_load ... lds, 16 bytes
-// per lane, no staging registers) through two distinct LDS tiles (ping-pong):
-// the load of tile t+1 is in flight while tile t is used.  The tiles use an
-// XOR-swizzled layout whose operand reads are free of bank conflicts.  The
-// softmax keeps a reference maximum per
-// query and rescales the accumulator only when a new score exceeds it by more
-// than 2^8 (exact: the final division uses the same reference maximum).
+// The S^T products of block j+1 are issued next to the softmax of block j.
+//
+// Data movement.  K and V tiles stream from HBM into LDS with buffer_load ... lds
+// (16 bytes per lane, no staging registers) through two LDS slots.  The load
+// sequence of a workgroup is: tiles of the first query tile, the memory snapshot
+// (M^T, z, colsum(M)), tiles of the second query tile, the snapshot again.  Item
+// i+1 is in flight while item i is used; every query tile covers an even number
+// of key-tile steps, so each item's slot is known at compile time (the loop is
+// unrolled by two) and the compiler never waits on a load into the other slot.
+// The slot layouts are XOR-swizzled so that the operand reads are free of bank
+// conflicts.
+//
+// Softmax.  Each query keeps a reference maximum m, set before the tile loop to
+// the exact maximum of its first 32-key block (which always holds an unmasked
+// key); probabilities are exp2(s * scale * log2 e - m) and are never rescaled.
+// The result is exact for any m; m only has to keep the sums finite.  A block
+// whose probabilities sum past 2^64 (or to inf or NaN) raises a flag, and a
+// flagged query block is recomputed after the loop by a slow two-sweep path
+// (exact row maximum first) that reads K and V straight from memory.
 //
 // Epilogue: with sigma(q) = 1 + q', q' = sigma(q) - 1,
 //   sigma(q) M = colsum(M) + q' M   and   sigma(q) z = sum(z) + q' z,
@@ -37,26 +52,27 @@ namespace infini {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;   // query rows per tile
-constexpr int kBN = 64;            // keys per LDS tile
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 2;         // LDS ring depth (the tile in use + the one in flight)
-constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr int kBM = 64 * kWaves;   // query rows per tile: two 32-row blocks per wave
+constexpr int kBN = 128;           // keys per LDS tile
+constexpr int kKB = kBN / 32;      // 32-key blocks per tile
+constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
 
 template <int D>
 struct FaLayout {
   static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
   static constexpr int TILE_ELEMS = kBN * D;           // one K or V tile, unpadded
   static constexpr int ROWS_PER_INSTR = 64 * 8 / D;    // rows one wave-wide 16-byte load covers
-  static constexpr int INSTR_PER_WAVE = kBN / ROWS_PER_INSTR / kWaves;  // per 64-row tile and tensor
-  static_assert(INSTR_PER_WAVE >= 1, "tile too small for the wave count");
-  static_assert(D <= 2 * kBN, "the snapshot of M^T must fit the two K buffers");
+  static constexpr int NI = kBN / ROWS_PER_INSTR / kWaves;  // loads per wave, tensor and tile
+  static_assert(NI >= 1 && NI % kKB == 0, "tile loads must split evenly over the 32-key blocks");
+  static_assert(D <= kBN, "the snapshot of M^T must fit a K slot");
+  static_assert(D <= 256, "z and colsum must fit their LDS array");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r (an XOR, so the same map
 // takes physical to logical).  An LDS read of 16 bytes per lane is served 16
-// lanes at a time and a 32-row transposing read 32 lanes at a time; each group
-// must touch 16 distinct 16-byte bank groups of the 256-byte bank line.
+// lanes at a time and a transposing read 32 lanes at a time; each group must
+// touch 16 distinct 16-byte bank groups of the 256-byte bank line.
 //   K: lanes 0-15 of an operand read read the same logical chunk of 16
 //   consecutive rows: XOR with r % 16 (D = 128, one row per bank line) or with
 //   (r / 2) % 8 (D = 64, two rows per bank line).
@@ -70,10 +86,9 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ k_swz<D>(r); }
 template <int D>
 __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ (D == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2); }
 
-// Issue this wave's share of the direct-to-LDS loads of a row-major [rows x D]
+// Issue this wave's share of the direct-to-LDS loads of a row-major [kBN x D]
 // tile: wave-wide instruction `ins` fills bytes [1024 ins, 1024 ins + 1024) of the
-// LDS tile, lane l landing at 16 l (row ROWS_PER_INSTR * ins + l / CHUNKS).  The
-// global address is a uniform base plus a 32-bit per-lane element offset.
+// LDS tile, lane l landing at 16 l (row ROWS_PER_INSTR * ins + l / CHUNKS).
 template <int D, bool IS_V>
 __device__ __forceinline__ int tile_lane_offset(int ins, int lane) {
   using L = FaLayout<D>;
@@ -85,47 +100,91 @@ __device__ __forceinline__ int tile_lane_offset(int ins, int lane) {
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer, no stride); reads past
 // the end return zeros instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// buffer_load_dwordx4 ... lds: uniform descriptor + 32-bit per-lane offset; the
-// tile's position in the buffer goes into the scalar offset.  The per-lane
-// offsets are recomputed at each issue (a few integer ops) rather than kept in
-// registers across the tile loop: the lane id passes through an empty asm so the
-// arithmetic is not hoisted.
-template <int D, bool IS_V, int NI>
-__device__ __forceinline__ void issue_tile(const bf16* base, uint32_t bytes, int soff_bytes, bf16* lds_tile,
-                                           int wave) {
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, bytes);
-  // the LDS destination (M0) is wave-uniform: derive it in scalar registers
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  int lane = threadIdx.x & 63;
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "+v"(lane));  // device pass only: "v" is a gfx register class
+// The arguments are wave-uniform; readfirstlane states it, so the descriptor
+// lives in scalar registers (a descriptor in vector registers makes the
+// compiler wrap each load in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
 #endif
+
+// Per-lane byte offsets of the direct-to-LDS loads.  Wave-wide instruction ins
+// of a [kBN x D] tile fills bytes [1024 ins, 1024 ins + 1024) of the LDS tile;
+// the K swizzle repeats every 4 instructions and the V swizzle does not depend
+// on the instruction, so lane l's global offset is k[ins % 4] + 1024 (ins - ins
+// % 4) for K and v + 1024 ins for V (same row pitch in HBM and LDS).
+template <int D>
+struct DmaOfs {
+  int k[4];
+  int v;
+  __device__ __forceinline__ void init(int lane) {
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (INFINI_LDS void*)(lds_tile + (wv * NI + j) * 512), 16,
-                                             2 * tile_lane_offset<D, IS_V>(wv * NI + j, lane), soff_bytes, 0, 0);
+    for (int i = 0; i < 4; ++i) k[i] = 2 * tile_lane_offset<D, false>(i, lane);
+    v = 2 * tile_lane_offset<D, true>(0, lane);
+  }
+};
+
+// buffer_load_dwordx4 ... lds: uniform descriptor (base = the tile's first
+// element, num_records = bytes left in the tensor range) + 32-bit per-lane
+// offset, which is what the bounds check compares; instructions [j0, j0 + CNT)
+// of this wave's NI.  A range of 0 bytes issues loads that
+// write zeros (used to keep the number of loads per step uniform).
+template <int D, bool IS_V, int CNT>
+__device__ __forceinline__ void issue_part(int j0, const bf16* base, uint32_t bytes, bf16* lds_tile, int wave,
+                                           const DmaOfs<D>& dof) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist in the device pass only
+  constexpr int NI = FaLayout<D>::NI;
+  static_assert(NI % 4 == 0, "K swizzle period");
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, bytes);
+  // the LDS destination (M0) and the instruction's share of the offset are
+  // wave-uniform: derive them in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int jj = 0; jj < CNT; ++jj) {
+    const int j = j0 + jj;
+    const int ins = wv * NI + j;
+    const int voff = IS_V ? dof.v + 1024 * ins : dof.k[j & 3] + 1024 * (ins - (j & 3));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (INFINI_LDS void*)(lds_tile + ins * 512), 16, voff, 0, 0, 0);
+  }
+#endif
+}
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile(const bf16* base, uint32_t bytes, bf16* lds_tile, int wave,
+                                           const DmaOfs<D>& dof) {
+  issue_part<D, IS_V, FaLayout<D>::NI>(0, base, bytes, lds_tile, wave, dof);
 }
 
+// One wave-wide 16-byte-per-lane load of `bytes` (<= 1024) contiguous bytes into LDS.
+__device__ __forceinline__ void issue_row(const void* base, uint32_t bytes, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, bytes);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (INFINI_LDS void*)lds, 16, 16 * (int)(threadIdx.x & 63), 0, 0, 0);
+#endif
+}
+
+// Waits until this wave's outstanding loads (LDS-bound and register-bound) have
+// landed, then synchronises the workgroup.
 __device__ __forceinline__ void wait_loads_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-bound loads have landed
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
 }
 
 }  // namespace
 
 // Per-lane LDS element offsets, relative to a tile's base, of the MFMA operand
-// reads of attend_tile; they do not depend on the tile or stage, so the tile
-// loop needs only these registers plus immediate offsets.
-//   K: logical chunk 2c + hi of row 32 b2 + l32, c = 4m + j, sits at physical
+// reads; they do not depend on the tile or slot, so the tile loop needs only
+// these registers plus immediate offsets.
+//   K: logical chunk 2c + hi of row 32 j + l32, c = 4m + i, sits at physical
 //   chunk (2c + hi) ^ w, w = k_swz(l32) (row steps of 32 keep w): element offset
-//   k[j] + m * kd + 32 b2 D, where k[j] covers m = 0 and kd = +-64 flips bit 3
+//   k[i] + m * kd + 32 j D, where k[i] covers m = 0 and kd = +-64 flips bit 3
 //   of the chunk for m = 1 (D = 128 only).
-//   V^T (tr16 reads): rows 32 b2 + 16 hf + 4 hi + sidx / 4 (+ 8), column 32 db + ...,
-//   element offset v[db] + (32 b2 + 16 hf) D (+ 8 D); those row steps keep the
+//   V^T (tr16 reads): rows 32 j + 16 hf + 4 hi + sidx / 4 (+ 8), column 32 db + ...,
+//   element offset v[db] + (32 j + 16 hf) D (+ 8 D); those row steps keep the
 //   swizzle unchanged.
 template <int D>
 struct LdsAddr {
@@ -136,7 +195,7 @@ struct LdsAddr {
     const int l32 = lane & 31, hi = lane >> 5, grp = lane >> 4, sidx = lane & 15;
     const int w = k_swz<D>(l32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k[j] = l32 * D + 8 * ((2 * j + hi) ^ w);
+    for (int i = 0; i < 4; ++i) k[i] = l32 * D + 8 * ((2 * i + hi) ^ w);
     kd = (w & 8) ? -64 : 64;
     const int rowA = 4 * hi + (sidx >> 2);
 #pragma unroll
@@ -149,71 +208,81 @@ struct LdsAddr {
   __device__ __forceinline__ int kofs(int c) const { return c < 4 ? k[c] : k[c - 4] + kd; }
 };
 
-// Per-wave running state of one 32-row query block.
+// Running state of one 32-row query block of a wave.
 template <int D>
-struct RowState {
-  bf16x8 qreg[D / 16];   // Q^T as the B operand: lane holds Q[row][16c + 8hi .. +7]
-  f32x16 o[D / 32];      // O^T accumulator: lane holds O[row][32db + 8(r/4) + 4hi + r%4]
-  float m_run;           // reference maximum of the row (log2 domain)
-  float l_run;           // this lane's share of the softmax denominator
+struct QBlock {
+  bf16x8 q[D / 16];    // Q^T as the B operand: lane holds Q[row][16c + 8hi .. +7]
+  f32x16 o[D / 32];    // O^T accumulator: lane holds O[row][32db + 8(r/4) + 4hi + r%4]
+  float m;             // reference maximum of the row (log2 domain)
+  float l;             // this lane's share of the softmax denominator
+  bool bad;            // some block summed past the limit: recompute the block
 };
 
-// S^T for 32 keys (block b2 of the tile): K operands read four at a time.
+// The load item a step brings into the other slot: a K part and a V part, NI
+// wave-wide instructions each; empty ranges load zeros.
 template <int D>
-__device__ __forceinline__ void s_block(f32x16& acc, const bf16* __restrict__ kt_lds, int b2, const LdsAddr<D>& ad,
-                                        const bf16x8 (&qreg)[D / 16]) {
+struct Prefetch {
+  const bf16* kb;
+  const bf16* vb;
+  uint32_t kbytes, vbytes;
+  bf16* kn;
+  bf16* vn;
+  int wave;
+  const DmaOfs<D>* dof;
+  template <int CNT>
+  __device__ __forceinline__ void issue(int j0) const {
+    issue_part<D, false, CNT>(j0, kb, kbytes, kn, wave, *dof);
+    issue_part<D, true, CNT>(j0, vb, vbytes, vn, wave, *dof);
+  }
+};
+
+// S^T of one 32-key block (block j of the tile) for one or both query blocks;
+// the K operands are read once.
+template <int D, bool TWO>
+__device__ __forceinline__ void s_pair(f32x16& sa, f32x16& sb, const bf16* __restrict__ kt, int j,
+                                       const LdsAddr<D>& ad, const bf16x8 (&qa)[D / 16],
+                                       const bf16x8 (&qb)[D / 16]) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int r = 0; r < 16; ++r) {
+    sa[r] = 0.f;
+    if (TWO) sb[r] = 0.f;
+  }
+  bf16x8 ka[D / 16];
 #pragma unroll
-  for (int m = 0; m < D / 64; ++m) {
-    bf16x8 ka[4];
+  for (int c = 0; c < D / 16; ++c) ka[c] = lds_read8(kt + 32 * j * D + ad.kofs(c));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ka[j] = lds_read8(kt_lds + 32 * b2 * D + ad.kofs(4 * m + j));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma32(ka[j], qreg[4 * m + j], acc);
+  for (int c = 0; c < D / 16; ++c) {
+    sa = mfma32(ka[c], qa[c], sa);
+    if (TWO) sb = mfma32(ka[c], qb[c], sb);
   }
 }
 
-// O^T += V^T P^T for 32 keys (block b2 of the tile).
-template <int D>
-__device__ __forceinline__ void pv_block(RowState<D>& st, const bf16* __restrict__ vt_lds, int b2,
-                                         const LdsAddr<D>& ad, const bf16x8 (&pb)[2]) {
+// O^T += V^T P^T for one 32-key block (block j of the tile), one or both query
+// blocks; the V operands are read once.
+template <int D, bool TWO>
+__device__ __forceinline__ void pv_pair(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ vt, int j,
+                                        const LdsAddr<D>& ad, const bf16x8 (&pa)[2], const bf16x8 (&pb)[2]) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     bf16x8 va[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const bf16* p = vt_lds + (32 * b2 + 16 * hf) * D + ad.v[db];
+      const bf16* p = vt + (32 * j + 16 * hf) * D + ad.v[db];
       const s16x4 x = lds_read_tr16(p);
       const s16x4 y = lds_read_tr16(p + 8 * D);
       va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.o[db] = mfma32(va[db], pb[hf], st.o[db]);
+    for (int db = 0; db < D / 32; ++db) {
+      A.o[db] = mfma32(va[db], pa[hf], A.o[db]);
+      if (TWO) B.o[db] = mfma32(va[db], pb[hf], B.o[db]);
+    }
   }
-}
-
-// Softmax of one 32-key block, first part (no branches, no state change): the
-// probabilities against the current reference maximum of the row.  Returns
-// whether one of them exceeds 2^8, i.e. a score grew past the reference by more
-// than the slack (then the caller rescales).  The row maximum itself is only
-// needed in that rare case.
-__device__ __forceinline__ bool softmax_exp(const f32x16& s, float m_run, float sc, f32x16& p) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) p[r] = exp2_fast(__builtin_fmaf(s[r], sc, -m_run));
-  float pm = p[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) pm = fmaxf(pm, p[r]);
-  return pm > 256.f;  // exp2(kRescaleSlack)
 }
 
 // Causal mask of a block whose first key is kb0: keys after the lane's query get -inf.
 __device__ __forceinline__ void mask_block(f32x16& sacc, int kb0, int my_row) {
-  int lane = threadIdx.x & 63;
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "+v"(lane));  // recomputed here, not kept live across the tile loop
-#endif
-  const int hi = lane >> 5;
+  const int hi = (threadIdx.x >> 5) & 1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = kb0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -221,109 +290,500 @@ __device__ __forceinline__ void mask_block(f32x16& sacc, int kb0, int my_row) {
   }
 }
 
-// Second part: if some row's maximum grew past the slack (rare after the first
-// block of a row), move that row's reference to its new maximum (the two lanes
-// holding a row take the same decision), rescale the accumulator and recompute
-// the probabilities; then add them to the denominator and pack them to bf16.
+// Softmax of one 32 x 32 block: probabilities against the reference maximum,
+// added to the denominator and packed to bf16 as the B operand of PV.
 template <int D>
-__device__ __forceinline__ void softmax_finish(RowState<D>& st, const f32x16& s, f32x16& p, float sc, bool big,
-                                               bf16x8 (&pb)[2]) {
-  if (__any(big)) {
-    float mx = s[0];
+__device__ __forceinline__ void softmax_block(QBlock<D>& X, const f32x16& s, float sc, bf16x8 (&p)[2]) {
+  f32x16 e;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * sc;
-    const bool grow = mxs > st.m_run + kRescaleSlack;
-    const float alpha = grow ? exp2_fast(st.m_run - mxs) : 1.f;
-    st.m_run = grow ? mxs : st.m_run;
-    st.l_run *= alpha;
+  for (int r = 0; r < 16; ++r) e[r] = exp2_fast(__builtin_fmaf(s[r], sc, -X.m));
+  float t[8];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int r = 0; r < 8; ++r) t[r] = e[r] + e[r + 8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(__builtin_fmaf(s[r], sc, -st.m_run));
-  }
+  for (int r = 0; r < 4; ++r) t[r] += t[r + 4];
+  const float sum = (t[0] + t[2]) + (t[1] + t[3]);
+  X.bad |= !(sum <= kSumLimit);
+  X.l += sum;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      st.l_run += p[8 * hf + i];
-      pb[hf][i] = f2bf(p[8 * hf + i]);
+    for (int i = 0; i < 8; ++i) p[hf][i] = f2bf(e[8 * hf + i]);
+}
+
+// Row maximum (scaled, log2 domain) of a 32 x 32 score block; the two lanes
+// holding a row exchange their halves.
+__device__ __forceinline__ float block_row_max(const f32x16& s, float sc) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  return mx * sc;
+}
+
+// Operand stages of the pipelined tile: K operands of one 32-key block (all D /
+// 16 steps), V^T operands of one 32-key block (both 16-key halves).
+template <int D>
+__device__ __forceinline__ void load_k(bf16x8 (&ko)[D / 16], const bf16* __restrict__ kt, int j,
+                                       const LdsAddr<D>& ad) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) ko[c] = lds_read8(kt + 32 * j * D + ad.kofs(c));
+}
+template <int D>
+__device__ __forceinline__ void load_v(bf16x8 (&vo)[2][D / 32], const bf16* __restrict__ vt, int j,
+                                       const LdsAddr<D>& ad) {
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16* p = vt + (32 * j + 16 * hf) * D + ad.v[db];
+      const s16x4 x = lds_read_tr16(p);
+      const s16x4 y = lds_read_tr16(p + 8 * D);
+      vo[hf][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+template <int D>
+__device__ __forceinline__ void s_mfma(f32x16& sa, f32x16& sb, const bf16x8 (&ko)[D / 16],
+                                       const bf16x8 (&qa)[D / 16], const bf16x8 (&qb)[D / 16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sa[r] = sb[r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    sa = mfma32(ko[c], qa[c], sa);
+    sb = mfma32(ko[c], qb[c], sb);
+  }
+}
+template <int D>
+__device__ __forceinline__ void s_mfma1(f32x16& sb, const bf16x8 (&ko)[D / 16], const bf16x8 (&qb)[D / 16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sb[r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) sb = mfma32(ko[c], qb[c], sb);
+}
+template <int D>
+__device__ __forceinline__ void pv_mfma(f32x16 (&o)[D / 32], const bf16x8 (&vo)[2][D / 32], const bf16x8 (&p)[2]) {
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vo[hf][db], p[hf], o[db]);
+}
+
+// Scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+
+// Causal mask of a 32 x 32 score block by lane masks: element r of lane l holds
+// key 8 (r / 4) + 4 (l / 32) + r % 4 of the block for query l % 32, so the lanes
+// that mask element r on the diagonal block form a fixed 64-bit set.
+__host__ __device__ constexpr uint64_t diag_lane_mask(int r) {
+  return ((1ull << (8 * (r / 4) + r % 4)) - 1) | (((1ull << (8 * (r / 4) + r % 4 + 4)) - 1) << 32);
+}
+
+// Scores of key block kb for the query block starting at row r0 (both multiples
+// of 32, wave-uniform): unchanged left of the diagonal, causally masked on it,
+// all -inf right of it (one v_cndmask per element, lane set in scalar registers).
+__device__ __forceinline__ void mask_scores(f32x16& s, int kb, int r0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int d = __builtin_amdgcn_readfirstlane(kb - r0);
+  const float ninf = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint64_t m = d < 0 ? 0ull : (d == 0 ? diag_lane_mask(r) : ~0ull);
+    float out;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(out) : "v"(s[r]), "v"(ninf), "s"(m));
+    s[r] = out;
+  }
+#endif
+}
+
+// A 128-key tile through the software pipeline over its four 32-key blocks j:
+//   phase 1: S^T(j+1) MFMAs | softmax of query block A (VALU) | V^T operands of
+//            block j and K operands of block j+2 (LDS reads)
+//   phase 2: A's O^T update | softmax of query block B
+//   phase 3: B's O^T update
+// The sched_group_barrier list pins that interleave; each LDS read is issued
+// at least a phase before its use.  The next load item's instructions are
+// spread over the four blocks, so the CU's load path streams them while the
+// MFMAs run instead of stalling the waves at the start of the step.
+// MASK_A / MASK_B: the tile holds the diagonal of that query block (blocks
+// right of it are fully masked); WITH_A = false: query block A sees none of the
+// tile's keys and is skipped.
+template <int D, bool MASK_A, bool MASK_B, bool WITH_A>
+__device__ __forceinline__ void tile_pipe(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
+                                          const bf16* __restrict__ vt, const LdsAddr<D>& ad, float sc,
+                                          const Prefetch<D>& pf, int k0, int ra, int rb) {
+  constexpr int NIJ = FaLayout<D>::NI / kKB;   // prefetch instructions per block and tensor
+  constexpr int NQ = WITH_A ? 2 : 1;           // query blocks
+  constexpr int NS = NQ * (D / 16);            // S^T MFMAs per block
+  constexpr int NP = D / 16;                   // O^T MFMAs per block and query block
+  bf16x8 ko[D / 16];
+  bf16x8 vo[2][D / 32];
+  f32x16 sa, sb;
+  load_k<D>(ko, kt, 0, ad);
+  if (WITH_A) s_mfma<D>(sa, sb, ko, A.q, B.q);
+  else s_mfma1<D>(sb, ko, B.q);
+  load_k<D>(ko, kt, 1, ad);
+#pragma unroll
+  for (int j = 0; j < kKB; ++j) {
+    pf.template issue<NIJ>(NIJ * j);
+    load_v<D>(vo, vt, j, ad);
+    f32x16 na, nb;
+    bf16x8 pa[2], pb[2];
+    if (j + 1 < kKB) {
+      if (WITH_A) s_mfma<D>(na, nb, ko, A.q, B.q);
+      else s_mfma1<D>(nb, ko, B.q);
+    }
+    if (MASK_A) mask_scores(sa, k0 + 32 * j, ra);
+    if (MASK_B) mask_scores(sb, k0 + 32 * j, rb);
+    if (WITH_A) softmax_block<D>(A, sa, sc, pa);
+    if (j + 2 < kKB) load_k<D>(ko, kt, j + 2, ad);
+    if (WITH_A) pv_mfma<D>(A.o, vo, pa);
+    softmax_block<D>(B, sb, sc, pb);
+    pv_mfma<D>(B.o, vo, pb);
+    if (j + 1 < kKB) {
+      if (WITH_A) sa = na;
+      sb = nb;
+#pragma unroll
+      for (int i = 0; i < NS / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NS / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
+      }
+    }
+    if (WITH_A) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 2, 0);
+    }
+  }
+}
+
+// A tile that crosses the diagonal of a query block: per 32-key block, only the
+// active query blocks that see some of its keys, with the causal mask on the
+// diagonal block.  Query block rows start at ra < rb (multiples of 32); the
+// block with first key kb is needed when kb <= r.
+template <int D>
+__device__ __forceinline__ void tile_diag(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
+                                          const bf16* __restrict__ vt, const LdsAddr<D>& ad, float sc, int k0,
+                                          int ra, int rb, bool act_a, bool act_b) {
+  const int l32 = threadIdx.x & 31;
+#pragma unroll
+  for (int j = 0; j < kKB; ++j) {
+    const int kb = k0 + 32 * j;
+    const bool need_a = act_a && kb <= ra;
+    const bool need_b = act_b && kb <= rb;
+    if (!need_a && !need_b) break;  // later blocks start even further right
+    f32x16 sa, sb;
+    bf16x8 pa[2], pb[2];
+    if (need_a && need_b) {
+      s_pair<D, true>(sa, sb, kt, j, ad, A.q, B.q);
+      if (kb == ra) mask_block(sa, kb, ra + l32);
+      if (kb == rb) mask_block(sb, kb, rb + l32);
+      softmax_block<D>(A, sa, sc, pa);
+      softmax_block<D>(B, sb, sc, pb);
+      pv_pair<D, true>(A, B, vt, j, ad, pa, pb);
+    } else if (need_a) {  // query block B inactive
+      s_pair<D, false>(sa, sb, kt, j, ad, A.q, A.q);
+      if (kb == ra) mask_block(sa, kb, ra + l32);
+      softmax_block<D>(A, sa, sc, pa);
+      pv_pair<D, false>(A, A, vt, j, ad, pa, pa);
+    } else {              // block j lies right of block A's rows
+      s_pair<D, false>(sb, sa, kt, j, ad, B.q, B.q);
+      if (kb == rb) mask_block(sb, kb, rb + l32);
+      softmax_block<D>(B, sb, sc, pb);
+      pv_pair<D, false>(B, B, vt, j, ad, pb, pb);
+    }
+  }
+}
+
+// Reference maxima before the tile loop: the exact row maxima of key block 0,
+// the first block every query sees (tile 0 is in LDS).  ra < rb.
+template <int D>
+__device__ __forceinline__ void init_m(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
+                                       const LdsAddr<D>& ad, float sc, int ra, int rb, bool act_a, bool act_b) {
+  const int l32 = threadIdx.x & 31;
+  f32x16 sa, sb;
+  if (act_b) {
+    s_pair<D, true>(sa, sb, kt, 0, ad, A.q, B.q);
+    if (rb == 0) mask_block(sb, 0, l32);
+    B.m = block_row_max(sb, sc);
+  } else if (act_a) {
+    s_pair<D, false>(sa, sb, kt, 0, ad, A.q, A.q);
+  }
+  if (act_a) {
+    if (ra == 0) mask_block(sa, 0, l32);
+    A.m = block_row_max(sa, sc);
+  }
+}
+
+// Slow, exact recompute of one query block whose sums left the safe range: two
+// sweeps over its keys (row maxima, then probabilities against them, all <= 1),
+// with K and V operands loaded straight from memory (no LDS, no barriers).
+template <int D>
+__device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ kseg,
+                                const bf16* __restrict__ vseg, float sc) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  auto scores = [&](int kb) {
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kseg + (int64_t)(kb + l32) * D + 16 * c + 8 * hi);
+      s = mfma32(ka, X.q[c], s);
+    }
+    if (kb == r0) mask_block(s, kb, r0 + l32);
+    return s;
+  };
+  float m = -__builtin_inff();
+#pragma unroll 1
+  for (int kb = 0; kb <= r0; kb += 32) m = fmaxf(m, block_row_max(scores(kb), sc));
+  X.m = m;
+  X.l = 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) X.o[db][r] = 0.f;
+#pragma unroll 1
+  for (int kb = 0; kb <= r0; kb += 32) {
+    const f32x16 s = scores(kb);
+    bf16x8 p[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = exp2_fast(__builtin_fmaf(s[r], sc, -m));
+      X.l += e;
+      p[r >> 3][r & 7] = f2bf(e);
+    }
+    // V^T operand: key order of the P^T rows (see pv_pair), column d_value 32 db + l32
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        bf16x8 va;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = kb + 16 * hf + (j < 4 ? 4 * hi + j : 8 + 4 * hi + (j - 4));
+          va[j] = vseg[(int64_t)key * D + 32 * db + l32];
+        }
+        X.o[db] = mfma32(va, p[hf], X.o[db]);
+      }
+  }
+  X.bad = false;
+}
+
+// Retrieval, gate and store of one query block.  mt: M^T snapshot (K-slot
+// layout), zs / cs: z and colsum(M) in LDS.
+template <int D>
+__device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __restrict__ mt,
+                                             const float* __restrict__ zs, const float* __restrict__ cs,
+                                             const LdsAddr<D>& ad, bool has_memory, float g, bf16* __restrict__ orow) {
+  const int hi = (threadIdx.x >> 5) & 1;
+  const float l_tot = X.l + __shfl_xor(X.l, 32);
+  const float inv_l = 1.f / l_tot;
+  f32x16 am[D / 32];
+  float den = 0.f;
+  if (has_memory) {
+    // accumulator starts at colsum(M)[d_value of each element]
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 c4 = *(const INFINI_LDS f32x4*)(cs + 32 * db + 8 * j + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) am[db][4 * j + e] = c4[e];
+      }
+    float zpart = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      bf16x8 qp;
+      const f32x4 z0 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi);
+      const f32x4 z1 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi + 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = bf2f(X.q[c][i]);
+        const float f = x > 0.f ? x : exp_e(x) - 1.f;   // q' = sigma(q) - 1
+        const float zz = i < 4 ? z0[i] : z1[i - 4];
+        den = __builtin_fmaf(f, zz, den);
+        zpart += zz;
+        qp[i] = f2bf(f);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 ma = lds_read8(mt + 32 * db * D + ad.kofs(c));
+        am[db] = mfma32(ma, qp, am[db]);
+      }
+    }
+    den += zpart;                      // sum(z) over this lane's half of d_key
+    den += __shfl_xor(den, 32);
+  } else {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) am[db][r] = 0.f;
+  }
+  // lane holds query row orow, values d = 32db + 8j + 4hi + 0..3
+  const float inv_den = (has_memory && den > 0.f) ? 1.f / den : 0.f;
+  const float wg_mem = g * inv_den;
+  const float wg_dot = (1.f - g) * inv_l;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 outv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[db][4 * j + e] * wg_mem));
+      *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * hi) = outv;
     }
 }
 
-// One 64-key tile: S^T, mask, softmax and O^T update for the keys of this tile
-// that the wave's rows can see.  (The DMA of the next tile into the other pair
-// of buffers is issued just before; the buffers are distinct objects, so the
-// compiler never waits on that DMA before reading this tile.)  A tile wholly
-// below the wave's diagonal runs software-pipelined: the S^T MFMAs of the
-// second 32-key block are issued next to the softmax VALU work of the first,
-// and the PV MFMAs of the first next to the softmax of the second.
+// Per-workgroup context shared by both passes.
 template <int D>
-__device__ __forceinline__ void attend_tile(RowState<D>& st, const bf16* __restrict__ kt_lds,
-                                            const bf16* __restrict__ vt_lds, const LdsAddr<D>& ad, int k0,
-                                            int r0, int my_row, bool active, float sc) {
+struct FaCtx {
+  const bf16* qb;          // Q rows of this (b, h, segment)
+  bf16* ob;
+  const bf16* kseg;
+  const bf16* vseg;
+  const bf16* snapM;       // M^T snapshot of this (b, h, segment)
+  const float* snapz;
+  const float* snapc;
+  uint32_t seg_bytes;
+  int N, nk, wave;
+  bool has_memory;
+  float g, sc;
+};
+
+// The load item after step t of a pass with nsteps steps: tile t+1 (zeros past
+// the segment), or after the last step the snapshot of M^T (K part; the V part
+// loads zeros).
+template <int D>
+__device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int nsteps, bf16* kn, bf16* vn,
+                                                const DmaOfs<D>& dof) {
+  Prefetch<D> pf;
+  pf.kn = kn;
+  pf.vn = vn;
+  pf.wave = cx.wave;
+  pf.dof = &dof;
+  if (t + 1 < nsteps) {
+    const uint32_t off = (uint32_t)(t + 1) * kBN * D * 2;   // byte offset of tile t+1
+    const uint32_t left = off < cx.seg_bytes ? cx.seg_bytes - off : 0u;
+    pf.kb = cx.kseg + (off < cx.seg_bytes ? off / 2 : 0u);
+    pf.vb = cx.vseg + (off < cx.seg_bytes ? off / 2 : 0u);
+    pf.kbytes = pf.vbytes = left;
+  } else {
+    pf.kb = pf.vb = cx.snapM;
+    pf.kbytes = cx.has_memory ? (uint32_t)(D * D * 2) : 0u;
+    pf.vbytes = 0u;
+  }
+  return pf;
+}
+
+// One query tile (pass) of the workgroup: the tiles alternate between the slots
+// starting at slot S0; the snapshot arrives in slot S0 after the last step.  On
+// entry tile 0 is in slot S0 (waited and synchronised); with `next` set, the
+// following pass's tile 0 is issued into slot S0^1 during the epilogue.
+template <int D, int S0>
+__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, bf16* k0s, bf16* v0s, bf16* k1s,
+                                         bf16* v1s, float* zc, const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
   const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31;
   const int hi = lane >> 5;
-  if (!active || k0 > r0 + 31) return;
-  if (k0 + kBN - 1 <= r0) {
-    // full tile: no mask, pipelined
-    f32x16 s0, s1, p;
-    bf16x8 pb0[2], pb1[2];
-    s_block<D>(s0, kt_lds, 0, ad, st.qreg);
-    s_block<D>(s1, kt_lds, 1, ad, st.qreg);
-    const bool g0 = softmax_exp(s0, st.m_run, sc, p);
-    softmax_finish<D>(st, s0, p, sc, g0, pb0);
-    pv_block<D>(st, vt_lds, 0, ad, pb0);
-    const bool g1 = softmax_exp(s1, st.m_run, sc, p);
-    softmax_finish<D>(st, s1, p, sc, g1, pb1);
-    pv_block<D>(st, vt_lds, 1, ad, pb1);
-    return;
-  }
-  // tile on the diagonal: per 32-key block, masked
-#pragma unroll
-  for (int b2 = 0; b2 < 2; ++b2) {
-    const int kb0 = k0 + 32 * b2;          // first key of this 32-key block
-    if (kb0 > r0 + 31) break;              // block entirely above the diagonal
-    f32x16 sacc;
-    s_block<D>(sacc, kt_lds, b2, ad, st.qreg);
-    const bool masked = kb0 + 31 > r0;
-    if (masked) mask_block(sacc, kb0, my_row);
-    f32x16 p;
-    bf16x8 pb[2];
-    const bool g = softmax_exp(sacc, st.m_run, sc, p);
-    softmax_finish<D>(st, sacc, p, sc, g, pb);
-    pv_block<D>(st, vt_lds, b2, ad, pb);
-  }
-}
+  bf16* const kc = S0 == 0 ? k0s : k1s;      // slot S0
+  bf16* const vc = S0 == 0 ? v0s : v1s;
+  bf16* const kn = S0 == 0 ? k1s : k0s;      // slot S0^1
+  bf16* const vn = S0 == 0 ? v1s : v0s;
+  const int q0 = qt * kBM;
+  const int ra = q0 + 32 * cx.wave;          // first rows of the two query blocks
+  const int rb = ra + kBM / 2;
+  const bool act_a = ra < cx.N;
+  const bool act_b = rb < cx.N;
+  const int last = min(cx.nk - 1, (q0 + kBM - 1) / kBN);
+  const int nsteps = (last + 2) & ~1;        // even: pads with a tile beyond the segment
 
-// Waits until this wave's loads of the tile needed next have landed (the loads
-// of `later` younger tiles may stay in flight), then synchronises the workgroup.
-template <int NI>
-__device__ __forceinline__ void stage_barrier(int later) {
-  // s_waitcnt vmcnt(n) lgkmcnt(0); n = 2 * NI * later (K and V instructions per tile)
-  if (later >= 2)
-    __builtin_amdgcn_s_waitcnt((4 * NI) | 0x0070);
-  else if (later == 1)
-    __builtin_amdgcn_s_waitcnt((2 * NI) | 0x0070);
-  else
-    __builtin_amdgcn_s_waitcnt(0x0070);
-  __builtin_amdgcn_s_barrier();
+  QBlock<D> A, B;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    A.q[c] = act_a ? *reinterpret_cast<const bf16x8*>(cx.qb + (int64_t)(ra + l32) * D + 16 * c + 8 * hi) : bf16x8{};
+    B.q[c] = act_b ? *reinterpret_cast<const bf16x8*>(cx.qb + (int64_t)(rb + l32) * D + 16 * c + 8 * hi) : bf16x8{};
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      A.o[db][r] = 0.f;
+      B.o[db][r] = 0.f;
+    }
+  A.m = B.m = 0.f;
+  A.l = B.l = 0.f;
+  A.bad = B.bad = false;
+  init_m<D>(A, B, kc, ad, cx.sc, ra, rb, act_a, act_b);
+
+  // Step t uses slot S0 + (t % 2) and loads item t+1 into the other slot: tile
+  // t+1, or the snapshot after the last step (z and colsum go to zc).
+#define INFINI_FA_STEP(T, KC, VC, KN, VN)                                                        \
+  {                                                                                              \
+    const int t_ = (T);                                                                          \
+    const Prefetch<D> pf_ = next_item<D>(cx, t_, nsteps, KN, VN, dof);                           \
+    if (t_ + 1 == nsteps && cx.has_memory && cx.wave == 0) {                                     \
+      issue_row(cx.snapz, D * 4, zc);                                                            \
+      issue_row(cx.snapc, D * 4, zc + 256);                                                      \
+    }                                                                                            \
+    const int k0_ = t_ * kBN;                                                                    \
+    if (act_a && k0_ + kBN <= ra) {                                                              \
+      tile_pipe<D, false, false, true>(A, B, KC, VC, ad, cx.sc, pf_, k0_, ra, rb);               \
+    } else if (act_b && k0_ <= ra && ra < k0_ + kBN) {                                          \
+      tile_pipe<D, true, false, true>(A, B, KC, VC, ad, cx.sc, pf_, k0_, ra, rb);                \
+    } else if (act_b && ra < k0_ && k0_ <= rb && rb < k0_ + kBN) {                              \
+      tile_pipe<D, false, true, false>(A, B, KC, VC, ad, cx.sc, pf_, k0_, ra, rb);               \
+    } else {                                                                                     \
+      pf_.template issue<FaLayout<D>::NI>(0);                                                    \
+      if ((act_b && k0_ <= rb) || (act_a && k0_ <= ra))                                          \
+        tile_diag<D>(A, B, KC, VC, ad, cx.sc, k0_, ra, rb, act_a, act_b);                       \
+    }                                                                                            \
+    wait_loads_and_sync();                                                                       \
+  }
+  for (int t = 0; t < nsteps; t += 2) {
+    INFINI_FA_STEP(t, kc, vc, kn, vn)
+    INFINI_FA_STEP(t + 1, kn, vn, kc, vc)
+  }
+#undef INFINI_FA_STEP
+
+  if (act_a && __any(A.bad)) recompute_block<D>(A, ra, cx.kseg, cx.vseg, cx.sc);
+  if (act_b && __any(B.bad)) recompute_block<D>(B, rb, cx.kseg, cx.vseg, cx.sc);
+
+  // The snapshot is in slot S0; slot S0^1 is free: start the next pass's tile 0.
+  if (next) {
+    issue_tile<D, false>(cx.kseg, cx.seg_bytes, kn, cx.wave, dof);
+    issue_tile<D, true>(cx.vseg, cx.seg_bytes, vn, cx.wave, dof);
+  }
+  const float* zs = zc;
+  const float* cs = zc + 256;
+  if (act_a) finish_block<D>(A, kc, zs, cs, ad, cx.has_memory, cx.g, cx.ob + (int64_t)(ra + l32) * D);
+  if (act_b) finish_block<D>(B, kc, zs, cs, ad, cx.has_memory, cx.g, cx.ob + (int64_t)(rb + l32) * D);
+  wait_loads_and_sync();
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2)
+__global__ __launch_bounds__(kThreads, 1)
 void fa_fwd_kernel(FaArgs a) {
   using L = FaLayout<D>;
-  constexpr int NI = L::INSTR_PER_WAVE;
-  __shared__ __attribute__((aligned(1024))) bf16 ks0[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 ks1[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 vs0[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 vs1[L::TILE_ELEMS];
-  __shared__ float zsh[D];
-  __shared__ __attribute__((aligned(16))) float csh[D];
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) float zc[512];   // z at [0, D), colsum(M) at [256, 256 + D)
 
   const int npair = (a.nq + 1) / 2;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -332,153 +792,40 @@ void fa_fwd_kernel(FaArgs a) {
   const int bh = sh / a.S;
   const int s = sh % a.S;
   const int h = bh % a.H;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int rowblk = wave;
-
   const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const bf16* __restrict__ qb = a.q + tok0 * D;
-  bf16* __restrict__ ob = a.out + tok0 * D;
 
-  const bool has_memory = (a.seg_base + s) > 0;
-  const float g = sigmoid_gate(a.beta[h]);
-  const float sc = a.sc_log2;
-  const int nk = a.N / kBN;
+  FaCtx<D> cx;
+  cx.qb = a.q + tok0 * D;
+  cx.ob = a.out + tok0 * D;
+  cx.kseg = a.k + tok0 * D;
+  cx.vseg = a.v + tok0 * D;
+  cx.snapM = a.snapM + (int64_t)sh * D * D;
+  cx.snapz = a.snapz + (int64_t)sh * D;
+  cx.snapc = a.snapc + (int64_t)sh * D;
+  cx.seg_bytes = (uint32_t)a.N * D * 2;
+  cx.N = a.N;
+  cx.nk = (a.N + kBN - 1) / kBN;
+  cx.wave = threadIdx.x >> 6;
+  cx.has_memory = (a.seg_base + s) > 0;
+  cx.g = sigmoid_gate(a.beta[h]);
+  cx.sc = a.sc_log2;
 
-  const uint32_t seg_bytes = (uint32_t)a.N * D * 2;
-  const bf16* kseg = a.k + tok0 * D;
-  const bf16* vseg = a.v + tok0 * D;
-  constexpr int kTileBytes = kBN * D * 2;
   LdsAddr<D> ad;
-  ad.init(lane);
+  ad.init(threadIdx.x & 63);
 
-  for (int pass = 0; pass < 2; ++pass) {
-    const int qt = pass == 0 ? pair : a.nq - 1 - pair;
-    if (pass == 1 && qt == pair) break;
-    const int q0 = qt * kBM;
-    const int r0 = q0 + 32 * rowblk;          // first query row of this wave
-    const bool active = r0 < a.N;
-    const int my_row = r0 + l32;               // query of this lane
-    const int last = min(nk - 1, (q0 + kBM - 1) / kBN);
+  // the longer query tile first: the workgroups of one (b, h, segment) then
+  // stream the same K/V tiles at about the same time (L2 reuse)
+  const int qt0 = a.nq - 1 - pair;
+  const int qt1 = pair;
+  const bool two = qt1 != qt0;
 
-    // Q^T as the B operand (issued first: the oldest loads of this pass)
-    RowState<D> st;
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-        st.qreg[c] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)my_row * D + 16 * c + 8 * hi);
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
-    st.m_run = -__builtin_inff();
-    st.l_run = 0.f;
-
-    // prologue: tile 0 into stage 0; wait for it (and Q)
-    issue_tile<D, false, NI>(kseg, seg_bytes, 0, ks0, wave);
-    issue_tile<D, true, NI>(vseg, seg_bytes, 0, vs0, wave);
-    stage_barrier<NI>(0);
-
-    // One step: prefetch tile t+1 into the other stage, use tile t, wait for t+1.
-#define INFINI_FA_STEP(T, KC, VC, KN, VN)                                                              \
-    {                                                                                                  \
-      const int t_ = (T);                                                                              \
-      if (t_ + 1 <= last) {                                                                            \
-        issue_tile<D, false, NI>(kseg, seg_bytes, (t_ + 1) * kTileBytes, KN, wave);                     \
-        issue_tile<D, true, NI>(vseg, seg_bytes, (t_ + 1) * kTileBytes, VN, wave);                      \
-      }                                                                                                \
-      attend_tile<D>(st, KC, VC, ad, t_ * kBN, r0, my_row, active, sc);                               \
-      stage_barrier<NI>(0);                                                                            \
-    }
-    for (int kt = 0; kt <= last; kt += kStages) {
-      INFINI_FA_STEP(kt, ks0, vs0, ks1, vs1)
-      if (kt + 1 > last) break;
-      INFINI_FA_STEP(kt + 1, ks1, vs1, ks0, vs0)
-    }
-#undef INFINI_FA_STEP
-
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    const float inv_l = 1.f / l_tot;
-
-    // ---- retrieval epilogue: rows [0, 64) of the M^T snapshot go to ks0, the
-    // rest to ks1 (same layout and swizzle as a K tile)
-    f32x16 am[D / 32];
-    float den = 0.f;
-    if (has_memory) {
-      {
-        const bf16* snap = a.snapM + (int64_t)sh * D * D;
-        issue_tile<D, false, NI>(snap, kBN * D * 2, 0, ks0, wave);
-        if (D > kBN) issue_tile<D, false, NI>(snap + kBN * D, (D - kBN) * D * 2, 0, ks1, wave);
-      }
-      for (int i = threadIdx.x; i < D; i += kThreads) {
-        zsh[i] = a.snapz[(int64_t)sh * D + i];
-        csh[i] = a.snapc[(int64_t)sh * D + i];
-      }
-      wait_loads_and_sync();
-      if (active) {
-        // accumulator starts at colsum(M)[d_value of each element]
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 c4 = *(const INFINI_LDS f32x4*)(csh + 32 * db + 8 * j + 4 * hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) am[db][4 * j + e] = c4[e];
-          }
-        float zpart = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          bf16x8 qp;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float x = bf2f(st.qreg[c][i]);
-            const float f = x > 0.f ? x : exp_e(x) - 1.f;   // q' = sigma(q) - 1
-            const float zz = zsh[16 * c + 8 * hi + i];
-            den = __builtin_fmaf(f, zz, den);
-            zpart += zz;
-            qp[i] = f2bf(f);
-          }
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            // row 32 db + l32 of M^T: rows [0, 64) in ks0, [64, 128) in ks1
-            const bf16* mt = (db < 2 ? ks0 : ks1) + 32 * (db & 1) * D;
-            const bf16x8 ma = lds_read8(mt + ad.kofs(c));
-            am[db] = mfma32(ma, qp, am[db]);
-          }
-        }
-        den += zpart;                      // sum(z) over this lane's half of d_key
-        den += __shfl_xor(den, 32);
-      }
-    } else {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[db][r] = 0.f;
-    }
-
-    // ---- gate and store: lane holds query my_row, values d = 32db + 8j + 4hi + 0..3
-    if (active) {
-      const float inv_den = (has_memory && den > 0.f) ? 1.f / den : 0.f;
-      const float wg_mem = g * inv_den;
-      const float wg_dot = (1.f - g) * inv_l;
-      bf16* orow = ob + (int64_t)my_row * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 outv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            outv[e] = f2bf(__builtin_fmaf(st.o[db][4 * j + e], wg_dot, am[db][4 * j + e] * wg_mem));
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * hi) = outv;
-        }
-    }
-    __syncthreads();  // every stage (snapshot, z, colsum) is reused by the next tile pair
-  }
+  DmaOfs<D> dof;
+  dof.init(threadIdx.x & 63);
+  issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
+  issue_tile<D, true>(cx.vseg, cx.seg_bytes, v0s, cx.wave, dof);
+  wait_loads_and_sync();
+  run_pass<D, 0>(cx, qt0, two, k0s, v0s, k1s, v1s, zc, ad, dof);
+  if (two) run_pass<D, 1>(cx, qt1, false, k0s, v0s, k1s, v1s, zc, ad, dof);
 }
 
 int64_t fa_fwd_blocks(int64_t seg_heads, int N) {
