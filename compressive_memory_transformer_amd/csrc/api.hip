@@ -83,7 +83,7 @@ int check_state(const infini_attn_state* st) {
 }
 
 struct WsLayout {
-  size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, U = 0, total = 0;
+  size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, kp = 0, czp = 0, inv = 0, U = 0, total = 0;
 };
 
 // Workspace regions, each 256-byte aligned.  Returns false on overflow.
@@ -101,6 +101,13 @@ bool workspace_layout(const infini_attn_state* st, int64_t S, WsLayout* w) {
     if (st->rule == INFINI_RULE_LINEAR) {
       w->cM = off; off = align_up(off + (size_t)n * 4);
       w->cz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
+    } else {
+      int64_t tokens, parts;
+      if (!mul_ok(BH, S * (int64_t)st->segment_len, &tokens)) return false;
+      if (!mul_ok(seg_heads, (int64_t)infini::delta_parts(st->segment_len) * D, &parts)) return false;
+      w->kp = off; off = align_up(off + (size_t)tokens * D * 2);
+      w->czp = off; off = align_up(off + (size_t)parts * 4);
+      w->inv = off; off = align_up(off + (size_t)tokens * 4);
     }
   } else if (st->rule == INFINI_RULE_DELTA) {
     if (!mul_ok(BH, (int64_t)st->segment_len * st->d_value, &n)) return false;
@@ -147,8 +154,9 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
     if ((e = infini::launch_lin_scan<D>(sarg, stream)) != hipSuccess) return hip_fail(e, "lin_scan launch");
   } else {
     infini::DeltaArgs d{static_cast<const bf16*>(k), static_cast<const bf16*>(v), st->M, st->z, snapM, snapz,
-                        snapc, B * H, S, N, L, st->segments_done};
-    if ((e = infini::launch_delta_chain<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta_chain launch");
+                        snapc, reinterpret_cast<bf16*>(ws + w.kp), reinterpret_cast<float*>(ws + w.czp),
+                        reinterpret_cast<float*>(ws + w.inv), B * H, S, N, L, st->segments_done, 0};
+    if ((e = infini::launch_delta_state<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta state launch");
   }
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,

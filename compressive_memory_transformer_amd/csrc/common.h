@@ -74,6 +74,13 @@ __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : exp_e(x); }
 
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+// A bf16 held as the raw 16 bits of a short (e.g. an element of a transposing
+// LDS read) widened to fp32 by placing the bits in the upper half.  (A
+// __builtin_bit_cast of a vector element to __bf16 has compiled to the wrong
+// element here.)
+__device__ __forceinline__ float bf16_bits_to_f32(short b) {
+  return __builtin_bit_cast(float, (unsigned)(unsigned short)b << 16);
+}
 __device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }  // round to nearest even
 
 // sigmoid(beta) with exact limits: beta = +inf -> 1, beta = -inf -> 0.

@@ -56,8 +56,10 @@ struct LinScanArgs {
 };
 template <int D> hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream);
 
-// Delta rule: persistent chain over the S segments of each head; each workgroup
-// owns 16 columns (d_value) of M.  Emits the snapshots and updates the state.
+// Delta rule: a parallel pre-pass over K (k' = sigma(K) - 1 in bf16, the z
+// snapshots and 1/den per token), then the chain over the S segments of each
+// head, one workgroup per 16 columns of M.  Emits the snapshots and updates the
+// state.
 struct DeltaArgs {
   const bf16* k;
   const bf16* v;
@@ -66,11 +68,17 @@ struct DeltaArgs {
   bf16* snapM;           // [B*H*S][D][D] (row = d_value)
   float* snapz;          // [B*H*S][D]
   float* snapc;          // [B*H*S][D]
+  bf16* kp;              // workspace [B*H][L][D]: sigma(K) - 1
+  float* czp;            // workspace [B*H*S][nparts][D]: column sums of sigma(K) per 256 tokens
+  float* inv_den;        // workspace [B*H][L]
   int BH, S, N;
   int64_t L;
   int64_t seg_base;
+  int nparts;            // 256-token parts per segment (set by the launcher)
 };
-template <int D> hipError_t launch_delta_chain(const DeltaArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream);
+// 256-token parts per segment of the pre-pass (size of czp).
+int delta_parts(int N);
 
 // ------------------------------------------------------------------ fp32 path
 // One segment per launch; M and z are read as M_{s-1}, z_{s-1}.

@@ -1,19 +1,16 @@
-// Compressive-memory state kernels of the bf16 path (page "精读笔记：Infini-attention",
-// section 3.4; delta fraction as written in section 2.1 of the CSDN page).
+// Linear-rule memory state of the bf16 path (page "精读笔记：Infini-attention",
+// section 3.4, linear rule; z as in section 3.3):
 //
-//   linear: M_s = M_{s-1} + sigma(K)^T V, z_s = z_{s-1} + sum_t sigma(K_t)
-//   delta : M_s = M_{s-1} + sigma(K)^T (V - sigma(K) M_{s-1} / (sigma(K) z_{s-1}))
+//   M_s = M_{s-1} + sigma(K)^T V,   z_s = z_{s-1} + sum_t sigma(K_t)
 //
-// Both leave a snapshot of (M_{s-1}^T in bf16, z_{s-1} in fp32) per segment for
-// the fused attention kernel and the final (M_S, z_S) in the fp32 state.
+// It leaves a snapshot of (M_{s-1}^T in bf16, z_{s-1} and colsum(M_{s-1}) in
+// fp32) per segment for the fused attention kernel and the final (M_S, z_S) in
+// the fp32 state.  The delta rule lives in state_delta.hip.
 //
 // Precision.  sigma(K) = 1 + k for the small keys of these workloads, so rounding
-// sigma(K) to bf16 keeps only a few bits of k.  Every GEMM whose result is
-// accumulated into M therefore splits its fp32 operands into bf16 hi + lo parts
-// (x = hi + lo to about 16 bits) and sums the hi*hi, hi*lo and lo*hi products in
-// fp32: sigma(K) in the linear contributions (V is exact in bf16), sigma(K) and
-// the residual U = V - R in the delta update.  The delta read-back R and the
-// retrieval use single bf16 operands, whose error does not accumulate.
+// sigma(K) to bf16 keeps only a few bits of k.  The contribution GEMM therefore
+// splits sigma(K) into bf16 hi + lo parts (x = hi + lo to about 16 bits) and sums
+// the hi*V and lo*V products in fp32 (V is exact in bf16).
 #include "common.h"
 #include "kernels.h"
 
@@ -21,12 +18,6 @@ namespace infini {
 
 namespace {
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ bf16 lo_part(float x, bf16 hi) { return f2bf(x - bf2f(hi)); }
@@ -196,201 +187,6 @@ void lin_scan_kernel(LinScanArgs a) {
   a.M[(int64_t)bh * D * D + dk * D + dv] = run;
 }
 
-// ==================================================================== delta
-// One workgroup per (b, h, 16-column block of M); the chain over segments runs
-// inside the kernel with the fp32 block of M^T and z resident in LDS.  The
-// columns of M are independent under the delta rule (column j of the read-back
-// needs only column j of M; z is shared and depends on K alone), so the blocks
-// of a head never communicate.  Each of the 4 waves takes every 4th 32-token
-// sub-tile of the segment; the per-wave partial updates are summed in a fixed
-// order at the end of the segment (deterministic).
-template <int D>
-__global__ __launch_bounds__(kThreads)
-void delta_chain_kernel(DeltaArgs a) {
-  constexpr int CB = 16;              // columns per workgroup
-  constexpr int NCB = D / CB;
-  constexpr int P = D + 16;           // staging pitch (elements)
-  constexpr int STAGE = 32 * P;       // one 32-token sigma(K) tile
-  __shared__ float mt[CB][D];         // M^T block (row = column of M), fp32
-  __shared__ float zs[D];
-  __shared__ float zred[4][D];
-  __shared__ float csum[CB];          // column sums of the M block over d_key (fp32)
-  __shared__ __attribute__((aligned(16))) bf16 stage[4][2][STAGE];  // per wave: hi, lo
-
-  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int bh = blk / NCB, cb = blk % NCB;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int grp = lane >> 4, sidx = lane & 15;
-
-  float* __restrict__ Mg = a.M + (int64_t)bh * D * D;
-  float* __restrict__ zg = a.z + (int64_t)bh * D;
-  for (int i = t; i < CB * D; i += kThreads) {
-    const int j = i / D, dk = i % D;
-    mt[j][dk] = Mg[dk * D + cb * CB + j];
-  }
-  for (int i = t; i < D; i += kThreads) zs[i] = zg[i];
-  __syncthreads();
-
-  bf16* khs = stage[wave][0];
-  bf16* kls = stage[wave][1];
-  float* red = reinterpret_cast<float*>(&stage[0][0][0]);  // [4][CB][D] after the token loop
-  static_assert(4 * CB * D * sizeof(float) <= sizeof(stage), "reduction buffer too small");
-
-  for (int s = 0; s < a.S; ++s) {
-    const int64_t sh = (int64_t)bh * a.S + s;
-    const bool has_memory = (a.seg_base + s) > 0;
-    // ---- snapshot of M_{s-1}^T (this block's rows) and z_{s-1}
-    for (int i = t; i < CB * D / 8; i += kThreads) {
-      const int j = i / (D / 8), c8 = (i % (D / 8)) * 8;
-      bf16x8 w8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w8[e] = f2bf(mt[j][c8 + e]);
-      *reinterpret_cast<bf16x8*>(a.snapM + sh * D * D + (int64_t)(cb * CB + j) * D + c8) = w8;
-    }
-    if (cb == 0)
-      for (int i = t; i < D; i += kThreads) a.snapz[sh * D + i] = zs[i];
-    {
-      // column sums: 16 threads per column, fixed-order reduction
-      const int j = t >> 4, q16 = t & 15;
-      float part = 0.f;
-      for (int i = q16; i < D; i += 16) part += mt[j][i];
-      part += __shfl_xor(part, 1);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 4);
-      part += __shfl_xor(part, 8);
-      if (q16 == 0) {
-        csum[j] = part;
-        a.snapc[sh * D + cb * CB + j] = part;
-      }
-    }
-    __syncthreads();
-
-    // ---- B operand of the read-back: M[dk][col] = mt[col][dk], bf16
-    bf16x8 mop[D / 32];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mop[c][i] = f2bf(mt[sidx][32 * c + 8 * grp + i]);
-
-    f32x4 acc[D / 16];
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[nb][r] = 0.f;
-    float zacc[D / 32][8];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zacc[c][i] = 0.f;
-
-    const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-    const bf16* __restrict__ kb = a.k + tok0 * D;
-    const bf16* __restrict__ vb = a.v + tok0 * D + cb * CB;
-
-    for (int st = wave; st < a.N / 32; st += 4) {
-      bf16 uh[2][4], ul[2][4];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int trow = 32 * st + 16 * h2 + sidx;  // token whose key this lane loads
-        float den = 0.f;
-        bf16x8 kop[D / 32];
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          const bf16x8 kx = *reinterpret_cast<const bf16x8*>(kb + (int64_t)trow * D + 32 * c + 8 * grp);
-          bf16x8 h8, l8;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float x = bf2f(kx[i]);
-            const float kp = x > 0.f ? x : exp_e(x) - 1.f;   // k' = sigma(k) - 1
-            const float f = kp + 1.f;
-            zacc[c][i] += f;
-            den = __builtin_fmaf(f, zs[32 * c + 8 * grp + i], den);
-            h8[i] = f2bf(f);
-            l8[i] = lo_part(f, h8[i]);
-            kop[c][i] = f2bf(kp);
-          }
-          *(INFINI_LDS bf16x8*)(khs + (16 * h2 + sidx) * P + 32 * c + 8 * grp) = h8;
-          *(INFINI_LDS bf16x8*)(kls + (16 * h2 + sidx) * P + 32 * c + 8 * grp) = l8;
-        }
-        den += __shfl_xor(den, 16);
-        den += __shfl_xor(den, 32);
-        // R = sigma(K) M_{s-1} = colsum(M) + K' M: lane holds (K' M)[token 4*grp + r][col sidx]
-        f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
-        if (has_memory) {
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) r4 = mfma16(kop[c], mop[c], r4);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tl = 4 * grp + r;                     // token within the 16-row half
-          const float den_t = __shfl(den, tl);
-          const float vv = bf2f(vb[(int64_t)(32 * st + 16 * h2 + tl) * D + sidx]);
-          const float u = (has_memory && den_t > 0.f) ? vv - (csum[sidx] + r4[r]) / den_t : vv;
-          uh[h2][r] = f2bf(u);
-          ul[h2][r] = lo_part(u, uh[h2][r]);
-        }
-      }
-      wave_lds_fence();
-      // ---- M^T[col][dk] += U^T sigma(K) over the 32 tokens (hi*hi + lo*hi + hi*lo)
-      bf16x8 ua, ub;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ua[r] = uh[0][r];
-        ua[4 + r] = uh[1][r];
-        ub[r] = ul[0][r];
-        ub[4 + r] = ul[1][r];
-      }
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) {
-        const bf16x8 kh = lds_operand_tr(khs, P, 4 * grp, 16 + 4 * grp, 16 * nb, sidx);
-        const bf16x8 kl = lds_operand_tr(kls, P, 4 * grp, 16 + 4 * grp, 16 * nb, sidx);
-        acc[nb] = mfma16(ua, kh, acc[nb]);
-        acc[nb] = mfma16(ub, kh, acc[nb]);
-        acc[nb] = mfma16(ua, kl, acc[nb]);
-      }
-      wave_lds_fence();
-    }
-    // ---- z partial of this wave: reduce over the 16 lanes of each group
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = zacc[c][i];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        zacc[c][i] = x;
-      }
-    __syncthreads();  // every wave is done with its staging tiles
-    if (sidx == 0) {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) zred[wave][32 * c + 8 * grp + i] = zacc[c][i];
-    }
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[(wave * CB + 4 * grp + r) * D + 16 * nb + sidx] = acc[nb][r];
-    __syncthreads();
-    for (int i = t; i < CB * D; i += kThreads) {
-      const int j = i / D, dk = i % D;
-      mt[j][dk] += ((red[(0 * CB + j) * D + dk] + red[(1 * CB + j) * D + dk]) +
-                    red[(2 * CB + j) * D + dk]) + red[(3 * CB + j) * D + dk];
-    }
-    for (int i = t; i < D; i += kThreads) zs[i] += ((zred[0][i] + zred[1][i]) + zred[2][i]) + zred[3][i];
-    __syncthreads();
-  }
-
-  for (int i = t; i < CB * D; i += kThreads) {
-    const int j = i / D, dk = i % D;
-    Mg[dk * D + cb * CB + j] = mt[j][dk];
-  }
-  if (cb == 0)
-    for (int i = t; i < D; i += kThreads) zg[i] = zs[i];
-}
-
 // ------------------------------------------------------------------ launchers
 template <int D>
 hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
@@ -408,19 +204,9 @@ hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_delta_chain(const DeltaArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.BH * (D / 16);
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(delta_chain_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
 template hipError_t launch_lin_contrib<64>(const LinContribArgs&, hipStream_t);
 template hipError_t launch_lin_contrib<128>(const LinContribArgs&, hipStream_t);
 template hipError_t launch_lin_scan<64>(const LinScanArgs&, hipStream_t);
 template hipError_t launch_lin_scan<128>(const LinScanArgs&, hipStream_t);
-template hipError_t launch_delta_chain<64>(const DeltaArgs&, hipStream_t);
-template hipError_t launch_delta_chain<128>(const DeltaArgs&, hipStream_t);
 
 }  // namespace infini
