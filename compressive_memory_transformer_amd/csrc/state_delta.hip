@@ -23,7 +23,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kCB = 16;          // columns of M (d_value) per chain workgroup
-constexpr int kChunk = 256;      // tokens per LDS chunk of the chain
+constexpr int kChainWaves = 8;   // chain workgroup: two waves per SIMD
+constexpr int kChunk = 32 * kChainWaves;   // tokens per LDS chunk: one 32-token block per wave
+constexpr int kInvSlot = 256;    // floats per 1/den slot: one wave-wide 16-byte load writes 1 KB
 constexpr int kPart = 256;       // tokens per workgroup of the pre-pass kernels
 
 // ------------------------------------------------------------------ pre-pass
@@ -77,8 +79,8 @@ void delta_ksig_kernel(DeltaArgs a) {
 
 // z_{s-1} of every segment (snapshots) and the final z: a prefix over the
 // segments of one head, one thread per d_key entry, in a fixed order.  The
-// per-segment sums of a batch of 16 segments are loaded before they are added,
-// so the loads overlap instead of forming one dependent chain.
+// part sums of a batch of 16 segments are loaded 16 at a time (independent
+// loads), so they overlap instead of forming one dependent chain.
 template <int D>
 __global__ __launch_bounds__(D)
 void delta_zscan_kernel(DeltaArgs a) {
@@ -86,18 +88,19 @@ void delta_zscan_kernel(DeltaArgs a) {
   const int bh = blockIdx.x, dk = threadIdx.x;
   float z = a.z[(int64_t)bh * D + dk];
   for (int s0 = 0; s0 < a.S; s0 += kBatch) {
+    const int nb = min(kBatch, a.S - s0);
     float cz[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      cz[i] = 0.f;
-      if (s0 + i < a.S) {
-        const float* cp = a.czp + ((int64_t)bh * a.S + s0 + i) * a.nparts * D + dk;
-        for (int p = 0; p < a.nparts; ++p) cz[i] += cp[(int64_t)p * D];
-      }
+    for (int i = 0; i < kBatch; ++i) cz[i] = 0.f;
+    const float* cp = a.czp + ((int64_t)bh * a.S + s0) * a.nparts * D + dk;
+    for (int p = 0; p < a.nparts; ++p) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (i < nb) cz[i] += cp[((int64_t)i * a.nparts + p) * D];
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (s0 + i < a.S) {
+      if (i < nb) {
         a.snapz[((int64_t)bh * a.S + s0 + i) * D + dk] = z;
         z += cz[i];
       }
@@ -156,10 +159,13 @@ struct ChainLayout {
   static constexpr int CHUNKS = D / 8;
   static constexpr int KP_ELEMS = kChunk * D;
   static constexpr int RPI = 64 * 8 / D;                      // k' rows per wave-wide 16-byte load
-  static constexpr int NIK = kChunk / RPI / 4;                // k' loads per wave and chunk
-  static constexpr int NIV = kChunk * kCB * 2 / 1024 / 4;     // V loads per wave and chunk
+  static constexpr int NIK = kChunk / RPI / kChainWaves;                // k' loads per wave and chunk
+  static constexpr int NIV = kChunk * kCB * 2 / 1024 / kChainWaves;     // V loads per wave and chunk
   static_assert(NIK >= 1 && NIV >= 1, "chunk too small");
-  static_assert(4 * D * kCB * 4 <= KP_ELEMS * 2, "update reduction must fit a k' chunk");
+  static_assert(kChainWaves * D * kCB * 4 <= KP_ELEMS * 2, "update reduction must fit a k' chunk");
+  static_assert(kInvSlot * 4 == 1024 && kChunk <= kInvSlot, "1/den slot holds one 64-lane load");
+  static_assert(NIK * kChainWaves * 1024 == KP_ELEMS * 2 && NIV * kChainWaves * 1024 == kChunk * kCB * 2,
+                "loads fill the slots exactly");
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -182,15 +188,18 @@ struct ChainCtx {
   int N, cps, wave, lane;
 };
 
-// Direct-to-LDS loads of chunk c of segment s (zeros past the segment): k'
-// rows with the swizzle, 16 V columns per token, 1/den.
+// Direct-to-LDS loads of chunk q of the head's stream (segment q / cps, chunk
+// q % cps; zeros past the segment or past the last segment, so that every
+// chunk issues the same number of loads): k' rows with the swizzle, 16 V
+// columns per token, 1/den (wave 0).
 template <int D>
-__device__ __forceinline__ void chain_issue(const ChainCtx<D>& cx, int s, int c, bf16* kpl, bf16* vl, float* il) {
+__device__ __forceinline__ void chain_issue(const ChainCtx<D>& cx, int q, int S, bf16* kpl, bf16* vl, float* il) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using CL = ChainLayout<D>;
+  const int s = q / cx.cps, c = q % cx.cps;
   const int first = c * kChunk;                                   // first token of the chunk in the segment
-  const int64_t tok = (int64_t)s * cx.N + first;                  // within the head
-  const uint32_t left = first < cx.N ? (uint32_t)(cx.N - first) : 0u;
+  const int64_t tok = s < S ? (int64_t)s * cx.N + first : 0;      // within the head
+  const uint32_t left = (s < S && first < cx.N) ? (uint32_t)(cx.N - first) : 0u;
   const int wv = __builtin_amdgcn_readfirstlane(cx.wave);
   {
     const __amdgpu_buffer_rsrc_t r = chain_rsrc(cx.kp + tok * D, left * D * 2);
@@ -221,6 +230,11 @@ __device__ __forceinline__ void chain_issue(const ChainCtx<D>& cx, int s, int c,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (INFINI_LDS void*)il, 16, 16 * cx.lane, 0, 0, 0);
   }
 #endif
+}
+
+// Waits until this wave's loads (LDS-bound and register-bound) have landed.
+__device__ __forceinline__ void chain_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
 }
 
 // Per-wave state of one segment: the B operand of the read-back (bf16 M, d_key
@@ -296,26 +310,30 @@ __device__ __forceinline__ void chain_block(ChainSeg<D>& sg, const bf16* __restr
 // The chain over the segments of one head for 16 columns of M (columns of M are
 // independent under the delta rule: column j of the read-back needs only
 // column j of M).  One workgroup of 4 waves per (b, h, column block), one
-// workgroup per CU; k', V and 1/den stream through two LDS chunk slots
-// (direct-to-LDS loads, the next chunk in flight while one is used).  Each wave
-// takes two 32-token blocks of a chunk and accumulates its own share of the
-// update; the four shares and colsum_t(U) are reduced in a fixed order at the
-// end of each segment (deterministic).
+// workgroup per CU with two waves per SIMD; k', V and 1/den stream through two
+// LDS chunk slots (direct-to-LDS loads, the next chunk in flight while one is
+// used).  Each of the 8 waves takes one 32-token block of a chunk and
+// accumulates its own share of the update; the shares and colsum_t(U) are
+// reduced in a fixed order at the end of each segment (deterministic).
 template <int D>
-__global__ __launch_bounds__(kThreads, 1)
+__global__ __launch_bounds__(64 * kChainWaves, 1)
 void delta_chain_kernel(DeltaArgs a) {
   using CL = ChainLayout<D>;
+  constexpr int NT = 64 * kChainWaves;   // threads
   constexpr int NCB = D / kCB;
-  constexpr int RPT = D / 16;            // M rows per thread (thread: column t % 16, rows RPT (t / 16) ..)
+  constexpr int RG = NT / kCB;           // row groups of M (thread: column t % 16, rows RPT (t / 16) ..)
+  constexpr int RPT = D / RG;
+  // two slots, each a distinct object so that reads of one slot never wait on
+  // loads into the other
   __shared__ __attribute__((aligned(1024))) bf16 kp0[CL::KP_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 kp1[CL::KP_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 vc0[kChunk * kCB];
   __shared__ __attribute__((aligned(1024))) bf16 vc1[kChunk * kCB];
-  __shared__ __attribute__((aligned(16))) float iv0[kChunk];
-  __shared__ __attribute__((aligned(16))) float iv1[kChunk];
+  __shared__ __attribute__((aligned(16))) float iv0[kInvSlot];
+  __shared__ __attribute__((aligned(16))) float iv1[kInvSlot];
   __shared__ __attribute__((aligned(16))) bf16 mts[kCB * D];   // M^T rows (bf16) of this block
-  __shared__ float csred[16][kCB];
-  __shared__ float ucs[4][kCB];
+  __shared__ float csred[RG][kCB];
+  __shared__ float ucs[kChainWaves][kCB];
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   const int bh = blk / NCB, cb = blk % NCB;
@@ -336,8 +354,8 @@ void delta_chain_kernel(DeltaArgs a) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) m[i] = Mg[(int64_t)(mrow0 + i) * D + cb * kCB + mcol];
 
-  chain_issue<D>(cx, 0, 0, kp0, vc0, iv0);
-  __builtin_amdgcn_s_waitcnt(0x0070);
+  chain_issue<D>(cx, 0, a.S, kp0, vc0, iv0);
+  chain_wait_all();
   __syncthreads();
 
   for (int s = 0; s < a.S; ++s) {
@@ -350,7 +368,7 @@ void delta_chain_kernel(DeltaArgs a) {
         mts[mcol * D + mrow0 + i] = f2bf(m[i]);
         part += m[i];
       }
-      csred[t / kCB][mcol] = part;
+      csred[t / kCB][mcol] = part;     // t / kCB < RG
     }
     __syncthreads();
     ChainSeg<D> sg;
@@ -358,13 +376,13 @@ void delta_chain_kernel(DeltaArgs a) {
       const int col = lane & 15, g = lane >> 4;
       float c = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) c += csred[r][col];
+      for (int r = 0; r < RG; ++r) c += csred[r][col];
       sg.cs = c;
 #pragma unroll
       for (int k = 0; k < D / 32; ++k) sg.mop[k] = lds_read8(mts + col * D + 32 * k + 8 * g);
       if (t < kCB) a.snapc[sh * D + cb * kCB + t] = c;
       // snapshot rows: column cb*16 + j of M is row cb*16 + j of M^T
-      for (int i = t; i < kCB * D / 8; i += kThreads) {
+      for (int i = t; i < kCB * D / 8; i += NT) {
         const int j = i / (D / 8), c8 = (i % (D / 8)) * 8;
         *reinterpret_cast<bf16x8*>(a.snapM + sh * D * D + (int64_t)(cb * kCB + j) * D + c8) =
             lds_read8(mts + j * D + c8);
@@ -374,16 +392,15 @@ void delta_chain_kernel(DeltaArgs a) {
     for (int k = 0; k < D / 16; ++k) sg.dm[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     sg.ucol = 0.f;
 
-    // ---- chunks: step c uses slot c % 2 and loads the next chunk into the other
-    // slot (chunk 0 of the next segment after the last chunk).
+    // ---- chunks: step c uses slot c % 2 and loads chunk c + 1 of the stream (the
+    // next segment's first chunk after the last) into the other slot.
+    const int q0 = s * cx.cps;
 #define INFINI_CHAIN_STEP(C, KC, VC, IC, KN, VN, IN)                                       \
     {                                                                                      \
       const int c_ = (C);                                                                  \
-      if (c_ + 1 < cx.cps) chain_issue<D>(cx, s, c_ + 1, KN, VN, IN);                      \
-      else if (s + 1 < a.S) chain_issue<D>(cx, s + 1, 0, KN, VN, IN);                      \
+      chain_issue<D>(cx, q0 + c_ + 1, a.S, KN, VN, IN);                                    \
       chain_block<D>(sg, KC, VC, IC, wave);                                                \
-      chain_block<D>(sg, KC, VC, IC, wave + 4);                                            \
-      __builtin_amdgcn_s_waitcnt(0x0070);                                                  \
+      chain_wait_all();                                                                    \
       __syncthreads();                                                                     \
     }
     for (int c = 0; c < cx.cps; c += 2) {
@@ -392,14 +409,15 @@ void delta_chain_kernel(DeltaArgs a) {
     }
 #undef INFINI_CHAIN_STEP
 
-    // ---- M_s = M_{s-1} + 1 colsum_t(U) + sum over waves of k'^T U (slot 1 is free)
+    // ---- M_s = M_{s-1} + 1 colsum_t(U) + sum over waves of k'^T U (slot 1 is free:
+    // the last chunk of the segment used it, the next one is in slot 0)
     {
       const int col = lane & 15, g = lane >> 4;
       float uc = sg.ucol;
       uc += __shfl_xor(uc, 16);
       uc += __shfl_xor(uc, 32);
       if (g == 0) ucs[wave][col] = uc;
-      float* red = reinterpret_cast<float*>(kp1);          // [4][D][16]
+      float* red = reinterpret_cast<float*>(kp1);          // [waves][D][16]
 #pragma unroll
       for (int k = 0; k < D / 16; ++k)
 #pragma unroll
@@ -408,12 +426,15 @@ void delta_chain_kernel(DeltaArgs a) {
     __syncthreads();
     {
       const float* red = reinterpret_cast<const float*>(kp1);
-      const float ucsum = ((ucs[0][mcol] + ucs[1][mcol]) + ucs[2][mcol]) + ucs[3][mcol];
+      float ucsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kChainWaves; ++w) ucsum += ucs[w][mcol];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int dk = mrow0 + i;
-        const float d = ((red[(0 * D + dk) * kCB + mcol] + red[(1 * D + dk) * kCB + mcol]) +
-                         red[(2 * D + dk) * kCB + mcol]) + red[(3 * D + dk) * kCB + mcol];
+        float d = 0.f;
+#pragma unroll
+        for (int w = 0; w < kChainWaves; ++w) d += red[(w * D + dk) * kCB + mcol];
         m[i] += ucsum + d;
       }
     }
@@ -442,7 +463,7 @@ hipError_t launch_delta_state(const DeltaArgs& args, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(delta_den_kernel<D>, dim3((unsigned)pblocks), dim3(kThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(delta_chain_kernel<D>, dim3((unsigned)(a.BH * (D / kCB))), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(delta_chain_kernel<D>, dim3((unsigned)(a.BH * (D / kCB))), dim3(64 * kChainWaves), 0, stream, a);
   return hipGetLastError();
 }
 
