@@ -104,7 +104,7 @@ bool workspace_layout(const infini_attn_state* st, int64_t S, WsLayout* w) {
     } else {
       int64_t tokens, parts;
       if (!mul_ok(BH, S * (int64_t)st->segment_len, &tokens)) return false;
-      if (!mul_ok(seg_heads, (int64_t)infini::delta_parts(st->segment_len) * D, &parts)) return false;
+      if (!mul_ok(seg_heads, D, &parts)) return false;
       w->kp = off; off = align_up(off + (size_t)tokens * D * 2);
       w->czp = off; off = align_up(off + (size_t)parts * 4);
       w->inv = off; off = align_up(off + (size_t)tokens * 4);

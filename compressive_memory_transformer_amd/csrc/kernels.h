@@ -69,15 +69,15 @@ struct DeltaArgs {
   float* snapz;          // [B*H*S][D]
   float* snapc;          // [B*H*S][D]
   bf16* kp;              // workspace [B*H][L][D]: sigma(K) - 1
-  float* czp;            // workspace [B*H*S][nparts][D]: column sums of sigma(K) per 256 tokens
+  float* czp;            // workspace [B*H*S][D]: column sums of sigma(K) per segment
   float* inv_den;        // workspace [B*H][L]
   int BH, S, N;
   int64_t L;
   int64_t seg_base;
-  int nparts;            // 256-token parts per segment (set by the launcher)
+  int nparts;            // 256-token blocks of the 1/den kernel per segment (set by the launcher)
 };
 template <int D> hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream);
-// 256-token parts per segment of the pre-pass (size of czp).
+// 256-token blocks per segment of the 1/den kernel.
 int delta_parts(int N);
 
 // ------------------------------------------------------------------ fp32 path

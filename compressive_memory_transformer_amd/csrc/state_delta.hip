@@ -6,7 +6,7 @@
 //
 // Everything that depends on K alone runs in parallel before the chain:
 //   delta_ksig: k' = sigma(K) - 1 as bf16 (full relative precision of the
-//               deviation from 1) and the per-segment column sums of sigma(K);
+//               deviation from 1) and the column sums of sigma(K) per segment;
 //   delta_zscan: z_{s-1} for every segment (the snapshots) and the final z;
 //   delta_den:  1 / (sigma(K_s[t]) z_{s-1}) per token, in fp32 from K.
 // The chain then needs per segment only k', V and 1/den, and splits
@@ -26,7 +26,7 @@ constexpr int kCB = 16;          // columns of M (d_value) per chain workgroup
 constexpr int kChainWaves = 8;   // chain workgroup: two waves per SIMD
 constexpr int kChunk = 32 * kChainWaves;   // tokens per LDS chunk: one 32-token block per wave
 constexpr int kInvSlot = 256;    // floats per 1/den slot: one wave-wide 16-byte load writes 1 KB
-constexpr int kPart = 256;       // tokens per workgroup of the pre-pass kernels
+constexpr int kPart = 256;       // tokens per workgroup of the 1/den kernel
 
 // ------------------------------------------------------------------ pre-pass
 // Lanes per token and tokens per pass of a 256-thread block when each lane
@@ -39,23 +39,22 @@ struct TokLanes {
 
 }  // namespace
 
-// k' = sigma(K) - 1 (bf16) and the column sums of sigma(K) over each 256-token
-// part of a segment.  One workgroup per (b, h, segment, part).
+// k' = sigma(K) - 1 (bf16) and the column sums of sigma(K) over a segment.  One
+// workgroup per (b, h, segment); the sums are reduced in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void delta_ksig_kernel(DeltaArgs a) {
   using T = TokLanes<D>;
   __shared__ float red[T::TPI][D];
-  const int sh = blockIdx.x / a.nparts, part = blockIdx.x % a.nparts;
+  const int sh = blockIdx.x;
   const int bh = sh / a.S, s = sh % a.S;
   const int t = threadIdx.x, sub = t / T::LPT, d0 = (t % T::LPT) * 8;
-  const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N + (int64_t)part * kPart;
-  const int ntok = min(kPart, a.N - part * kPart);
+  const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll 4
-  for (int i = sub; i < ntok; i += T::TPI) {
+  for (int i = sub; i < a.N; i += T::TPI) {
     const bf16x8 kx = *reinterpret_cast<const bf16x8*>(a.k + (tok0 + i) * D + d0);
     bf16x8 kp;
 #pragma unroll
@@ -73,36 +72,31 @@ void delta_ksig_kernel(DeltaArgs a) {
   if (t < D) {
     float c = 0.f;
     for (int r = 0; r < T::TPI; ++r) c += red[r][t];
-    a.czp[((int64_t)sh * a.nparts + part) * D + t] = c;
+    a.czp[(int64_t)sh * D + t] = c;
   }
 }
 
 // z_{s-1} of every segment (snapshots) and the final z: a prefix over the
 // segments of one head, one thread per d_key entry, in a fixed order.  The
-// part sums of a batch of 16 segments are loaded 16 at a time (independent
-// loads), so they overlap instead of forming one dependent chain.
+// per-segment sums are loaded 32 at a time (independent loads at clamped
+// indices), so they overlap instead of forming one dependent chain.
 template <int D>
 __global__ __launch_bounds__(D)
 void delta_zscan_kernel(DeltaArgs a) {
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;
   const int bh = blockIdx.x, dk = threadIdx.x;
+  const float* cz = a.czp + (int64_t)bh * a.S * D + dk;
+  float* sz = a.snapz + (int64_t)bh * a.S * D + dk;
   float z = a.z[(int64_t)bh * D + dk];
   for (int s0 = 0; s0 < a.S; s0 += kBatch) {
-    const int nb = min(kBatch, a.S - s0);
-    float cz[kBatch];
+    float c[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) cz[i] = 0.f;
-    const float* cp = a.czp + ((int64_t)bh * a.S + s0) * a.nparts * D + dk;
-    for (int p = 0; p < a.nparts; ++p) {
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (i < nb) cz[i] += cp[((int64_t)i * a.nparts + p) * D];
-    }
+    for (int i = 0; i < kBatch; ++i) c[i] = cz[(int64_t)min(s0 + i, a.S - 1) * D];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (i < nb) {
-        a.snapz[((int64_t)bh * a.S + s0 + i) * D + dk] = z;
-        z += cz[i];
+      if (s0 + i < a.S) {
+        sz[(int64_t)(s0 + i) * D] = z;
+        z += c[i];
       }
     }
   }
@@ -446,7 +440,7 @@ void delta_chain_kernel(DeltaArgs a) {
 }
 
 // ------------------------------------------------------------------ launchers
-int delta_parts(int N) { return (N + kPart - 1) / kPart; }
+int delta_parts(int N) { return (N + kPart - 1) / kPart; }   // blocks of the 1/den kernel per segment
 
 template <int D>
 hipError_t launch_delta_state(const DeltaArgs& args, hipStream_t stream) {
@@ -456,7 +450,7 @@ hipError_t launch_delta_state(const DeltaArgs& args, hipStream_t stream) {
   if (seg_heads <= 0) return hipSuccess;
   const int64_t pblocks = seg_heads * a.nparts;
   if (pblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(delta_ksig_kernel<D>, dim3((unsigned)pblocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(delta_ksig_kernel<D>, dim3((unsigned)seg_heads), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(delta_zscan_kernel<D>, dim3((unsigned)a.BH), dim3(D), 0, stream, a);

@@ -81,8 +81,8 @@ def test_workspace_bytes():
     assert ia.workspace_bytes(st, S * 2048) == want
     st = _state(rule=ia.RULE_DELTA)
     L = S * 2048
-    # snapshots, then sigma(K) - 1 (bf16), per-256-token column sums of sigma(K), 1/den per token
-    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * L * D * 2 + BH * S * (2048 // 256) * D * 4 + BH * L * 4
+    # snapshots, then sigma(K) - 1 (bf16), column sums of sigma(K) per segment, 1/den per token
+    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * L * D * 2 + BH * S * D * 4 + BH * L * 4
     assert ia.workspace_bytes(st, L) == want
     assert ia.workspace_bytes(st, 2047) == 0
     assert ia.workspace_bytes(st, 0) == 0
