@@ -56,6 +56,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 64 * kWaves;   // query rows per tile: two 32-row blocks per wave
 constexpr int kBN = 128;           // keys per LDS tile
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
+constexpr int kDmaBlocks = 2;      // blocks of a tile that issue the next load item
 constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
 
 template <int D>
@@ -211,8 +212,9 @@ struct LdsAddr {
 // Running state of one 32-row query block of a wave.
 template <int D>
 struct QBlock {
-  bf16x8 q[D / 16];    // Q^T as the B operand: lane holds Q[row][16c + 8hi .. +7]
+  bf16x8 q[D / 16];    // Q^T * scale * log2 e as the B operand: lane holds Q[row][16c + 8hi .. +7]
   f32x16 o[D / 32];    // O^T accumulator: lane holds O[row][32db + 8(r/4) + 4hi + r%4]
+  f32x16 mneg;         // -m in every element: the initial accumulator of S^T
   float m;             // reference maximum of the row (log2 domain)
   float l;             // this lane's share of the softmax denominator
   bool bad;            // some block summed past the limit: recompute the block
@@ -290,13 +292,14 @@ __device__ __forceinline__ void mask_block(f32x16& sacc, int kb0, int my_row) {
   }
 }
 
-// Softmax of one 32 x 32 block: probabilities against the reference maximum,
-// added to the denominator and packed to bf16 as the B operand of PV.
+// Softmax of one 32 x 32 block from s = score - m (the S^T chains start at -m):
+// probabilities, added to the denominator and packed to bf16 as the B operand
+// of PV.
 template <int D>
-__device__ __forceinline__ void softmax_block(QBlock<D>& X, const f32x16& s, float sc, bf16x8 (&p)[2]) {
+__device__ __forceinline__ void softmax_block(QBlock<D>& X, const f32x16& s, bf16x8 (&p)[2]) {
   f32x16 e;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) e[r] = exp2_fast(__builtin_fmaf(s[r], sc, -X.m));
+  for (int r = 0; r < 16; ++r) e[r] = exp2_fast(s[r]);   // s = scores - m (log2 domain)
   float t[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) t[r] = e[r] + e[r + 8];
@@ -311,14 +314,26 @@ __device__ __forceinline__ void softmax_block(QBlock<D>& X, const f32x16& s, flo
     for (int i = 0; i < 8; ++i) p[hf][i] = f2bf(e[8 * hf + i]);
 }
 
-// Row maximum (scaled, log2 domain) of a 32 x 32 score block; the two lanes
-// holding a row exchange their halves.
-__device__ __forceinline__ float block_row_max(const f32x16& s, float sc) {
+// Row maximum of a 32 x 32 score block (log2 domain: Q carries the scale); the
+// two lanes holding a row exchange their halves.
+__device__ __forceinline__ float block_row_max(const f32x16& s) {
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  return mx * sc;
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// s - m for a block computed from a zero accumulator.
+__device__ __forceinline__ void sub_m(f32x16& s, float m) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] -= m;
+}
+
+template <int D>
+__device__ __forceinline__ void set_m(QBlock<D>& X, float m) {
+  X.m = m;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) X.mneg[r] = -m;
 }
 
 // Operand stages of the pipelined tile: K operands of one 32-key block (all D /
@@ -342,23 +357,24 @@ __device__ __forceinline__ void load_v(bf16x8 (&vo)[2][D / 32], const bf16* __re
       vo[hf][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 }
+// S^T - m for one 32-key block: the chains start from the -m accumulators, so
+// the result is the exp2 argument itself (Q carries the softmax scale).
 template <int D>
 __device__ __forceinline__ void s_mfma(f32x16& sa, f32x16& sb, const bf16x8 (&ko)[D / 16],
-                                       const bf16x8 (&qa)[D / 16], const bf16x8 (&qb)[D / 16]) {
+                                       const QBlock<D>& A, const QBlock<D>& B) {
+  sa = mfma32(ko[0], A.q[0], A.mneg);
+  sb = mfma32(ko[0], B.q[0], B.mneg);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sa[r] = sb[r] = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    sa = mfma32(ko[c], qa[c], sa);
-    sb = mfma32(ko[c], qb[c], sb);
+  for (int c = 1; c < D / 16; ++c) {
+    sa = mfma32(ko[c], A.q[c], sa);
+    sb = mfma32(ko[c], B.q[c], sb);
   }
 }
 template <int D>
-__device__ __forceinline__ void s_mfma1(f32x16& sb, const bf16x8 (&ko)[D / 16], const bf16x8 (&qb)[D / 16]) {
+__device__ __forceinline__ void s_mfma1(f32x16& sb, const bf16x8 (&ko)[D / 16], const QBlock<D>& B) {
+  sb = mfma32(ko[0], B.q[0], B.mneg);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sb[r] = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) sb = mfma32(ko[c], qb[c], sb);
+  for (int c = 1; c < D / 16; ++c) sb = mfma32(ko[c], B.q[c], sb);
 }
 template <int D>
 __device__ __forceinline__ void pv_mfma(f32x16 (&o)[D / 32], const bf16x8 (&vo)[2][D / 32], const bf16x8 (&p)[2]) {
@@ -395,77 +411,111 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int kb, int r0) {
 #endif
 }
 
-// A 128-key tile through the software pipeline over its four 32-key blocks j:
-//   phase 1: S^T(j+1) MFMAs | softmax of query block A (VALU) | V^T operands of
-//            block j and K operands of block j+2 (LDS reads)
-//   phase 2: A's O^T update | softmax of query block B
-//   phase 3: B's O^T update
-// The sched_group_barrier list pins that interleave; each LDS read is issued
-// at least a phase before its use.  The next load item's instructions are
-// spread over the four blocks, so the CU's load path streams them while the
-// MFMAs run instead of stalling the waves at the start of the step.
-// MASK_A / MASK_B: the tile holds the diagonal of that query block (blocks
-// right of it are fully masked); WITH_A = false: query block A sees none of the
-// tile's keys and is skipped.
+// Compiler fence: nothing is moved across it, so the slots of the tile pipeline
+// keep the order in which they are written.
+#define INFINI_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// A 128-key tile through the software pipeline over its four 32-key blocks j.
+// One wave per SIMD issues in order, so MFMA and VALU work only overlap when
+// they alternate in the instruction stream: an MFMA occupies the matrix pipe for
+// 32 cycles, during which the wave issues the next few independent VALU or LDS
+// instructions.  Each block is written as two phases of slots, one MFMA per slot
+// followed by that slot's share of the other work:
+//   phase 1: S^T(j+1) MFMAs | softmax of block j (a few elements per slot) and the
+//            V^T operand reads of block j
+//   phase 2: O^T += V^T P^T MFMAs of block j | K operand reads of block j+2, the
+//            block's share of the next load item, the softmax sums
+// MASK_A / MASK_B: the tile holds the diagonal of that query block (blocks right
+// of it are fully masked); WITH_A = false: query block A sees none of the tile's
+// keys and is skipped.
 template <int D, bool MASK_A, bool MASK_B, bool WITH_A>
 __device__ __forceinline__ void tile_pipe(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
-                                          const bf16* __restrict__ vt, const LdsAddr<D>& ad, float sc,
+                                          const bf16* __restrict__ vt, const LdsAddr<D>& ad,
                                           const Prefetch<D>& pf, int k0, int ra, int rb) {
-  constexpr int NIJ = FaLayout<D>::NI / kKB;   // prefetch instructions per block and tensor
+  constexpr int NI = FaLayout<D>::NI;          // prefetch instructions per tensor
+  constexpr int DPB = 2 * NI / kDmaBlocks;     // prefetch instructions per block (K and V)
+  constexpr int KS = D / 16;                   // 16-deep steps of an S^T chain
+  constexpr int NV = D / 32;                   // O^T accumulators per query block
   constexpr int NQ = WITH_A ? 2 : 1;           // query blocks
-  constexpr int NS = NQ * (D / 16);            // S^T MFMAs per block
-  constexpr int NP = D / 16;                   // O^T MFMAs per block and query block
-  bf16x8 ko[D / 16];
-  bf16x8 vo[2][D / 32];
-  f32x16 sa, sb;
+  constexpr int N1 = NQ * KS;                  // phase-1 slots (S^T MFMAs)
+  constexpr int N2 = NQ * 2 * NV;              // phase-2 slots (O^T MFMAs)
+  constexpr int E = 16 * NQ / N1;              // softmax elements per phase-1 slot
+  constexpr int DPS = (DPB + N2 - 1) / N2;     // prefetch instructions per phase-2 slot
+  static_assert(2 * NV <= N1 && KS <= N2 && (2 * NI) % kDmaBlocks == 0, "slot shares");
+  bf16x8 ko[KS];
+  bf16x8 vo[2][NV];
+  f32x16 sa, sb;   // S^T - m of the current block
   load_k<D>(ko, kt, 0, ad);
-  if (WITH_A) s_mfma<D>(sa, sb, ko, A.q, B.q);
-  else s_mfma1<D>(sb, ko, B.q);
+  if (WITH_A) s_mfma<D>(sa, sb, ko, A, B);
+  else s_mfma1<D>(sb, ko, B);
   load_k<D>(ko, kt, 1, ad);
+  INFINI_FENCE();
 #pragma unroll
   for (int j = 0; j < kKB; ++j) {
-    pf.template issue<NIJ>(NIJ * j);
-    load_v<D>(vo, vt, j, ad);
-    f32x16 na, nb;
-    bf16x8 pa[2], pb[2];
-    if (j + 1 < kKB) {
-      if (WITH_A) s_mfma<D>(na, nb, ko, A.q, B.q);
-      else s_mfma1<D>(nb, ko, B.q);
-    }
+    const bool more = j + 1 < kKB;
     if (MASK_A) mask_scores(sa, k0 + 32 * j, ra);
     if (MASK_B) mask_scores(sb, k0 + 32 * j, rb);
-    if (WITH_A) softmax_block<D>(A, sa, sc, pa);
-    if (j + 2 < kKB) load_k<D>(ko, kt, j + 2, ad);
-    if (WITH_A) pv_mfma<D>(A.o, vo, pa);
-    softmax_block<D>(B, sb, sc, pb);
-    pv_mfma<D>(B.o, vo, pb);
-    if (j + 1 < kKB) {
+    f32x16 na, nb;
+    bf16x8 pa[2], pb[2];
+    float ta = 0.f, tb = 0.f;
+    INFINI_FENCE();
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+      if (more) {
+        const int c = i / NQ;
+        if (WITH_A && i % 2 == 0) na = mfma32(ko[c], A.q[c], c == 0 ? A.mneg : na);
+        else nb = mfma32(ko[c], B.q[c], c == 0 ? B.mneg : nb);
+      }
+      if (i < 2 * NV) {
+        const int hf = i / NV, db = i % NV;
+        const bf16* p = vt + (32 * j + 16 * hf) * D + ad.v[db];
+        const s16x4 x = lds_read_tr16(p);
+        const s16x4 y = lds_read_tr16(p + 8 * D);
+        vo[hf][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const int g = E * i + u;            // element g of [A's 16, B's 16] (or B's 16 alone)
+        const bool in_a = WITH_A && g < 16;
+        const int r = in_a ? g : g % 16;
+        const float e = exp2_fast(in_a ? sa[r] : sb[r]);
+        if (in_a) {
+          ta += e;
+          pa[r / 8][r % 8] = f2bf(e);
+        } else {
+          tb += e;
+          pb[r / 8][r % 8] = f2bf(e);
+        }
+      }
+      INFINI_FENCE();
+    }
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      const int hf = (i / NV) % 2, db = i % NV;
+      if (WITH_A && i < 2 * NV) A.o[db] = mfma32(vo[hf][db], pa[hf], A.o[db]);
+      else B.o[db] = mfma32(vo[hf][db], pb[hf], B.o[db]);
+      if (j + 2 < kKB && i < KS) ko[i] = lds_read8(kt + 32 * (j + 2) * D + ad.kofs(i));
+      if (j < kDmaBlocks) {
+#pragma unroll
+        for (int w = 0; w < DPS; ++w) {
+          const int u = DPB * j + DPS * i + w;   // instruction u of this wave's K then V loads
+          if (DPS * i + w < DPB && u < NI) issue_part<D, false, 1>(u, pf.kb, pf.kbytes, pf.kn, pf.wave, *pf.dof);
+          else if (DPS * i + w < DPB) issue_part<D, true, 1>(u - NI, pf.vb, pf.vbytes, pf.vn, pf.wave, *pf.dof);
+        }
+      }
+      if (i == 0) {
+        if (WITH_A) {
+          A.bad |= !(ta <= kSumLimit);
+          A.l += ta;
+        }
+        B.bad |= !(tb <= kSumLimit);
+        B.l += tb;
+      }
+      INFINI_FENCE();
+    }
+    if (more) {
       if (WITH_A) sa = na;
       sb = nb;
-#pragma unroll
-      for (int i = 0; i < NS / 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < NS / 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
-      }
-    }
-    if (WITH_A) {
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgValu, 2, 0);
     }
   }
 }
@@ -489,20 +539,24 @@ __device__ __forceinline__ void tile_diag(QBlock<D>& A, QBlock<D>& B, const bf16
     bf16x8 pa[2], pb[2];
     if (need_a && need_b) {
       s_pair<D, true>(sa, sb, kt, j, ad, A.q, B.q);
+      sub_m(sa, A.m);
+      sub_m(sb, B.m);
       if (kb == ra) mask_block(sa, kb, ra + l32);
       if (kb == rb) mask_block(sb, kb, rb + l32);
-      softmax_block<D>(A, sa, sc, pa);
-      softmax_block<D>(B, sb, sc, pb);
+      softmax_block<D>(A, sa, pa);
+      softmax_block<D>(B, sb, pb);
       pv_pair<D, true>(A, B, vt, j, ad, pa, pb);
     } else if (need_a) {  // query block B inactive
       s_pair<D, false>(sa, sb, kt, j, ad, A.q, A.q);
+      sub_m(sa, A.m);
       if (kb == ra) mask_block(sa, kb, ra + l32);
-      softmax_block<D>(A, sa, sc, pa);
+      softmax_block<D>(A, sa, pa);
       pv_pair<D, false>(A, A, vt, j, ad, pa, pa);
     } else {              // block j lies right of block A's rows
       s_pair<D, false>(sb, sa, kt, j, ad, B.q, B.q);
+      sub_m(sb, B.m);
       if (kb == rb) mask_block(sb, kb, rb + l32);
-      softmax_block<D>(B, sb, sc, pb);
+      softmax_block<D>(B, sb, pb);
       pv_pair<D, false>(B, B, vt, j, ad, pb, pb);
     }
   }
@@ -512,19 +566,19 @@ __device__ __forceinline__ void tile_diag(QBlock<D>& A, QBlock<D>& B, const bf16
 // the first block every query sees (tile 0 is in LDS).  ra < rb.
 template <int D>
 __device__ __forceinline__ void init_m(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
-                                       const LdsAddr<D>& ad, float sc, int ra, int rb, bool act_a, bool act_b) {
+                                       const LdsAddr<D>& ad, int ra, int rb, bool act_a, bool act_b) {
   const int l32 = threadIdx.x & 31;
   f32x16 sa, sb;
   if (act_b) {
     s_pair<D, true>(sa, sb, kt, 0, ad, A.q, B.q);
     if (rb == 0) mask_block(sb, 0, l32);
-    B.m = block_row_max(sb, sc);
+    set_m(B, block_row_max(sb));
   } else if (act_a) {
     s_pair<D, false>(sa, sb, kt, 0, ad, A.q, A.q);
   }
   if (act_a) {
     if (ra == 0) mask_block(sa, 0, l32);
-    A.m = block_row_max(sa, sc);
+    set_m(A, block_row_max(sa));
   }
 }
 
@@ -533,7 +587,7 @@ __device__ __forceinline__ void init_m(QBlock<D>& A, QBlock<D>& B, const bf16* _
 // with K and V operands loaded straight from memory (no LDS, no barriers).
 template <int D>
 __device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ kseg,
-                                const bf16* __restrict__ vseg, float sc) {
+                                const bf16* __restrict__ vseg) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
   auto scores = [&](int kb) {
     f32x16 s;
@@ -549,8 +603,8 @@ __device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ k
   };
   float m = -__builtin_inff();
 #pragma unroll 1
-  for (int kb = 0; kb <= r0; kb += 32) m = fmaxf(m, block_row_max(scores(kb), sc));
-  X.m = m;
+  for (int kb = 0; kb <= r0; kb += 32) m = fmaxf(m, block_row_max(scores(kb)));
+  set_m(X, m);
   X.l = 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -562,7 +616,7 @@ __device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ k
     bf16x8 p[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = exp2_fast(__builtin_fmaf(s[r], sc, -m));
+      const float e = exp2_fast(s[r] - m);
       X.l += e;
       p[r >> 3][r & 7] = f2bf(e);
     }
@@ -583,13 +637,23 @@ __device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ k
   X.bad = false;
 }
 
+// Loads of one 32-row block of Q rows: lane l holds Q[row][16 c + 8 hi .. + 7] of
+// its row; p points at element 8 hi of the lane's row.
+template <int D>
+__device__ __forceinline__ void load_q_rows(bf16x8 (&q)[D / 16], const bf16* __restrict__ p) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) q[c] = *reinterpret_cast<const bf16x8*>(p + 16 * c);
+}
+
 // Retrieval, gate and store of one query block.  mt: M^T snapshot (K-slot
-// layout), zs / cs: z and colsum(M) in LDS.
+// layout), zs / cs: z and colsum(M) in LDS, ob: the block's first output row,
+// stage: this wave's 4 KB of LDS for the output.
 template <int D>
 __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __restrict__ mt,
                                              const float* __restrict__ zs, const float* __restrict__ cs,
-                                             const LdsAddr<D>& ad, bool has_memory, float g, bf16* __restrict__ orow) {
-  const int hi = (threadIdx.x >> 5) & 1;
+                                             const LdsAddr<D>& ad, bool has_memory, float g, float inv_sc,
+                                             bf16* __restrict__ ob, bf16* __restrict__ stage) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
   const float l_tot = X.l + __shfl_xor(X.l, 32);
   const float inv_l = 1.f / l_tot;
   f32x16 am[D / 32];
@@ -612,7 +676,7 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
       const f32x4 z1 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi + 4);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = bf2f(X.q[c][i]);
+        const float x = bf2f(X.q[c][i]) * inv_sc;       // q (the registers hold q * scale * log2 e)
         const float f = x > 0.f ? x : exp_e(x) - 1.f;   // q' = sigma(q) - 1
         const float zz = i < 4 ? z0[i] : z1[i - 4];
         den = __builtin_fmaf(f, zz, den);
@@ -633,20 +697,37 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) am[db][r] = 0.f;
   }
-  // lane holds query row orow, values d = 32db + 8j + 4hi + 0..3
+  // lane holds row l32 of the block, values d = 32db + 8j + 4hi + 0..3
   const float inv_den = (has_memory && den > 0.f) ? 1.f / den : 0.f;
   const float wg_mem = g * inv_den;
   const float wg_dot = (1.f - g) * inv_l;
+  // The rows go out through LDS, 64 columns at a time: each lane writes its
+  // 8-byte pieces of row l32 into a [32 x 64] stage (16-byte chunk k of row r at
+  // chunk k ^ ((r / 2) % 8), which keeps both access patterns free of bank
+  // conflicts), then reads back 16 bytes of row 8 i + lane / 8 so that every
+  // global store writes whole 128-byte row halves.  The stage is private to the
+  // wave, and LDS executes a wave's accesses in order, so no barrier is needed.
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int h = 0; h < D / 64; ++h) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x4 outv;
+    for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[db][4 * j + e] * wg_mem));
-      *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * hi) = outv;
+      for (int j = 0; j < 4; ++j) {
+        const int db = 2 * h + dh;
+        bf16x4 outv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[db][4 * j + e] * wg_mem));
+        const int chunk = (4 * dh + j) ^ ((l32 >> 1) & 7);
+        *(INFINI_LDS bf16x4*)(stage + l32 * 64 + 8 * chunk + 4 * hi) = outv;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3), c = lane & 7;
+      const bf16x8 x = *(const INFINI_LDS bf16x8*)(stage + r * 64 + 8 * (c ^ ((r >> 1) & 7)));
+      *reinterpret_cast<bf16x8*>(ob + (int64_t)r * D + 64 * h + 8 * c) = x;
     }
+  }
 }
 
 // Per-workgroup context shared by both passes.
@@ -664,6 +745,23 @@ struct FaCtx {
   bool has_memory;
   float g, sc;
 };
+
+// Q rows of this wave's two query blocks of query tile qt, as loaded (bf16).
+template <int D>
+struct QRaw {
+  bf16x8 a[D / 16];
+  bf16x8 b[D / 16];
+};
+
+// Row pointers for the Q loads of query tile qt (element 8 hi of the lane's
+// row of each block).  A block past the segment end reads the first rows
+// instead (its results are never used), so the loads need no branch.
+template <int D>
+__device__ __forceinline__ const bf16* q_rows(const FaCtx<D>& cx, int qt, int half) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int r = qt * kBM + half * (kBM / 2) + 32 * cx.wave;
+  return cx.qb + (int64_t)(r < cx.N ? r + l32 : l32) * D + 8 * hi;
+}
 
 // The load item after step t of a pass with nsteps steps: tile t+1 (zeros past
 // the segment), or after the last step the snapshot of M^T (K part; the V part
@@ -692,11 +790,13 @@ __device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int 
 
 // One query tile (pass) of the workgroup: the tiles alternate between the slots
 // starting at slot S0; the snapshot arrives in slot S0 after the last step.  On
-// entry tile 0 is in slot S0 (waited and synchronised); with `next` set, the
-// following pass's tile 0 is issued into slot S0^1 during the epilogue.
+// entry tile 0 is in slot S0 (waited for and synchronised); the first pass
+// finds its Q rows already loaded in qr, the second loads them itself.  With
+// `next` set, the epilogue issues the next pass's tile 0 into slot S0^1.
 template <int D, int S0>
-__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, bf16* k0s, bf16* v0s, bf16* k1s,
-                                         bf16* v1s, float* zc, const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
+__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, QRaw<D>& qr, bf16* k0s,
+                                         bf16* v0s, bf16* k1s, bf16* v1s, float* zc, bf16* ostage,
+                                         const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -713,11 +813,18 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
   const int nsteps = (last + 2) & ~1;        // even: pads with a tile beyond the segment
 
   QBlock<D> A, B;
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    A.q[c] = act_a ? *reinterpret_cast<const bf16x8*>(cx.qb + (int64_t)(ra + l32) * D + 16 * c + 8 * hi) : bf16x8{};
-    B.q[c] = act_b ? *reinterpret_cast<const bf16x8*>(cx.qb + (int64_t)(rb + l32) * D + 16 * c + 8 * hi) : bf16x8{};
+  // Q^T * scale * log2 e (rounded to bf16): the scores come out in the log2 domain
+  if (S0 == 1) {
+    load_q_rows<D>(qr.a, q_rows<D>(cx, qt, 0));
+    load_q_rows<D>(qr.b, q_rows<D>(cx, qt, 1));
   }
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      A.q[c][i] = f2bf(bf2f(qr.a[c][i]) * cx.sc);
+      B.q[c][i] = f2bf(bf2f(qr.b[c][i]) * cx.sc);
+    }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -725,10 +832,11 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
       A.o[db][r] = 0.f;
       B.o[db][r] = 0.f;
     }
-  A.m = B.m = 0.f;
+  set_m(A, 0.f);
+  set_m(B, 0.f);
   A.l = B.l = 0.f;
   A.bad = B.bad = false;
-  init_m<D>(A, B, kc, ad, cx.sc, ra, rb, act_a, act_b);
+  init_m<D>(A, B, kc, ad, ra, rb, act_a, act_b);
 
   // Step t uses slot S0 + (t % 2) and loads item t+1 into the other slot: tile
   // t+1, or the snapshot after the last step (z and colsum go to zc).
@@ -742,11 +850,11 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
     }                                                                                            \
     const int k0_ = t_ * kBN;                                                                    \
     if (act_a && k0_ + kBN <= ra) {                                                              \
-      tile_pipe<D, false, false, true>(A, B, KC, VC, ad, cx.sc, pf_, k0_, ra, rb);               \
+      tile_pipe<D, false, false, true>(A, B, KC, VC, ad, pf_, k0_, ra, rb);               \
     } else if (act_b && k0_ <= ra && ra < k0_ + kBN) {                                          \
-      tile_pipe<D, true, false, true>(A, B, KC, VC, ad, cx.sc, pf_, k0_, ra, rb);                \
+      tile_pipe<D, true, false, true>(A, B, KC, VC, ad, pf_, k0_, ra, rb);                \
     } else if (act_b && ra < k0_ && k0_ <= rb && rb < k0_ + kBN) {                              \
-      tile_pipe<D, false, true, false>(A, B, KC, VC, ad, cx.sc, pf_, k0_, ra, rb);               \
+      tile_pipe<D, false, true, false>(A, B, KC, VC, ad, pf_, k0_, ra, rb);               \
     } else {                                                                                     \
       pf_.template issue<FaLayout<D>::NI>(0);                                                    \
       if ((act_b && k0_ <= rb) || (act_a && k0_ <= ra))                                          \
@@ -760,8 +868,8 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
   }
 #undef INFINI_FA_STEP
 
-  if (act_a && __any(A.bad)) recompute_block<D>(A, ra, cx.kseg, cx.vseg, cx.sc);
-  if (act_b && __any(B.bad)) recompute_block<D>(B, rb, cx.kseg, cx.vseg, cx.sc);
+  if (act_a && __any(A.bad)) recompute_block<D>(A, ra, cx.kseg, cx.vseg);
+  if (act_b && __any(B.bad)) recompute_block<D>(B, rb, cx.kseg, cx.vseg);
 
   // The snapshot is in slot S0; slot S0^1 is free: start the next pass's tile 0.
   if (next) {
@@ -770,8 +878,10 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
   }
   const float* zs = zc;
   const float* cs = zc + 256;
-  if (act_a) finish_block<D>(A, kc, zs, cs, ad, cx.has_memory, cx.g, cx.ob + (int64_t)(ra + l32) * D);
-  if (act_b) finish_block<D>(B, kc, zs, cs, ad, cx.has_memory, cx.g, cx.ob + (int64_t)(rb + l32) * D);
+  const float inv_sc = 1.f / cx.sc;
+  bf16* const stage = ostage + 2048 * cx.wave;
+  if (act_a) finish_block<D>(A, kc, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)ra * D, stage);
+  if (act_b) finish_block<D>(B, kc, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)rb * D, stage);
   wait_loads_and_sync();
 }
 
@@ -784,6 +894,7 @@ void fa_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 k1s[L::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 v1s[L::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) float zc[512];   // z at [0, D), colsum(M) at [256, 256 + D)
+  __shared__ __attribute__((aligned(1024))) bf16 ostage[kWaves * 2048];   // output stage, 4 KB per wave
 
   const int npair = (a.nq + 1) / 2;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -823,9 +934,12 @@ void fa_fwd_kernel(FaArgs a) {
   dof.init(threadIdx.x & 63);
   issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
   issue_tile<D, true>(cx.vseg, cx.seg_bytes, v0s, cx.wave, dof);
+  QRaw<D> qr;
+  load_q_rows<D>(qr.a, q_rows<D>(cx, qt0, 0));
+  load_q_rows<D>(qr.b, q_rows<D>(cx, qt0, 1));
   wait_loads_and_sync();
-  run_pass<D, 0>(cx, qt0, two, k0s, v0s, k1s, v1s, zc, ad, dof);
-  if (two) run_pass<D, 1>(cx, qt1, false, k0s, v0s, k1s, v1s, zc, ad, dof);
+  run_pass<D, 0>(cx, qt0, two, qr, k0s, v0s, k1s, v1s, zc, ostage, ad, dof);
+  if (two) run_pass<D, 1>(cx, qt1, false, qr, k0s, v0s, k1s, v1s, zc, ostage, ad, dof);
 }
 
 int64_t fa_fwd_blocks(int64_t seg_heads, int N) {
