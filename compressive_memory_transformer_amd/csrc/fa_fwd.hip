@@ -671,9 +671,14 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
     float zpart = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      bf16x8 qp;
+      // operand reads first: their latency hides behind the q' arithmetic
+      bf16x8 ma[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) ma[db] = lds_read8(mt + 32 * db * D + ad.kofs(c));
       const f32x4 z0 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi);
       const f32x4 z1 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 qp;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = bf2f(X.q[c][i]) * inv_sc;       // q (the registers hold q * scale * log2 e)
@@ -684,10 +689,8 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
         qp[i] = f2bf(f);
       }
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 ma = lds_read8(mt + 32 * db * D + ad.kofs(c));
-        am[db] = mfma32(ma, qp, am[db]);
-      }
+      for (int db = 0; db < D / 32; ++db) am[db] = mfma32(ma[db], qp, am[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     den += zpart;                      // sum(z) over this lane's half of d_key
     den += __shfl_xor(den, 32);
@@ -764,11 +767,11 @@ __device__ __forceinline__ const bf16* q_rows(const FaCtx<D>& cx, int qt, int ha
 }
 
 // The load item after step t of a pass with nsteps steps: tile t+1 (zeros past
-// the segment), or after the last step the snapshot of M^T (K part; the V part
-// loads zeros).
+// the segment), or after the last step the snapshot of M^T (K part) together
+// with the V part of the next pass's tile 0 (zeros when there is none).
 template <int D>
-__device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int nsteps, bf16* kn, bf16* vn,
-                                                const DmaOfs<D>& dof) {
+__device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int nsteps, bool next, bf16* kn,
+                                                bf16* vn, const DmaOfs<D>& dof) {
   Prefetch<D> pf;
   pf.kn = kn;
   pf.vn = vn;
@@ -781,29 +784,27 @@ __device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int 
     pf.vb = cx.vseg + (off < cx.seg_bytes ? off / 2 : 0u);
     pf.kbytes = pf.vbytes = left;
   } else {
-    pf.kb = pf.vb = cx.snapM;
+    pf.kb = cx.snapM;
     pf.kbytes = cx.has_memory ? (uint32_t)(D * D * 2) : 0u;
-    pf.vbytes = 0u;
+    pf.vb = cx.vseg;
+    pf.vbytes = next ? cx.seg_bytes : 0u;
   }
   return pf;
 }
 
-// One query tile (pass) of the workgroup: the tiles alternate between the slots
-// starting at slot S0; the snapshot arrives in slot S0 after the last step.  On
-// entry tile 0 is in slot S0 (waited for and synchronised); the first pass
-// finds its Q rows already loaded in qr, the second loads them itself.  With
-// `next` set, the epilogue issues the next pass's tile 0 into slot S0^1.
-template <int D, int S0>
-__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, QRaw<D>& qr, bf16* k0s,
+// One query tile (pass) of the workgroup.  Tile t of the pass sits in slot t % 2
+// (k0s/v0s, k1s/v1s); every pass has an even number of steps, so the last one
+// uses slot 1 and brings the snapshot of M^T into k0s (with z and colsum into
+// zc) and, with `next` set, the V part of the next pass's tile 0 into v0s.  On
+// entry tile 0 is in slot 0 and the Q rows are in qr (waited for and
+// synchronised).
+template <int D>
+__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, bf16* k0s,
                                          bf16* v0s, bf16* k1s, bf16* v1s, float* zc, bf16* ostage,
                                          const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  bf16* const kc = S0 == 0 ? k0s : k1s;      // slot S0
-  bf16* const vc = S0 == 0 ? v0s : v1s;
-  bf16* const kn = S0 == 0 ? k1s : k0s;      // slot S0^1
-  bf16* const vn = S0 == 0 ? v1s : v0s;
   const int q0 = qt * kBM;
   const int ra = q0 + 32 * cx.wave;          // first rows of the two query blocks
   const int rb = ra + kBM / 2;
@@ -814,10 +815,9 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
 
   QBlock<D> A, B;
   // Q^T * scale * log2 e (rounded to bf16): the scores come out in the log2 domain
-  if (S0 == 1) {
-    load_q_rows<D>(qr.a, q_rows<D>(cx, qt, 0));
-    load_q_rows<D>(qr.b, q_rows<D>(cx, qt, 1));
-  }
+  QRaw<D> qr;
+  load_q_rows<D>(qr.a, q_rows<D>(cx, qt, 0));
+  load_q_rows<D>(qr.b, q_rows<D>(cx, qt, 1));
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
 #pragma unroll
@@ -836,14 +836,13 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
   set_m(B, 0.f);
   A.l = B.l = 0.f;
   A.bad = B.bad = false;
-  init_m<D>(A, B, kc, ad, ra, rb, act_a, act_b);
+  init_m<D>(A, B, k0s, ad, ra, rb, act_a, act_b);
 
-  // Step t uses slot S0 + (t % 2) and loads item t+1 into the other slot: tile
-  // t+1, or the snapshot after the last step (z and colsum go to zc).
+  // Step t uses slot t % 2 and loads item t+1 into the other slot.
 #define INFINI_FA_STEP(T, KC, VC, KN, VN)                                                        \
   {                                                                                              \
     const int t_ = (T);                                                                          \
-    const Prefetch<D> pf_ = next_item<D>(cx, t_, nsteps, KN, VN, dof);                           \
+    const Prefetch<D> pf_ = next_item<D>(cx, t_, nsteps, next, KN, VN, dof);                     \
     if (t_ + 1 == nsteps && cx.has_memory && cx.wave == 0) {                                     \
       issue_row(cx.snapz, D * 4, zc);                                                            \
       issue_row(cx.snapc, D * 4, zc + 256);                                                      \
@@ -863,25 +862,20 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
     wait_loads_and_sync();                                                                       \
   }
   for (int t = 0; t < nsteps; t += 2) {
-    INFINI_FA_STEP(t, kc, vc, kn, vn)
-    INFINI_FA_STEP(t + 1, kn, vn, kc, vc)
+    INFINI_FA_STEP(t, k0s, v0s, k1s, v1s)
+    INFINI_FA_STEP(t + 1, k1s, v1s, k0s, v0s)
   }
 #undef INFINI_FA_STEP
 
   if (act_a && __any(A.bad)) recompute_block<D>(A, ra, cx.kseg, cx.vseg);
   if (act_b && __any(B.bad)) recompute_block<D>(B, rb, cx.kseg, cx.vseg);
 
-  // The snapshot is in slot S0; slot S0^1 is free: start the next pass's tile 0.
-  if (next) {
-    issue_tile<D, false>(cx.kseg, cx.seg_bytes, kn, cx.wave, dof);
-    issue_tile<D, true>(cx.vseg, cx.seg_bytes, vn, cx.wave, dof);
-  }
   const float* zs = zc;
   const float* cs = zc + 256;
   const float inv_sc = 1.f / cx.sc;
   bf16* const stage = ostage + 2048 * cx.wave;
-  if (act_a) finish_block<D>(A, kc, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)ra * D, stage);
-  if (act_b) finish_block<D>(B, kc, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)rb * D, stage);
+  if (act_a) finish_block<D>(A, k0s, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)ra * D, stage);
+  if (act_b) finish_block<D>(B, k0s, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)rb * D, stage);
   wait_loads_and_sync();
 }
 
@@ -934,12 +928,19 @@ void fa_fwd_kernel(FaArgs a) {
   dof.init(threadIdx.x & 63);
   issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
   issue_tile<D, true>(cx.vseg, cx.seg_bytes, v0s, cx.wave, dof);
-  QRaw<D> qr;
-  load_q_rows<D>(qr.a, q_rows<D>(cx, qt0, 0));
-  load_q_rows<D>(qr.b, q_rows<D>(cx, qt0, 1));
   wait_loads_and_sync();
-  run_pass<D, 0>(cx, qt0, two, qr, k0s, v0s, k1s, v1s, zc, ostage, ad, dof);
-  if (two) run_pass<D, 1>(cx, qt1, false, qr, k0s, v0s, k1s, v1s, zc, ostage, ad, dof);
+  // One copy of the pass code serves both passes (the loop is not unrolled).
+  // Between them, the K part of tile 0 goes into k0s (free once the snapshot has
+  // been used) while the second pass's Q rows load; its V part is already in v0s.
+  const int npass = two ? 2 : 1;
+#pragma unroll 1
+  for (int p = 0; p < npass; ++p) {
+    run_pass<D>(cx, p == 0 ? qt0 : qt1, p + 1 < npass, k0s, v0s, k1s, v1s, zc, ostage, ad, dof);
+    if (p + 1 < npass) {
+      issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
+      wait_loads_and_sync();
+    }
+  }
 }
 
 int64_t fa_fwd_blocks(int64_t seg_heads, int N) {
