@@ -7,29 +7,30 @@
 // section 3.3; the gate of section 3.5.  The N x N score matrix never leaves
 // registers (chapter-24 page, section 24.1.2).
 //
-// Work decomposition.  One workgroup (4 waves, one per SIMD, one workgroup per
+// Work decomposition.  One workgroup (8 waves, two per SIMD, one workgroup per
 // CU) handles a pair of 256-row query tiles of one (b, h, segment): tile w and
-// tile NQ-1-w, so that every workgroup does the same causal work.  Each wave
-// owns two 32-row query blocks of a tile, rows 32 w + [0, 32) and 128 + 32 w +
-// [0, 32), so every K or V operand read from LDS feeds two MFMAs.  Per 32-key
-// block of a 128-key tile:
-//   S^T (32 keys x 32 queries) = K Q^T on v_mfma_f32_32x32x16_bf16 for both query
-//   blocks: each lane holds one query column, so the softmax statistics are per
-//   lane (one exchange with lane l^32 holds the rest of a row);
+// tile NQ-1-w, so that every workgroup does the same causal work.  Wave w owns
+// the 32-row query block 32 w + [0, 32) of a tile.  The two waves of a SIMD
+// interleave in hardware: while one runs its softmax (VALU) or waits for LDS,
+// the other keeps the matrix pipe busy.  Per 32-key block of a 128-key tile:
+//   S^T (32 keys x 32 queries) = K Q^T on v_mfma_f32_32x32x16_bf16: each lane
+//   holds one query column, so the softmax statistics are per lane (one
+//   exchange with lane l^32 holds the rest of a row);
 //   O^T (D x 32) += V^T P^T, with V^T read from the row-major V tile by
 //   ds_read_b64_tr_b16 and P^T taken straight from the S^T accumulators (the key
 //   order inside each 16-key step is permuted identically on both operands).
-// The S^T products of block j+1 are issued next to the softmax of block j.
+// Within a wave, the S^T products of block j+1 are issued next to the softmax
+// of block j.
 //
 // Data movement.  K and V tiles stream from HBM into LDS with buffer_load ... lds
-// (16 bytes per lane, no staging registers) through two LDS slots.  The load
-// sequence of a workgroup is: tiles of the first query tile, the memory snapshot
-// (M^T, z, colsum(M)), tiles of the second query tile, the snapshot again.  Item
-// i+1 is in flight while item i is used; every query tile covers an even number
-// of key-tile steps, so each item's slot is known at compile time (the loop is
-// unrolled by two) and the compiler never waits on a load into the other slot.
-// The slot layouts are XOR-swizzled so that the operand reads are free of bank
-// conflicts.
+// (16 bytes per lane, no staging registers) through two LDS slots; tile t of a
+// pass sits in slot t % 2 and the load of item t+1 is in flight while tile t is
+// used.  Every pass covers an even number of key tiles, so the last one uses
+// slot 1 and brings the memory snapshot (M^T, z, colsum(M)) into slot 0 along
+// with the V part of the next pass's tile 0; the slot of every load is known at
+// compile time (the step loop is unrolled by two), so the compiler never waits
+// on a load into the other slot.  The slot layouts are XOR-swizzled so that the
+// operand reads are free of bank conflicts.
 //
 // Softmax.  Each query keeps a reference maximum m, set before the tile loop to
 // the exact maximum of its first 32-key block (which always holds an unmasked
@@ -43,7 +44,8 @@
 //   sigma(q) M = colsum(M) + q' M   and   sigma(q) z = sum(z) + q' z,
 // where colsum(M) (sum over d_key) comes in fp32 with the snapshot and q' M runs
 // on MFMA from the bf16 snapshot of M_{s-1}^T.  q' keeps the full relative
-// precision of bf16, unlike sigma(q) ~ 1 + q itself.  Gate, round to bf16, store.
+// precision of bf16, unlike sigma(q) ~ 1 + q itself.  Gate, round to bf16, store
+// through LDS (slot 1 is free by then) as whole 128-byte row segments.
 #include "common.h"
 #include "kernels.h"
 
@@ -51,9 +53,9 @@ namespace infini {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 64 * kWaves;   // query rows per tile: two 32-row blocks per wave
+constexpr int kBM = 32 * kWaves;   // query rows per tile: one 32-row block per wave
 constexpr int kBN = 128;           // keys per LDS tile
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kDmaBlocks = 2;      // blocks of a tile that issue the next load item
@@ -65,9 +67,12 @@ struct FaLayout {
   static constexpr int TILE_ELEMS = kBN * D;           // one K or V tile, unpadded
   static constexpr int ROWS_PER_INSTR = 64 * 8 / D;    // rows one wave-wide 16-byte load covers
   static constexpr int NI = kBN / ROWS_PER_INSTR / kWaves;  // loads per wave, tensor and tile
-  static_assert(NI >= 1 && NI % kKB == 0, "tile loads must split evenly over the 32-key blocks");
+  static constexpr int KPER = 16 / ROWS_PER_INSTR;     // instructions per period of the K swizzle
+  static_assert(NI >= 1 && (2 * NI) % kDmaBlocks == 0, "tile loads must split evenly over the blocks");
+  static_assert(NI % KPER == 0, "each wave's first load starts a K swizzle period");
   static_assert(D <= kBN, "the snapshot of M^T must fit a K slot");
   static_assert(D <= 256, "z and colsum must fit their LDS array");
+  static_assert(kWaves * 32 * 64 * 2 <= 2 * TILE_ELEMS * 2, "the output stages must fit slot 1");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r (an XOR, so the same map
@@ -116,16 +121,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Per-lane byte offsets of the direct-to-LDS loads.  Wave-wide instruction ins
 // of a [kBN x D] tile fills bytes [1024 ins, 1024 ins + 1024) of the LDS tile;
-// the K swizzle repeats every 4 instructions and the V swizzle does not depend
-// on the instruction, so lane l's global offset is k[ins % 4] + 1024 (ins - ins
-// % 4) for K and v + 1024 ins for V (same row pitch in HBM and LDS).
+// the K swizzle repeats every KPER instructions and the V swizzle does not
+// depend on the instruction, so lane l's global offset is k[ins % KPER] + 1024
+// (ins - ins % KPER) for K and v + 1024 ins for V (same row pitch in HBM and LDS).
 template <int D>
 struct DmaOfs {
-  int k[4];
+  int k[FaLayout<D>::KPER];
   int v;
   __device__ __forceinline__ void init(int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) k[i] = 2 * tile_lane_offset<D, false>(i, lane);
+    for (int i = 0; i < FaLayout<D>::KPER; ++i) k[i] = 2 * tile_lane_offset<D, false>(i, lane);
     v = 2 * tile_lane_offset<D, true>(0, lane);
   }
 };
@@ -140,7 +145,7 @@ __device__ __forceinline__ void issue_part(int j0, const bf16* base, uint32_t by
                                            const DmaOfs<D>& dof) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist in the device pass only
   constexpr int NI = FaLayout<D>::NI;
-  static_assert(NI % 4 == 0, "K swizzle period");
+  constexpr int KPER = FaLayout<D>::KPER;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, bytes);
   // the LDS destination (M0) and the instruction's share of the offset are
   // wave-uniform: derive them in scalar registers
@@ -148,8 +153,8 @@ __device__ __forceinline__ void issue_part(int j0, const bf16* base, uint32_t by
 #pragma unroll
   for (int jj = 0; jj < CNT; ++jj) {
     const int j = j0 + jj;
-    const int ins = wv * NI + j;
-    const int voff = IS_V ? dof.v + 1024 * ins : dof.k[j & 3] + 1024 * (ins - (j & 3));
+    const int ins = wv * NI + j;   // ins % KPER == j % KPER (NI is a multiple of KPER)
+    const int voff = IS_V ? dof.v + 1024 * ins : dof.k[j % KPER] + 1024 * (ins - j % KPER);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (INFINI_LDS void*)(lds_tile + ins * 512), 16, voff, 0, 0, 0);
   }
 #endif
@@ -238,48 +243,20 @@ struct Prefetch {
   }
 };
 
-// S^T of one 32-key block (block j of the tile) for one or both query blocks;
-// the K operands are read once.
-template <int D, bool TWO>
-__device__ __forceinline__ void s_pair(f32x16& sa, f32x16& sb, const bf16* __restrict__ kt, int j,
-                                       const LdsAddr<D>& ad, const bf16x8 (&qa)[D / 16],
-                                       const bf16x8 (&qb)[D / 16]) {
+// S^T of key block j of the tile for one query block (K operands from LDS),
+// from a zero accumulator.
+template <int D>
+__device__ __forceinline__ f32x16 s_block(const bf16* __restrict__ kt, int j, const LdsAddr<D>& ad,
+                                          const bf16x8 (&q)[D / 16]) {
+  f32x16 s;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    sa[r] = 0.f;
-    if (TWO) sb[r] = 0.f;
-  }
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
   bf16x8 ka[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) ka[c] = lds_read8(kt + 32 * j * D + ad.kofs(c));
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    sa = mfma32(ka[c], qa[c], sa);
-    if (TWO) sb = mfma32(ka[c], qb[c], sb);
-  }
-}
-
-// O^T += V^T P^T for one 32-key block (block j of the tile), one or both query
-// blocks; the V operands are read once.
-template <int D, bool TWO>
-__device__ __forceinline__ void pv_pair(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ vt, int j,
-                                        const LdsAddr<D>& ad, const bf16x8 (&pa)[2], const bf16x8 (&pb)[2]) {
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    bf16x8 va[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16* p = vt + (32 * j + 16 * hf) * D + ad.v[db];
-      const s16x4 x = lds_read_tr16(p);
-      const s16x4 y = lds_read_tr16(p + 8 * D);
-      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      A.o[db] = mfma32(va[db], pa[hf], A.o[db]);
-      if (TWO) B.o[db] = mfma32(va[db], pb[hf], B.o[db]);
-    }
-  }
+  for (int c = 0; c < D / 16; ++c) s = mfma32(ka[c], q[c], s);
+  return s;
 }
 
 // Causal mask of a block whose first key is kb0: keys after the lane's query get -inf.
@@ -290,28 +267,6 @@ __device__ __forceinline__ void mask_block(f32x16& sacc, int kb0, int my_row) {
     const int key = kb0 + 8 * (r >> 2) + 4 * hi + (r & 3);
     if (key > my_row) sacc[r] = -__builtin_inff();
   }
-}
-
-// Softmax of one 32 x 32 block from s = score - m (the S^T chains start at -m):
-// probabilities, added to the denominator and packed to bf16 as the B operand
-// of PV.
-template <int D>
-__device__ __forceinline__ void softmax_block(QBlock<D>& X, const f32x16& s, bf16x8 (&p)[2]) {
-  f32x16 e;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) e[r] = exp2_fast(s[r]);   // s = scores - m (log2 domain)
-  float t[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) t[r] = e[r] + e[r + 8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) t[r] += t[r + 4];
-  const float sum = (t[0] + t[2]) + (t[1] + t[3]);
-  X.bad |= !(sum <= kSumLimit);
-  X.l += sum;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[hf][i] = f2bf(e[8 * hf + i]);
 }
 
 // Row maximum of a 32 x 32 score block (log2 domain: Q carries the scale); the
@@ -336,56 +291,6 @@ __device__ __forceinline__ void set_m(QBlock<D>& X, float m) {
   for (int r = 0; r < 16; ++r) X.mneg[r] = -m;
 }
 
-// Operand stages of the pipelined tile: K operands of one 32-key block (all D /
-// 16 steps), V^T operands of one 32-key block (both 16-key halves).
-template <int D>
-__device__ __forceinline__ void load_k(bf16x8 (&ko)[D / 16], const bf16* __restrict__ kt, int j,
-                                       const LdsAddr<D>& ad) {
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) ko[c] = lds_read8(kt + 32 * j * D + ad.kofs(c));
-}
-template <int D>
-__device__ __forceinline__ void load_v(bf16x8 (&vo)[2][D / 32], const bf16* __restrict__ vt, int j,
-                                       const LdsAddr<D>& ad) {
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16* p = vt + (32 * j + 16 * hf) * D + ad.v[db];
-      const s16x4 x = lds_read_tr16(p);
-      const s16x4 y = lds_read_tr16(p + 8 * D);
-      vo[hf][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-}
-// S^T - m for one 32-key block: the chains start from the -m accumulators, so
-// the result is the exp2 argument itself (Q carries the softmax scale).
-template <int D>
-__device__ __forceinline__ void s_mfma(f32x16& sa, f32x16& sb, const bf16x8 (&ko)[D / 16],
-                                       const QBlock<D>& A, const QBlock<D>& B) {
-  sa = mfma32(ko[0], A.q[0], A.mneg);
-  sb = mfma32(ko[0], B.q[0], B.mneg);
-#pragma unroll
-  for (int c = 1; c < D / 16; ++c) {
-    sa = mfma32(ko[c], A.q[c], sa);
-    sb = mfma32(ko[c], B.q[c], sb);
-  }
-}
-template <int D>
-__device__ __forceinline__ void s_mfma1(f32x16& sb, const bf16x8 (&ko)[D / 16], const QBlock<D>& B) {
-  sb = mfma32(ko[0], B.q[0], B.mneg);
-#pragma unroll
-  for (int c = 1; c < D / 16; ++c) sb = mfma32(ko[c], B.q[c], sb);
-}
-template <int D>
-__device__ __forceinline__ void pv_mfma(f32x16 (&o)[D / 32], const bf16x8 (&vo)[2][D / 32], const bf16x8 (&p)[2]) {
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vo[hf][db], p[hf], o[db]);
-}
-
-// Scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier).
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
 
 // Causal mask of a 32 x 32 score block by lane masks: element r of lane l holds
 // key 8 (r / 4) + 4 (l / 32) + r % 4 of the block for query l % 32, so the lanes
@@ -416,84 +321,70 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int kb, int r0) {
 #define INFINI_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // A 128-key tile through the software pipeline over its four 32-key blocks j.
-// One wave per SIMD issues in order, so MFMA and VALU work only overlap when
-// they alternate in the instruction stream: an MFMA occupies the matrix pipe for
-// 32 cycles, during which the wave issues the next few independent VALU or LDS
-// instructions.  Each block is written as two phases of slots, one MFMA per slot
+// A wave issues in order, so its own MFMA and VALU work only overlap when they
+// alternate in its instruction stream (the other wave of the SIMD fills what is
+// left).  Each block is written as two phases of slots, one MFMA per slot
 // followed by that slot's share of the other work:
-//   phase 1: S^T(j+1) MFMAs | softmax of block j (a few elements per slot) and the
-//            V^T operand reads of block j
-//   phase 2: O^T += V^T P^T MFMAs of block j | K operand reads of block j+2, the
-//            block's share of the next load item, the softmax sums
-// MASK_A / MASK_B: the tile holds the diagonal of that query block (blocks right
-// of it are fully masked); WITH_A = false: query block A sees none of the tile's
-// keys and is skipped.
-template <int D, bool MASK_A, bool MASK_B, bool WITH_A>
-__device__ __forceinline__ void tile_pipe(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
-                                          const bf16* __restrict__ vt, const LdsAddr<D>& ad,
-                                          const Prefetch<D>& pf, int k0, int ra, int rb) {
+//   phase 1: S^T(j+1) MFMAs | probabilities of block j (exp2, sums, bf16
+//            packing, a few elements per slot) and the V^T operand reads of
+//            block j
+//   phase 2: O^T += V^T P^T MFMAs of block j | K operand reads of block j+2 and
+//            the block's share of the next load item
+// MASK: the tile holds the diagonal of the query block starting at row r0
+// (blocks right of it are fully masked).
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_pipe(QBlock<D>& X, const bf16* __restrict__ kt, const bf16* __restrict__ vt,
+                                          const LdsAddr<D>& ad, const Prefetch<D>& pf, int k0, int r0) {
   constexpr int NI = FaLayout<D>::NI;          // prefetch instructions per tensor
   constexpr int DPB = 2 * NI / kDmaBlocks;     // prefetch instructions per block (K and V)
-  constexpr int KS = D / 16;                   // 16-deep steps of an S^T chain
-  constexpr int NV = D / 32;                   // O^T accumulators per query block
-  constexpr int NQ = WITH_A ? 2 : 1;           // query blocks
-  constexpr int N1 = NQ * KS;                  // phase-1 slots (S^T MFMAs)
-  constexpr int N2 = NQ * 2 * NV;              // phase-2 slots (O^T MFMAs)
-  constexpr int E = 16 * NQ / N1;              // softmax elements per phase-1 slot
+  constexpr int KS = D / 16;                   // 16-deep steps of an S^T chain = phase-1 slots
+  constexpr int NV = D / 32;                   // O^T accumulators
+  constexpr int N2 = 2 * NV;                   // phase-2 slots (O^T MFMAs)
+  constexpr int E = 16 / KS;                   // softmax elements per phase-1 slot
   constexpr int DPS = (DPB + N2 - 1) / N2;     // prefetch instructions per phase-2 slot
-  static_assert(2 * NV <= N1 && KS <= N2 && (2 * NI) % kDmaBlocks == 0, "slot shares");
+  static_assert(2 * NV <= KS && KS <= N2, "slot shares");
   bf16x8 ko[KS];
   bf16x8 vo[2][NV];
-  f32x16 sa, sb;   // S^T - m of the current block
-  load_k<D>(ko, kt, 0, ad);
-  if (WITH_A) s_mfma<D>(sa, sb, ko, A, B);
-  else s_mfma1<D>(sb, ko, B);
-  load_k<D>(ko, kt, 1, ad);
+  f32x16 s;   // S^T - m of the current block
+#pragma unroll
+  for (int c = 0; c < KS; ++c) ko[c] = lds_read8(kt + ad.kofs(c));
+  s = mfma32(ko[0], X.q[0], X.mneg);
+#pragma unroll
+  for (int c = 1; c < KS; ++c) s = mfma32(ko[c], X.q[c], s);
+#pragma unroll
+  for (int c = 0; c < KS; ++c) ko[c] = lds_read8(kt + 32 * D + ad.kofs(c));
   INFINI_FENCE();
 #pragma unroll
   for (int j = 0; j < kKB; ++j) {
     const bool more = j + 1 < kKB;
-    if (MASK_A) mask_scores(sa, k0 + 32 * j, ra);
-    if (MASK_B) mask_scores(sb, k0 + 32 * j, rb);
-    f32x16 na, nb;
-    bf16x8 pa[2], pb[2];
-    float ta = 0.f, tb = 0.f;
+    if (MASK) mask_scores(s, k0 + 32 * j, r0);
+    f32x16 ns;
+    bf16x8 p[2];
+    float t = 0.f;
     INFINI_FENCE();
 #pragma unroll
-    for (int i = 0; i < N1; ++i) {
-      if (more) {
-        const int c = i / NQ;
-        if (WITH_A && i % 2 == 0) na = mfma32(ko[c], A.q[c], c == 0 ? A.mneg : na);
-        else nb = mfma32(ko[c], B.q[c], c == 0 ? B.mneg : nb);
-      }
+    for (int i = 0; i < KS; ++i) {
+      if (more) ns = mfma32(ko[i], X.q[i], i == 0 ? X.mneg : ns);
       if (i < 2 * NV) {
         const int hf = i / NV, db = i % NV;
-        const bf16* p = vt + (32 * j + 16 * hf) * D + ad.v[db];
-        const s16x4 x = lds_read_tr16(p);
-        const s16x4 y = lds_read_tr16(p + 8 * D);
+        const bf16* pv = vt + (32 * j + 16 * hf) * D + ad.v[db];
+        const s16x4 x = lds_read_tr16(pv);
+        const s16x4 y = lds_read_tr16(pv + 8 * D);
         vo[hf][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int u = 0; u < E; ++u) {
-        const int g = E * i + u;            // element g of [A's 16, B's 16] (or B's 16 alone)
-        const bool in_a = WITH_A && g < 16;
-        const int r = in_a ? g : g % 16;
-        const float e = exp2_fast(in_a ? sa[r] : sb[r]);
-        if (in_a) {
-          ta += e;
-          pa[r / 8][r % 8] = f2bf(e);
-        } else {
-          tb += e;
-          pb[r / 8][r % 8] = f2bf(e);
-        }
+        const int r = E * i + u;
+        const float e = exp2_fast(s[r]);
+        t += e;
+        p[r / 8][r % 8] = f2bf(e);
       }
       INFINI_FENCE();
     }
 #pragma unroll
     for (int i = 0; i < N2; ++i) {
-      const int hf = (i / NV) % 2, db = i % NV;
-      if (WITH_A && i < 2 * NV) A.o[db] = mfma32(vo[hf][db], pa[hf], A.o[db]);
-      else B.o[db] = mfma32(vo[hf][db], pb[hf], B.o[db]);
+      const int hf = i / NV, db = i % NV;
+      X.o[db] = mfma32(vo[hf][db], p[hf], X.o[db]);
       if (j + 2 < kKB && i < KS) ko[i] = lds_read8(kt + 32 * (j + 2) * D + ad.kofs(i));
       if (j < kDmaBlocks) {
 #pragma unroll
@@ -504,82 +395,22 @@ __device__ __forceinline__ void tile_pipe(QBlock<D>& A, QBlock<D>& B, const bf16
         }
       }
       if (i == 0) {
-        if (WITH_A) {
-          A.bad |= !(ta <= kSumLimit);
-          A.l += ta;
-        }
-        B.bad |= !(tb <= kSumLimit);
-        B.l += tb;
+        X.bad |= !(t <= kSumLimit);
+        X.l += t;
       }
       INFINI_FENCE();
     }
-    if (more) {
-      if (WITH_A) sa = na;
-      sb = nb;
-    }
+    if (more) s = ns;
   }
 }
 
-// A tile that crosses the diagonal of a query block: per 32-key block, only the
-// active query blocks that see some of its keys, with the causal mask on the
-// diagonal block.  Query block rows start at ra < rb (multiples of 32); the
-// block with first key kb is needed when kb <= r.
+// Reference maximum before the tile loop: the exact row maximum of key block 0,
+// the first block every query sees (tile 0 is in LDS).
 template <int D>
-__device__ __forceinline__ void tile_diag(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
-                                          const bf16* __restrict__ vt, const LdsAddr<D>& ad, float sc, int k0,
-                                          int ra, int rb, bool act_a, bool act_b) {
-  const int l32 = threadIdx.x & 31;
-#pragma unroll
-  for (int j = 0; j < kKB; ++j) {
-    const int kb = k0 + 32 * j;
-    const bool need_a = act_a && kb <= ra;
-    const bool need_b = act_b && kb <= rb;
-    if (!need_a && !need_b) break;  // later blocks start even further right
-    f32x16 sa, sb;
-    bf16x8 pa[2], pb[2];
-    if (need_a && need_b) {
-      s_pair<D, true>(sa, sb, kt, j, ad, A.q, B.q);
-      sub_m(sa, A.m);
-      sub_m(sb, B.m);
-      if (kb == ra) mask_block(sa, kb, ra + l32);
-      if (kb == rb) mask_block(sb, kb, rb + l32);
-      softmax_block<D>(A, sa, pa);
-      softmax_block<D>(B, sb, pb);
-      pv_pair<D, true>(A, B, vt, j, ad, pa, pb);
-    } else if (need_a) {  // query block B inactive
-      s_pair<D, false>(sa, sb, kt, j, ad, A.q, A.q);
-      sub_m(sa, A.m);
-      if (kb == ra) mask_block(sa, kb, ra + l32);
-      softmax_block<D>(A, sa, pa);
-      pv_pair<D, false>(A, A, vt, j, ad, pa, pa);
-    } else {              // block j lies right of block A's rows
-      s_pair<D, false>(sb, sa, kt, j, ad, B.q, B.q);
-      sub_m(sb, B.m);
-      if (kb == rb) mask_block(sb, kb, rb + l32);
-      softmax_block<D>(B, sb, pb);
-      pv_pair<D, false>(B, B, vt, j, ad, pb, pb);
-    }
-  }
-}
-
-// Reference maxima before the tile loop: the exact row maxima of key block 0,
-// the first block every query sees (tile 0 is in LDS).  ra < rb.
-template <int D>
-__device__ __forceinline__ void init_m(QBlock<D>& A, QBlock<D>& B, const bf16* __restrict__ kt,
-                                       const LdsAddr<D>& ad, int ra, int rb, bool act_a, bool act_b) {
-  const int l32 = threadIdx.x & 31;
-  f32x16 sa, sb;
-  if (act_b) {
-    s_pair<D, true>(sa, sb, kt, 0, ad, A.q, B.q);
-    if (rb == 0) mask_block(sb, 0, l32);
-    set_m(B, block_row_max(sb));
-  } else if (act_a) {
-    s_pair<D, false>(sa, sb, kt, 0, ad, A.q, A.q);
-  }
-  if (act_a) {
-    if (ra == 0) mask_block(sa, 0, l32);
-    set_m(A, block_row_max(sa));
-  }
+__device__ __forceinline__ void init_m(QBlock<D>& X, const bf16* __restrict__ kt, const LdsAddr<D>& ad, int r0) {
+  f32x16 s = s_block<D>(kt, 0, ad, X.q);
+  if (r0 == 0) mask_block(s, 0, threadIdx.x & 31);
+  set_m(X, block_row_max(s));
 }
 
 // Slow, exact recompute of one query block whose sums left the safe range: two
@@ -749,20 +580,13 @@ struct FaCtx {
   float g, sc;
 };
 
-// Q rows of this wave's two query blocks of query tile qt, as loaded (bf16).
-template <int D>
-struct QRaw {
-  bf16x8 a[D / 16];
-  bf16x8 b[D / 16];
-};
-
-// Row pointers for the Q loads of query tile qt (element 8 hi of the lane's
-// row of each block).  A block past the segment end reads the first rows
+// Row pointer for the Q loads of this wave's block of query tile qt (element 8 hi
+// of the lane's row).  A block past the segment end reads the first rows
 // instead (its results are never used), so the loads need no branch.
 template <int D>
-__device__ __forceinline__ const bf16* q_rows(const FaCtx<D>& cx, int qt, int half) {
+__device__ __forceinline__ const bf16* q_rows(const FaCtx<D>& cx, int qt) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-  const int r = qt * kBM + half * (kBM / 2) + 32 * cx.wave;
+  const int r = qt * kBM + 32 * cx.wave;
   return cx.qb + (int64_t)(r < cx.N ? r + l32 : l32) * D + 8 * hi;
 }
 
@@ -796,47 +620,32 @@ __device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int 
 // (k0s/v0s, k1s/v1s); every pass has an even number of steps, so the last one
 // uses slot 1 and brings the snapshot of M^T into k0s (with z and colsum into
 // zc) and, with `next` set, the V part of the next pass's tile 0 into v0s.  On
-// entry tile 0 is in slot 0 and the Q rows are in qr (waited for and
-// synchronised).
+// entry tile 0 is in slot 0 (waited for and synchronised).
 template <int D>
-__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, bf16* k0s,
-                                         bf16* v0s, bf16* k1s, bf16* v1s, float* zc, bf16* ostage,
-                                         const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
-  const int lane = threadIdx.x & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, bf16* k0s, bf16* v0s, bf16* k1s,
+                                         bf16* v1s, float* zc, const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
   const int q0 = qt * kBM;
-  const int ra = q0 + 32 * cx.wave;          // first rows of the two query blocks
-  const int rb = ra + kBM / 2;
-  const bool act_a = ra < cx.N;
-  const bool act_b = rb < cx.N;
+  const int r0 = q0 + 32 * cx.wave;          // first row of this wave's query block
+  const bool act = r0 < cx.N;
   const int last = min(cx.nk - 1, (q0 + kBM - 1) / kBN);
   const int nsteps = (last + 2) & ~1;        // even: pads with a tile beyond the segment
 
-  QBlock<D> A, B;
+  QBlock<D> X;
   // Q^T * scale * log2 e (rounded to bf16): the scores come out in the log2 domain
-  QRaw<D> qr;
-  load_q_rows<D>(qr.a, q_rows<D>(cx, qt, 0));
-  load_q_rows<D>(qr.b, q_rows<D>(cx, qt, 1));
+  bf16x8 qr[D / 16];
+  load_q_rows<D>(qr, q_rows<D>(cx, qt));
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      A.q[c][i] = f2bf(bf2f(qr.a[c][i]) * cx.sc);
-      B.q[c][i] = f2bf(bf2f(qr.b[c][i]) * cx.sc);
-    }
+    for (int i = 0; i < 8; ++i) X.q[c][i] = f2bf(bf2f(qr[c][i]) * cx.sc);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      A.o[db][r] = 0.f;
-      B.o[db][r] = 0.f;
-    }
-  set_m(A, 0.f);
-  set_m(B, 0.f);
-  A.l = B.l = 0.f;
-  A.bad = B.bad = false;
-  init_m<D>(A, B, k0s, ad, ra, rb, act_a, act_b);
+    for (int r = 0; r < 16; ++r) X.o[db][r] = 0.f;
+  set_m(X, 0.f);
+  X.l = 0.f;
+  X.bad = false;
+  if (act) init_m<D>(X, k0s, ad, r0);
 
   // Step t uses slot t % 2 and loads item t+1 into the other slot.
 #define INFINI_FA_STEP(T, KC, VC, KN, VN)                                                        \
@@ -848,17 +657,12 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
       issue_row(cx.snapc, D * 4, zc + 256);                                                      \
     }                                                                                            \
     const int k0_ = t_ * kBN;                                                                    \
-    if (act_a && k0_ + kBN <= ra) {                                                              \
-      tile_pipe<D, false, false, true>(A, B, KC, VC, ad, pf_, k0_, ra, rb);               \
-    } else if (act_b && k0_ <= ra && ra < k0_ + kBN) {                                          \
-      tile_pipe<D, true, false, true>(A, B, KC, VC, ad, pf_, k0_, ra, rb);                \
-    } else if (act_b && ra < k0_ && k0_ <= rb && rb < k0_ + kBN) {                              \
-      tile_pipe<D, false, true, false>(A, B, KC, VC, ad, pf_, k0_, ra, rb);               \
-    } else {                                                                                     \
+    if (act && k0_ + kBN <= r0)                                                                  \
+      tile_pipe<D, false>(X, KC, VC, ad, pf_, k0_, r0);                                          \
+    else if (act && k0_ <= r0 && r0 < k0_ + kBN)                                                 \
+      tile_pipe<D, true>(X, KC, VC, ad, pf_, k0_, r0);                                           \
+    else                                                                                         \
       pf_.template issue<FaLayout<D>::NI>(0);                                                    \
-      if ((act_b && k0_ <= rb) || (act_a && k0_ <= ra))                                          \
-        tile_diag<D>(A, B, KC, VC, ad, cx.sc, k0_, ra, rb, act_a, act_b);                       \
-    }                                                                                            \
     wait_loads_and_sync();                                                                       \
   }
   for (int t = 0; t < nsteps; t += 2) {
@@ -867,15 +671,11 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
   }
 #undef INFINI_FA_STEP
 
-  if (act_a && __any(A.bad)) recompute_block<D>(A, ra, cx.kseg, cx.vseg);
-  if (act_b && __any(B.bad)) recompute_block<D>(B, rb, cx.kseg, cx.vseg);
+  if (act && __any(X.bad)) recompute_block<D>(X, r0, cx.kseg, cx.vseg);
 
-  const float* zs = zc;
-  const float* cs = zc + 256;
-  const float inv_sc = 1.f / cx.sc;
-  bf16* const stage = ostage + 2048 * cx.wave;
-  if (act_a) finish_block<D>(A, k0s, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)ra * D, stage);
-  if (act_b) finish_block<D>(B, k0s, zs, cs, ad, cx.has_memory, cx.g, inv_sc, cx.ob + (int64_t)rb * D, stage);
+  // slot 1 is free after the last step: 4 KB of output stage per wave
+  bf16* const stage = (cx.wave < 4 ? k1s : v1s) + 2048 * (cx.wave & 3);
+  if (act) finish_block<D>(X, k0s, zc, zc + 256, ad, cx.has_memory, cx.g, 1.f / cx.sc, cx.ob + (int64_t)r0 * D, stage);
   wait_loads_and_sync();
 }
 
@@ -888,7 +688,6 @@ void fa_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 k1s[L::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 v1s[L::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) float zc[512];   // z at [0, D), colsum(M) at [256, 256 + D)
-  __shared__ __attribute__((aligned(1024))) bf16 ostage[kWaves * 2048];   // output stage, 4 KB per wave
 
   const int npair = (a.nq + 1) / 2;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -931,11 +730,11 @@ void fa_fwd_kernel(FaArgs a) {
   wait_loads_and_sync();
   // One copy of the pass code serves both passes (the loop is not unrolled).
   // Between them, the K part of tile 0 goes into k0s (free once the snapshot has
-  // been used) while the second pass's Q rows load; its V part is already in v0s.
+  // been used); its V part is already in v0s.
   const int npass = two ? 2 : 1;
 #pragma unroll 1
   for (int p = 0; p < npass; ++p) {
-    run_pass<D>(cx, p == 0 ? qt0 : qt1, p + 1 < npass, k0s, v0s, k1s, v1s, zc, ostage, ad, dof);
+    run_pass<D>(cx, p == 0 ? qt0 : qt1, p + 1 < npass, k0s, v0s, k1s, v1s, zc, ad, dof);
     if (p + 1 < npass) {
       issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
       wait_loads_and_sync();
