@@ -478,7 +478,10 @@ __device__ __forceinline__ void load_q_rows(bf16x8 (&q)[D / 16], const bf16* __r
 
 // Retrieval, gate and store of one query block.  mt: M^T snapshot (K-slot
 // layout), zs / cs: z and colsum(M) in LDS, ob: the block's first output row,
-// stage: this wave's 4 KB of LDS for the output.
+// stage: this wave's 4 KB of LDS for the output.  First q' and the denominator
+// for all of d_key; then, one 32-column group of d_value at a time, the
+// retrieval accumulator (colsum + M^T q'), the gate and the output, so that only
+// one group's accumulator is live.
 template <int D>
 __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __restrict__ mt,
                                              const float* __restrict__ zs, const float* __restrict__ cs,
@@ -487,29 +490,14 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
   const float l_tot = X.l + __shfl_xor(X.l, 32);
   const float inv_l = 1.f / l_tot;
-  f32x16 am[D / 32];
+  bf16x8 qp[D / 16];                   // q' = sigma(q) - 1 (bf16), the B operand of M^T q'
   float den = 0.f;
   if (has_memory) {
-    // accumulator starts at colsum(M)[d_value of each element]
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 c4 = *(const INFINI_LDS f32x4*)(cs + 32 * db + 8 * j + 4 * hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) am[db][4 * j + e] = c4[e];
-      }
     float zpart = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      // operand reads first: their latency hides behind the q' arithmetic
-      bf16x8 ma[D / 32];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) ma[db] = lds_read8(mt + 32 * db * D + ad.kofs(c));
       const f32x4 z0 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi);
       const f32x4 z1 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 qp;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = bf2f(X.q[c][i]) * inv_sc;       // q (the registers hold q * scale * log2 e)
@@ -517,19 +505,11 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
         const float zz = i < 4 ? z0[i] : z1[i - 4];
         den = __builtin_fmaf(f, zz, den);
         zpart += zz;
-        qp[i] = f2bf(f);
+        qp[c][i] = f2bf(f);
       }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) am[db] = mfma32(ma[db], qp, am[db]);
-      __builtin_amdgcn_sched_barrier(0);
     }
     den += zpart;                      // sum(z) over this lane's half of d_key
     den += __shfl_xor(den, 32);
-  } else {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) am[db][r] = 0.f;
   }
   // lane holds row l32 of the block, values d = 32db + 8j + 4hi + 0..3
   const float inv_den = (has_memory && den > 0.f) ? 1.f / den : 0.f;
@@ -544,17 +524,36 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
 #pragma unroll
   for (int h = 0; h < D / 64; ++h) {
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
+    for (int dh = 0; dh < 2; ++dh) {
+      const int db = 2 * h + dh;
+      f32x16 am;
+      if (has_memory) {
+        // accumulator starts at colsum(M)[d_value of each element]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 c4 = *(const INFINI_LDS f32x4*)(cs + 32 * db + 8 * j + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) am[4 * j + e] = c4[e];
+        }
+        bf16x8 ma[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) ma[c] = lds_read8(mt + 32 * db * D + ad.kofs(c));
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) am = mfma32(ma[c], qp[c], am);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am[r] = 0.f;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int db = 2 * h + dh;
         bf16x4 outv;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[db][4 * j + e] * wg_mem));
+          outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[4 * j + e] * wg_mem));
         const int chunk = (4 * dh + j) ^ ((l32 >> 1) & 7);
         *(INFINI_LDS bf16x4*)(stage + l32 * 64 + 8 * chunk + 4 * hi) = outv;
       }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * i + (lane >> 3), c = lane & 7;
