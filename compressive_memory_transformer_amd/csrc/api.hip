@@ -192,9 +192,7 @@ int run_f32(infini_attn_state* st, const void* q, const void* k, const void* v, 
 
 int zero_state(infini_attn_state* st, float* M, float* z, hipStream_t stream) {
   const int64_t BH = (int64_t)st->batch * st->heads;
-  hipError_t e = infini::launch_fill_zero(M, BH * st->d_key * st->d_value, stream);
-  if (e != hipSuccess) return hip_fail(e, "fill launch");
-  e = infini::launch_fill_zero(z, BH * st->d_key, stream);
+  const hipError_t e = infini::launch_fill_zero(M, BH * st->d_key * st->d_value, z, BH * st->d_key, stream);
   if (e != hipSuccess) return hip_fail(e, "fill launch");
   return INFINI_OK;
 }

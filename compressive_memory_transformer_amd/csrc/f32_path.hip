@@ -163,9 +163,12 @@ void f32_znorm_kernel(F32UpdateArgs a) {
   a.z[i] += acc;
 }
 
-__global__ void fill_zero_kernel(float* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0.f;
+// Zeroes p[0, n) and p2[0, n2) (two ranges in one launch).
+__global__ void fill_zero_kernel(float* p, int64_t n, float* p2, int64_t n2) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n + n2; i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < n) p[i] = 0.f;
+    else p2[i - n] = 0.f;
+  }
 }
 
 hipError_t launch_f32_attn(const F32AttnArgs& a, hipStream_t stream) {
@@ -191,11 +194,12 @@ hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int64_t want = (n + kThreads - 1) / kThreads;
+hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream) {
+  if (n < 0 || n2 < 0) return hipErrorInvalidValue;
+  if (n + n2 == 0) return hipSuccess;
+  const int64_t want = (n + n2 + kThreads - 1) / kThreads;
   const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, stream, p, n);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, stream, p, n, p2, n2);
   return hipGetLastError();
 }
 

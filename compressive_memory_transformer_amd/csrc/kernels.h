@@ -109,7 +109,7 @@ struct F32UpdateArgs {
 };
 hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream);
 
-// Zero n floats.
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+// Zero n floats at p and n2 floats at p2 (one launch).
+hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);
 
 }  // namespace infini

@@ -143,15 +143,20 @@ void lin_contrib_kernel(LinContribArgs a) {
 }
 
 // Exclusive prefix over segments.  One thread per element of M^T; the last
-// workgroup of each head carries z.  Each snapshot also gets the fp32 column sums
-// of M over d_key (row sums of M^T), reduced in a fixed order.
+// workgroup of each head carries z.  The contributions of the next kPf segments
+// are loaded while the current kPf are folded in, so the chain over segments
+// runs at arithmetic speed instead of one memory latency per segment.  Each
+// snapshot also gets the fp32 column sums of M over d_key (row sums of M^T),
+// reduced in a fixed order (wave sums, then the waves of a row in order).
+constexpr int kPf = 16;
+
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void lin_scan_kernel(LinScanArgs a) {
   constexpr int MB = D * D / kThreads;     // workgroups holding M^T per head
   constexpr int WPR = D / 64;              // waves per row of M^T
   static_assert(D * D % kThreads == 0 && D % 64 == 0, "shape");
-  __shared__ float red[2][kThreads / 64];
+  __shared__ float red[kPf][kThreads / 64];
   const int bh = blockIdx.x / (MB + 1);
   const int sub = blockIdx.x % (MB + 1);
   const int64_t base = (int64_t)bh * a.S;
@@ -159,9 +164,21 @@ void lin_scan_kernel(LinScanArgs a) {
     const int dk = threadIdx.x;
     if (dk >= D) return;
     float run = a.z[(int64_t)bh * D + dk];
-    for (int s = 0; s < a.S; ++s) {
-      a.snapz[(base + s) * D + dk] = run;
-      run += a.cz[(base + s) * D + dk];
+    float cur[kPf], nxt[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) cur[i] = i < a.S ? a.cz[(base + i) * D + dk] : 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += kPf) {
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) nxt[i] = s0 + kPf + i < a.S ? a.cz[(base + s0 + kPf + i) * D + dk] : 0.f;
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) {
+        if (s0 + i < a.S) {
+          a.snapz[(base + s0 + i) * D + dk] = run;
+          run += cur[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) cur[i] = nxt[i];
     }
     a.z[(int64_t)bh * D + dk] = run;
     return;
@@ -169,20 +186,36 @@ void lin_scan_kernel(LinScanArgs a) {
   const int e = sub * kThreads + threadIdx.x;
   const int dv = e / D, dk = e % D;
   const int wave = threadIdx.x >> 6;
+  const float* __restrict__ cm = a.cM + base * D * D + e;
   float run = a.M[(int64_t)bh * D * D + dk * D + dv];
-  for (int s = 0; s < a.S; ++s) {
-    const int64_t sh = base + s;
-    a.snapM[sh * D * D + e] = f2bf(run);
-    const float part = wave_sum(run);
-    if ((threadIdx.x & 63) == 0) red[s & 1][wave] = part;
+  float cur[kPf], nxt[kPf];
+#pragma unroll
+  for (int i = 0; i < kPf; ++i) cur[i] = i < a.S ? cm[(int64_t)i * D * D] : 0.f;
+  for (int s0 = 0; s0 < a.S; s0 += kPf) {
+#pragma unroll
+    for (int i = 0; i < kPf; ++i)
+      nxt[i] = s0 + kPf + i < a.S ? cm[(int64_t)(s0 + kPf + i) * D * D] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) {
+      if (s0 + i < a.S) {
+        a.snapM[(base + s0 + i) * D * D + e] = f2bf(run);
+        const float part = wave_sum(run);
+        if ((threadIdx.x & 63) == 0) red[i][wave] = part;
+        run += cur[i];
+      }
+    }
     __syncthreads();
     if (threadIdx.x % D == 0) {
-      float c = 0.f;
+      for (int i = 0; i < kPf && s0 + i < a.S; ++i) {
+        float c = 0.f;
 #pragma unroll
-      for (int w = 0; w < WPR; ++w) c += red[s & 1][wave + w];
-      a.snapc[sh * D + dv] = c;
+        for (int w = 0; w < WPR; ++w) c += red[i][wave + w];
+        a.snapc[(base + s0 + i) * D + dv] = c;
+      }
     }
-    run += a.cM[sh * D * D + e];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) cur[i] = nxt[i];
   }
   a.M[(int64_t)bh * D * D + dk * D + dv] = run;
 }
