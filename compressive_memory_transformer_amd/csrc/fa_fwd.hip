@@ -487,7 +487,12 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
                                              const float* __restrict__ zs, const float* __restrict__ cs,
                                              const LdsAddr<D>& ad, bool has_memory, float g, float inv_sc,
                                              bf16* __restrict__ ob, bf16* __restrict__ stage) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  // The lane index is made opaque here so that the per-lane addresses below are
+  // computed in the epilogue instead of being hoisted to the kernel start and
+  // kept live (spilled) across the tile loop.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hi = lane >> 5;
   const float l_tot = X.l + __shfl_xor(X.l, 32);
   const float inv_l = 1.f / l_tot;
   bf16x8 qp[D / 16];                   // q' = sigma(q) - 1 (bf16), the B operand of M^T q'
@@ -498,9 +503,15 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
     for (int c = 0; c < D / 16; ++c) {
       const f32x4 z0 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi);
       const f32x4 z1 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi + 4);
+      // unpacked from the packed operand registers (opaque, so the compiler does
+      // not keep separate unpacked copies of Q alive through the tile loop)
+      u32x4 qw = __builtin_bit_cast(u32x4, X.q[c]);
+      asm volatile("" : "+v"(qw));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = bf2f(X.q[c][i]) * inv_sc;       // q (the registers hold q * scale * log2 e)
+        const unsigned wq = qw[i / 2];
+        const float qs = __builtin_bit_cast(float, (i & 1) ? (wq & 0xffff0000u) : (wq << 16));
+        const float x = qs * inv_sc;                    // q (the registers hold q * scale * log2 e)
         const float f = x > 0.f ? x : exp_e(x) - 1.f;   // q' = sigma(q) - 1
         const float zz = i < 4 ? z0[i] : z1[i - 4];
         den = __builtin_fmaf(f, zz, den);
