@@ -24,47 +24,137 @@ __device__ __forceinline__ bf16 lo_part(float x, bf16 hi) { return f2bf(x - bf2f
 }  // namespace
 
 // =================================================================== linear
-// One workgroup per (b, h, s, 32-column block of d_key).  sigma(K) of the block
-// is computed once per element (split into bf16 hi + lo) and staged in LDS with
-// V (row-major); the contraction over tokens reads both operands transposed with
-// ds_read_b64_tr_b16.  Output C^T[d_value][d_key block] on
-// v_mfma_f32_32x32x16_bf16, plus c[d_key block] = sum_t sigma(K_t).  The next
-// 64-token tile is prefetched into registers while the current one is used.
+// One workgroup (8 waves) per (b, h, s) and 64-column block of d_key; the two
+// blocks of a segment (d = 128) run on the same XCD and share its V through L2.
+// 64-token stages of K (this block's columns) and V stream into a 4-slot LDS
+// ring with buffer_load ... lds (three stages in flight).  Per stage each thread
+// turns 8 elements of K into sigma(K), split into bf16 hi + lo, written to LDS in
+// the layout of the transposing operand reads; then C^T[d_value][d_key] +=
+// V^T sigma(K) on v_mfma_f32_32x32x16_bf16 (hi and lo products into one fp32
+// accumulator), one 32 x 32 output tile per wave (d = 128; at d = 64 two waves
+// share a tile, taking alternate 16-token steps).  c = sum_t sigma(K_t) is
+// reduced over the workgroup at the end in a fixed order.
+namespace {
+constexpr int kLcWaves = 8;
+constexpr int kLcThreads = 64 * kLcWaves;
+constexpr int kLcKb = 64;        // d_key columns per workgroup
+constexpr int kLcTt = 64;        // tokens per stage
+constexpr int kLcStages = 4;     // ring slots
+
+// Physical 16-byte chunk of logical chunk c in row r of a [tokens x P] tile read
+// by ds_read_b64_tr_b16 (P = 128 or 64 elements): a 32-lane half of a read covers
+// 4 consecutive rows x 4 chunks, and rows r % 4 (P = 128) or (r / 2) % 2 (P = 64)
+// move them to disjoint groups of 4 chunks.
+template <int P>
+__device__ __forceinline__ int lc_chunk(int r, int c) { return c ^ (P == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2); }
+
+// Element offset (relative to a 16-token step) of this lane's first transposing
+// read for 32-column block cb of a [tokens x P] tile; the second read is 8 rows
+// further.  Lane l gets column 32 cb + l % 32 of tokens {4 hi + e, 8 + 4 hi + e}.
+template <int P>
+__device__ __forceinline__ int lc_tr_offset(int lane, int cb) {
+  const int hi = lane >> 5, grp = lane >> 4, sidx = lane & 15;
+  const int row = 4 * hi + (sidx >> 2);
+  const int col = 32 * cb + 16 * (grp & 1) + 4 * (sidx & 3);
+  return row * P + 8 * lc_chunk<P>(row, col >> 3) + (col & 7);
+}
+
+template <int P>
+__device__ __forceinline__ bf16x8 lc_read_tr(const bf16* tile, int ofs) {
+  const s16x4 x = lds_read_tr16(tile + ofs);
+  const s16x4 y = lds_read_tr16(tile + ofs + 8 * P);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lc_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+#endif
+
+// Direct-to-LDS loads of stage q (tokens [64 q, 64 q + 64) of the segment; zeros
+// past its end): this wave's share of the K block (one 1 KB load: 8 rows x 128 B,
+// row-major) and of V (1 KB loads of 1024 / (2 D) rows each, swizzled).
 template <int D>
-__global__ __launch_bounds__(kThreads, 2)
+__device__ __forceinline__ void lc_issue(const bf16* kseg, const bf16* vseg, int N, int q, int dkb, bf16* ks,
+                                         bf16* vs, int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int VI = kLcTt * D * 2 / 1024 / kLcWaves;   // V loads per wave and stage
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int t0 = q * kLcTt;
+  const uint32_t rows = t0 < N ? (uint32_t)(N - t0) : 0u;
+  {
+    const __amdgpu_buffer_rsrc_t r = lc_rsrc(kseg + (int64_t)(t0 < N ? t0 : 0) * D, rows * D * 2);
+    const int row = 8 * wv + lane / 8;
+    const int off = 2 * (row * D + dkb * kLcKb + 8 * (lane % 8));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (INFINI_LDS void*)(ks + wv * 512), 16, off, 0, 0, 0);
+  }
+  {
+    constexpr int RPI = 512 / D;   // rows per 1 KB load
+    const __amdgpu_buffer_rsrc_t r = lc_rsrc(vseg + (int64_t)(t0 < N ? t0 : 0) * D, rows * D * 2);
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int ins = VI * wv + j;
+      const int row = RPI * ins + lane / (D / 8);
+      const int phys = lane % (D / 8);
+      const int off = 2 * (row * D + 8 * lc_chunk<D>(row, phys));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (INFINI_LDS void*)(vs + ins * 512), 16, off, 0, 0, 0);
+    }
+  }
+#endif
+}
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(kLcThreads, 1)
 void lin_contrib_kernel(LinContribArgs a) {
-  constexpr int KB = 32;               // d_key columns per workgroup
-  constexpr int NKB = D / KB;
-  constexpr int KP = KB + 16;          // sigma(K) tile pitch: 4 rows x 32 B of a tr16 group on distinct banks
-  constexpr int VP = D + 16;           // V tile pitch
-  constexpr int VCH = D / 8;           // 16-byte chunks per V row
-  constexpr int VPT = 64 * VCH / kThreads;
-  constexpr int NDVB = D / 32;         // 32-row blocks of d_value = output blocks
-  constexpr int WPB = 4 / NDVB;        // waves sharing one output block (token-interleaved)
-  __shared__ __attribute__((aligned(16))) bf16 khi[64 * KP];
-  __shared__ __attribute__((aligned(16))) bf16 klo[64 * KP];
-  __shared__ __attribute__((aligned(16))) bf16 vt[64 * VP];
-  __shared__ float zred[64][KB + 1];
+  constexpr int NKB = D / kLcKb;                 // d_key blocks per segment
+  constexpr int KT = kLcTt * kLcKb;              // elements of a K stage
+  constexpr int VT = kLcTt * D;                  // elements of a V stage
+  constexpr int NDV = D / 32;                    // 32-row blocks of d_value
+  constexpr int TILES = NDV * (kLcKb / 32);      // output tiles per workgroup
+  constexpr int SHARE = kLcWaves / TILES;        // waves per tile (token steps interleaved)
+  constexpr int NST = kLcTt / 16 / SHARE;        // 16-token steps per wave and stage
+  constexpr int EPS = 8 / NST;                   // sigma(K) elements per step
+  constexpr int IPW = 1 + kLcTt * D * 2 / 1024 / kLcWaves;   // loads per wave and stage
+  static_assert(TILES * SHARE == kLcWaves && (SHARE == 1 || SHARE == 2), "tiles per wave");
+  static_assert(KT / kLcThreads == 8, "one 16-byte chunk of K per thread and stage");
+  static_assert(kLcStages == 4, "the stage loop is unrolled over the four slots");
+  // Each slot and buffer is an array of its own, and the loop is unrolled over
+  // the slots: the compiler then sees that the LDS reads of one slot never
+  // alias the direct-to-LDS loads into another and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) bf16 ks0[KT], ks1[KT], ks2[KT], ks3[KT];
+  __shared__ __attribute__((aligned(1024))) bf16 vs0[VT], vs1[VT], vs2[VT], vs3[VT];
+  __shared__ __attribute__((aligned(1024))) bf16 kh0[KT], kh1[KT], kl0[KT], kl1[KT];
+  __shared__ float lc_red[kLcTt * (kLcKb + 1)];   // end-of-kernel reductions
+  static_assert(SHARE == 1 || TILES * 1024 <= kLcTt * (kLcKb + 1), "partials fit the reduction area");
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   const int sh = blk / NKB, dkb = blk % NKB;
   const int bh = sh / a.S, s = sh % a.S;
   const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const bf16* __restrict__ kb = a.k + tok0 * D + dkb * KB;
-  const bf16* __restrict__ vb = a.v + tok0 * D;
+  const bf16* kseg = a.k + tok0 * D;
+  const bf16* vseg = a.v + tok0 * D;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int hi = lane >> 5, grp = lane >> 4, sidx = lane & 15, l32 = lane & 31;
-  const int krow = t >> 2, kch = t & 3;            // this thread's 16-byte chunk of the K block
-  const int dvb = wave % NDVB, part = wave / NDVB;
+  const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+  const int tile = wave % TILES, part = wave / TILES;
+  const int dvb = tile % NDV, dkq = tile / NDV;
+  const int vofs = lc_tr_offset<D>(lane, dvb);
+  const int kofs = lc_tr_offset<kLcKb>(lane, dkq);
+  // sigma(K) pass: row th / 8 of the stage, logical chunk th % 8
+  const int srow = th >> 3, sch = th & 7;
+  const int ssrc = srow * kLcKb + 8 * sch;
+  const int sdst = srow * kLcKb + 8 * lc_chunk<kLcKb>(srow, sch);
 
-  bf16x8 kx = *reinterpret_cast<const bf16x8*>(kb + (int64_t)krow * D + kch * 8);
-  u32x4 vx[VPT];
-#pragma unroll
-  for (int p = 0; p < VPT; ++p) {
-    const int c = t + kThreads * p;
-    vx[p] = *reinterpret_cast<const u32x4*>(vb + (int64_t)(c / VCH) * D + (c % VCH) * 8);
-  }
+  const int nst = a.N / kLcTt;
+  lc_issue<D>(kseg, vseg, a.N, 0, dkb, ks0, vs0, wave, lane);
+  lc_issue<D>(kseg, vseg, a.N, 1, dkb, ks1, vs1, wave, lane);
+  lc_issue<D>(kseg, vseg, a.N, 2, dkb, ks2, vs2, wave, lane);
+
   float zp[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) zp[i] = 0.f;
@@ -72,73 +162,103 @@ void lin_contrib_kernel(LinContribArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  for (int t0 = 0; t0 < a.N; t0 += 64) {
-    bf16x8 h8, l8;
+  // sigma(K) of elements [i0, i0 + n) of this thread's chunk: column sums and
+  // the bf16 hi + lo parts
+  auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, bf16x8& l8, int i0, int n) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = i0; i < i0 + n; ++i) {
       const float f = elu1(bf2f(kx[i]));
       zp[i] += f;
       h8[i] = f2bf(f);
       l8[i] = lo_part(f, h8[i]);
     }
-    *(INFINI_LDS bf16x8*)(khi + krow * KP + kch * 8) = h8;
-    *(INFINI_LDS bf16x8*)(klo + krow * KP + kch * 8) = l8;
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const int c = t + kThreads * p;
-      *(INFINI_LDS u32x4*)(vt + (c / VCH) * VP + (c % VCH) * 8) = vx[p];
-    }
-    if (t0 + 64 < a.N) {
-      kx = *reinterpret_cast<const bf16x8*>(kb + (int64_t)(t0 + 64 + krow) * D + kch * 8);
-#pragma unroll
-      for (int p = 0; p < VPT; ++p) {
-        const int c = t + kThreads * p;
-        vx[p] = *reinterpret_cast<const u32x4*>(vb + (int64_t)(t0 + 64 + c / VCH) * D + (c % VCH) * 8);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = part; ks < 4; ks += WPB) {
-      const int ra = 16 * ks + 8 * hi;
-      const bf16x8 va = lds_operand_tr(vt, VP, ra, ra + 4, 32 * dvb + 16 * (grp & 1), sidx);
-      const bf16x8 bh8 = lds_operand_tr(khi, KP, ra, ra + 4, 16 * (grp & 1), sidx);
-      const bf16x8 bl8 = lds_operand_tr(klo, KP, ra, ra + 4, 16 * (grp & 1), sidx);
-      acc = mfma32(va, bh8, acc);
-      acc = mfma32(va, bl8, acc);
-    }
-    __syncthreads();
-  }
+  };
 
-  // token-interleaved partials of one block are summed in wave order (D = 64)
-  float* red = reinterpret_cast<float*>(vt);
-  if (WPB > 1) {
+  // prologue: stage 0 landed, its sigma(K) parts in buffer 0
+  {
+    constexpr int VM = 2 * IPW;
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0F70);
+    __builtin_amdgcn_s_barrier();
+    const bf16x8 kx = *(const INFINI_LDS bf16x8*)(ks0 + ssrc);
+    bf16x8 h8, l8;
+    sigma_part(kx, h8, l8, 0, 8);
+    *(INFINI_LDS bf16x8*)(kh0 + sdst) = h8;
+    *(INFINI_LDS bf16x8*)(kl0 + sdst) = l8;
+  }
+  // Iteration q: the products of stage q (MFMA, slot q % 4, buffer q % 2)
+  // interleaved with the sigma(K) parts of stage q+1 (VALU, into the other
+  // buffer); the loads of stage q+3 go into the slot of stage q-1, which every
+  // wave has finished reading at the barrier.
+#define INFINI_LC_ITER(Q, VC, KN, KHC, KLC, KHN, KLN, KLD, VLD)                                   \
+  {                                                                                             \
+    const int q_ = (Q);                                                                         \
+    /* stage q+1 has landed once at most stage q+2's loads are in flight */                      \
+    __builtin_amdgcn_s_waitcnt((IPW & 15) | ((IPW >> 4) << 14) | 0x0070);  /* and lgkmcnt(0) */ \
+    __builtin_amdgcn_s_barrier();                                                               \
+    lc_issue<D>(kseg, vseg, a.N, q_ + 3, dkb, KLD, VLD, wave, lane);                            \
+    const bool more_ = q_ + 1 < nst;                                                            \
+    const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + ssrc);                                  \
+    bf16x8 h8_, l8_;                                                                            \
+    _Pragma("unroll")                                                                           \
+    for (int j = 0; j < NST; ++j) {                                                             \
+      const int st = part + SHARE * j;                                                          \
+      const bf16x8 va = lc_read_tr<D>(VC, 16 * st * D + vofs);                                  \
+      const bf16x8 bh8 = lc_read_tr<kLcKb>(KHC, 16 * st * kLcKb + kofs);                        \
+      const bf16x8 bl8 = lc_read_tr<kLcKb>(KLC, 16 * st * kLcKb + kofs);                        \
+      acc = mfma32(va, bh8, acc);                                                               \
+      acc = mfma32(va, bl8, acc);                                                               \
+      if (more_) sigma_part(kx_, h8_, l8_, EPS * j, EPS);                                       \
+    }                                                                                           \
+    if (more_) {                                                                                \
+      *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                                  \
+      *(INFINI_LDS bf16x8*)(KLN + sdst) = l8_;                                                  \
+    }                                                                                           \
+  }
+  for (int q = 0; q < nst; q += 4) {
+    INFINI_LC_ITER(q, vs0, ks1, kh0, kl0, kh1, kl1, ks3, vs3)
+    if (q + 1 >= nst) break;
+    INFINI_LC_ITER(q + 1, vs1, ks2, kh1, kl1, kh0, kl0, ks0, vs0)
+    if (q + 2 >= nst) break;
+    INFINI_LC_ITER(q + 2, vs2, ks3, kh0, kl0, kh1, kl1, ks1, vs1)
+    if (q + 3 >= nst) break;
+    INFINI_LC_ITER(q + 3, vs3, ks0, kh1, kl1, kh0, kl0, ks2, vs2)
+  }
+#undef INFINI_LC_ITER
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // token-interleaved partials of one tile are summed in wave order (d = 64)
+  float* red = lc_red;
+  if (SHARE > 1) {
     if (part > 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[((part - 1) * NDVB + dvb) * 1024 + r * 64 + lane] = acc[r];
+      for (int r = 0; r < 16; ++r) red[tile * 1024 + r * 64 + lane] = acc[r];
     }
     __syncthreads();
     if (part == 0) {
 #pragma unroll
-      for (int w = 1; w < WPB; ++w)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += red[((w - 1) * NDVB + dvb) * 1024 + r * 64 + lane];
+      for (int r = 0; r < 16; ++r) acc[r] += red[tile * 1024 + r * 64 + lane];
     }
+    __syncthreads();
   }
   float* __restrict__ cm = a.cM + (int64_t)sh * D * D;
   if (part == 0) {
+    const int hi = lane >> 5, l32 = lane & 31;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int dv = 32 * dvb + 8 * (r >> 2) + 4 * hi + (r & 3);
-      cm[dv * D + dkb * KB + l32] = acc[r];
+      cm[dv * D + dkb * kLcKb + 32 * dkq + l32] = acc[r];
     }
   }
+  // c: column sums of sigma(K) over the 64 row positions, in row order
+  float* zred = red;   // [64 rows][kLcKb + 1]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) zred[krow][kch * 8 + i] = zp[i];
+  for (int i = 0; i < 8; ++i) zred[srow * (kLcKb + 1) + 8 * sch + i] = zp[i];
   __syncthreads();
-  if (t < KB) {
+  if (th < kLcKb) {
     float sum = 0.f;
-    for (int r = 0; r < 64; ++r) sum += zred[r][t];
-    a.cz[(int64_t)sh * D + dkb * KB + t] = sum;
+    for (int r = 0; r < kLcTt; ++r) sum += zred[r * (kLcKb + 1) + th];
+    a.cz[(int64_t)sh * D + dkb * kLcKb + th] = sum;
   }
 }
 
@@ -223,9 +343,10 @@ void lin_scan_kernel(LinScanArgs a) {
 // ------------------------------------------------------------------ launchers
 template <int D>
 hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / 32);
+  const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / kLcKb);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (a.N % kLcTt != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kLcThreads), 0, stream, a);
   return hipGetLastError();
 }
 
