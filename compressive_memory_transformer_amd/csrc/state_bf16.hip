@@ -262,21 +262,21 @@ void lin_contrib_kernel(LinContribArgs a) {
   }
 }
 
-// Exclusive prefix over segments.  One thread per element of M^T; the last
-// workgroup of each head carries z.  The contributions of the next kPf segments
-// are loaded while the current kPf are folded in, so the chain over segments
-// runs at arithmetic speed instead of one memory latency per segment.  Each
-// snapshot also gets the fp32 column sums of M over d_key (row sums of M^T),
-// reduced in a fixed order (wave sums, then the waves of a row in order).
+// Exclusive prefix over segments.  Each thread carries two adjacent elements of
+// one row of M^T (a row of d_key elements is one wave at d = 128, half a wave at
+// d = 64), so the snapshot's column sum of M (row sum of M^T) is a wave reduction
+// with no LDS or barrier; the last workgroup of each head carries z.  The
+// contributions of the next kPf segments are loaded while the current kPf are
+// folded in, so the chain over segments runs at arithmetic speed instead of one
+// memory latency per segment.
 constexpr int kPf = 16;
 
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void lin_scan_kernel(LinScanArgs a) {
-  constexpr int MB = D * D / kThreads;     // workgroups holding M^T per head
-  constexpr int WPR = D / 64;              // waves per row of M^T
-  static_assert(D * D % kThreads == 0 && D % 64 == 0, "shape");
-  __shared__ float red[kPf][kThreads / 64];
+  constexpr int MB = D * D / (2 * kThreads);   // workgroups holding M^T per head
+  constexpr int TPR = D / 2;                   // threads per row of M^T
+  static_assert(D * D % (2 * kThreads) == 0 && (TPR == 64 || TPR == 32), "shape");
   const int bh = blockIdx.x / (MB + 1);
   const int sub = blockIdx.x % (MB + 1);
   const int64_t base = (int64_t)bh * a.S;
@@ -303,41 +303,42 @@ void lin_scan_kernel(LinScanArgs a) {
     a.z[(int64_t)bh * D + dk] = run;
     return;
   }
-  const int e = sub * kThreads + threadIdx.x;
+  const int e = 2 * (sub * kThreads + threadIdx.x);   // elements e, e + 1 of M^T
   const int dv = e / D, dk = e % D;
-  const int wave = threadIdx.x >> 6;
   const float* __restrict__ cm = a.cM + base * D * D + e;
-  float run = a.M[(int64_t)bh * D * D + dk * D + dv];
-  float cur[kPf], nxt[kPf];
+  const float* __restrict__ m0 = a.M + (int64_t)bh * D * D;
+  float r0 = m0[dk * D + dv], r1 = m0[(dk + 1) * D + dv];
+  float2 cur[kPf], nxt[kPf];
 #pragma unroll
-  for (int i = 0; i < kPf; ++i) cur[i] = i < a.S ? cm[(int64_t)i * D * D] : 0.f;
+  for (int i = 0; i < kPf; ++i)
+    cur[i] = i < a.S ? *reinterpret_cast<const float2*>(cm + (int64_t)i * D * D) : make_float2(0.f, 0.f);
   for (int s0 = 0; s0 < a.S; s0 += kPf) {
 #pragma unroll
     for (int i = 0; i < kPf; ++i)
-      nxt[i] = s0 + kPf + i < a.S ? cm[(int64_t)(s0 + kPf + i) * D * D] : 0.f;
+      nxt[i] = s0 + kPf + i < a.S ? *reinterpret_cast<const float2*>(cm + (int64_t)(s0 + kPf + i) * D * D)
+                                  : make_float2(0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < kPf; ++i) {
       if (s0 + i < a.S) {
-        a.snapM[(base + s0 + i) * D * D + e] = f2bf(run);
-        const float part = wave_sum(run);
-        if ((threadIdx.x & 63) == 0) red[i][wave] = part;
-        run += cur[i];
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x % D == 0) {
-      for (int i = 0; i < kPf && s0 + i < a.S; ++i) {
-        float c = 0.f;
+        const int64_t sh = base + s0 + i;
+        bf16x2 pk;
+        pk[0] = f2bf(r0);
+        pk[1] = f2bf(r1);
+        *reinterpret_cast<bf16x2*>(a.snapM + sh * D * D + e) = pk;
+        float c = r0 + r1;
 #pragma unroll
-        for (int w = 0; w < WPR; ++w) c += red[i][wave + w];
-        a.snapc[(base + s0 + i) * D + dv] = c;
+        for (int o = TPR / 2; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+        if (threadIdx.x % TPR == 0) a.snapc[sh * D + dv] = c;
+        r0 += cur[i].x;
+        r1 += cur[i].y;
       }
     }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPf; ++i) cur[i] = nxt[i];
   }
-  a.M[(int64_t)bh * D * D + dk * D + dv] = run;
+  float* __restrict__ mout = a.M + (int64_t)bh * D * D;
+  mout[dk * D + dv] = r0;
+  mout[(dk + 1) * D + dv] = r1;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -352,7 +353,7 @@ hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.BH * (D * D / kThreads + 1);
+  const int64_t blocks = (int64_t)a.BH * (D * D / (2 * kThreads) + 1);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(lin_scan_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
