@@ -95,6 +95,17 @@ def attention_flops(w, first_segment_global: int = 0) -> int:
     return w.batch * w.heads * (w.segments * att + seg_with_memory * ret)
 
 
+def state_bytes(w) -> int:
+    """Algorithmic HBM bytes of the memory-state stage (either rule): K and V read
+    once, one snapshot per (b, h, segment) written (M^T in bf16 or fp32, z and the
+    column sums of M in fp32), and the state (M, z) read and written once per head."""
+    el = 2 if w.dtype == "bf16" else 4
+    N, dk, dv = w.segment_len, w.d_key, w.d_value
+    per_seg = N * (dk + dv) * el + dk * dv * el + (dk + dv) * 4
+    per_head = 2 * (dk * dv + dk) * 4
+    return w.batch * w.heads * (w.segments * per_seg + per_head)
+
+
 def state_flops(w, rule: str) -> int:
     N, dk, dv = w.segment_len, w.d_key, w.d_value
     upd = 2 * N * dk * dv + N * dk
@@ -262,7 +273,17 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": fa_avg},
-        "stages_ms": {"state": st_avg, "attention": fa_avg},
+        "stages_ms": {"state": st_avg, "attention": fa_avg,
+                      "attention_min": min(fa_ms), "attention_max": max(fa_ms)},
+        # the memory-state stage against its own bounds: HBM for the linear rule
+        # (contributions + prefix scan), the dependent chain for the delta rule
+        "state_roofline": {"bound": "hbm" if rule == "linear" else "latency",
+                           "achieved_GBps": state_bytes(w) / (st_avg * 1e-3) / 1e9,
+                           "peak_GBps": HBM_PEAK_GBS,
+                           "frac_hbm": state_bytes(w) / (st_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "tflops": state_flops(w, rule) / (st_avg * 1e-3) / 1e12,
+                           "frac_mfma": state_flops(w, rule) / (st_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                           "bytes": state_bytes(w), "flops": state_flops(w, rule)},
         "step_tflops": step_fl / (wall / args.steps) / 1e12,
         "cpu_baseline": cpu,
     }
