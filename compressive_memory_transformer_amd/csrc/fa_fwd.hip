@@ -45,7 +45,12 @@
 // where colsum(M) (sum over d_key) comes in fp32 with the snapshot and q' M runs
 // on MFMA from the bf16 snapshot of M_{s-1}^T.  q' keeps the full relative
 // precision of bf16, unlike sigma(q) ~ 1 + q itself.  Gate, round to bf16, store
-// through LDS (slot 1 is free by then) as whole 128-byte row segments.
+// through a small LDS stage per wave as whole 64-byte row segments.
+//
+// Q rows reach LDS like K and V: a pass's 256 rows load into slot 1 (free while
+// the epilogue of the previous pass runs, or with tile 0 for the first pass), so
+// their memory latency hides behind other work; each wave reads its 32 rows
+// from there before the first key tile.
 #include "common.h"
 #include "kernels.h"
 
@@ -72,8 +77,11 @@ struct FaLayout {
   static_assert(NI % KPER == 0, "each wave's first load starts a K swizzle period");
   static_assert(D <= kBN, "the snapshot of M^T must fit a K slot");
   static_assert(D <= 256, "z and colsum must fit their LDS array");
-  static_assert(kWaves * 32 * 64 * 2 <= 2 * TILE_ELEMS * 2, "the output stages must fit slot 1");
+  static_assert(kBM == 2 * kBN, "the Q rows of a query tile fill the two parts of a slot");
 };
+
+// Output stage: 32 rows x 32 columns (bf16) per wave.
+constexpr int kStageElems = 32 * 32;
 
 // Physical 16-byte chunk of logical chunk c in row r (an XOR, so the same map
 // takes physical to logical).  An LDS read of 16 bytes per lane is served 16
@@ -177,6 +185,13 @@ __device__ __forceinline__ void issue_row(const void* base, uint32_t bytes, void
 // landed, then synchronises the workgroup.
 __device__ __forceinline__ void wait_loads_and_sync() {
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Waits for this wave's LDS accesses only (stores and loads to memory may stay in
+// flight), then synchronises the workgroup.
+__device__ __forceinline__ void wait_lds_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 }
 
@@ -468,30 +483,31 @@ __device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ k
   X.bad = false;
 }
 
-// Loads of one 32-row block of Q rows: lane l holds Q[row][16 c + 8 hi .. + 7] of
-// its row; p points at element 8 hi of the lane's row.
-template <int D>
-__device__ __forceinline__ void load_q_rows(bf16x8 (&q)[D / 16], const bf16* __restrict__ p) {
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) q[c] = *reinterpret_cast<const bf16x8*>(p + 16 * c);
-}
-
 // Retrieval, gate and store of one query block.  mt: M^T snapshot (K-slot
 // layout), zs / cs: z and colsum(M) in LDS, ob: the block's first output row,
-// stage: this wave's 4 KB of LDS for the output.  First q' and the denominator
+// stages: 2 KB of LDS per wave for the output.  First q' and the denominator
 // for all of d_key; then, one 32-column group of d_value at a time, the
 // retrieval accumulator (colsum + M^T q'), the gate and the output, so that only
 // one group's accumulator is live.
 template <int D>
 __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __restrict__ mt,
                                              const float* __restrict__ zs, const float* __restrict__ cs,
-                                             const LdsAddr<D>& ad, bool has_memory, float g, float inv_sc,
-                                             bf16* __restrict__ ob, bf16* __restrict__ stage) {
-  // The lane index is made opaque here so that the per-lane addresses below are
-  // computed in the epilogue instead of being hoisted to the kernel start and
-  // kept live (spilled) across the tile loop.
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
+                                             const LdsAddr<D>& ad, bool has_memory, float beta, float inv_sc,
+                                             bf16* __restrict__ ob, bf16* __restrict__ stages, int wave) {
+  // The lane index is computed here (from the exec mask, with an opaque base) so
+  // that it and the per-lane addresses below are not hoisted to the kernel start
+  // and kept live (spilled) across the tile loop: the reload of a spill here
+  // would wait for the next pass's Q loads in flight.
+  unsigned base = 0;
+  asm volatile("" : "+v"(base));
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, base));
+  asm volatile("" : "+v"(wave));
+  bf16* const stage = stages + kStageElems * wave;
+  // Likewise the gate is computed here from beta (a scalar register): a vector
+  // copy kept from the kernel start is spilled, and its reload here would wait
+  // for the next pass's Q loads in flight.
+  asm volatile("" : "+s"(beta));
+  const float g = sigmoid_gate(beta);
   const int l32 = lane & 31, hi = lane >> 5;
   const float l_tot = X.l + __shfl_xor(X.l, 32);
   const float inv_l = 1.f / l_tot;
@@ -526,50 +542,47 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
   const float inv_den = (has_memory && den > 0.f) ? 1.f / den : 0.f;
   const float wg_mem = g * inv_den;
   const float wg_dot = (1.f - g) * inv_l;
-  // The rows go out through LDS, 64 columns at a time: each lane writes its
-  // 8-byte pieces of row l32 into a [32 x 64] stage (16-byte chunk k of row r at
-  // chunk k ^ ((r / 2) % 8), which keeps both access patterns free of bank
-  // conflicts), then reads back 16 bytes of row 8 i + lane / 8 so that every
-  // global store writes whole 128-byte row halves.  The stage is private to the
-  // wave, and LDS executes a wave's accesses in order, so no barrier is needed.
+  // The rows go out through LDS, 32 columns at a time: each lane writes its
+  // 8-byte pieces of row l32 into a [32 x 32] stage (16-byte chunk k of row r at
+  // chunk k ^ ((r / 4) % 4): the reads below are free of bank conflicts, the
+  // writes conflict two ways), then reads back 16 bytes of row 16 i + lane / 4 so
+  // that every global store writes whole 64-byte row segments.  The stage is
+  // private to the wave, and LDS executes a wave's accesses in order, so no
+  // barrier is needed.
 #pragma unroll
-  for (int h = 0; h < D / 64; ++h) {
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      const int db = 2 * h + dh;
-      f32x16 am;
-      if (has_memory) {
-        // accumulator starts at colsum(M)[d_value of each element]
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 c4 = *(const INFINI_LDS f32x4*)(cs + 32 * db + 8 * j + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) am[4 * j + e] = c4[e];
-        }
-        bf16x8 ma[D / 16];
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) ma[c] = lds_read8(mt + 32 * db * D + ad.kofs(c));
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) am = mfma32(ma[c], qp[c], am);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) am[r] = 0.f;
-      }
+  for (int db = 0; db < D / 32; ++db) {
+    f32x16 am;
+    if (has_memory) {
+      // accumulator starts at colsum(M)[d_value of each element]
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x4 outv;
+        const f32x4 c4 = *(const INFINI_LDS f32x4*)(cs + 32 * db + 8 * j + 4 * hi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[4 * j + e] * wg_mem));
-        const int chunk = (4 * dh + j) ^ ((l32 >> 1) & 7);
-        *(INFINI_LDS bf16x4*)(stage + l32 * 64 + 8 * chunk + 4 * hi) = outv;
+        for (int e = 0; e < 4; ++e) am[4 * j + e] = c4[e];
       }
+      bf16x8 ma[D / 16];
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) ma[c] = lds_read8(mt + 32 * db * D + ad.kofs(c));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) am = mfma32(ma[c], qp[c], am);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) am[r] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * i + (lane >> 3), c = lane & 7;
-      const bf16x8 x = *(const INFINI_LDS bf16x8*)(stage + r * 64 + 8 * (c ^ ((r >> 1) & 7)));
-      *reinterpret_cast<bf16x8*>(ob + (int64_t)r * D + 64 * h + 8 * c) = x;
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 outv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        outv[e] = f2bf(__builtin_fmaf(X.o[db][4 * j + e], wg_dot, am[4 * j + e] * wg_mem));
+      const int chunk = j ^ ((l32 >> 2) & 3);
+      *(INFINI_LDS bf16x4*)(stage + l32 * 32 + 8 * chunk + 4 * hi) = outv;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + (lane >> 2), c = lane & 3;
+      const bf16x8 x = *(const INFINI_LDS bf16x8*)(stage + r * 32 + 8 * (c ^ ((r >> 2) & 3)));
+      *reinterpret_cast<bf16x8*>(ob + (int64_t)r * D + 32 * db + 8 * c) = x;
     }
   }
 }
@@ -587,17 +600,22 @@ struct FaCtx {
   uint32_t seg_bytes;
   int N, nk, wave;
   bool has_memory;
-  float g, sc;
+  float beta, sc;
 };
 
-// Row pointer for the Q loads of this wave's block of query tile qt (element 8 hi
-// of the lane's row).  A block past the segment end reads the first rows
-// instead (its results are never used), so the loads need no branch.
+// Direct-to-LDS loads of the Q rows of query tile qt into slot 1: rows 0-127 of
+// the tile into its K part, rows 128-255 into its V part, both in the K layout,
+// so that a wave reads its 32 rows as it reads a 32-key block of K.  Rows past
+// the segment end load zeros (their results are never used).
 template <int D>
-__device__ __forceinline__ const bf16* q_rows(const FaCtx<D>& cx, int qt) {
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-  const int r = qt * kBM + 32 * cx.wave;
-  return cx.qb + (int64_t)(r < cx.N ? r + l32 : l32) * D + 8 * hi;
+__device__ __forceinline__ void issue_q(const FaCtx<D>& cx, int qt, bf16* k1s, bf16* v1s, const DmaOfs<D>& dof) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = qt * kBM + half * kBN;
+    const bool in = r < cx.N;
+    issue_tile<D, false>(cx.qb + (in ? (int64_t)r * D : 0), in ? (uint32_t)(cx.N - r) * D * 2 : 0u,
+                         half ? v1s : k1s, cx.wave, dof);
+  }
 }
 
 // The load item after step t of a pass with nsteps steps: tile t+1 (zeros past
@@ -629,11 +647,15 @@ __device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int 
 // One query tile (pass) of the workgroup.  Tile t of the pass sits in slot t % 2
 // (k0s/v0s, k1s/v1s); every pass has an even number of steps, so the last one
 // uses slot 1 and brings the snapshot of M^T into k0s (with z and colsum into
-// zc) and, with `next` set, the V part of the next pass's tile 0 into v0s.  On
-// entry tile 0 is in slot 0 (waited for and synchronised).
+// zc) and, with a next pass (query tile qn >= 0), the V part of its tile 0 into
+// v0s; the Q rows of that pass go into slot 1 during the epilogue.  On entry
+// tile 0 is in slot 0 and the pass's Q rows in slot 1 (waited for and
+// synchronised).
 template <int D>
-__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, bf16* k0s, bf16* v0s, bf16* k1s,
-                                         bf16* v1s, float* zc, const LdsAddr<D>& ad, const DmaOfs<D>& dof) {
+__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf16* k0s, bf16* v0s, bf16* k1s,
+                                         bf16* v1s, float* zc, bf16* stg, const LdsAddr<D>& ad,
+                                         const DmaOfs<D>& dof) {
+  const bool next = qn >= 0;
   const int q0 = qt * kBM;
   const int r0 = q0 + 32 * cx.wave;          // first row of this wave's query block
   const bool act = r0 < cx.N;
@@ -642,12 +664,18 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
 
   QBlock<D> X;
   // Q^T * scale * log2 e (rounded to bf16): the scores come out in the log2 domain
-  bf16x8 qr[D / 16];
-  load_q_rows<D>(qr, q_rows<D>(cx, qt));
+  {
+    const bf16* qs = (cx.wave < 4 ? k1s : v1s) + 32 * (cx.wave & 3) * D;
+    bf16x8 qr[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
+    for (int c = 0; c < D / 16; ++c) qr[c] = lds_read8(qs + ad.kofs(c));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) X.q[c][i] = f2bf(bf2f(qr[c][i]) * cx.sc);
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) X.q[c][i] = f2bf(bf2f(qr[c][i]) * cx.sc);
+  }
+  // every wave has its Q rows before step 0 loads tile 1 into slot 1
+  wait_lds_and_sync();
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -681,12 +709,15 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, bool next, 
   }
 #undef INFINI_FA_STEP
 
+  // slot 1 is free after the last step: the next pass's Q rows load during the
+  // epilogue
+  if (next) issue_q<D>(cx, qn, k1s, v1s, dof);
   if (act && __any(X.bad)) recompute_block<D>(X, r0, cx.kseg, cx.vseg);
 
-  // slot 1 is free after the last step: 4 KB of output stage per wave
-  bf16* const stage = (cx.wave < 4 ? k1s : v1s) + 2048 * (cx.wave & 3);
-  if (act) finish_block<D>(X, k0s, zc, zc + 256, ad, cx.has_memory, cx.g, 1.f / cx.sc, cx.ob + (int64_t)r0 * D, stage);
-  wait_loads_and_sync();
+  if (act) finish_block<D>(X, k0s, zc, zc + 256, ad, cx.has_memory, cx.beta, 1.f / cx.sc, cx.ob + (int64_t)r0 * D,
+                           stg, cx.wave);
+  // the snapshot in k0s is no longer read (the output stores stay in flight)
+  if (next) wait_lds_and_sync();
 }
 
 template <int D>
@@ -698,6 +729,7 @@ void fa_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 k1s[L::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 v1s[L::TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) float zc[512];   // z at [0, D), colsum(M) at [256, 256 + D)
+  __shared__ __attribute__((aligned(1024))) bf16 stg[kWaves * kStageElems];   // output stages
 
   const int npair = (a.nq + 1) / 2;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -721,7 +753,7 @@ void fa_fwd_kernel(FaArgs a) {
   cx.nk = (a.N + kBN - 1) / kBN;
   cx.wave = threadIdx.x >> 6;
   cx.has_memory = (a.seg_base + s) > 0;
-  cx.g = sigmoid_gate(a.beta[h]);
+  cx.beta = a.beta[h];
   cx.sc = a.sc_log2;
 
   LdsAddr<D> ad;
@@ -737,14 +769,15 @@ void fa_fwd_kernel(FaArgs a) {
   dof.init(threadIdx.x & 63);
   issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
   issue_tile<D, true>(cx.vseg, cx.seg_bytes, v0s, cx.wave, dof);
+  issue_q<D>(cx, qt0, k1s, v1s, dof);
   wait_loads_and_sync();
   // One copy of the pass code serves both passes (the loop is not unrolled).
   // Between them, the K part of tile 0 goes into k0s (free once the snapshot has
-  // been used); its V part is already in v0s.
+  // been used); its V part is already in v0s and the Q rows in slot 1.
   const int npass = two ? 2 : 1;
 #pragma unroll 1
   for (int p = 0; p < npass; ++p) {
-    run_pass<D>(cx, p == 0 ? qt0 : qt1, p + 1 < npass, k0s, v0s, k1s, v1s, zc, ad, dof);
+    run_pass<D>(cx, p == 0 ? qt0 : qt1, p + 1 < npass ? qt1 : -1, k0s, v0s, k1s, v1s, zc, stg, ad, dof);
     if (p + 1 < npass) {
       issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
       wait_loads_and_sync();
