@@ -71,9 +71,6 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // e^x as 2^(x log2 e) on the hardware exp2 unit.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// sigma(x) = ELU(x) + 1: x + 1 for x > 0, e^x otherwise.
-__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : exp_e(x); }
-
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 // A bf16 held as the raw 16 bits of a short (e.g. an element of a transposing
 // LDS read) widened to fp32 by placing the bits in the upper half.  (A

@@ -7,10 +7,12 @@
 // fp32) per segment for the fused attention kernel and the final (M_S, z_S) in
 // the fp32 state.  The delta rule lives in state_delta.hip.
 //
-// Precision.  sigma(K) = 1 + k for the small keys of these workloads, so rounding
-// sigma(K) to bf16 keeps only a few bits of k.  The contribution GEMM therefore
-// splits sigma(K) into bf16 hi + lo parts (x = hi + lo to about 16 bits) and sums
-// the hi*V and lo*V products in fp32 (V is exact in bf16).
+// Precision.  sigma(K) = 1 + k' with k' = sigma(K) - 1 small for the keys of these
+// workloads, so rounding sigma(K) itself to bf16 would keep only a few bits of k'.
+// The contribution GEMM therefore runs on k' in bf16 (full relative precision of
+// the deviation from 1) and adds the rank-one term 1^T V as a second product with
+// an all-ones operand, both summed in fp32 (V is exact in bf16):
+//   sigma(K)^T V = k'^T V + 1^T V.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,9 +20,6 @@ namespace infini {
 
 namespace {
 constexpr int kThreads = 256;
-
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ bf16 lo_part(float x, bf16 hi) { return f2bf(x - bf2f(hi)); }
 }  // namespace
 
 // =================================================================== linear
@@ -28,9 +27,9 @@ __device__ __forceinline__ bf16 lo_part(float x, bf16 hi) { return f2bf(x - bf2f
 // blocks of a segment (d = 128) run on the same XCD and share its V through L2.
 // 64-token stages of K (this block's columns) and V stream into a 4-slot LDS
 // ring with buffer_load ... lds (three stages in flight).  Per stage each thread
-// turns 8 elements of K into sigma(K), split into bf16 hi + lo, written to LDS in
-// the layout of the transposing operand reads; then C^T[d_value][d_key] +=
-// V^T sigma(K) on v_mfma_f32_32x32x16_bf16 (hi and lo products into one fp32
+// turns 8 elements of K into k' = sigma(K) - 1 in bf16, written to LDS in the
+// layout of the transposing operand reads; then C^T[d_value][d_key] +=
+// V^T k' + V^T 1 on v_mfma_f32_32x32x16_bf16 (both products into one fp32
 // accumulator), one 32 x 32 output tile per wave (d = 128; at d = 64 two waves
 // share a tile, taking alternate 16-token steps).  c = sum_t sigma(K_t) is
 // reduced over the workgroup at the end in a fixed order.
@@ -129,7 +128,7 @@ void lin_contrib_kernel(LinContribArgs a) {
   // alias the direct-to-LDS loads into another and does not wait for them.
   __shared__ __attribute__((aligned(1024))) bf16 ks0[KT], ks1[KT], ks2[KT], ks3[KT];
   __shared__ __attribute__((aligned(1024))) bf16 vs0[VT], vs1[VT], vs2[VT], vs3[VT];
-  __shared__ __attribute__((aligned(1024))) bf16 kh0[KT], kh1[KT], kl0[KT], kl1[KT];
+  __shared__ __attribute__((aligned(1024))) bf16 kh0[KT], kh1[KT];
   __shared__ float lc_red[kLcTt * (kLcKb + 1)];   // end-of-kernel reductions
   static_assert(SHARE == 1 || TILES * 1024 <= kLcTt * (kLcKb + 1), "partials fit the reduction area");
 
@@ -162,17 +161,21 @@ void lin_contrib_kernel(LinContribArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  // sigma(K) of elements [i0, i0 + n) of this thread's chunk: column sums and
-  // the bf16 hi + lo parts
-  auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, bf16x8& l8, int i0, int n) {
+  // k' = sigma(K) - 1 of elements [i0, i0 + n) of this thread's chunk (bf16) and
+  // the column sums of sigma(K)
+  auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, int i0, int n) {
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i) {
-      const float f = elu1(bf2f(kx[i]));
-      zp[i] += f;
+      const float x = bf2f(kx[i]);
+      const float f = x > 0.f ? x : exp_e(x) - 1.f;
+      zp[i] += f + 1.f;
       h8[i] = f2bf(f);
-      l8[i] = lo_part(f, h8[i]);
     }
   };
+  // B operand of the rank-one product: every element 1
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = f2bf(1.f);
 
   // prologue: stage 0 landed, its sigma(K) parts in buffer 0
   {
@@ -180,16 +183,15 @@ void lin_contrib_kernel(LinContribArgs a) {
     __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0F70);
     __builtin_amdgcn_s_barrier();
     const bf16x8 kx = *(const INFINI_LDS bf16x8*)(ks0 + ssrc);
-    bf16x8 h8, l8;
-    sigma_part(kx, h8, l8, 0, 8);
+    bf16x8 h8;
+    sigma_part(kx, h8, 0, 8);
     *(INFINI_LDS bf16x8*)(kh0 + sdst) = h8;
-    *(INFINI_LDS bf16x8*)(kl0 + sdst) = l8;
   }
   // Iteration q: the products of stage q (MFMA, slot q % 4, buffer q % 2)
-  // interleaved with the sigma(K) parts of stage q+1 (VALU, into the other
-  // buffer); the loads of stage q+3 go into the slot of stage q-1, which every
-  // wave has finished reading at the barrier.
-#define INFINI_LC_ITER(Q, VC, KN, KHC, KLC, KHN, KLN, KLD, VLD)                                   \
+  // interleaved with k' of stage q+1 (VALU, into the other buffer); the loads
+  // of stage q+3 go into the slot of stage q-1, which every wave has finished
+  // reading at the barrier.
+#define INFINI_LC_ITER(Q, VC, KN, KHC, KHN, KLD, VLD)                                             \
   {                                                                                             \
     const int q_ = (Q);                                                                         \
     /* stage q+1 has landed once at most stage q+2's loads are in flight */                      \
@@ -198,30 +200,26 @@ void lin_contrib_kernel(LinContribArgs a) {
     lc_issue<D>(kseg, vseg, a.N, q_ + 3, dkb, KLD, VLD, wave, lane);                            \
     const bool more_ = q_ + 1 < nst;                                                            \
     const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + ssrc);                                  \
-    bf16x8 h8_, l8_;                                                                            \
+    bf16x8 h8_;                                                                                 \
     _Pragma("unroll")                                                                           \
     for (int j = 0; j < NST; ++j) {                                                             \
       const int st = part + SHARE * j;                                                          \
       const bf16x8 va = lc_read_tr<D>(VC, 16 * st * D + vofs);                                  \
-      const bf16x8 bh8 = lc_read_tr<kLcKb>(KHC, 16 * st * kLcKb + kofs);                        \
-      const bf16x8 bl8 = lc_read_tr<kLcKb>(KLC, 16 * st * kLcKb + kofs);                        \
-      acc = mfma32(va, bh8, acc);                                                               \
-      acc = mfma32(va, bl8, acc);                                                               \
-      if (more_) sigma_part(kx_, h8_, l8_, EPS * j, EPS);                                       \
+      const bf16x8 bk8 = lc_read_tr<kLcKb>(KHC, 16 * st * kLcKb + kofs);                        \
+      acc = mfma32(va, bk8, acc);                                                               \
+      acc = mfma32(va, ones, acc);                                                              \
+      if (more_) sigma_part(kx_, h8_, EPS * j, EPS);                                            \
     }                                                                                           \
-    if (more_) {                                                                                \
-      *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                                  \
-      *(INFINI_LDS bf16x8*)(KLN + sdst) = l8_;                                                  \
-    }                                                                                           \
+    if (more_) *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                         \
   }
   for (int q = 0; q < nst; q += 4) {
-    INFINI_LC_ITER(q, vs0, ks1, kh0, kl0, kh1, kl1, ks3, vs3)
+    INFINI_LC_ITER(q, vs0, ks1, kh0, kh1, ks3, vs3)
     if (q + 1 >= nst) break;
-    INFINI_LC_ITER(q + 1, vs1, ks2, kh1, kl1, kh0, kl0, ks0, vs0)
+    INFINI_LC_ITER(q + 1, vs1, ks2, kh1, kh0, ks0, vs0)
     if (q + 2 >= nst) break;
-    INFINI_LC_ITER(q + 2, vs2, ks3, kh0, kl0, kh1, kl1, ks1, vs1)
+    INFINI_LC_ITER(q + 2, vs2, ks3, kh0, kh1, ks1, vs1)
     if (q + 3 >= nst) break;
-    INFINI_LC_ITER(q + 3, vs3, ks0, kh1, kl1, kh0, kl0, ks2, vs2)
+    INFINI_LC_ITER(q + 3, vs3, ks0, kh1, kh0, ks2, vs2)
   }
 #undef INFINI_LC_ITER
   __builtin_amdgcn_s_waitcnt(0);
@@ -262,10 +260,33 @@ void lin_contrib_kernel(LinContribArgs a) {
   }
 }
 
+// v moved across lanes by the DPP control CTRL; lanes outside ROW_MASK (rows of 16
+// lanes) get old.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over each group of TPR (32 or 64) consecutive lanes in a fixed order, on
+// DPP lane moves (no LDS): quad sums, then half rows and rows of 16 lanes by
+// mirrors, then rows combined by broadcasts.  The group's last lane holds the sum.
+template <int TPR>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_move<0xB1, 0xf>(0.f, x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_move<0x4E, 0xf>(0.f, x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_move<0x141, 0xf>(0.f, x);   // row_half_mirror
+  x += dpp_move<0x140, 0xf>(0.f, x);   // row_mirror
+  x += dpp_move<0x142, 0xa>(0.f, x);   // row_bcast:15 into rows 1 and 3
+  if (TPR == 64) x += dpp_move<0x143, 0xc>(0.f, x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Exclusive prefix over segments.  Each thread carries two adjacent elements of
 // one row of M^T (a row of d_key elements is one wave at d = 128, half a wave at
-// d = 64), so the snapshot's column sum of M (row sum of M^T) is a wave reduction
-// with no LDS or barrier; the last workgroup of each head carries z.  The
+// d = 64), so the snapshot's column sum of M (row sum of M^T) is a reduction over
+// the lanes of a wave with no LDS or barrier; the last workgroup of each head
+// carries z.  The
 // contributions of the next kPf segments are loaded while the current kPf are
 // folded in, so the chain over segments runs at arithmetic speed instead of one
 // memory latency per segment.
@@ -325,10 +346,8 @@ void lin_scan_kernel(LinScanArgs a) {
         pk[0] = f2bf(r0);
         pk[1] = f2bf(r1);
         *reinterpret_cast<bf16x2*>(a.snapM + sh * D * D + e) = pk;
-        float c = r0 + r1;
-#pragma unroll
-        for (int o = TPR / 2; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-        if (threadIdx.x % TPR == 0) a.snapc[sh * D + dv] = c;
+        const float c = group_sum<TPR>(r0 + r1);
+        if (threadIdx.x % TPR == TPR - 1) a.snapc[sh * D + dv] = c;
         r0 += cur[i].x;
         r1 += cur[i].y;
       }
