@@ -162,13 +162,13 @@ void lin_contrib_kernel(LinContribArgs a) {
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
   // k' = sigma(K) - 1 of elements [i0, i0 + n) of this thread's chunk (bf16) and
-  // the column sums of sigma(K)
+  // its column sums
   auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, int i0, int n) {
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i) {
       const float x = bf2f(kx[i]);
       const float f = x > 0.f ? x : exp_e(x) - 1.f;
-      zp[i] += f + 1.f;
+      zp[i] += f;   // sum of k'; the count of tokens is added at the end
       h8[i] = f2bf(f);
     }
   };
@@ -198,27 +198,35 @@ void lin_contrib_kernel(LinContribArgs a) {
     __builtin_amdgcn_s_waitcnt((IPW & 15) | ((IPW >> 4) << 14) | 0x0070);  /* and lgkmcnt(0) */ \
     __builtin_amdgcn_s_barrier();                                                               \
     lc_issue<D>(kseg, vseg, a.N, q_ + 3, dkb, KLD, VLD, wave, lane);                            \
-    const bool more_ = q_ + 1 < nst;                                                            \
-    const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + ssrc);                                  \
-    bf16x8 h8_;                                                                                 \
-    _Pragma("unroll")                                                                           \
-    for (int j = 0; j < NST; ++j) {                                                             \
-      const int st = part + SHARE * j;                                                          \
-      const bf16x8 va = lc_read_tr<D>(VC, 16 * st * D + vofs);                                  \
-      const bf16x8 bk8 = lc_read_tr<kLcKb>(KHC, 16 * st * kLcKb + kofs);                        \
-      acc = mfma32(va, bk8, acc);                                                               \
-      acc = mfma32(va, ones, acc);                                                              \
-      if (more_) sigma_part(kx_, h8_, EPS * j, EPS);                                            \
+    if (q_ < nst) {                                                                             \
+      const bool more_ = q_ + 1 < nst;                                                          \
+      /* all operand reads of the stage first: one LDS latency per stage */                     \
+      const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + ssrc);                                \
+      bf16x8 va_[NST], vk_[NST];                                                                \
+      _Pragma("unroll")                                                                         \
+      for (int j = 0; j < NST; ++j) {                                                           \
+        const int st = part + SHARE * j;                                                        \
+        va_[j] = lc_read_tr<D>(VC, 16 * st * D + vofs);                                         \
+        vk_[j] = lc_read_tr<kLcKb>(KHC, 16 * st * kLcKb + kofs);                                \
+      }                                                                                         \
+      bf16x8 h8_;                                                                               \
+      _Pragma("unroll")                                                                         \
+      for (int j = 0; j < NST; ++j) {                                                           \
+        acc = mfma32(va_[j], vk_[j], acc);                                                      \
+        acc = mfma32(va_[j], ones, acc);                                                        \
+        if (more_) sigma_part(kx_, h8_, EPS * j, EPS);                                          \
+      }                                                                                         \
+      if (more_) *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                       \
     }                                                                                           \
-    if (more_) *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                         \
   }
+  // Iterations past the last stage (when the stage count is not a multiple of
+  // four) only wait, synchronise and issue empty loads: every load is issued
+  // unconditionally, so the compiler tracks exactly which slots have loads in
+  // flight and adds no waits of its own.
   for (int q = 0; q < nst; q += 4) {
     INFINI_LC_ITER(q, vs0, ks1, kh0, kh1, ks3, vs3)
-    if (q + 1 >= nst) break;
     INFINI_LC_ITER(q + 1, vs1, ks2, kh1, kh0, ks0, vs0)
-    if (q + 2 >= nst) break;
     INFINI_LC_ITER(q + 2, vs2, ks3, kh0, kh1, ks1, vs1)
-    if (q + 3 >= nst) break;
     INFINI_LC_ITER(q + 3, vs3, ks0, kh1, kh0, ks2, vs2)
   }
 #undef INFINI_LC_ITER
@@ -248,10 +256,11 @@ void lin_contrib_kernel(LinContribArgs a) {
       cm[dv * D + dkb * kLcKb + 32 * dkq + l32] = acc[r];
     }
   }
-  // c: column sums of sigma(K) over the 64 row positions, in row order
+  // c: column sums of sigma(K) = k' + 1 over the 64 row positions, in row order
+  // (each row position saw nst tokens)
   float* zred = red;   // [64 rows][kLcKb + 1]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) zred[srow * (kLcKb + 1) + 8 * sch + i] = zp[i];
+  for (int i = 0; i < 8; ++i) zred[srow * (kLcKb + 1) + 8 * sch + i] = zp[i] + (float)nst;
   __syncthreads();
   if (th < kLcKb) {
     float sum = 0.f;
