@@ -23,7 +23,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kCB = 16;          // columns of M (d_value) per chain workgroup
-constexpr int kChainWaves = 8;   // chain workgroup: two waves per SIMD
+constexpr int kChainWaves = 4;   // chain workgroup: one wave per SIMD
+constexpr int kChainSlots = 4;   // LDS chunk slots: three chunks in flight while one is used
 constexpr int kChunk = 32 * kChainWaves;   // tokens per LDS chunk: one 32-token block per wave
 constexpr int kInvSlot = 256;    // floats per 1/den slot: one wave-wide 16-byte load writes 1 KB
 constexpr int kPart = 256;       // tokens per workgroup of the 1/den kernel
@@ -226,9 +227,24 @@ __device__ __forceinline__ void chain_issue(const ChainCtx<D>& cx, int q, int S,
 #endif
 }
 
-// Waits until this wave's loads (LDS-bound and register-bound) have landed.
-__device__ __forceinline__ void chain_wait_all() {
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+// Waits until at most the loads of the two most recently issued chunks are in
+// flight (vmcnt over this wave's loads per chunk: the k' and V shares, plus 1/den
+// on wave 0) and this wave's LDS accesses are done.
+// Workgroup barrier for LDS traffic only.  (__syncthreads() also orders global
+// memory, which makes it wait for every load into LDS still in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int D>
+__device__ __forceinline__ void chain_wait_older(int wave) {
+  using CL = ChainLayout<D>;
+  constexpr int L = CL::NIK + CL::NIV;
+  constexpr int W0 = 2 * (L + 1), WN = 2 * L;
+  static_assert(W0 < 64, "vmcnt range");
+  if (__builtin_amdgcn_readfirstlane(wave) == 0) __builtin_amdgcn_s_waitcnt((W0 & 15) | ((W0 >> 4) << 14) | 0x0070);
+  else __builtin_amdgcn_s_waitcnt((WN & 15) | ((WN >> 4) << 14) | 0x0070);
 }
 
 // Per-wave state of one segment: the B operand of the read-back (bf16 M, d_key
@@ -304,11 +320,12 @@ __device__ __forceinline__ void chain_block(ChainSeg<D>& sg, const bf16* __restr
 // The chain over the segments of one head for 16 columns of M (columns of M are
 // independent under the delta rule: column j of the read-back needs only
 // column j of M).  One workgroup of 4 waves per (b, h, column block), one
-// workgroup per CU with two waves per SIMD; k', V and 1/den stream through two
-// LDS chunk slots (direct-to-LDS loads, the next chunk in flight while one is
-// used).  Each of the 8 waves takes one 32-token block of a chunk and
-// accumulates its own share of the update; the shares and colsum_t(U) are
-// reduced in a fixed order at the end of each segment (deterministic).
+// workgroup per CU; k', V and 1/den stream through four LDS chunk slots
+// (direct-to-LDS loads, three chunks in flight while one is used: the chain is
+// bound by the bytes in flight per CU, not by its arithmetic).  Each wave takes
+// one 32-token block of a 128-token chunk and accumulates its own share of the
+// update; the shares and colsum_t(U) are reduced in a fixed order at the end of
+// each segment (deterministic).
 template <int D>
 __global__ __launch_bounds__(64 * kChainWaves, 1)
 void delta_chain_kernel(DeltaArgs a) {
@@ -317,14 +334,14 @@ void delta_chain_kernel(DeltaArgs a) {
   constexpr int NCB = D / kCB;
   constexpr int RG = NT / kCB;           // row groups of M (thread: column t % 16, rows RPT (t / 16) ..)
   constexpr int RPT = D / RG;
-  // two slots, each a distinct object so that reads of one slot never wait on
-  // loads into the other
-  __shared__ __attribute__((aligned(1024))) bf16 kp0[CL::KP_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 kp1[CL::KP_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 vc0[kChunk * kCB];
-  __shared__ __attribute__((aligned(1024))) bf16 vc1[kChunk * kCB];
-  __shared__ __attribute__((aligned(16))) float iv0[kInvSlot];
-  __shared__ __attribute__((aligned(16))) float iv1[kInvSlot];
+  // four slots, each a distinct object so that reads of one slot never wait on
+  // loads into another
+  static_assert(kChainSlots == 4, "the chunk loop is unrolled over the four slots");
+  __shared__ __attribute__((aligned(1024))) bf16 kp0[CL::KP_ELEMS], kp1[CL::KP_ELEMS], kp2[CL::KP_ELEMS],
+      kp3[CL::KP_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 vc0[kChunk * kCB], vc1[kChunk * kCB], vc2[kChunk * kCB],
+      vc3[kChunk * kCB];
+  __shared__ __attribute__((aligned(16))) float iv0[kInvSlot], iv1[kInvSlot], iv2[kInvSlot], iv3[kInvSlot];
   __shared__ __attribute__((aligned(16))) bf16 mts[kCB * D];   // M^T rows (bf16) of this block
   __shared__ float csred[RG][kCB];
   __shared__ float ucs[kChainWaves][kCB];
@@ -339,7 +356,7 @@ void delta_chain_kernel(DeltaArgs a) {
   cx.v = a.v + (int64_t)bh * a.L * D + cb * kCB;
   cx.inv = a.inv_den + (int64_t)bh * a.L;
   cx.N = a.N;
-  cx.cps = ((a.N + kChunk - 1) / kChunk + 1) & ~1;   // chunks per segment, padded to even
+  cx.cps = ((a.N + kChunk - 1) / kChunk + 3) & ~3;   // chunks per segment, padded to a multiple of 4
   cx.wave = wave;
   cx.lane = lane;
 
@@ -349,8 +366,10 @@ void delta_chain_kernel(DeltaArgs a) {
   for (int i = 0; i < RPT; ++i) m[i] = Mg[(int64_t)(mrow0 + i) * D + cb * kCB + mcol];
 
   chain_issue<D>(cx, 0, a.S, kp0, vc0, iv0);
-  chain_wait_all();
-  __syncthreads();
+  chain_issue<D>(cx, 1, a.S, kp1, vc1, iv1);
+  chain_issue<D>(cx, 2, a.S, kp2, vc2, iv2);
+  chain_wait_older<D>(wave);
+  lds_barrier();
 
   for (int s = 0; s < a.S; ++s) {
     const int64_t sh = (int64_t)bh * a.S + s;
@@ -364,7 +383,7 @@ void delta_chain_kernel(DeltaArgs a) {
       }
       csred[t / kCB][mcol] = part;     // t / kCB < RG
     }
-    __syncthreads();
+    lds_barrier();
     ChainSeg<D> sg;
     {
       const int col = lane & 15, g = lane >> 4;
@@ -386,40 +405,43 @@ void delta_chain_kernel(DeltaArgs a) {
     for (int k = 0; k < D / 16; ++k) sg.dm[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     sg.ucol = 0.f;
 
-    // ---- chunks: step c uses slot c % 2 and loads chunk c + 1 of the stream (the
-    // next segment's first chunk after the last) into the other slot.
+    // ---- chunks: step c uses slot c % 4 and loads chunk c + 3 of the stream
+    // (past the segment's end: the next segment's first chunks) into the slot of
+    // chunk c - 1, which every wave has finished with at the last barrier.
     const int q0 = s * cx.cps;
 #define INFINI_CHAIN_STEP(C, KC, VC, IC, KN, VN, IN)                                       \
     {                                                                                      \
       const int c_ = (C);                                                                  \
-      chain_issue<D>(cx, q0 + c_ + 1, a.S, KN, VN, IN);                                    \
+      chain_issue<D>(cx, q0 + c_ + 3, a.S, KN, VN, IN);                                    \
       chain_block<D>(sg, KC, VC, IC, wave);                                                \
-      chain_wait_all();                                                                    \
-      __syncthreads();                                                                     \
+      chain_wait_older<D>(wave);                                                           \
+      lds_barrier();                                                                     \
     }
-    for (int c = 0; c < cx.cps; c += 2) {
-      INFINI_CHAIN_STEP(c, kp0, vc0, iv0, kp1, vc1, iv1)
+    for (int c = 0; c < cx.cps; c += 4) {
+      INFINI_CHAIN_STEP(c, kp0, vc0, iv0, kp3, vc3, iv3)
       INFINI_CHAIN_STEP(c + 1, kp1, vc1, iv1, kp0, vc0, iv0)
+      INFINI_CHAIN_STEP(c + 2, kp2, vc2, iv2, kp1, vc1, iv1)
+      INFINI_CHAIN_STEP(c + 3, kp3, vc3, iv3, kp2, vc2, iv2)
     }
 #undef INFINI_CHAIN_STEP
 
-    // ---- M_s = M_{s-1} + 1 colsum_t(U) + sum over waves of k'^T U (slot 1 is free:
-    // the last chunk of the segment used it, the next one is in slot 0)
+    // ---- M_s = M_{s-1} + 1 colsum_t(U) + sum over waves of k'^T U (slot 3 is free:
+    // the last chunk of the segment used it, the next three are in slots 0-2)
     {
       const int col = lane & 15, g = lane >> 4;
       float uc = sg.ucol;
       uc += __shfl_xor(uc, 16);
       uc += __shfl_xor(uc, 32);
       if (g == 0) ucs[wave][col] = uc;
-      float* red = reinterpret_cast<float*>(kp1);          // [waves][D][16]
+      float* red = reinterpret_cast<float*>(kp3);          // [waves][D][16]
 #pragma unroll
       for (int k = 0; k < D / 16; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[(wave * D + 16 * k + 4 * g + r) * kCB + col] = sg.dm[k][r];
     }
-    __syncthreads();
+    lds_barrier();
     {
-      const float* red = reinterpret_cast<const float*>(kp1);
+      const float* red = reinterpret_cast<const float*>(kp3);
       float ucsum = 0.f;
 #pragma unroll
       for (int w = 0; w < kChainWaves; ++w) ucsum += ucs[w][mcol];
@@ -432,7 +454,7 @@ void delta_chain_kernel(DeltaArgs a) {
         m[i] += ucsum + d;
       }
     }
-    __syncthreads();   // slot 1, ucs and csred are reused by the next segment
+    lds_barrier();   // slot 3, ucs and csred are reused by the next segment
   }
 
 #pragma unroll
