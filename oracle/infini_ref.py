@@ -39,7 +39,14 @@ reason in the design notes of the repository):
 * the delta correction is segment-batched: every token of segment s reads the
   same M_{s-1} and z_{s-1}; z is updated exactly as in the linear rule;
 * the gate is g * A_mem + (1 - g) * A_dot with g = sigmoid(beta_h), one beta per
-  head shared over the batch, applied in every segment including the first.
+  head shared over the batch, applied in every segment including the first;
+* streaming (the pages' "streaming inference", abstract of the close-reading
+  page and point 4 of the key-idea list of the CSDN page): a token that arrives
+  before its segment is complete attends causally to the tokens of its segment
+  that have arrived (itself included) and reads the memory as of the segment's
+  start; the segment is folded into (M, z) once its N-th token has arrived.
+  Because the local attention is causal, this gives every token the output it
+  has when the segment is processed whole.
 
 Parity status per function (see the pins in ``tests/test_oracle_pins.py``):
 every function here is pinned by at least one closed form, invariant, special
@@ -96,6 +103,22 @@ def local_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: f
     n = q.shape[0]
     scores = scale * (q @ k.T)
     scores = np.where(causal_mask(n), scores, -np.inf)
+    row_max = scores.max(axis=1, keepdims=True)
+    p = np.exp(scores - row_max)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def prefix_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, offset: int,
+                            scale: float) -> np.ndarray:
+    """A_dot for queries that sit at positions offset, offset + 1, ... of a segment
+    whose first offset + len(q) keys and values are k, v: query i sees keys
+    j <= offset + i (close-reading page section 3.1 with the causal mask of
+    section 3.8 step 2, for a segment that has not received all its tokens)."""
+    n = q.shape[0]
+    scores = scale * (q @ k.T)
+    visible = np.arange(k.shape[0])[None, :] <= offset + np.arange(n)[:, None]
+    scores = np.where(visible, scores, -np.inf)
     row_max = scores.max(axis=1, keepdims=True)
     p = np.exp(scores - row_max)
     p = p / p.sum(axis=1, keepdims=True)
@@ -238,6 +261,62 @@ def forward_sequence(q, k, v, beta, rule, segment_len, M0=None, z0=None,
         out["A_dot"] = A_dot
         out["A_mem"] = A_mem
     return out
+
+
+def forward_stream(q, k, v, beta, rule, segment_len, M0=None, z0=None, segments_done=0,
+                   open_k=None, open_v=None, scale=None):
+    """Append T tokens per (batch, head) to a stream whose current segment already
+    holds the keys and values open_k, open_v ([B, H, f, d], f < segment_len; none
+    when omitted).  Each token is answered with the segment it falls in as it
+    stands when the token arrives (streaming reading in the module notes): local
+    causal attention over the segment's tokens up to itself, retrieval from the
+    memory as of the segment's start, gate; a segment is folded into (M, z) when
+    its last token arrives.
+
+    q, k: [B, H, T, d_key]; v: [B, H, T, d_value]; T >= 1 and any length.  Returns
+    a dict with A [B, H, T, d_value], the final M, z, segment count and the keys
+    and values of the segment left open (possibly empty)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, T, d_key = q.shape
+    d_value = v.shape[-1]
+    N = segment_len
+    sc = default_scale(d_key, scale)
+    M = np.zeros((B, H, d_key, d_value)) if M0 is None else np.array(M0, dtype=np.float64)
+    z = np.zeros((B, H, d_key)) if z0 is None else np.array(z0, dtype=np.float64)
+    f0 = 0 if open_k is None else np.asarray(open_k).shape[2]
+    if f0 >= N:
+        raise ValueError("the open segment must hold fewer than segment_len tokens")
+    A = np.zeros((B, H, T, d_value))
+    f_end = (f0 + T) % N                      # tokens left in the open segment
+    open_k_out = np.zeros((B, H, f_end, d_key))
+    open_v_out = np.zeros((B, H, f_end, d_value))
+    done = segments_done
+    for b in range(B):
+        for h in range(H):
+            seg_k = np.zeros((0, d_key)) if f0 == 0 else np.asarray(open_k[b, h], dtype=np.float64)
+            seg_v = np.zeros((0, d_value)) if f0 == 0 else np.asarray(open_v[b, h], dtype=np.float64)
+            done = segments_done
+            pos = 0
+            while pos < T:
+                f = seg_k.shape[0]
+                m = min(N - f, T - pos)
+                new = slice(pos, pos + m)
+                seg_k = np.concatenate([seg_k, k[b, h, new]])
+                seg_v = np.concatenate([seg_v, v[b, h, new]])
+                first = done == 0
+                a_mem = memory_retrieval(q[b, h, new], M[b, h], z[b, h], first)
+                a_dot = prefix_causal_attention(q[b, h, new], seg_k, seg_v, f, sc)
+                A[b, h, new] = gate(beta[h], a_mem, a_dot)
+                if f + m == N:
+                    M[b, h], z[b, h] = memory_update(seg_k, seg_v, M[b, h], z[b, h], rule, first)
+                    seg_k, seg_v = np.zeros((0, d_key)), np.zeros((0, d_value))
+                    done += 1
+                pos += m
+            open_k_out[b, h] = seg_k
+            open_v_out[b, h] = seg_v
+    return {"A": A, "M": M, "z": z, "segments_done": done, "open_k": open_k_out, "open_v": open_v_out}
 
 
 def state_floats_per_head(d_key: int, d_value: int) -> int:

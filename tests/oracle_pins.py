@@ -297,6 +297,77 @@ def pin_stream_equals_chained_segments(o):
         assert np.allclose(z, whole["z"], rtol=1e-14, atol=0)
 
 
+def pin_prefix_attention_is_masked_sdpa(o):
+    """Queries at positions f, f + 1, ... of a segment prefix attend to keys j <= f + i:
+    torch's scaled_dot_product_attention with that boolean mask."""
+    f, m, dk, dv = 5, 4, 3, 2
+    q, k, v = _randn(160, m, dk), _randn(161, f + m, dk), _randn(162, f + m, dv)
+    mask = np.arange(f + m)[None, :] <= f + np.arange(m)[:, None]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=torch.from_numpy(mask))
+    assert np.allclose(o.prefix_causal_attention(q, k, v, f, 1.0 / math.sqrt(dk)), ref[0, 0].numpy(),
+                       rtol=1e-13, atol=1e-14)
+
+
+def pin_stream_of_whole_segments_equals_forward_sequence(o):
+    """Appending whole segments to an empty open segment is forward_sequence (every
+    segment completes, so each is processed whole)."""
+    B, H, S, N, dk, dv = 1, 2, 3, 4, 3, 3
+    q, k, v = _stream(170, B, H, S, N, dk, dv)
+    beta = np.array([0.4, -0.7])
+    for rule in (o.RULE_LINEAR, o.RULE_DELTA):
+        a = o.forward_stream(q, k, v, beta, rule, N)
+        b = o.forward_sequence(q, k, v, beta, rule, N)
+        assert np.allclose(a["A"], b["A"], rtol=1e-13, atol=1e-14)
+        assert np.allclose(a["M"], b["M"], rtol=1e-13, atol=1e-13)
+        assert np.allclose(a["z"], b["z"], rtol=1e-14, atol=0)
+        assert a["segments_done"] == S and a["open_k"].shape[2] == 0
+
+
+def pin_stream_outputs_do_not_depend_on_chunking(o):
+    """Feeding a ragged stream in chunks of 1, 2, N - 1, N + 2, ... tokens (carrying the
+    state and the open segment) gives the outputs, state and open segment of one
+    call: the streaming reading makes a token's output a function of the stream
+    up to it."""
+    B, H, N, dk, dv, T = 1, 2, 4, 3, 2, 23
+    q, k, v = (_randn(180 + i, B, H, T, d) for i, d in enumerate((dk, dk, dv)))
+    beta = np.array([1.1, -0.3])
+    for rule in (o.RULE_LINEAR, o.RULE_DELTA):
+        whole = o.forward_stream(q, k, v, beta, rule, N)
+        M = z = ok = ov = None
+        done, pos, A = 0, 0, []
+        for c in (1, 2, 3, 1, 6, 2, 5, 3):
+            r = slice(pos, pos + c)
+            part = o.forward_stream(q[:, :, r], k[:, :, r], v[:, :, r], beta, rule, N, M0=M, z0=z,
+                                    segments_done=done, open_k=ok, open_v=ov)
+            A.append(part["A"])
+            M, z, done, ok, ov = part["M"], part["z"], part["segments_done"], part["open_k"], part["open_v"]
+            pos += c
+        assert pos == T and done == whole["segments_done"] == T // N
+        assert np.allclose(np.concatenate(A, axis=2), whole["A"], rtol=1e-12, atol=1e-13)
+        assert np.allclose(M, whole["M"], rtol=1e-12, atol=1e-12)
+        assert np.allclose(ok, whole["open_k"]) and np.allclose(ov, whole["open_v"])
+        assert ok.shape[2] == T % N
+
+
+def pin_open_segment_rows_match_whole_segment(o):
+    """The first p tokens of a segment, answered before the rest arrive, get the rows
+    they get when the segment is processed whole (the local attention is causal),
+    and (M, z) do not change until the segment's last token has arrived."""
+    B, H, S, N, dk, dv = 1, 1, 2, 5, 3, 3
+    q, k, v = _stream(190, B, H, S, N, dk, dv)
+    beta = np.array([0.25])
+    for rule in (o.RULE_LINEAR, o.RULE_DELTA):
+        whole = o.forward_sequence(q, k, v, beta, rule, N)
+        first_seg = o.forward_sequence(q[:, :, :N], k[:, :, :N], v[:, :, :N], beta, rule, N)
+        for p in range(1, N):
+            r = slice(0, N + p)
+            part = o.forward_stream(q[:, :, r], k[:, :, r], v[:, :, r], beta, rule, N)
+            assert np.allclose(part["A"], whole["A"][:, :, r], rtol=1e-13, atol=1e-14)
+            assert part["segments_done"] == 1
+            assert np.array_equal(part["M"], first_seg["M"]) and np.array_equal(part["z"], first_seg["z"])
+
+
 def pin_state_size_matches_table_1(o):
     """The carried state of one head is d_key x d_value + d_key numbers, for any
     segment count (close-reading page section 3.7, Table 1)."""

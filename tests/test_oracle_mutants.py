@@ -98,7 +98,40 @@ def _write_before_read(q, k, v, M, z, beta, rule, first, scale):
     return o.gate(beta, a_mem, a_dot), M2, z2, a_dot, a_mem
 
 
+def _prefix_mask_excludes_diagonal(q, k, v, offset, scale):
+    scores = scale * (q @ k.T)
+    visible = np.arange(k.shape[0])[None, :] < offset + np.arange(q.shape[0])[:, None]
+    scores = np.where(visible, scores, -np.inf)
+    p = np.exp(scores - scores.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+def _prefix_offset_ignored(q, k, v, offset, scale):
+    return _real_prefix(q, k, v, 0, scale)
+
+
+_real_prefix = o.prefix_causal_attention
+_real_stream = o.forward_stream
+
+
+def _stream_commits_every_call(q, k, v, beta, rule, segment_len, M0=None, z0=None, segments_done=0,
+                               open_k=None, open_v=None, scale=None):
+    # folds whatever the call brought into the memory, complete segment or not
+    res = _real_stream(q, k, v, beta, rule, segment_len, M0, z0, segments_done, open_k, open_v, scale)
+    if res["open_k"].shape[2]:
+        M, z = res["M"].copy(), res["z"].copy()
+        for b in range(M.shape[0]):
+            for h in range(M.shape[1]):
+                M[b, h], z[b, h] = o.memory_update(res["open_k"][b, h], res["open_v"][b, h], M[b, h], z[b, h],
+                                                   rule, res["segments_done"] == 0)
+        res = dict(res, M=M, z=z, open_k=res["open_k"][:, :, :0], open_v=res["open_v"][:, :, :0])
+    return res
+
+
 MUTANTS = {
+    "prefix_mask_excludes_diagonal": ("prefix_causal_attention", _prefix_mask_excludes_diagonal),
+    "prefix_offset_ignored": ("prefix_causal_attention", _prefix_offset_ignored),
+    "stream_commits_every_call": ("forward_stream", _stream_commits_every_call),
     "mask_excludes_diagonal": ("causal_mask", _strict_mask),
     "scale_uses_model_width": ("default_scale", _scale_model_width),
     "sigma_is_plain_elu": ("sigma", _elu_without_plus_one),
