@@ -8,6 +8,7 @@
 //   bf16, delta : delta_chain (persistent, sequential over segments, snapshots and
 //                 the final state) -> fused attention kernel
 //   fp32        : per segment, attention (reads M_{s-1}, z_{s-1}) then update
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -86,8 +87,10 @@ struct WsLayout {
   size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, kp = 0, czp = 0, inv = 0, U = 0, total = 0;
 };
 
-// Workspace regions, each 256-byte aligned.  Returns false on overflow.
-bool workspace_layout(const infini_attn_state* st, int64_t S, WsLayout* w) {
+// Workspace regions for S segments whose tokens sit at a row stride of L per
+// (b, h) (L = S * N for a whole stream), each 256-byte aligned.  Returns false on
+// overflow.
+bool workspace_layout(const infini_attn_state* st, int64_t S, int64_t L, WsLayout* w) {
   const int64_t BH = (int64_t)st->batch * st->heads;
   int64_t seg_heads, n;
   if (!mul_ok(BH, S, &seg_heads)) return false;
@@ -103,7 +106,7 @@ bool workspace_layout(const infini_attn_state* st, int64_t S, WsLayout* w) {
       w->cz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
     } else {
       int64_t tokens, parts;
-      if (!mul_ok(BH, S * (int64_t)st->segment_len, &tokens)) return false;
+      if (!mul_ok(BH, L, &tokens)) return false;
       if (!mul_ok(seg_heads, D, &parts)) return false;
       w->kp = off; off = align_up(off + (size_t)tokens * D * 2);
       w->czp = off; off = align_up(off + (size_t)parts * 4);
@@ -190,6 +193,65 @@ int run_f32(infini_attn_state* st, const void* q, const void* k, const void* v, 
   return record(events, 2, stream);
 }
 
+// ------------------------------------------------------------------ open segment
+// Workspace of infini_attn_append for n tokens: the largest of the three stages
+// it runs one after another on the stream (whole segments straight from the
+// input at a row stride of n, the commit of a completed open segment, and the
+// open-segment attention's key partitions).
+bool append_layout(const infini_attn_state* st, int64_t n, WsLayout* whole, WsLayout* one, size_t* part_off,
+                   size_t* total) {
+  const int64_t N = st->segment_len, BH = (int64_t)st->batch * st->heads;
+  const int64_t S = n / N;
+  if (S > 0 && !workspace_layout(st, S, n, whole)) return false;
+  if (!workspace_layout(st, 1, N, one)) return false;
+  const int64_t mq = n < N - 1 ? n : N - 1;   // queries of one open-segment piece
+  int64_t parts;
+  if (!mul_ok(BH * mq, (int64_t)infini::open_attn_parts((int)N) * (st->d_value + 2), &parts)) return false;
+  *part_off = 0;
+  size_t t = one->total;
+  if (S > 0 && whole->total > t) t = whole->total;
+  if (align_up((size_t)parts * 4) > t) t = align_up((size_t)parts * 4);
+  *total = t;
+  return true;
+}
+
+// Folds the completed open segment (N tokens per (b, h) in k_open, v_open) into
+// (M, z) with the state's rule.
+int commit_open(infini_attn_state* st, const infini_attn_open_segment* os, char* ws, const WsLayout& w,
+                hipStream_t stream) {
+  const int B = st->batch, H = st->heads, N = st->segment_len;
+  hipError_t e;
+  if (st->dtype == INFINI_BF16) {
+    using infini::bf16;
+    bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
+    float* snapz = reinterpret_cast<float*>(ws + w.snapz);
+    float* snapc = reinterpret_cast<float*>(ws + w.snapc);
+    const bf16* k = static_cast<const bf16*>(os->k_open);
+    const bf16* v = static_cast<const bf16*>(os->v_open);
+    if (st->rule == INFINI_RULE_LINEAR) {
+      infini::LinContribArgs c{k, v, reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
+                               B, H, 1, N, N};
+      infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, snapc, B * H, 1};
+      e = st->d_key == 128 ? infini::launch_lin_contrib<128>(c, stream) : infini::launch_lin_contrib<64>(c, stream);
+      if (e != hipSuccess) return hip_fail(e, "lin_contrib launch");
+      e = st->d_key == 128 ? infini::launch_lin_scan<128>(sarg, stream) : infini::launch_lin_scan<64>(sarg, stream);
+      if (e != hipSuccess) return hip_fail(e, "lin_scan launch");
+    } else {
+      infini::DeltaArgs d{k, v, st->M, st->z, snapM, snapz, snapc, reinterpret_cast<bf16*>(ws + w.kp),
+                          reinterpret_cast<float*>(ws + w.czp), reinterpret_cast<float*>(ws + w.inv), B * H, 1, N,
+                          (int64_t)N, st->segments_done, 0};
+      e = st->d_key == 128 ? infini::launch_delta_state<128>(d, stream) : infini::launch_delta_state<64>(d, stream);
+      if (e != hipSuccess) return hip_fail(e, "delta state launch");
+    }
+  } else {
+    infini::F32UpdateArgs u{static_cast<const float*>(os->k_open), static_cast<const float*>(os->v_open), st->M,
+                            st->z, reinterpret_cast<float*>(ws + w.U), B * H, N, st->d_key, st->d_value,
+                            (int64_t)N, 0, st->rule == INFINI_RULE_DELTA, st->segments_done > 0};
+    if ((e = infini::launch_f32_update(u, stream)) != hipSuccess) return hip_fail(e, "f32 update launch");
+  }
+  return INFINI_OK;
+}
+
 int zero_state(infini_attn_state* st, float* M, float* z, hipStream_t stream) {
   const int64_t BH = (int64_t)st->batch * st->heads;
   const hipError_t e = infini::launch_fill_zero(M, BH * st->d_key * st->d_value, z, BH * st->d_key, stream);
@@ -238,7 +300,7 @@ size_t infini_attn_workspace_bytes(const infini_attn_state* st, int64_t seq_len)
   if (check_state(st) != INFINI_OK) return 0;
   if (seq_len <= 0 || seq_len % st->segment_len != 0) return 0;
   WsLayout w;
-  if (!workspace_layout(st, seq_len / st->segment_len, &w)) return 0;
+  if (!workspace_layout(st, seq_len / st->segment_len, seq_len, &w)) return 0;
   return w.total;
 }
 
@@ -272,7 +334,7 @@ static int forward_impl(infini_attn_state* st, const void* q, const void* k, con
   if (overlaps(out, out_bytes, st->M, m_bytes) || overlaps(out, out_bytes, st->z, z_bytes))
     return fail(INFINI_EINVAL, "out must not alias the state");
   WsLayout w;
-  if (!workspace_layout(st, S, &w)) return fail(INFINI_EINVAL, "workspace size overflows");
+  if (!workspace_layout(st, S, seq_len, &w)) return fail(INFINI_EINVAL, "workspace size overflows");
   if (!workspace || workspace_bytes < w.total)
     return fail(INFINI_EWORKSPACE, "workspace of %zu bytes required, %zu given%s", w.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -319,6 +381,143 @@ int infini_attn_forward_segment(infini_attn_state* st, const void* q, const void
                                 void* stream) {
   if (!st) return fail(INFINI_EINVAL, "state pointer is NULL");
   return infini_attn_forward_sequence(st, q, k, v, st->segment_len, beta, out, workspace, workspace_bytes, stream);
+}
+
+int infini_attn_open_segment_init(const infini_attn_state* st, infini_attn_open_segment* os, void* k_open,
+                                  void* v_open) {
+  int rc = check_state(st);
+  if (rc != INFINI_OK) return rc;
+  if (!os) return fail(INFINI_EINVAL, "open-segment pointer is NULL");
+  if (!k_open || !v_open) return fail(INFINI_EINVAL, "open-segment buffers must be device pointers (got NULL)");
+  const uintptr_t align = st->dtype == INFINI_BF16 ? 16 : 4;
+  if ((reinterpret_cast<uintptr_t>(k_open) | reinterpret_cast<uintptr_t>(v_open)) % align != 0)
+    return fail(INFINI_EINVAL, "open-segment buffers must be %d-byte aligned", (int)align);
+  const int64_t BH = (int64_t)st->batch * st->heads;
+  const size_t esz = st->dtype == INFINI_BF16 ? 2 : 4;
+  const size_t kb = (size_t)BH * st->segment_len * st->d_key * esz, vb = (size_t)BH * st->segment_len * st->d_value * esz;
+  const size_t mb = (size_t)BH * st->d_key * st->d_value * 4, zb = (size_t)BH * st->d_key * 4;
+  if (overlaps(k_open, kb, v_open, vb) || overlaps(k_open, kb, st->M, mb) || overlaps(k_open, kb, st->z, zb) ||
+      overlaps(v_open, vb, st->M, mb) || overlaps(v_open, vb, st->z, zb))
+    return fail(INFINI_EINVAL, "open-segment buffers must not overlap each other or the state");
+  os->k_open = k_open;
+  os->v_open = v_open;
+  os->filled = 0;
+  return ok();
+}
+
+size_t infini_attn_append_workspace_bytes(const infini_attn_state* st, int64_t n_tokens) {
+  if (check_state(st) != INFINI_OK || n_tokens < 1) return 0;
+  WsLayout whole, one;
+  size_t part_off, total;
+  if (!append_layout(st, n_tokens, &whole, &one, &part_off, &total)) return 0;
+  return total;
+}
+
+int infini_attn_append(infini_attn_state* st, infini_attn_open_segment* os, const void* q, const void* k,
+                       const void* v, int64_t n_tokens, const float* beta, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = check_state(st);
+  if (rc != INFINI_OK) return rc;
+  if (!os) return fail(INFINI_EINVAL, "open-segment pointer is NULL");
+  const int N = st->segment_len;
+  if (!os->k_open || !os->v_open || os->filled < 0 || os->filled >= N)
+    return fail(INFINI_EINVAL, "open segment not initialised (buffers NULL or filled %d outside [0, %d))",
+                os->filled, N);
+  if (!q || !k || !v || !beta || !out) return fail(INFINI_EINVAL, "q, k, v, beta and out must be non-NULL");
+  if (n_tokens < 1) return fail(INFINI_EINVAL, "n_tokens must be positive (got %lld)", (long long)n_tokens);
+  const int64_t BH = (int64_t)st->batch * st->heads;
+  int64_t rows, nqk, nvo;
+  if (!mul_ok(BH, n_tokens, &rows) || !mul_ok(rows, st->d_key, &nqk) || !mul_ok(rows, st->d_value, &nvo))
+    return fail(INFINI_EINVAL, "tensor sizes overflow");
+  if (n_tokens / N > 0x7fffffff) return fail(INFINI_EINVAL, "too many segments");
+  const size_t esz = st->dtype == INFINI_BF16 ? 2 : 4;
+  const uintptr_t align = st->dtype == INFINI_BF16 ? 16 : 4;
+  for (const void* p : {q, k, v, static_cast<const void*>(out), static_cast<const void*>(os->k_open),
+                        static_cast<const void*>(os->v_open)})
+    if (reinterpret_cast<uintptr_t>(p) % align != 0)
+      return fail(INFINI_EINVAL, "q, k, v, out and the open-segment buffers must be %d-byte aligned", (int)align);
+  if (reinterpret_cast<uintptr_t>(beta) % 4 != 0) return fail(INFINI_EINVAL, "beta must be 4-byte aligned");
+  const size_t out_bytes = (size_t)nvo * esz;
+  const size_t kob = (size_t)BH * N * st->d_key * esz, vob = (size_t)BH * N * st->d_value * esz;
+  const size_t m_bytes = (size_t)BH * st->d_key * st->d_value * 4, z_bytes = (size_t)BH * st->d_key * 4;
+  if (overlaps(out, out_bytes, q, (size_t)nqk * esz) || overlaps(out, out_bytes, k, (size_t)nqk * esz) ||
+      overlaps(out, out_bytes, v, (size_t)nvo * esz) || overlaps(out, out_bytes, st->M, m_bytes) ||
+      overlaps(out, out_bytes, st->z, z_bytes) || overlaps(out, out_bytes, os->k_open, kob) ||
+      overlaps(out, out_bytes, os->v_open, vob))
+    return fail(INFINI_EINVAL, "out must not alias q, k, v, the state or the open-segment buffers");
+  WsLayout whole, one;
+  size_t part_off, total;
+  if (!append_layout(st, n_tokens, &whole, &one, &part_off, &total))
+    return fail(INFINI_EINVAL, "workspace size overflows");
+  if (!workspace || workspace_bytes < total)
+    return fail(INFINI_EWORKSPACE, "workspace of %zu bytes required, %zu given%s", total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(INFINI_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (overlaps(workspace, total, out, out_bytes) || overlaps(workspace, total, st->M, m_bytes) ||
+      overlaps(workspace, total, st->z, z_bytes) || overlaps(workspace, total, os->k_open, kob) ||
+      overlaps(workspace, total, os->v_open, vob))
+    return fail(INFINI_EWORKSPACE, "workspace must not alias out, the state or the open-segment buffers");
+  if (st->dtype == INFINI_BF16 && n_tokens >= N) {
+    const int64_t fa_blocks = infini::fa_fwd_blocks(BH * (n_tokens / N), N);
+    if (fa_blocks > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
+  }
+  if (BH > 65535) return fail(INFINI_EUNSUPPORTED, "batch * heads above 65535 for the open-segment kernels");
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const char* qb = static_cast<const char*>(q);
+  const char* kb = static_cast<const char*>(k);
+  const char* vb = static_cast<const char*>(v);
+  char* ob = static_cast<char*>(out);
+  const size_t qrow = (size_t)st->d_key * esz, vrow = (size_t)st->d_value * esz;
+  infini_attn_state s = *st;
+  infini_attn_open_segment o = *os;
+  int64_t t = 0;
+  while (t < n_tokens) {
+    if (o.filled > 0 || n_tokens - t < N) {
+      // into the open segment: copy the keys and values, then answer the queries
+      const int m = (int)std::min<int64_t>(N - o.filled, n_tokens - t);
+      hipError_t e = hipMemcpy2DAsync(static_cast<char*>(o.k_open) + (size_t)o.filled * qrow, (size_t)N * qrow,
+                                      kb + (size_t)t * qrow, (size_t)n_tokens * qrow, (size_t)m * qrow,
+                                      (size_t)BH, hipMemcpyDeviceToDevice, strm);
+      if (e != hipSuccess) return hip_fail(e, "open-segment key copy");
+      e = hipMemcpy2DAsync(static_cast<char*>(o.v_open) + (size_t)o.filled * vrow, (size_t)N * vrow,
+                           vb + (size_t)t * vrow, (size_t)n_tokens * vrow, (size_t)m * vrow, (size_t)BH,
+                           hipMemcpyDeviceToDevice, strm);
+      if (e != hipSuccess) return hip_fail(e, "open-segment value copy");
+      infini::OpenAttnArgs a{qb + (size_t)t * qrow, o.k_open, o.v_open, beta, s.M, s.z, ob + (size_t)t * vrow,
+                             reinterpret_cast<float*>(ws + part_off), (int)BH, s.heads, N, s.d_key, s.d_value, m,
+                             o.filled, 0, n_tokens, s.segments_done > 0, s.dtype == INFINI_BF16, s.scale};
+      if ((e = infini::launch_open_attn(a, strm)) != hipSuccess) return hip_fail(e, "open-segment attention launch");
+      o.filled += m;
+      t += m;
+      if (o.filled == N) {
+        if ((rc = commit_open(&s, &o, ws, one, strm)) != INFINI_OK) return rc;
+        s.segments_done += 1;
+        o.filled = 0;
+      }
+    } else {
+      // whole segments straight from the input (row stride n_tokens per (b, h))
+      const int S = (int)((n_tokens - t) / N);
+      if (s.dtype == INFINI_BF16) {
+        rc = s.d_key == 128
+                 ? run_bf16<128>(&s, qb + t * qrow, kb + t * qrow, vb + t * vrow, n_tokens, S, beta,
+                                 ob + t * vrow, ws, whole, strm, nullptr)
+                 : run_bf16<64>(&s, qb + t * qrow, kb + t * qrow, vb + t * vrow, n_tokens, S, beta,
+                                ob + t * vrow, ws, whole, strm, nullptr);
+      } else {
+        rc = run_f32(&s, qb + t * qrow, kb + t * qrow, vb + t * vrow, n_tokens, S, beta, ob + t * vrow, ws, whole,
+                     strm, nullptr);
+      }
+      if (rc != INFINI_OK) return rc;
+      s.segments_done += S;
+      t += (int64_t)S * N;
+    }
+  }
+  *st = s;
+  *os = o;
+  return ok();
 }
 
 int infini_attn_reset(infini_attn_state* st, void* stream) {

@@ -109,6 +109,29 @@ struct F32UpdateArgs {
 };
 hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------ open segment
+// Queries j < m that arrive at positions pos0 + j of an open segment whose keys
+// and values (rows bh * N + t, t < pos0 + m) are already in kseg / vseg; the
+// memory (M, z) is read as it stands.  Query and output row j of head bh is
+// bh * q_stride + j.  part: workspace [BH][m][P][dv + 2] (P set by the launcher).
+struct OpenAttnArgs {
+  const void* q;
+  const void* kseg;
+  const void* vseg;
+  const float* beta;
+  const float* M;
+  const float* z;
+  void* out;
+  float* part;
+  int BH, H, N, dk, dv, m, pos0, P;
+  int64_t q_stride;
+  int has_memory, bf16;
+  float scale;
+};
+hipError_t launch_open_attn(const OpenAttnArgs& a, hipStream_t stream);
+// Key partitions of the open-segment attention for `keys` keys.
+int open_attn_parts(int keys);
+
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);
 

@@ -58,6 +58,15 @@ class State(ctypes.Structure):
 _lib = None
 
 
+class OpenSegment(ctypes.Structure):
+    """Mirror of infini_attn_open_segment."""
+    _fields_ = [
+        ("k_open", ctypes.c_void_p),
+        ("v_open", ctypes.c_void_p),
+        ("filled", ctypes.c_int32),
+    ]
+
+
 def load_library(path: str | None = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
@@ -85,6 +94,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_forward_sequence_profiled.restype = ctypes.c_int
     lib.infini_attn_forward_segment.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.infini_attn_forward_segment.restype = ctypes.c_int
+    op = ctypes.POINTER(OpenSegment)
+    lib.infini_attn_open_segment_init.argtypes = [sp, op, vp, vp]
+    lib.infini_attn_open_segment_init.restype = ctypes.c_int
+    lib.infini_attn_append_workspace_bytes.argtypes = [sp, i64]
+    lib.infini_attn_append_workspace_bytes.restype = sz
+    lib.infini_attn_append.argtypes = [sp, op, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    lib.infini_attn_append.restype = ctypes.c_int
     lib.infini_attn_reset.argtypes = [sp, vp]
     lib.infini_attn_reset.restype = ctypes.c_int
     lib.infini_attn_last_error.argtypes = []
@@ -158,6 +174,23 @@ def forward_segment(st: State, q, k, v, beta, out, workspace, ws_bytes, stream=N
     return _check(rc) if check else rc
 
 
+def open_segment_init(st: State, os_: OpenSegment, k_open, v_open, check=True) -> int:
+    rc = load_library().infini_attn_open_segment_init(ctypes.byref(st), ctypes.byref(os_), _ptr(k_open),
+                                                      _ptr(v_open))
+    return _check(rc) if check else rc
+
+
+def append_workspace_bytes(st: State, n_tokens: int) -> int:
+    return load_library().infini_attn_append_workspace_bytes(ctypes.byref(st), n_tokens)
+
+
+def append(st: State, os_: OpenSegment, q, k, v, n_tokens, beta, out, workspace, ws_bytes, stream=None,
+           check=True) -> int:
+    rc = load_library().infini_attn_append(ctypes.byref(st), ctypes.byref(os_), _ptr(q), _ptr(k), _ptr(v),
+                                           n_tokens, _ptr(beta), _ptr(out), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
 def reset(st: State, stream=None, check=True) -> int:
     rc = load_library().infini_attn_reset(ctypes.byref(st), stream)
     return _check(rc) if check else rc
@@ -226,3 +259,38 @@ class InfiniAttention:
 
     def reset(self, stream=None):
         reset(self.state, _stream_handle(self.torch, stream))
+        if getattr(self, "open", None) is not None:
+            open_segment_init(self.state, self.open, self.k_open, self.v_open)
+
+    def open_stream(self):
+        """Allocates the open-segment buffers ([B, H, N, d]) and empties the open
+        segment; append() then takes tokens in any number per call."""
+        B, H, N = self.state.batch, self.state.heads, self.state.segment_len
+        dt = self.torch_dtype
+        self.k_open = self.torch.empty((B, H, N, self.state.d_key), dtype=dt, device=self.device)
+        self.v_open = self.torch.empty((B, H, N, self.state.d_value), dtype=dt, device=self.device)
+        self.open = OpenSegment()
+        open_segment_init(self.state, self.open, self.k_open, self.v_open)
+
+    @property
+    def filled(self) -> int:
+        return int(self.open.filled)
+
+    def append_workspace(self, n_tokens: int):
+        need = append_workspace_bytes(self.state, n_tokens)
+        if need == 0:
+            raise InfiniError(EINVAL, f"no workspace size for n_tokens={n_tokens}")
+        if self._ws_bytes < need:
+            raw = self.torch.empty(need + 256, dtype=self.torch.uint8, device=self.device)
+            off = (-raw.data_ptr()) % 256
+            self._ws_raw, self._ws, self._ws_bytes = raw, raw[off:off + need], need
+        return self._ws, self._ws_bytes
+
+    def append(self, q, k, v, beta, out=None, stream=None):
+        """Appends q.shape[2] tokens per (b, h) (see open_stream)."""
+        n = q.shape[2]
+        if out is None:
+            out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
+        ws, nbytes = self.append_workspace(n)
+        append(self.state, self.open, q, k, v, n, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
+        return out

@@ -124,6 +124,50 @@ int infini_attn_forward_segment(infini_attn_state *st, const void *q, const void
                                 const void *v, const float *beta, void *out,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Open segment: streaming inference and ragged tails ("streaming inference",
+ * abstract of the page "精读笔记：Infini-attention"; point 4 of the key-idea list
+ * of the page "忘记遗忘：解锁无限上下文的 Infini-attention").
+ *
+ * Tokens may arrive in any number per call, one at a time (decode) included.  A
+ * token that arrives before its segment is complete is answered with the
+ * segment as it stands: local causal attention over the segment's tokens that
+ * have arrived (itself included), retrieval from (M, z) as of the segment's
+ * start, the gate.  The segment is folded into (M, z) when its N-th token
+ * arrives.  Because the local attention is causal, every token gets the output
+ * it gets when its segment is processed whole; appending whole segments at a
+ * segment boundary runs the segment path of forward_sequence (bitwise the same
+ * results).  The keys and values of the open segment live in caller-owned
+ * device buffers; the fill level is kept on the host. */
+typedef struct {
+  void *k_open;    /* device [B, H, N, d_key], dtype of the state, caller-owned */
+  void *v_open;    /* device [B, H, N, d_value], caller-owned */
+  int32_t filled;  /* tokens of the open segment held in k_open / v_open, 0 <= filled < N */
+} infini_attn_open_segment;
+
+/* Binds the buffers to *os and empties the open segment (filled = 0); no HIP
+ * call.  The buffers must not overlap each other or the state.  Call it again
+ * after infini_attn_reset. */
+int infini_attn_open_segment_init(const infini_attn_state *st, infini_attn_open_segment *os,
+                                  void *k_open, void *v_open);
+
+/* Bytes of device workspace that infini_attn_append needs for n_tokens tokens
+ * (0 for an invalid state or n_tokens < 1). */
+size_t infini_attn_append_workspace_bytes(const infini_attn_state *st, int64_t n_tokens);
+
+/* Appends n_tokens tokens per (b, h) to the stream of *st / *os and writes their
+ * outputs: q, k: [B, H, n_tokens, d_key]; v, out: [B, H, n_tokens, d_value];
+ * beta: device fp32 [H].  Completed segments are folded into (M, z)
+ * (segments_done += 1 each) and the open segment restarts empty; os->filled
+ * ends at (filled + n_tokens) % N.  The workspace rules are those of
+ * forward_sequence with infini_attn_append_workspace_bytes.  out must not alias
+ * q, k, v, the state, the open-segment buffers or the workspace.  Do not mix
+ * with forward_sequence / forward_segment while the open segment holds tokens
+ * (those start at a segment boundary). */
+int infini_attn_append(infini_attn_state *st, infini_attn_open_segment *os, const void *q,
+                       const void *k, const void *v, int64_t n_tokens, const float *beta,
+                       void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* M, z <- 0 on `stream`; segments_done <- 0. */
 int infini_attn_reset(infini_attn_state *st, void *stream);
 

@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 8
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -43,6 +43,7 @@ def test_exports_every_declared_function():
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(ia.State) == 56
     assert ia.State.M.offset == 32 and ia.State.segments_done.offset == 48
+    assert ctypes.sizeof(ia.OpenSegment) == 24 and ia.OpenSegment.filled.offset == 16
 
 
 @pytest.mark.parametrize("args,code", [
@@ -147,3 +148,73 @@ def test_segment_and_reset_validate():
     assert ia.reset(ia.State(), None, check=False) == ia.EINVAL
     assert ia.load_library().infini_attn_reset(None, None) == ia.EINVAL
     assert _snapshot(st) == before
+
+
+def _open(st, filled=0):
+    os_ = ia.OpenSegment()
+    assert ia.open_segment_init(st, os_, FAKE * 10, FAKE * 12, check=False) == ia.OK
+    os_.filled = filled
+    return os_
+
+
+def test_open_segment_init_validates():
+    st = _state()
+    os_ = ia.OpenSegment()
+    assert ia.open_segment_init(st, os_, None, FAKE, check=False) == ia.EINVAL
+    assert ia.open_segment_init(st, os_, FAKE * 10 + 2, FAKE * 12, check=False) == ia.EINVAL
+    assert ia.open_segment_init(st, os_, FAKE * 10, FAKE * 10 + 4096, check=False) == ia.EINVAL  # overlap
+    assert ia.open_segment_init(ia.State(), os_, FAKE * 10, FAKE * 12, check=False) == ia.EINVAL
+    assert ia.load_library().infini_attn_open_segment_init(ctypes.byref(st), None, FAKE, FAKE * 2) == ia.EINVAL
+    os_.filled = 7
+    assert ia.open_segment_init(st, os_, FAKE * 10, FAKE * 12) == ia.OK
+    assert os_.filled == 0 and os_.k_open == FAKE * 10 and os_.v_open == FAKE * 12
+
+
+def test_append_workspace_bytes():
+    st = _state()                       # bf16, linear, N = 2048, BH = 2, d = 128
+    one = ia.workspace_bytes(st, 2048)  # the commit of one segment
+    parts = 2 * 1 * 16 * 130 * 4        # one query: 16 key partitions of d_value + 2 floats
+    assert ia.append_workspace_bytes(st, 1) == max(one, -(-parts // 256) * 256)
+    assert ia.append_workspace_bytes(st, 3 * 2048 + 5) >= ia.workspace_bytes(st, 3 * 2048)
+    assert ia.append_workspace_bytes(st, 0) == 0
+    assert ia.append_workspace_bytes(ia.State(), 1) == 0
+
+
+@pytest.mark.parametrize("case", ["null_q", "null_os", "zero_len", "filled_range", "unbound", "small_ws",
+                                  "misaligned", "alias_open", "alias_state"])
+def test_append_rejects_bad_arguments(case):
+    st = _state()
+    os_ = _open(st, filled=5)
+    n = 3
+    need = ia.append_workspace_bytes(st, n)
+    q, k, v, beta = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7
+    out, ws, nbytes = FAKE * 8, FAKE * 9, need
+    expect = ia.EINVAL
+    if case == "null_q":
+        q = None
+    elif case == "null_os":
+        os_ = None
+    elif case == "zero_len":
+        n = 0
+    elif case == "filled_range":
+        os_.filled = 2048
+    elif case == "unbound":
+        os_ = ia.OpenSegment()
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    elif case == "misaligned":
+        v = FAKE * 6 + 8
+    elif case == "alias_open":
+        out = FAKE * 12 + 512
+    elif case == "alias_state":
+        out = st.z
+    before = _snapshot(st)
+    fill_before = None if os_ is None else os_.filled
+    lib = ia.load_library()
+    rc = lib.infini_attn_append(ctypes.byref(st), None if os_ is None else ctypes.byref(os_), q, k, v, n, beta, out,
+                                ws, nbytes, None)
+    assert rc == expect, ia.last_error()
+    assert ia.last_error()
+    assert _snapshot(st) == before
+    if os_ is not None:
+        assert os_.filled == fill_before
