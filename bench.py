@@ -44,6 +44,10 @@ def parse():
     p.add_argument("--rule", default=None)
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="budget of the oracle leg (0 disables it)")
+    p.add_argument("--decode", type=int, default=0, metavar="FILLED",
+                   help="time single-token decode steps (infini_attn_append of one token per (b, h)) with "
+                        "the open segment holding FILLED tokens when the timed steps start and the memory "
+                        "holding all but the last segment of the workload; prints its own JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 launches), to calibrate "
                         "the HBM byte counters of a profiler against a known size")
@@ -170,6 +174,120 @@ def cpu_baseline(w, rule: str, budget_s: float):
                       f"in stream order, float64 numpy, {spent:.1f}s"}
 
 
+def decode_bytes(w, filled: int, steps: int) -> int:
+    """Algorithmic HBM bytes of `steps` decode steps starting at an open segment of
+    `filled` tokens: per (b, h) and step, the open segment's keys and values up to
+    the new token, M and z, and the token's q, k, v in and A out."""
+    esz = 2 if w.dtype == "bf16" else 4
+    bh = w.batch * w.heads
+    kv = sum(filled + i + 1 for i in range(steps)) * (w.d_key + w.d_value) * esz
+    per_step = (w.d_key * w.d_value + w.d_key) * 4 + (2 * w.d_key + 2 * w.d_value) * esz
+    return bh * (kv + steps * per_step)
+
+
+def decode_cpu_baseline(w, rule: str, filled: int, budget_s: float):
+    """The float64 oracle's decode: tokens appended one at a time to an open
+    segment of `filled` tokens, all heads, until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from compressive_memory_transformer_amd import synthetic as syn
+    from oracle import infini_ref as ref
+
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    s = w.segments - 1
+    q, k, v = (np.stack([np.stack([syn.tile(w, i, b, h, s) for h in range(w.heads)]) for b in range(w.batch)])
+               .astype(np.float64) for i in (0, 1, 2))
+    rng = np.random.default_rng(0)
+    M = rng.standard_normal((w.batch, w.heads, w.d_key, w.d_value))
+    z = np.abs(rng.standard_normal((w.batch, w.heads, w.d_key))) + 1.0
+    ok, ov = k[:, :, :filled], v[:, :, :filled]
+    spent, n = 0.0, 0
+    while spent < budget_s and filled + n < w.segment_len - 1:
+        t = filled + n
+        t0 = time.perf_counter()
+        res = ref.forward_stream(q[:, :, t:t + 1], k[:, :, t:t + 1], v[:, :, t:t + 1], syn.betas(w), rule,
+                                 w.segment_len, M0=M, z0=z, segments_done=s, open_k=ok, open_v=ov)
+        spent += time.perf_counter() - t0
+        ok, ov = res["open_k"], res["open_v"]
+        n += 1
+    return {"value": n * w.batch / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode steps of {w.name}/{rule} from an open segment of {filled} tokens, all "
+                      f"{w.batch * w.heads} heads, float64 numpy, {spent:.1f}s"}
+
+
+def bench_decode(args):
+    import torch
+
+    from compressive_memory_transformer_amd import infini as ia
+    from compressive_memory_transformer_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    rule = args.rule or w.rules[0]
+    filled, N = args.decode, w.segment_len
+    if filled + args.warmup + args.steps > N - 1:
+        print(f"--decode {filled} plus {args.warmup + args.steps} steps does not fit one open segment of {N}",
+              file=sys.stderr)
+        sys.exit(2)
+    ia.load_library()
+
+    def upload(tid):
+        arr = syn.full_tensor(w, tid, as_bits=True)
+        if w.dtype == "bf16":
+            import numpy as np
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(arr).to("cuda")
+
+    q, k, v = (upload(i) for i in (0, 1, 2))
+    beta = torch.from_numpy(syn.betas(w)).to("cuda")
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, N, w.dtype, rule)
+    L0 = (w.segments - 1) * N
+    eng.forward_sequence(q[:, :, :L0].contiguous(), k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), beta)
+    eng.open_stream()
+    if filled:
+        sl = slice(L0, L0 + filled)
+        eng.append(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(), v[:, :, sl].contiguous(), beta)
+    toks = [tuple(x[:, :, L0 + filled + i:L0 + filled + i + 1].contiguous() for x in (q, k, v))
+            for i in range(args.warmup + args.steps)]
+    out = torch.empty((w.batch, w.heads, 1, w.d_value), dtype=q.dtype, device="cuda")
+    ws, nbytes = eng.append_workspace(1)
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(args.warmup):
+        ia.append(eng.state, eng.open, *toks[i], 1, beta, out, ws, nbytes, sh)
+    torch.cuda.synchronize()
+    start = filled + args.warmup
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        ia.append(eng.state, eng.open, *toks[i], 1, beta, out, ws, nbytes, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    byts = decode_bytes(w, start, args.steps)
+    gbs = byts / wall / 1e9
+    cpu = decode_cpu_baseline(w, rule, start, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    line = {
+        "metric": "Infini-attention decode tokens/sec on 1 MI355X (one new token per (b, h) per step)",
+        "value": w.batch * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode/{w.name}", "batch": w.batch, "heads": w.heads, "segment_len": N,
+                   "d_key": w.d_key, "d_value": w.d_value, "rule": rule, "open_segment_filled": start,
+                   "segments_in_memory": w.segments - 1, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "open_attn_partial + open_attn_combine",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_step": byts / args.steps},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -196,6 +314,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.decode:
+        bench_decode(args)
+        return
     w = syn.WORKLOADS[args.workload]
     rule = args.rule or w.rules[0]
     ia.load_library()

@@ -476,20 +476,15 @@ int infini_attn_append(infini_attn_state* st, infini_attn_open_segment* os, cons
   int64_t t = 0;
   while (t < n_tokens) {
     if (o.filled > 0 || n_tokens - t < N) {
-      // into the open segment: copy the keys and values, then answer the queries
+      // into the open segment: answer the queries (the kernels also copy the new
+      // keys and values into the open-segment buffers)
       const int m = (int)std::min<int64_t>(N - o.filled, n_tokens - t);
-      hipError_t e = hipMemcpy2DAsync(static_cast<char*>(o.k_open) + (size_t)o.filled * qrow, (size_t)N * qrow,
-                                      kb + (size_t)t * qrow, (size_t)n_tokens * qrow, (size_t)m * qrow,
-                                      (size_t)BH, hipMemcpyDeviceToDevice, strm);
-      if (e != hipSuccess) return hip_fail(e, "open-segment key copy");
-      e = hipMemcpy2DAsync(static_cast<char*>(o.v_open) + (size_t)o.filled * vrow, (size_t)N * vrow,
-                           vb + (size_t)t * vrow, (size_t)n_tokens * vrow, (size_t)m * vrow, (size_t)BH,
-                           hipMemcpyDeviceToDevice, strm);
-      if (e != hipSuccess) return hip_fail(e, "open-segment value copy");
-      infini::OpenAttnArgs a{qb + (size_t)t * qrow, o.k_open, o.v_open, beta, s.M, s.z, ob + (size_t)t * vrow,
+      infini::OpenAttnArgs a{qb + (size_t)t * qrow, kb + (size_t)t * qrow, vb + (size_t)t * vrow, o.k_open,
+                             o.v_open, o.k_open, o.v_open, beta, s.M, s.z, ob + (size_t)t * vrow,
                              reinterpret_cast<float*>(ws + part_off), (int)BH, s.heads, N, s.d_key, s.d_value, m,
                              o.filled, 0, n_tokens, s.segments_done > 0, s.dtype == INFINI_BF16, s.scale};
-      if ((e = infini::launch_open_attn(a, strm)) != hipSuccess) return hip_fail(e, "open-segment attention launch");
+      const hipError_t e = infini::launch_open_attn(a, strm);
+      if (e != hipSuccess) return hip_fail(e, "open-segment attention launch");
       o.filled += m;
       t += m;
       if (o.filled == N) {

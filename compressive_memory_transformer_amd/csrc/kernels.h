@@ -110,14 +110,20 @@ struct F32UpdateArgs {
 hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------ open segment
-// Queries j < m that arrive at positions pos0 + j of an open segment whose keys
-// and values (rows bh * N + t, t < pos0 + m) are already in kseg / vseg; the
-// memory (M, z) is read as it stands.  Query and output row j of head bh is
-// bh * q_stride + j.  part: workspace [BH][m][P][dv + 2] (P set by the launcher).
+// Queries j < m that arrive at positions pos0 + j of an open segment whose
+// earlier keys and values (rows bh * N + t, t < pos0) are in kseg / vseg; the new
+// ones are knew / vnew, row bh * q_stride + j like the queries and outputs, and
+// are copied into the open segment (kseg_out / vseg_out, the same buffers) by the
+// second kernel.  The memory (M, z) is read as it stands.  part: workspace
+// [BH][m][P][dv + 2] (P set by the launcher).
 struct OpenAttnArgs {
   const void* q;
+  const void* knew;
+  const void* vnew;
   const void* kseg;
   const void* vseg;
+  void* kseg_out;
+  void* vseg_out;
   const float* beta;
   const float* M;
   const float* z;

@@ -4,15 +4,17 @@
 // step 2 for A_dot, section 3.3 for A_mem, section 3.5 for the gate).
 //
 // A query at position p of the open segment attends to the segment's keys
-// 0..p (which the host has already copied into the open-segment buffers) and
-// reads the memory (M, z) as it stands, i.e. as of the segment's start.  Both
-// dtypes run in fp32 arithmetic.
+// 0..p (those before pos0 from the open-segment buffers, the new ones straight
+// from the input) and reads the memory (M, z) as it stands, i.e. as of the
+// segment's start.  Both dtypes run in fp32 arithmetic.
 //
 // Split over keys (the decode case has one query per head and up to N keys):
 //   open_attn_partial: one workgroup per (128-key partition, group of 8 queries,
 //     head); scores, the partition's maximum and sum, and its share of P V;
 //   open_attn_combine: one workgroup per (query, head); the partitions merged in
-//     a fixed order, the retrieval sigma(q) M / (sigma(q) z), the gate, the output.
+//     a fixed order, the retrieval sigma(q) M / (sigma(q) z), the gate, the output,
+//     and the query's key and value rows copied into the open-segment buffers
+//     (after the partial kernel has read them, in stream order).
 #include "common.h"
 #include "kernels.h"
 
@@ -74,6 +76,8 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
   const T* q = static_cast<const T*>(a.q);
   const T* kseg = static_cast<const T*>(a.kseg);
   const T* vseg = static_cast<const T*>(a.vseg);
+  const T* knew = static_cast<const T*>(a.knew);
+  const T* vnew = static_cast<const T*>(a.vnew);
   __shared__ float qs[kOpenQ][128];
   __shared__ float ps[kOpenQ][kOpenThreads];
   __shared__ float red[2];
@@ -90,7 +94,8 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
 #pragma unroll
   for (int jj = 0; jj < kOpenQ; ++jj) s[jj] = 0.f;
   if (kk < nkeys) {
-    const T* krow = kseg + ((int64_t)bh * a.N + kk) * a.dk;
+    const T* krow = kk < a.pos0 ? kseg + ((int64_t)bh * a.N + kk) * a.dk
+                                : knew + ((int64_t)bh * a.q_stride + kk - a.pos0) * a.dk;
     if (a.dk % 8 == 0) {
       for (int c = 0; c < a.dk; c += 8) {
         float x[8];
@@ -125,10 +130,12 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
     float o[kOpenQ];
 #pragma unroll
     for (int jj = 0; jj < kOpenQ; ++jj) o[jj] = 0.f;
-    const int kend = min(kOpenThreads, nkeys - part * kOpenThreads);
-    const T* vcol = vseg + ((int64_t)bh * a.N + part * kOpenThreads) * a.dv + t;
+    const int k0 = part * kOpenThreads;
+    const int kend = min(kOpenThreads, nkeys - k0);
     for (int i = 0; i < kend; ++i) {
-      const float x = load_elem(vcol, (int64_t)i * a.dv);
+      const int key = k0 + i;
+      const float x = key < a.pos0 ? load_elem(vseg, ((int64_t)bh * a.N + key) * a.dv + t)
+                                   : load_elem(vnew, ((int64_t)bh * a.q_stride + key - a.pos0) * a.dv + t);
 #pragma unroll
       for (int jj = 0; jj < kOpenQ; ++jj) o[jj] = __builtin_fmaf(ps[jj][i], x, o[jj]);
     }
@@ -189,6 +196,10 @@ void open_attn_combine_kernel(OpenAttnArgs a) {
     const float g = sigmoid_gate(a.beta[h]);
     store_elem(static_cast<T*>(a.out), qrow * a.dv + t, g * a_mem + (1.f - g) * a_dot);
   }
+  // the new token's key and value join the open segment
+  const int64_t orow = (int64_t)bh * a.N + a.pos0 + j;
+  if (t < a.dk) static_cast<T*>(a.kseg_out)[orow * a.dk + t] = static_cast<const T*>(a.knew)[qrow * a.dk + t];
+  if (t < a.dv) static_cast<T*>(a.vseg_out)[orow * a.dv + t] = static_cast<const T*>(a.vnew)[qrow * a.dv + t];
 }
 
 int open_attn_parts(int keys) { return (keys + kOpenThreads - 1) / kOpenThreads; }
