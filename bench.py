@@ -256,13 +256,17 @@ def bench_decode(args):
         ia.append(eng.state, eng.open, *toks[i], 1, beta, out, ws, nbytes, sh)
     torch.cuda.synchronize()
     start = filled + args.warmup
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()   # torch's current stream: the stream the steps are enqueued on
     for i in range(args.warmup, args.warmup + args.steps):
         ia.append(eng.state, eng.open, *toks[i], 1, beta, out, ws, nbytes, sh)
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3
     byts = decode_bytes(w, start, args.steps)
-    gbs = byts / wall / 1e9
+    gbs = byts / gpu_s / 1e9
     cpu = decode_cpu_baseline(w, rule, start, args.cpu_seconds) if args.cpu_seconds > 0 else None
     line = {
         "metric": "Infini-attention decode tokens/sec on 1 MI355X (one new token per (b, h) per step)",
@@ -282,7 +286,8 @@ def bench_decode(args):
                    "segments_in_memory": w.segments - 1, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "open_attn_partial + open_attn_combine",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_step": byts / args.steps},
+                     "traffic": None, "bytes_per_step": byts / args.steps,
+                     "avg_step_ms_on_stream": gpu_s / args.steps * 1e3},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -206,7 +206,7 @@ bool append_layout(const infini_attn_state* st, int64_t n, WsLayout* whole, WsLa
   if (!workspace_layout(st, 1, N, one)) return false;
   const int64_t mq = n < N - 1 ? n : N - 1;   // queries of one open-segment piece
   int64_t parts;
-  if (!mul_ok(BH * mq, (int64_t)infini::open_attn_parts((int)N) * (st->d_value + 2), &parts)) return false;
+  if (!mul_ok(BH * mq, (int64_t)infini::open_attn_slots((int)N, st->d_key) * (st->d_value + 2), &parts)) return false;
   *part_off = 0;
   size_t t = one->total;
   if (S > 0 && whole->total > t) t = whole->total;
@@ -482,7 +482,7 @@ int infini_attn_append(infini_attn_state* st, infini_attn_open_segment* os, cons
       infini::OpenAttnArgs a{qb + (size_t)t * qrow, kb + (size_t)t * qrow, vb + (size_t)t * vrow, o.k_open,
                              o.v_open, o.k_open, o.v_open, beta, s.M, s.z, ob + (size_t)t * vrow,
                              reinterpret_cast<float*>(ws + part_off), (int)BH, s.heads, N, s.d_key, s.d_value, m,
-                             o.filled, 0, n_tokens, s.segments_done > 0, s.dtype == INFINI_BF16, s.scale};
+                             o.filled, 0, 0, n_tokens, s.segments_done > 0, s.dtype == INFINI_BF16, s.scale};
       const hipError_t e = infini::launch_open_attn(a, strm);
       if (e != hipSuccess) return hip_fail(e, "open-segment attention launch");
       o.filled += m;

@@ -115,7 +115,8 @@ hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream);
 // ones are knew / vnew, row bh * q_stride + j like the queries and outputs, and
 // are copied into the open segment (kseg_out / vseg_out, the same buffers) by the
 // second kernel.  The memory (M, z) is read as it stands.  part: workspace
-// [BH][m][P][dv + 2] (P set by the launcher).
+// [BH][m][P + R][dv + 2] (P key partitions and R memory slots, set by the
+// launcher).
 struct OpenAttnArgs {
   const void* q;
   const void* knew;
@@ -129,14 +130,15 @@ struct OpenAttnArgs {
   const float* z;
   void* out;
   float* part;
-  int BH, H, N, dk, dv, m, pos0, P;
+  int BH, H, N, dk, dv, m, pos0, P, R;
   int64_t q_stride;
   int has_memory, bf16;
   float scale;
 };
 hipError_t launch_open_attn(const OpenAttnArgs& a, hipStream_t stream);
-// Key partitions of the open-segment attention for `keys` keys.
-int open_attn_parts(int keys);
+// Workspace slots (key partitions plus memory slots) per query of the
+// open-segment attention for `keys` keys and d_key = dk.
+int open_attn_slots(int keys, int dk);
 
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);

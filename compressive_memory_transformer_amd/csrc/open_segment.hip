@@ -8,13 +8,17 @@
 // from the input) and reads the memory (M, z) as it stands, i.e. as of the
 // segment's start.  Both dtypes run in fp32 arithmetic.
 //
-// Split over keys (the decode case has one query per head and up to N keys):
-//   open_attn_partial: one workgroup per (128-key partition, group of 8 queries,
-//     head); scores, the partition's maximum and sum, and its share of P V;
-//   open_attn_combine: one workgroup per (query, head); the partitions merged in
-//     a fixed order, the retrieval sigma(q) M / (sigma(q) z), the gate, the output,
-//     and the query's key and value rows copied into the open-segment buffers
-//     (after the partial kernel has read them, in stream order).
+// Split over keys and memory rows (the decode case has one query per head, up
+// to N keys and a 64 KiB memory per head at d = 128):
+//   open_attn_partial: one workgroup per (slot, group of 8 queries, head).  Slots
+//     below P are 128-key partitions: scores, the partition's maximum and sum,
+//     and its share of P V.  The R slots after them each take 16 rows of M and z:
+//     their share of sigma(q) M and of sigma(q) z;
+//   open_attn_combine: one workgroup per (query, head); the key partitions merged
+//     in a fixed order, the memory shares summed in a fixed order, the retrieval
+//     sigma(q) M / (sigma(q) z), the gate, the output, and the query's key and
+//     value rows copied into the open-segment buffers (after the partial kernel
+//     has read them, in stream order).
 #include "common.h"
 #include "kernels.h"
 
@@ -24,6 +28,7 @@ namespace {
 
 constexpr int kOpenThreads = 128;   // threads per workgroup = keys per partition
 constexpr int kOpenQ = 8;           // queries per partial workgroup
+constexpr int kMemRows = 16;        // rows of M per memory slot
 
 __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_elem(const bf16* p, int64_t i) { return bf2f(p[i]); }
@@ -66,13 +71,20 @@ __device__ __forceinline__ float wg_sum(float x, float* red) {
 
 }  // namespace
 
-template <typename T>
+// Q queries per workgroup: 1 for a decode step, kOpenQ otherwise.  With one
+// query, each thread issues all of its K row loads (and later its 16 V row
+// loads) at once: a decode step is a few dependent memory round trips.  With
+// eight, the accumulators take the registers and the loads go one at a time.
+template <typename T, int Q>
 __global__ __launch_bounds__(kOpenThreads)
 void open_attn_partial_kernel(OpenAttnArgs a) {
+  constexpr int kOpenQ = Q;
+  constexpr int LB = Q == 1 ? 16 : 1;
   const int part = blockIdx.x, j0 = blockIdx.y * kOpenQ, bh = blockIdx.z;
   const int t = threadIdx.x;
   const int nq = min(kOpenQ, a.m - j0);
   const int nkeys = a.pos0 + a.m;               // keys of the open segment after the append
+  const int slot_stride = a.P + a.R;
   const T* q = static_cast<const T*>(a.q);
   const T* kseg = static_cast<const T*>(a.kseg);
   const T* vseg = static_cast<const T*>(a.vseg);
@@ -80,6 +92,7 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
   const T* vnew = static_cast<const T*>(a.vnew);
   __shared__ float qs[kOpenQ][128];
   __shared__ float ps[kOpenQ][kOpenThreads];
+  __shared__ float pv[kOpenThreads / 16][kOpenQ][128];   // P V shares of the 8 key groups
   __shared__ float red[2];
   for (int i = t; i < kOpenQ * a.dk; i += kOpenThreads) {
     const int jj = i / a.dk, c = i % a.dk;
@@ -87,23 +100,72 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
   }
   __syncthreads();
 
+  if (part >= a.P) {
+    // memory slot: rows r0 .. r0 + 15 of M and z.  The loads are issued
+    // together (rows past d_key clamped to the last one and then ignored).
+    const int r0 = (part - a.P) * kMemRows;
+    if (t < a.dv) {
+      const float* Mh = a.M + (int64_t)bh * a.dk * a.dv + t;
+      float mv[kMemRows];
+#pragma unroll
+      for (int i = 0; i < kMemRows; ++i) mv[i] = Mh[(int64_t)min(r0 + i, a.dk - 1) * a.dv];
+      float num[kOpenQ];
+#pragma unroll
+      for (int jj = 0; jj < kOpenQ; ++jj) num[jj] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMemRows; ++i) {
+        if (r0 + i >= a.dk) break;
+#pragma unroll
+        for (int jj = 0; jj < kOpenQ; ++jj) {
+          const float x = qs[jj][r0 + i];
+          num[jj] = __builtin_fmaf(x > 0.f ? x + 1.f : exp_e(x), mv[i], num[jj]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kOpenQ; ++jj)
+        if (jj < nq) a.part[(((int64_t)bh * a.m + j0 + jj) * slot_stride + part) * (a.dv + 2) + t] = num[jj];
+    }
+    if (t < nq) {
+      float zv[kMemRows];
+#pragma unroll
+      for (int i = 0; i < kMemRows; ++i) zv[i] = a.z[(int64_t)bh * a.dk + min(r0 + i, a.dk - 1)];
+      float den = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMemRows; ++i) {
+        if (r0 + i >= a.dk) break;
+        const float x = qs[t][r0 + i];
+        den = __builtin_fmaf(x > 0.f ? x + 1.f : exp_e(x), zv[i], den);
+      }
+      a.part[(((int64_t)bh * a.m + j0 + t) * slot_stride + part) * (a.dv + 2) + a.dv] = den;
+    }
+    return;
+  }
+
   // score of this thread's key for every query of the group (-inf where the
   // query may not see the key)
   const int kk = part * kOpenThreads + t;
+  const int kr = min(kk, nkeys - 1);            // rows past the last key: clamped, masked below
   float s[kOpenQ];
 #pragma unroll
   for (int jj = 0; jj < kOpenQ; ++jj) s[jj] = 0.f;
-  if (kk < nkeys) {
-    const T* krow = kk < a.pos0 ? kseg + ((int64_t)bh * a.N + kk) * a.dk
-                                : knew + ((int64_t)bh * a.q_stride + kk - a.pos0) * a.dk;
+  {
+    const T* krow = kr < a.pos0 ? kseg + ((int64_t)bh * a.N + kr) * a.dk
+                                : knew + ((int64_t)bh * a.q_stride + kr - a.pos0) * a.dk;
     if (a.dk % 8 == 0) {
-      for (int c = 0; c < a.dk; c += 8) {
-        float x[8];
-        load8(krow + c, x);
+      // the row's loads LB at a time (columns past d_key clamped, then skipped)
+      for (int cb = 0; cb < 16; cb += LB) {
+        if (8 * cb >= a.dk) break;
+        float x[LB][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int i = 0; i < LB; ++i) load8(krow + min(8 * (cb + i), a.dk - 8), x[i]);
 #pragma unroll
-          for (int jj = 0; jj < kOpenQ; ++jj) s[jj] = __builtin_fmaf(qs[jj][c + e], x[e], s[jj]);
+        for (int i = 0; i < LB; ++i) {
+          if (8 * (cb + i) >= a.dk) break;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int jj = 0; jj < kOpenQ; ++jj) s[jj] = __builtin_fmaf(qs[jj][8 * (cb + i) + e], x[i][e], s[jj]);
+        }
       }
     } else {
       for (int c = 0; c < a.dk; ++c) {
@@ -116,7 +178,11 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
   float mx[kOpenQ], l[kOpenQ];
 #pragma unroll
   for (int jj = 0; jj < kOpenQ; ++jj) {
-    const bool vis = jj < nq && kk < nkeys && kk <= a.pos0 + j0 + jj;
+    ps[jj][t] = 0.f;
+    mx[jj] = -__builtin_inff();
+    l[jj] = 0.f;
+    if (jj >= nq) continue;   // uniform over the workgroup
+    const bool vis = kk < nkeys && kk <= a.pos0 + j0 + jj;
     const float sc = vis ? s[jj] * a.scale : -__builtin_inff();
     mx[jj] = wg_max(sc, red);
     const float p = (mx[jj] == -__builtin_inff() || !vis) ? 0.f : exp_e(sc - mx[jj]);
@@ -125,13 +191,69 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
   }
   __syncthreads();
 
-  // this partition's share of P V: thread t holds column t of d_value
-  if (t < a.dv) {
+  // this partition's share of P V
+  const int k0 = part * kOpenThreads;
+  const int kend = min(kOpenThreads, nkeys - k0);
+  if (Q == 1 && a.dv % 8 == 0) {
+    // thread = (key group kg of 16 keys, 8 columns cg); its row loads are
+    // issued LB at a time (keys past the last clamped, weighted 0), then the 8
+    // key groups are summed through LDS
+    const int cg = t & 15, kg = t >> 4;
+    if (8 * cg < a.dv) {
+      float o[kOpenQ][8];
+#pragma unroll
+      for (int jj = 0; jj < kOpenQ; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[jj][e] = 0.f;
+      for (int ib = 0; ib < 16; ib += LB) {
+        if (kg + 8 * ib >= kend) break;
+        float x[LB][8];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+          const int key = k0 + min(kg + 8 * (ib + i), kend - 1);
+          const T* vrow = key < a.pos0 ? vseg + ((int64_t)bh * a.N + key) * a.dv
+                                       : vnew + ((int64_t)bh * a.q_stride + key - a.pos0) * a.dv;
+          load8(vrow + 8 * cg, x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+          const int kl = kg + 8 * (ib + i);
+          const bool in = kl < kend;
+#pragma unroll
+          for (int jj = 0; jj < kOpenQ; ++jj) {
+            const float p = in ? ps[jj][kl] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[jj][e] = __builtin_fmaf(p, in ? x[i][e] : 0.f, o[jj][e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kOpenQ; ++jj)
+        if (jj < nq)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[kg][jj][8 * cg + e] = o[jj][e];
+    }
+    __syncthreads();
+    if (t < a.dv) {
+#pragma unroll
+      for (int jj = 0; jj < kOpenQ; ++jj) {
+        if (jj >= nq) break;
+        float o = 0.f;
+#pragma unroll
+        for (int g = 0; g < kOpenThreads / 16; ++g) o += pv[g][jj][t];
+        float* dst = a.part + (((int64_t)bh * a.m + j0 + jj) * slot_stride + part) * (a.dv + 2);
+        dst[t] = o;
+        if (t == 0) {
+          dst[a.dv] = mx[jj];
+          dst[a.dv + 1] = l[jj];
+        }
+      }
+    }
+  } else if (t < a.dv) {
+    // thread t holds column t of d_value
     float o[kOpenQ];
 #pragma unroll
     for (int jj = 0; jj < kOpenQ; ++jj) o[jj] = 0.f;
-    const int k0 = part * kOpenThreads;
-    const int kend = min(kOpenThreads, nkeys - k0);
     for (int i = 0; i < kend; ++i) {
       const int key = k0 + i;
       const float x = key < a.pos0 ? load_elem(vseg, ((int64_t)bh * a.N + key) * a.dv + t)
@@ -141,13 +263,12 @@ void open_attn_partial_kernel(OpenAttnArgs a) {
     }
 #pragma unroll
     for (int jj = 0; jj < kOpenQ; ++jj) {
-      if (jj < nq) {
-        float* dst = a.part + (((int64_t)bh * a.m + j0 + jj) * a.P + part) * (a.dv + 2);
-        dst[t] = o[jj];
-        if (t == 0) {
-          dst[a.dv] = mx[jj];
-          dst[a.dv + 1] = l[jj];
-        }
+      if (jj >= nq) break;
+      float* dst = a.part + (((int64_t)bh * a.m + j0 + jj) * slot_stride + part) * (a.dv + 2);
+      dst[t] = o[jj];
+      if (t == 0) {
+        dst[a.dv] = mx[jj];
+        dst[a.dv + 1] = l[jj];
       }
     }
   }
@@ -158,66 +279,78 @@ __global__ __launch_bounds__(kOpenThreads)
 void open_attn_combine_kernel(OpenAttnArgs a) {
   const int j = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
   const int t = threadIdx.x;
-  const T* q = static_cast<const T*>(a.q);
-  __shared__ float sq[128];
-  __shared__ float red[2];
-  const float* parts = a.part + ((int64_t)bh * a.m + j) * a.P * (a.dv + 2);
+  const int nslots = a.P + a.R;
+  const float g = sigmoid_gate(a.beta[h]);
+  const float* parts = a.part + ((int64_t)bh * a.m + j) * nslots * (a.dv + 2);
 
-  // A_dot: the partitions merged against the overall maximum, in partition order
-  float mx = -__builtin_inff();
-  for (int p = 0; p < a.P; ++p) mx = fmaxf(mx, parts[(int64_t)p * (a.dv + 2) + a.dv]);
-  float l = 0.f, o = 0.f;
-  for (int p = 0; p < a.P; ++p) {
-    const float* src = parts + (int64_t)p * (a.dv + 2);
-    const float mp = src[a.dv];
-    if (mp == -__builtin_inff()) continue;
-    const float w = exp_e(mp - mx);
-    l = __builtin_fmaf(w, src[a.dv + 1], l);
-    if (t < a.dv) o = __builtin_fmaf(w, src[t], o);
+  // One pass over the slots, 16 at a time with their loads issued together
+  // (slots past the last clamped, then skipped).  Key partitions are merged
+  // online against the running maximum, in partition order; the memory slots'
+  // shares of sigma(q) M and sigma(q) z are summed in slot order.
+  float mx = -__builtin_inff(), l = 0.f, o = 0.f, num = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < nslots; s0 += 16) {
+    float vo[16], vm[16], vl[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* src = parts + (int64_t)min(s0 + i, nslots - 1) * (a.dv + 2);
+      vo[i] = src[min(t, a.dv - 1)];
+      vm[i] = src[a.dv];
+      vl[i] = src[a.dv + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sl = s0 + i;
+      if (sl >= nslots) break;
+      if (sl < a.P) {
+        if (vm[i] == -__builtin_inff()) continue;   // no visible key in this partition
+        const float nm = fmaxf(mx, vm[i]);
+        const float ca = exp_e(mx - nm), cb = exp_e(vm[i] - nm);   // exp(-inf) = 0 on the first
+        l = l * ca + vl[i] * cb;
+        o = o * ca + vo[i] * cb;
+        mx = nm;
+      } else {
+        num += vo[i];
+        den += vm[i];
+      }
+    }
   }
   const float a_dot = o / l;   // l > 0: every query sees at least its own key
-
   // A_mem = sigma(q) M / (sigma(q) z), 0 for a stream's first segment
+  const float a_mem = a.has_memory && den > 0.f ? num / den : 0.f;
   const int64_t qrow = ((int64_t)bh * a.q_stride + j);
-  if (t < a.dk) {
-    const float x = load_elem(q, qrow * a.dk + t);
-    sq[t] = x > 0.f ? x + 1.f : exp_e(x);
-  }
-  __syncthreads();
-  const float den = wg_sum(t < a.dk ? sq[t] * a.z[(int64_t)bh * a.dk + t] : 0.f, red);
-  float a_mem = 0.f;
-  if (a.has_memory && den > 0.f && t < a.dv) {
-    const float* Mh = a.M + (int64_t)bh * a.dk * a.dv + t;
-    float num = 0.f;
-    for (int c = 0; c < a.dk; ++c) num = __builtin_fmaf(sq[c], Mh[(int64_t)c * a.dv], num);
-    a_mem = num / den;
-  }
-  if (t < a.dv) {
-    const float g = sigmoid_gate(a.beta[h]);
-    store_elem(static_cast<T*>(a.out), qrow * a.dv + t, g * a_mem + (1.f - g) * a_dot);
-  }
+  if (t < a.dv) store_elem(static_cast<T*>(a.out), qrow * a.dv + t, g * a_mem + (1.f - g) * a_dot);
   // the new token's key and value join the open segment
   const int64_t orow = (int64_t)bh * a.N + a.pos0 + j;
   if (t < a.dk) static_cast<T*>(a.kseg_out)[orow * a.dk + t] = static_cast<const T*>(a.knew)[qrow * a.dk + t];
   if (t < a.dv) static_cast<T*>(a.vseg_out)[orow * a.dv + t] = static_cast<const T*>(a.vnew)[qrow * a.dv + t];
 }
 
-int open_attn_parts(int keys) { return (keys + kOpenThreads - 1) / kOpenThreads; }
+int open_attn_slots(int keys, int dk) {
+  return (keys + kOpenThreads - 1) / kOpenThreads + (dk + kMemRows - 1) / kMemRows;
+}
 
 hipError_t launch_open_attn(const OpenAttnArgs& args, hipStream_t stream) {
   OpenAttnArgs a = args;
   if (a.m <= 0) return hipSuccess;
   if (a.dk > 128 || a.dv > 128 || a.pos0 + a.m > a.N) return hipErrorInvalidValue;
-  a.P = open_attn_parts(a.pos0 + a.m);
-  const dim3 gp((unsigned)a.P, (unsigned)((a.m + kOpenQ - 1) / kOpenQ), (unsigned)a.BH);
+  a.P = (a.pos0 + a.m + kOpenThreads - 1) / kOpenThreads;
+  a.R = a.has_memory ? (a.dk + kMemRows - 1) / kMemRows : 0;
+  const bool one = a.m == 1;
+  const dim3 gp((unsigned)(a.P + a.R), (unsigned)(one ? 1 : (a.m + kOpenQ - 1) / kOpenQ), (unsigned)a.BH);
   const dim3 gc((unsigned)a.m, (unsigned)a.BH);
   if (a.bf16) {
-    hipLaunchKernelGGL(open_attn_partial_kernel<bf16>, gp, dim3(kOpenThreads), 0, stream, a);
+    if (one)
+      hipLaunchKernelGGL((open_attn_partial_kernel<bf16, 1>), gp, dim3(kOpenThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((open_attn_partial_kernel<bf16, kOpenQ>), gp, dim3(kOpenThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(open_attn_combine_kernel<bf16>, gc, dim3(kOpenThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(open_attn_partial_kernel<float>, gp, dim3(kOpenThreads), 0, stream, a);
+    if (one)
+      hipLaunchKernelGGL((open_attn_partial_kernel<float, 1>), gp, dim3(kOpenThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((open_attn_partial_kernel<float, kOpenQ>), gp, dim3(kOpenThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(open_attn_combine_kernel<float>, gc, dim3(kOpenThreads), 0, stream, a);
