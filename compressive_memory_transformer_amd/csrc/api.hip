@@ -259,6 +259,39 @@ int zero_state(infini_attn_state* st, float* M, float* z, hipStream_t stream) {
   return INFINI_OK;
 }
 
+struct BwdLayout {
+  size_t snapM, snapz, dMr, dzr, ez, gzs, lse, drow, rs, dden, de, dq, dk, dv, dfk, dbp, total;
+};
+
+bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w) {
+  const int64_t BH = (int64_t)st->batch * st->heads, S = seq_len / st->segment_len;
+  const int64_t dk = st->d_key, dv = st->d_value;
+  int64_t segs, rows, mm, rk, rv, nb;
+  if (!mul_ok(BH, S, &segs) || !mul_ok(BH, seq_len, &rows) || !mul_ok(segs, dk * dv, &mm) ||
+      !mul_ok(rows, dk, &rk) || !mul_ok(rows, dv, &rv) || !mul_ok(segs, infini::bwd_query_blocks(st->segment_len), &nb))
+    return false;
+  size_t off = 0;
+  auto take = [&](size_t* field, int64_t floats) { *field = off; off = align_up(off + (size_t)floats * 4); };
+  take(&w->snapM, mm);
+  take(&w->snapz, segs * dk);
+  take(&w->dMr, mm);
+  take(&w->dzr, segs * dk);
+  take(&w->ez, segs * dk);
+  take(&w->gzs, segs * dk);
+  take(&w->lse, rows);
+  take(&w->drow, rows);
+  take(&w->rs, rows);
+  take(&w->dden, rows);
+  take(&w->de, rows);
+  take(&w->dq, rk);
+  take(&w->dk, rk);
+  take(&w->dv, rv);
+  take(&w->dfk, rk);
+  take(&w->dbp, nb);
+  w->total = off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +407,82 @@ int infini_attn_forward_sequence_profiled(infini_attn_state* st, const void* q, 
   if (!events || n_events != 3 || !events[0] || !events[1] || !events[2])
     return fail(INFINI_EINVAL, "profiled forward needs exactly 3 non-NULL events");
   return forward_impl(st, q, k, v, seq_len, beta, out, workspace, workspace_bytes, stream, events);
+}
+
+size_t infini_attn_backward_workspace_bytes(const infini_attn_state* st, int64_t seq_len) {
+  if (check_state(st) != INFINI_OK) return 0;
+  if (seq_len <= 0 || seq_len % st->segment_len != 0) return 0;
+  BwdLayout w;
+  if (!backward_layout(st, seq_len, &w)) return 0;
+  return w.total;
+}
+
+int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, const void* k, const void* v,
+                                  int64_t seq_len, const float* beta, const void* dout, const float* dM,
+                                  const float* dz, void* dq, void* dk, void* dv, float* dbeta, float* dM0,
+                                  float* dz0, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_state(st);
+  if (rc != INFINI_OK) return rc;
+  if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta)
+    return fail(INFINI_EINVAL, "q, k, v, beta, dout, dq, dk, dv and dbeta must be non-NULL");
+  if (seq_len <= 0 || seq_len % st->segment_len != 0)
+    return fail(INFINI_EINVAL, "seq_len (%lld) must be a positive multiple of segment_len (%d)",
+                (long long)seq_len, st->segment_len);
+  const int64_t S64 = seq_len / st->segment_len;
+  if (S64 > 65535) return fail(INFINI_EUNSUPPORTED, "more than 65535 segments in one backward call");
+  const int64_t BH = (int64_t)st->batch * st->heads;
+  if (BH > 65535) return fail(INFINI_EUNSUPPORTED, "batch * heads above 65535 for the backward kernels");
+  int64_t rows, nqk, nvo;
+  if (!mul_ok(BH, seq_len, &rows) || !mul_ok(rows, st->d_key, &nqk) || !mul_ok(rows, st->d_value, &nvo))
+    return fail(INFINI_EINVAL, "tensor sizes overflow");
+  if ((rows + 1) / 2 > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
+  const size_t esz = st->dtype == INFINI_BF16 ? 2 : 4;
+  const uintptr_t align = st->dtype == INFINI_BF16 ? 2 : 4;
+  for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (reinterpret_cast<uintptr_t>(p) % align != 0)
+      return fail(INFINI_EINVAL, "q, k, v, dout, dq, dk and dv must be %d-byte aligned", (int)align);
+  for (const void* p : {static_cast<const void*>(beta), static_cast<const void*>(dM), static_cast<const void*>(dz),
+                        static_cast<const void*>(dbeta), static_cast<const void*>(dM0), static_cast<const void*>(dz0)})
+    if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return fail(INFINI_EINVAL, "fp32 arguments must be 4-byte aligned");
+  const size_t qkb = (size_t)nqk * esz, vb = (size_t)nvo * esz;
+  const size_t mb = (size_t)BH * st->d_key * st->d_value * 4, zb = (size_t)BH * st->d_key * 4;
+  BwdLayout w;
+  if (!backward_layout(st, seq_len, &w)) return fail(INFINI_EINVAL, "workspace size overflows");
+  if (!workspace || workspace_bytes < w.total)
+    return fail(INFINI_EWORKSPACE, "workspace of %zu bytes required, %zu given%s", w.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(INFINI_EWORKSPACE, "workspace must be 256-byte aligned");
+  struct Buf { const void* p; size_t n; };
+  const Buf outs[] = {{dq, qkb}, {dk, qkb}, {dv, vb}, {dbeta, (size_t)st->heads * 4}, {dM0, dM0 ? mb : 0},
+                      {dz0, dz0 ? zb : 0}, {workspace, w.total}};
+  const Buf ins[] = {{q, qkb}, {k, qkb}, {v, vb}, {dout, vb}, {beta, (size_t)st->heads * 4}, {dM, dM ? mb : 0},
+                     {dz, dz ? zb : 0}, {st->M, mb}, {st->z, zb}};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    if (!outs[i].n) continue;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (outs[j].n && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(INFINI_EINVAL, "the outputs and the workspace must not overlap each other");
+    for (const Buf& b : ins)
+      if (b.n && overlaps(outs[i].p, outs[i].n, b.p, b.n))
+        return fail(INFINI_EINVAL, "the outputs and the workspace must not alias the inputs or the state");
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  infini::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.beta = beta; a.M0 = st->M; a.z0 = st->z; a.dM = dM; a.dz = dz;
+  a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dbeta = dbeta; a.dM0 = dM0; a.dz0 = dz0;
+  a.snapM = f(w.snapM); a.snapz = f(w.snapz); a.dMr = f(w.dMr); a.dzr = f(w.dzr); a.ez = f(w.ez); a.gzs = f(w.gzs);
+  a.lse = f(w.lse); a.drow = f(w.drow); a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
+  a.dq_acc = f(w.dq); a.dk_acc = f(w.dk); a.dv_acc = f(w.dv); a.dfk_acc = f(w.dfk); a.dbeta_part = f(w.dbp);
+  a.B = st->batch; a.H = st->heads; a.BH = (int)BH; a.N = st->segment_len; a.S = (int)S64;
+  a.dk = st->d_key; a.dv = st->d_value; a.nqb = infini::bwd_query_blocks(st->segment_len);
+  a.L = seq_len; a.seg_base = st->segments_done; a.delta = st->rule == INFINI_RULE_DELTA; a.scale = st->scale;
+  const hipError_t e = infini::launch_backward(a, st->dtype == INFINI_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
 }
 
 int infini_attn_forward_segment(infini_attn_state* st, const void* q, const void* k, const void* v,

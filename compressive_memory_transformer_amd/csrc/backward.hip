@@ -1,0 +1,699 @@
+// Gradients of the segment stream (training through the layer: close-reading
+// page "精读笔记：Infini-attention", section 4).  The pages print no backward
+// formulas; every kernel below applies the chain rule to the forward equations
+// (section 3.1 with the causal mask of section 3.8 step 2 for A_dot, 3.3 for
+// A_mem, 3.5 for the gate, 3.4 and the CSDN page's section 2.1 for the linear and
+// delta updates).  For the loss <dA, A> + <dM, M_S> + <dz, z_S>:
+//
+//   snap        replays the memory updates and keeps every M_{s-1}, z_{s-1} (fp32);
+//   query       per 32 query rows of a segment: the row's softmax statistics and
+//               A_dot (first sweep over the keys), A_mem, the gate's share of
+//               dbeta, D = <(1 - g) dA, A_dot>, the retrieval's share of dq, then
+//               the local attention's share of dq (second sweep);
+//   key         per 32 keys of a segment: the local attention's dk and dv;
+//   memgrad     per segment: the retrieval's gradient of M_{s-1} and z_{s-1};
+//   chain       per 16 columns of M, segments in reverse: dL/dM_s carried back,
+//               the update's dv, its d sigma(K) (atomically summed over the column
+//               blocks) and, for the delta rule, the gradient of each token's
+//               denominator;
+//   ez, zchain  dL/dz_s carried back;  finish  the outputs in the input dtype;
+//   dbeta       the per-block shares of dbeta summed in a fixed order.
+//
+// All arithmetic is fp32 on the VALU, tiles staged in LDS.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace infini {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTok = 64;      // token chunk of the state kernels
+constexpr int kColB = 16;     // columns of M per chain / snapshot workgroup
+constexpr int kQB = 32;       // query rows per query-block workgroup
+constexpr int kKC = 64;       // key chunk
+constexpr int kKB = 32;       // keys per key-block workgroup
+constexpr int kQC = 64;       // query chunk of the key-block kernel
+constexpr int kP = 129;       // LDS pitch of 128-wide fp32 rows
+
+__device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const bf16* p, int64_t i) { return bf2f(p[i]); }
+__device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void st(bf16* p, int64_t i, float x) { p[i] = f2bf(x); }
+
+__device__ __forceinline__ float sig(float x) { return x > 0.f ? x + 1.f : exp_e(x); }
+__device__ __forceinline__ float sig_prime(float x) { return x > 0.f ? 1.f : exp_e(x); }
+
+// Sum over the 8 consecutive lanes that share a row.
+__device__ __forceinline__ float row8_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x;
+}
+__device__ __forceinline__ float row8_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, __shfl_xor(x, 4));
+  return x;
+}
+
+__device__ __forceinline__ bool is_first(const BwdArgs& a, int s) { return a.seg_base + s == 0; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ snap
+// grid (column blocks, BH).  Replays the updates of the stream for 16 columns
+// of M and writes M_{s-1}[:, cols] (and, from column block 0, z_{s-1}) for
+// every segment s.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_snap_kernel(BwdArgs a) {
+  const int cb = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  __shared__ float Ms[128][kColB + 1];
+  __shared__ float zs[128];
+  __shared__ float fk[kTok][kP];
+  __shared__ float uu[kTok][kColB + 1];
+  __shared__ float ee[kTok];
+  for (int i = t; i < 128 * kColB; i += kThreads) {
+    const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+    Ms[r][c] = (r < a.dk && col < a.dv) ? a.M0[((int64_t)bh * a.dk + r) * a.dv + col] : 0.f;
+  }
+  if (t < 128) zs[t] = t < a.dk ? a.z0[(int64_t)bh * a.dk + t] : 0.f;
+  __syncthreads();
+  for (int s = 0; s < a.S; ++s) {
+    const bool hasd = a.delta && !is_first(a, s);
+    float* snap = a.snapM + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+    for (int i = t; i < a.dk * kColB; i += kThreads) {
+      const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+      if (col < a.dv) snap[(int64_t)r * a.dv + col] = Ms[r][c];
+    }
+    if (cb == 0 && t < a.dk) a.snapz[((int64_t)bh * a.S + s) * a.dk + t] = zs[t];
+    float dM[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float zacc = 0.f;
+    for (int t0 = 0; t0 < a.N; t0 += kTok) {
+      const int64_t row0 = (int64_t)bh * a.L + (int64_t)s * a.N + t0;
+      for (int i = t; i < kTok * 128; i += kThreads) {
+        const int r = i >> 7, c = i & 127;
+        fk[r][c] = (t0 + r < a.N && c < a.dk) ? sig(ld(K, (row0 + r) * a.dk + c)) : 0.f;
+      }
+      for (int i = t; i < kTok * kColB; i += kThreads) {
+        const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+        uu[r][c] = (t0 + r < a.N && col < a.dv) ? ld(V, (row0 + r) * a.dv + col) : 0.f;
+      }
+      __syncthreads();
+      if (hasd) {
+        if (t < kTok) {
+          float e = 0.f;
+          for (int c = 0; c < a.dk; ++c) e = __builtin_fmaf(fk[t][c], zs[c], e);
+          ee[t] = e;
+        }
+        __syncthreads();
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = t + kThreads * r, tt = i / kColB, c = i % kColB;
+          float num = 0.f;
+          for (int x = 0; x < a.dk; ++x) num = __builtin_fmaf(fk[tt][x], Ms[x][c], num);
+          u[r] = uu[tt][c] - (ee[tt] > 0.f ? num / ee[tt] : 0.f);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = t + kThreads * r;
+          uu[i / kColB][i % kColB] = u[r];
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = t + kThreads * r, x = i / kColB, c = i % kColB;
+        float acc = dM[r];
+        for (int tt = 0; tt < kTok; ++tt) acc = __builtin_fmaf(fk[tt][x], uu[tt][c], acc);
+        dM[r] = acc;
+      }
+      if (t < 128)
+        for (int tt = 0; tt < kTok; ++tt) zacc += fk[tt][t];
+      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = t + kThreads * r;
+      Ms[i / kColB][i % kColB] += dM[r];
+    }
+    if (t < 128) zs[t] += zacc;
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------- query
+// grid (query blocks of 32, S, BH).  Thread = (row i = t / 8, part p = t % 8).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
+  const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H, t = threadIdx.x;
+  const int i = t >> 3, p = t & 7;
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  const T* DO = static_cast<const T*>(a.dout);
+  __shared__ float qs[kQB][kP];
+  __shared__ float das[kQB][kP];
+  __shared__ float kv[2 * kKC * kP];   // key / value chunk; later M_{s-1}
+  __shared__ float ps[kQB][kKC + 1];
+  __shared__ float dn[kQB][kP];
+  __shared__ float zsh[128];
+  __shared__ float red[kThreads / 64];
+  float (*ks)[kP] = reinterpret_cast<float (*)[kP]>(kv);
+  float (*vs)[kP] = reinterpret_cast<float (*)[kP]>(kv + kKC * kP);
+
+  const int i0 = qb * kQB;
+  const int qi = i0 + i;                          // row in the segment
+  const bool valid = qi < a.N;
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  const float g = sigmoid_gate(a.beta[h]);
+  const bool first = is_first(a, s);
+  for (int x = t; x < kQB * 128; x += kThreads) {
+    const int r = x >> 7, c = x & 127;
+    const bool ok = i0 + r < a.N;
+    qs[r][c] = (ok && c < a.dk) ? ld(Q, (seg0 + i0 + r) * a.dk + c) : 0.f;
+    das[r][c] = (ok && c < a.dv) ? ld(DO, (seg0 + i0 + r) * a.dv + c) : 0.f;
+  }
+  const int kend = min(a.N, i0 + kQB);            // keys any row of the block sees
+
+  // first sweep: softmax statistics and A_dot (columns c = 16 p + e)
+  float m = -__builtin_inff(), l = 0.f, o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  for (int kc = 0; kc < kend; kc += kKC) {
+    __syncthreads();
+    for (int x = t; x < kKC * 128; x += kThreads) {
+      const int r = x >> 7, c = x & 127;
+      const bool ok = kc + r < kend;
+      ks[r][c] = (ok && c < a.dk) ? ld(K, (seg0 + kc + r) * a.dk + c) : 0.f;
+      vs[r][c] = (ok && c < a.dv) ? ld(V, (seg0 + kc + r) * a.dv + c) : 0.f;
+    }
+    __syncthreads();
+    float sc[8], cmax = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = p + 8 * u;
+      float d = 0.f;
+      for (int c = 0; c < a.dk; ++c) d = __builtin_fmaf(qs[i][c], ks[j][c], d);
+      sc[u] = (valid && kc + j <= qi) ? d * a.scale : -__builtin_inff();
+      cmax = fmaxf(cmax, sc[u]);
+    }
+    cmax = row8_max(cmax);
+    const float mn = fmaxf(m, cmax);
+    const float alpha = mn == -__builtin_inff() ? 1.f : exp_e(m - mn);
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float pe = sc[u] == -__builtin_inff() ? 0.f : exp_e(sc[u] - mn);
+      ps[i][p + 8 * u] = pe;
+      lsum += pe;
+    }
+    l = l * alpha + row8_sum(lsum);
+    m = mn;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 16 * p + e;
+      float acc = o[e] * alpha;
+      if (c < a.dv)
+        for (int j = 0; j < kKC; ++j) acc = __builtin_fmaf(ps[i][j], vs[j][c], acc);
+      o[e] = acc;
+    }
+  }
+  const float lse = valid ? m + __logf(l) : 0.f;
+  const float inv_l = valid ? 1.f / l : 0.f;
+
+  // retrieval from M_{s-1}, z_{s-1}; the gate; D; the retrieval's dq
+  __syncthreads();
+  const float* Mg = a.snapM + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+  for (int x = t; x < a.dk * a.dv; x += kThreads) kv[x] = Mg[x];
+  if (t < 128) zsh[t] = t < a.dk ? a.snapz[((int64_t)bh * a.S + s) * a.dk + t] : 0.f;
+  __syncthreads();
+  float num[16], dpart = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) num[e] = 0.f;
+  for (int x = 0; x < a.dk; ++x) {
+    const float f = sig(qs[i][x]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 16 * p + e;
+      if (c < a.dv) num[e] = __builtin_fmaf(f, kv[x * a.dv + c], num[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int x = 16 * p + e;
+    if (x < a.dk) dpart = __builtin_fmaf(sig(qs[i][x]), zsh[x], dpart);
+  }
+  const float den = row8_sum(dpart);
+  const bool has = valid && !first && den > 0.f;
+  float dsum = 0.f, bsum = 0.f, msum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int c = 16 * p + e;
+    if (c < a.dv) {
+      const float adot = o[e] * inv_l;
+      const float amem = has ? num[e] / den : 0.f;
+      const float d = das[i][c];
+      dsum = __builtin_fmaf(d, adot, dsum);
+      bsum = __builtin_fmaf(d, amem - adot, bsum);
+      msum = __builtin_fmaf(d, amem, msum);
+    }
+  }
+  const float D = (1.f - g) * row8_sum(dsum);
+  const float rs = has ? g / den : 0.f;
+  const float msum_row = row8_sum(msum);
+  const float dden = has ? -g * msum_row / den : 0.f;
+  bsum = valid ? bsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int c = 16 * p + e;
+    if (c < 128) dn[i][c] = rs * das[i][c];
+  }
+  if (valid && p == 0) {
+    const int64_t row = seg0 + qi;
+    a.lse[row] = lse;
+    a.drow[row] = D;
+    a.rs[row] = rs;
+    a.dden[row] = dden;
+  }
+  // dbeta share of the block: g (1 - g) sum dA (A_mem - A_dot)
+  float bt = wave_sum(bsum);
+  if ((t & 63) == 0) red[t >> 6] = bt;
+  __syncthreads();
+  if (t == 0) {
+    float b = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) b += red[w];
+    a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qb] = b * g * (1.f - g);
+  }
+  float dq[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int x = 16 * p + e;
+    float acc = 0.f;
+    if (x < a.dk) {
+      for (int c = 0; c < a.dv; ++c) acc = __builtin_fmaf(kv[x * a.dv + c], dn[i][c], acc);
+      acc = (acc + dden * zsh[x]) * sig_prime(qs[i][x]);
+    }
+    dq[e] = acc;
+  }
+
+  // second sweep: the local attention's dq = scale sum_j dS_ij k_j
+  for (int kc = 0; kc < kend; kc += kKC) {
+    __syncthreads();
+    for (int x = t; x < kKC * 128; x += kThreads) {
+      const int r = x >> 7, c = x & 127;
+      const bool ok = kc + r < kend;
+      ks[r][c] = (ok && c < a.dk) ? ld(K, (seg0 + kc + r) * a.dk + c) : 0.f;
+      vs[r][c] = (ok && c < a.dv) ? ld(V, (seg0 + kc + r) * a.dv + c) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = p + 8 * u;
+      float ds = 0.f;
+      if (valid && kc + j <= qi) {
+        float d = 0.f, dp = 0.f;
+        for (int c = 0; c < a.dk; ++c) d = __builtin_fmaf(qs[i][c], ks[j][c], d);
+        for (int c = 0; c < a.dv; ++c) dp = __builtin_fmaf(das[i][c], vs[j][c], dp);
+        const float pe = exp_e(d * a.scale - lse);
+        ds = pe * ((1.f - g) * dp - D);
+      }
+      ps[i][j] = ds;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = 16 * p + e;
+      if (x < a.dk) {
+        float acc = 0.f;
+        for (int j = 0; j < kKC; ++j) acc = __builtin_fmaf(ps[i][j], ks[j][x], acc);
+        dq[e] = __builtin_fmaf(a.scale, acc, dq[e]);
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int x = 16 * p + e;
+      if (x < a.dk) a.dq_acc[(seg0 + qi) * a.dk + x] = dq[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------- key
+// grid (key blocks of 32, S, BH).  Thread = (key j = t / 8, part p = t % 8).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_key_kernel(BwdArgs a) {
+  const int kb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H, t = threadIdx.x;
+  const int j = t >> 3, p = t & 7;
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  const T* DO = static_cast<const T*>(a.dout);
+  __shared__ float kbs[kKB][kP];
+  __shared__ float vbs[kKB][kP];
+  __shared__ float qc[kQC][kP];
+  __shared__ float dac[kQC][kP];
+  __shared__ float lc[kQC], dc[kQC];
+  __shared__ float pss[kKB][kQC + 1];
+  __shared__ float dss[kKB][kQC + 1];
+  const int j0 = kb * kKB, kj = j0 + j;
+  const bool valid = kj < a.N;
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  const float g = sigmoid_gate(a.beta[h]);
+  for (int x = t; x < kKB * 128; x += kThreads) {
+    const int r = x >> 7, c = x & 127;
+    const bool ok = j0 + r < a.N;
+    kbs[r][c] = (ok && c < a.dk) ? ld(K, (seg0 + j0 + r) * a.dk + c) : 0.f;
+    vbs[r][c] = (ok && c < a.dv) ? ld(V, (seg0 + j0 + r) * a.dv + c) : 0.f;
+  }
+  float dkv[16], dvv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dkv[e] = dvv[e] = 0.f;
+  for (int qc0 = j0; qc0 < a.N; qc0 += kQC) {
+    __syncthreads();
+    for (int x = t; x < kQC * 128; x += kThreads) {
+      const int r = x >> 7, c = x & 127;
+      const bool ok = qc0 + r < a.N;
+      qc[r][c] = (ok && c < a.dk) ? ld(Q, (seg0 + qc0 + r) * a.dk + c) : 0.f;
+      dac[r][c] = (ok && c < a.dv) ? ld(DO, (seg0 + qc0 + r) * a.dv + c) : 0.f;
+    }
+    if (t < kQC) {
+      const bool ok = qc0 + t < a.N;
+      lc[t] = ok ? a.lse[seg0 + qc0 + t] : 0.f;
+      dc[t] = ok ? a.drow[seg0 + qc0 + t] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ii = p + 8 * u, qi = qc0 + ii;
+      float pe = 0.f, ds = 0.f;
+      if (valid && qi < a.N && kj <= qi) {
+        float d = 0.f, dp = 0.f;
+        for (int c = 0; c < a.dk; ++c) d = __builtin_fmaf(qc[ii][c], kbs[j][c], d);
+        for (int c = 0; c < a.dv; ++c) dp = __builtin_fmaf(dac[ii][c], vbs[j][c], dp);
+        pe = exp_e(d * a.scale - lc[ii]);
+        ds = pe * ((1.f - g) * dp - dc[ii]);
+      }
+      pss[j][ii] = pe;
+      dss[j][ii] = ds;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 16 * p + e;
+      float av = dvv[e], ak = dkv[e];
+      for (int ii = 0; ii < kQC; ++ii) {
+        av = __builtin_fmaf(pss[j][ii], dac[ii][c], av);
+        ak = __builtin_fmaf(dss[j][ii], qc[ii][c], ak);
+      }
+      dvv[e] = av;
+      dkv[e] = ak;
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 16 * p + e;
+      if (c < a.dv) a.dv_acc[(seg0 + kj) * a.dv + c] = (1.f - g) * dvv[e];
+      if (c < a.dk) a.dk_acc[(seg0 + kj) * a.dk + c] = a.scale * dkv[e];
+    }
+  }
+}
+
+// --------------------------------------------------------------- memgrad
+// grid (S, BH): dMr_s = sigma(Q)^T (rs * dA), dzr_s = sigma(Q)^T dden.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_memgrad_kernel(BwdArgs a) {
+  const int s = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const T* Q = static_cast<const T*>(a.q);
+  const T* DO = static_cast<const T*>(a.dout);
+  __shared__ float fq[32][kP];
+  __shared__ float w[32][kP];
+  __shared__ float dd[32];
+  const int c = t & 127, ah = t >> 7;
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  float acc[64];
+#pragma unroll
+  for (int m = 0; m < 64; ++m) acc[m] = 0.f;
+  float zacc = 0.f;
+  for (int r0 = 0; r0 < a.N; r0 += 32) {
+    __syncthreads();
+    for (int x = t; x < 32 * 128; x += kThreads) {
+      const int r = x >> 7, cc = x & 127;
+      const bool ok = r0 + r < a.N;
+      const int64_t row = seg0 + r0 + r;
+      fq[r][cc] = (ok && cc < a.dk) ? sig(ld(Q, row * a.dk + cc)) : 0.f;
+      w[r][cc] = (ok && cc < a.dv) ? a.rs[row] * ld(DO, row * a.dv + cc) : 0.f;
+    }
+    if (t < 32) dd[t] = r0 + t < a.N ? a.dden[seg0 + r0 + t] : 0.f;
+    __syncthreads();
+    for (int r = 0; r < 32; ++r) {
+      const float wv = w[r][c];
+#pragma unroll
+      for (int m = 0; m < 64; ++m) acc[m] = __builtin_fmaf(fq[r][ah + 2 * m], wv, acc[m]);
+    }
+    if (t < 128)
+      for (int r = 0; r < 32; ++r) zacc = __builtin_fmaf(dd[r], fq[r][t], zacc);
+  }
+  float* out = a.dMr + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    const int x = ah + 2 * m;
+    if (x < a.dk && c < a.dv) out[(int64_t)x * a.dv + c] = acc[m];
+  }
+  if (t < a.dk) a.dzr[((int64_t)bh * a.S + s) * a.dk + t] = zacc;
+}
+
+// ----------------------------------------------------------------- chain
+// grid (column blocks, BH).  dL/dM_s for 16 columns carried from the last
+// segment to the first.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs a) {
+  const int cb = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  __shared__ float GMs[128][kColB + 1];
+  __shared__ float Ms[128][kColB + 1];
+  __shared__ float zs[128];
+  __shared__ float fk[kTok][kP];
+  __shared__ float du[kTok][kColB + 1];
+  __shared__ float rr[kTok][kColB + 1];
+  __shared__ float uu[kTok][kColB + 1];
+  __shared__ float ee[kTok];
+  for (int i = t; i < 128 * kColB; i += kThreads) {
+    const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+    GMs[r][c] = (a.dM && r < a.dk && col < a.dv) ? a.dM[((int64_t)bh * a.dk + r) * a.dv + col] : 0.f;
+  }
+  for (int s = a.S - 1; s >= 0; --s) {
+    const bool hasd = a.delta && !is_first(a, s);
+    const float* snap = a.snapM + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+    __syncthreads();
+    for (int i = t; i < 128 * kColB; i += kThreads) {
+      const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+      Ms[r][c] = (r < a.dk && col < a.dv) ? snap[(int64_t)r * a.dv + col] : 0.f;
+    }
+    if (t < 128) zs[t] = t < a.dk ? a.snapz[((int64_t)bh * a.S + s) * a.dk + t] : 0.f;
+    float gacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < a.N; t0 += kTok) {
+      const int64_t row0 = (int64_t)bh * a.L + (int64_t)s * a.N + t0;
+      __syncthreads();
+      for (int i = t; i < kTok * 128; i += kThreads) {
+        const int r = i >> 7, c = i & 127;
+        fk[r][c] = (t0 + r < a.N && c < a.dk) ? sig(ld(K, (row0 + r) * a.dk + c)) : 0.f;
+      }
+      __syncthreads();
+      if (t < kTok) {
+        float e = 0.f;
+        if (hasd)
+          for (int c = 0; c < a.dk; ++c) e = __builtin_fmaf(fk[t][c], zs[c], e);
+        ee[t] = e;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = t + kThreads * r, tt = i / kColB, c = i % kColB, col = cb * kColB + c;
+        const bool ok = t0 + tt < a.N && col < a.dv;
+        float d = 0.f, R = 0.f;
+        for (int x = 0; x < a.dk; ++x) d = __builtin_fmaf(fk[tt][x], GMs[x][c], d);
+        if (hasd && ee[tt] > 0.f) {
+          float n = 0.f;
+          for (int x = 0; x < a.dk; ++x) n = __builtin_fmaf(fk[tt][x], Ms[x][c], n);
+          R = n / ee[tt];
+        }
+        const float vv = ok ? ld(V, (row0 + tt) * a.dv + col) : 0.f;
+        du[tt][c] = ok ? d : 0.f;
+        rr[tt][c] = ok ? R : 0.f;
+        uu[tt][c] = ok ? vv - R : 0.f;
+        if (ok) a.dv_acc[(row0 + tt) * a.dv + col] += d;
+      }
+      __syncthreads();
+      // d sigma(K) share of these columns: U GM^T (+ M dr for the delta rule)
+      for (int r = 0; r < kTok * 128 / kThreads; ++r) {
+        const int i = t + kThreads * r, tt = i >> 7, x = i & 127;
+        if (t0 + tt >= a.N || x >= a.dk) continue;
+        float val = 0.f;
+#pragma unroll
+        for (int c = 0; c < kColB; ++c) val = __builtin_fmaf(uu[tt][c], GMs[x][c], val);
+        if (hasd && ee[tt] > 0.f) {
+          const float ie = 1.f / ee[tt];
+          float mdr = 0.f;
+#pragma unroll
+          for (int c = 0; c < kColB; ++c) mdr = __builtin_fmaf(Ms[x][c], du[tt][c], mdr);
+          val -= mdr * ie;
+        }
+        atomicAdd(&a.dfk_acc[(row0 + tt) * a.dk + x], val);
+      }
+      if (hasd && t < kTok && t0 + t < a.N && ee[t] > 0.f) {
+        float sde = 0.f;
+#pragma unroll
+        for (int c = 0; c < kColB; ++c) sde = __builtin_fmaf(du[t][c], rr[t][c], sde);
+        atomicAdd(&a.de[row0 + t], sde / ee[t]);
+      }
+      if (hasd) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int i = t + kThreads * r, x = i / kColB, c = i % kColB;
+          float acc = gacc[r];
+          for (int tt = 0; tt < kTok; ++tt)
+            if (ee[tt] > 0.f) acc -= fk[tt][x] * du[tt][c] / ee[tt];
+          gacc[r] = acc;
+        }
+      }
+    }
+    __syncthreads();
+    const float* dmr = a.dMr + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = t + kThreads * r, x = i / kColB, c = i % kColB, col = cb * kColB + c;
+      if (x < a.dk && col < a.dv) GMs[x][c] += gacc[r] + dmr[(int64_t)x * a.dv + col];
+    }
+  }
+  __syncthreads();
+  if (a.dM0)
+    for (int i = t; i < a.dk * kColB; i += kThreads) {
+      const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+      if (col < a.dv) a.dM0[((int64_t)bh * a.dk + r) * a.dv + col] = GMs[r][c];
+    }
+}
+
+// -------------------------------------------------------- ez and zchain
+// grid (S, BH), 128 threads: ez_s = sum_t de_t sigma(K_t) (delta rule, not the
+// stream's first segment).
+template <typename T>
+__global__ __launch_bounds__(128) void bwd_ez_kernel(BwdArgs a) {
+  const int s = blockIdx.x, bh = blockIdx.y, x = threadIdx.x;
+  if (x >= a.dk) return;
+  const T* K = static_cast<const T*>(a.k);
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  float acc = 0.f;
+  if (a.delta && !is_first(a, s))
+    for (int r = 0; r < a.N; ++r) acc = __builtin_fmaf(a.de[seg0 + r], sig(ld(K, (seg0 + r) * a.dk + x)), acc);
+  a.ez[((int64_t)bh * a.S + s) * a.dk + x] = acc;
+}
+
+// grid (BH), 128 threads: gzs_s = dL/dz_s; dz0 = dL/dz_0.
+__global__ __launch_bounds__(128) void bwd_zchain_kernel(BwdArgs a) {
+  const int bh = blockIdx.x, x = threadIdx.x;
+  if (x >= a.dk) return;
+  float gz = a.dz ? a.dz[(int64_t)bh * a.dk + x] : 0.f;
+  for (int s = a.S - 1; s >= 0; --s) {
+    const int64_t i = ((int64_t)bh * a.S + s) * a.dk + x;
+    a.gzs[i] = gz;
+    gz += a.dzr[i] + a.ez[i];
+  }
+  if (a.dz0) a.dz0[(int64_t)bh * a.dk + x] = gz;
+}
+
+// ---------------------------------------------------------------- finish
+// grid (ceil(BH * L / 2)), 256 threads: two rows per workgroup.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int x = threadIdx.x & 127;
+  if (row >= (int64_t)a.BH * a.L) return;
+  const int bh = (int)(row / a.L);
+  const int s = (int)((row % a.L) / a.N);
+  const T* K = static_cast<const T*>(a.k);
+  if (x < a.dk) {
+    const int64_t zi = ((int64_t)bh * a.S + s) * a.dk + x;
+    float dfk = a.dfk_acc[row * a.dk + x] + a.gzs[zi];
+    if (a.delta && !is_first(a, s)) dfk = __builtin_fmaf(a.de[row], a.snapz[zi], dfk);
+    const float kx = ld(K, row * a.dk + x);
+    st(static_cast<T*>(a.dk_out), row * a.dk + x, a.dk_acc[row * a.dk + x] + dfk * sig_prime(kx));
+    st(static_cast<T*>(a.dq_out), row * a.dk + x, a.dq_acc[row * a.dk + x]);
+  }
+  if (x < a.dv) st(static_cast<T*>(a.dv_out), row * a.dv + x, a.dv_acc[row * a.dv + x]);
+}
+
+// grid (H), 256 threads: dbeta_h = sum over batch, segments and query blocks.
+__global__ __launch_bounds__(kThreads) void bwd_dbeta_kernel(BwdArgs a) {
+  const int h = blockIdx.x, t = threadIdx.x;
+  __shared__ float red[kThreads];
+  const int64_t per = (int64_t)a.S * a.nqb;
+  float acc = 0.f;
+  for (int b = 0; b < a.B; ++b) {
+    const float* src = a.dbeta_part + (int64_t)(b * a.H + h) * per;
+    for (int64_t i = t; i < per; i += kThreads) acc += src[i];
+  }
+  red[t] = acc;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) a.dbeta[h] = red[0];
+}
+
+__global__ void bwd_zero_kernel(float* p, int64_t n, float* p2, int64_t n2) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n + n2; i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < n) p[i] = 0.f;
+    else p2[i - n] = 0.f;
+  }
+}
+
+int bwd_query_blocks(int N) { return (N + kQB - 1) / kQB; }
+
+template <typename T>
+static hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
+  const unsigned BH = (unsigned)a.BH, S = (unsigned)a.S;
+  const unsigned ncb = (unsigned)((a.dv + kColB - 1) / kColB);
+  hipError_t e;
+#define INFINI_BWD_LAUNCH(...)                    \
+  do {                                            \
+    hipLaunchKernelGGL(__VA_ARGS__);              \
+    if ((e = hipGetLastError()) != hipSuccess) return e; \
+  } while (0)
+  INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_query_kernel<T>, dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_key_kernel<T>, dim3((unsigned)((a.N + kKB - 1) / kKB), S, BH), dim3(kThreads), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_memgrad_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+  {
+    const int64_t n1 = (int64_t)a.BH * a.L * a.dk, n2 = (int64_t)a.BH * a.L;
+    const int64_t blocks = std::min<int64_t>((n1 + n2 + kThreads - 1) / kThreads, 65536);
+    INFINI_BWD_LAUNCH(bwd_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a.dfk_acc, n1, a.de, n2);
+  }
+  INFINI_BWD_LAUNCH(bwd_chain_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(128), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_finish_kernel<T>, dim3((unsigned)(((int64_t)a.BH * a.L + 1) / 2)), dim3(kThreads), 0, stream,
+                    a);
+  INFINI_BWD_LAUNCH(bwd_dbeta_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, stream, a);
+#undef INFINI_BWD_LAUNCH
+  return hipSuccess;
+}
+
+hipError_t launch_backward(const BwdArgs& a, bool bf16_io, hipStream_t stream) {
+  if (a.dk > 128 || a.dv > 128 || a.N < 1 || a.S < 1) return hipErrorInvalidValue;
+  return bf16_io ? launch_all<bf16>(a, stream) : launch_all<float>(a, stream);
+}
+
+}  // namespace infini

@@ -140,6 +140,51 @@ hipError_t launch_open_attn(const OpenAttnArgs& a, hipStream_t stream);
 // open-segment attention for `keys` keys and d_key = dk.
 int open_attn_slots(int keys, int dk);
 
+// ------------------------------------------------------------------ backward
+// Gradients of forward_sequence for the loss <dA, A> + <dM, M_S> + <dz, z_S>.
+// q, k, v, dout, dq, dk, dv in the I/O dtype; everything else fp32.  Workspace
+// arrays (row = bh * L + t, segment index = bh * S + s):
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* beta;     // [H]
+  const float* M0;       // [BH][dk][dv] state before the stream
+  const float* z0;       // [BH][dk]
+  const float* dM;       // [BH][dk][dv] gradient of M_S, or null (zero)
+  const float* dz;       // [BH][dk] or null
+  void* dq_out;
+  void* dk_out;
+  void* dv_out;
+  float* dbeta;          // [H]
+  float* dM0;            // [BH][dk][dv] or null
+  float* dz0;            // [BH][dk] or null
+  float* snapM;          // [BH*S][dk][dv] M_{s-1}
+  float* snapz;          // [BH*S][dk]
+  float* dMr;            // [BH*S][dk][dv] retrieval's gradient of M_{s-1}
+  float* dzr;            // [BH*S][dk]
+  float* ez;             // [BH*S][dk]
+  float* gzs;            // [BH*S][dk] dL/dz_s
+  float* lse;            // [BH*L] softmax log-normaliser of each row
+  float* drow;           // [BH*L] <(1 - g) dA, A_dot>
+  float* rs;             // [BH*L] g / den (0 without memory)
+  float* dden;           // [BH*L]
+  float* de;             // [BH*L] delta rule: gradient of sigma(K_t) . z_{s-1}
+  float* dq_acc;         // [BH*L][dk]
+  float* dk_acc;         // [BH*L][dk] local attention's dk
+  float* dv_acc;         // [BH*L][dv]
+  float* dfk_acc;        // [BH*L][dk] update's d sigma(K)
+  float* dbeta_part;     // [BH*S][nqb]
+  int B, H, BH, N, S, dk, dv, nqb;
+  int64_t L, seg_base;
+  int delta;
+  float scale;
+};
+hipError_t launch_backward(const BwdArgs& a, bool bf16_io, hipStream_t stream);
+// Query blocks per segment of the backward (the dbeta_part width).
+int bwd_query_blocks(int N);
+
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);
 

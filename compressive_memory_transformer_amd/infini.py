@@ -101,6 +101,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_append_workspace_bytes.restype = sz
     lib.infini_attn_append.argtypes = [sp, op, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     lib.infini_attn_append.restype = ctypes.c_int
+    lib.infini_attn_backward_workspace_bytes.argtypes = [sp, i64]
+    lib.infini_attn_backward_workspace_bytes.restype = sz
+    lib.infini_attn_backward_sequence.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  vp, sz, vp]
+    lib.infini_attn_backward_sequence.restype = ctypes.c_int
     lib.infini_attn_reset.argtypes = [sp, vp]
     lib.infini_attn_reset.restype = ctypes.c_int
     lib.infini_attn_last_error.argtypes = []
@@ -188,6 +193,18 @@ def append(st: State, os_: OpenSegment, q, k, v, n_tokens, beta, out, workspace,
            check=True) -> int:
     rc = load_library().infini_attn_append(ctypes.byref(st), ctypes.byref(os_), _ptr(q), _ptr(k), _ptr(v),
                                            n_tokens, _ptr(beta), _ptr(out), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
+def backward_workspace_bytes(st: State, seq_len: int) -> int:
+    return load_library().infini_attn_backward_workspace_bytes(ctypes.byref(st), seq_len)
+
+
+def backward_sequence(st: State, q, k, v, seq_len, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, workspace,
+                      ws_bytes, stream=None, check=True) -> int:
+    rc = load_library().infini_attn_backward_sequence(
+        ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len, _ptr(beta), _ptr(dout), _ptr(dM), _ptr(dz),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(workspace), ws_bytes, stream)
     return _check(rc) if check else rc
 
 
@@ -293,4 +310,27 @@ class InfiniAttention:
             out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
         ws, nbytes = self.append_workspace(n)
         append(self.state, self.open, q, k, v, n, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
+        return out
+
+    def backward_sequence(self, q, k, v, beta, dout, M0, z0, segments_done, dM=None, dz=None, stream=None):
+        """Gradients of a forward_sequence call over q, k, v, beta that started
+        from the state (M0, z0, segments_done), for the output gradient dout and
+        the final-state gradients dM, dz (None for zero).  Returns a dict with dq,
+        dk, dv (input dtype), dbeta [H], dM0 and dz0 (fp32)."""
+        torch = self.torch
+        st = State.from_buffer_copy(self.state)
+        st.M, st.z, st.segments_done = _ptr(M0), _ptr(z0), int(segments_done)
+        seq_len = q.shape[2]
+        need = backward_workspace_bytes(st, seq_len)
+        if need == 0:
+            raise InfiniError(EINVAL, f"no backward workspace size for seq_len={seq_len}")
+        raw = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
+        off = (-raw.data_ptr()) % 256
+        ws = raw[off:off + need]
+        out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+               "dbeta": torch.empty(self.state.heads, dtype=torch.float32, device=self.device),
+               "dM0": torch.empty_like(M0), "dz0": torch.empty_like(z0)}
+        backward_sequence(st, q, k, v, seq_len, beta, dout, dM, dz, out["dq"], out["dk"], out["dv"], out["dbeta"],
+                          out["dM0"], out["dz0"], ws, need, _stream_handle(torch, stream))
+        out["_workspace"] = raw   # kept alive until the caller synchronises
         return out

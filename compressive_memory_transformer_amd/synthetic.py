@@ -27,6 +27,9 @@ from dataclasses import dataclass, field
 import numpy as np
 
 Q_ID, K_ID, V_ID, BETA_ID, PLANT_ID = 0, 1, 2, 3, 4
+# output gradient tiles (d_value wide, like V), the final-state gradients and a
+# starting state for streams that resume from a non-empty memory
+DOUT_ID, STATE_GRAD_ID, STATE0_ID = 5, 6, 7
 
 
 @dataclass(frozen=True)
@@ -114,7 +117,7 @@ def planted_pair(w: Workload):
 def tile(w: Workload, tensor_id: int, b: int, h: int, s: int) -> np.ndarray:
     """One [segment_len, d] tile of Q (0), K (1) or V (2) as float32 values that are
     exact in the workload's storage dtype."""
-    d = w.d_value if tensor_id == V_ID else w.d_key
+    d = w.d_value if tensor_id in (V_ID, DOUT_ID) else w.d_key
     x = rng(w.seed, tensor_id, b, h, s).standard_normal((w.segment_len, d), dtype=np.float32)
     if w.input_scale != 1.0:
         x *= np.float32(w.input_scale)
@@ -129,6 +132,26 @@ def tile(w: Workload, tensor_id: int, b: int, h: int, s: int) -> np.ndarray:
         elif s == w.segments - 1 and tensor_id == Q_ID:
             x[p1] = kstar[h]
     return x
+
+
+def state_grads(w: Workload):
+    """Gradients of the final state: dM [B, H, d_key, d_value] and dz [B, H, d_key],
+    float32 standard normals scaled by the input scale."""
+    g = rng(w.seed, STATE_GRAD_ID)
+    dM = g.standard_normal((w.batch, w.heads, w.d_key, w.d_value), dtype=np.float32) * np.float32(w.input_scale)
+    dz = g.standard_normal((w.batch, w.heads, w.d_key), dtype=np.float32) * np.float32(w.input_scale)
+    return dM, dz
+
+
+def initial_state(w: Workload, segments: int = 2):
+    """A starting state (M0, z0) shaped like the memory after `segments` segments
+    of the workload's inputs: z0 about segments * N per entry (positive), M0 entries
+    of standard deviation sqrt(segments * N) times the input scale.  float32."""
+    g = rng(w.seed, STATE0_ID)
+    n0 = float(segments * w.segment_len)
+    M0 = (g.standard_normal((w.batch, w.heads, w.d_key, w.d_value)) * math.sqrt(n0) * w.input_scale)
+    z0 = n0 * (1.0 + 0.05 * np.abs(g.standard_normal((w.batch, w.heads, w.d_key))))
+    return M0.astype(np.float32), z0.astype(np.float32)
 
 
 def betas(w: Workload) -> np.ndarray:
@@ -152,7 +175,7 @@ def full_tensor(w: Workload, tensor_id: int, as_bits: bool = False,
 
     With ``as_bits`` and a bf16 workload the result is the uint16 bit pattern,
     ready to be viewed as bfloat16 on the device."""
-    d = w.d_value if tensor_id == V_ID else w.d_key
+    d = w.d_value if tensor_id in (V_ID, DOUT_ID) else w.d_key
     hs = list(range(w.heads)) if heads is None else list(heads)
     S = w.segments if segments is None else segments
     bits = as_bits and w.dtype == "bf16"

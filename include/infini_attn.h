@@ -168,6 +168,30 @@ int infini_attn_append(infini_attn_state *st, infini_attn_open_segment *os, cons
                        const void *k, const void *v, int64_t n_tokens, const float *beta,
                        void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Gradients (training through the layer: section 4 of the page
+ * "精读笔记：Infini-attention"; the pages give the forward equations of sections
+ * 3.1, 3.3, 3.4 and 3.5, and these are their derivatives).
+ *
+ * For a forward_sequence call that started from the state *st (M, z and
+ * segments_done as they were BEFORE that call: keep a copy, the forward updates
+ * them in place) over q, k, v, beta, and the loss
+ *     <dout, A> + <dM, M_S> + <dz, z_S>
+ * (A the forward's output, M_S, z_S the state after it), writes dq, dk, dv (the
+ * dtype of the state, layouts of q, k, v), dbeta (fp32 [H], summed over the
+ * batch), and, when non-NULL, dM0, dz0 (fp32, layouts of M and z: the gradient
+ * of the state the call started from, to chain calls backwards).  dM and dz
+ * (fp32, the gradient of the final state) may be NULL for zero.  *st is not
+ * changed.  The forward is recomputed from the inputs (nothing has to be kept
+ * from it besides the starting state).  No output may overlap another, the
+ * workspace, the inputs or the state.  Errors as for forward_sequence. */
+size_t infini_attn_backward_workspace_bytes(const infini_attn_state *st, int64_t seq_len);
+int infini_attn_backward_sequence(const infini_attn_state *st, const void *q, const void *k,
+                                  const void *v, int64_t seq_len, const float *beta,
+                                  const void *dout, const float *dM, const float *dz, void *dq,
+                                  void *dk, void *dv, float *dbeta, float *dM0, float *dz0,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
 /* M, z <- 0 on `stream`; segments_done <- 0. */
 int infini_attn_reset(infini_attn_state *st, void *stream);
 

@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -218,3 +218,53 @@ def test_append_rejects_bad_arguments(case):
     assert _snapshot(st) == before
     if os_ is not None:
         assert os_.filled == fill_before
+
+
+def test_backward_workspace_bytes():
+    st = _state(rule=ia.RULE_DELTA)
+    S, D, BH, N = 4, 128, 2, 2048
+    L = S * N
+    mm, seg, rows = BH * S * D * D, BH * S * D, BH * L
+    # snapshots + retrieval gradients of M, four per-segment d_key vectors, five per-row
+    # scalars, four per-row accumulators, the dbeta shares (64 query blocks per segment)
+    want = 4 * (2 * mm + 4 * seg + 5 * rows + 4 * rows * D + BH * S * 64)
+    assert ia.backward_workspace_bytes(st, L) == want
+    assert ia.backward_workspace_bytes(st, L + 1) == 0
+    assert ia.backward_workspace_bytes(_state(batch=0), L) == 0
+
+
+@pytest.mark.parametrize("case", ["null_dout", "null_dq", "ragged", "small_ws", "alias_out_in", "alias_outs",
+                                  "alias_ws_state", "misaligned_beta", "bad_state"])
+def test_backward_rejects_bad_arguments(case):
+    st = _state()
+    L = 2 * 2048
+    need = ia.backward_workspace_bytes(st, L)
+    q, k, v, beta, dout = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8
+    dq, dk, dv, dbeta, dM0, dz0 = FAKE * 9, FAKE * 10, FAKE * 11, FAKE * 12, FAKE * 13, FAKE * 14
+    dM, dz, ws, nbytes = None, None, FAKE * 15, need
+    expect = ia.EINVAL
+    if case == "null_dout":
+        dout = None
+    elif case == "null_dq":
+        dq = None
+    elif case == "ragged":
+        L = 2048 + 64
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    elif case == "alias_out_in":
+        dk = k + 64
+    elif case == "alias_outs":
+        dv = dq + 64
+    elif case == "alias_ws_state":
+        ws = st.M - 256 * 4
+    elif case == "misaligned_beta":
+        beta = FAKE * 7 + 2
+    elif case == "bad_state":
+        st.d_key = 100
+        expect = ia.EUNSUPPORTED
+    before = _snapshot(st)
+    rc = ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, nbytes, None,
+                              check=False)
+    assert rc == expect, (case, ia.last_error())
+    assert ia.last_error()
+    assert _snapshot(st) == before

@@ -1,0 +1,88 @@
+"""GPU parity of infini_attn_backward_sequence (the gradients of forward_sequence)
+against the float64 gradient oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+
+from compressive_memory_transformer_amd import synthetic as syn
+from oracle import infini_grad as og
+from tests import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = gh.torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from compressive_memory_transformer_amd import infini as ia
+    ia.load_library()
+    yield
+
+
+def _workload(name, seed, B, H, dk, dv, N, S, dtype):
+    scale = 1.0 / np.sqrt(dk) if dtype == "bf16" else 1.0
+    return syn.Workload(name, seed, B, H, dk, dv, N, S, dtype, ("linear", "delta"), "uniform", 2.0, scale)
+
+
+CASES = [
+    # name, seed, B, H, d_key, d_value, N, S, dtype, segments already in the memory
+    ("f32_tiny", 31, 1, 2, 32, 32, 64, 4, "f32", 0),
+    ("f32_ragged_resume", 32, 2, 1, 20, 24, 37, 3, "f32", 2),
+    ("bf16_d64", 33, 1, 2, 64, 64, 128, 3, "bf16", 0),
+    ("bf16_d128_resume", 34, 1, 2, 128, 128, 256, 3, "bf16", 2),
+]
+
+
+def _device(torch, arr, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to("cuda")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(case, rule):
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    name, seed, B, H, dk, dv, N, S, dtype, done = case
+    gh.log(f"backward {name} rule={rule}")
+    w = _workload(name, seed, B, H, dk, dv, N, S, dtype)
+    qn, kn, vn, don = (syn.full_tensor(w, i) for i in (syn.Q_ID, syn.K_ID, syn.V_ID, syn.DOUT_ID))
+    beta = syn.betas(w)
+    dM, dz = syn.state_grads(w)
+    if done:
+        M0, z0 = syn.initial_state(w, done)
+    else:
+        M0, z0 = np.zeros((B, H, dk, dv), np.float32), np.zeros((B, H, dk), np.float32)
+    # bf16 values are exact in float32, so the device gets exactly what the oracle sees
+    q, k, v, dout = (_device(torch, x, dtype) for x in (qn, kn, vn, don))
+    eng = ia.InfiniAttention(B, H, dk, dv, N, dtype, rule)
+    g = eng.backward_sequence(q, k, v, torch.from_numpy(beta).cuda(), dout, torch.from_numpy(M0).cuda(),
+                              torch.from_numpy(z0).cuda(), done, dM=torch.from_numpy(dM).cuda(),
+                              dz=torch.from_numpy(dz).cuda())
+    torch.cuda.synchronize()
+    want = og.backward_sequence(qn, kn, vn, beta, rule, N, don, dM=dM, dz=dz, M0=M0, z0=z0, segments_done=done)
+    tol = gh.tol(dtype)
+    worst = {}
+    for key in ("dq", "dk", "dv"):
+        got = gh.to_host(g[key])
+        for b in range(B):
+            for h in range(H):
+                for s in range(S):
+                    rows = slice(s * N, (s + 1) * N)
+                    e = gh.metric(got[b, h, rows], want[key][b, h, rows], dtype)
+                    worst[key] = max(worst.get(key, 0.0), e)
+                    assert e <= tol, f"{name}/{rule} {key} b={b} h={h} s={s}: error {e:.3e}"
+    for key in ("dM0", "dz0"):
+        got = gh.to_host(g[key])
+        for b in range(B):
+            for h in range(H):
+                e = gh.metric(got[b, h], want[key][b, h], "f32" if dtype == "f32" else "bf16")
+                worst[key] = max(worst.get(key, 0.0), e)
+                assert e <= tol, f"{name}/{rule} {key} b={b} h={h}: error {e:.3e}"
+    gb = gh.to_host(g["dbeta"])
+    e = float(np.abs(gb - want["dbeta"]).max() / max(np.abs(want["dbeta"]).max(), 1e-30))
+    worst["dbeta"] = e
+    gh.log("  " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert e <= tol, f"{name}/{rule} dbeta: error {e:.3e} ({gb} vs {want['dbeta']})"
