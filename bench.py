@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+VALU_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector (256 CUs x 2.4 GHz x 256 FLOP/clk)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 DOMINANT_SOURCES = ["compressive_memory_transformer_amd/csrc/fa_fwd.hip",
@@ -48,6 +49,9 @@ def parse():
                    help="time single-token decode steps (infini_attn_append of one token per (b, h)) with "
                         "the open segment holding FILLED tokens when the timed steps start and the memory "
                         "holding all but the last segment of the workload; prints its own JSON line")
+    p.add_argument("--backward", action="store_true",
+                   help="time infini_attn_backward_sequence over the workload (gradients of a forward from an "
+                        "empty memory); prints its own JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 launches), to calibrate "
                         "the HBM byte counters of a profiler against a known size")
@@ -216,6 +220,121 @@ def decode_cpu_baseline(w, rule: str, filled: int, budget_s: float):
                       f"{w.batch * w.heads} heads, float64 numpy, {spent:.1f}s"}
 
 
+def backward_flops(w, rule: str) -> float:
+    """Algorithmic FLOP of one backward over the whole workload.  Per seg-head: the
+    local attention's five products over the causal pairs (scores recomputed, dP,
+    dV, dQ, dK: (3 d_key + 2 d_value) N (N + 1)), the retrieval's three (numerator
+    recomputed, d sigma(q), dM: 6 N d_key d_value), the update's (linear: dV and
+    d sigma(K), 4 N d_k d_v; delta: R recomputed, dV, two d sigma(K) terms and dM,
+    10 N d_k d_v) and its replay (linear 2, delta 4 N d_k d_v)."""
+    N, dk, dv = w.segment_len, w.d_key, w.d_value
+    att = (3 * dk + 2 * dv) * N * (N + 1)
+    mem = 6 * N * dk * dv + (6 if rule == "linear" else 14) * N * dk * dv
+    return float(att + mem) * w.batch * w.heads * w.segments
+
+
+def backward_cpu_baseline(w, rule: str, budget_s: float):
+    """The float64 gradient oracle on the first segments of one (batch, head),
+    doubling the number of segments until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from compressive_memory_transformer_amd import synthetic as syn
+    from oracle import infini_grad as og
+
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    beta = syn.betas(w)[:1]
+    dM, dz = syn.state_grads(w)
+    spent, segs, n = 0.0, 0, 1
+    while spent < budget_s / 3 and n <= w.segments:
+        q, k, v, do = (np.concatenate([syn.tile(w, i, 0, 0, s) for s in range(n)])[None, None].astype(np.float64)
+                       for i in (syn.Q_ID, syn.K_ID, syn.V_ID, syn.DOUT_ID))
+        t0 = time.perf_counter()
+        og.backward_sequence(q, k, v, beta, rule, w.segment_len, do, dM=dM[:1, :1], dz=dz[:1, :1])
+        spent, segs = time.perf_counter() - t0, n
+        n *= 2
+    tokens = segs * w.segment_len / w.heads   # a token is all heads of one position
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"backward of the first {segs} segments of one (batch, head) of {w.name}/{rule}, "
+                      f"float64 numpy, {spent:.1f}s"}
+
+
+def bench_backward(args):
+    import numpy as np
+    import torch
+
+    from compressive_memory_transformer_amd import infini as ia
+    from compressive_memory_transformer_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    rule = args.rule or w.rules[0]
+    ia.load_library()
+
+    def upload(tid):
+        arr = syn.full_tensor(w, tid, as_bits=True)
+        if w.dtype == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(arr).to("cuda")
+
+    q, k, v, dout = (upload(i) for i in (syn.Q_ID, syn.K_ID, syn.V_ID, syn.DOUT_ID))
+    beta = torch.from_numpy(syn.betas(w)).to("cuda")
+    dM, dz = (torch.from_numpy(x).to("cuda") for x in syn.state_grads(w))
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, w.dtype, rule)
+    M0, z0 = torch.zeros_like(eng.M), torch.zeros_like(eng.z)
+    st = ia.State.from_buffer_copy(eng.state)
+    st.M, st.z, st.segments_done = M0.data_ptr(), z0.data_ptr(), 0
+    L = w.seq_len
+    need = ia.backward_workspace_bytes(st, L)
+    raw = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    ws = raw[(-raw.data_ptr()) % 256:][:need]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbeta = torch.empty(w.heads, dtype=torch.float32, device="cuda")
+    dM0, dz0 = torch.empty_like(M0), torch.empty_like(z0)
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, need, sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    fl = backward_flops(w, rule)
+    tf = fl / gpu_s / 1e12
+    cpu = backward_cpu_baseline(w, rule, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    line = {
+        "metric": "Infini-attention backward tokens/sec on 1 MI355X (gradients of forward_sequence)",
+        "value": w.tokens * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"backward/{w.name}", "batch": w.batch, "heads": w.heads,
+                   "segment_len": w.segment_len, "segments": w.segments, "d_key": w.d_key, "d_value": w.d_value,
+                   "rule": rule, "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "kernel": "whole backward (fp32 VALU kernels)", "achieved": tf,
+                     "peak": VALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / VALU_F32_PEAK_TFLOPS,
+                     "traffic": None, "flops_per_step": fl, "avg_step_ms_on_stream": gpu_s * 1e3,
+                     "frac_of_bf16_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_decode(args):
     import torch
 
@@ -319,6 +438,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.backward:
+        bench_backward(args)
+        return
     if args.decode:
         bench_decode(args)
         return

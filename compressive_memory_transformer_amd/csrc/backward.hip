@@ -151,7 +151,10 @@ __global__ __launch_bounds__(kThreads) void bwd_snap_kernel(BwdArgs a) {
 
 // ----------------------------------------------------------------- query
 // grid (query blocks of 32, S, BH).  Thread = (row i = t / 8, part p = t % 8).
-template <typename T>
+// ATT = false (bf16 path): the local attention's share (statistics, A_dot, its
+// dq) has come from the MFMA kernel, which left E = <dA, A_dot> per row and dq
+// in dq_acc; only the retrieval's share is computed and added.
+template <typename T, bool ATT>
 __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H, t = threadIdx.x;
   const int i = t >> 3, p = t & 7;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   float m = -__builtin_inff(), l = 0.f, o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
-  for (int kc = 0; kc < kend; kc += kKC) {
+  for (int kc = 0; ATT && kc < kend; kc += kKC) {
     __syncthreads();
     for (int x = t; x < kKC * 128; x += kThreads) {
       const int r = x >> 7, c = x & 127;
@@ -227,8 +230,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
       o[e] = acc;
     }
   }
-  const float lse = valid ? m + __logf(l) : 0.f;
-  const float inv_l = valid ? 1.f / l : 0.f;
+  const float lse = valid && ATT ? m + __logf(l) : 0.f;
+  const float inv_l = valid && ATT ? 1.f / l : 0.f;
 
   // retrieval from M_{s-1}, z_{s-1}; the gate; D; the retrieval's dq
   __syncthreads();
@@ -267,7 +270,9 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
       msum = __builtin_fmaf(d, amem, msum);
     }
   }
-  const float D = (1.f - g) * row8_sum(dsum);
+  const float erow = ATT ? row8_sum(dsum) : (valid ? a.erow[seg0 + qi] : 0.f);
+  const float D = (1.f - g) * erow;
+  if (!ATT && p == 0) bsum -= erow;
   const float rs = has ? g / den : 0.f;
   const float msum_row = row8_sum(msum);
   const float dden = has ? -g * msum_row / den : 0.f;
@@ -279,8 +284,10 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   }
   if (valid && p == 0) {
     const int64_t row = seg0 + qi;
-    a.lse[row] = lse;
-    a.drow[row] = D;
+    if (ATT) {
+      a.lse[row] = lse;
+      a.drow[row] = D;
+    }
     a.rs[row] = rs;
     a.dden[row] = dden;
   }
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   }
 
   // second sweep: the local attention's dq = scale sum_j dS_ij k_j
-  for (int kc = 0; kc < kend; kc += kKC) {
+  for (int kc = 0; ATT && kc < kend; kc += kKC) {
     __syncthreads();
     for (int x = t; x < kKC * 128; x += kThreads) {
       const int r = x >> 7, c = x & 127;
@@ -343,7 +350,10 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int x = 16 * p + e;
-      if (x < a.dk) a.dq_acc[(seg0 + qi) * a.dk + x] = dq[e];
+      if (x < a.dk) {
+        float* dst = a.dq_acc + (seg0 + qi) * a.dk + x;
+        *dst = ATT ? dq[e] : *dst + dq[e];
+      }
     }
   }
 }
@@ -663,7 +673,7 @@ __global__ void bwd_zero_kernel(float* p, int64_t n, float* p2, int64_t n2) {
 int bwd_query_blocks(int N) { return (N + kQB - 1) / kQB; }
 
 template <typename T>
-static hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
   const unsigned BH = (unsigned)a.BH, S = (unsigned)a.S;
   const unsigned ncb = (unsigned)((a.dv + kColB - 1) / kColB);
   hipError_t e;
@@ -673,8 +683,15 @@ static hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e; \
   } while (0)
   INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
-  INFINI_BWD_LAUNCH(bwd_query_kernel<T>, dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
-  INFINI_BWD_LAUNCH(bwd_key_kernel<T>, dim3((unsigned)((a.N + kKB - 1) / kKB), S, BH), dim3(kThreads), 0, stream, a);
+  if (mfma) {
+    e = a.dk == 128 ? launch_backward_attention_mfma<128>(a, stream) : launch_backward_attention_mfma<64>(a, stream);
+    if (e != hipSuccess) return e;
+    INFINI_BWD_LAUNCH((bwd_query_kernel<T, false>), dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
+  } else {
+    INFINI_BWD_LAUNCH((bwd_query_kernel<T, true>), dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
+    INFINI_BWD_LAUNCH(bwd_key_kernel<T>, dim3((unsigned)((a.N + kKB - 1) / kKB), S, BH), dim3(kThreads), 0, stream,
+                      a);
+  }
   INFINI_BWD_LAUNCH(bwd_memgrad_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
   {
     const int64_t n1 = (int64_t)a.BH * a.L * a.dk, n2 = (int64_t)a.BH * a.L;
@@ -693,7 +710,10 @@ static hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_backward(const BwdArgs& a, bool bf16_io, hipStream_t stream) {
   if (a.dk > 128 || a.dv > 128 || a.N < 1 || a.S < 1) return hipErrorInvalidValue;
-  return bf16_io ? launch_all<bf16>(a, stream) : launch_all<float>(a, stream);
+  // the bf16 path (d_key = d_value in {64, 128}, N a multiple of 64) takes the
+  // MFMA kernels for the local attention
+  const bool mfma = bf16_io && a.dk == a.dv && (a.dk == 64 || a.dk == 128) && a.N % 64 == 0;
+  return bf16_io ? launch_all<bf16>(a, mfma, stream) : launch_all<float>(a, false, stream);
 }
 
 }  // namespace infini

@@ -1,0 +1,339 @@
+// Local attention part of the gradients on the bf16 MFMA units (the chain rule
+// through A_dot = softmax(scale Q K^T, causal) V of the close-reading page
+// "精读笔记：Infini-attention", section 3.1 with the mask of section 3.8 step 2).
+//
+//   bwd_q_mfma_kernel<D>: one workgroup (4 waves) per 128 query rows of a
+//     segment, one wave per 32 rows.  First sweep over the keys: the row's
+//     softmax maximum and sum, A_dot, then E = <dA, A_dot> and D = (1 - g) E.
+//     Second sweep: dS = P ((1 - g) dP - D) and dq += scale dS K.  Scores are
+//     computed transposed (keys x queries), so every register operand is already
+//     in the accumulator layout of the product that consumes it.
+//   bwd_kv_mfma_kernel<D>: one workgroup per 128 keys, one wave per 32 keys,
+//     the wave's keys and values held as operands in registers; for every chunk
+//     of 64 later queries: S, dP, P, dS, then dv += (1 - g) P^T dA and
+//     dk += scale dS^T Q.
+//
+// Operands (v_mfma_f32_32x32x16_bf16): a row-major LDS tile X is read either by
+// rows (row_op: lane l gets X[r0 + l % 32][k0 + 8 (l / 32) + 0..7]) or, for a
+// contraction over its rows, with the transposing LDS read (tr_op: lane l gets
+// X[r0 + 4 h + e][c0 + l % 32] and X[r0 + 8 + 4 h + e][...], h = l / 32), whose
+// row order matches a 32 x 32 accumulator used as the other operand (lane l
+// holds rows 8 (r / 4) + 4 h + r % 4 of column l % 32).  Chunks of K, V (or Q,
+// dA) are staged through two LDS buffers, the next chunk's global loads issued
+// before the current chunk's products.
+#include "common.h"
+#include "kernels.h"
+
+namespace infini {
+
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdBlock = 32 * kBwdWaves;   // rows (queries or keys) per workgroup
+constexpr int kChunk = 64;                  // rows of the streamed operand per step
+
+__device__ __forceinline__ bf16x8 row_op(const bf16* X, int pitch, int r0, int k0, int lane) {
+  return lds_read8(X + (r0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
+}
+
+__device__ __forceinline__ bf16x8 tr_op(const bf16* X, int pitch, int r0, int c0, int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 3, s = lane & 15;
+  return lds_operand_tr(X, pitch, r0 + 4 * h, r0 + 8 + 4 * h, c0 + 16 * (g & 1), s);
+}
+
+// Accumulator rows 8 ks .. 8 ks + 7 of `c` as a bf16 B operand.
+__device__ __forceinline__ bf16x8 acc_op(const f32x16& c, int ks) {
+  bf16x8 b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = f2bf(c[8 * ks + j]);
+  return b;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Row of accumulator element r for lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Loads a 64-row chunk of two row-major [rows][D] bf16 tensors into registers
+// (16 bytes per piece) and stores it into LDS tiles of pitch D + 8.
+template <int D>
+struct ChunkPair {
+  static constexpr int P = D + 8;
+  static constexpr int PIECES = kChunk * D / 8 / (64 * kBwdWaves);
+  bf16x8 x[PIECES], y[PIECES];
+  __device__ __forceinline__ void load(const bf16* X, const bf16* Y, int64_t row0) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = threadIdx.x + 64 * kBwdWaves * i, r = p / (D / 8), c8 = p % (D / 8);
+      x[i] = *reinterpret_cast<const bf16x8*>(X + (row0 + r) * D + 8 * c8);
+      y[i] = *reinterpret_cast<const bf16x8*>(Y + (row0 + r) * D + 8 * c8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* xs, bf16* ys) const {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = threadIdx.x + 64 * kBwdWaves * i, r = p / (D / 8), c8 = p % (D / 8);
+      *reinterpret_cast<bf16x8*>(xs + r * P + 8 * c8) = x[i];
+      *reinterpret_cast<bf16x8*>(ys + r * P + 8 * c8) = y[i];
+    }
+  }
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
+  constexpr int P = D + 8, KS = D / 16, DB = D / 32;
+  const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  const bf16* K = static_cast<const bf16*>(a.k);
+  const bf16* V = static_cast<const bf16*>(a.v);
+  const bf16* DO = static_cast<const bf16*>(a.dout);
+  __shared__ __attribute__((aligned(16))) bf16 kc[2][kChunk * P];
+  __shared__ __attribute__((aligned(16))) bf16 vc[2][kChunk * P];
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  const int q0 = qb * kBwdBlock, qw0 = q0 + 32 * w;
+  const bool qvalid = qw0 < a.N;
+  const int qcol = qw0 + l32;                      // this lane's query (column of S^T)
+  const int64_t qrow = seg0 + min(qcol, a.N - 1);
+  const float g = sigmoid_gate(a.beta[h]);
+  const float sl2 = a.scale * kLog2e;
+  bf16x8 qr[KS], dr[KS];
+#pragma unroll
+  for (int c = 0; c < KS; ++c) {
+    qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
+    dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
+  }
+  const int kend = min(a.N, q0 + kBwdBlock);
+
+  // ---- first sweep: maximum, sum and A_dot^T of the wave's 32 query columns
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = zero16();
+  float m2 = -__builtin_inff(), l = 0.f;
+  ChunkPair<D> cp;
+  cp.load(K, V, seg0);
+  cp.store(kc[0], vc[0]);
+  __syncthreads();
+  for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kChunk, buf ^= 1) {
+    const bool next = kc0 + kChunk < kend;
+    if (next) cp.load(K, V, seg0 + kc0 + kChunk);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key0 = kc0 + 32 * kt;
+      if (!qvalid || key0 > qw0 + 31) continue;   // keys all after the wave's queries
+      f32x16 sacc = zero16();
+#pragma unroll
+      for (int c = 0; c < KS; ++c) sacc = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sacc);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = key0 + acc_row(r, hh) <= qcol ? sacc[r] * sl2 : -__builtin_inff();
+        sacc[r] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m2, mx);               // finite: key 0 is in the first tile
+      const float alpha = exp2_fast(m2 - mn);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(sacc[r] - mn);
+        sacc[r] = p;
+        l += p;
+      }
+      m2 = mn;
+      const bf16x8 p0 = acc_op(sacc, 0), p1 = acc_op(sacc, 1);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        o[d] = mfma32(tr_op(vc[buf], P, 32 * kt, 32 * d, lane), p0, o[d]);
+        o[d] = mfma32(tr_op(vc[buf], P, 32 * kt + 16, 32 * d, lane), p1, o[d]);
+      }
+    }
+    if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
+    __syncthreads();
+  }
+  const float lt = l + __shfl_xor(l, 32);
+  const float lse2 = m2 + log2f(lt);
+  const float inv_l = 1.f / lt;
+  // E = <dA, A_dot> of the lane's query: the lane holds 16 DB values of A_dot^T
+  float e = 0.f;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e = __builtin_fmaf(bf2f(DO[qrow * D + 32 * d + acc_row(r, hh)]), o[d][r], e);
+  e = (e + __shfl_xor(e, 32)) * inv_l;
+  const float Dv = (1.f - g) * e;
+  if (qvalid && hh == 0) {
+    a.lse[qrow] = lse2 * (1.f / kLog2e);
+    a.drow[qrow] = Dv;
+    a.erow[qrow] = e;
+  }
+
+  // ---- second sweep: dq^T += K^T dS^T
+  f32x16 dq[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) dq[d] = zero16();
+  cp.load(K, V, seg0);
+  cp.store(kc[0], vc[0]);
+  __syncthreads();
+  for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kChunk, buf ^= 1) {
+    const bool next = kc0 + kChunk < kend;
+    if (next) cp.load(K, V, seg0 + kc0 + kChunk);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key0 = kc0 + 32 * kt;
+      if (!qvalid || key0 > qw0 + 31) continue;
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        sacc = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sacc);
+        pacc = mfma32(row_op(vc[buf], P, 32 * kt, 16 * c, lane), dr[c], pacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool vis = key0 + acc_row(r, hh) <= qcol;
+        const float p = vis ? exp2_fast(sacc[r] * sl2 - lse2) : 0.f;
+        sacc[r] = p * ((1.f - g) * pacc[r] - Dv);
+      }
+      const bf16x8 d0 = acc_op(sacc, 0), d1 = acc_op(sacc, 1);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt, 32 * d, lane), d0, dq[d]);
+        dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt + 16, 32 * d, lane), d1, dq[d]);
+      }
+    }
+    if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
+    __syncthreads();
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a.dq_acc[qrow * D + 32 * d + acc_row(r, hh)] = a.scale * dq[d][r];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) {
+  constexpr int P = D + 8, KS = D / 16, DB = D / 32;
+  const int kb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  const bf16* K = static_cast<const bf16*>(a.k);
+  const bf16* V = static_cast<const bf16*>(a.v);
+  const bf16* DO = static_cast<const bf16*>(a.dout);
+  __shared__ __attribute__((aligned(16))) bf16 qc[2][kChunk * P];
+  __shared__ __attribute__((aligned(16))) bf16 dc[2][kChunk * P];
+  __shared__ float lc[2][kChunk], dcr[2][kChunk];
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  const int j0 = kb * kBwdBlock, kw0 = j0 + 32 * w;
+  const bool kvalid = kw0 < a.N;
+  const int kcol = kw0 + l32;                      // this lane's key (column of S)
+  const int64_t krow = seg0 + min(kcol, a.N - 1);
+  const float g = sigmoid_gate(a.beta[h]);
+  const float sl2 = a.scale * kLog2e;
+  bf16x8 kr[KS], vr[KS];
+#pragma unroll
+  for (int c = 0; c < KS; ++c) {
+    kr[c] = *reinterpret_cast<const bf16x8*>(K + krow * D + 16 * c + 8 * hh);
+    vr[c] = *reinterpret_cast<const bf16x8*>(V + krow * D + 16 * c + 8 * hh);
+  }
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) dk[d] = dv[d] = zero16();
+  ChunkPair<D> cp;
+  const int qbeg = min(j0, a.N - kChunk);          // queries before j0 see none of these keys
+  cp.load(Q, DO, seg0 + qbeg);
+  cp.store(qc[0], dc[0]);
+  if (threadIdx.x < kChunk) {
+    lc[0][threadIdx.x] = a.lse[seg0 + qbeg + threadIdx.x] * kLog2e;
+    dcr[0][threadIdx.x] = a.drow[seg0 + qbeg + threadIdx.x];
+  }
+  __syncthreads();
+  for (int qc0 = qbeg, buf = 0; qc0 < a.N; qc0 += kChunk, buf ^= 1) {
+    const bool next = qc0 + kChunk < a.N;
+    float nl = 0.f, nd = 0.f;
+    if (next) {
+      cp.load(Q, DO, seg0 + qc0 + kChunk);
+      if (threadIdx.x < kChunk) {
+        nl = a.lse[seg0 + qc0 + kChunk + threadIdx.x];
+        nd = a.drow[seg0 + qc0 + kChunk + threadIdx.x];
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int qr0 = qc0 + 32 * qt;
+      if (!kvalid || qr0 + 31 < kw0) continue;     // queries all before the wave's keys
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        sacc = mfma32(row_op(qc[buf], P, 32 * qt, 16 * c, lane), kr[c], sacc);
+        pacc = mfma32(row_op(dc[buf], P, 32 * qt, 16 * c, lane), vr[c], pacc);
+      }
+      // S: rows are queries qr0 + acc_row, the lane's column the key kcol
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = 32 * qt + acc_row(r, hh);
+        const bool vis = kcol <= qc0 + il;
+        const float p = vis ? exp2_fast(sacc[r] * sl2 - lc[buf][il]) : 0.f;
+        sacc[r] = p;
+        ds[r] = p * ((1.f - g) * pacc[r] - dcr[buf][il]);
+      }
+      const bf16x8 p0 = acc_op(sacc, 0), p1 = acc_op(sacc, 1);
+      const bf16x8 d0 = acc_op(ds, 0), d1 = acc_op(ds, 1);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt, 32 * d, lane), p0, dv[d]);
+        dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt + 16, 32 * d, lane), p1, dv[d]);
+        dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt, 32 * d, lane), d0, dk[d]);
+        dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt + 16, 32 * d, lane), d1, dk[d]);
+      }
+    }
+    if (next) {
+      cp.store(qc[buf ^ 1], dc[buf ^ 1]);
+      if (threadIdx.x < kChunk) {
+        lc[buf ^ 1][threadIdx.x] = nl * kLog2e;
+        dcr[buf ^ 1][threadIdx.x] = nd;
+      }
+    }
+    __syncthreads();
+  }
+  if (kvalid) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = krow * D + 32 * d + acc_row(r, hh);
+        a.dv_acc[i] = (1.f - g) * dv[d][r];
+        a.dk_acc[i] = a.scale * dk[d][r];
+      }
+  }
+}
+
+int bwd_mfma_blocks(int N) { return (N + kBwdBlock - 1) / kBwdBlock; }
+
+template <int D>
+hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
+  hipLaunchKernelGGL(bwd_q_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_kv_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  return hipGetLastError();
+}
+template hipError_t launch_backward_attention_mfma<64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_backward_attention_mfma<128>(const BwdArgs&, hipStream_t);
+
+}  // namespace infini

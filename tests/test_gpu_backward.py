@@ -32,6 +32,8 @@ CASES = [
     ("f32_ragged_resume", 32, 2, 1, 20, 24, 37, 3, "f32", 2),
     ("bf16_d64", 33, 1, 2, 64, 64, 128, 3, "bf16", 0),
     ("bf16_d128_resume", 34, 1, 2, 128, 128, 256, 3, "bf16", 2),
+    # N = 192: the last 128-row block of the MFMA kernels has two idle waves
+    ("bf16_d128_n192", 35, 2, 1, 128, 128, 192, 2, "bf16", 1),
 ]
 
 
