@@ -260,7 +260,7 @@ int zero_state(infini_attn_state* st, float* M, float* z, hipStream_t stream) {
 }
 
 struct BwdLayout {
-  size_t snapM, snapz, dMr, dzr, ez, gzs, lse, drow, erow, rs, dden, de, dq, dk, dv, dfk, dbp, total;
+  size_t snapM, snapz, dMr, dzr, ez, gzs, lse, drow, rs, dden, de, dq, dk, dv, dfk, dbp, total;
 };
 
 bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w) {
@@ -280,7 +280,6 @@ bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w)
   take(&w->gzs, segs * dk);
   take(&w->lse, rows);
   take(&w->drow, rows);
-  take(&w->erow, rows);
   take(&w->rs, rows);
   take(&w->dden, rows);
   take(&w->de, rows);
@@ -476,7 +475,7 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.beta = beta; a.M0 = st->M; a.z0 = st->z; a.dM = dM; a.dz = dz;
   a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dbeta = dbeta; a.dM0 = dM0; a.dz0 = dz0;
   a.snapM = f(w.snapM); a.snapz = f(w.snapz); a.dMr = f(w.dMr); a.dzr = f(w.dzr); a.ez = f(w.ez); a.gzs = f(w.gzs);
-  a.lse = f(w.lse); a.drow = f(w.drow); a.erow = f(w.erow); a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
+  a.lse = f(w.lse); a.drow = f(w.drow); a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
   a.dq_acc = f(w.dq); a.dk_acc = f(w.dk); a.dv_acc = f(w.dv); a.dfk_acc = f(w.dfk); a.dbeta_part = f(w.dbp);
   a.B = st->batch; a.H = st->heads; a.BH = (int)BH; a.N = st->segment_len; a.S = (int)S64;
   a.dk = st->d_key; a.dv = st->d_value; a.nqb = infini::bwd_query_blocks(st->segment_len);

@@ -5,14 +5,20 @@
 // A_mem, 3.5 for the gate, 3.4 and the CSDN page's section 2.1 for the linear and
 // delta updates).  For the loss <dA, A> + <dM, M_S> + <dz, z_S>:
 //
-//   snap        replays the memory updates and keeps every M_{s-1}, z_{s-1} (fp32);
-//   query       per 32 query rows of a segment: the row's softmax statistics and
+//   snap        delta rule: replays the memory updates and keeps every M_{s-1},
+//               z_{s-1} (fp32);
+//   query       (fp32 path) per 32 query rows of a segment: the row's softmax statistics and
 //               A_dot (first sweep over the keys), A_mem, the gate's share of
 //               dbeta, D = <(1 - g) dA, A_dot>, the retrieval's share of dq, then
 //               the local attention's share of dq (second sweep);
-//   key         per 32 keys of a segment: the local attention's dk and dv;
-//   memgrad     per segment: the retrieval's gradient of M_{s-1} and z_{s-1};
-//   chain       per 16 columns of M, segments in reverse: dL/dM_s carried back,
+//   key         (fp32 path) per 32 keys of a segment: the local attention's dk and dv;
+//               the bf16 path runs both on the MFMA units (backward_mfma.hip);
+//   tall        per segment and 32 columns: the retrieval's gradient of M_{s-1}
+//               and z_{s-1}; for the linear rule also the replay's contributions;
+//   scan        linear rule: prefix sums of the contributions (the replay) and
+//               suffix sums of the retrieval gradients (dL/dM_s);
+//   lin_update  linear rule, per 64 tokens: the update's dv and d sigma(K);
+//   chain       delta rule, per 16 columns of M, segments in reverse: dL/dM_s carried back,
 //               the update's dv, its d sigma(K) (atomically summed over the column
 //               blocks) and, for the delta rule, the gradient of each token's
 //               denominator;
@@ -151,10 +157,7 @@ __global__ __launch_bounds__(kThreads) void bwd_snap_kernel(BwdArgs a) {
 
 // ----------------------------------------------------------------- query
 // grid (query blocks of 32, S, BH).  Thread = (row i = t / 8, part p = t % 8).
-// ATT = false (bf16 path): the local attention's share (statistics, A_dot, its
-// dq) has come from the MFMA kernel, which left E = <dA, A_dot> per row and dq
-// in dq_acc; only the retrieval's share is computed and added.
-template <typename T, bool ATT>
+template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H, t = threadIdx.x;
   const int i = t >> 3, p = t & 7;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   float m = -__builtin_inff(), l = 0.f, o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
-  for (int kc = 0; ATT && kc < kend; kc += kKC) {
+  for (int kc = 0; kc < kend; kc += kKC) {
     __syncthreads();
     for (int x = t; x < kKC * 128; x += kThreads) {
       const int r = x >> 7, c = x & 127;
@@ -230,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
       o[e] = acc;
     }
   }
-  const float lse = valid && ATT ? m + __logf(l) : 0.f;
-  const float inv_l = valid && ATT ? 1.f / l : 0.f;
+  const float lse = valid ? m + __logf(l) : 0.f;
+  const float inv_l = valid ? 1.f / l : 0.f;
 
   // retrieval from M_{s-1}, z_{s-1}; the gate; D; the retrieval's dq
   __syncthreads();
@@ -270,9 +273,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
       msum = __builtin_fmaf(d, amem, msum);
     }
   }
-  const float erow = ATT ? row8_sum(dsum) : (valid ? a.erow[seg0 + qi] : 0.f);
-  const float D = (1.f - g) * erow;
-  if (!ATT && p == 0) bsum -= erow;
+  const float D = (1.f - g) * row8_sum(dsum);
   const float rs = has ? g / den : 0.f;
   const float msum_row = row8_sum(msum);
   const float dden = has ? -g * msum_row / den : 0.f;
@@ -284,10 +285,8 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   }
   if (valid && p == 0) {
     const int64_t row = seg0 + qi;
-    if (ATT) {
-      a.lse[row] = lse;
-      a.drow[row] = D;
-    }
+    a.lse[row] = lse;
+    a.drow[row] = D;
     a.rs[row] = rs;
     a.dden[row] = dden;
   }
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
   }
 
   // second sweep: the local attention's dq = scale sum_j dS_ij k_j
-  for (int kc = 0; ATT && kc < kend; kc += kKC) {
+  for (int kc = 0; kc < kend; kc += kKC) {
     __syncthreads();
     for (int x = t; x < kKC * 128; x += kThreads) {
       const int r = x >> 7, c = x & 127;
@@ -350,10 +349,7 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int x = 16 * p + e;
-      if (x < a.dk) {
-        float* dst = a.dq_acc + (seg0 + qi) * a.dk + x;
-        *dst = ATT ? dq[e] : *dst + dq[e];
-      }
+      if (x < a.dk) a.dq_acc[(seg0 + qi) * a.dk + x] = dq[e];
     }
   }
 }
@@ -437,50 +433,6 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(BwdArgs a) {
       if (c < a.dk) a.dk_acc[(seg0 + kj) * a.dk + c] = a.scale * dkv[e];
     }
   }
-}
-
-// --------------------------------------------------------------- memgrad
-// grid (S, BH): dMr_s = sigma(Q)^T (rs * dA), dzr_s = sigma(Q)^T dden.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_memgrad_kernel(BwdArgs a) {
-  const int s = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const T* Q = static_cast<const T*>(a.q);
-  const T* DO = static_cast<const T*>(a.dout);
-  __shared__ float fq[32][kP];
-  __shared__ float w[32][kP];
-  __shared__ float dd[32];
-  const int c = t & 127, ah = t >> 7;
-  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  float acc[64];
-#pragma unroll
-  for (int m = 0; m < 64; ++m) acc[m] = 0.f;
-  float zacc = 0.f;
-  for (int r0 = 0; r0 < a.N; r0 += 32) {
-    __syncthreads();
-    for (int x = t; x < 32 * 128; x += kThreads) {
-      const int r = x >> 7, cc = x & 127;
-      const bool ok = r0 + r < a.N;
-      const int64_t row = seg0 + r0 + r;
-      fq[r][cc] = (ok && cc < a.dk) ? sig(ld(Q, row * a.dk + cc)) : 0.f;
-      w[r][cc] = (ok && cc < a.dv) ? a.rs[row] * ld(DO, row * a.dv + cc) : 0.f;
-    }
-    if (t < 32) dd[t] = r0 + t < a.N ? a.dden[seg0 + r0 + t] : 0.f;
-    __syncthreads();
-    for (int r = 0; r < 32; ++r) {
-      const float wv = w[r][c];
-#pragma unroll
-      for (int m = 0; m < 64; ++m) acc[m] = __builtin_fmaf(fq[r][ah + 2 * m], wv, acc[m]);
-    }
-    if (t < 128)
-      for (int r = 0; r < 32; ++r) zacc = __builtin_fmaf(dd[r], fq[r][t], zacc);
-  }
-  float* out = a.dMr + ((int64_t)bh * a.S + s) * a.dk * a.dv;
-#pragma unroll
-  for (int m = 0; m < 64; ++m) {
-    const int x = ah + 2 * m;
-    if (x < a.dk && c < a.dv) out[(int64_t)x * a.dv + c] = acc[m];
-  }
-  if (t < a.dk) a.dzr[((int64_t)bh * a.S + s) * a.dk + t] = zacc;
 }
 
 // ----------------------------------------------------------------- chain
@@ -623,6 +575,143 @@ __global__ __launch_bounds__(128) void bwd_zchain_kernel(BwdArgs a) {
   if (a.dz0) a.dz0[(int64_t)bh * a.dk + x] = gz;
 }
 
+// ------------------------------------------------------------------ tall
+// grid (column blocks of 32, S, BH).  A per-segment product over the segment's
+// rows, out_s = X^T Y (d_key x d_value, this block's 32 columns) and, from column
+// block 0, the weighted column sums colsum_s = X^T w:
+//   MODE 0 (linear rule, replay): X = sigma(K), Y = V, w = 1; written into the
+//     snapshot buffers as C_s and c_s, then turned into M_{s-1}, z_{s-1} by the
+//     prefix kernel;
+//   MODE 1 (both rules): X = sigma(Q), Y = rs dA, w = dden: the retrieval's
+//     gradient of M_{s-1} and z_{s-1}.
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_tall_kernel(BwdArgs a) {
+  const int cb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, t = threadIdx.x;
+  const T* X = static_cast<const T*>(MODE == 0 ? a.k : a.q);
+  const T* Y = static_cast<const T*>(MODE == 0 ? a.v : a.dout);
+  __shared__ float xs[32][kP];
+  __shared__ float ys[32][33];
+  __shared__ float ws[32];
+  const int c = t & 31, ah = t >> 5, col = cb * 32 + c;
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  float acc[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+  float zacc = 0.f;
+  for (int r0 = 0; r0 < a.N; r0 += 32) {
+    __syncthreads();
+    for (int x = t; x < 32 * 128; x += kThreads) {
+      const int r = x >> 7, cc = x & 127;
+      xs[r][cc] = (r0 + r < a.N && cc < a.dk) ? sig(ld(X, (seg0 + r0 + r) * a.dk + cc)) : 0.f;
+    }
+    for (int x = t; x < 32 * 32; x += kThreads) {
+      const int r = x >> 5, cc = x & 31, cl = cb * 32 + cc;
+      const int64_t row = seg0 + r0 + r;
+      float y = 0.f;
+      if (r0 + r < a.N && cl < a.dv) y = MODE == 0 ? ld(Y, row * a.dv + cl) : a.rs[row] * ld(Y, row * a.dv + cl);
+      ys[r][cc] = y;
+    }
+    if (t < 32) ws[t] = r0 + t < a.N ? (MODE == 0 ? 1.f : a.dden[seg0 + r0 + t]) : 0.f;
+    __syncthreads();
+#pragma unroll 2
+    for (int r = 0; r < 32; ++r) {
+      const float yv = ys[r][c];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) acc[m] = __builtin_fmaf(xs[r][ah + 8 * m], yv, acc[m]);
+    }
+    if (cb == 0 && t < 128)
+      for (int r = 0; r < 32; ++r) zacc = __builtin_fmaf(ws[r], xs[r][t], zacc);
+  }
+  float* out = (MODE == 0 ? a.snapM : a.dMr) + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int x = ah + 8 * m;
+    if (x < a.dk && col < a.dv) out[(int64_t)x * a.dv + col] = acc[m];
+  }
+  if (cb == 0 && t < a.dk) (MODE == 0 ? a.snapz : a.dzr)[((int64_t)bh * a.S + s) * a.dk + t] = zacc;
+}
+
+// ----------------------------------------------------------------- scans
+// One thread per element of M (and of z): REVERSE = false turns the
+// contributions C_s, c_s in snapM / snapz into M_{s-1} = M_0 + sum_{s' < s} C_s'
+// (z likewise); REVERSE = true turns the retrieval gradients dMr_s into
+// dL/dM_s = dM + sum_{s' > s} dMr_s' and writes dL/dM_0 to dM0.
+template <bool REVERSE>
+__global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs a) {
+  const int64_t per = (int64_t)a.dk * a.dv + (REVERSE ? 0 : a.dk);
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)a.BH * per) return;
+  const int bh = (int)(i / per);
+  const int64_t e = i % per;
+  const bool isz = e >= (int64_t)a.dk * a.dv;
+  const int64_t ez = e - (int64_t)a.dk * a.dv;
+  float* base = REVERSE ? a.dMr : (isz ? a.snapz : a.snapM);
+  const int64_t stride = isz ? a.dk : (int64_t)a.dk * a.dv;
+  const int64_t off = (int64_t)bh * a.S * stride + (isz ? ez : e);
+  float run;
+  if (REVERSE) run = a.dM ? a.dM[(int64_t)bh * a.dk * a.dv + e] : 0.f;
+  else run = isz ? a.z0[(int64_t)bh * a.dk + ez] : a.M0[(int64_t)bh * a.dk * a.dv + e];
+  if (REVERSE) {
+    for (int s = a.S - 1; s >= 0; --s) {
+      float* p = base + off + (int64_t)s * stride;
+      const float c = *p;
+      *p = run;
+      run += c;
+    }
+    if (a.dM0) a.dM0[(int64_t)bh * a.dk * a.dv + e] = run;
+  } else {
+    for (int s = 0; s < a.S; ++s) {
+      float* p = base + off + (int64_t)s * stride;
+      const float c = *p;
+      *p = run;
+      run += c;
+    }
+  }
+}
+
+// ------------------------------------------------------------ lin_update
+// grid (blocks of 64 tokens, S, BH).  Linear rule, given G = dL/dM_s (in dMr
+// after the reverse scan): dv += sigma(K) G and d sigma(K) = V G^T (the z share
+// is added by the finish kernel).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_lin_update_kernel(BwdArgs a) {
+  const int rb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, t = threadIdx.x;
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  __shared__ float G[128 * kP];
+  __shared__ float fk[kTok][kP];
+  __shared__ float vs[kTok][kP];
+  const int64_t row0 = (int64_t)bh * a.L + (int64_t)s * a.N + (int64_t)rb * kTok;
+  const int nrow = min(kTok, a.N - rb * kTok);
+  const float* Gg = a.dMr + ((int64_t)bh * a.S + s) * a.dk * a.dv;
+  for (int x = t; x < a.dk * a.dv; x += kThreads) G[(x / a.dv) * kP + x % a.dv] = Gg[x];
+  for (int x = t; x < kTok * 128; x += kThreads) {
+    const int r = x >> 7, c = x & 127;
+    fk[r][c] = (r < nrow && c < a.dk) ? sig(ld(K, (row0 + r) * a.dk + c)) : 0.f;
+    vs[r][c] = (r < nrow && c < a.dv) ? ld(V, (row0 + r) * a.dv + c) : 0.f;
+  }
+  __syncthreads();
+  const int c = t & 127, rh = t >> 7;
+  if (c < a.dv) {
+    for (int m = 0; m < kTok / 2; ++m) {
+      const int r = rh + 2 * m;
+      if (r >= nrow) break;
+      float acc = 0.f;
+      for (int x = 0; x < a.dk; ++x) acc = __builtin_fmaf(fk[r][x], G[x * kP + c], acc);
+      a.dv_acc[(row0 + r) * a.dv + c] += acc;
+    }
+  }
+  if (c < a.dk) {
+    for (int m = 0; m < kTok / 2; ++m) {
+      const int r = rh + 2 * m;
+      if (r >= nrow) break;
+      float acc = 0.f;
+      for (int y = 0; y < a.dv; ++y) acc = __builtin_fmaf(vs[r][y], G[c * kP + y], acc);
+      a.dfk_acc[(row0 + r) * a.dk + c] = acc;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- finish
 // grid (ceil(BH * L / 2)), 256 threads: two rows per workgroup.
 template <typename T>
@@ -682,23 +771,36 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     hipLaunchKernelGGL(__VA_ARGS__);              \
     if ((e = hipGetLastError()) != hipSuccess) return e; \
   } while (0)
-  INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+  const unsigned ncb32 = (unsigned)((a.dv + 31) / 32);
+  if (a.delta) {
+    INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+  } else {
+    INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 0>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
+    const int64_t n = (int64_t)a.BH * ((int64_t)a.dk * a.dv + a.dk);
+    INFINI_BWD_LAUNCH(bwd_scan_kernel<false>, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                      stream, a);
+  }
   if (mfma) {
     e = a.dk == 128 ? launch_backward_attention_mfma<128>(a, stream) : launch_backward_attention_mfma<64>(a, stream);
     if (e != hipSuccess) return e;
-    INFINI_BWD_LAUNCH((bwd_query_kernel<T, false>), dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
   } else {
-    INFINI_BWD_LAUNCH((bwd_query_kernel<T, true>), dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
+    INFINI_BWD_LAUNCH(bwd_query_kernel<T>, dim3((unsigned)a.nqb, S, BH), dim3(kThreads), 0, stream, a);
     INFINI_BWD_LAUNCH(bwd_key_kernel<T>, dim3((unsigned)((a.N + kKB - 1) / kKB), S, BH), dim3(kThreads), 0, stream,
                       a);
   }
-  INFINI_BWD_LAUNCH(bwd_memgrad_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
-  {
+  INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 1>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
+  if (a.delta) {
     const int64_t n1 = (int64_t)a.BH * a.L * a.dk, n2 = (int64_t)a.BH * a.L;
     const int64_t blocks = std::min<int64_t>((n1 + n2 + kThreads - 1) / kThreads, 65536);
     INFINI_BWD_LAUNCH(bwd_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a.dfk_acc, n1, a.de, n2);
+    INFINI_BWD_LAUNCH(bwd_chain_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+  } else {
+    const int64_t n = (int64_t)a.BH * a.dk * a.dv;
+    INFINI_BWD_LAUNCH(bwd_scan_kernel<true>, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                      stream, a);
+    INFINI_BWD_LAUNCH(bwd_lin_update_kernel<T>, dim3((unsigned)((a.N + kTok - 1) / kTok), S, BH), dim3(kThreads), 0,
+                      stream, a);
   }
-  INFINI_BWD_LAUNCH(bwd_chain_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
   INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(128), 0, stream, a);
   INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
   INFINI_BWD_LAUNCH(bwd_finish_kernel<T>, dim3((unsigned)(((int64_t)a.BH * a.L + 1) / 2)), dim3(kThreads), 0, stream,

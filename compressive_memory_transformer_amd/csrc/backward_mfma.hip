@@ -5,7 +5,11 @@
 //   bwd_q_mfma_kernel<D>: one workgroup (4 waves) per 128 query rows of a
 //     segment, one wave per 32 rows.  First sweep over the keys: the row's
 //     softmax maximum and sum, A_dot, then E = <dA, A_dot> and D = (1 - g) E.
-//     Second sweep: dS = P ((1 - g) dP - D) and dq += scale dS K.  Scores are
+//     The retrieval (section 3.3) from M_{s-1} staged in LDS as bf16:
+//     A_mem = (colsum(M) + (sigma(q) - 1) M) / (sigma(q) z) (the column sums in
+//     fp32 keep sigma(q) ~ 1 from costing bf16 precision), the gate's share of
+//     dbeta, rs = g / den and dden.  Second sweep: dS = P ((1 - g) dP - D) and
+//     dq += scale dS K; then the retrieval's dq = (M (rs dA) + dden z) sigma'(q).  Scores are
 //     computed transposed (keys x queries), so every register operand is already
 //     in the accumulator layout of the product that consumes it.
 //   bwd_kv_mfma_kernel<D>: one workgroup per 128 keys, one wave per 32 keys,
@@ -39,6 +43,13 @@ __device__ __forceinline__ bf16x8 row_op(const bf16* X, int pitch, int r0, int k
 __device__ __forceinline__ bf16x8 tr_op(const bf16* X, int pitch, int r0, int c0, int lane) {
   const int h = lane >> 5, g = (lane >> 4) & 3, s = lane & 15;
   return lds_operand_tr(X, pitch, r0 + 4 * h, r0 + 8 + 4 * h, c0 + 16 * (g & 1), s);
+}
+
+// Transposed operand in natural contraction order (for a B operand loaded by
+// rows): lane l gets X[r0 + 8 h + e][c0 + l % 32], e = 0..7.
+__device__ __forceinline__ bf16x8 tr_nat(const bf16* X, int pitch, int r0, int c0, int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 3, s = lane & 15;
+  return lds_operand_tr(X, pitch, r0 + 8 * h, r0 + 8 * h + 4, c0 + 16 * (g & 1), s);
 }
 
 // Accumulator rows 8 ks .. 8 ks + 7 of `c` as a bf16 B operand.
@@ -97,8 +108,11 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   const bf16* DO = static_cast<const bf16*>(a.dout);
   __shared__ __attribute__((aligned(16))) bf16 kc[2][kChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 vc[2][kChunk * P];
+  __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
+  __shared__ float msum[D], zsh[D];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int q0 = qb * kBwdBlock, qw0 = q0 + 32 * w;
+  const bool has_mem = a.seg_base + s > 0;
   const bool qvalid = qw0 < a.N;
   const int qcol = qw0 + l32;                      // this lane's query (column of S^T)
   const int64_t qrow = seg0 + min(qcol, a.N - 1);
@@ -111,6 +125,16 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
     dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
   }
   const int kend = min(a.N, q0 + kBwdBlock);
+  {
+    const float* Mg = a.snapM + ((int64_t)bh * a.S + s) * D * D;
+    for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) ms[(x / D) * P + x % D] = f2bf(Mg[x]);
+    if (threadIdx.x < D) {
+      float cs = 0.f;
+      for (int r = 0; r < D; ++r) cs += Mg[r * D + threadIdx.x];
+      msum[threadIdx.x] = cs;
+      zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
+    }
+  }
 
   // ---- first sweep: maximum, sum and A_dot^T of the wave's 32 query columns
   f32x16 o[DB];
@@ -166,18 +190,54 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   const float lt = l + __shfl_xor(l, 32);
   const float lse2 = m2 + log2f(lt);
   const float inv_l = 1.f / lt;
-  // E = <dA, A_dot> of the lane's query: the lane holds 16 DB values of A_dot^T
-  float e = 0.f;
+  // A_mem^T = (colsum(M) + M^T (sigma(q) - 1)^T) / den for the lane's query
+  bf16x8 qm[KS];
+  float den = 0.f;
 #pragma unroll
-  for (int d = 0; d < DB; ++d)
+  for (int c = 0; c < KS; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e = __builtin_fmaf(bf2f(DO[qrow * D + 32 * d + acc_row(r, hh)]), o[d][r], e);
+    for (int j = 0; j < 8; ++j) {
+      const float x = bf2f(qr[c][j]);
+      const float f = x > 0.f ? x : exp_e(x) - 1.f;
+      qm[c][j] = f2bf(f);
+      den = __builtin_fmaf(f + 1.f, zsh[16 * c + 8 * hh + j], den);
+    }
+  den += __shfl_xor(den, 32);
+  const bool has = has_mem && den > 0.f;
+  const float inv_den = has ? 1.f / den : 0.f;
+  // E = <dA, A_dot> and <dA, A_mem> of the lane's query: the lane holds 16 DB
+  // values of each transposed row
+  float e = 0.f, em = 0.f;
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    f32x16 am = zero16();
+    if (has_mem) {
+#pragma unroll
+      for (int c = 0; c < KS; ++c) am = mfma32(tr_nat(ms, P, 16 * c, 32 * d, lane), qm[c], am);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int col = 32 * d + acc_row(r, hh);
+      const float da = bf2f(DO[qrow * D + col]);
+      e = __builtin_fmaf(da, o[d][r], e);
+      em = __builtin_fmaf(da, (msum[col] + am[r]) * inv_den, em);
+    }
+  }
   e = (e + __shfl_xor(e, 32)) * inv_l;
+  em += __shfl_xor(em, 32);
   const float Dv = (1.f - g) * e;
+  const float rs = g * inv_den;
+  const float dden = -g * em * inv_den;
   if (qvalid && hh == 0) {
     a.lse[qrow] = lse2 * (1.f / kLog2e);
     a.drow[qrow] = Dv;
-    a.erow[qrow] = e;
+    a.rs[qrow] = rs;
+    a.dden[qrow] = dden;
+  }
+  // the gate's share of dbeta for the wave's 32 queries: g (1 - g) sum (<dA, A_mem> - E)
+  {
+    const float bt = wave_sum(qvalid && hh == 0 ? em - e : 0.f);
+    if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] = bt * g * (1.f - g);
   }
 
   // ---- second sweep: dq^T += K^T dS^T
@@ -216,11 +276,29 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
     if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
     __syncthreads();
   }
+  // the retrieval's dq^T = (M (rs dA)^T + dden z) sigma'(q): M rows from LDS,
+  // rs dA as the B operand from the dA rows already in registers
+  bf16x8 dn[KS];
+#pragma unroll
+  for (int c = 0; c < KS; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dn[c][j] = f2bf(rs * bf2f(dr[c][j]));
   if (qvalid) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+    for (int d = 0; d < DB; ++d) {
+      f32x16 dm = zero16();
+      if (has_mem) {   // wave-uniform; rows without memory have rs = dden = 0
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a.dq_acc[qrow * D + 32 * d + acc_row(r, hh)] = a.scale * dq[d][r];
+        for (int c = 0; c < KS; ++c) dm = mfma32(row_op(ms, P, 32 * d, 16 * c, lane), dn[c], dm);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = 32 * d + acc_row(r, hh);
+        const float x = bf2f(Q[qrow * D + col]);
+        const float sp = x > 0.f ? 1.f : exp_e(x);
+        a.dq_acc[qrow * D + col] = __builtin_fmaf(a.scale, dq[d][r], (dm[r] + dden * zsh[col]) * sp);
+      }
+    }
   }
 }
 

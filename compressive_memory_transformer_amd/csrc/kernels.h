@@ -168,7 +168,6 @@ struct BwdArgs {
   float* gzs;            // [BH*S][dk] dL/dz_s
   float* lse;            // [BH*L] softmax log-normaliser of each row
   float* drow;           // [BH*L] <(1 - g) dA, A_dot>
-  float* erow;           // [BH*L] <dA, A_dot> (bf16 path: from the MFMA kernel to the retrieval kernel)
   float* rs;             // [BH*L] g / den (0 without memory)
   float* dden;           // [BH*L]
   float* de;             // [BH*L] delta rule: gradient of sigma(K_t) . z_{s-1}
@@ -185,8 +184,9 @@ struct BwdArgs {
 hipError_t launch_backward(const BwdArgs& a, bool bf16_io, hipStream_t stream);
 // Query blocks per segment of the backward (the dbeta_part width).
 int bwd_query_blocks(int N);
-// bf16 path: the local attention's dq (with the softmax statistics, D and E of
-// every row) and dk, dv on the MFMA units; N a multiple of 64.
+// bf16 path: the local attention's and the retrieval's dq (with the softmax
+// statistics, D, rs, dden of every row and the dbeta shares) and the local
+// attention's dk, dv on the MFMA units; N a multiple of 64.
 template <int D> hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream);
 
 // Zero n floats at p and n2 floats at p2 (one launch).
