@@ -634,9 +634,10 @@ __global__ __launch_bounds__(kThreads) void bwd_tall_kernel(BwdArgs a) {
 // ----------------------------------------------------------------- scans
 // One thread per element of M (and of z): REVERSE = false turns the
 // contributions C_s, c_s in snapM / snapz into M_{s-1} = M_0 + sum_{s' < s} C_s'
-// (z likewise); REVERSE = true turns the retrieval gradients dMr_s into
-// dL/dM_s = dM + sum_{s' > s} dMr_s' and writes dL/dM_0 to dM0.
-template <bool REVERSE>
+// (z likewise; with FROM_T the contributions C_s^T come from dMr, the layout
+// of the MFMA contribution kernel); REVERSE = true turns the retrieval
+// gradients dMr_s into dL/dM_s = dM + sum_{s' > s} dMr_s' and writes dL/dM_0.
+template <bool REVERSE, bool FROM_T>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs a) {
   const int64_t per = (int64_t)a.dk * a.dv + (REVERSE ? 0 : a.dk);
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -660,9 +661,11 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs a) {
     }
     if (a.dM0) a.dM0[(int64_t)bh * a.dk * a.dv + e] = run;
   } else {
+    // element (x, y) of M reads C_s^T[y][x] when the contributions are transposed
+    const int64_t et = isz ? 0 : (e % a.dv) * a.dk + e / a.dv;
     for (int s = 0; s < a.S; ++s) {
       float* p = base + off + (int64_t)s * stride;
-      const float c = *p;
+      const float c = (FROM_T && !isz) ? a.dMr[((int64_t)bh * a.S + s) * stride + et] : *p;
       *p = run;
       run += c;
     }
@@ -775,10 +778,20 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
   if (a.delta) {
     INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
   } else {
-    INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 0>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
     const int64_t n = (int64_t)a.BH * ((int64_t)a.dk * a.dv + a.dk);
-    INFINI_BWD_LAUNCH(bwd_scan_kernel<false>, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                      stream, a);
+    const dim3 sg((unsigned)((n + kThreads - 1) / kThreads));
+    if (mfma) {
+      // the forward's MFMA contribution kernel: C_s^T into dMr (free until the
+      // retrieval gradients), c_s into snapz
+      const LinContribArgs lc{static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v), a.dMr, a.snapz,
+                              a.B, a.H, a.S, a.N, a.L};
+      e = a.dk == 128 ? launch_lin_contrib<128>(lc, stream) : launch_lin_contrib<64>(lc, stream);
+      if (e != hipSuccess) return e;
+      INFINI_BWD_LAUNCH((bwd_scan_kernel<false, true>), sg, dim3(kThreads), 0, stream, a);
+    } else {
+      INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 0>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
+      INFINI_BWD_LAUNCH((bwd_scan_kernel<false, false>), sg, dim3(kThreads), 0, stream, a);
+    }
   }
   if (mfma) {
     e = a.dk == 128 ? launch_backward_attention_mfma<128>(a, stream) : launch_backward_attention_mfma<64>(a, stream);
@@ -796,10 +809,15 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     INFINI_BWD_LAUNCH(bwd_chain_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
   } else {
     const int64_t n = (int64_t)a.BH * a.dk * a.dv;
-    INFINI_BWD_LAUNCH(bwd_scan_kernel<true>, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                      stream, a);
-    INFINI_BWD_LAUNCH(bwd_lin_update_kernel<T>, dim3((unsigned)((a.N + kTok - 1) / kTok), S, BH), dim3(kThreads), 0,
-                      stream, a);
+    INFINI_BWD_LAUNCH((bwd_scan_kernel<true, false>), dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                      dim3(kThreads), 0, stream, a);
+    if (mfma) {
+      e = a.dk == 128 ? launch_backward_lin_update_mfma<128>(a, stream) : launch_backward_lin_update_mfma<64>(a, stream);
+      if (e != hipSuccess) return e;
+    } else {
+      INFINI_BWD_LAUNCH(bwd_lin_update_kernel<T>, dim3((unsigned)((a.N + kTok - 1) / kTok), S, BH), dim3(kThreads),
+                        0, stream, a);
+    }
   }
   INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(128), 0, stream, a);
   INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);

@@ -400,6 +400,60 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) 
   }
 }
 
+// Linear rule, per 128 tokens of a segment (one wave per 32), given G = dL/dM_s
+// (fp32 [d_key][d_value], staged in LDS as bf16 with fp32 column sums):
+//   dv += sigma(K) G = colsum(G) + (sigma(K) - 1) G;   d sigma(K) = V G^T.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(BwdArgs a) {
+  constexpr int P = D + 8, KS = D / 16, DB = D / 32;
+  const int rb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  const bf16* K = static_cast<const bf16*>(a.k);
+  const bf16* V = static_cast<const bf16*>(a.v);
+  __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
+  __shared__ float gsum[D];
+  const float* Gg = a.dMr + ((int64_t)bh * a.S + s) * D * D;
+  for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) gs[(x / D) * P + x % D] = f2bf(Gg[x]);
+  if (threadIdx.x < D) {
+    float cs = 0.f;
+    for (int r = 0; r < D; ++r) cs += Gg[r * D + threadIdx.x];
+    gsum[threadIdx.x] = cs;
+  }
+  const int t0 = rb * kBwdBlock + 32 * w;           // the wave's first token in the segment
+  const bool valid = t0 < a.N;
+  const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
+  bf16x8 kp[KS], vr[KS];
+#pragma unroll
+  for (int c = 0; c < KS; ++c) {
+    const bf16x8 kx = *reinterpret_cast<const bf16x8*>(K + row * D + 16 * c + 8 * hh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = bf2f(kx[j]);
+      kp[c][j] = f2bf(x > 0.f ? x : exp_e(x) - 1.f);
+    }
+    vr[c] = *reinterpret_cast<const bf16x8*>(V + row * D + 16 * c + 8 * hh);
+  }
+  __syncthreads();
+  if (!valid) return;
+  const int64_t out0 = (int64_t)bh * a.L + (int64_t)s * a.N + t0;
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    f32x16 dv = zero16(), df = zero16();
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      dv = mfma32(kp[c], tr_nat(gs, P, 16 * c, 32 * d, lane), dv);
+      df = mfma32(vr[c], row_op(gs, P, 32 * d, 16 * c, lane), df);
+    }
+    const int col = 32 * d + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = (out0 + acc_row(r, hh)) * D + col;
+      a.dv_acc[i] += gsum[col] + dv[r];
+      a.dfk_acc[i] = df[r];
+    }
+  }
+}
+
 int bwd_mfma_blocks(int N) { return (N + kBwdBlock - 1) / kBwdBlock; }
 
 template <int D>
@@ -413,5 +467,14 @@ hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) 
 }
 template hipError_t launch_backward_attention_mfma<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_attention_mfma<128>(const BwdArgs&, hipStream_t);
+
+template <int D>
+hipError_t launch_backward_lin_update_mfma(const BwdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
+  hipLaunchKernelGGL(bwd_lin_update_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  return hipGetLastError();
+}
+template hipError_t launch_backward_lin_update_mfma<64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_backward_lin_update_mfma<128>(const BwdArgs&, hipStream_t);
 
 }  // namespace infini

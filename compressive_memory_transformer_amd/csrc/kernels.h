@@ -188,6 +188,8 @@ int bwd_query_blocks(int N);
 // statistics, D, rs, dden of every row and the dbeta shares) and the local
 // attention's dk, dv on the MFMA units; N a multiple of 64.
 template <int D> hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream);
+// bf16 path, linear rule: the update's dv and d sigma(K) on the MFMA units.
+template <int D> hipError_t launch_backward_lin_update_mfma(const BwdArgs& a, hipStream_t stream);
 
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);
