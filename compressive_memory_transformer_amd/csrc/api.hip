@@ -260,7 +260,7 @@ int zero_state(infini_attn_state* st, float* M, float* z, hipStream_t stream) {
 }
 
 struct BwdLayout {
-  size_t snapM, snapz, dMr, dzr, ez, gzs, lse, drow, rs, dden, de, dq, dk, dv, dfk, dbp, total;
+  size_t snapM, snapz, dMr, dzr, ez, gzs, lse, drow, rs, dden, de, dq, dk, dv, dfk, dbp, amat, total;
 };
 
 bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w) {
@@ -288,6 +288,9 @@ bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w)
   take(&w->dv, rv);
   take(&w->dfk, rk);
   take(&w->dbp, nb);
+  // delta rule on the bf16 path: sigma(K)^T diag(1/e) sigma(K) per segment
+  const bool amat = st->rule == INFINI_RULE_DELTA && st->dtype == INFINI_BF16;
+  take(&w->amat, amat ? segs * dk * dk : 0);
   w->total = off;
   return true;
 }
@@ -477,6 +480,7 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   a.snapM = f(w.snapM); a.snapz = f(w.snapz); a.dMr = f(w.dMr); a.dzr = f(w.dzr); a.ez = f(w.ez); a.gzs = f(w.gzs);
   a.lse = f(w.lse); a.drow = f(w.drow); a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
   a.dq_acc = f(w.dq); a.dk_acc = f(w.dk); a.dv_acc = f(w.dv); a.dfk_acc = f(w.dfk); a.dbeta_part = f(w.dbp);
+  a.Amat = f(w.amat);
   a.B = st->batch; a.H = st->heads; a.BH = (int)BH; a.N = st->segment_len; a.S = (int)S64;
   a.dk = st->d_key; a.dv = st->d_value; a.nqb = infini::bwd_query_blocks(st->segment_len);
   a.L = seq_len; a.seg_base = st->segments_done; a.delta = st->rule == INFINI_RULE_DELTA; a.scale = st->scale;

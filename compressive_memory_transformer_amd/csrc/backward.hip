@@ -5,8 +5,8 @@
 // A_mem, 3.5 for the gate, 3.4 and the CSDN page's section 2.1 for the linear and
 // delta updates).  For the loss <dA, A> + <dM, M_S> + <dz, z_S>:
 //
-//   snap        delta rule: replays the memory updates and keeps every M_{s-1},
-//               z_{s-1} (fp32);
+//   snap        delta rule, fp32 path: replays the memory updates and keeps every
+//               M_{s-1}, z_{s-1} (fp32);
 //   query       (fp32 path) per 32 query rows of a segment: the row's softmax statistics and
 //               A_dot (first sweep over the keys), A_mem, the gate's share of
 //               dbeta, D = <(1 - g) dA, A_dot>, the retrieval's share of dq, then
@@ -18,7 +18,9 @@
 //   scan        linear rule: prefix sums of the contributions (the replay) and
 //               suffix sums of the retrieval gradients (dL/dM_s);
 //   lin_update  linear rule, per 64 tokens: the update's dv and d sigma(K);
-//   chain       delta rule, per 16 columns of M, segments in reverse: dL/dM_s carried back,
+//   delta_chain delta rule, bf16 path: the replay and the backward carry of dL/dM_s
+//               as d x d x 16 products with A_s (the per-token work on MFMA);
+//   chain       delta rule, fp32 path, per 16 columns of M, segments in reverse: dL/dM_s carried back,
 //               the update's dv, its d sigma(K) (atomically summed over the column
 //               blocks) and, for the delta rule, the gradient of each token's
 //               denominator;
@@ -715,6 +717,92 @@ __global__ __launch_bounds__(kThreads) void bwd_lin_update_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------- delta, bf16 path
+// With A_s = sigma(K)^T diag(1 / e) sigma(K) (e_t = sigma(K_t) . z_{s-1}; A_s = 0
+// in a stream's first segment), the delta update is M_s = (I - A_s) M_{s-1} + C_s
+// (C_s = sigma(K)^T V) and its gradient dL/dM_{s-1} = (I - A_s) dL/dM_s + dMr_s
+// (A_s is symmetric).  A_s and C_s come from parallel kernels; the two chains
+// below carry only a d_key x d_key x 16 product per segment.
+// grid (column blocks of 16, BH).  FWD: M_{s-1} snapshots from C_s^T (in dMr).
+// !FWD: dMr_s replaced by dL/dM_s, dL/dM_0 to dM0.
+template <bool FWD>
+__global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
+  const int cb = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  __shared__ float As[128][kP];
+  __shared__ float Xs[128][kColB + 1];
+  const int D = a.dk;
+  for (int i = t; i < 128 * kColB; i += kThreads) {
+    const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+    float x = 0.f;
+    if (r < D && col < a.dv) {
+      const int64_t m = ((int64_t)bh * D + r) * a.dv + col;
+      x = FWD ? a.M0[m] : (a.dM ? a.dM[m] : 0.f);
+    }
+    Xs[r][c] = x;
+  }
+  for (int k = 0; k < a.S; ++k) {
+    const int s = FWD ? k : a.S - 1 - k;
+    const bool first = is_first(a, s);
+    const int64_t seg = (int64_t)bh * a.S + s;
+    __syncthreads();
+    if (!first)
+      for (int i = t; i < D * D; i += kThreads) As[i / D][i % D] = a.Amat[seg * D * D + i];
+    float add[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = t + kThreads * r, x = i / kColB, c = i % kColB, col = cb * kColB + c;
+      add[r] = 0.f;
+      if (x < D && col < a.dv) {
+        if (FWD) {
+          add[r] = a.dMr[seg * D * a.dv + (int64_t)col * D + x];   // C_s^T[col][x]
+          a.snapM[seg * D * a.dv + (int64_t)x * a.dv + col] = Xs[x][c];
+        } else {
+          float* p = a.dMr + seg * D * a.dv + (int64_t)x * a.dv + col;
+          add[r] = *p;
+          *p = Xs[x][c];
+        }
+      }
+    }
+    __syncthreads();
+    float nx[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = t + kThreads * r, x = i / kColB, c = i % kColB;
+      float acc = 0.f;
+      if (!first && x < D)
+        for (int y = 0; y < D; ++y) acc = __builtin_fmaf(As[x][y], Xs[y][c], acc);
+      nx[r] = Xs[x][c] - acc + add[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = t + kThreads * r;
+      Xs[i / kColB][i % kColB] = nx[r];
+    }
+  }
+  __syncthreads();
+  if (!FWD && a.dM0)
+    for (int i = t; i < D * kColB; i += kThreads) {
+      const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+      if (col < a.dv) a.dM0[((int64_t)bh * D + r) * a.dv + col] = Xs[r][c];
+    }
+}
+
+// z_{s-1} = z_0 + sum_{s' < s} c_s' in place in snapz (c_s from the contribution
+// kernel), one thread per (head, d_key).
+__global__ __launch_bounds__(kThreads) void bwd_zscan_kernel(BwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)a.BH * a.dk) return;
+  const int bh = (int)(i / a.dk), x = (int)(i % a.dk);
+  float run = a.z0[i];
+  for (int s = 0; s < a.S; ++s) {
+    float* p = a.snapz + ((int64_t)bh * a.S + s) * a.dk + x;
+    const float c = *p;
+    *p = run;
+    run += c;
+  }
+}
+
 // ---------------------------------------------------------------- finish
 // grid (ceil(BH * L / 2)), 256 threads: two rows per workgroup.
 template <typename T>
@@ -775,7 +863,8 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e; \
   } while (0)
   const unsigned ncb32 = (unsigned)((a.dv + 31) / 32);
-  if (a.delta) {
+  const bool delta_mfma = mfma && a.delta;
+  if (a.delta && !mfma) {
     INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
   } else {
     const int64_t n = (int64_t)a.BH * ((int64_t)a.dk * a.dv + a.dk);
@@ -787,7 +876,17 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
                               a.B, a.H, a.S, a.N, a.L};
       e = a.dk == 128 ? launch_lin_contrib<128>(lc, stream) : launch_lin_contrib<64>(lc, stream);
       if (e != hipSuccess) return e;
-      INFINI_BWD_LAUNCH((bwd_scan_kernel<false, true>), sg, dim3(kThreads), 0, stream, a);
+      if (delta_mfma) {
+        const int64_t nz = (int64_t)a.BH * a.dk;
+        INFINI_BWD_LAUNCH(bwd_zscan_kernel, dim3((unsigned)((nz + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                          stream, a);
+        e = a.dk == 128 ? launch_backward_delta_amat_mfma<128>(a, stream)
+                        : launch_backward_delta_amat_mfma<64>(a, stream);
+        if (e != hipSuccess) return e;
+        INFINI_BWD_LAUNCH(bwd_delta_chain_kernel<true>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+      } else {
+        INFINI_BWD_LAUNCH((bwd_scan_kernel<false, true>), sg, dim3(kThreads), 0, stream, a);
+      }
     } else {
       INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 0>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
       INFINI_BWD_LAUNCH((bwd_scan_kernel<false, false>), sg, dim3(kThreads), 0, stream, a);
@@ -802,7 +901,12 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
                       a);
   }
   INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 1>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
-  if (a.delta) {
+  if (delta_mfma) {
+    INFINI_BWD_LAUNCH(bwd_delta_chain_kernel<false>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+    e = a.dk == 128 ? launch_backward_delta_update_mfma<128>(a, stream)
+                    : launch_backward_delta_update_mfma<64>(a, stream);
+    if (e != hipSuccess) return e;
+  } else if (a.delta) {
     const int64_t n1 = (int64_t)a.BH * a.L * a.dk, n2 = (int64_t)a.BH * a.L;
     const int64_t blocks = std::min<int64_t>((n1 + n2 + kThreads - 1) / kThreads, 65536);
     INFINI_BWD_LAUNCH(bwd_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a.dfk_acc, n1, a.de, n2);

@@ -454,6 +454,214 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(Bwd
   }
 }
 
+// Delta rule: A_s = sigma(K)^T diag(w) sigma(K), w_t = 1 / (sigma(K_t) . z_{s-1})
+// (0 in a stream's first segment), one workgroup per segment.  With
+// sigma(K) = 1 + K' (K' = sigma(K) - 1, rounded to bf16 for the products):
+//   A_s = (sum w) 1 1^T + 1 u^T + u 1^T + K'^T diag(w) K',  u = K'^T w,
+// the rank-one terms in fp32 and the last product on MFMA (both operands read
+// transposed from LDS, 64 tokens per step).
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_amat_kernel(BwdArgs a) {
+  constexpr int P = D + 8, NT = D / 32;   // NT x NT output tiles, NT * NT / 4 per wave
+  const int s = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const bf16* K = static_cast<const bf16*>(a.k);
+  __shared__ __attribute__((aligned(16))) bf16 kps[kChunk * P];
+  __shared__ __attribute__((aligned(16))) bf16 wks[kChunk * P];
+  __shared__ float zsh[D], ush[D], wsh[kChunk];
+  float* out = a.Amat + ((int64_t)bh * a.S + s) * D * D;
+  if (a.seg_base + s == 0) {
+    for (int i = t; i < D * D; i += 64 * kBwdWaves) out[i] = 0.f;
+    return;
+  }
+  if (t < D) {
+    zsh[t] = a.snapz[((int64_t)bh * a.S + s) * D + t];
+    ush[t] = 0.f;
+  }
+  constexpr int TPW = NT * NT / kBwdWaves > 0 ? NT * NT / kBwdWaves : 1;   // tiles per wave
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = zero16();
+  float wsum = 0.f, upart = 0.f;
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  // thread -> (token tt = t / 4, quarter of the row qq = t % 4)
+  const int tt = t >> 2, qq = t & 3;
+  constexpr int QW = D / 4;   // columns per thread
+  __syncthreads();
+  for (int t0 = 0; t0 < a.N; t0 += kChunk) {
+    float kv[QW];
+    float e = 0.f;
+#pragma unroll
+    for (int i = 0; i < QW / 8; ++i) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(K + (seg0 + t0 + tt) * D + qq * QW + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = bf2f(x[j]);
+        const float f = v > 0.f ? v : exp_e(v) - 1.f;
+        kv[8 * i + j] = f;
+        e = __builtin_fmaf(f + 1.f, zsh[qq * QW + 8 * i + j], e);
+      }
+    }
+    e += __shfl_xor(e, 1);
+    e += __shfl_xor(e, 2);
+    const float wt = e > 0.f ? 1.f / e : 0.f;
+#pragma unroll
+    for (int i = 0; i < QW / 8; ++i) {
+      bf16x8 kb, wb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kb[j] = f2bf(kv[8 * i + j]);
+        wb[j] = f2bf(wt * kv[8 * i + j]);
+      }
+      *reinterpret_cast<bf16x8*>(kps + tt * P + qq * QW + 8 * i) = kb;
+      *reinterpret_cast<bf16x8*>(wks + tt * P + qq * QW + 8 * i) = wb;
+    }
+    if (qq == 0) wsh[tt] = wt;
+    __syncthreads();
+    if (t < D)
+      for (int r = 0; r < kChunk; ++r) upart = __builtin_fmaf(wsh[r], bf2f(kps[r * P + t]), upart);
+    if (t == 0)
+      for (int r = 0; r < kChunk; ++r) wsum += wsh[r];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tile = w * TPW + i, bi = tile / NT, bj = tile % NT;
+#pragma unroll
+      for (int ks = 0; ks < kChunk / 16; ++ks)
+        acc[i] = mfma32(tr_nat(kps, P, 16 * ks, 32 * bi, lane), tr_nat(wks, P, 16 * ks, 32 * bj, lane), acc[i]);
+    }
+    __syncthreads();
+  }
+  if (t < D) ush[t] = upart;
+  if (t == 0) wsh[0] = wsum;
+  __syncthreads();
+  const float ws = wsh[0];
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tile = w * TPW + i, bi = tile / NT, bj = tile % NT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int x = 32 * bi + acc_row(r, hh), y = 32 * bj + l32;
+      out[x * D + y] = acc[i][r] + ws + ush[x] + ush[y];
+    }
+  }
+}
+
+// Delta rule, per 128 tokens of a segment (one wave per 32, lanes = tokens),
+// given G = dL/dM_s (in dMr after the backward chain), M_{s-1}, z_{s-1}:
+//   dU = sigma(K) G,  R = sigma(K) M_{s-1} / e (0 in the first segment),
+//   U = V - R;  dv += dU;  d sigma(K) = U G^T - M_{s-1} (dU / e)^T;
+//   de_t = <dU_t, R_t> / e_t  (the gradient of the token's denominator).
+// Transposed products (d_value x tokens) keep every register operand in the
+// accumulator layout of the product that consumes it.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(BwdArgs a) {
+  constexpr int P = D + 8, KS = D / 16, DB = D / 32;
+  const int rb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
+  const bf16* K = static_cast<const bf16*>(a.k);
+  const bf16* V = static_cast<const bf16*>(a.v);
+  __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
+  __shared__ __attribute__((aligned(16))) bf16 msb[D * P];
+  __shared__ float gsum[D], msum[D], zsh[D];
+  const int64_t seg = (int64_t)bh * a.S + s;
+  const float* Gg = a.dMr + seg * D * D;
+  const float* Mg = a.snapM + seg * D * D;
+  for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) {
+    gs[(x / D) * P + x % D] = f2bf(Gg[x]);
+    msb[(x / D) * P + x % D] = f2bf(Mg[x]);
+  }
+  if (threadIdx.x < D) {
+    float cg = 0.f, cm = 0.f;
+    for (int r = 0; r < D; ++r) {
+      cg += Gg[r * D + threadIdx.x];
+      cm += Mg[r * D + threadIdx.x];
+    }
+    gsum[threadIdx.x] = cg;
+    msum[threadIdx.x] = cm;
+    zsh[threadIdx.x] = a.snapz[seg * D + threadIdx.x];
+  }
+  const bool first = a.seg_base + s == 0;
+  const int t0 = rb * kBwdBlock + 32 * w;
+  const bool valid = t0 < a.N;
+  const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
+  __syncthreads();
+  bf16x8 kp[KS];
+  float e = 0.f;
+#pragma unroll
+  for (int c = 0; c < KS; ++c) {
+    const bf16x8 kx = *reinterpret_cast<const bf16x8*>(K + row * D + 16 * c + 8 * hh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = bf2f(kx[j]);
+      const float f = x > 0.f ? x : exp_e(x) - 1.f;
+      kp[c][j] = f2bf(f);
+      e = __builtin_fmaf(f + 1.f, zsh[16 * c + 8 * hh + j], e);
+    }
+  }
+  e += __shfl_xor(e, 32);
+  const float wt = (!first && e > 0.f) ? 1.f / e : 0.f;
+  if (!valid) return;
+  // dU^T, R^T, U^T per 32-row tile of d_value; B operands for d sigma(K)^T
+  bf16x8 ub[DB][2], db[DB][2];
+  float de = 0.f;
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    f32x16 du = zero16(), re = zero16();
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      du = mfma32(tr_nat(gs, P, 16 * c, 32 * d, lane), kp[c], du);
+      if (!first) re = mfma32(tr_nat(msb, P, 16 * c, 32 * d, lane), kp[c], re);
+    }
+    f32x16 u, dw;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int col = 32 * d + acc_row(r, hh);
+      const float dut = du[r] + gsum[col];
+      const float R = first ? 0.f : (re[r] + msum[col]) * wt;
+      a.dv_acc[row * D + col] += dut;
+      u[r] = bf2f(V[row * D + col]) - R;
+      dw[r] = -dut * wt;
+      de = __builtin_fmaf(dut, R, de);
+    }
+    ub[d][0] = acc_op(u, 0);
+    ub[d][1] = acc_op(u, 1);
+    db[d][0] = acc_op(dw, 0);
+    db[d][1] = acc_op(dw, 1);
+  }
+  de = (de + __shfl_xor(de, 32)) * wt;
+  if (hh == 0) a.de[row] = de;
+  // d sigma(K)^T = G U^T - M (dU w)^T: A operands are rows of G and M read at the
+  // accumulator's row order (two 4-element pieces per lane)
+#pragma unroll
+  for (int d2 = 0; d2 < DB; ++d2) {
+    f32x16 df = zero16();
+    const int xr = 32 * d2 + l32;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 32 * d + 16 * ks + 4 * hh;
+        bf16x8 ga, ma;
+        const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(gs + xr * P + c0);
+        const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(gs + xr * P + c0 + 8);
+        const bf16x4 m0 = *reinterpret_cast<const bf16x4*>(msb + xr * P + c0);
+        const bf16x4 m1 = *reinterpret_cast<const bf16x4*>(msb + xr * P + c0 + 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ga[j] = g0[j];
+          ga[4 + j] = g1[j];
+          ma[j] = m0[j];
+          ma[4 + j] = m1[j];
+        }
+        df = mfma32(ga, ub[d][ks], df);
+        if (!first) df = mfma32(ma, db[d][ks], df);
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a.dfk_acc[row * D + 32 * d2 + acc_row(r, hh)] = df[r];
+  }
+}
+
 int bwd_mfma_blocks(int N) { return (N + kBwdBlock - 1) / kBwdBlock; }
 
 template <int D>
@@ -476,5 +684,22 @@ hipError_t launch_backward_lin_update_mfma(const BwdArgs& a, hipStream_t stream)
 }
 template hipError_t launch_backward_lin_update_mfma<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_lin_update_mfma<128>(const BwdArgs&, hipStream_t);
+
+template <int D>
+hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_delta_amat_kernel<D>, dim3((unsigned)a.S, (unsigned)a.BH), dim3(64 * kBwdWaves), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+template <int D>
+hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
+  hipLaunchKernelGGL(bwd_delta_update_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  return hipGetLastError();
+}
+template hipError_t launch_backward_delta_amat_mfma<64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_backward_delta_amat_mfma<128>(const BwdArgs&, hipStream_t);
+template hipError_t launch_backward_delta_update_mfma<64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_backward_delta_update_mfma<128>(const BwdArgs&, hipStream_t);
 
 }  // namespace infini

@@ -176,6 +176,7 @@ struct BwdArgs {
   float* dv_acc;         // [BH*L][dv]
   float* dfk_acc;        // [BH*L][dk] update's d sigma(K)
   float* dbeta_part;     // [BH*S][nqb]
+  float* Amat;           // delta rule, bf16 path: [BH*S][dk][dk] sigma(K)^T diag(1/e) sigma(K)
   int B, H, BH, N, S, dk, dv, nqb;
   int64_t L, seg_base;
   int delta;
@@ -190,6 +191,10 @@ int bwd_query_blocks(int N);
 template <int D> hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream);
 // bf16 path, linear rule: the update's dv and d sigma(K) on the MFMA units.
 template <int D> hipError_t launch_backward_lin_update_mfma(const BwdArgs& a, hipStream_t stream);
+// bf16 path, delta rule: A_s per segment, and (after the chains) the update's dv,
+// d sigma(K) and the denominators' gradients de on the MFMA units.
+template <int D> hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hipStream_t stream);
+template <int D> hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t stream);
 
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);

@@ -225,9 +225,9 @@ def test_backward_workspace_bytes():
     S, D, BH, N = 4, 128, 2, 2048
     L = S * N
     mm, seg, rows = BH * S * D * D, BH * S * D, BH * L
-    # snapshots + retrieval gradients of M, four per-segment d_key vectors, five per-row
+    # snapshots, retrieval gradients of M and (delta, bf16) A_s; four per-segment d_key vectors, five per-row
     # scalars, four per-row accumulators, the dbeta shares (64 query blocks per segment)
-    want = 4 * (2 * mm + 4 * seg + 5 * rows + 4 * rows * D + BH * S * 64)
+    want = 4 * (3 * mm + 4 * seg + 5 * rows + 4 * rows * D + BH * S * 64)
     assert ia.backward_workspace_bytes(st, L) == want
     assert ia.backward_workspace_bytes(st, L + 1) == 0
     assert ia.backward_workspace_bytes(_state(batch=0), L) == 0
