@@ -553,15 +553,28 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs a) {
 // grid (S, BH), 128 threads: ez_s = sum_t de_t sigma(K_t) (delta rule, not the
 // stream's first segment).
 template <typename T>
-__global__ __launch_bounds__(128) void bwd_ez_kernel(BwdArgs a) {
-  const int s = blockIdx.x, bh = blockIdx.y, x = threadIdx.x;
-  if (x >= a.dk) return;
+__global__ __launch_bounds__(kThreads) void bwd_ez_kernel(BwdArgs a) {
+  const int s = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, x = t & 127, half = t >> 7;
   const T* K = static_cast<const T*>(a.k);
+  __shared__ float part[128];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   float acc = 0.f;
-  if (a.delta && !is_first(a, s))
-    for (int r = 0; r < a.N; ++r) acc = __builtin_fmaf(a.de[seg0 + r], sig(ld(K, (seg0 + r) * a.dk + x)), acc);
-  a.ez[((int64_t)bh * a.S + s) * a.dk + x] = acc;
+  if (a.delta && !is_first(a, s) && x < a.dk) {
+    // rows half, half + 2, ...: eight independent partial sums keep the loads in flight
+    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int r = half;
+    for (; r + 14 < a.N; r += 16)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t row = seg0 + r + 2 * u;
+        p[u] = __builtin_fmaf(a.de[row], sig(ld(K, row * a.dk + x)), p[u]);
+      }
+    for (; r < a.N; r += 2) p[0] = __builtin_fmaf(a.de[seg0 + r], sig(ld(K, (seg0 + r) * a.dk + x)), p[0]);
+    acc = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  }
+  if (half == 1) part[x] = acc;
+  __syncthreads();
+  if (half == 0 && x < a.dk) a.ez[((int64_t)bh * a.S + s) * a.dk + x] = acc + part[x];
 }
 
 // grid (BH), 128 threads: gzs_s = dL/dz_s; dz0 = dL/dz_0.
@@ -804,24 +817,62 @@ __global__ __launch_bounds__(kThreads) void bwd_zscan_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- finish
-// grid (ceil(BH * L / 2)), 256 threads: two rows per workgroup.
-template <typename T>
+// dq, dk, dv in the I/O dtype: dk = dk_att + (d sigma(K) + dL/dz_s [+ de z_{s-1}]) sigma'(k).
+// Four consecutive elements per thread when d_key and d_value are multiples of 4,
+// else one; grid-stride over (rows x groups of d_key) then (rows x groups of d_value).
+__device__ __forceinline__ void st4(bf16* p, const float (&x)[4]) {
+  bf16x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = f2bf(x[j]);
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void st4(float* p, const float (&x)[4]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+}
+template <typename T, int W>
 __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
-  const int x = threadIdx.x & 127;
-  if (row >= (int64_t)a.BH * a.L) return;
-  const int bh = (int)(row / a.L);
-  const int s = (int)((row % a.L) / a.N);
+  const int gk = a.dk / W, gv = a.dv / W;
+  const int64_t rows = (int64_t)a.BH * a.L, nk = rows * gk, nv = rows * gv;
   const T* K = static_cast<const T*>(a.k);
-  if (x < a.dk) {
-    const int64_t zi = ((int64_t)bh * a.S + s) * a.dk + x;
-    float dfk = a.dfk_acc[row * a.dk + x] + a.gzs[zi];
-    if (a.delta && !is_first(a, s)) dfk = __builtin_fmaf(a.de[row], a.snapz[zi], dfk);
-    const float kx = ld(K, row * a.dk + x);
-    st(static_cast<T*>(a.dk_out), row * a.dk + x, a.dk_acc[row * a.dk + x] + dfk * sig_prime(kx));
-    st(static_cast<T*>(a.dq_out), row * a.dk + x, a.dq_acc[row * a.dk + x]);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nk + nv; i += (int64_t)gridDim.x * kThreads) {
+    if (i < nk) {
+      const int64_t row = i / gk;
+      const int x0 = W * (int)(i % gk);
+      const int bh = (int)(row / a.L), s = (int)((row % a.L) / a.N);
+      const bool hasd = a.delta && !is_first(a, s);
+      const int64_t zi = ((int64_t)bh * a.S + s) * a.dk + x0, ri = row * a.dk + x0;
+      const float de = hasd ? a.de[row] : 0.f;
+      float dk[W], dq[W];
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const float dfk = __builtin_fmaf(de, a.snapz[zi + j], a.dfk_acc[ri + j] + a.gzs[zi + j]);
+        dk[j] = a.dk_acc[ri + j] + dfk * sig_prime(ld(K, ri + j));
+        dq[j] = a.dq_acc[ri + j];
+      }
+      if constexpr (W == 4) {
+        st4(static_cast<T*>(a.dk_out) + ri, dk);
+        st4(static_cast<T*>(a.dq_out) + ri, dq);
+      } else {
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+          st(static_cast<T*>(a.dk_out), ri + j, dk[j]);
+          st(static_cast<T*>(a.dq_out), ri + j, dq[j]);
+        }
+      }
+    } else {
+      const int64_t j0 = i - nk, row = j0 / gv;
+      const int64_t ri = row * a.dv + W * (j0 % gv);
+      float dv[W];
+#pragma unroll
+      for (int j = 0; j < W; ++j) dv[j] = a.dv_acc[ri + j];
+      if constexpr (W == 4) {
+        st4(static_cast<T*>(a.dv_out) + ri, dv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < W; ++j) st(static_cast<T*>(a.dv_out), ri + j, dv[j]);
+      }
+    }
   }
-  if (x < a.dv) st(static_cast<T*>(a.dv_out), row * a.dv + x, a.dv_acc[row * a.dv + x]);
 }
 
 // grid (H), 256 threads: dbeta_h = sum over batch, segments and query blocks.
@@ -900,7 +951,13 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     INFINI_BWD_LAUNCH(bwd_key_kernel<T>, dim3((unsigned)((a.N + kKB - 1) / kKB), S, BH), dim3(kThreads), 0, stream,
                       a);
   }
-  INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 1>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
+  if (mfma) {
+    e = a.dk == 128 ? launch_backward_retrieval_grad_mfma<128>(a, stream)
+                    : launch_backward_retrieval_grad_mfma<64>(a, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 1>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
+  }
   if (delta_mfma) {
     INFINI_BWD_LAUNCH(bwd_delta_chain_kernel<false>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
     e = a.dk == 128 ? launch_backward_delta_update_mfma<128>(a, stream)
@@ -923,10 +980,18 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
                         0, stream, a);
     }
   }
-  INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(128), 0, stream, a);
+  INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
   INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
-  INFINI_BWD_LAUNCH(bwd_finish_kernel<T>, dim3((unsigned)(((int64_t)a.BH * a.L + 1) / 2)), dim3(kThreads), 0, stream,
-                    a);
+  {
+    const uintptr_t al = 4 * sizeof(T) - 1;
+    const bool vec = a.dk % 4 == 0 && a.dv % 4 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.dq_out) | reinterpret_cast<uintptr_t>(a.dk_out) |
+                       reinterpret_cast<uintptr_t>(a.dv_out)) & al) == 0;
+    const int64_t n = (int64_t)a.BH * a.L * (a.dk + a.dv) / (vec ? 4 : 1);
+    const dim3 grid((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1 << 20));
+    if (vec) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4>), grid, dim3(kThreads), 0, stream, a);
+    else INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 1>), grid, dim3(kThreads), 0, stream, a);
+  }
   INFINI_BWD_LAUNCH(bwd_dbeta_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, stream, a);
 #undef INFINI_BWD_LAUNCH
   return hipSuccess;

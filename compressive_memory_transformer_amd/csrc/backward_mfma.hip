@@ -454,85 +454,119 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(Bwd
   }
 }
 
-// Delta rule: A_s = sigma(K)^T diag(w) sigma(K), w_t = 1 / (sigma(K_t) . z_{s-1})
-// (0 in a stream's first segment), one workgroup per segment.  With
-// sigma(K) = 1 + K' (K' = sigma(K) - 1, rounded to bf16 for the products):
-//   A_s = (sum w) 1 1^T + 1 u^T + u 1^T + K'^T diag(w) K',  u = K'^T w,
-// the rank-one terms in fp32 and the last product on MFMA (both operands read
-// transposed from LDS, 64 tokens per step).
-template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_amat_kernel(BwdArgs a) {
-  constexpr int P = D + 8, NT = D / 32;   // NT x NT output tiles, NT * NT / 4 per wave
+// A per-segment Gram product on MFMA, one workgroup per segment, 64 tokens per
+// step, both operands read transposed from LDS:
+//   GRAM = false (delta rule): A_s = sigma(K)^T diag(w) sigma(K), w_t = 1 / (sigma(K_t) .
+//     z_{s-1}) (0 in a stream's first segment).  With sigma(K) = 1 + K' (K' rounded
+//     to bf16 for the product) A_s = (sum w) 1 1^T + 1 u^T + u 1^T + K'^T diag(w) K',
+//     u = K'^T w, the rank-one terms in fp32;
+//   GRAM = true (retrieval gradients, both rules): dMr_s = sigma(Q)^T diag(rs) dA =
+//     1 (dA^T rs)^T + Q'^T diag(rs) dA and dzr_s = sigma(Q)^T dden, the column sums
+//     in fp32 from the inputs.
+template <int D, bool RETR>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
+  constexpr int P = D + 8, NT = D / 32;
+  constexpr int TPW = NT * NT / kBwdWaves > 0 ? NT * NT / kBwdWaves : 1;   // output tiles per wave
   const int s = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const bf16* K = static_cast<const bf16*>(a.k);
-  __shared__ __attribute__((aligned(16))) bf16 kps[kChunk * P];
-  __shared__ __attribute__((aligned(16))) bf16 wks[kChunk * P];
-  __shared__ float zsh[D], ush[D], wsh[kChunk];
-  float* out = a.Amat + ((int64_t)bh * a.S + s) * D * D;
-  if (a.seg_base + s == 0) {
+  const bf16* X = static_cast<const bf16*>(RETR ? a.q : a.k);
+  const bf16* Y = static_cast<const bf16*>(a.dout);
+  __shared__ __attribute__((aligned(16))) bf16 xs[kChunk * P];
+  __shared__ __attribute__((aligned(16))) bf16 ys[kChunk * P];
+  __shared__ float zsh[D], ush[D], wsh[kChunk], dsh[kChunk];
+  const int64_t seg = (int64_t)bh * a.S + s;
+  float* out = (RETR ? a.dMr : a.Amat) + seg * D * D;
+  if (!RETR && a.seg_base + s == 0) {
     for (int i = t; i < D * D; i += 64 * kBwdWaves) out[i] = 0.f;
     return;
   }
   if (t < D) {
-    zsh[t] = a.snapz[((int64_t)bh * a.S + s) * D + t];
+    zsh[t] = RETR ? 0.f : a.snapz[seg * D + t];
     ush[t] = 0.f;
   }
-  constexpr int TPW = NT * NT / kBwdWaves > 0 ? NT * NT / kBwdWaves : 1;   // tiles per wave
   f32x16 acc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = zero16();
-  float wsum = 0.f, upart = 0.f;
+  float wsum = 0.f, upart = 0.f, zpart = 0.f;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  // thread -> (token tt = t / 4, quarter of the row qq = t % 4)
-  const int tt = t >> 2, qq = t & 3;
-  constexpr int QW = D / 4;   // columns per thread
+  const int tt = t >> 2, qq = t & 3;   // staging: token tt, quarter qq of its row
+  constexpr int QW = D / 4;
   __syncthreads();
   for (int t0 = 0; t0 < a.N; t0 += kChunk) {
-    float kv[QW];
+    const int64_t row = seg0 + t0 + tt;
+    float xv[QW];
     float e = 0.f;
 #pragma unroll
     for (int i = 0; i < QW / 8; ++i) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(K + (seg0 + t0 + tt) * D + qq * QW + 8 * i);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(X + row * D + qq * QW + 8 * i);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float v = bf2f(x[j]);
         const float f = v > 0.f ? v : exp_e(v) - 1.f;
-        kv[8 * i + j] = f;
-        e = __builtin_fmaf(f + 1.f, zsh[qq * QW + 8 * i + j], e);
+        xv[8 * i + j] = f;
+        if (!RETR) e = __builtin_fmaf(f + 1.f, zsh[qq * QW + 8 * i + j], e);
       }
     }
-    e += __shfl_xor(e, 1);
-    e += __shfl_xor(e, 2);
-    const float wt = e > 0.f ? 1.f / e : 0.f;
+    float wt;
+    if (RETR) {
+      wt = a.rs[row];
+    } else {
+      e += __shfl_xor(e, 1);
+      e += __shfl_xor(e, 2);
+      wt = e > 0.f ? 1.f / e : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < QW / 8; ++i) {
-      bf16x8 kb, wb;
+      bf16x8 xb, yb;
+      if (RETR) {
+        const bf16x8 y = *reinterpret_cast<const bf16x8*>(Y + row * D + qq * QW + 8 * i);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kb[j] = f2bf(kv[8 * i + j]);
-        wb[j] = f2bf(wt * kv[8 * i + j]);
+        for (int j = 0; j < 8; ++j) {
+          xb[j] = f2bf(xv[8 * i + j]);
+          yb[j] = f2bf(wt * bf2f(y[j]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xb[j] = f2bf(xv[8 * i + j]);
+          yb[j] = f2bf(wt * xv[8 * i + j]);
+        }
       }
-      *reinterpret_cast<bf16x8*>(kps + tt * P + qq * QW + 8 * i) = kb;
-      *reinterpret_cast<bf16x8*>(wks + tt * P + qq * QW + 8 * i) = wb;
+      *reinterpret_cast<bf16x8*>(xs + tt * P + qq * QW + 8 * i) = xb;
+      *reinterpret_cast<bf16x8*>(ys + tt * P + qq * QW + 8 * i) = yb;
     }
-    if (qq == 0) wsh[tt] = wt;
+    if (qq == 0) {
+      wsh[tt] = wt;
+      if (RETR) dsh[tt] = a.dden[row];
+    }
     __syncthreads();
-    if (t < D)
-      for (int r = 0; r < kChunk; ++r) upart = __builtin_fmaf(wsh[r], bf2f(kps[r * P + t]), upart);
-    if (t == 0)
+    if (t < D) {
+      if (RETR) {
+        // fp32 column sums from the inputs: sum_t rs_t dA_t and sum_t dden_t sigma(q_t)
+        for (int r = 0; r < kChunk; ++r) {
+          const int64_t rr = seg0 + t0 + r;
+          upart = __builtin_fmaf(wsh[r], bf2f(Y[rr * D + t]), upart);
+          const float q = bf2f(X[rr * D + t]);
+          zpart = __builtin_fmaf(dsh[r], q > 0.f ? q + 1.f : exp_e(q), zpart);
+        }
+      } else {
+        for (int r = 0; r < kChunk; ++r) upart = __builtin_fmaf(wsh[r], bf2f(xs[r * P + t]), upart);
+      }
+    }
+    if (!RETR && t == 0)
       for (int r = 0; r < kChunk; ++r) wsum += wsh[r];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tile = w * TPW + i, bi = tile / NT, bj = tile % NT;
 #pragma unroll
       for (int ks = 0; ks < kChunk / 16; ++ks)
-        acc[i] = mfma32(tr_nat(kps, P, 16 * ks, 32 * bi, lane), tr_nat(wks, P, 16 * ks, 32 * bj, lane), acc[i]);
+        acc[i] = mfma32(tr_nat(xs, P, 16 * ks, 32 * bi, lane), tr_nat(ys, P, 16 * ks, 32 * bj, lane), acc[i]);
     }
     __syncthreads();
   }
   if (t < D) ush[t] = upart;
   if (t == 0) wsh[0] = wsum;
+  if (RETR && t < D) a.dzr[seg * D + t] = zpart;
   __syncthreads();
   const float ws = wsh[0];
   const int l32 = lane & 31, hh = lane >> 5;
@@ -542,7 +576,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_amat_kernel(BwdArgs 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int x = 32 * bi + acc_row(r, hh), y = 32 * bj + l32;
-      out[x * D + y] = acc[i][r] + ws + ush[x] + ush[y];
+      out[x * D + y] = RETR ? acc[i][r] + ush[y] : acc[i][r] + ws + ush[x] + ush[y];
     }
   }
 }
@@ -687,7 +721,7 @@ template hipError_t launch_backward_lin_update_mfma<128>(const BwdArgs&, hipStre
 
 template <int D>
 hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_delta_amat_kernel<D>, dim3((unsigned)a.S, (unsigned)a.BH), dim3(64 * kBwdWaves), 0, stream,
+  hipLaunchKernelGGL((bwd_gram_kernel<D, false>), dim3((unsigned)a.S, (unsigned)a.BH), dim3(64 * kBwdWaves), 0, stream,
                      a);
   return hipGetLastError();
 }
@@ -697,6 +731,14 @@ hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t strea
   hipLaunchKernelGGL(bwd_delta_update_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
   return hipGetLastError();
 }
+template <int D>
+hipError_t launch_backward_retrieval_grad_mfma(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_gram_kernel<D, true>), dim3((unsigned)a.S, (unsigned)a.BH), dim3(64 * kBwdWaves), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+template hipError_t launch_backward_retrieval_grad_mfma<64>(const BwdArgs&, hipStream_t);
+template hipError_t launch_backward_retrieval_grad_mfma<128>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_delta_amat_mfma<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_delta_amat_mfma<128>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_delta_update_mfma<64>(const BwdArgs&, hipStream_t);

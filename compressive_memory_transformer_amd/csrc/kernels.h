@@ -194,6 +194,8 @@ template <int D> hipError_t launch_backward_lin_update_mfma(const BwdArgs& a, hi
 // bf16 path, delta rule: A_s per segment, and (after the chains) the update's dv,
 // d sigma(K) and the denominators' gradients de on the MFMA units.
 template <int D> hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hipStream_t stream);
+// bf16 path: the retrieval's gradients dMr, dzr of every segment on the MFMA units.
+template <int D> hipError_t launch_backward_retrieval_grad_mfma(const BwdArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t stream);
 
 // Zero n floats at p and n2 floats at p2 (one launch).
