@@ -148,22 +148,25 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kChunk, buf ^= 1) {
     const bool next = kc0 + kChunk < kend;
     if (next) cp.load(K, V, seg0 + kc0 + kChunk);
+    // both 32-key halves of the chunk at once: four independent product chains,
+    // one rescale per 64 keys (a chunk wholly after the wave's queries is skipped)
+    if (qvalid && kc0 <= qw0 + 31) {
+      f32x16 sa[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key0 = kc0 + 32 * kt;
-      if (!qvalid || key0 > qw0 + 31) continue;   // keys all after the wave's queries
-      f32x16 sacc = zero16();
+      for (int c = 0; c < KS; ++c)
 #pragma unroll
-      for (int c = 0; c < KS; ++c) sacc = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sacc);
+        for (int kt = 0; kt < 2; ++kt) sa[kt] = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sa[kt]);
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = key0 + acc_row(r, hh) <= qcol ? sacc[r] * sl2 : -__builtin_inff();
-        sacc[r] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = kc0 + 32 * kt + acc_row(r, hh) <= qcol ? sa[kt][r] * sl2 : -__builtin_inff();
+          sa[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m2, mx);               // finite: key 0 is in the first tile
+      const float mn = fmaxf(m2, mx);               // finite: key 0 is in the first chunk
       const float alpha = exp2_fast(m2 - mn);
       l *= alpha;
 #pragma unroll
@@ -171,18 +174,27 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(sacc[r] - mn);
-        sacc[r] = p;
-        l += p;
-      }
-      m2 = mn;
-      const bf16x8 p0 = acc_op(sacc, 0), p1 = acc_op(sacc, 1);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        o[d] = mfma32(tr_op(vc[buf], P, 32 * kt, 32 * d, lane), p0, o[d]);
-        o[d] = mfma32(tr_op(vc[buf], P, 32 * kt + 16, 32 * d, lane), p1, o[d]);
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(sa[kt][r] - mn);
+          sa[kt][r] = p;
+          l += p;
+        }
+      m2 = mn;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        pb[kt][0] = acc_op(sa[kt], 0);
+        pb[kt][1] = acc_op(sa[kt], 1);
       }
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          o[d] = mfma32(tr_op(vc[buf], P, 32 * kt, 32 * d, lane), pb[kt][0], o[d]);
+          o[d] = mfma32(tr_op(vc[buf], P, 32 * kt + 16, 32 * d, lane), pb[kt][1], o[d]);
+        }
     }
     if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
     __syncthreads();
@@ -250,28 +262,34 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kChunk, buf ^= 1) {
     const bool next = kc0 + kChunk < kend;
     if (next) cp.load(K, V, seg0 + kc0 + kChunk);
+    if (qvalid && kc0 <= qw0 + 31) {
+      f32x16 sa[2] = {zero16(), zero16()}, pa[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key0 = kc0 + 32 * kt;
-      if (!qvalid || key0 > qw0 + 31) continue;
-      f32x16 sacc = zero16(), pacc = zero16();
+      for (int c = 0; c < KS; ++c)
 #pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        sacc = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sacc);
-        pacc = mfma32(row_op(vc[buf], P, 32 * kt, 16 * c, lane), dr[c], pacc);
+        for (int kt = 0; kt < 2; ++kt) {
+          sa[kt] = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sa[kt]);
+          pa[kt] = mfma32(row_op(vc[buf], P, 32 * kt, 16 * c, lane), dr[c], pa[kt]);
+        }
+      bf16x8 db[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool vis = kc0 + 32 * kt + acc_row(r, hh) <= qcol;
+          const float p = vis ? exp2_fast(sa[kt][r] * sl2 - lse2) : 0.f;
+          sa[kt][r] = p * ((1.f - g) * pa[kt][r] - Dv);
+        }
+        db[kt][0] = acc_op(sa[kt], 0);
+        db[kt][1] = acc_op(sa[kt], 1);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool vis = key0 + acc_row(r, hh) <= qcol;
-        const float p = vis ? exp2_fast(sacc[r] * sl2 - lse2) : 0.f;
-        sacc[r] = p * ((1.f - g) * pacc[r] - Dv);
-      }
-      const bf16x8 d0 = acc_op(sacc, 0), d1 = acc_op(sacc, 1);
+      for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt, 32 * d, lane), d0, dq[d]);
-        dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt + 16, 32 * d, lane), d1, dq[d]);
-      }
+        for (int kt = 0; kt < 2; ++kt) {
+          dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt, 32 * d, lane), db[kt][0], dq[d]);
+          dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt + 16, 32 * d, lane), db[kt][1], dq[d]);
+        }
     }
     if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
     __syncthreads();
@@ -349,35 +367,44 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) 
         nd = a.drow[seg0 + qc0 + kChunk + threadIdx.x];
       }
     }
+    // both 32-query halves of the chunk at once (a chunk wholly before the wave's
+    // keys is skipped)
+    if (kvalid && qc0 + kChunk - 1 >= kw0) {
+      f32x16 sa[2] = {zero16(), zero16()}, pa[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int qr0 = qc0 + 32 * qt;
-      if (!kvalid || qr0 + 31 < kw0) continue;     // queries all before the wave's keys
-      f32x16 sacc = zero16(), pacc = zero16();
+      for (int c = 0; c < KS; ++c)
 #pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        sacc = mfma32(row_op(qc[buf], P, 32 * qt, 16 * c, lane), kr[c], sacc);
-        pacc = mfma32(row_op(dc[buf], P, 32 * qt, 16 * c, lane), vr[c], pacc);
+        for (int qt = 0; qt < 2; ++qt) {
+          sa[qt] = mfma32(row_op(qc[buf], P, 32 * qt, 16 * c, lane), kr[c], sa[qt]);
+          pa[qt] = mfma32(row_op(dc[buf], P, 32 * qt, 16 * c, lane), vr[c], pa[qt]);
+        }
+      // S: rows are queries qc0 + 32 qt + acc_row, the lane's column the key kcol
+      bf16x8 pb[2][2], db[2][2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x16 ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 32 * qt + acc_row(r, hh);
+          const bool vis = kcol <= qc0 + il;
+          const float p = vis ? exp2_fast(sa[qt][r] * sl2 - lc[buf][il]) : 0.f;
+          sa[qt][r] = p;
+          ds[r] = p * ((1.f - g) * pa[qt][r] - dcr[buf][il]);
+        }
+        pb[qt][0] = acc_op(sa[qt], 0);
+        pb[qt][1] = acc_op(sa[qt], 1);
+        db[qt][0] = acc_op(ds, 0);
+        db[qt][1] = acc_op(ds, 1);
       }
-      // S: rows are queries qr0 + acc_row, the lane's column the key kcol
-      f32x16 ds;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = 32 * qt + acc_row(r, hh);
-        const bool vis = kcol <= qc0 + il;
-        const float p = vis ? exp2_fast(sacc[r] * sl2 - lc[buf][il]) : 0.f;
-        sacc[r] = p;
-        ds[r] = p * ((1.f - g) * pacc[r] - dcr[buf][il]);
-      }
-      const bf16x8 p0 = acc_op(sacc, 0), p1 = acc_op(sacc, 1);
-      const bf16x8 d0 = acc_op(ds, 0), d1 = acc_op(ds, 1);
+      for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt, 32 * d, lane), p0, dv[d]);
-        dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt + 16, 32 * d, lane), p1, dv[d]);
-        dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt, 32 * d, lane), d0, dk[d]);
-        dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt + 16, 32 * d, lane), d1, dk[d]);
-      }
+        for (int qt = 0; qt < 2; ++qt) {
+          dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt, 32 * d, lane), pb[qt][0], dv[d]);
+          dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt + 16, 32 * d, lane), pb[qt][1], dv[d]);
+          dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt, 32 * d, lane), db[qt][0], dk[d]);
+          dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt + 16, 32 * d, lane), db[qt][1], dk[d]);
+        }
     }
     if (next) {
       cp.store(qc[buf ^ 1], dc[buf ^ 1]);
