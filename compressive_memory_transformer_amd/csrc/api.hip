@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 
 #include "../../include/infini_attn.h"
 #include "kernels.h"
@@ -486,6 +487,105 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   a.L = seq_len; a.seg_base = st->segments_done; a.delta = st->rule == INFINI_RULE_DELTA; a.scale = st->scale;
   const hipError_t e = infini::launch_backward(a, st->dtype == INFINI_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+// ------------------------------------------------------------------ layer
+namespace {
+// Workspace of the layer: q, k, v and the heads' outputs (bf16 [B, H, L, d]), then
+// the forward's own workspace.
+bool layer_layout(const infini_attn_state* st, int64_t seq_len, size_t* qo, size_t* ko, size_t* vo, size_t* ao,
+                  size_t* fo, WsLayout* fw, size_t* total) {
+  const int64_t BH = (int64_t)st->batch * st->heads;
+  int64_t rows, nq, nv;
+  if (!mul_ok(BH, seq_len, &rows) || !mul_ok(rows, st->d_key, &nq) || !mul_ok(rows, st->d_value, &nv)) return false;
+  if (!workspace_layout(st, seq_len / st->segment_len, seq_len, fw)) return false;
+  size_t off = 0;
+  *qo = off; off = align_up(off + (size_t)nq * 2);
+  *ko = off; off = align_up(off + (size_t)nq * 2);
+  *vo = off; off = align_up(off + (size_t)nv * 2);
+  *ao = off; off = align_up(off + (size_t)nv * 2);
+  *fo = off; off = align_up(off + fw->total);
+  *total = off;
+  return true;
+}
+}  // namespace
+
+size_t infini_attn_layer_workspace_bytes(const infini_attn_state* st, int32_t d_model, int64_t seq_len) {
+  if (check_state(st) != INFINI_OK || st->dtype != INFINI_BF16 || d_model <= 0 || d_model % 64 != 0) return 0;
+  if (seq_len <= 0 || seq_len % st->segment_len != 0) return 0;
+  size_t qo, ko, vo, ao, fo, total;
+  WsLayout fw;
+  if (!layer_layout(st, seq_len, &qo, &ko, &vo, &ao, &fo, &fw, &total)) return 0;
+  return total;
+}
+
+int infini_attn_layer_forward(infini_attn_state* st, const void* x, int32_t d_model, const void* w_qkv,
+                              const void* w_o, int64_t seq_len, const float* beta, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  int rc = check_state(st);
+  if (rc != INFINI_OK) return rc;
+  if (st->dtype != INFINI_BF16) return fail(INFINI_EUNSUPPORTED, "the layer entry point runs the bf16 path only");
+  if (!x || !w_qkv || !w_o || !beta || !y) return fail(INFINI_EINVAL, "x, w_qkv, w_o, beta and y must be non-NULL");
+  if (d_model <= 0 || d_model % 64 != 0)
+    return fail(INFINI_EUNSUPPORTED, "d_model must be a positive multiple of 64 (got %d)", d_model);
+  if (seq_len <= 0 || seq_len % st->segment_len != 0)
+    return fail(INFINI_EINVAL, "seq_len (%lld) must be a positive multiple of segment_len (%d)",
+                (long long)seq_len, st->segment_len);
+  const int64_t S64 = seq_len / st->segment_len;
+  if (S64 > 0x7fffffff) return fail(INFINI_EINVAL, "too many segments");
+  const int64_t BH = (int64_t)st->batch * st->heads;
+  const int64_t M = (int64_t)st->batch * seq_len;
+  const int64_t nqkv = (int64_t)st->heads * (2 * st->d_key + st->d_value);
+  if (M > 0x7fffffff - 256 || (M + 127) / 128 > 65535)
+    return fail(INFINI_EUNSUPPORTED, "batch * seq_len too large for one layer call; split the call");
+  for (const void* p : {x, w_qkv, w_o, static_cast<const void*>(y)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(INFINI_EINVAL, "x, w_qkv, w_o and y must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(beta) % 4 != 0) return fail(INFINI_EINVAL, "beta must be 4-byte aligned");
+  size_t qo, ko, vo, ao, fo, total;
+  WsLayout fw;
+  if (!layer_layout(st, seq_len, &qo, &ko, &vo, &ao, &fo, &fw, &total))
+    return fail(INFINI_EINVAL, "workspace size overflows");
+  if (!workspace || workspace_bytes < total)
+    return fail(INFINI_EWORKSPACE, "workspace of %zu bytes required, %zu given%s", total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(INFINI_EWORKSPACE, "workspace must be 256-byte aligned");
+  const size_t xb = (size_t)M * d_model * 2, wqb = (size_t)d_model * nqkv * 2;
+  const size_t wob = (size_t)st->heads * st->d_value * d_model * 2;
+  const size_t mb = (size_t)BH * st->d_key * st->d_value * 4, zb = (size_t)BH * st->d_key * 4;
+  for (const auto& in : {std::make_pair(x, xb), std::make_pair(w_qkv, wqb), std::make_pair(w_o, wob),
+                         std::make_pair(static_cast<const void*>(st->M), mb),
+                         std::make_pair(static_cast<const void*>(st->z), zb)}) {
+    if (overlaps(y, xb, in.first, in.second)) return fail(INFINI_EINVAL, "y must not alias the inputs or the state");
+    if (overlaps(workspace, total, in.first, in.second))
+      return fail(INFINI_EWORKSPACE, "workspace must not alias the inputs or the state");
+  }
+  if (overlaps(workspace, total, y, xb)) return fail(INFINI_EWORKSPACE, "workspace must not alias y");
+  const int64_t fa_blocks = infini::fa_fwd_blocks(BH * S64, st->segment_len);
+  if (fa_blocks > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  typedef infini::bf16 bf;
+  bf* q = reinterpret_cast<bf*>(ws + qo);
+  bf* k = reinterpret_cast<bf*>(ws + ko);
+  bf* v = reinterpret_cast<bf*>(ws + vo);
+  bf* a = reinterpret_cast<bf*>(ws + ao);
+  infini::GemmArgs g1{static_cast<const bf*>(x), static_cast<const bf*>(w_qkv), nullptr, q, k, v,
+                      (int)M, (int)nqkv, d_model, 0, 1, (int)seq_len, st->heads, st->d_key, st->d_value};
+  hipError_t e = infini::launch_gemm_bf16(g1, strm);
+  if (e != hipSuccess) return hip_fail(e, "QKV projection launch");
+  infini_attn_state s = *st;
+  rc = s.d_key == 128 ? run_bf16<128>(&s, q, k, v, seq_len, (int)S64, beta, a, ws + fo, fw, strm, nullptr)
+                      : run_bf16<64>(&s, q, k, v, seq_len, (int)S64, beta, a, ws + fo, fw, strm, nullptr);
+  if (rc != INFINI_OK) return rc;
+  infini::GemmArgs g2{a, static_cast<const bf*>(w_o), static_cast<bf*>(y), nullptr, nullptr, nullptr,
+                      (int)M, d_model, st->heads * st->d_value, 1, 0, (int)seq_len, st->heads, st->d_key,
+                      st->d_value};
+  e = infini::launch_gemm_bf16(g2, strm);
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  st->segments_done += S64;
   return ok();
 }
 

@@ -198,6 +198,24 @@ template <int D> hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hi
 template <int D> hipError_t launch_backward_retrieval_grad_mfma(const BwdArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- projections
+// C = A B in bf16 with fp32 accumulation; B row-major [K][N].  a_heads: A is the
+// heads' outputs [B, H, L, dv] read as [B L, H dv] (K = H dv); else row-major
+// [M][K].  c_heads: column n of C goes to q (n < H dk), k (n < 2 H dk) or v,
+// each [B, H, L, d]; else C is row-major [M][N].  K a multiple of 64, N of 8.
+struct GemmArgs {
+  const bf16* a;
+  const bf16* b;
+  bf16* c;
+  bf16* q;
+  bf16* k;
+  bf16* v;
+  int M, N, K;
+  int a_heads, c_heads;
+  int L, H, dk, dv;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
+
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);
 

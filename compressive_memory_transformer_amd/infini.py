@@ -106,6 +106,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_backward_sequence.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                   vp, sz, vp]
     lib.infini_attn_backward_sequence.restype = ctypes.c_int
+    lib.infini_attn_layer_workspace_bytes.argtypes = [sp, i32, i64]
+    lib.infini_attn_layer_workspace_bytes.restype = sz
+    lib.infini_attn_layer_forward.argtypes = [sp, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
+    lib.infini_attn_layer_forward.restype = ctypes.c_int
     lib.infini_attn_reset.argtypes = [sp, vp]
     lib.infini_attn_reset.restype = ctypes.c_int
     lib.infini_attn_last_error.argtypes = []
@@ -205,6 +209,17 @@ def backward_sequence(st: State, q, k, v, seq_len, beta, dout, dM, dz, dq, dk, d
     rc = load_library().infini_attn_backward_sequence(
         ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len, _ptr(beta), _ptr(dout), _ptr(dM), _ptr(dz),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
+def layer_workspace_bytes(st: State, d_model: int, seq_len: int) -> int:
+    return load_library().infini_attn_layer_workspace_bytes(ctypes.byref(st), d_model, seq_len)
+
+
+def layer_forward(st: State, x, d_model, w_qkv, w_o, seq_len, beta, y, workspace, ws_bytes, stream=None,
+                  check=True) -> int:
+    rc = load_library().infini_attn_layer_forward(ctypes.byref(st), _ptr(x), d_model, _ptr(w_qkv), _ptr(w_o),
+                                                  seq_len, _ptr(beta), _ptr(y), _ptr(workspace), ws_bytes, stream)
     return _check(rc) if check else rc
 
 
@@ -311,6 +326,25 @@ class InfiniAttention:
         ws, nbytes = self.append_workspace(n)
         append(self.state, self.open, q, k, v, n, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
         return out
+
+    def layer_forward(self, x, w_qkv, w_o, beta, y=None, stream=None):
+        """y = concat_h(A_h) w_o with q, k, v = x w_qkv split into heads (x: [B, L,
+        d_model] bf16; w_qkv: [d_model, H (2 d_key + d_value)]; w_o: [H d_value,
+        d_model])."""
+        torch = self.torch
+        d_model, seq_len = x.shape[2], x.shape[1]
+        if y is None:
+            y = torch.empty_like(x)
+        need = layer_workspace_bytes(self.state, d_model, seq_len)
+        if need == 0:
+            raise InfiniError(EINVAL, f"no layer workspace size for d_model={d_model}, seq_len={seq_len}")
+        if self._ws_bytes < need:
+            raw = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
+            off = (-raw.data_ptr()) % 256
+            self._ws_raw, self._ws, self._ws_bytes = raw, raw[off:off + need], need
+        layer_forward(self.state, x, d_model, w_qkv, w_o, seq_len, beta, y, self._ws, self._ws_bytes,
+                      _stream_handle(torch, stream))
+        return y
 
     def backward_sequence(self, q, k, v, beta, dout, M0, z0, segments_done, dM=None, dz=None, stream=None):
         """Gradients of a forward_sequence call over q, k, v, beta that started

@@ -30,6 +30,8 @@ Q_ID, K_ID, V_ID, BETA_ID, PLANT_ID = 0, 1, 2, 3, 4
 # output gradient tiles (d_value wide, like V), the final-state gradients and a
 # starting state for streams that resume from a non-empty memory
 DOUT_ID, STATE_GRAD_ID, STATE0_ID = 5, 6, 7
+# the layer around the stream: input rows and the two projection weights
+X_ID, WQKV_ID, WO_ID = 8, 9, 10
 
 
 @dataclass(frozen=True)
@@ -152,6 +154,23 @@ def initial_state(w: Workload, segments: int = 2):
     M0 = (g.standard_normal((w.batch, w.heads, w.d_key, w.d_value)) * math.sqrt(n0) * w.input_scale)
     z0 = n0 * (1.0 + 0.05 * np.abs(g.standard_normal((w.batch, w.heads, w.d_key))))
     return M0.astype(np.float32), z0.astype(np.float32)
+
+
+def layer_tensors(w: Workload, d_model: int):
+    """Input x [B, L, d_model] ~ N(0, 1), fused projection weights w_qkv
+    [d_model, H (2 d_key + d_value)] ~ N(0, 1 / d_model) times the input scale (so
+    the projected q, k, v have the spread of the workload's own inputs) and w_o
+    [H d_value, d_model] ~ N(0, 1 / (H d_value)); float32 values, rounded to bf16
+    for bf16 workloads."""
+    H = w.heads
+    x = rng(w.seed, X_ID).standard_normal((w.batch, w.seq_len, d_model), dtype=np.float32)
+    wq = rng(w.seed, WQKV_ID).standard_normal((d_model, H * (2 * w.d_key + w.d_value)), dtype=np.float32)
+    wq *= np.float32(w.input_scale / math.sqrt(d_model))
+    wo = rng(w.seed, WO_ID).standard_normal((H * w.d_value, d_model), dtype=np.float32)
+    wo *= np.float32(1.0 / math.sqrt(H * w.d_value))
+    if w.dtype == "bf16":
+        x, wq, wo = round_bf16(x), round_bf16(wq), round_bf16(wo)
+    return x, wq, wo
 
 
 def betas(w: Workload) -> np.ndarray:

@@ -192,6 +192,26 @@ int infini_attn_backward_sequence(const infini_attn_state *st, const void *q, co
                                   void *dk, void *dv, float *dbeta, float *dM0, float *dz0,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * The layer: the projections on either side of the segment stream
+ * (section 3.1 of the page "精读笔记：Infini-attention": Q = X W_Q, K = X W_K,
+ * V = X W_V per head; section 3.6: O = [A^1; ...; A^H] W_O).  bf16 path only.
+ *
+ * x, y: [B, seq_len, d_model] bf16; w_qkv: [d_model, H (2 d_key + d_value)] bf16,
+ * its columns the H query heads (d_key each, head h at h d_key), then the H key
+ * heads, then the H value heads; w_o: [H d_value, d_model] bf16, its rows the
+ * heads' outputs in head order.  Runs y = concat_h(A_h) w_o with A_h the stream
+ * of head h over the projected q, k, v (forward_sequence semantics: the state
+ * advances by seq_len / segment_len segments).  d_model a multiple of 64;
+ * x, the weights and y 16-byte aligned; y must not alias the inputs, the state
+ * or the workspace.  The workspace holds the projected q, k, v, the heads'
+ * outputs and the forward's workspace.  Errors as for forward_sequence;
+ * INFINI_EUNSUPPORTED for the fp32 path. */
+size_t infini_attn_layer_workspace_bytes(const infini_attn_state *st, int32_t d_model, int64_t seq_len);
+int infini_attn_layer_forward(infini_attn_state *st, const void *x, int32_t d_model, const void *w_qkv,
+                              const void *w_o, int64_t seq_len, const float *beta, void *y,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* M, z <- 0 on `stream`; segments_done <- 0. */
 int infini_attn_reset(infini_attn_state *st, void *stream);
 

@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -265,6 +265,47 @@ def test_backward_rejects_bad_arguments(case):
     before = _snapshot(st)
     rc = ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, nbytes, None,
                               check=False)
+    assert rc == expect, (case, ia.last_error())
+    assert ia.last_error()
+    assert _snapshot(st) == before
+
+
+def test_layer_workspace_bytes():
+    st = _state()
+    L, BH, D = 2 * 2048, 2, 128
+    fwd = ia.workspace_bytes(st, L)
+    assert ia.layer_workspace_bytes(st, 1024, L) == 4 * BH * L * D * 2 + fwd
+    assert ia.layer_workspace_bytes(st, 1000, L) == 0
+    assert ia.layer_workspace_bytes(_state(dtype=ia.F32, d_key=32, d_value=32, segment_len=64), 64, 128) == 0
+
+
+@pytest.mark.parametrize("case", ["null_x", "bad_dmodel", "f32", "ragged", "misaligned", "small_ws", "alias_y",
+                                  "alias_ws"])
+def test_layer_rejects_bad_arguments(case):
+    st = _state()
+    L, dm = 2 * 2048, 1024
+    need = ia.layer_workspace_bytes(st, dm, L)
+    x, wq, wo, beta, y, ws, nbytes = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, FAKE * 9, need
+    expect = ia.EINVAL
+    if case == "null_x":
+        x = None
+    elif case == "bad_dmodel":
+        dm, expect = 1000, ia.EUNSUPPORTED
+    elif case == "f32":
+        st = _state(dtype=ia.F32, d_key=32, d_value=32, segment_len=64)
+        expect = ia.EUNSUPPORTED
+    elif case == "ragged":
+        L = 2048 + 64
+    elif case == "misaligned":
+        wq = FAKE * 5 + 8
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    elif case == "alias_y":
+        y = x + 4096
+    elif case == "alias_ws":
+        ws, expect = x + 256 * 16, ia.EWORKSPACE
+    before = _snapshot(st)
+    rc = ia.layer_forward(st, x, dm, wq, wo, L, beta, y, ws, nbytes, None, check=False)
     assert rc == expect, (case, ia.last_error())
     assert ia.last_error()
     assert _snapshot(st) == before
