@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="time infini_attn_backward_sequence over the workload (gradients of a forward from an "
                         "empty memory); prints its own JSON line")
+    p.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
+                   help="time infini_attn_layer_forward (QKV projection, stream, output projection) with model "
+                        "width D_MODEL (0: off); prints its own JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 launches), to calibrate "
                         "the HBM byte counters of a profiler against a known size")
@@ -338,6 +341,104 @@ def bench_backward(args):
     print(json.dumps(line), flush=True)
 
 
+def layer_flops(w, rule: str, d_model: int) -> int:
+    """Algorithmic FLOP of one layer call: the two projections (2 B L d_model
+    H (2 d_k + d_v) and 2 B L H d_v d_model), the fused kernel's and the state
+    stage's."""
+    H, dk, dv, BL = w.heads, w.d_key, w.d_value, w.batch * w.seq_len
+    proj = 2 * BL * d_model * H * (2 * dk + dv) + 2 * BL * H * dv * d_model
+    return proj + attention_flops(w) + state_flops(w, rule)
+
+
+def layer_cpu_baseline(w, rule: str, d_model: int, budget_s: float):
+    """The float64 layer oracle on the first segments of batch 0 (all heads),
+    doubling the number of segments until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from compressive_memory_transformer_amd import synthetic as syn
+    from oracle import infini_layer as ol
+
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    x, wq, wo = syn.layer_tensors(w, d_model)
+    beta = syn.betas(w)
+    spent, segs, n = 0.0, 0, 1
+    while spent < budget_s / 3 and n <= w.segments:
+        t0 = time.perf_counter()
+        ol.layer_forward(x[:1, :n * w.segment_len], wq, wo, beta, rule, w.segment_len, w.heads, w.d_key, w.d_value)
+        spent, segs = time.perf_counter() - t0, n
+        n *= 2
+    return {"value": segs * w.segment_len / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer over the first {segs} segments of batch 0 of {w.name}/{rule}, d_model {d_model}, "
+                      f"float64 numpy, {spent:.1f}s"}
+
+
+def bench_layer(args):
+    import numpy as np
+    import torch
+
+    from compressive_memory_transformer_amd import infini as ia
+    from compressive_memory_transformer_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    rule = args.rule or w.rules[0]
+    dm = args.layer
+    ia.load_library()
+    dev = [torch.from_numpy(t).to("cuda").to(torch.bfloat16) for t in syn.layer_tensors(w, dm)]
+    x, wq, wo = dev
+    beta = torch.from_numpy(syn.betas(w)).to("cuda")
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, w.dtype, rule)
+    y = torch.empty_like(x)
+    L = w.seq_len
+    need = ia.layer_workspace_bytes(eng.state, dm, L)
+    raw = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    ws = raw[(-raw.data_ptr()) % 256:][:need]
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        ia.reset(eng.state, sh)
+        ia.layer_forward(eng.state, x, dm, wq, wo, L, beta, y, ws, need, sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    fl = layer_flops(w, rule, dm)
+    tf = fl / gpu_s / 1e12
+    cpu = layer_cpu_baseline(w, rule, dm, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    line = {
+        "metric": "Infini-attention layer tokens/sec on 1 MI355X (projections + segment stream)",
+        "value": w.tokens * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"layer/{w.name}", "batch": w.batch, "heads": w.heads, "d_model": dm,
+                   "segment_len": w.segment_len, "segments": w.segments, "d_key": w.d_key, "d_value": w.d_value,
+                   "rule": rule, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "whole layer call (reset + 2 GEMMs + state stage + fused kernel)",
+                     "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "flops_per_step": fl,
+                     "avg_step_ms_on_stream": gpu_s * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_decode(args):
     import torch
 
@@ -443,6 +544,9 @@ def main():
         sys.exit(1)
     if args.backward:
         bench_backward(args)
+        return
+    if args.layer:
+        bench_layer(args)
         return
     if args.decode:
         bench_decode(args)
