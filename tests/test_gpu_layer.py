@@ -27,6 +27,8 @@ CASES = [
     ("d128_dm512", 42, 2, 4, 128, 256, 2, 512),
     # d_model = 192: the output projection's last 128-column tile is partial
     ("d128_dm192", 43, 1, 2, 128, 128, 3, 192),
+    # enough output tiles for the 256 x 256 GEMM tiling in both projections
+    ("d64_dm1024_big", 44, 2, 8, 64, 128, 64, 1024),
 ]
 
 
