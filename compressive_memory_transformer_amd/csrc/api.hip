@@ -589,6 +589,65 @@ int infini_attn_layer_forward(infini_attn_state* st, const void* x, int32_t d_mo
   return ok();
 }
 
+int infini_attn_kernel_linear_attention(infini_attn_state* st, const void* q, const void* k, const void* v,
+                                        int64_t seq_len, void* out, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  int rc = check_state(st);
+  if (rc != INFINI_OK) return rc;
+  if (st->dtype != INFINI_BF16) return fail(INFINI_EUNSUPPORTED, "kernel linear attention runs on the bf16 path only");
+  if (st->rule != INFINI_RULE_LINEAR)
+    return fail(INFINI_EINVAL, "kernel linear attention needs a state with the linear update rule");
+  if (!q || !k || !v || !out) return fail(INFINI_EINVAL, "q, k, v and out must be non-NULL");
+  if (seq_len <= 0 || seq_len % st->segment_len != 0)
+    return fail(INFINI_EINVAL, "seq_len (%lld) must be a positive multiple of segment_len (%d)",
+                (long long)seq_len, st->segment_len);
+  const int64_t S64 = seq_len / st->segment_len;
+  const int64_t BH = (int64_t)st->batch * st->heads;
+  if (S64 > 65535 || BH > 65535) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
+  int64_t rows, nqk;
+  if (!mul_ok(BH, seq_len, &rows) || !mul_ok(rows, st->d_key, &nqk))
+    return fail(INFINI_EINVAL, "tensor sizes overflow");
+  for (const void* p : {q, k, v, static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(INFINI_EINVAL, "q, k, v and out must be 16-byte aligned");
+  const size_t tb = (size_t)nqk * 2;
+  const size_t mb = (size_t)BH * st->d_key * st->d_value * 4, zb = (size_t)BH * st->d_key * 4;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
+      overlaps(out, tb, st->M, mb) || overlaps(out, tb, st->z, zb))
+    return fail(INFINI_EINVAL, "out must not alias q, k, v or the state");
+  WsLayout w;
+  if (!workspace_layout(st, S64, seq_len, &w)) return fail(INFINI_EINVAL, "workspace size overflows");
+  if (!workspace || workspace_bytes < w.total)
+    return fail(INFINI_EWORKSPACE, "workspace of %zu bytes required, %zu given%s", w.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(INFINI_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (overlaps(workspace, w.total, out, tb) || overlaps(workspace, w.total, st->M, mb) ||
+      overlaps(workspace, w.total, st->z, zb))
+    return fail(INFINI_EWORKSPACE, "workspace must not alias out or the state");
+
+  using infini::bf16;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int B = st->batch, H = st->heads, N = st->segment_len, S = (int)S64, D = st->d_key;
+  bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
+  float* snapz = reinterpret_cast<float*>(ws + w.snapz);
+  float* snapc = reinterpret_cast<float*>(ws + w.snapc);
+  infini::LinContribArgs c{static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                           reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz), B, H, S, N,
+                           seq_len};
+  hipError_t e = D == 128 ? infini::launch_lin_contrib<128>(c, strm) : infini::launch_lin_contrib<64>(c, strm);
+  if (e != hipSuccess) return hip_fail(e, "lin_contrib launch");
+  infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, snapc, B * H, S};
+  e = D == 128 ? infini::launch_lin_scan<128>(sarg, strm) : infini::launch_lin_scan<64>(sarg, strm);
+  if (e != hipSuccess) return hip_fail(e, "lin_scan launch");
+  infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), nullptr,
+                   snapM, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, seq_len, 0, st->segments_done, 0.f};
+  e = D == 128 ? infini::launch_kla<128>(f, strm) : infini::launch_kla<64>(f, strm);
+  if (e != hipSuccess) return hip_fail(e, "kernel linear attention launch");
+  st->segments_done += S64;
+  return ok();
+}
+
 int infini_attn_forward_segment(infini_attn_state* st, const void* q, const void* k, const void* v,
                                 const float* beta, void* out, void* workspace, size_t workspace_bytes,
                                 void* stream) {

@@ -198,6 +198,12 @@ template <int D> hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hi
 template <int D> hipError_t launch_backward_retrieval_grad_mfma(const BwdArgs& a, hipStream_t stream);
 template <int D> hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t stream);
 
+// ----------------------------------------------------- kernel linear attention
+// Causal kernel linear attention over chunks of N tokens, given every chunk's
+// starting state in snapM / snapz / snapc (the linear-rule state kernels' output);
+// beta, nq, seg_base and sc_log2 of FaArgs are not used.  N a multiple of 64.
+template <int D> hipError_t launch_kla(const FaArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- projections
 // C = A B in bf16 with fp32 accumulation; B row-major [K][N].  a_heads: A is the
 // heads' outputs [B, H, L, dv] read as [B L, H dv] (K = H dv); else row-major

@@ -1,0 +1,47 @@
+// MFMA operand helpers for v_mfma_f32_32x32x16_bf16 over row-major bf16 LDS
+// tiles (operand and accumulator layouts in common.h).
+#pragma once
+
+#include "common.h"
+
+namespace infini {
+
+// Row operand: lane l gets X[r0 + l % 32][k0 + 8 (l / 32) + 0..7] (an A operand, or
+// the B operand of a product with X^T).
+__device__ __forceinline__ bf16x8 mo_row(const bf16* X, int pitch, int r0, int k0, int lane) {
+  return lds_read8(X + (r0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
+}
+
+// Transposed operand in natural contraction order: lane l gets
+// X[r0 + 8 (l / 32) + e][c0 + l % 32], e = 0..7.
+__device__ __forceinline__ bf16x8 mo_col(const bf16* X, int pitch, int r0, int c0, int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 3, s = lane & 15;
+  return lds_operand_tr(X, pitch, r0 + 8 * h, r0 + 8 * h + 4, c0 + 16 * (g & 1), s);
+}
+
+// Transposed operand in the row order of a 32 x 32 accumulator used as the other
+// operand: lane l gets X[r0 + 4 h + e][c0 + l % 32] and X[r0 + 8 + 4 h + e][...].
+__device__ __forceinline__ bf16x8 mo_col_acc(const bf16* X, int pitch, int r0, int c0, int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 3, s = lane & 15;
+  return lds_operand_tr(X, pitch, r0 + 4 * h, r0 + 8 + 4 * h, c0 + 16 * (g & 1), s);
+}
+
+// Rows 8 ks .. 8 ks + 7 of an accumulator as a bf16 B operand.
+__device__ __forceinline__ bf16x8 mo_acc(const f32x16& c, int ks) {
+  bf16x8 b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = f2bf(c[8 * ks + j]);
+  return b;
+}
+
+__device__ __forceinline__ f32x16 mo_zero() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Row of accumulator element r for lane half h.
+__device__ __forceinline__ int mo_acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+}  // namespace infini

@@ -110,6 +110,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_layer_workspace_bytes.restype = sz
     lib.infini_attn_layer_forward.argtypes = [sp, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
     lib.infini_attn_layer_forward.restype = ctypes.c_int
+    lib.infini_attn_kernel_linear_attention.argtypes = [sp, vp, vp, vp, i64, vp, vp, sz, vp]
+    lib.infini_attn_kernel_linear_attention.restype = ctypes.c_int
     lib.infini_attn_reset.argtypes = [sp, vp]
     lib.infini_attn_reset.restype = ctypes.c_int
     lib.infini_attn_last_error.argtypes = []
@@ -223,6 +225,12 @@ def layer_forward(st: State, x, d_model, w_qkv, w_o, seq_len, beta, y, workspace
     return _check(rc) if check else rc
 
 
+def kernel_linear_attention(st: State, q, k, v, seq_len, out, workspace, ws_bytes, stream=None, check=True) -> int:
+    rc = load_library().infini_attn_kernel_linear_attention(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len,
+                                                            _ptr(out), _ptr(workspace), ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
 def reset(st: State, stream=None, check=True) -> int:
     rc = load_library().infini_attn_reset(ctypes.byref(st), stream)
     return _check(rc) if check else rc
@@ -325,6 +333,16 @@ class InfiniAttention:
             out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
         ws, nbytes = self.append_workspace(n)
         append(self.state, self.open, q, k, v, n, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
+        return out
+
+    def kernel_linear_attention(self, q, k, v, out=None, stream=None):
+        """Causal kernel linear attention over q.shape[2] tokens (linear-rule state;
+        its segment length is the chunk)."""
+        seq_len = q.shape[2]
+        if out is None:
+            out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
+        ws, nbytes = self.workspace(seq_len)
+        kernel_linear_attention(self.state, q, k, v, seq_len, out, ws, nbytes, _stream_handle(self.torch, stream))
         return out
 
     def layer_forward(self, x, w_qkv, w_o, beta, y=None, stream=None):

@@ -212,6 +212,22 @@ int infini_attn_layer_forward(infini_attn_state *st, const void *x, int32_t d_mo
                               const void *w_o, int64_t seq_len, const float *beta, void *y,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Causal kernel linear attention (section 24.4 of the page "第24章 Sparse与
+ * Infinite Attention"): out_i = phi(q_i)^T S_i / (phi(q_i)^T Z_i) with the
+ * prefix states S_i = M_0 + sum_{j <= i} phi(k_j) v_j^T and Z_i = z_0 +
+ * sum_{j <= i} phi(k_j) over the stream (phi = ELU + 1; the query's own key
+ * included).  The state carries (S, Z) across calls exactly as the linear rule
+ * carries (M, z): it must use INFINI_RULE_LINEAR, and its segment length is the
+ * chunk the kernels work in (any multiple of 64; the result does not depend on
+ * it beyond rounding).  q, k, v, out [B, H, seq_len, d] bf16, 16-byte aligned;
+ * seq_len a multiple of segment_len; the workspace of forward_sequence
+ * (infini_attn_workspace_bytes).  M, z end as S, Z of the last token and
+ * segments_done advances by seq_len / segment_len.  bf16 path only. */
+int infini_attn_kernel_linear_attention(infini_attn_state *st, const void *q, const void *k,
+                                        const void *v, int64_t seq_len, void *out, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
 /* M, z <- 0 on `stream`; segments_done <- 0. */
 int infini_attn_reset(infini_attn_state *st, void *stream);
 

@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -308,4 +308,32 @@ def test_layer_rejects_bad_arguments(case):
     rc = ia.layer_forward(st, x, dm, wq, wo, L, beta, y, ws, nbytes, None, check=False)
     assert rc == expect, (case, ia.last_error())
     assert ia.last_error()
+    assert _snapshot(st) == before
+
+
+@pytest.mark.parametrize("case", ["null_q", "f32", "delta", "ragged", "misaligned", "small_ws", "alias_out"])
+def test_kernel_linear_attention_rejects_bad_arguments(case):
+    st = _state()
+    L = 2 * 2048
+    need = ia.workspace_bytes(st, L)
+    q, k, v, out, ws, nbytes = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, need
+    expect = ia.EINVAL
+    if case == "null_q":
+        q = None
+    elif case == "f32":
+        st = _state(dtype=ia.F32, d_key=32, d_value=32, segment_len=64)
+        expect = ia.EUNSUPPORTED
+    elif case == "delta":
+        st = _state(rule=ia.RULE_DELTA)
+    elif case == "ragged":
+        L = 2048 + 64
+    elif case == "misaligned":
+        k = FAKE * 5 + 2
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    elif case == "alias_out":
+        out = v + 512
+    before = _snapshot(st)
+    rc = ia.kernel_linear_attention(st, q, k, v, L, out, ws, nbytes, None, check=False)
+    assert rc == expect, (case, ia.last_error())
     assert _snapshot(st) == before
