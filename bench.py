@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
                    help="time infini_attn_layer_forward (QKV projection, stream, output projection) with model "
                         "width D_MODEL (0: off); prints its own JSON line")
+    p.add_argument("--kla", type=int, default=0, metavar="CHUNK",
+                   help="time causal kernel linear attention over the workload's q, k, v with chunks of CHUNK "
+                        "tokens (0: off); prints its own JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 launches), to calibrate "
                         "the HBM byte counters of a profiler against a known size")
@@ -439,6 +442,115 @@ def bench_layer(args):
     print(json.dumps(line), flush=True)
 
 
+def kla_work(w, chunk: int):
+    """Algorithmic FLOP and HBM bytes of one causal kernel linear attention pass in
+    chunks of `chunk` tokens: per chunk and head, the weights and their product
+    with V over the causal pairs (2 (d_k + d_v) C (C + 1) / 2), the retrieval from
+    the chunk's starting state (2 C d_k d_v) and the chunk's contribution to the
+    state (2 C d_k d_v); bytes: q, k, v read and the output written once, plus one
+    starting state (bf16 M^T and two fp32 vectors) per chunk."""
+    C, dk, dv = chunk, w.d_key, w.d_value
+    chunks = w.batch * w.heads * (w.seq_len // C)
+    fl = chunks * ((dk + dv) * C * (C + 1) + 4 * C * dk * dv)
+    by = w.batch * w.heads * w.seq_len * (2 * dk + 2 * dv) * 2 + chunks * (dk * dv * 2 + 8 * dk)
+    return fl, by
+
+
+def kla_cpu_baseline(w, chunk: int, budget_s: float):
+    """The float64 oracle on the first tokens of one (batch, head), doubling the
+    length until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from compressive_memory_transformer_amd import synthetic as syn
+    from oracle import kernel_linear as kl
+
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    spent, segs, n = 0.0, 0, 1
+    while spent < budget_s / 3 and n <= w.segments:
+        q, k, v = (np.concatenate([syn.tile(w, i, 0, 0, s) for s in range(n)])[None, None].astype(np.float64)
+                   for i in (syn.Q_ID, syn.K_ID, syn.V_ID))
+        t0 = time.perf_counter()
+        kl.causal_kernel_linear_attention(q, k, v)
+        spent, segs = time.perf_counter() - t0, n
+        n *= 2
+    tokens = segs * w.segment_len / w.heads   # a token is all heads of one position
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {segs * w.segment_len} tokens of one (batch, head) of {w.name}, float64 numpy, "
+                      f"{spent:.1f}s"}
+
+
+def bench_kla(args):
+    import numpy as np
+    import torch
+
+    from compressive_memory_transformer_amd import infini as ia
+    from compressive_memory_transformer_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    C = args.kla
+    if w.seq_len % C != 0:
+        print(f"--kla {C} does not divide the workload's {w.seq_len} tokens", file=sys.stderr)
+        sys.exit(2)
+    ia.load_library()
+
+    def upload(tid):
+        return torch.from_numpy(syn.full_tensor(w, tid, as_bits=True).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    q, k, v = (upload(i) for i in (syn.Q_ID, syn.K_ID, syn.V_ID))
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, C, "bf16", "linear")
+    out = torch.empty_like(v)
+    L = w.seq_len
+    ws, nbytes = eng.workspace(L)
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        ia.reset(eng.state, sh)
+        ia.kernel_linear_attention(eng.state, q, k, v, L, out, ws, nbytes, sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    fl, by = kla_work(w, C)
+    tf, gbs = fl / gpu_s / 1e12, by / gpu_s / 1e9
+    mfma_bound = fl / by > MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
+    roof = ({"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": tf / MFMA_BF16_PEAK_TFLOPS} if mfma_bound else
+            {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS})
+    roof.update({"kernel": "whole call (reset + contributions + prefix scan + chunk kernel)", "traffic": None,
+                 "flops_per_step": fl, "bytes_per_step": by, "tflops": tf, "gbs": gbs,
+                 "avg_step_ms_on_stream": gpu_s * 1e3})
+    cpu = kla_cpu_baseline(w, C, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    line = {
+        "metric": "Causal kernel linear attention tokens/sec on 1 MI355X",
+        "value": w.tokens * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"kla/{w.name}", "batch": w.batch, "heads": w.heads, "chunk": C,
+                   "seq_len": w.seq_len, "d_key": w.d_key, "d_value": w.d_value, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_decode(args):
     import torch
 
@@ -547,6 +659,9 @@ def main():
         return
     if args.layer:
         bench_layer(args)
+        return
+    if args.kla:
+        bench_kla(args)
         return
     if args.decode:
         bench_decode(args)

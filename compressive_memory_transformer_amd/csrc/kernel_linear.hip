@@ -33,7 +33,6 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, hh = lane >> 5;
   __shared__ __attribute__((aligned(16))) bf16 kc[2][kKlChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 vc[2][kKlChunk * P];
-  __shared__ __attribute__((aligned(16))) bf16 mt[D * P];
   __shared__ float rk[2][kKlChunk], zsh[D], csh[D];
   const int64_t seg = (int64_t)bh * a.S + s;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
@@ -43,17 +42,11 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   const int64_t qrow = seg0 + min(qcol, a.N - 1);
   const int kend = min(a.N, q0 + kKlBlock);
 
-  // the chunk's starting state: M^T (bf16, rows = d_value), its column sums and z
-  {
-    const bf16* Mg = a.snapM + seg * D * D;
-    for (int x = t; x < D * D / 8; x += 64 * kKlWaves) {
-      const int r = x / (D / 8), c8 = x % (D / 8);
-      *reinterpret_cast<bf16x8*>(mt + r * P + 8 * c8) = *reinterpret_cast<const bf16x8*>(Mg + r * D + 8 * c8);
-    }
-    if (t < D) {
-      zsh[t] = a.snapz[seg * D + t];
-      csh[t] = a.snapc[seg * D + t];
-    }
+  // the chunk's starting state: column sums of M and z (M^T itself is read as an
+  // operand straight from memory at the end)
+  if (t < D) {
+    zsh[t] = a.snapz[seg * D + t];
+    csh[t] = a.snapc[seg * D + t];
   }
   // the lane's query: q' as the B operand (natural order), sum q', phi(q) . z later
   bf16x8 qm[KS];
@@ -73,7 +66,8 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   }
   rq += __shfl_xor(rq, 32);
 
-  // staging of one key chunk: k' into kc, v into vc, then the row sums of k'
+  // staging of one key chunk: k' into kc, v into vc, and the row sums of k' (the
+  // D / 8 threads of a row are consecutive lanes: a shuffle reduction)
   bf16x8 pk[PIECES], pv[PIECES];
   auto load = [&](int kc0) {
 #pragma unroll
@@ -88,20 +82,18 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
     for (int i = 0; i < PIECES; ++i) {
       const int p = t + 64 * kKlWaves * i, r = p / (D / 8), c8 = p % (D / 8);
       bf16x8 kp;
+      float rs = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float v = bf2f(pk[i][j]);
         kp[j] = f2bf(v > 0.f ? v : exp_e(v) - 1.f);
+        rs += bf2f(kp[j]);
       }
+#pragma unroll
+      for (int o = 1; o < D / 8; o <<= 1) rs += __shfl_xor(rs, o);
+      if (c8 == 0) rk[buf][r] = rs;
       *reinterpret_cast<bf16x8*>(kc[buf] + r * P + 8 * c8) = kp;
       *reinterpret_cast<bf16x8*>(vc[buf] + r * P + 8 * c8) = pv[i];
-    }
-  };
-  auto row_sums = [&](int buf) {
-    if (t < kKlChunk) {
-      float r = 0.f;
-      for (int c = 0; c < D; ++c) r += bf2f(kc[buf][t * P + c]);
-      rk[buf][t] = r;
     }
   };
 
@@ -111,8 +103,6 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   float den = 0.f;
   load(0);
   store(0);
-  __syncthreads();
-  row_sums(0);
   __syncthreads();
   for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kKlChunk, buf ^= 1) {
     const bool next = kc0 + kKlChunk < kend;
@@ -146,8 +136,6 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
     }
     if (next) store(buf ^ 1);
     __syncthreads();
-    if (next) row_sums(buf ^ 1);
-    __syncthreads();
   }
   // phi(q) . z of the starting state
   float dz = 0.f;
@@ -163,7 +151,11 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   for (int d = 0; d < DB; ++d) {
     f32x16 rt = mo_zero();
 #pragma unroll
-    for (int c = 0; c < KS; ++c) rt = mfma32(mo_row(mt, P, 32 * d, 16 * c, lane), qm[c], rt);
+    for (int c = 0; c < KS; ++c) {
+      // A operand: row 32 d + l % 32 of M^T (d_value), columns 16 c + 8 (l / 32) ..
+      const bf16x8 ma = *reinterpret_cast<const bf16x8*>(a.snapM + seg * D * D + (32 * d + l32) * D + 16 * c + 8 * hh);
+      rt = mfma32(ma, qm[c], rt);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int col = 32 * d + mo_acc_row(r, hh);
