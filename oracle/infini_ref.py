@@ -54,7 +54,8 @@ case or library routine, except the delta rule for s >= 2 with general V,
 which is pinned only through its special cases (delta = linear in the first
 segment, zero update when V equals the retrieved value, zero update for a
 re-written single pair, equality with the linear rule when all earlier V are
-zero, and affinity in V): beyond those special cases its parity is unpinned.
+zero, and affinity in V) and by its matrix form (I - A) M + sigma(K)^T V, a
+second computation of the same equation: beyond those its parity is unpinned.
 """
 
 from __future__ import annotations

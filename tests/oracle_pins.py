@@ -378,4 +378,22 @@ def pin_state_size_matches_table_1(o):
     assert per_head == dk * (dv + 1) == o.state_floats_per_head(dk, dv)
 
 
+
+def pin_delta_matrix_form(o):
+    """For any segment with a non-empty memory and general V, the delta update
+    equals M_s = (I - A) M_{s-1} + sigma(K)^T V with A = sigma(K)^T diag(1/e) sigma(K),
+    e_t = sigma(K_t) . z_{s-1}: the row-wise correction sigma(K)^T (sigma(K) M / e)
+    rewritten as one d_key x d_key operator (and A symmetric)."""
+    rng = np.random.default_rng(77)
+    for n, dk, dv in ((5, 3, 4), (16, 8, 8), (9, 6, 2)):
+        k, v = rng.standard_normal((n, dk)), rng.standard_normal((n, dv))
+        M = rng.standard_normal((dk, dv))
+        z = np.abs(rng.standard_normal(dk)) + 0.3
+        got, gz = o.update_delta(k, v, M, z, first=False)
+        fk = o.sigma(k)
+        A = fk.T @ np.diag(1.0 / (fk @ z)) @ fk
+        assert np.allclose(A, A.T, rtol=0, atol=1e-13)
+        assert np.allclose(got, (np.eye(dk) - A) @ M + fk.T @ v, rtol=1e-12, atol=1e-12)
+        assert np.allclose(gz, z + fk.sum(axis=0))
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
