@@ -88,3 +88,42 @@ def test_backward_matches_oracle(case, rule):
     worst["dbeta"] = e
     gh.log("  " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
     assert e <= tol, f"{name}/{rule} dbeta: error {e:.3e} ({gb} vs {want['dbeta']})"
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_full_size_sampled_head(rule):
+    """The 32K-token single-layer stream at its full size (the shape bench.py times):
+    one head's gradients over all 16 segments against the oracle (heads are
+    independent; with one batch row dbeta of that head is that head's alone)."""
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    w = syn.WORKLOADS["layer_32k_linear"]
+    h = 3
+    gh.log(f"backward full size {w.name} rule={rule}, head {h}")
+    q, k, v, beta = gh.device_inputs(w)
+    dout = gh.upload(w, syn.DOUT_ID)
+    dM, dz = syn.state_grads(w)
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, "bf16", rule)
+    zM, zz = torch.zeros_like(eng.M), torch.zeros_like(eng.z)
+    g = eng.backward_sequence(q, k, v, beta, dout, zM, zz, 0, dM=torch.from_numpy(dM).cuda(),
+                              dz=torch.from_numpy(dz).cuda())
+    torch.cuda.synchronize()
+    qn, kn, vn, don = (syn.full_tensor(w, i, heads=[h]) for i in (syn.Q_ID, syn.K_ID, syn.V_ID, syn.DOUT_ID))
+    want = og.backward_sequence(qn, kn, vn, syn.betas(w)[[h]], rule, w.segment_len, don, dM=dM[:, [h]],
+                                dz=dz[:, [h]])
+    N, worst = w.segment_len, {}
+    for key in ("dq", "dk", "dv"):
+        got = gh.to_host(g[key][:, h:h + 1])
+        for s in range(w.segments):
+            rows = slice(s * N, (s + 1) * N)
+            e = gh.metric(got[0, 0, rows], want[key][0, 0, rows], "bf16")
+            worst[key] = max(worst.get(key, 0.0), e)
+            assert e <= gh.tol("bf16"), f"{rule} {key} segment {s}: error {e:.3e}"
+    for key in ("dM0", "dz0"):
+        e = gh.metric(gh.to_host(g[key][:, h:h + 1]), want[key], "bf16")
+        worst[key] = e
+        assert e <= gh.tol("bf16"), f"{rule} {key}: error {e:.3e}"
+    gb, wb = float(gh.to_host(g["dbeta"])[h]), float(want["dbeta"][0])
+    worst["dbeta"] = abs(gb - wb) / max(abs(wb), 1e-30)
+    gh.log("  " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert worst["dbeta"] <= gh.tol("bf16")

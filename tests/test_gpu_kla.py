@@ -63,3 +63,30 @@ def test_kernel_linear_attention_matches_oracle(case):
     gh.log(f"  worst tile {worst:.3e}; S {eS:.3e}; Z {eZ:.3e}")
     assert eS <= gh.tol("bf16") and eZ <= gh.tol("bf16")
     assert eng.segments_done == S
+
+
+def test_full_size_prefix():
+    """The 32K-token stream with 8 heads in chunks of 256 (the shape bench.py --kla
+    256 times): the outputs of the first 4096 tokens of every head (they depend on
+    those tokens only) against the oracle."""
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    w = syn.WORKLOADS["layer_32k_linear"]
+    C, T = 256, 4096
+    gh.log(f"kla full size {w.name}, chunk {C}")
+    q, k, v, _ = gh.device_inputs(w)
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, C, "bf16", "linear")
+    out = eng.kernel_linear_attention(q, k, v)
+    torch.cuda.synchronize()
+    got = gh.to_host(out[:, :, :T])
+    seg = T // w.segment_len
+    qn, kn, vn = (syn.full_tensor(w, i, segments=seg) for i in (0, 1, 2))
+    want = kl.causal_kernel_linear_attention(qn, kn, vn)
+    worst = 0.0
+    for h in range(w.heads):
+        for c in range(T // C):
+            rows = slice(c * C, (c + 1) * C)
+            e = gh.metric(got[0, h, rows], want["O"][0, h, rows], "bf16")
+            worst = max(worst, e)
+            assert e <= gh.tol("bf16"), f"head {h} chunk {c}: error {e:.3e}"
+    gh.log(f"  worst tile {worst:.3e}")

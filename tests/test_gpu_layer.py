@@ -63,3 +63,27 @@ def test_layer_matches_oracle(case, rule):
     gh.log(f"  worst y tile {worst:.3e}; M {eM:.3e}; z {ez:.3e}")
     assert eM <= gh.tol("bf16") and ez <= gh.tol("bf16")
     assert eng.segments_done == S
+
+
+def test_full_size_layer():
+    """The 32K-token stream with d_model 1024 (the shape bench.py --layer 1024 times):
+    every output tile against the oracle."""
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    w = syn.WORKLOADS["layer_32k_linear"]
+    dm = 1024
+    gh.log(f"layer full size {w.name}, d_model {dm}")
+    x, wq, wo = syn.layer_tensors(w, dm)
+    beta = syn.betas(w)
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, "bf16", "linear")
+    y = eng.layer_forward(_bf16(torch, x), _bf16(torch, wq), _bf16(torch, wo), torch.from_numpy(beta).cuda())
+    torch.cuda.synchronize()
+    want = ol.layer_forward(x, wq, wo, beta, "linear", w.segment_len, w.heads, w.d_key, w.d_value)
+    got = gh.to_host(y)
+    N, worst = w.segment_len, 0.0
+    for s in range(w.segments):
+        rows = slice(s * N, (s + 1) * N)
+        e = gh.metric(got[0, rows], want["y"][0, rows], "bf16")
+        worst = max(worst, e)
+        assert e <= gh.tol("bf16"), f"y segment {s}: error {e:.3e}"
+    gh.log(f"  worst y tile {worst:.3e}")
