@@ -8,8 +8,9 @@
 // from the input) and reads the memory (M, z) as it stands, i.e. as of the
 // segment's start.  Both dtypes run in fp32 arithmetic.
 //
-// Split over keys and memory rows (the decode case has one query per head, up
-// to N keys and a 64 KiB memory per head at d = 128):
+// Appends of 64 or more tokens (bf16) take open_attn_mfma_kernel (below); the
+// rest split over keys and memory rows (the decode case has one query per head,
+// up to N keys and a 64 KiB memory per head at d = 128):
 //   open_attn_partial: one workgroup per (slot, group of 8 queries, head).  Slots
 //     below P are 128-key partitions: scores, the partition's maximum and sum,
 //     and its share of P V.  The R slots after them each take 16 rows of M and z:
@@ -21,6 +22,7 @@
 //     has read them, in stream order).
 #include "common.h"
 #include "kernels.h"
+#include "mfma_ops.h"
 
 namespace infini {
 
@@ -325,6 +327,177 @@ void open_attn_combine_kernel(OpenAttnArgs a) {
   if (t < a.dv) static_cast<T*>(a.vseg_out)[orow * a.dv + t] = static_cast<const T*>(a.vnew)[qrow * a.dv + t];
 }
 
+// Many queries at once (bf16, d_key = d_value = D): one workgroup (4 waves) per 128
+// of the m new queries, one wave per 32, the segment's keys up to the block's last
+// query in chunks of 64 (those before pos0 from the open-segment buffers, the new
+// ones from the input) staged through two LDS buffers.  Scores transposed (keys x
+// queries) with an online softmax per query column, then the retrieval from
+// (M, z) (M staged as bf16 with fp32 column sums, (sigma(q) - 1) as the operand),
+// the gate, and the new rows copied into the open segment.
+template <int D>
+__global__ __launch_bounds__(256) void open_attn_mfma_kernel(OpenAttnArgs a) {
+  constexpr int P = D + 8, KS = D / 16, DB = D / 32, CH = 64;
+  constexpr int PIECES = CH * D / 8 / 256;
+  const int qb = blockIdx.x, bh = blockIdx.y, h = bh % a.H;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, hh = lane >> 5;
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  const bf16* kseg = static_cast<const bf16*>(a.kseg);
+  const bf16* vseg = static_cast<const bf16*>(a.vseg);
+  const bf16* knew = static_cast<const bf16*>(a.knew);
+  const bf16* vnew = static_cast<const bf16*>(a.vnew);
+  __shared__ __attribute__((aligned(16))) bf16 kc[2][CH * P];
+  __shared__ __attribute__((aligned(16))) bf16 vc[2][CH * P];
+  __shared__ __attribute__((aligned(16))) bf16 ms[D * P];
+  __shared__ float msum[D], zsh[D];
+  const int j0 = qb * 128 + 32 * w;                  // the wave's first new query
+  const bool qvalid = j0 < a.m;
+  const int jq = min(j0 + l32, a.m - 1);             // the lane's query (column of S^T)
+  const int qpos = a.pos0 + j0 + l32;                // its position in the segment
+  const int64_t qrow = (int64_t)bh * a.q_stride + jq;
+  const int kend = min(a.pos0 + a.m, a.pos0 + qb * 128 + 128);   // keys the block's queries see
+  const float sl2 = a.scale * kLog2e;
+  if (a.has_memory) {
+    const float* Mg = a.M + (int64_t)bh * D * D;
+    for (int x = t; x < D * D; x += 256) ms[(x / D) * P + x % D] = f2bf(Mg[x]);
+    if (t < D) {
+      float cs = 0.f;
+      for (int r = 0; r < D; ++r) cs += Mg[r * D + t];
+      msum[t] = cs;
+      zsh[t] = a.z[(int64_t)bh * D + t];
+    }
+  }
+  bf16x8 qr[KS];
+#pragma unroll
+  for (int c = 0; c < KS; ++c) qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
+  // key row r of the segment (clamped to the last key; later ones are masked)
+  auto krow = [&](const bf16* seg, const bf16* nw, int r) -> const bf16* {
+    r = min(r, kend - 1);
+    return r < a.pos0 ? seg + ((int64_t)bh * a.N + r) * D : nw + ((int64_t)bh * a.q_stride + r - a.pos0) * D;
+  };
+  bf16x8 pk[PIECES], pv[PIECES];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = t + 256 * i, r = p / (D / 8), c8 = p % (D / 8);
+      pk[i] = *reinterpret_cast<const bf16x8*>(krow(kseg, knew, k0 + r) + 8 * c8);
+      pv[i] = *reinterpret_cast<const bf16x8*>(krow(vseg, vnew, k0 + r) + 8 * c8);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = t + 256 * i, r = p / (D / 8), c8 = p % (D / 8);
+      *reinterpret_cast<bf16x8*>(kc[buf] + r * P + 8 * c8) = pk[i];
+      *reinterpret_cast<bf16x8*>(vc[buf] + r * P + 8 * c8) = pv[i];
+    }
+  };
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = mo_zero();
+  float m2 = -__builtin_inff(), l = 0.f;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int k0 = 0, buf = 0; k0 < kend; k0 += CH, buf ^= 1) {
+    const bool next = k0 + CH < kend;
+    if (next) load(k0 + CH);
+    if (qvalid && k0 <= a.pos0 + j0 + 31) {
+      f32x16 sa[2] = {mo_zero(), mo_zero()};
+#pragma unroll
+      for (int c = 0; c < KS; ++c)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sa[kt] = mfma32(mo_row(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sa[kt]);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = k0 + 32 * kt + mo_acc_row(r, hh) <= qpos ? sa[kt][r] * sl2 : -__builtin_inff();
+          sa[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m2, mx);                // finite: key 0 is in the first chunk
+      const float alpha = exp2_fast(m2 - mn);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pe = exp2_fast(sa[kt][r] - mn);
+          sa[kt][r] = pe;
+          l += pe;
+        }
+      m2 = mn;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        pb[kt][0] = mo_acc(sa[kt], 0);
+        pb[kt][1] = mo_acc(sa[kt], 1);
+      }
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          o[d] = mfma32(mo_col_acc(vc[buf], P, 32 * kt, 32 * d, lane), pb[kt][0], o[d]);
+          o[d] = mfma32(mo_col_acc(vc[buf], P, 32 * kt + 16, 32 * d, lane), pb[kt][1], o[d]);
+        }
+    }
+    if (next) store(buf ^ 1);
+    __syncthreads();
+  }
+  const float inv_l = 1.f / (l + __shfl_xor(l, 32));
+  // retrieval: (colsum(M) + M^T (sigma(q) - 1)) / (sigma(q) . z); 0 in a stream's first segment
+  bf16x8 qm[KS];
+  float den = 0.f;
+#pragma unroll
+  for (int c = 0; c < KS; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = bf2f(qr[c][j]);
+      const float f = x > 0.f ? x : exp_e(x) - 1.f;
+      qm[c][j] = f2bf(f);
+      if (a.has_memory) den = __builtin_fmaf(f + 1.f, zsh[16 * c + 8 * hh + j], den);
+    }
+  den += __shfl_xor(den, 32);
+  const float g = sigmoid_gate(a.beta[h]);
+  const float wm = a.has_memory && den > 0.f ? g / den : 0.f;
+  const float wd = (1.f - g) * inv_l;
+  if (!qvalid) return;
+  bf16* out = static_cast<bf16*>(a.out);
+  const bool mine = j0 + l32 < a.m;
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    f32x16 am = mo_zero();
+    if (a.has_memory) {
+#pragma unroll
+      for (int c = 0; c < KS; ++c) am = mfma32(mo_col(ms, P, 16 * c, 32 * d, lane), qm[c], am);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int col = 32 * d + mo_acc_row(r, hh);
+      const float mem = a.has_memory ? msum[col] + am[r] : 0.f;
+      if (mine) out[qrow * D + col] = f2bf(__builtin_fmaf(o[d][r], wd, mem * wm));
+    }
+  }
+  // the new key and value rows join the open segment (rows pos0 + j; the reads of
+  // this launch take new keys from the input, so these writes race with none)
+  if (mine) {
+    const int64_t orow = (int64_t)bh * a.N + a.pos0 + jq;
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.kseg_out) + orow * D + 16 * c + 8 * hh) =
+          *reinterpret_cast<const bf16x8*>(knew + qrow * D + 16 * c + 8 * hh);
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.vseg_out) + orow * D + 16 * c + 8 * hh) =
+          *reinterpret_cast<const bf16x8*>(vnew + qrow * D + 16 * c + 8 * hh);
+    }
+  }
+}
+
 int open_attn_slots(int keys, int dk) {
   return (keys + kOpenThreads - 1) / kOpenThreads + (dk + kMemRows - 1) / kMemRows;
 }
@@ -335,6 +508,13 @@ hipError_t launch_open_attn(const OpenAttnArgs& args, hipStream_t stream) {
   if (a.dk > 128 || a.dv > 128 || a.pos0 + a.m > a.N) return hipErrorInvalidValue;
   a.P = (a.pos0 + a.m + kOpenThreads - 1) / kOpenThreads;
   a.R = a.has_memory ? (a.dk + kMemRows - 1) / kMemRows : 0;
+  if (a.bf16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) && a.m >= 64) {
+    // many queries: the MFMA kernel (no partial results, one launch)
+    const dim3 grid((unsigned)((a.m + 127) / 128), (unsigned)a.BH);
+    if (a.dk == 128) hipLaunchKernelGGL(open_attn_mfma_kernel<128>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(open_attn_mfma_kernel<64>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const bool one = a.m == 1;
   const dim3 gp((unsigned)(a.P + a.R), (unsigned)(one ? 1 : (a.m + kOpenQ - 1) / kOpenQ), (unsigned)a.BH);
   const dim3 gc((unsigned)a.m, (unsigned)a.BH);
