@@ -49,6 +49,13 @@
  *
  * Threads.  One state must not be used from two threads or two streams at once.
  * The counter segments_done advances on the host at enqueue time.
+ *
+ * Entry points beyond the segment stream (each documented at its declaration):
+ * the open segment (tokens in any number per call, single-token decode, ragged
+ * tails: infini_attn_open_segment_init / _append_workspace_bytes / _append), the
+ * gradients of a forward_sequence call (infini_attn_backward_sequence), the
+ * layer with its Q/K/V and output projections (infini_attn_layer_forward) and
+ * causal kernel linear attention on the same state (infini_attn_kernel_linear_attention).
  */
 #ifndef INFINI_ATTN_H
 #define INFINI_ATTN_H
