@@ -107,3 +107,40 @@ def test_whole_segments_take_the_segment_path(rule):
     assert torch.equal(out_a, out_b)
     assert torch.equal(a.M, b.M) and torch.equal(a.z, b.z)
     assert a.segments_done == b.segments_done == 2 and a.filled == 0
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_full_size_decode_shape(rule):
+    """The shape bench.py --decode 1024 times: the 32K-token stream's first 15
+    segments through forward_sequence, then 1024 tokens of the last segment in one
+    append (the many-query path) and 10 single-token appends; one head's outputs
+    of the open segment, the state and the open buffers against the oracle."""
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    w = syn.WORKLOADS["layer_32k_linear"]
+    N, h, F, T = w.segment_len, 5, 1024, 10
+    L0 = (w.segments - 1) * N
+    gh.log(f"open segment full size {w.name} rule={rule}, head {h}")
+    q, k, v, beta = gh.device_inputs(w)
+    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, N, "bf16", rule)
+    eng.forward_sequence(q[:, :, :L0].contiguous(), k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), beta)
+    eng.open_stream()
+    outs = [eng.append(*(x[:, :, L0:L0 + F].contiguous() for x in (q, k, v)), beta)]
+    for i in range(T):
+        sl = slice(L0 + F + i, L0 + F + i + 1)
+        outs.append(eng.append(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(), v[:, :, sl].contiguous(), beta))
+    torch.cuda.synchronize()
+    got = gh.to_host(torch.cat(outs, dim=2)[:, h:h + 1])
+    qn, kn, vn = (syn.full_tensor(w, i, heads=[h]) for i in (0, 1, 2))
+    bn = syn.betas(w)[[h]]
+    pre = ref.forward_sequence(qn[:, :, :L0], kn[:, :, :L0], vn[:, :, :L0], bn, rule, N)
+    sl = slice(L0, L0 + F + T)
+    res = ref.forward_stream(qn[:, :, sl], kn[:, :, sl], vn[:, :, sl], bn, rule, N, M0=pre["M"], z0=pre["z"],
+                             segments_done=w.segments - 1)
+    e_big = gh.metric(got[0, 0, :F], res["A"][0, 0, :F], "bf16")
+    e_dec = gh.metric(got[0, 0, F:], res["A"][0, 0, F:], "bf16")
+    eM = gh.metric(gh.to_host(eng.M)[:, h:h + 1], res["M"], "bf16")
+    gh.log(f"  1024-token append {e_big:.3e}; decode steps {e_dec:.3e}; M {eM:.3e}")
+    assert e_big <= gh.tol("bf16") and e_dec <= gh.tol("bf16") and eM <= gh.tol("bf16")
+    assert eng.filled == F + T and eng.segments_done == w.segments - 1
+    assert torch.equal(eng.k_open[:, :, :F + T], k[:, :, L0:L0 + F + T])
