@@ -331,7 +331,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) 
   const bf16* DO = static_cast<const bf16*>(a.dout);
   __shared__ __attribute__((aligned(16))) bf16 qc[2][kChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 dc[2][kChunk * P];
-  __shared__ float lc[2][kChunk], dcr[2][kChunk];
+  __shared__ __attribute__((aligned(16))) float lc[2][kChunk];
+  __shared__ __attribute__((aligned(16))) float dcr[2][kChunk];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int j0 = kb * kBwdBlock, kw0 = j0 + 32 * w;
   const bool kvalid = kw0 < a.N;
@@ -382,14 +383,21 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) 
       bf16x8 pb[2][2], db[2][2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
+        // the rows' log-normalisers and D: accumulator rows come in runs of four
+        f32x4 lq[4], dq4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lq[j] = *reinterpret_cast<const f32x4*>(&lc[buf][32 * qt + 8 * j + 4 * hh]);
+          dq4[j] = *reinterpret_cast<const f32x4*>(&dcr[buf][32 * qt + 8 * j + 4 * hh]);
+        }
         f32x16 ds;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int il = 32 * qt + acc_row(r, hh);
           const bool vis = kcol <= qc0 + il;
-          const float p = vis ? exp2_fast(sa[qt][r] * sl2 - lc[buf][il]) : 0.f;
+          const float p = vis ? exp2_fast(sa[qt][r] * sl2 - lq[r >> 2][r & 3]) : 0.f;
           sa[qt][r] = p;
-          ds[r] = p * ((1.f - g) * pa[qt][r] - dcr[buf][il]);
+          ds[r] = p * ((1.f - g) * pa[qt][r] - dq4[r >> 2][r & 3]);
         }
         pb[qt][0] = acc_op(sa[qt], 0);
         pb[qt][1] = acc_op(sa[qt], 1);

@@ -33,7 +33,8 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, hh = lane >> 5;
   __shared__ __attribute__((aligned(16))) bf16 kc[2][kKlChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 vc[2][kKlChunk * P];
-  __shared__ float rk[2][kKlChunk], zsh[D], csh[D];
+  __shared__ __attribute__((aligned(16))) float rk[2][kKlChunk];
+  __shared__ float zsh[D], csh[D];
   const int64_t seg = (int64_t)bh * a.S + s;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int q0 = qb * kKlBlock, qw0 = q0 + 32 * w;
@@ -116,10 +117,14 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
       bf16x8 pb[2][2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        // the keys' row sums: accumulator rows come in runs of four
+        f32x4 rk4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rk4[j] = *reinterpret_cast<const f32x4*>(&rk[buf][32 * kt + 8 * j + 4 * hh]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kl = 32 * kt + mo_acc_row(r, hh);
-          const float wv = kc0 + kl <= qcol ? (float)D + rk[buf][kl] + rq + sa[kt][r] : 0.f;
+          const float wv = kc0 + kl <= qcol ? (float)D + rk4[r >> 2][r & 3] + rq + sa[kt][r] : 0.f;
           sa[kt][r] = wv;
           den += wv;
         }
