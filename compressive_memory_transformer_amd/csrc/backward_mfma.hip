@@ -27,6 +27,7 @@
 // before the current chunk's products.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_ops.h"
 
 namespace infini {
 
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 kc[2][kChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 vc[2][kChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
-  __shared__ float msum[D], zsh[D];
+  __shared__ float msum[D], zsh[D], ctmp[128];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int q0 = qb * kBwdBlock, qw0 = q0 + 32 * w;
   const bool has_mem = a.seg_base + s > 0;
@@ -128,12 +129,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   {
     const float* Mg = a.snapM + ((int64_t)bh * a.S + s) * D * D;
     for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) ms[(x / D) * P + x % D] = f2bf(Mg[x]);
-    if (threadIdx.x < D) {
-      float cs = 0.f;
-      for (int r = 0; r < D; ++r) cs += Mg[r * D + threadIdx.x];
-      msum[threadIdx.x] = cs;
-      zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
-    }
+    if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
+    block_colsum256(Mg, D, D, msum, ctmp);
   }
 
   // ---- first sweep: maximum, sum and A_dot^T of the wave's 32 query columns
@@ -446,14 +443,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(Bwd
   const bf16* K = static_cast<const bf16*>(a.k);
   const bf16* V = static_cast<const bf16*>(a.v);
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
-  __shared__ float gsum[D];
+  __shared__ float gsum[D], ctmp[128];
   const float* Gg = a.dMr + ((int64_t)bh * a.S + s) * D * D;
   for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) gs[(x / D) * P + x % D] = f2bf(Gg[x]);
-  if (threadIdx.x < D) {
-    float cs = 0.f;
-    for (int r = 0; r < D; ++r) cs += Gg[r * D + threadIdx.x];
-    gsum[threadIdx.x] = cs;
-  }
+  block_colsum256(Gg, D, D, gsum, ctmp);
   const int t0 = rb * kBwdBlock + 32 * w;           // the wave's first token in the segment
   const bool valid = t0 < a.N;
   const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
@@ -632,7 +625,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
   const bf16* V = static_cast<const bf16*>(a.v);
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
   __shared__ __attribute__((aligned(16))) bf16 msb[D * P];
-  __shared__ float gsum[D], msum[D], zsh[D];
+  __shared__ float gsum[D], msum[D], zsh[D], ctmp[128], ctmp2[128];
   const int64_t seg = (int64_t)bh * a.S + s;
   const float* Gg = a.dMr + seg * D * D;
   const float* Mg = a.snapM + seg * D * D;
@@ -640,16 +633,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
     gs[(x / D) * P + x % D] = f2bf(Gg[x]);
     msb[(x / D) * P + x % D] = f2bf(Mg[x]);
   }
-  if (threadIdx.x < D) {
-    float cg = 0.f, cm = 0.f;
-    for (int r = 0; r < D; ++r) {
-      cg += Gg[r * D + threadIdx.x];
-      cm += Mg[r * D + threadIdx.x];
-    }
-    gsum[threadIdx.x] = cg;
-    msum[threadIdx.x] = cm;
-    zsh[threadIdx.x] = a.snapz[seg * D + threadIdx.x];
-  }
+  if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[seg * D + threadIdx.x];
+  block_colsum256(Gg, D, D, gsum, ctmp);
+  block_colsum256(Mg, D, D, msum, ctmp2);
   const bool first = a.seg_base + s == 0;
   const int t0 = rb * kBwdBlock + 32 * w;
   const bool valid = t0 < a.N;

@@ -44,4 +44,28 @@ __device__ __forceinline__ f32x16 mo_zero() {
 // Row of accumulator element r for lane half h.
 __device__ __forceinline__ int mo_acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Column sums of a row-major fp32 [R][C] matrix in global memory (C <= 128) by a
+// workgroup of 256 threads: threads t and t + 128 take alternate rows of column
+// t % 128 with four loads in flight each, and meet in `tmp` (128 floats of LDS).
+// Call from every thread; out[c] (c < C) is written by threads c < C after the
+// internal barrier (readers need a barrier of their own).
+__device__ __forceinline__ void block_colsum256(const float* X, int R, int C, float* out, float* tmp) {
+  const int t = threadIdx.x, c = t & 127, half = t >> 7;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if (c < C) {
+    int r = half;
+    for (; r + 6 < R; r += 8) {
+      a0 += X[(int64_t)r * C + c];
+      a1 += X[(int64_t)(r + 2) * C + c];
+      a2 += X[(int64_t)(r + 4) * C + c];
+      a3 += X[(int64_t)(r + 6) * C + c];
+    }
+    for (; r < R; r += 2) a0 += X[(int64_t)r * C + c];
+  }
+  const float sum = (a0 + a1) + (a2 + a3);
+  if (half == 1) tmp[c] = sum;
+  __syncthreads();
+  if (half == 0 && c < C) out[c] = sum + tmp[c];
+}
+
 }  // namespace infini

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void open_attn_mfma_kernel(OpenAttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 kc[2][CH * P];
   __shared__ __attribute__((aligned(16))) bf16 vc[2][CH * P];
   __shared__ __attribute__((aligned(16))) bf16 ms[D * P];
-  __shared__ float msum[D], zsh[D];
+  __shared__ float msum[D], zsh[D], ctmp[128];
   const int j0 = qb * 128 + 32 * w;                  // the wave's first new query
   const bool qvalid = j0 < a.m;
   const int jq = min(j0 + l32, a.m - 1);             // the lane's query (column of S^T)
@@ -356,15 +356,11 @@ __global__ __launch_bounds__(256) void open_attn_mfma_kernel(OpenAttnArgs a) {
   const int64_t qrow = (int64_t)bh * a.q_stride + jq;
   const int kend = min(a.pos0 + a.m, a.pos0 + qb * 128 + 128);   // keys the block's queries see
   const float sl2 = a.scale * kLog2e;
-  if (a.has_memory) {
+  if (a.has_memory) {   // uniform over the workgroup
     const float* Mg = a.M + (int64_t)bh * D * D;
     for (int x = t; x < D * D; x += 256) ms[(x / D) * P + x % D] = f2bf(Mg[x]);
-    if (t < D) {
-      float cs = 0.f;
-      for (int r = 0; r < D; ++r) cs += Mg[r * D + t];
-      msum[t] = cs;
-      zsh[t] = a.z[(int64_t)bh * D + t];
-    }
+    if (t < D) zsh[t] = a.z[(int64_t)bh * D + t];
+    block_colsum256(Mg, D, D, msum, ctmp);
   }
   bf16x8 qr[KS];
 #pragma unroll
