@@ -269,13 +269,19 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
           pa[kt] = mfma32(row_op(vc[buf], P, 32 * kt, 16 * c, lane), dr[c], pa[kt]);
         }
       bf16x8 db[2][2];
+      const bool below = kc0 + kChunk - 1 <= qw0;   // every key of the chunk precedes every query
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        if (below) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool vis = kc0 + 32 * kt + acc_row(r, hh) <= qcol;
-          const float p = vis ? exp2_fast(sa[kt][r] * sl2 - lse2) : 0.f;
-          sa[kt][r] = p * ((1.f - g) * pa[kt][r] - Dv);
+          for (int r = 0; r < 16; ++r) sa[kt][r] = exp2_fast(sa[kt][r] * sl2 - lse2) * ((1.f - g) * pa[kt][r] - Dv);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool vis = kc0 + 32 * kt + acc_row(r, hh) <= qcol;
+            const float p = vis ? exp2_fast(sa[kt][r] * sl2 - lse2) : 0.f;
+            sa[kt][r] = p * ((1.f - g) * pa[kt][r] - Dv);
+          }
         }
         db[kt][0] = acc_op(sa[kt], 0);
         db[kt][1] = acc_op(sa[kt], 1);
@@ -368,6 +374,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) 
     // both 32-query halves of the chunk at once (a chunk wholly before the wave's
     // keys is skipped)
     if (kvalid && qc0 + kChunk - 1 >= kw0) {
+      const bool below = qc0 >= kw0 + 31;   // wave-uniform
       f32x16 sa[2] = {zero16(), zero16()}, pa[2] = {zero16(), zero16()};
 #pragma unroll
       for (int c = 0; c < KS; ++c)
@@ -388,13 +395,22 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) 
           dq4[j] = *reinterpret_cast<const f32x4*>(&dcr[buf][32 * qt + 8 * j + 4 * hh]);
         }
         f32x16 ds;
+        if (below) {   // every query of the chunk follows every key of the wave
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int il = 32 * qt + acc_row(r, hh);
-          const bool vis = kcol <= qc0 + il;
-          const float p = vis ? exp2_fast(sa[qt][r] * sl2 - lq[r >> 2][r & 3]) : 0.f;
-          sa[qt][r] = p;
-          ds[r] = p * ((1.f - g) * pa[qt][r] - dq4[r >> 2][r & 3]);
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(sa[qt][r] * sl2 - lq[r >> 2][r & 3]);
+            sa[qt][r] = p;
+            ds[r] = p * ((1.f - g) * pa[qt][r] - dq4[r >> 2][r & 3]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int il = 32 * qt + acc_row(r, hh);
+            const bool vis = kcol <= qc0 + il;
+            const float p = vis ? exp2_fast(sa[qt][r] * sl2 - lq[r >> 2][r & 3]) : 0.f;
+            sa[qt][r] = p;
+            ds[r] = p * ((1.f - g) * pa[qt][r] - dq4[r >> 2][r & 3]);
+          }
         }
         pb[qt][0] = acc_op(sa[qt], 0);
         pb[qt][1] = acc_op(sa[qt], 1);
