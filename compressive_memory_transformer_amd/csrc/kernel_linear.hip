@@ -109,6 +109,7 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
     const bool next = kc0 + kKlChunk < kend;
     if (next) load(kc0 + kKlChunk);
     if (qvalid && kc0 <= qw0 + 31) {   // a chunk wholly after the wave's queries is skipped
+      const bool below = kc0 + kKlChunk - 1 <= qw0;
       f32x16 sa[2] = {mo_zero(), mo_zero()};
 #pragma unroll
       for (int c = 0; c < KS; ++c)
@@ -121,12 +122,21 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
         f32x4 rk4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) rk4[j] = *reinterpret_cast<const f32x4*>(&rk[buf][32 * kt + 8 * j + 4 * hh]);
+        if (below) {   // every key of the chunk precedes every query of the wave
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = 32 * kt + mo_acc_row(r, hh);
-          const float wv = kc0 + kl <= qcol ? (float)D + rk4[r >> 2][r & 3] + rq + sa[kt][r] : 0.f;
-          sa[kt][r] = wv;
-          den += wv;
+          for (int r = 0; r < 16; ++r) {
+            const float wv = (float)D + rk4[r >> 2][r & 3] + rq + sa[kt][r];
+            sa[kt][r] = wv;
+            den += wv;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kl = 32 * kt + mo_acc_row(r, hh);
+            const float wv = kc0 + kl <= qcol ? (float)D + rk4[r >> 2][r & 3] + rq + sa[kt][r] : 0.f;
+            sa[kt][r] = wv;
+            den += wv;
+          }
         }
         pb[kt][0] = mo_acc(sa[kt], 0);
         pb[kt][1] = mo_acc(sa[kt], 1);
