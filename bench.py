@@ -4,13 +4,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rule RULE]
 
 One step = one pass of the whole path over one batch of the workload's synthetic
-stream: reset the state, then forward_sequence over all segments of every head
-(memory-state stage + fused attention/retrieval/gate stage), inputs resident in
-HBM.  The timed region is K steps bracketed by device synchronisation.  Prints
-one JSON line with the whole-job tokens/s, the roofline position of the
+stream for each update rule the workload names (the default, the 500K-token
+stream over 32 heads, names both): reset the rule's state, then forward_sequence
+over all segments of every head (memory-state stage + fused
+attention/retrieval/gate stage), inputs resident in HBM.  The timed region is K
+steps bracketed by device synchronisation.  Prints one JSON line with the
+whole-job tokens/s (tokens of every rule's pass), the roofline position of the
 dominant kernel (the fused attention kernel, timed live with HIP events around
-its stage on the stream it runs on) and the float64 oracle timed on the host
-cores over a bounded prefix of the same stream.
+its stage on the stream it runs on), a per-rule breakdown and the float64 oracle
+timed on the host cores over a bounded prefix of the same stream.
 """
 
 from __future__ import annotations
@@ -39,10 +41,13 @@ DOMINANT_SOURCES = ["compressive_memory_transformer_amd/csrc/fa_fwd.hip",
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="layer_32k_linear")
-    p.add_argument("--rule", default=None)
+    p.add_argument("--workload", default=None,
+                   help="synthetic workload (default: the 500K-token stream over 32 heads; the 32K-token "
+                        "stream for --decode, --backward, --layer and --kla)")
+    p.add_argument("--rule", default=None,
+                   help="update rule to time (default: every rule the workload names, one pass each per step)")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="budget of the oracle leg (0 disables it)")
     p.add_argument("--decode", type=int, default=0, metavar="FILLED",
@@ -150,38 +155,56 @@ def traffic_for(workload: str, rule: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def cpu_baseline(w, rule: str, budget_s: float):
-    """The float64 oracle on the host over a prefix of the same stream: segments in
-    order, all heads of a segment before the next, until the budget is spent."""
+def blas_info() -> str:
+    """The BLAS library numpy runs on and its thread count."""
+    from threadpoolctl import threadpool_info
+    libs = [f"{i.get('internal_api', '?')} {i.get('version', '')} ({i.get('num_threads', 1)} threads)"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    return ", ".join(libs) or "unknown"
+
+
+def cpu_baseline(w, rules, budget_s: float):
+    """The float64 oracle on the host over a prefix of the same stream, for each
+    rule with an equal share of the budget: segments in order, all heads of a
+    segment before the next, until the rule's share is spent.  The value is the
+    tokens of all rules over the time of all rules (the rate of the GPU step's
+    mix)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from compressive_memory_transformer_amd import synthetic as syn
     from oracle import infini_ref as ref
 
+    if isinstance(rules, str):
+        rules = [rules]
     threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     sc = ref.default_scale(w.d_key)
     betas = syn.betas(w)
-    M = {(b, h): np.zeros((w.d_key, w.d_value)) for b in range(w.batch) for h in range(w.heads)}
-    z = {key: np.zeros(w.d_key) for key in M}
-    done = 0
-    spent = 0.0
-    for s in range(w.segments):
-        for (b, h) in M:
-            q, k, v = (syn.tile(w, i, b, h, s).astype(np.float64) for i in (0, 1, 2))
-            t0 = time.perf_counter()
-            _, M[(b, h)], z[(b, h)], _, _ = ref.segment_forward(q, k, v, M[(b, h)], z[(b, h)], float(betas[h]),
-                                                                rule, s == 0, sc)
-            spent += time.perf_counter() - t0
-            done += 1
-            if spent >= budget_s:
+    total_tok, total_s, samples = 0.0, 0.0, []
+    for rule in rules:
+        share = budget_s / len(rules)
+        M = {(b, h): np.zeros((w.d_key, w.d_value)) for b in range(w.batch) for h in range(w.heads)}
+        z = {key: np.zeros(w.d_key) for key in M}
+        done = 0
+        spent = 0.0
+        for s in range(w.segments):
+            for (b, h) in M:
+                q, k, v = (syn.tile(w, i, b, h, s).astype(np.float64) for i in (0, 1, 2))
+                t0 = time.perf_counter()
+                _, M[(b, h)], z[(b, h)], _, _ = ref.segment_forward(q, k, v, M[(b, h)], z[(b, h)],
+                                                                    float(betas[h]), rule, s == 0, sc)
+                spent += time.perf_counter() - t0
+                done += 1
+                if spent >= share:
+                    break
+            if spent >= share:
                 break
-        if spent >= budget_s:
-            break
-    tokens = done * w.segment_len / w.heads
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.batch * w.heads * w.segments} (batch, head, segment) tiles of {w.name}/{rule}, "
-                      f"in stream order, float64 numpy, {spent:.1f}s"}
+        total_tok += done * w.segment_len / w.heads
+        total_s += spent
+        samples.append(f"{done} of {w.batch * w.heads * w.segments} (batch, head, segment) tiles of "
+                       f"{w.name}/{rule} in stream order ({spent:.1f}s)")
+    return {"value": total_tok / total_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(samples) + f"; float64 numpy on {blas_info()}"}
 
 
 def decode_bytes(w, filled: int, steps: int) -> int:
@@ -654,6 +677,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload is None:
+        side = args.backward or args.layer or args.kla or args.decode
+        args.workload = "layer_32k_linear" if side else "wide_500k"
     if args.backward:
         bench_backward(args)
         return
@@ -667,7 +693,7 @@ def main():
         bench_decode(args)
         return
     w = syn.WORKLOADS[args.workload]
-    rule = args.rule or w.rules[0]
+    rules = [args.rule] if args.rule else list(w.rules)
     ia.load_library()
 
     def upload(tid):
@@ -677,11 +703,14 @@ def main():
             return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to("cuda")
         return torch.from_numpy(arr).to("cuda")
 
+    t_in = time.perf_counter()
     q, k, v = (upload(i) for i in (0, 1, 2))
     beta = torch.from_numpy(syn.betas(w)).to("cuda")
-    eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, w.dtype, rule)
+    print(f"inputs of {w.name} on the device in {time.perf_counter() - t_in:.1f}s", file=sys.stderr, flush=True)
+    # one engine (state + workspace) per rule; the output buffer is shared
+    engs = {r: ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, w.dtype, r) for r in rules}
     out = torch.empty((w.batch, w.heads, w.seq_len, w.d_value), dtype=q.dtype, device="cuda")
-    ws, ws_bytes = eng.workspace(w.seq_len)
+    wss = {r: engs[r].workspace(w.seq_len) for r in rules}
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
     hip = hip_runtime()
@@ -689,40 +718,68 @@ def main():
     # event record costs a few microseconds of GPU time, so stamping every step
     # would slow down the very steps being timed.
     prof_steps = [i for i in range(args.steps) if i % PROFILE_EVERY == 0]
-    ev = Events(hip, 3 * len(prof_steps))
+    ev = Events(hip, 3 * len(prof_steps) * len(rules))
 
-    def step(events=None):
-        ia.reset(eng.state, sh)
-        if events is None:
-            ia.forward_sequence(eng.state, q, k, v, w.seq_len, beta, out, ws, ws_bytes, sh)
-        else:
-            ia.forward_sequence_profiled(eng.state, q, k, v, w.seq_len, beta, out, ws, ws_bytes, sh, events)
+    def step(j=None):
+        """One pass of the path: for each rule, reset its state and stream the whole
+        workload through forward_sequence."""
+        for ri, r in enumerate(rules):
+            eng = engs[r]
+            ws, ws_bytes = wss[r]
+            ia.reset(eng.state, sh)
+            if j is None:
+                ia.forward_sequence(eng.state, q, k, v, w.seq_len, beta, out, ws, ws_bytes, sh)
+            else:
+                b = 3 * (j * len(rules) + ri)
+                ia.forward_sequence_profiled(eng.state, q, k, v, w.seq_len, beta, out, ws, ws_bytes, sh,
+                                             ev.ev[b:b + 3])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        j = i // PROFILE_EVERY
-        step(ev.ev[3 * j:3 * j + 3] if i % PROFILE_EVERY == 0 else None)
+        step(i // PROFILE_EVERY if i % PROFILE_EVERY == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     wall = t1 - t0
-    tokens = w.batch * w.seq_len
-    fa_ms = [ev.elapsed_ms(3 * j + 1, 3 * j + 2) for j in range(len(prof_steps))]
-    st_ms = [ev.elapsed_ms(3 * j, 3 * j + 1) for j in range(len(prof_steps))]
+    tokens = w.batch * w.seq_len * len(rules)
+    per_rule = {}
+    fa_all = []
+    for ri, r in enumerate(rules):
+        idx = [3 * (j * len(rules) + ri) for j in range(len(prof_steps))]
+        fa_ms = [ev.elapsed_ms(b + 1, b + 2) for b in idx]
+        st_ms = [ev.elapsed_ms(b, b + 1) for b in idx]
+        fw_ms = [ev.elapsed_ms(b, b + 2) for b in idx]
+        fa_all += fa_ms
+        st_avg = sum(st_ms) / len(st_ms)
+        fw_avg = sum(fw_ms) / len(fw_ms)
+        per_rule[r] = {
+            "forward_ms": fw_avg,
+            "tokens_per_s": w.batch * w.seq_len / (fw_avg * 1e-3),
+            "stages_ms": {"state": st_avg, "attention": sum(fa_ms) / len(fa_ms),
+                          "attention_min": min(fa_ms), "attention_max": max(fa_ms)},
+            # the memory-state stage against its own bounds: HBM for the linear rule
+            # (contributions + prefix scan), the dependent chain for the delta rule
+            "state_roofline": {"bound": "hbm" if r == "linear" else "latency",
+                               "achieved_GBps": state_bytes(w) / (st_avg * 1e-3) / 1e9,
+                               "peak_GBps": HBM_PEAK_GBS,
+                               "frac_hbm": state_bytes(w) / (st_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "tflops": state_flops(w, r) / (st_avg * 1e-3) / 1e12,
+                               "frac_mfma": state_flops(w, r) / (st_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                               "bytes": state_bytes(w), "flops": state_flops(w, r)},
+        }
     ev.destroy()
-    fa_avg = sum(fa_ms) / len(fa_ms)
-    st_avg = sum(st_ms) / len(st_ms)
+    fa_avg = sum(fa_all) / len(fa_all)
     fl = attention_flops(w)
     achieved = fl / (fa_avg * 1e-3) / 1e12
-    step_fl = fl + state_flops(w, rule)
-    traffic = traffic_for(w.name, rule)
+    step_fl = len(rules) * fl + sum(state_flops(w, r) for r in rules)
+    traffic = traffic_for(w.name, "+".join(rules))
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, rule, args.cpu_seconds)
+        cpu = cpu_baseline(w, rules, args.cpu_seconds)
 
     line = {
         "metric": "Infini-attention fwd tokens/sec on 1 MI355X + % of bf16 MFMA/HBM roofline",
@@ -738,22 +795,14 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
-                   "segment_len": w.segment_len, "d_key": w.d_key, "d_value": w.d_value, "rule": rule,
-                   "parallelism": "single GPU"},
+                   "segment_len": w.segment_len, "d_key": w.d_key, "d_value": w.d_value, "rules": rules,
+                   "step": "reset + forward_sequence over the whole stream, once per rule",
+                   "tokens_per_step": tokens, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": fa_avg},
-        "stages_ms": {"state": st_avg, "attention": fa_avg,
-                      "attention_min": min(fa_ms), "attention_max": max(fa_ms)},
-        # the memory-state stage against its own bounds: HBM for the linear rule
-        # (contributions + prefix scan), the dependent chain for the delta rule
-        "state_roofline": {"bound": "hbm" if rule == "linear" else "latency",
-                           "achieved_GBps": state_bytes(w) / (st_avg * 1e-3) / 1e9,
-                           "peak_GBps": HBM_PEAK_GBS,
-                           "frac_hbm": state_bytes(w) / (st_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           "tflops": state_flops(w, rule) / (st_avg * 1e-3) / 1e12,
-                           "frac_mfma": state_flops(w, rule) / (st_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                           "bytes": state_bytes(w), "flops": state_flops(w, rule)},
+                     "traffic": traffic, "flops_per_launch": fl, "avg_launch_ms": fa_avg,
+                     "launches_sampled": len(fa_all)},
+        "per_rule": per_rule,
         "step_tflops": step_fl / (wall / args.steps) / 1e12,
         "cpu_baseline": cpu,
     }

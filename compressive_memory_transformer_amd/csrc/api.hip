@@ -50,6 +50,14 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// Shapes the MFMA kernels take (bf16 only); every other supported shape runs the
+// VALU path.
+bool mfma_shape(int32_t dk, int32_t dv, int32_t N) { return dk == dv && (dk == 64 || dk == 128) && N % 64 == 0; }
+
+bool mfma_path(const infini_attn_state* st) {
+  return st->dtype == INFINI_BF16 && mfma_shape(st->d_key, st->d_value, st->segment_len);
+}
+
 // Validates a configuration; returns INFINI_OK or an error code with the message set.
 int check_config(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t N, int32_t dtype, int32_t rule,
                  float scale) {
@@ -61,15 +69,13 @@ int check_config(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t N, int32_
   if (std::isinf(scale)) return fail(INFINI_EINVAL, "scale must be finite");
   int64_t t;
   if (!mul_ok((int64_t)B * H, (int64_t)dk * dv, &t)) return fail(INFINI_EINVAL, "state too large");
-  if (dtype == INFINI_BF16) {
-    if (dk != dv || (dk != 64 && dk != 128))
-      return fail(INFINI_EUNSUPPORTED, "bf16 path needs d_key == d_value in {64, 128} (got %d, %d)", dk, dv);
-    if (N % 64 != 0) return fail(INFINI_EUNSUPPORTED, "bf16 path needs segment_len %% 64 == 0 (got %d)", N);
-  } else {
-    if (dk > 128 || dv > 128)
-      return fail(INFINI_EUNSUPPORTED, "fp32 path supports d_key, d_value <= 128 (got %d, %d)", dk, dv);
-    if (N > 4096) return fail(INFINI_EUNSUPPORTED, "fp32 path supports segment_len <= 4096 (got %d)", N);
-  }
+  if (dtype == INFINI_BF16 && mfma_shape(dk, dv, N)) return INFINI_OK;
+  // the VALU path (fp32, and bf16 shapes the MFMA kernels do not take)
+  if (dk > 128 || dv > 128)
+    return fail(INFINI_EUNSUPPORTED, "d_key and d_value must be <= 128 (got %d, %d)", dk, dv);
+  if (N > 4096)
+    return fail(INFINI_EUNSUPPORTED, "segment_len must be <= 4096 (got %d) unless the state is bf16 with "
+                                     "d_key == d_value in {64, 128} and segment_len a multiple of 64", N);
   return INFINI_OK;
 }
 
@@ -85,7 +91,7 @@ int check_state(const infini_attn_state* st) {
 }
 
 struct WsLayout {
-  size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, kp = 0, czp = 0, inv = 0, U = 0, total = 0;
+  size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, amat = 0, U = 0, total = 0;
 };
 
 // Workspace regions for S segments whose tokens sit at a row stride of L per
@@ -96,23 +102,18 @@ bool workspace_layout(const infini_attn_state* st, int64_t S, int64_t L, WsLayou
   int64_t seg_heads, n;
   if (!mul_ok(BH, S, &seg_heads)) return false;
   size_t off = 0;
-  if (st->dtype == INFINI_BF16) {
+  if (mfma_path(st)) {
     const int64_t D = st->d_key;
     if (!mul_ok(seg_heads, D * D, &n)) return false;
     w->snapM = off; off = align_up(off + (size_t)n * 2);
     w->snapz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
     w->snapc = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
-    if (st->rule == INFINI_RULE_LINEAR) {
-      w->cM = off; off = align_up(off + (size_t)n * 4);
-      w->cz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
-    } else {
-      int64_t tokens, parts;
-      if (!mul_ok(BH, L, &tokens)) return false;
-      if (!mul_ok(seg_heads, D, &parts)) return false;
-      w->kp = off; off = align_up(off + (size_t)tokens * D * 2);
-      w->czp = off; off = align_up(off + (size_t)parts * 4);
-      w->inv = off; off = align_up(off + (size_t)tokens * 4);
-    }
+    // both rules: the per-segment contributions C_s^T and c_s
+    w->cM = off; off = align_up(off + (size_t)n * 4);
+    w->cz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
+    // delta rule: A_s per segment as two bf16 parts
+    if (st->rule == INFINI_RULE_DELTA) { w->amat = off; off = align_up(off + (size_t)n * 4); }
+    (void)L;
   } else if (st->rule == INFINI_RULE_DELTA) {
     if (!mul_ok(BH, (int64_t)st->segment_len * st->d_value, &n)) return false;
     w->U = off; off = align_up(off + (size_t)n * 4);
@@ -158,8 +159,8 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
     if ((e = infini::launch_lin_scan<D>(sarg, stream)) != hipSuccess) return hip_fail(e, "lin_scan launch");
   } else {
     infini::DeltaArgs d{static_cast<const bf16*>(k), static_cast<const bf16*>(v), st->M, st->z, snapM, snapz,
-                        snapc, reinterpret_cast<bf16*>(ws + w.kp), reinterpret_cast<float*>(ws + w.czp),
-                        reinterpret_cast<float*>(ws + w.inv), B * H, S, N, L, st->segments_done, 0};
+                        snapc, reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
+                        reinterpret_cast<bf16*>(ws + w.amat), B * H, S, N, L, st->segments_done};
     if ((e = infini::launch_delta_state<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta state launch");
   }
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
@@ -179,14 +180,13 @@ int run_f32(infini_attn_state* st, const void* q, const void* k, const void* v, 
   for (int s = 0; s < S; ++s) {
     const int64_t off = (int64_t)s * N;
     const int has_memory = (st->segments_done + s) > 0;
-    infini::F32AttnArgs a{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-                          beta, st->M, st->z, static_cast<float*>(out), st->heads, BH, N, st->d_key, st->d_value,
-                          L, off, has_memory, st->scale};
+    infini::F32AttnArgs a{q, k, v, beta, st->M, st->z, out, st->heads, BH, N, st->d_key, st->d_value,
+                          L, off, has_memory, st->scale, st->dtype == INFINI_BF16};
     hipError_t e = infini::launch_f32_attn(a, stream);
     if (e != hipSuccess) return hip_fail(e, "f32 attention launch");
-    infini::F32UpdateArgs u{static_cast<const float*>(k), static_cast<const float*>(v), st->M, st->z,
-                            reinterpret_cast<float*>(ws + w.U), BH, N, st->d_key, st->d_value, L, off,
-                            st->rule == INFINI_RULE_DELTA, has_memory};
+    infini::F32UpdateArgs u{k, v, st->M, st->z, reinterpret_cast<float*>(ws + w.U), BH, N, st->d_key,
+                            st->d_value, L, off, st->rule == INFINI_RULE_DELTA, has_memory,
+                            st->dtype == INFINI_BF16};
     e = infini::launch_f32_update(u, stream);
     if (e != hipSuccess) return hip_fail(e, "f32 update launch");
   }
@@ -222,7 +222,7 @@ int commit_open(infini_attn_state* st, const infini_attn_open_segment* os, char*
                 hipStream_t stream) {
   const int B = st->batch, H = st->heads, N = st->segment_len;
   hipError_t e;
-  if (st->dtype == INFINI_BF16) {
+  if (mfma_path(st)) {
     using infini::bf16;
     bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
     float* snapz = reinterpret_cast<float*>(ws + w.snapz);
@@ -238,16 +238,16 @@ int commit_open(infini_attn_state* st, const infini_attn_open_segment* os, char*
       e = st->d_key == 128 ? infini::launch_lin_scan<128>(sarg, stream) : infini::launch_lin_scan<64>(sarg, stream);
       if (e != hipSuccess) return hip_fail(e, "lin_scan launch");
     } else {
-      infini::DeltaArgs d{k, v, st->M, st->z, snapM, snapz, snapc, reinterpret_cast<bf16*>(ws + w.kp),
-                          reinterpret_cast<float*>(ws + w.czp), reinterpret_cast<float*>(ws + w.inv), B * H, 1, N,
-                          (int64_t)N, st->segments_done, 0};
+      infini::DeltaArgs d{k, v, st->M, st->z, snapM, snapz, snapc, reinterpret_cast<float*>(ws + w.cM),
+                          reinterpret_cast<float*>(ws + w.cz), reinterpret_cast<bf16*>(ws + w.amat), B * H, 1, N,
+                          (int64_t)N, st->segments_done};
       e = st->d_key == 128 ? infini::launch_delta_state<128>(d, stream) : infini::launch_delta_state<64>(d, stream);
       if (e != hipSuccess) return hip_fail(e, "delta state launch");
     }
   } else {
-    infini::F32UpdateArgs u{static_cast<const float*>(os->k_open), static_cast<const float*>(os->v_open), st->M,
-                            st->z, reinterpret_cast<float*>(ws + w.U), B * H, N, st->d_key, st->d_value,
-                            (int64_t)N, 0, st->rule == INFINI_RULE_DELTA, st->segments_done > 0};
+    infini::F32UpdateArgs u{os->k_open, os->v_open, st->M, st->z, reinterpret_cast<float*>(ws + w.U), B * H, N,
+                            st->d_key, st->d_value, (int64_t)N, 0, st->rule == INFINI_RULE_DELTA,
+                            st->segments_done > 0, st->dtype == INFINI_BF16};
     if ((e = infini::launch_f32_update(u, stream)) != hipSuccess) return hip_fail(e, "f32 update launch");
   }
   return INFINI_OK;
@@ -380,14 +380,14 @@ static int forward_impl(infini_attn_state* st, const void* q, const void* k, con
   if (overlaps(workspace, w.total, out, out_bytes) || overlaps(workspace, w.total, st->M, m_bytes) ||
       overlaps(workspace, w.total, st->z, z_bytes))
     return fail(INFINI_EWORKSPACE, "workspace must not alias out or the state");
-  if (st->dtype == INFINI_BF16) {
+  if (mfma_path(st)) {
     const int64_t fa_blocks = infini::fa_fwd_blocks(BH * S64, st->segment_len);
     if (fa_blocks > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
   }
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if (st->dtype == INFINI_BF16) {
+  if (mfma_path(st)) {
     rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events)
                           : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events);
   } else {
@@ -441,7 +441,9 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
     return fail(INFINI_EINVAL, "tensor sizes overflow");
   if ((rows + 1) / 2 > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
   const size_t esz = st->dtype == INFINI_BF16 ? 2 : 4;
-  const uintptr_t align = st->dtype == INFINI_BF16 ? 2 : 4;
+  // bf16: the MFMA kernels read and write whole 16-byte row pieces; fp32: the
+  // final stores take 16-byte vectors only where the outputs allow it
+  const uintptr_t align = st->dtype == INFINI_BF16 ? 16 : 4;
   for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv)})
     if (reinterpret_cast<uintptr_t>(p) % align != 0)
@@ -512,7 +514,7 @@ bool layer_layout(const infini_attn_state* st, int64_t seq_len, size_t* qo, size
 }  // namespace
 
 size_t infini_attn_layer_workspace_bytes(const infini_attn_state* st, int32_t d_model, int64_t seq_len) {
-  if (check_state(st) != INFINI_OK || st->dtype != INFINI_BF16 || d_model <= 0 || d_model % 64 != 0) return 0;
+  if (check_state(st) != INFINI_OK || !mfma_path(st) || d_model <= 0 || d_model % 64 != 0) return 0;
   if (seq_len <= 0 || seq_len % st->segment_len != 0) return 0;
   size_t qo, ko, vo, ao, fo, total;
   WsLayout fw;
@@ -525,7 +527,9 @@ int infini_attn_layer_forward(infini_attn_state* st, const void* x, int32_t d_mo
                               size_t workspace_bytes, void* stream) {
   int rc = check_state(st);
   if (rc != INFINI_OK) return rc;
-  if (st->dtype != INFINI_BF16) return fail(INFINI_EUNSUPPORTED, "the layer entry point runs the bf16 path only");
+  if (!mfma_path(st))
+    return fail(INFINI_EUNSUPPORTED, "the layer entry point runs the MFMA path only (bf16, d_key == d_value in "
+                                     "{64, 128}, segment_len a multiple of 64)");
   if (!x || !w_qkv || !w_o || !beta || !y) return fail(INFINI_EINVAL, "x, w_qkv, w_o, beta and y must be non-NULL");
   if (d_model <= 0 || d_model % 64 != 0)
     return fail(INFINI_EUNSUPPORTED, "d_model must be a positive multiple of 64 (got %d)", d_model);
@@ -594,7 +598,9 @@ int infini_attn_kernel_linear_attention(infini_attn_state* st, const void* q, co
                                         void* stream) {
   int rc = check_state(st);
   if (rc != INFINI_OK) return rc;
-  if (st->dtype != INFINI_BF16) return fail(INFINI_EUNSUPPORTED, "kernel linear attention runs on the bf16 path only");
+  if (!mfma_path(st))
+    return fail(INFINI_EUNSUPPORTED, "kernel linear attention runs on the MFMA path only (bf16, d_key == d_value "
+                                     "in {64, 128}, segment_len a multiple of 64)");
   if (st->rule != INFINI_RULE_LINEAR)
     return fail(INFINI_EINVAL, "kernel linear attention needs a state with the linear update rule");
   if (!q || !k || !v || !out) return fail(INFINI_EINVAL, "q, k, v and out must be non-NULL");
@@ -730,7 +736,7 @@ int infini_attn_append(infini_attn_state* st, infini_attn_open_segment* os, cons
       overlaps(workspace, total, st->z, z_bytes) || overlaps(workspace, total, os->k_open, kob) ||
       overlaps(workspace, total, os->v_open, vob))
     return fail(INFINI_EWORKSPACE, "workspace must not alias out, the state or the open-segment buffers");
-  if (st->dtype == INFINI_BF16 && n_tokens >= N) {
+  if (mfma_path(st) && n_tokens >= N) {
     const int64_t fa_blocks = infini::fa_fwd_blocks(BH * (n_tokens / N), N);
     if (fa_blocks > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
   }
@@ -767,7 +773,7 @@ int infini_attn_append(infini_attn_state* st, infini_attn_open_segment* os, cons
     } else {
       // whole segments straight from the input (row stride n_tokens per (b, h))
       const int S = (int)((n_tokens - t) / N);
-      if (s.dtype == INFINI_BF16) {
+      if (mfma_path(&s)) {
         rc = s.d_key == 128
                  ? run_bf16<128>(&s, qb + t * qrow, kb + t * qrow, vb + t * vrow, n_tokens, S, beta,
                                  ob + t * vrow, ws, whole, strm, nullptr)

@@ -94,6 +94,15 @@ __device__ __forceinline__ int xcd_logical_block(int hw, int nblocks) {
   return (hw % kXcd) * (nblocks / kXcd) + hw / kXcd;
 }
 
+// Workgroup barrier that orders LDS accesses only: the fences are restricted to
+// the LDS address space, so the barrier waits for this wave's LDS operations
+// (lgkmcnt) but not for its global loads in flight (register prefetches).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

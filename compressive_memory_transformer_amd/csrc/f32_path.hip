@@ -1,7 +1,10 @@
-// fp32 path: plain VALU kernels, one segment per launch, for fp32 inputs of any
-// width up to 128 and any segment length up to 4096.  Same equations as the bf16
-// path (page "精读笔记：Infini-attention", sections 3.1, 3.3, 3.4, 3.5); all
-// arithmetic in fp32.
+// The VALU path: plain kernels, one segment per launch, for any widths d_key,
+// d_value up to 128 and any segment length up to 4096.  It serves every fp32
+// state, and bf16 states whose shapes the MFMA kernels do not take (d_key !=
+// d_value, widths other than 64 and 128, segment lengths that are not a
+// multiple of 64).  Same equations as the MFMA path (page "精读笔记：
+// Infini-attention", sections 3.1, 3.3, 3.4, 3.5); q, k, v and the output in the
+// state's dtype (T = float or bf16), all arithmetic in fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,11 +15,16 @@ constexpr int kThreads = 256;
 constexpr int kRows = 4;          // query rows per workgroup
 constexpr int kMaxN = 4096;       // scores of kRows rows kept in LDS
 constexpr int kMaxD = 128;
+__device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const bf16* p, int64_t i) { return bf2f(p[i]); }
+__device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void st(bf16* p, int64_t i, float x) { p[i] = f2bf(x); }
 }  // namespace
 
 // One workgroup per (head, block of kRows query rows).  Scores for the block are
 // materialised in LDS (masked softmax over keys j <= i of this segment), then
 // A_dot, A_mem and the gate are formed with one thread per output element.
+template <typename T>
 __global__ __launch_bounds__(kThreads)
 void f32_attn_kernel(F32AttnArgs a) {
   __shared__ float sc[kRows][kMaxN];
@@ -28,15 +36,15 @@ void f32_attn_kernel(F32AttnArgs a) {
   const int h = bh % a.H;
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)bh * a.L + a.seg_off;
-  const float* __restrict__ q = a.q + row0 * a.dk;
-  const float* __restrict__ k = a.k + row0 * a.dk;
-  const float* __restrict__ v = a.v + row0 * a.dv;
-  float* __restrict__ o = a.out + row0 * a.dv;
+  const T* __restrict__ q = static_cast<const T*>(a.q) + row0 * a.dk;
+  const T* __restrict__ k = static_cast<const T*>(a.k) + row0 * a.dk;
+  const T* __restrict__ v = static_cast<const T*>(a.v) + row0 * a.dv;
+  T* __restrict__ o = static_cast<T*>(a.out) + row0 * a.dv;
   const int nr = min(kRows, a.N - r0);
 
   for (int i = t; i < kRows * a.dk; i += kThreads) {
     const int r = i / a.dk, c = i % a.dk;
-    qs[r][c] = r < nr ? q[(int64_t)(r0 + r) * a.dk + c] : 0.f;
+    qs[r][c] = r < nr ? ld(q, (int64_t)(r0 + r) * a.dk + c) : 0.f;
   }
   __syncthreads();
   const int nkeys = r0 + nr;  // keys 0 .. r0+nr-1 may be needed
@@ -45,7 +53,7 @@ void f32_attn_kernel(F32AttnArgs a) {
     float s = -__builtin_inff();
     if (j <= r0 + r) {
       float d = 0.f;
-      for (int c = 0; c < a.dk; ++c) d = __builtin_fmaf(qs[r][c], k[(int64_t)j * a.dk + c], d);
+      for (int c = 0; c < a.dk; ++c) d = __builtin_fmaf(qs[r][c], ld(k, (int64_t)j * a.dk + c), d);
       s = d * a.scale;
     }
     sc[r][j] = s;
@@ -82,7 +90,7 @@ void f32_attn_kernel(F32AttnArgs a) {
   for (int i = t; i < nr * a.dv; i += kThreads) {
     const int r = i / a.dv, c = i % a.dv;
     float acc = 0.f;
-    for (int j = 0; j <= r0 + r; ++j) acc = __builtin_fmaf(sc[r][j], v[(int64_t)j * a.dv + c], acc);
+    for (int j = 0; j <= r0 + r; ++j) acc = __builtin_fmaf(sc[r][j], ld(v, (int64_t)j * a.dv + c), acc);
     const float a_dot = acc / rowstat[r][0];
     float a_mem = 0.f;
     if (a.has_memory) {
@@ -94,12 +102,13 @@ void f32_attn_kernel(F32AttnArgs a) {
       const float den = rowstat[r][1];
       a_mem = den > 0.f ? num / den : 0.f;
     }
-    o[(int64_t)(r0 + r) * a.dv + c] = g * a_mem + (1.f - g) * a_dot;
+    st(o, (int64_t)(r0 + r) * a.dv + c, g * a_mem + (1.f - g) * a_dot);
   }
 }
 
 // Delta rule, step 1: U = V - sigma(K) M_{s-1} / (sigma(K) z_{s-1}), one thread per
 // (token, column); the denominator is recomputed per thread (small widths only).
+template <typename T>
 __global__ __launch_bounds__(kThreads)
 void f32_residual_kernel(F32UpdateArgs a) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -108,15 +117,15 @@ void f32_residual_kernel(F32UpdateArgs a) {
   const int bh = (int)(i / per_head);
   const int tt = (int)((i % per_head) / a.dv), c = (int)(i % a.dv);
   const int64_t row = (int64_t)bh * a.L + a.seg_off + tt;
-  const float* __restrict__ kr = a.k + row * a.dk;
-  const float vv = a.v[row * a.dv + c];
+  const T* __restrict__ kr = static_cast<const T*>(a.k) + row * a.dk;
+  const float vv = ld(static_cast<const T*>(a.v), row * a.dv + c);
   float u = vv;
   if (a.has_memory) {
     const float* __restrict__ M = a.M + (int64_t)bh * a.dk * a.dv;
     const float* __restrict__ z = a.z + (int64_t)bh * a.dk;
     float num = 0.f, den = 0.f;
     for (int kk = 0; kk < a.dk; ++kk) {
-      const float x = kr[kk];
+      const float x = ld(kr, kk);
       const float f = x > 0.f ? x + 1.f : expf(x);
       num = __builtin_fmaf(f, M[(int64_t)kk * a.dv + c], num);
       den = __builtin_fmaf(f, z[kk], den);
@@ -128,6 +137,7 @@ void f32_residual_kernel(F32UpdateArgs a) {
 
 // Step 2 (both rules): M[i][c] += sum_t sigma(K[t][i]) W[t][c] with W = V (linear)
 // or U (delta); one thread per element of M.
+template <typename T>
 __global__ __launch_bounds__(kThreads)
 void f32_bind_kernel(F32UpdateArgs a) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -138,10 +148,10 @@ void f32_bind_kernel(F32UpdateArgs a) {
   const int64_t row0 = (int64_t)bh * a.L + a.seg_off;
   float acc = 0.f;
   for (int tt = 0; tt < a.N; ++tt) {
-    const float x = a.k[(row0 + tt) * a.dk + r];
+    const float x = ld(static_cast<const T*>(a.k), (row0 + tt) * a.dk + r);
     const float f = x > 0.f ? x + 1.f : expf(x);
     const float w = a.delta ? a.U[(int64_t)bh * a.N * a.dv + (int64_t)tt * a.dv + c]
-                            : a.v[(row0 + tt) * a.dv + c];
+                            : ld(static_cast<const T*>(a.v), (row0 + tt) * a.dv + c);
     acc = __builtin_fmaf(f, w, acc);
   }
   a.M[(int64_t)bh * per_head + (int64_t)r * a.dv + c] += acc;
@@ -149,6 +159,7 @@ void f32_bind_kernel(F32UpdateArgs a) {
 
 // Step 3: z[i] += sum_t sigma(K[t][i]); after step 2 so that the delta read-back
 // above used z_{s-1}.
+template <typename T>
 __global__ __launch_bounds__(kThreads)
 void f32_znorm_kernel(F32UpdateArgs a) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -157,7 +168,7 @@ void f32_znorm_kernel(F32UpdateArgs a) {
   const int64_t row0 = (int64_t)bh * a.L + a.seg_off;
   float acc = 0.f;
   for (int tt = 0; tt < a.N; ++tt) {
-    const float x = a.k[(row0 + tt) * a.dk + r];
+    const float x = ld(static_cast<const T*>(a.k), (row0 + tt) * a.dk + r);
     acc += x > 0.f ? x + 1.f : expf(x);
   }
   a.z[i] += acc;
@@ -175,23 +186,29 @@ hipError_t launch_f32_attn(const F32AttnArgs& a, hipStream_t stream) {
   if (a.N > kMaxN || a.dk > kMaxD || a.dv > kMaxD) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.BH * ((a.N + kRows - 1) / kRows);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(f32_attn_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  if (a.bf16) hipLaunchKernelGGL(f32_attn_kernel<bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL(f32_attn_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t f32_update(const F32UpdateArgs& a, hipStream_t stream) {
+  auto grid = [](int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads)); };
+  if (a.delta) {
+    const int64_t n = (int64_t)a.BH * a.N * a.dv;
+    hipLaunchKernelGGL(f32_residual_kernel<T>, grid(n), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(f32_bind_kernel<T>, grid((int64_t)a.BH * a.dk * a.dv), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(f32_znorm_kernel<T>, grid((int64_t)a.BH * a.dk), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream) {
-  auto grid = [](int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads)); };
-  if (a.delta) {
-    const int64_t n = (int64_t)a.BH * a.N * a.dv;
-    hipLaunchKernelGGL(f32_residual_kernel, grid(n), dim3(kThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(f32_bind_kernel, grid((int64_t)a.BH * a.dk * a.dv), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(f32_znorm_kernel, grid((int64_t)a.BH * a.dk), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return a.bf16 ? f32_update<bf16>(a, stream) : f32_update<float>(a, stream);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream) {

@@ -4,15 +4,20 @@
 // phi = ELU + 1.
 //
 // The stream is cut into chunks (the state's segment length).  The linear-rule
-// state kernels give every chunk's starting state (bf16 M^T with fp32 column
-// sums, fp32 z); this kernel adds the chunk's own keys up to each query:
-//   num_i = colsum(M) + M^T q'_i + sum_{j <= i} w_ij v_j,
-//   den_i = phi(q_i) . z + sum_{j <= i} w_ij,
-//   w_ij  = phi(q_i) . phi(k_j) = d + sum k'_j + sum q'_i + k'_j . q'_i,
-// with q' = phi(q) - 1 and k' = phi(k) - 1 rounded to bf16 for the products (the
-// constant and rank-one parts of phi . phi stay in fp32).  One workgroup (4 waves)
-// per 128 queries of a chunk, one wave per 32; weights transposed (keys x
-// queries) so the accumulator feeds the product with V^T directly.
+// state kernels give every chunk's starting state (bf16 M^T, fp32 z); this kernel
+// adds the chunk's own keys up to each query:
+//   num_i = phi(q_i) M + sum_{j <= i} w_ij v_j,
+//   den_i = phi(q_i) . z + sum_{j <= i} w_ij,      w_ij = phi(q_i) . phi(k_j),
+// with phi(q) and phi(k) rounded to bf16 as MFMA operands.  Every term of w_ij and
+// of phi(q) M is then a product of positive (or, for M, bounded) factors each
+// carrying bf16's relative precision whatever the magnitude of phi: a 128-term
+// weight is good to about 2e-4 relative both for inputs near 0 (phi ~ 1) and for
+// strongly negative inputs (phi ~ e^x << 1), where forming w as
+// d + sum (phi(k) - 1) + sum (phi(q) - 1) + (phi(q) - 1).(phi(k) - 1) cancels
+// almost completely.  The denominator's memory part phi(q) . z is an fp32 dot
+// product.  One workgroup (4 waves) per 128 queries of a chunk, one wave per 32;
+// weights transposed (keys x queries) so the accumulator feeds the product with
+// V^T directly.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_ops.h"
@@ -33,8 +38,7 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, hh = lane >> 5;
   __shared__ __attribute__((aligned(16))) bf16 kc[2][kKlChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 vc[2][kKlChunk * P];
-  __shared__ __attribute__((aligned(16))) float rk[2][kKlChunk];
-  __shared__ float zsh[D], csh[D];
+  __shared__ float zsh[D];
   const int64_t seg = (int64_t)bh * a.S + s;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int q0 = qb * kKlBlock, qw0 = q0 + 32 * w;
@@ -43,32 +47,25 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
   const int64_t qrow = seg0 + min(qcol, a.N - 1);
   const int kend = min(a.N, q0 + kKlBlock);
 
-  // the chunk's starting state: column sums of M and z (M^T itself is read as an
-  // operand straight from memory at the end)
-  if (t < D) {
-    zsh[t] = a.snapz[seg * D + t];
-    csh[t] = a.snapc[seg * D + t];
-  }
-  // the lane's query: q' as the B operand (natural order), sum q', phi(q) . z later
+  // the chunk's starting z (M^T itself is read as an operand straight from
+  // memory at the end)
+  if (t < D) zsh[t] = a.snapz[seg * D + t];
+  // the lane's query: phi(q) as the B operand (natural order) and in fp32
   bf16x8 qm[KS];
   float qf[KS][8];
-  float rq = 0.f;
 #pragma unroll
   for (int c = 0; c < KS; ++c) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(a.q + qrow * D + 16 * c + 8 * hh);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float v = bf2f(x[j]);
-      const float f = v > 0.f ? v : exp_e(v) - 1.f;
+      const float f = v > 0.f ? v + 1.f : exp_e(v);
       qf[c][j] = f;
       qm[c][j] = f2bf(f);
-      rq += f;
     }
   }
-  rq += __shfl_xor(rq, 32);
 
-  // staging of one key chunk: k' into kc, v into vc, and the row sums of k' (the
-  // D / 8 threads of a row are consecutive lanes: a shuffle reduction)
+  // staging of one key chunk: phi(k) into kc, v into vc
   bf16x8 pk[PIECES], pv[PIECES];
   auto load = [&](int kc0) {
 #pragma unroll
@@ -83,16 +80,11 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
     for (int i = 0; i < PIECES; ++i) {
       const int p = t + 64 * kKlWaves * i, r = p / (D / 8), c8 = p % (D / 8);
       bf16x8 kp;
-      float rs = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float v = bf2f(pk[i][j]);
-        kp[j] = f2bf(v > 0.f ? v : exp_e(v) - 1.f);
-        rs += bf2f(kp[j]);
+        kp[j] = f2bf(v > 0.f ? v + 1.f : exp_e(v));
       }
-#pragma unroll
-      for (int o = 1; o < D / 8; o <<= 1) rs += __shfl_xor(rs, o);
-      if (c8 == 0) rk[buf][r] = rs;
       *reinterpret_cast<bf16x8*>(kc[buf] + r * P + 8 * c8) = kp;
       *reinterpret_cast<bf16x8*>(vc[buf] + r * P + 8 * c8) = pv[i];
     }
@@ -118,22 +110,14 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
       bf16x8 pb[2][2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        // the keys' row sums: accumulator rows come in runs of four
-        f32x4 rk4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rk4[j] = *reinterpret_cast<const f32x4*>(&rk[buf][32 * kt + 8 * j + 4 * hh]);
         if (below) {   // every key of the chunk precedes every query of the wave
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float wv = (float)D + rk4[r >> 2][r & 3] + rq + sa[kt][r];
-            sa[kt][r] = wv;
-            den += wv;
-          }
+          for (int r = 0; r < 16; ++r) den += sa[kt][r];
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kl = 32 * kt + mo_acc_row(r, hh);
-            const float wv = kc0 + kl <= qcol ? (float)D + rk4[r >> 2][r & 3] + rq + sa[kt][r] : 0.f;
+            const float wv = kc0 + kl <= qcol ? sa[kt][r] : 0.f;
             sa[kt][r] = wv;
             den += wv;
           }
@@ -157,10 +141,14 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
 #pragma unroll
   for (int c = 0; c < KS; ++c)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dz = __builtin_fmaf(qf[c][j] + 1.f, zsh[16 * c + 8 * hh + j], dz);
+    for (int j = 0; j < 8; ++j) dz = __builtin_fmaf(qf[c][j], zsh[16 * c + 8 * hh + j], dz);
   den += __shfl_xor(den, 32);
   dz += __shfl_xor(dz, 32);
-  const float inv = 1.f / (den + dz);   // > 0: the query's own key is in the sum
+  // The exact denominator is > 0 (the query's own key is in the sum); a
+  // non-positive one (only from underflow of every phi) gives a zero row, the
+  // rule of the forward retrieval.
+  const float tot = den + dz;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
   if (!qvalid) return;
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
@@ -174,7 +162,7 @@ __global__ __launch_bounds__(64 * kKlWaves) void kla_kernel(FaArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int col = 32 * d + mo_acc_row(r, hh);
-      a.out[qrow * D + col] = f2bf((csh[col] + rt[r] + o[d][r]) * inv);
+      a.out[qrow * D + col] = f2bf((rt[r] + o[d][r]) * inv);
     }
   }
 }

@@ -56,10 +56,12 @@ struct LinScanArgs {
 };
 template <int D> hipError_t launch_lin_scan(const LinScanArgs& a, hipStream_t stream);
 
-// Delta rule: a parallel pre-pass over K (k' = sigma(K) - 1 in bf16, the z
-// snapshots and 1/den per token), then the chain over the S segments of each
-// head, one workgroup per 16 columns of M.  Emits the snapshots and updates the
-// state.
+// Delta rule as the matrix recurrence M_s = M_{s-1} + C_s - A_s M_{s-1} with
+// C_s = sigma(K)^T V and A_s = sigma(K)^T diag(w) sigma(K), w_t = 1 / (sigma(K_t) .
+// z_{s-1}) (0 in a stream's first segment): C_s, c_s (the linear rule's
+// contribution kernel), the z snapshots (a prefix scan) and A_s (MFMA) for all
+// segments in parallel, then the chain over the S segments of each head, one
+// workgroup per 16 columns of M.  Emits the snapshots and updates the state.
 struct DeltaArgs {
   const bf16* k;
   const bf16* v;
@@ -68,44 +70,45 @@ struct DeltaArgs {
   bf16* snapM;           // [B*H*S][D][D] (row = d_value)
   float* snapz;          // [B*H*S][D]
   float* snapc;          // [B*H*S][D]
-  bf16* kp;              // workspace [B*H][L][D]: sigma(K) - 1
-  float* czp;            // workspace [B*H*S][D]: column sums of sigma(K) per segment
-  float* inv_den;        // workspace [B*H][L]
+  float* cM;             // workspace [B*H*S][D][D]: C_s^T (row = d_value)
+  float* cz;             // workspace [B*H*S][D]: c_s
+  bf16* amat;            // workspace [B*H*S][2][D][D]: A_s as bf16 hi, then lo
   int BH, S, N;
   int64_t L;
   int64_t seg_base;
-  int nparts;            // 256-token blocks of the 1/den kernel per segment (set by the launcher)
 };
 template <int D> hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream);
-// 256-token blocks per segment of the 1/den kernel.
-int delta_parts(int N);
 
-// ------------------------------------------------------------------ fp32 path
-// One segment per launch; M and z are read as M_{s-1}, z_{s-1}.
+// ------------------------------------------------------------------ VALU path
+// fp32 states and the bf16 shapes without MFMA kernels.  One segment per launch;
+// M and z are read as M_{s-1}, z_{s-1}.  q, k, v, out in the state's dtype (bf16
+// when the flag is set, else fp32).
 struct F32AttnArgs {
-  const float* q;        // rows of this segment: q + (bh * L + seg_off) * dk
-  const float* k;
-  const float* v;
+  const void* q;         // rows of this segment: q + (bh * L + seg_off) * dk
+  const void* k;
+  const void* v;
   const float* beta;
   const float* M;        // [BH][dk][dv]
   const float* z;        // [BH][dk]
-  float* out;
+  void* out;
   int H, BH, N, dk, dv;
   int64_t L, seg_off;
   int has_memory;
   float scale;
+  int bf16;
 };
 hipError_t launch_f32_attn(const F32AttnArgs& a, hipStream_t stream);
 
 struct F32UpdateArgs {
-  const float* k;
-  const float* v;
+  const void* k;
+  const void* v;
   float* M;
   float* z;
   float* U;              // workspace [BH][N][dv] (delta rule)
   int BH, N, dk, dv;
   int64_t L, seg_off;
   int delta, has_memory;
+  int bf16;
 };
 hipError_t launch_f32_update(const F32UpdateArgs& a, hipStream_t stream);
 

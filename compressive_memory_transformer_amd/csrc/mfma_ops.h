@@ -26,6 +26,34 @@ __device__ __forceinline__ bf16x8 mo_col_acc(const bf16* X, int pitch, int r0, i
   return lds_operand_tr(X, pitch, r0 + 4 * h, r0 + 8 + 4 * h, c0 + 16 * (g & 1), s);
 }
 
+// Row-major [rows x P] bf16 tiles (P = 128 or 64 elements) in LDS whose rows are
+// the contraction index, read as v_mfma_f32_32x32x16_bf16 operands by
+// ds_read_b64_tr_b16.  A 32-lane half of a read covers 4 consecutive rows x 4
+// 16-byte chunks; the chunk swizzle moves rows r % 4 (P = 128) or (r / 2) % 2
+// (P = 64) to disjoint groups of 4 chunks, so each half touches 16 distinct bank
+// groups.  Physical chunk of logical chunk c in row r (an XOR: also the inverse):
+template <int P>
+__device__ __forceinline__ int trt_chunk(int r, int c) { return c ^ (P == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2); }
+
+// Element offset (relative to a 16-row step) of this lane's first transposing
+// read for 32-column block cb; the second read is 8 rows further.  Lane l gets
+// column 32 cb + l % 32 of rows {4 hi + e, 8 + 4 hi + e}, e = 0..3 (a fixed
+// permutation of the 16 rows, the same for every operand read this way).
+template <int P>
+__device__ __forceinline__ int trt_offset(int lane, int cb) {
+  const int hi = lane >> 5, grp = lane >> 4, sidx = lane & 15;
+  const int row = 4 * hi + (sidx >> 2);
+  const int col = 32 * cb + 16 * (grp & 1) + 4 * (sidx & 3);
+  return row * P + 8 * trt_chunk<P>(row, col >> 3) + (col & 7);
+}
+
+template <int P>
+__device__ __forceinline__ bf16x8 trt_read(const bf16* tile, int ofs) {
+  const s16x4 x = lds_read_tr16(tile + ofs);
+  const s16x4 y = lds_read_tr16(tile + ofs + 8 * P);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Rows 8 ks .. 8 ks + 7 of an accumulator as a bf16 B operand.
 __device__ __forceinline__ bf16x8 mo_acc(const f32x16& c, int ks) {
   bf16x8 b;

@@ -7,12 +7,14 @@
 // fp32) per segment for the fused attention kernel and the final (M_S, z_S) in
 // the fp32 state.  The delta rule lives in state_delta.hip.
 //
-// Precision.  sigma(K) = 1 + k' with k' = sigma(K) - 1 small for the keys of these
-// workloads, so rounding sigma(K) itself to bf16 would keep only a few bits of k'.
-// The contribution GEMM therefore runs on k' in bf16 (full relative precision of
-// the deviation from 1) and adds the rank-one term 1^T V as a second product with
-// an all-ones operand, both summed in fp32 (V is exact in bf16):
-//   sigma(K)^T V = k'^T V + 1^T V.
+// Precision.  sigma(K) is split exactly into two bf16 parts, sigma = hi + lo with
+// hi = bf16(sigma) and lo = bf16(sigma - hi), and the contribution GEMM runs as two
+// bf16 products into one fp32 accumulator (V is exact in bf16):
+//   sigma(K)^T V = hi^T V + lo^T V,
+// which keeps about 16 bits of sigma whatever its size: for keys near 0
+// (sigma ~ 1 + k, where bf16(sigma) alone would keep only a few bits of k) and for
+// strongly negative keys (sigma ~ e^k << 1, where writing sigma as
+// 1 + (sigma - 1) would cancel).
 #include "common.h"
 #include "kernels.h"
 
@@ -27,9 +29,9 @@ constexpr int kThreads = 256;
 // blocks of a segment (d = 128) run on the same XCD and share its V through L2.
 // 64-token stages of K (this block's columns) and V stream into a 4-slot LDS
 // ring with buffer_load ... lds (three stages in flight).  Per stage each thread
-// turns 8 elements of K into k' = sigma(K) - 1 in bf16, written to LDS in the
-// layout of the transposing operand reads; then C^T[d_value][d_key] +=
-// V^T k' + V^T 1 on v_mfma_f32_32x32x16_bf16 (both products into one fp32
+// turns 8 elements of K into sigma(K) = hi + lo (bf16 each), written to two LDS
+// buffers in the layout of the transposing operand reads; then C^T[d_value][d_key]
+// += V^T hi + V^T lo on v_mfma_f32_32x32x16_bf16 (both products into one fp32
 // accumulator), one 32 x 32 output tile per wave (d = 128; at d = 64 two waves
 // share a tile, taking alternate 16-token steps).  c = sum_t sigma(K_t) is
 // reduced over the workgroup at the end in a fixed order.
@@ -128,7 +130,8 @@ void lin_contrib_kernel(LinContribArgs a) {
   // alias the direct-to-LDS loads into another and does not wait for them.
   __shared__ __attribute__((aligned(1024))) bf16 ks0[KT], ks1[KT], ks2[KT], ks3[KT];
   __shared__ __attribute__((aligned(1024))) bf16 vs0[VT], vs1[VT], vs2[VT], vs3[VT];
-  __shared__ __attribute__((aligned(1024))) bf16 kh0[KT], kh1[KT];
+  __shared__ __attribute__((aligned(1024))) bf16 kh0[KT], kh1[KT];   // hi parts of sigma(K)
+  __shared__ __attribute__((aligned(1024))) bf16 kl0[KT], kl1[KT];   // lo parts
   __shared__ float lc_red[kLcTt * (kLcKb + 1)];   // end-of-kernel reductions
   static_assert(SHARE == 1 || TILES * 1024 <= kLcTt * (kLcKb + 1), "partials fit the reduction area");
 
@@ -161,21 +164,18 @@ void lin_contrib_kernel(LinContribArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  // k' = sigma(K) - 1 of elements [i0, i0 + n) of this thread's chunk (bf16) and
-  // its column sums
-  auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, int i0, int n) {
+  // sigma(K) = hi + lo of elements [i0, i0 + n) of this thread's chunk (bf16
+  // each) and its column sums (fp32)
+  auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, bf16x8& l8, int i0, int n) {
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i) {
       const float x = bf2f(kx[i]);
-      const float f = x > 0.f ? x : exp_e(x) - 1.f;
-      zp[i] += f;   // sum of k'; the count of tokens is added at the end
+      const float f = x > 0.f ? x + 1.f : exp_e(x);
+      zp[i] += f;
       h8[i] = f2bf(f);
+      l8[i] = f2bf(f - bf2f(h8[i]));
     }
   };
-  // B operand of the rank-one product: every element 1
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = f2bf(1.f);
 
   // prologue: stage 0 landed, its sigma(K) parts in buffer 0
   {
@@ -183,15 +183,16 @@ void lin_contrib_kernel(LinContribArgs a) {
     __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0F70);
     __builtin_amdgcn_s_barrier();
     const bf16x8 kx = *(const INFINI_LDS bf16x8*)(ks0 + ssrc);
-    bf16x8 h8;
-    sigma_part(kx, h8, 0, 8);
+    bf16x8 h8, l8;
+    sigma_part(kx, h8, l8, 0, 8);
     *(INFINI_LDS bf16x8*)(kh0 + sdst) = h8;
+    *(INFINI_LDS bf16x8*)(kl0 + sdst) = l8;
   }
   // Iteration q: the products of stage q (MFMA, slot q % 4, buffer q % 2)
   // interleaved with k' of stage q+1 (VALU, into the other buffer); the loads
   // of stage q+3 go into the slot of stage q-1, which every wave has finished
   // reading at the barrier.
-#define INFINI_LC_ITER(Q, VC, KN, KHC, KHN, KLD, VLD)                                             \
+#define INFINI_LC_ITER(Q, VC, KN, KHC, KHN, KLC, KLN, KLD, VLD)                                   \
   {                                                                                             \
     const int q_ = (Q);                                                                         \
     /* stage q+1 has landed once at most stage q+2's loads are in flight */                      \
@@ -202,21 +203,25 @@ void lin_contrib_kernel(LinContribArgs a) {
       const bool more_ = q_ + 1 < nst;                                                          \
       /* all operand reads of the stage first: one LDS latency per stage */                     \
       const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + ssrc);                                \
-      bf16x8 va_[NST], vk_[NST];                                                                \
+      bf16x8 va_[NST], vk_[NST], vl_[NST];                                                      \
       _Pragma("unroll")                                                                         \
       for (int j = 0; j < NST; ++j) {                                                           \
         const int st = part + SHARE * j;                                                        \
         va_[j] = lc_read_tr<D>(VC, 16 * st * D + vofs);                                         \
         vk_[j] = lc_read_tr<kLcKb>(KHC, 16 * st * kLcKb + kofs);                                \
+        vl_[j] = lc_read_tr<kLcKb>(KLC, 16 * st * kLcKb + kofs);                                \
       }                                                                                         \
-      bf16x8 h8_;                                                                               \
+      bf16x8 h8_, l8_;                                                                          \
       _Pragma("unroll")                                                                         \
       for (int j = 0; j < NST; ++j) {                                                           \
         acc = mfma32(va_[j], vk_[j], acc);                                                      \
-        acc = mfma32(va_[j], ones, acc);                                                        \
-        if (more_) sigma_part(kx_, h8_, EPS * j, EPS);                                          \
+        acc = mfma32(va_[j], vl_[j], acc);                                                      \
+        if (more_) sigma_part(kx_, h8_, l8_, EPS * j, EPS);                                     \
       }                                                                                         \
-      if (more_) *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                       \
+      if (more_) {                                                                              \
+        *(INFINI_LDS bf16x8*)(KHN + sdst) = h8_;                                                \
+        *(INFINI_LDS bf16x8*)(KLN + sdst) = l8_;                                                \
+      }                                                                                         \
     }                                                                                           \
   }
   // Iterations past the last stage (when the stage count is not a multiple of
@@ -224,10 +229,10 @@ void lin_contrib_kernel(LinContribArgs a) {
   // unconditionally, so the compiler tracks exactly which slots have loads in
   // flight and adds no waits of its own.
   for (int q = 0; q < nst; q += 4) {
-    INFINI_LC_ITER(q, vs0, ks1, kh0, kh1, ks3, vs3)
-    INFINI_LC_ITER(q + 1, vs1, ks2, kh1, kh0, ks0, vs0)
-    INFINI_LC_ITER(q + 2, vs2, ks3, kh0, kh1, ks1, vs1)
-    INFINI_LC_ITER(q + 3, vs3, ks0, kh1, kh0, ks2, vs2)
+    INFINI_LC_ITER(q, vs0, ks1, kh0, kh1, kl0, kl1, ks3, vs3)
+    INFINI_LC_ITER(q + 1, vs1, ks2, kh1, kh0, kl1, kl0, ks0, vs0)
+    INFINI_LC_ITER(q + 2, vs2, ks3, kh0, kh1, kl0, kl1, ks1, vs1)
+    INFINI_LC_ITER(q + 3, vs3, ks0, kh1, kh0, kl1, kl0, ks2, vs2)
   }
 #undef INFINI_LC_ITER
   __builtin_amdgcn_s_waitcnt(0);
@@ -256,11 +261,10 @@ void lin_contrib_kernel(LinContribArgs a) {
       cm[dv * D + dkb * kLcKb + 32 * dkq + l32] = acc[r];
     }
   }
-  // c: column sums of sigma(K) = k' + 1 over the 64 row positions, in row order
-  // (each row position saw nst tokens)
+  // c: column sums of sigma(K) over the 64 row positions, in row order
   float* zred = red;   // [64 rows][kLcKb + 1]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) zred[srow * (kLcKb + 1) + 8 * sch + i] = zp[i] + (float)nst;
+  for (int i = 0; i < 8; ++i) zred[srow * (kLcKb + 1) + 8 * sch + i] = zp[i];
   __syncthreads();
   if (th < kLcKb) {
     float sum = 0.f;

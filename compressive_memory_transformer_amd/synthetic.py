@@ -216,8 +216,9 @@ def full_tensor(w: Workload, tensor_id: int, as_bits: bool = False,
 
 
 def stress_variant(w: Workload, name_suffix: str = "_stress") -> Workload:
-    """Same shapes with unscaled N(0, 1) inputs, so scores spread widely and the
-    running-max rescale of an online softmax is exercised."""
+    """Same shapes with unscaled N(0, 1) inputs: at d = 128 with the 1/sqrt(d)
+    softmax scale the scores have a spread of about one unit, ten times that of
+    the scaled workloads, so the softmax weights are far from uniform."""
     return Workload(w.name + name_suffix, w.seed + 100, w.batch, w.heads, w.d_key, w.d_value,
                     w.segment_len, w.segments, w.dtype, w.rules, w.beta_kind, w.beta_width, 1.0,
                     False, notes="stress variant of " + w.name)
@@ -225,9 +226,10 @@ def stress_variant(w: Workload, name_suffix: str = "_stress") -> Workload:
 
 def custom(name: str, seed: int, batch: int, heads: int, d: int, segment_len: int, segments: int,
            dtype: str = "bf16", rules=("linear", "delta"), input_scale: float | None = None,
-           beta_width: float = 2.0) -> Workload:
-    """A workload of arbitrary shape for tests (several tiles and a ragged tail)."""
+           beta_width: float = 2.0, d_value: int | None = None) -> Workload:
+    """A workload of arbitrary shape for tests (several tiles and a ragged tail);
+    d is the key width and, unless d_value is given, the value width too."""
     if input_scale is None:
         input_scale = 1.0 / math.sqrt(d) if dtype == "bf16" else 1.0
-    return Workload(name, seed, batch, heads, d, d, segment_len, segments, dtype, tuple(rules),
-                    "uniform", beta_width, input_scale)
+    return Workload(name, seed, batch, heads, d, d if d_value is None else d_value, segment_len, segments, dtype,
+                    tuple(rules), "uniform", beta_width, input_scale)

@@ -36,9 +36,19 @@
  *   M     : [B, H, d_key, d_value] fp32;  z: [B, H, d_key] fp32
  * out must not alias q, k, v, M, z or the workspace.
  *
- * Supported shapes.  fp32: 1 <= d_key, d_value <= 128, any N >= 1.
- * bf16 (the fast path): d_key == d_value in {64, 128}, N a positive multiple of 64.
- * Other shapes return INFINI_EUNSUPPORTED.
+ * Supported shapes.  bf16 with d_key == d_value in {64, 128} and N a positive
+ * multiple of 64 runs the MFMA kernels (any N of that form).  Every other state
+ * with 1 <= d_key, d_value <= 128 and 1 <= N <= 4096 (fp32, and bf16 with other
+ * widths, d_key != d_value or a ragged N) runs the VALU kernels, one segment per
+ * launch, with the same arithmetic in fp32.  Other shapes return
+ * INFINI_EUNSUPPORTED.  The layer and kernel-linear-attention entry points run
+ * the MFMA shapes only.
+ *
+ * Accuracy.  sigma(q) and sigma(K) enter the bf16 kernels' memory products as
+ * (sigma - 1) or as an exact pair of bf16 parts, so keys and queries near 0
+ * (sigma ~ 1) keep their full precision; the retrieval of the fused kernel forms
+ * sigma(q) M as colsum(M) + (sigma(q) - 1) M, which loses relative precision for
+ * queries far below 0 (sigma(q) << 1, about 1e-2 relative at q ~ -4).
  *
  * Errors.  Every entry point validates all of its arguments before making any
  * HIP call; on an error it enqueues nothing, leaves *st unchanged and returns a
@@ -90,7 +100,13 @@ typedef struct {
 } infini_attn_state;
 
 /* Validates the configuration, fills *st, zeroes M and z on `stream` and sets the
- * counter to 0 (the state of a fresh stream: M_0 = 0, z_0 = 0). */
+ * counter to 0 (the state of a fresh stream: M_0 = 0, z_0 = 0).  The state is the
+ * compressive memory of section 3.4 of "精读笔记：Infini-attention", one M
+ * (d_key x d_value) and one z (d_key) per head (section 3.6), d_key (d_value + 1)
+ * values per head (section 3.7, Table 1).  M and z: device fp32, 4-byte aligned,
+ * caller-owned, not overlapping.  Errors: EINVAL for a NULL pointer, a
+ * non-positive size, an unknown dtype or rule, an infinite scale; EUNSUPPORTED
+ * for the shapes listed above. */
 int infini_attn_init_state(infini_attn_state *st, int32_t batch, int32_t heads,
                            int32_t d_key, int32_t d_value, int32_t segment_len,
                            int32_t dtype, int32_t rule, float scale,
@@ -103,10 +119,19 @@ size_t infini_attn_workspace_bytes(const infini_attn_state *st, int64_t seq_len)
 
 /* Processes the S = seq_len / N segments of every (b, h) in order, starting from
  * the state's (M, z, segments_done), writes A to out and leaves (M_S, z_S) in the
- * state; segments_done += S.  q, k, v, out hold seq_len tokens per (b, h).
- * beta: device fp32 [H].  workspace: device memory of at least
- * infini_attn_workspace_bytes(st, seq_len) bytes, 256-byte aligned, contents
- * irrelevant on entry and undefined on return. */
+ * state; segments_done += S.  Each segment is the forward of section 3.8 of
+ * "精读笔记：Infini-attention" (steps 1-5): local causal attention (section 3.1),
+ * retrieval (section 3.3), gate (section 3.5), memory update (section 3.4, the
+ * delta fraction as written in section 2.1 of "忘记遗忘：解锁无限上下文的
+ * Infini-attention"); the order retrieve-then-update follows section 24.5 of
+ * "第24章 Sparse与Infinite Attention".  q, k, v, out hold seq_len tokens per
+ * (b, h), 16-byte aligned for bf16 and 4-byte for fp32.  beta: device fp32 [H].
+ * workspace: device memory of at least infini_attn_workspace_bytes(st, seq_len)
+ * bytes, 256-byte aligned, contents irrelevant on entry and undefined on return.
+ * Errors: EINVAL (NULL pointers, seq_len not a positive multiple of N,
+ * misalignment, out aliasing an input or the state), EWORKSPACE (workspace
+ * missing, too small, misaligned or aliasing), EUNSUPPORTED (a launch grid above
+ * 2^31 workgroups: split the call), EHIP (a launch failed). */
 int infini_attn_forward_sequence(infini_attn_state *st, const void *q, const void *k,
                                  const void *v, int64_t seq_len, const float *beta,
                                  void *out, void *workspace, size_t workspace_bytes,
@@ -124,9 +149,11 @@ int infini_attn_forward_sequence_profiled(infini_attn_state *st, const void *q, 
                                           void *out, void *workspace, size_t workspace_bytes,
                                           void *stream, void *const *events, int32_t n_events);
 
-/* One segment: the same as forward_sequence with seq_len = segment_len.  A stream
- * fed segment by segment gives bitwise the same results as one
- * forward_sequence call over the whole stream. */
+/* One segment: the same as forward_sequence with seq_len = segment_len (the
+ * per-segment recurrence of section 3.4 of "精读笔记：Infini-attention": the
+ * state carries M_{s-1}, z_{s-1} from one call to the next).  A stream fed
+ * segment by segment gives bitwise the same results as one forward_sequence
+ * call over the whole stream.  Arguments and errors as forward_sequence. */
 int infini_attn_forward_segment(infini_attn_state *st, const void *q, const void *k,
                                 const void *v, const float *beta, void *out,
                                 void *workspace, size_t workspace_bytes, void *stream);
@@ -235,7 +262,10 @@ int infini_attn_kernel_linear_attention(infini_attn_state *st, const void *q, co
                                         const void *v, int64_t seq_len, void *out, void *workspace,
                                         size_t workspace_bytes, void *stream);
 
-/* M, z <- 0 on `stream`; segments_done <- 0. */
+/* M, z <- 0 on `stream`; segments_done <- 0: the empty memory M_0 = 0, z_0 = 0 a
+ * stream starts from (the first segment then reads A_mem = 0, the convention of
+ * this library for section 3.3's 0 / 0 of "精读笔记：Infini-attention").  No
+ * allocation; EINVAL for an invalid state. */
 int infini_attn_reset(infini_attn_state *st, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */

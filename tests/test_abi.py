@@ -52,9 +52,9 @@ def test_struct_layout_matches_header():
     ((1, 2, 128, 128, 0, ia.BF16, ia.RULE_LINEAR), ia.EINVAL),
     ((1, 2, 128, 128, 2048, 7, ia.RULE_LINEAR), ia.EINVAL),
     ((1, 2, 128, 128, 2048, ia.BF16, 9), ia.EINVAL),
-    ((1, 2, 96, 96, 2048, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
-    ((1, 2, 128, 64, 2048, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
-    ((1, 2, 128, 128, 2000, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
+    ((1, 2, 256, 256, 2048, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
+    ((1, 2, 96, 96, 8192, ia.BF16, ia.RULE_DELTA), ia.EUNSUPPORTED),
+    ((1, 2, 128, 64, 8192, ia.BF16, ia.RULE_LINEAR), ia.EUNSUPPORTED),
     ((1, 2, 256, 32, 64, ia.F32, ia.RULE_LINEAR), ia.EUNSUPPORTED),
     ((1, 2, 32, 32, 8192, ia.F32, ia.RULE_LINEAR), ia.EUNSUPPORTED),
 ])
@@ -82,8 +82,8 @@ def test_workspace_bytes():
     assert ia.workspace_bytes(st, S * 2048) == want
     st = _state(rule=ia.RULE_DELTA)
     L = S * 2048
-    # snapshots, then sigma(K) - 1 (bf16), column sums of sigma(K) per segment, 1/den per token
-    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * L * D * 2 + BH * S * D * 4 + BH * L * 4
+    # snapshots, the contributions C_s^T and c_s, then A_s per segment as two bf16 parts
+    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4 + BH * S * D * D * 4
     assert ia.workspace_bytes(st, L) == want
     assert ia.workspace_bytes(st, 2047) == 0
     assert ia.workspace_bytes(st, 0) == 0
@@ -121,7 +121,7 @@ def test_forward_rejects_bad_arguments(case):
     elif case == "alias_state":
         out = st.M - 64
     elif case == "bad_state":
-        st.d_key = 100
+        st.d_key = 200
         expect = ia.EUNSUPPORTED
     elif case == "uninit":
         st = ia.State()
@@ -234,7 +234,8 @@ def test_backward_workspace_bytes():
 
 
 @pytest.mark.parametrize("case", ["null_dout", "null_dq", "ragged", "small_ws", "alias_out_in", "alias_outs",
-                                  "alias_ws_state", "misaligned_beta", "bad_state"])
+                                  "alias_ws_state", "misaligned_beta", "misaligned_q", "misaligned_dv",
+                                  "bad_state"])
 def test_backward_rejects_bad_arguments(case):
     st = _state()
     L = 2 * 2048
@@ -259,8 +260,12 @@ def test_backward_rejects_bad_arguments(case):
         ws = st.M - 256 * 4
     elif case == "misaligned_beta":
         beta = FAKE * 7 + 2
+    elif case == "misaligned_q":
+        q = FAKE * 4 + 8      # 8-byte aligned: the bf16 kernels read 16-byte row pieces
+    elif case == "misaligned_dv":
+        dv = FAKE * 11 + 2
     elif case == "bad_state":
-        st.d_key = 100
+        st.d_key = 200
         expect = ia.EUNSUPPORTED
     before = _snapshot(st)
     rc = ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, nbytes, None,

@@ -34,6 +34,8 @@ CASES = [
     ("bf16_d128_resume", 34, 1, 2, 128, 128, 256, 3, "bf16", 2),
     # N = 192: the last 128-row block of the MFMA kernels has two idle waves
     ("bf16_d128_n192", 35, 2, 1, 128, 128, 192, 2, "bf16", 1),
+    # a bf16 shape without MFMA kernels (different widths, ragged N): the VALU kernels
+    ("bf16_dk32_dv48_n80", 36, 1, 2, 32, 48, 80, 3, "bf16", 1),
 ]
 
 

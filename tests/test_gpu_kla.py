@@ -90,3 +90,33 @@ def test_full_size_prefix():
             worst = max(worst, e)
             assert e <= gh.tol("bf16"), f"head {h} chunk {c}: error {e:.3e}"
     gh.log(f"  worst tile {worst:.3e}")
+
+
+@pytest.mark.parametrize("mean,sd", [(-1.0, 0.5), (-4.0, 0.3), (0.0, 1.0)])
+def test_shifted_inputs(mean, sd):
+    """Queries and keys drawn around a negative mean (phi well below 1, down to
+    e^-4) and unscaled: the weights phi(q) . phi(k) keep their relative precision,
+    every chunk against the oracle."""
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    B, H, d, C, S = 1, 2, 128, 256, 4
+    w = syn.custom(f"kla_shift_{mean}", 57, B, H, d, C, S, dtype="bf16", rules=("linear",), input_scale=1.0)
+    qn, kn = (syn.round_bf16(syn.full_tensor(w, i) * np.float32(sd) + np.float32(mean)) for i in (0, 1))
+    vn = syn.round_bf16(syn.full_tensor(w, 2) * np.float32(1.0 / np.sqrt(d)))
+    gh.log(f"kla shifted inputs mean {mean} sd {sd}")
+    q, k, v = (gh.upload_values(x, "bf16") for x in (qn, kn, vn))
+    eng = ia.InfiniAttention(B, H, d, d, C, "bf16", "linear")
+    out = eng.kernel_linear_attention(q, k, v)
+    torch.cuda.synchronize()
+    got = gh.to_host(out)
+    want = kl.causal_kernel_linear_attention(qn, kn, vn)
+    worst = 0.0
+    for h in range(H):
+        for s in range(S):
+            rows = slice(s * C, (s + 1) * C)
+            e = gh.metric(got[0, h, rows], want["O"][0, h, rows], "bf16")
+            worst = max(worst, e)
+            assert e <= gh.tol("bf16"), f"mean {mean} head {h} chunk {s}: error {e:.3e}"
+    eS = gh.metric(gh.to_host(eng.M), want["S"], "bf16")
+    gh.log(f"  worst tile {worst:.3e}; S {eS:.3e}")
+    assert eS <= gh.tol("bf16")

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 from compressive_memory_transformer_amd import synthetic as syn
+from oracle import infini_ref as ref
 from tests import gpu_harness as gh
 
 pytestmark = pytest.mark.gpu
@@ -29,22 +30,28 @@ def _gpu():
 
 
 SMALL = [
-    # name, seed, B, H, d, N, S, dtype
+    # name, seed, B, H, d_key, N, S, dtype[, d_value]
     ("f32_tiny_shape", 11, 1, 2, 32, 64, 4, "f32"),
     ("f32_ragged", 12, 2, 3, 20, 37, 3, "f32"),
     ("bf16_d128_n192", 13, 2, 3, 128, 192, 3, "bf16"),
     ("bf16_d64_n256", 14, 1, 4, 64, 256, 4, "bf16"),
     ("bf16_d128_n64", 15, 1, 2, 128, 64, 5, "bf16"),
     ("bf16_d64_n320", 16, 2, 1, 64, 320, 2, "bf16"),
+    # bf16 shapes the MFMA kernels do not take (the VALU path): the tiny
+    # workload's shape, different key and value widths, a ragged segment length
+    ("bf16_d32_n64", 17, 1, 2, 32, 64, 4, "bf16"),
+    ("bf16_dk64_dv32_n100", 18, 2, 2, 64, 100, 3, "bf16", 32),
+    ("bf16_dk32_dv128_n96", 19, 1, 3, 32, 96, 3, "bf16", 128),
 ]
 
 
 @pytest.mark.parametrize("rule", ["linear", "delta"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shapes(case, rule):
-    name, seed, B, H, d, N, S, dtype = case
+    name, seed, B, H, d, N, S, dtype = case[:8]
+    dv = case[8] if len(case) > 8 else None
     gh.log(f"case {name} rule={rule}")
-    w = syn.custom(name, seed, B, H, d, N, S, dtype=dtype)
+    w = syn.custom(name, seed, B, H, d, N, S, dtype=dtype, d_value=dv)
     q, k, v, beta = gh.device_inputs(w)
     out, eng = gh.run(w, rule, q, k, v, beta)
     gh.torch_mod().cuda.synchronize()
@@ -87,8 +94,9 @@ def test_gate_limits(rule, sign):
 
 
 def test_stress_scores():
-    """Unscaled N(0, 1) queries and keys: scores spread over tens of units, so the
-    running maximum of the online softmax moves and rescales."""
+    """Unscaled N(0, 1) queries and keys: scores with a spread of about one unit
+    (ten times the workloads'), so the softmax weights are far from uniform and the
+    exponentials span several binades."""
     base = syn.custom("stress_case", 31, 1, 2, 128, 512, 3)
     w = syn.stress_variant(base)
     gh.log("stress input")
@@ -167,3 +175,85 @@ def test_single_layer_32k_linear_full():
     gh.torch_mod().cuda.synchronize()
     res = gh.oracle_full(w, "linear")
     gh.compare_full(w, "linear", out, eng, res, label=w.name)
+
+
+OVERFLOW_CASES = [
+    # name, seed, N, segments, (query row, key row) pairs: query row i is made a
+    # large multiple of key row j (j <= i), so its score against key j exceeds the
+    # maximum over the first 32-key block by far more than 64 ln 2
+    ("n2048", 71, 2048, 2, [(200, 100), (1000, 1000), (1800, 1000), (2047, 40)]),
+    ("n192", 72, 192, 3, [(150, 64), (191, 33), (40, 40)]),
+]
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+@pytest.mark.parametrize("case", OVERFLOW_CASES, ids=[c[0] for c in OVERFLOW_CASES])
+def test_softmax_overflow_recompute(case, rule):
+    """Scores far above the reference maximum the fused kernel takes from the
+    first 32-key block: the block's probability sums leave the safe range and the
+    query block is recomputed exactly.  Queries in the first and in later query
+    tiles, on the diagonal tile and left of it, in a segment without memory and in
+    one with memory; every tile against the oracle."""
+    name, seed, N, S, pairs = case
+    w = syn.custom(f"overflow_{name}", seed, 1, 2, 128, N, S)
+    q, k, v = (syn.full_tensor(w, i) for i in (syn.Q_ID, syn.K_ID, syn.V_ID))
+    sc = 1.0 / math.sqrt(128.0)
+    for h in range(w.heads):
+        for seg in (0, S - 1):
+            for (i, j) in pairs:
+                kj = k[0, h, seg * N + j].astype(np.float64)
+                c = 150.0 / (sc * float(kj @ kj))      # score about 150 (natural units)
+                q[0, h, seg * N + i] = syn.round_bf16((c * kj).astype(np.float32))
+    # on the host: every planted row's best score beats its first block's maximum
+    # by far more than 64 ln 2 (where the kernel's sums would pass 2^64)
+    for seg in (0, S - 1):
+        for (i, j) in pairs:
+            qi = q[0, 0, seg * N + i].astype(np.float64)
+            s_row = sc * (k[0, 0, seg * N:seg * N + i + 1].astype(np.float64) @ qi)
+            assert s_row.max() - s_row[:min(32, i + 1)].max() > 64 * math.log(2) + 20 or j < 32
+    gh.log(f"overflow case {name} rule={rule}")
+    dq, dk, dv = (gh.upload_values(x, "bf16") for x in (q, k, v))
+    beta = gh.torch_mod().from_numpy(syn.betas(w)).to("cuda")
+    out, eng = gh.run(w, rule, dq, dk, dv, beta)
+    gh.torch_mod().cuda.synchronize()
+    res = ref.forward_sequence(q, k, v, syn.betas(w), rule, N)
+    gh.compare_full(w, rule, out, eng, res, label=f"overflow_{name}/{rule}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_nonfinite_inputs_propagate(rule, dtype):
+    """A NaN in one query element and an infinity in one key element are carried
+    to the outputs and the state the way the float64 oracle carries them: the rows
+    and state entries that are not finite there are not finite on the GPU, and
+    every other row and entry matches."""
+    d, N = (128, 256) if dtype == "bf16" else (32, 64)
+    w = syn.custom(f"nonfinite_{dtype}", 81, 1, 2, d, N, 3, dtype=dtype)
+    q, k, v = (syn.full_tensor(w, i) for i in (syn.Q_ID, syn.K_ID, syn.V_ID))
+    q[0, 0, 1 * N + 77, 5] = np.nan          # head 0, segment 1
+    k[0, 1, 2 * N + 30, 9] = np.inf          # head 1, last segment
+    gh.log(f"non-finite inputs {dtype}/{rule}")
+    dq, dk, dv = (gh.upload_values(x, dtype) for x in (q, k, v))
+    beta = gh.torch_mod().from_numpy(syn.betas(w)).to("cuda")
+    out, eng = gh.run(w, rule, dq, dk, dv, beta)
+    gh.torch_mod().cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        res = ref.forward_sequence(q, k, v, syn.betas(w), rule, N)
+    got = gh.to_host(out)
+    fin_ref = np.isfinite(res["A"]).all(axis=-1)
+    fin_gpu = np.isfinite(got).all(axis=-1)
+    assert (~fin_ref).any(), "the planted values must make some output rows non-finite"
+    assert np.array_equal(fin_ref, fin_gpu), (np.argwhere(fin_ref != fin_gpu)[:5])
+    for h in range(w.heads):
+        for s in range(w.segments):
+            rows = slice(s * N, (s + 1) * N)
+            ok = fin_ref[0, h, rows]
+            e = gh.metric(got[0, h, rows][ok], res["A"][0, h, rows][ok], dtype)
+            assert e <= gh.tol(dtype), (h, s, e)
+    for name, g, o in (("M", gh.to_host(eng.M), res["M"]), ("z", gh.to_host(eng.z), res["z"])):
+        assert np.array_equal(np.isfinite(g), np.isfinite(o)), name
+        for h in range(w.heads):
+            ok = np.isfinite(o[0, h])
+            if ok.any():
+                assert gh.metric(g[0, h][ok], o[0, h][ok], dtype) <= gh.tol(dtype), (name, h)
+    gh.log(f"  non-finite {dtype}/{rule}: {int((~fin_ref).sum())} non-finite rows, all matched")
