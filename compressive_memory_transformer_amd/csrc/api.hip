@@ -91,7 +91,7 @@ int check_state(const infini_attn_state* st) {
 }
 
 struct WsLayout {
-  size_t snapM = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, amat = 0, U = 0, total = 0;
+  size_t snapM = 0, snapMlo = 0, snapz = 0, snapc = 0, cM = 0, cz = 0, amat = 0, U = 0, total = 0;
 };
 
 // Workspace regions for S segments whose tokens sit at a row stride of L per
@@ -106,6 +106,7 @@ bool workspace_layout(const infini_attn_state* st, int64_t S, int64_t L, WsLayou
     const int64_t D = st->d_key;
     if (!mul_ok(seg_heads, D * D, &n)) return false;
     w->snapM = off; off = align_up(off + (size_t)n * 2);
+    w->snapMlo = off; off = align_up(off + (size_t)n * 2);
     w->snapz = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
     w->snapc = off; off = align_up(off + (size_t)(seg_heads * D) * 4);
     // both rules: the per-segment contributions C_s^T and c_s
@@ -147,6 +148,7 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
   using infini::bf16;
   const int B = st->batch, H = st->heads, N = st->segment_len;
   bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
+  bf16* snapMlo = reinterpret_cast<bf16*>(ws + w.snapMlo);
   float* snapz = reinterpret_cast<float*>(ws + w.snapz);
   float* snapc = reinterpret_cast<float*>(ws + w.snapc);
   hipError_t e;
@@ -155,17 +157,17 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
                              reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
                              B, H, S, N, L};
     if ((e = infini::launch_lin_contrib<D>(c, stream)) != hipSuccess) return hip_fail(e, "lin_contrib launch");
-    infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, snapc, B * H, S};
+    infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapMlo, snapz, snapc, B * H, S};
     if ((e = infini::launch_lin_scan<D>(sarg, stream)) != hipSuccess) return hip_fail(e, "lin_scan launch");
   } else {
-    infini::DeltaArgs d{static_cast<const bf16*>(k), static_cast<const bf16*>(v), st->M, st->z, snapM, snapz,
-                        snapc, reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
+    infini::DeltaArgs d{static_cast<const bf16*>(k), static_cast<const bf16*>(v), st->M, st->z, snapM, snapMlo,
+                        snapz, snapc, reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
                         reinterpret_cast<bf16*>(ws + w.amat), B * H, S, N, L, st->segments_done};
     if ((e = infini::launch_delta_state<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta state launch");
   }
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,
-                   snapM, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, 0,
+                   snapM, snapMlo, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, 0,
                    st->segments_done, (float)((double)st->scale * 1.4426950408889634)};
   if ((e = infini::launch_fa_fwd<D>(f, stream)) != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return record(events, 2, stream);
@@ -225,6 +227,7 @@ int commit_open(infini_attn_state* st, const infini_attn_open_segment* os, char*
   if (mfma_path(st)) {
     using infini::bf16;
     bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
+    bf16* snapMlo = reinterpret_cast<bf16*>(ws + w.snapMlo);
     float* snapz = reinterpret_cast<float*>(ws + w.snapz);
     float* snapc = reinterpret_cast<float*>(ws + w.snapc);
     const bf16* k = static_cast<const bf16*>(os->k_open);
@@ -232,13 +235,13 @@ int commit_open(infini_attn_state* st, const infini_attn_open_segment* os, char*
     if (st->rule == INFINI_RULE_LINEAR) {
       infini::LinContribArgs c{k, v, reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
                                B, H, 1, N, N};
-      infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, snapc, B * H, 1};
+      infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapMlo, snapz, snapc, B * H, 1};
       e = st->d_key == 128 ? infini::launch_lin_contrib<128>(c, stream) : infini::launch_lin_contrib<64>(c, stream);
       if (e != hipSuccess) return hip_fail(e, "lin_contrib launch");
       e = st->d_key == 128 ? infini::launch_lin_scan<128>(sarg, stream) : infini::launch_lin_scan<64>(sarg, stream);
       if (e != hipSuccess) return hip_fail(e, "lin_scan launch");
     } else {
-      infini::DeltaArgs d{k, v, st->M, st->z, snapM, snapz, snapc, reinterpret_cast<float*>(ws + w.cM),
+      infini::DeltaArgs d{k, v, st->M, st->z, snapM, snapMlo, snapz, snapc, reinterpret_cast<float*>(ws + w.cM),
                           reinterpret_cast<float*>(ws + w.cz), reinterpret_cast<bf16*>(ws + w.amat), B * H, 1, N,
                           (int64_t)N, st->segments_done};
       e = st->d_key == 128 ? infini::launch_delta_state<128>(d, stream) : infini::launch_delta_state<64>(d, stream);
@@ -636,6 +639,7 @@ int infini_attn_kernel_linear_attention(infini_attn_state* st, const void* q, co
   char* ws = static_cast<char*>(workspace);
   const int B = st->batch, H = st->heads, N = st->segment_len, S = (int)S64, D = st->d_key;
   bf16* snapM = reinterpret_cast<bf16*>(ws + w.snapM);
+  bf16* snapMlo = reinterpret_cast<bf16*>(ws + w.snapMlo);
   float* snapz = reinterpret_cast<float*>(ws + w.snapz);
   float* snapc = reinterpret_cast<float*>(ws + w.snapc);
   infini::LinContribArgs c{static_cast<const bf16*>(k), static_cast<const bf16*>(v),
@@ -643,11 +647,12 @@ int infini_attn_kernel_linear_attention(infini_attn_state* st, const void* q, co
                            seq_len};
   hipError_t e = D == 128 ? infini::launch_lin_contrib<128>(c, strm) : infini::launch_lin_contrib<64>(c, strm);
   if (e != hipSuccess) return hip_fail(e, "lin_contrib launch");
-  infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapz, snapc, B * H, S};
+  infini::LinScanArgs sarg{c.cM, c.cz, st->M, st->z, snapM, snapMlo, snapz, snapc, B * H, S};
   e = D == 128 ? infini::launch_lin_scan<128>(sarg, strm) : infini::launch_lin_scan<64>(sarg, strm);
   if (e != hipSuccess) return hip_fail(e, "lin_scan launch");
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), nullptr,
-                   snapM, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, seq_len, 0, st->segments_done, 0.f};
+                   snapM, snapMlo, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, seq_len, 0, st->segments_done,
+                   0.f};
   e = D == 128 ? infini::launch_kla<128>(f, strm) : infini::launch_kla<64>(f, strm);
   if (e != hipSuccess) return hip_fail(e, "kernel linear attention launch");
   st->segments_done += S64;

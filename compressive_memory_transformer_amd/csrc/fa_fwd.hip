@@ -65,6 +65,11 @@ constexpr int kBN = 128;           // keys per LDS tile
 constexpr int kKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kDmaBlocks = 2;      // blocks of a tile that issue the next load item
 constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
+// A query block with a component of magnitude above this takes the precise
+// retrieval (exact q re-read, q' and M each as bf16 hi + lo).  Below it the
+// query-dependent part q' M is a small share of the retrieval and one bf16 part
+// of each is exact enough.
+constexpr float kPreciseQ = 0.5f;
 
 template <int D>
 struct FaLayout {
@@ -238,6 +243,7 @@ struct QBlock {
   float m;             // reference maximum of the row (log2 domain)
   float l;             // this lane's share of the softmax denominator
   bool bad;            // some block summed past the limit: recompute the block
+  bool big;            // some query component of the block exceeds kPreciseQ (wave-uniform)
 };
 
 // The load item a step brings into the other slot: a K part and a V part, NI
@@ -489,11 +495,17 @@ __device__ void recompute_block(QBlock<D>& X, int r0, const bf16* __restrict__ k
 // for all of d_key; then, one 32-column group of d_value at a time, the
 // retrieval accumulator (colsum + M^T q'), the gate and the output, so that only
 // one group's accumulator is live.
+// Precise path (a block with a large query component, X.big): q is read again
+// from memory (qg: the block's first query row) instead of being recovered from
+// the scaled bf16 operand, q' = sigma(q) - 1 is split into bf16 hi + lo, and the
+// product takes the snapshot's bf16 remainder (mlo: this segment's M^T
+// remainder, row-major) as well: colsum + M_hi q'_hi + M_hi q'_lo + M_lo q'_hi.
 template <int D>
 __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __restrict__ mt,
                                              const float* __restrict__ zs, const float* __restrict__ cs,
                                              const LdsAddr<D>& ad, bool has_memory, float beta, float inv_sc,
-                                             bf16* __restrict__ ob, bf16* __restrict__ stages, int wave) {
+                                             bf16* __restrict__ ob, bf16* __restrict__ stages, int wave,
+                                             const bf16* __restrict__ qg, const bf16* __restrict__ mlo) {
   // The lane index is computed here (from the exec mask, with an opaque base) so
   // that it and the per-lane addresses below are not hoisted to the kernel start
   // and kept live (spilled) across the tile loop: the reload of a spill here
@@ -512,8 +524,30 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
   const float l_tot = X.l + __shfl_xor(X.l, 32);
   const float inv_l = 1.f / l_tot;
   bf16x8 qp[D / 16];                   // q' = sigma(q) - 1 (bf16), the B operand of M^T q'
+  bf16x8 ql[D / 16];                   // precise path: q' - qp (bf16)
+  const bool precise = X.big;
   float den = 0.f;
-  if (has_memory) {
+  if (has_memory && precise) {
+    float zpart = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const f32x4 z0 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi);
+      const f32x4 z1 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi + 4);
+      const bf16x8 qx = *reinterpret_cast<const bf16x8*>(qg + (int64_t)l32 * D + 16 * c + 8 * hi);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = bf2f(qx[i]);
+        const float f = x > 0.f ? x : exp_e(x) - 1.f;
+        const float zz = i < 4 ? z0[i] : z1[i - 4];
+        den = __builtin_fmaf(f, zz, den);
+        zpart += zz;
+        qp[c][i] = f2bf(f);
+        ql[c][i] = f2bf(f - bf2f(qp[c][i]));
+      }
+    }
+    den += zpart;
+    den += __shfl_xor(den, 32);
+  } else if (has_memory) {
     float zpart = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
@@ -565,6 +599,15 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
       for (int c = 0; c < D / 16; ++c) ma[c] = lds_read8(mt + 32 * db * D + ad.kofs(c));
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) am = mfma32(ma[c], qp[c], am);
+      if (precise) {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) am = mfma32(ma[c], ql[c], am);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const bf16x8 ml = *reinterpret_cast<const bf16x8*>(mlo + (int64_t)(32 * db + l32) * D + 16 * c + 8 * hi);
+          am = mfma32(ml, qp[c], am);
+        }
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) am[r] = 0.f;
@@ -595,6 +638,7 @@ struct FaCtx {
   const bf16* kseg;
   const bf16* vseg;
   const bf16* snapM;       // M^T snapshot of this (b, h, segment)
+  const bf16* snapMlo;     // its bf16 remainder
   const float* snapz;
   const float* snapc;
   uint32_t seg_bytes;
@@ -669,10 +713,16 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf1
     bf16x8 qr[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qr[c] = lds_read8(qs + ad.kofs(c));
+    bool big = false;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) X.q[c][i] = f2bf(bf2f(qr[c][i]) * cx.sc);
+      for (int i = 0; i < 8; ++i) {
+        const float x = bf2f(qr[c][i]);
+        X.q[c][i] = f2bf(x * cx.sc);
+        big |= fabsf(x) > kPreciseQ;
+      }
+    X.big = __any(big) != 0;
   }
   // every wave has its Q rows before step 0 loads tile 1 into slot 1
   wait_lds_and_sync();
@@ -715,7 +765,7 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf1
   if (act && __any(X.bad)) recompute_block<D>(X, r0, cx.kseg, cx.vseg);
 
   if (act) finish_block<D>(X, k0s, zc, zc + 256, ad, cx.has_memory, cx.beta, 1.f / cx.sc, cx.ob + (int64_t)r0 * D,
-                           stg, cx.wave);
+                           stg, cx.wave, cx.qb + (int64_t)r0 * D, cx.snapMlo);
   // the snapshot in k0s is no longer read (the output stores stay in flight)
   if (next) wait_lds_and_sync();
 }
@@ -746,6 +796,7 @@ void fa_fwd_kernel(FaArgs a) {
   cx.kseg = a.k + tok0 * D;
   cx.vseg = a.v + tok0 * D;
   cx.snapM = a.snapM + (int64_t)sh * D * D;
+  cx.snapMlo = a.snapMlo + (int64_t)sh * D * D;
   cx.snapz = a.snapz + (int64_t)sh * D;
   cx.snapc = a.snapc + (int64_t)sh * D;
   cx.seg_bytes = (uint32_t)a.N * D * 2;

@@ -17,6 +17,7 @@ struct FaArgs {
   const bf16* v;
   const float* beta;     // [H]
   const bf16* snapM;     // [B*H*S][D][D] bf16 snapshot of M_{s-1}^T (row = d_value)
+  const bf16* snapMlo;   // [B*H*S][D][D] bf16 remainder: M^T = snapM + snapMlo to ~16 bits
   const float* snapz;    // [B*H*S][D]    fp32 snapshot of z_{s-1}
   const float* snapc;    // [B*H*S][D]    fp32 column sums of M_{s-1} over d_key
   bf16* out;
@@ -50,6 +51,7 @@ struct LinScanArgs {
   float* M;              // state [B*H][D][D] (row = d_key), read then overwritten
   float* z;              // state [B*H][D]
   bf16* snapM;           // [B*H*S][D][D] (row = d_value)
+  bf16* snapMlo;         // [B*H*S][D][D] remainder M^T - snapM in bf16
   float* snapz;          // [B*H*S][D]
   float* snapc;          // [B*H*S][D] column sums of M over d_key
   int BH, S;
@@ -68,6 +70,7 @@ struct DeltaArgs {
   float* M;              // state [B*H][D][D] (row = d_key)
   float* z;              // state [B*H][D]
   bf16* snapM;           // [B*H*S][D][D] (row = d_value)
+  bf16* snapMlo;         // [B*H*S][D][D] remainder M^T - snapM in bf16
   float* snapz;          // [B*H*S][D]
   float* snapc;          // [B*H*S][D]
   float* cM;             // workspace [B*H*S][D][D]: C_s^T (row = d_value)

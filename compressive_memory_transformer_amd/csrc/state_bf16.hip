@@ -3,9 +3,9 @@
 //
 //   M_s = M_{s-1} + sigma(K)^T V,   z_s = z_{s-1} + sum_t sigma(K_t)
 //
-// It leaves a snapshot of (M_{s-1}^T in bf16, z_{s-1} and colsum(M_{s-1}) in
-// fp32) per segment for the fused attention kernel and the final (M_S, z_S) in
-// the fp32 state.  The delta rule lives in state_delta.hip.
+// It leaves a snapshot of (M_{s-1}^T as bf16 plus its bf16 remainder, z_{s-1}
+// and colsum(M_{s-1}) in fp32) per segment for the fused attention kernel and the
+// final (M_S, z_S) in the fp32 state.  The delta rule lives in state_delta.hip.
 //
 // Precision.  sigma(K) is split exactly into two bf16 parts, sigma = hi + lo with
 // hi = bf16(sigma) and lo = bf16(sigma - hi), and the contribution GEMM runs as two
@@ -355,10 +355,13 @@ void lin_scan_kernel(LinScanArgs a) {
     for (int i = 0; i < kPf; ++i) {
       if (s0 + i < a.S) {
         const int64_t sh = base + s0 + i;
-        bf16x2 pk;
+        bf16x2 pk, pl;
         pk[0] = f2bf(r0);
         pk[1] = f2bf(r1);
+        pl[0] = f2bf(r0 - bf2f(pk[0]));
+        pl[1] = f2bf(r1 - bf2f(pk[1]));
         *reinterpret_cast<bf16x2*>(a.snapM + sh * D * D + e) = pk;
+        *reinterpret_cast<bf16x2*>(a.snapMlo + sh * D * D + e) = pl;
         const float c = group_sum<TPR>(r0 + r1);
         if (threadIdx.x % TPR == TPR - 1) a.snapc[sh * D + dv] = c;
         r0 += cur[i].x;

@@ -217,8 +217,8 @@ struct ChainOps {
 // 16 x 16 tile (rows of the block) x (d_key columns 16 w ..) of P A on
 // v_mfma_f32_16x16x32_bf16.  Each step:
 //   P (fp32, accumulator layout in registers) -> LDS stage;
-//   snapshot of M_{s-1}: its 16 rows of M^T in bf16 and their sums (column sums
-//   of M over d_key), for the fused kernel;
+//   snapshot of M_{s-1}: its 16 rows of M^T in bf16 with their bf16 remainders,
+//   and their sums (column sums of M over d_key), for the fused kernel;
 //   A operand P_hi, P_lo from the stage; B operands A_hi, A_lo straight from
 //   memory (A_s is symmetric, so row n of A_s is column n);
 //   P += C_s^T - (P_hi A_hi + P_lo A_hi + P_hi A_lo).
@@ -277,10 +277,14 @@ void delta_chain_kernel(DeltaArgs a) {
     const int64_t shg = (int64_t)bh * S + s;
     {
       const f32x4 x = *(const INFINI_LDS f32x4*)(pl + srow * C::LDP + sk);
-      bf16x4 b;
+      bf16x4 b, bl;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = f2bf(x[e]);
+      for (int e = 0; e < 4; ++e) {
+        b[e] = f2bf(x[e]);
+        bl[e] = f2bf(x[e] - bf2f(b[e]));
+      }
       *reinterpret_cast<bf16x4*>(a.snapM + (shg * D + 16 * cb + srow) * D + sk) = b;
+      *reinterpret_cast<bf16x4*>(a.snapMlo + (shg * D + 16 * cb + srow) * D + sk) = bl;
       float rs = (x[0] + x[1]) + (x[2] + x[3]);
 #pragma unroll
       for (int o2 = 1; o2 < C::TPR; o2 <<= 1) rs += __shfl_xor(rs, o2);

@@ -78,12 +78,13 @@ def test_init_state_rejects_null_and_inf():
 def test_workspace_bytes():
     st = _state(rule=ia.RULE_LINEAR)
     S, D, BH = 16, 128, 2
-    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4
+    # snapshots (bf16 M^T and its bf16 remainder, z, column sums), contributions C_s^T and c_s
+    want = 2 * BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4
     assert ia.workspace_bytes(st, S * 2048) == want
     st = _state(rule=ia.RULE_DELTA)
     L = S * 2048
     # snapshots, the contributions C_s^T and c_s, then A_s per segment as two bf16 parts
-    want = BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4 + BH * S * D * D * 4
+    want = 2 * BH * S * D * D * 2 + 2 * BH * S * D * 4 + BH * S * D * D * 4 + BH * S * D * 4 + BH * S * D * D * 4
     assert ia.workspace_bytes(st, L) == want
     assert ia.workspace_bytes(st, 2047) == 0
     assert ia.workspace_bytes(st, 0) == 0
