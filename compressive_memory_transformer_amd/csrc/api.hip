@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 
@@ -301,9 +302,45 @@ bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w)
 
 }  // namespace
 
+// ------------------------------------------------------------------ allocation-free forward
+// The workspace of infini_attn_forward_sequence_noalloc: a file-scope device
+// array that every GPU the library runs on holds until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device memory: host code
+// only ever uses the device address that hipGetSymbolAddress returns for the
+// current device (kept per device below).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, looked up once per device with
+// that device current.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(INFINI_EUNSUPPORTED, "device index %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(INFINI_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return INFINI_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int infini_attn_abi_version(void) { return 1; }
+
+size_t infini_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 const char* infini_attn_last_error(void) { return g_error.c_str(); }
 
@@ -405,6 +442,24 @@ int infini_attn_forward_sequence(infini_attn_state* st, const void* q, const voi
                                  int64_t seq_len, const float* beta, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   return forward_impl(st, q, k, v, seq_len, beta, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int infini_attn_forward_sequence_noalloc(infini_attn_state* st, const void* q, const void* k, const void* v,
+                                         int64_t seq_len, const float* beta, void* out, void* stream) {
+  int rc = check_state(st);
+  if (rc != INFINI_OK) return rc;
+  if (seq_len <= 0 || seq_len % st->segment_len != 0)
+    return fail(INFINI_EINVAL, "seq_len (%lld) must be a positive multiple of segment_len (%d)",
+                (long long)seq_len, st->segment_len);
+  WsLayout w;
+  if (!workspace_layout(st, seq_len / st->segment_len, seq_len, &w)) return fail(INFINI_EINVAL, "workspace size overflows");
+  if (w.total > kScratchBytes)
+    return fail(INFINI_EWORKSPACE, "this call needs %zu bytes of scratch; the allocation-free entry point has %zu "
+                "(split the stream into shorter calls, or use infini_attn_forward_sequence with a workspace)",
+                w.total, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != INFINI_OK) return rc;
+  return forward_impl(st, q, k, v, seq_len, beta, out, ws, kScratchBytes, stream, nullptr);
 }
 
 int infini_attn_forward_sequence_profiled(infini_attn_state* st, const void* q, const void* k, const void* v,

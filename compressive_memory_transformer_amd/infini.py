@@ -89,6 +89,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_workspace_bytes.restype = sz
     lib.infini_attn_forward_sequence.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     lib.infini_attn_forward_sequence.restype = ctypes.c_int
+    lib.infini_attn_forward_sequence_noalloc.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp]
+    lib.infini_attn_forward_sequence_noalloc.restype = ctypes.c_int
+    lib.infini_attn_noalloc_scratch_bytes.argtypes = []
+    lib.infini_attn_noalloc_scratch_bytes.restype = sz
     lib.infini_attn_forward_sequence_profiled.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, sz, vp,
                                                           ctypes.POINTER(vp), i32]
     lib.infini_attn_forward_sequence_profiled.restype = ctypes.c_int
@@ -166,6 +170,17 @@ def forward_sequence(st: State, q, k, v, seq_len, beta, out, workspace, ws_bytes
     rc = load_library().infini_attn_forward_sequence(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len,
                                                      _ptr(beta), _ptr(out), _ptr(workspace), ws_bytes, stream)
     return _check(rc) if check else rc
+
+
+def forward_sequence_noalloc(st: State, q, k, v, seq_len, beta, out, stream=None, check=True) -> int:
+    """forward_sequence on the library's own device scratch array (no workspace)."""
+    rc = load_library().infini_attn_forward_sequence_noalloc(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len,
+                                                             _ptr(beta), _ptr(out), stream)
+    return _check(rc) if check else rc
+
+
+def noalloc_scratch_bytes() -> int:
+    return load_library().infini_attn_noalloc_scratch_bytes()
 
 
 def forward_sequence_profiled(st: State, q, k, v, seq_len, beta, out, workspace, ws_bytes, stream, events,

@@ -137,6 +137,23 @@ int infini_attn_forward_sequence(infini_attn_state *st, const void *q, const voi
                                  void *out, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* forward_sequence for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the call uses a scratch array of
+ * infini_attn_noalloc_scratch_bytes() bytes (64 MiB) that the library keeps in
+ * device memory, one per GPU, for the life of the process, and calls no
+ * allocating routine.  Calls whose workspace (infini_attn_workspace_bytes) exceeds
+ * it return INFINI_EWORKSPACE without enqueueing anything: split the stream into
+ * shorter calls.  Every call on a GPU shares that GPU's array (its contents on
+ * entry do not matter), so calls that overlap on one GPU (other streams, other
+ * threads) race: serialise them.  Otherwise as forward_sequence, bitwise the same
+ * results. */
+int infini_attn_forward_sequence_noalloc(infini_attn_state *st, const void *q, const void *k,
+                                         const void *v, int64_t seq_len, const float *beta,
+                                         void *out, void *stream);
+/* Size of the scratch array of infini_attn_forward_sequence_noalloc. */
+size_t infini_attn_noalloc_scratch_bytes(void);
+
 /* forward_sequence that also records caller-created HIP events (hipEvent_t, as
  * void*) on `stream` at the stage boundaries, for profiling tools:
  *   events[0] before the first kernel, events[1] after the memory-state stage

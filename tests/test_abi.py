@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -343,3 +343,20 @@ def test_kernel_linear_attention_rejects_bad_arguments(case):
     rc = ia.kernel_linear_attention(st, q, k, v, L, out, ws, nbytes, None, check=False)
     assert rc == expect, (case, ia.last_error())
     assert _snapshot(st) == before
+
+
+def test_noalloc_rejects_oversized_and_bad_calls():
+    """The allocation-free forward checks the call's workspace against its fixed
+    scratch array (64 MiB) before any HIP call."""
+    assert ia.noalloc_scratch_bytes() == 64 << 20
+    st = _state(heads=32)                       # 32 heads x 256 segments of 2048: far above 64 MiB
+    before = _snapshot(st)
+    rc = ia.forward_sequence_noalloc(st, FAKE * 4, FAKE * 5, FAKE * 6, 256 * 2048, FAKE * 7, FAKE * 8, None,
+                                     check=False)
+    assert rc == ia.EWORKSPACE and "scratch" in ia.last_error()
+    assert _snapshot(st) == before
+    rc = ia.forward_sequence_noalloc(st, FAKE * 4, FAKE * 5, FAKE * 6, 2047, FAKE * 7, FAKE * 8, None, check=False)
+    assert rc == ia.EINVAL
+    rc = ia.forward_sequence_noalloc(_state(d_key=200), FAKE * 4, FAKE * 5, FAKE * 6, 2048, FAKE * 7, FAKE * 8, None,
+                                     check=False)
+    assert rc == ia.EUNSUPPORTED
