@@ -17,7 +17,9 @@ import os
 import re
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libinfini_attn.so")
+# INFINI_ATTN_LIB selects another build of the same library (the host-sanitized
+# copy of the CPU checks); by default the in-tree build next to this file.
+LIB_PATH = os.environ.get("INFINI_ATTN_LIB") or os.path.join(PKG_DIR, "libinfini_attn.so")
 HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "infini_attn.h")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
