@@ -275,6 +275,7 @@ __device__ __forceinline__ f32x16 s_block(const bf16* __restrict__ kt, int j, co
   bf16x8 ka[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) ka[c] = lds_read8(kt + 32 * j * D + ad.kofs(c));
+  __builtin_amdgcn_sched_barrier(0);   // every read in flight before the first product
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) s = mfma32(ka[c], q[c], s);
   return s;
@@ -367,8 +368,12 @@ __device__ __forceinline__ void tile_pipe(QBlock<D>& X, const bf16* __restrict__
   bf16x8 ko[KS];
   bf16x8 vo[2][NV];
   f32x16 s;   // S^T - m of the current block
+  // all of block 0's K operand reads in flight before its first product (every
+  // wave enters here from the same barrier, so a read-wait-product sequence
+  // would leave the matrix pipe idle for one LDS round trip per product)
 #pragma unroll
   for (int c = 0; c < KS; ++c) ko[c] = lds_read8(kt + ad.kofs(c));
+  INFINI_FENCE();
   s = mfma32(ko[0], X.q[0], X.mneg);
 #pragma unroll
   for (int c = 1; c < KS; ++c) s = mfma32(ko[c], X.q[c], s);
@@ -548,7 +553,6 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
     den += zpart;
     den += __shfl_xor(den, 32);
   } else if (has_memory) {
-    float zpart = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       const f32x4 z0 = *(const INFINI_LDS f32x4*)(zs + 16 * c + 8 * hi);
@@ -565,12 +569,14 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
         const float f = x > 0.f ? x : exp_e(x) - 1.f;   // q' = sigma(q) - 1
         const float zz = i < 4 ? z0[i] : z1[i - 4];
         den = __builtin_fmaf(f, zz, den);
-        zpart += zz;
         qp[c][i] = f2bf(f);
       }
     }
-    den += zpart;                      // sum(z) over this lane's half of d_key
     den += __shfl_xor(den, 32);
+    // sigma(q) . z = sum(z) + q' . z; sum(z) by a reduction over the wave
+    float zsum = *(const INFINI_LDS float*)(zs + lane);
+    if (D > 64) zsum += *(const INFINI_LDS float*)(zs + lane + 64);
+    den += wave_sum(zsum);
   }
   // lane holds row l32 of the block, values d = 32db + 8j + 4hi + 0..3
   const float inv_den = (has_memory && den > 0.f) ? 1.f / den : 0.f;
