@@ -388,6 +388,11 @@ __device__ __forceinline__ void tile_pipe(QBlock<D>& X, const bf16* __restrict__
     bf16x8 p[2];
     float t = 0.f;
     INFINI_FENCE();
+    // Phase 1 runs at raised issue priority: of the two waves of a SIMD, the one
+    // in its softmax phase issues first, so the pair tends to alternate (one
+    // wave's exponentials next to the other's P V products) instead of running
+    // the same phase side by side.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       if (more) ns = mfma32(ko[i], X.q[i], i == 0 ? X.mneg : ns);
@@ -407,6 +412,7 @@ __device__ __forceinline__ void tile_pipe(QBlock<D>& X, const bf16* __restrict__
       }
       INFINI_FENCE();
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < N2; ++i) {
       const int hf = i / NV, db = i % NV;
