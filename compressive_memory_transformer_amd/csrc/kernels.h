@@ -228,6 +228,9 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
 
+// Compute units of the current device (looked up once per device).
+int device_compute_units();
+
 // Zero n floats at p and n2 floats at p2 (one launch).
 hipError_t launch_fill_zero(float* p, int64_t n, float* p2, int64_t n2, hipStream_t stream);
 

@@ -15,6 +15,8 @@
 // (sigma ~ 1 + k, where bf16(sigma) alone would keep only a few bits of k) and for
 // strongly negative keys (sigma ~ e^k << 1, where writing sigma as
 // 1 + (sigma - 1) would cancel).
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -273,6 +275,267 @@ void lin_contrib_kernel(LinContribArgs a) {
   }
 }
 
+// d = 128: one work item per (b, h, s), the whole segment, so that V is read
+// from memory once (the two 64-column halves of d_key in separate workgroups
+// share it only while they run side by side).  Persistent: one workgroup
+// (8 waves) per compute unit walks the items lw, lw + G, ... (lw its
+// XCD-grouped logical index); their 32-token stages of K and V (8 KB each) form
+// one stream through an 8-slot LDS ring, filled by buffer_load ... lds seven
+// stages ahead, across item boundaries.  Both tensors arrive in the layout of
+// the transposing operand reads (chunks swizzled as lc_chunk<128>).  Per stage
+// each thread turns one 16-byte chunk of K into sigma(K) = hi + lo: hi in place
+// in the K slot, lo into one of two LDS buffers; each wave owns two 32 x 32
+// tiles of C^T (one 32-row block of d_value, two 32-column blocks of d_key) and
+// adds V^T hi + V^T lo to both (v_mfma_f32_32x32x16_bf16, one fp32 accumulator
+// each).  At the end of an item its tiles go out and c = sum_t sigma(K_t) is
+// reduced over the workgroup in a fixed order.
+namespace {
+constexpr int kSgWaves = 8;
+constexpr int kSgThreads = 64 * kSgWaves;
+constexpr int kSgTt = 32;        // tokens per stage
+constexpr int kSgSlots = 8;      // ring slots (seven stages in flight)
+constexpr int kSgIpw = 2;        // loads per wave and stage (one 1 KB piece of K, one of V)
+
+struct SgPos {
+  int64_t tok0;
+  int sh, q, k;
+  bool valid;
+};
+
+__device__ __forceinline__ void sg_item(const LinContribArgs& a, int lw, int G, int items, SgPos& p) {
+  const int item = lw + p.k * G;
+  p.valid = item < items;
+  p.sh = p.valid ? item : lw;
+  const int bh = p.sh / a.S, s = p.sh - bh * a.S;
+  p.tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+}
+
+__device__ __forceinline__ void sg_advance(const LinContribArgs& a, int lw, int G, int items, int nst, SgPos& p) {
+  if (++p.q == nst) {
+    p.q = 0;
+    ++p.k;
+    sg_item(a, lw, G, items, p);
+  }
+}
+
+// This wave's loads of one stage: rows 4 w .. 4 w + 3 of the stage's K and V
+// (1 KB each, 16 bytes per lane, chunks swizzled); zeros past the segment end or
+// the last item.
+__device__ __forceinline__ void sg_issue(const LinContribArgs& a, const SgPos& p, bf16* ks, bf16* vs, int wave,
+                                         int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 128;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int t0 = p.q * kSgTt;
+  const uint32_t rows = p.valid && t0 < a.N ? (uint32_t)(a.N - t0) : 0u;
+  const int64_t e0 = (p.tok0 + t0) * D;
+  const int row = 4 * wv + lane / 16;
+  const int off = 2 * (row * D + 8 * lc_chunk<D>(row, lane % 16));
+  const __amdgpu_buffer_rsrc_t rk = lc_rsrc(a.k + e0, rows * D * 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (INFINI_LDS void*)(ks + wv * 512), 16, off, 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t rv = lc_rsrc(a.v + e0, rows * D * 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (INFINI_LDS void*)(vs + wv * 512), 16, off, 0, 0, 0);
+#endif
+}
+}  // namespace
+
+__global__ __launch_bounds__(kSgThreads, 1)
+void lin_contrib_seg_kernel(LinContribArgs a) {
+  constexpr int D = 128;
+  constexpr int ST = kSgTt * D;                  // elements of a K or V stage
+  static_assert(ST / kSgThreads == 8, "one 16-byte chunk of K per thread and stage");
+  static_assert(kSgSlots == 8, "the stage loop is unrolled over the eight slots");
+  // Each slot and buffer is an array of its own, and the loop is unrolled over
+  // them: the compiler then sees that the LDS accesses of one slot never alias
+  // the direct-to-LDS loads into another and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) bf16 ks0[ST], ks1[ST], ks2[ST], ks3[ST], ks4[ST], ks5[ST], ks6[ST],
+      ks7[ST];
+  __shared__ __attribute__((aligned(1024))) bf16 vs0[ST], vs1[ST], vs2[ST], vs3[ST], vs4[ST], vs5[ST], vs6[ST],
+      vs7[ST];
+  __shared__ __attribute__((aligned(1024))) bf16 kl0[ST], kl1[ST];   // lo parts of sigma(K)
+  __shared__ float zred[kSgWaves * D];                             // per-wave column sums of sigma(K)
+
+  const int nst = a.N / kSgTt;
+  const int items = a.B * a.H * a.S;             // below 2^31 (checked by the host)
+  const int G = (int)gridDim.x;
+  const int lw = xcd_logical_block(blockIdx.x, G);
+  if (lw >= items) return;
+  const int total = ((items - lw + G - 1) / G) * nst;   // stream positions of this workgroup
+
+  const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+  const int dvb = wave & 3, dkq = 2 * (wave >> 2);
+  const int vofs = lc_tr_offset<D>(lane, dvb);
+  const int kofs0 = lc_tr_offset<D>(lane, dkq);
+  const int kofs1 = lc_tr_offset<D>(lane, dkq + 1);
+  // sigma(K) pass: row th / 16 of the stage, logical chunk th % 16, at its
+  // physical position (the loads placed it there)
+  const int srow = th >> 4, sch = th & 15;
+  const int sdst = srow * D + 8 * lc_chunk<D>(srow, sch);
+
+  // cur: the position being multiplied; ld: the next position to load
+  SgPos cur;
+  cur.q = 0;
+  cur.k = 0;
+  sg_item(a, lw, G, items, cur);
+  SgPos ld = cur;
+#define INFINI_SG_PRE(KS, VS)                 \
+  sg_issue(a, ld, KS, VS, wave, lane);        \
+  sg_advance(a, lw, G, items, nst, ld);
+  INFINI_SG_PRE(ks0, vs0)
+  INFINI_SG_PRE(ks1, vs1)
+  INFINI_SG_PRE(ks2, vs2)
+  INFINI_SG_PRE(ks3, vs3)
+  INFINI_SG_PRE(ks4, vs4)
+  INFINI_SG_PRE(ks5, vs5)
+  INFINI_SG_PRE(ks6, vs6)
+#undef INFINI_SG_PRE
+
+  float zp[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zp[i] = 0.f;
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+
+  // sigma(K) = hi + lo of elements [i0, i0 + n) of this thread's chunk (bf16
+  // each) and its column sums (fp32)
+  auto sigma_part = [&](const bf16x8& kx, bf16x8& h8, bf16x8& l8, int i0, int n) {
+#pragma unroll
+    for (int i = i0; i < i0 + n; ++i) {
+      const float x = bf2f(kx[i]);
+      const float f = x > 0.f ? x + 1.f : exp_e(x);
+      zp[i] += f;
+      h8[i] = f2bf(f);
+      l8[i] = f2bf(f - bf2f(h8[i]));
+    }
+  };
+
+  // End of an item: its two C^T tiles per wave and c, the column sums of
+  // sigma(K) (over the 4 row positions of a wave by lane exchanges, then over
+  // the waves in order).
+  auto finish_item = [&](const SgPos& p, const float (&zf)[8]) {
+    // lane-derived indices recomputed here behind an opaque value, so that the
+    // store addresses are not hoisted out of the stage loop and kept live
+    unsigned base = 0;
+    asm volatile("" : "+v"(base));
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, base));
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = zf[i];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      z[i] = x;
+    }
+    if (ln < 16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zred[wave * D + 8 * ln + i] = z[i];
+    }
+    float* __restrict__ cm = a.cM + (int64_t)p.sh * D * D;
+    const int hi = ln >> 5, l32 = ln & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dv = 32 * dvb + 8 * (r >> 2) + 4 * hi + (r & 3);
+      cm[dv * D + 32 * dkq + l32] = acc0[r];
+      cm[dv * D + 32 * dkq + 32 + l32] = acc1[r];
+    }
+    // barrier after this wave's LDS writes only: an LDS fence would also wait for
+    // the ring's direct-to-LDS loads in flight
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int t = ln + 64 * wave;
+    if (t < D) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSgWaves; ++w) sum += zred[w * D + t];
+      a.cz[(int64_t)p.sh * D + t] = sum;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+    // zred is read above before the next item's writes (a barrier per stage
+    // separates them)
+  };
+
+  // prologue: position 0 landed, its sigma(K) parts in place
+  {
+    constexpr int VM = 6 * kSgIpw;
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0F70);
+    __builtin_amdgcn_s_barrier();
+    const bf16x8 kx = *(const INFINI_LDS bf16x8*)(ks0 + sdst);
+    bf16x8 h8, l8;
+    sigma_part(kx, h8, l8, 0, 8);
+    *(INFINI_LDS bf16x8*)(ks0 + sdst) = h8;
+    *(INFINI_LDS bf16x8*)(kl0 + sdst) = l8;
+  }
+  // Iteration g: the products of position g (MFMA, slot g % 8, lo buffer g % 2)
+  // interleaved with sigma(K) of position g+1 (VALU, in place in its slot, lo
+  // into the other buffer); the loads of position g+7 (cursor ld) go into the
+  // slot of position g-1, which every wave has finished reading at the barrier.
+#define INFINI_SG_ITER(GI, KC, VC, KN, KLC, KLN, KLD, VLD)                                         \
+  {                                                                                             \
+    const int g_ = (GI);                                                                        \
+    /* position g+1 has landed once at most positions g+2 .. g+6 are in flight */              \
+    __builtin_amdgcn_s_waitcnt(((5 * kSgIpw) & 15) | (((5 * kSgIpw) >> 4) << 14) | 0x0070);     \
+    __builtin_amdgcn_s_barrier();                                                               \
+    sg_issue(a, ld, KLD, VLD, wave, lane);                                                      \
+    sg_advance(a, lw, G, items, nst, ld);                                                       \
+    if (g_ < total) {                                                                           \
+      const bool more_ = g_ + 1 < total;                                                        \
+      const bool last_ = cur.q + 1 == nst;   /* position g ends its item */                     \
+      float zf_[8];                                                                             \
+      if (last_) {                                                                              \
+        _Pragma("unroll")                                                                       \
+        for (int i = 0; i < 8; ++i) { zf_[i] = zp[i]; zp[i] = 0.f; }                            \
+      }                                                                                         \
+      /* all operand reads of the stage first: one LDS latency per stage */                     \
+      const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + sdst);                                \
+      bf16x8 va_[2], k0_[2], l0_[2], k1_[2], l1_[2];                                            \
+      _Pragma("unroll")                                                                         \
+      for (int st = 0; st < 2; ++st) {                                                          \
+        va_[st] = lc_read_tr<D>(VC, 16 * st * D + vofs);                                        \
+        k0_[st] = lc_read_tr<D>(KC, 16 * st * D + kofs0);                                       \
+        l0_[st] = lc_read_tr<D>(KLC, 16 * st * D + kofs0);                                      \
+        k1_[st] = lc_read_tr<D>(KC, 16 * st * D + kofs1);                                       \
+        l1_[st] = lc_read_tr<D>(KLC, 16 * st * D + kofs1);                                      \
+      }                                                                                         \
+      bf16x8 h8_, l8_;                                                                          \
+      _Pragma("unroll")                                                                         \
+      for (int st = 0; st < 2; ++st) {                                                          \
+        acc0 = mfma32(va_[st], k0_[st], acc0);                                                  \
+        acc0 = mfma32(va_[st], l0_[st], acc0);                                                  \
+        acc1 = mfma32(va_[st], k1_[st], acc1);                                                  \
+        acc1 = mfma32(va_[st], l1_[st], acc1);                                                  \
+        if (more_) sigma_part(kx_, h8_, l8_, 4 * st, 4);                                        \
+      }                                                                                         \
+      if (more_) {                                                                              \
+        *(INFINI_LDS bf16x8*)(KN + sdst) = h8_;                                                 \
+        *(INFINI_LDS bf16x8*)(KLN + sdst) = l8_;                                                \
+      }                                                                                         \
+      if (last_) finish_item(cur, zf_);                                                         \
+      sg_advance(a, lw, G, items, nst, cur);                                                    \
+    }                                                                                           \
+  }
+  // Iterations past the last position (when the position count is not a
+  // multiple of eight) only wait, synchronise and issue empty loads: every load
+  // is issued unconditionally, so the compiler tracks exactly which slots have
+  // loads in flight and adds no waits of its own.
+#pragma unroll 1
+  for (int g = 0; g < total; g += 8) {
+    INFINI_SG_ITER(g, ks0, vs0, ks1, kl0, kl1, ks7, vs7)
+    INFINI_SG_ITER(g + 1, ks1, vs1, ks2, kl1, kl0, ks0, vs0)
+    INFINI_SG_ITER(g + 2, ks2, vs2, ks3, kl0, kl1, ks1, vs1)
+    INFINI_SG_ITER(g + 3, ks3, vs3, ks4, kl1, kl0, ks2, vs2)
+    INFINI_SG_ITER(g + 4, ks4, vs4, ks5, kl0, kl1, ks3, vs3)
+    INFINI_SG_ITER(g + 5, ks5, vs5, ks6, kl1, kl0, ks4, vs4)
+    INFINI_SG_ITER(g + 6, ks6, vs6, ks7, kl0, kl1, ks5, vs5)
+    INFINI_SG_ITER(g + 7, ks7, vs7, ks0, kl1, kl0, ks6, vs6)
+  }
+#undef INFINI_SG_ITER
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 // v moved across lanes by the DPP control CTRL; lanes outside ROW_MASK (rows of 16
 // lanes) get old.
 template <int CTRL, int ROW_MASK>
@@ -377,13 +640,37 @@ void lin_scan_kernel(LinScanArgs a) {
 }
 
 // ------------------------------------------------------------------ launchers
+int device_compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int D>
 hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / kLcKb);
-  if (blocks <= 0) return hipSuccess;
   if (a.N % kLcTt != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kLcThreads), 0, stream, a);
-  return hipGetLastError();
+  if constexpr (D == 128) {
+    const int64_t items = (int64_t)a.B * a.H * a.S;
+    if (items <= 0) return hipSuccess;
+    // one persistent workgroup per compute unit (the LDS use allows one)
+    const int64_t cus = device_compute_units();
+    const int64_t blocks = items < cus ? items : cus;
+    const int64_t positions = (items + blocks - 1) / blocks * (a.N / kSgTt);
+    if (items > 0x7fffffff || positions + kSgSlots > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lin_contrib_seg_kernel, dim3((unsigned)blocks), dim3(kSgThreads), 0, stream, a);
+    return hipGetLastError();
+  } else {
+    const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / kLcKb);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kLcThreads), 0, stream, a);
+    return hipGetLastError();
+  }
 }
 
 template <int D>
