@@ -655,9 +655,11 @@ int device_compute_units() {
 template <int D>
 hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
   if (a.N % kLcTt != 0) return hipErrorInvalidValue;
-  if constexpr (D == 128) {
+  // whole segments per workgroup once there are at least as many segments as
+  // compute units; below that, half segments (twice the workgroups) fill the
+  // chip better
+  if (D == 128 && (int64_t)a.B * a.H * a.S >= device_compute_units()) {
     const int64_t items = (int64_t)a.B * a.H * a.S;
-    if (items <= 0) return hipSuccess;
     // one persistent workgroup per compute unit (the LDS use allows one)
     const int64_t cus = device_compute_units();
     const int64_t blocks = items < cus ? items : cus;
@@ -665,12 +667,11 @@ hipError_t launch_lin_contrib(const LinContribArgs& a, hipStream_t stream) {
     if (items > 0x7fffffff || positions + kSgSlots > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(lin_contrib_seg_kernel, dim3((unsigned)blocks), dim3(kSgThreads), 0, stream, a);
     return hipGetLastError();
-  } else {
-    const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / kLcKb);
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kLcThreads), 0, stream, a);
-    return hipGetLastError();
   }
+  const int64_t blocks = (int64_t)a.B * a.H * a.S * (D / kLcKb);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lin_contrib_kernel<D>, dim3((unsigned)blocks), dim3(kLcThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int D>

@@ -29,6 +29,9 @@ CASES = [
     ("d128_dm192", 43, 1, 2, 128, 128, 3, 192),
     # enough output tiles for the 256 x 256 GEMM tiling in both projections
     ("d64_dm1024_big", 44, 2, 8, 64, 128, 64, 1024),
+    # 256 x 256 tiling of the QKV projection with a partial last row tile (8320
+    # rows) and a partial last column tile (1920 columns)
+    ("d64_h10_dm512_ragged", 45, 1, 10, 64, 128, 65, 512),
 ]
 
 
