@@ -1,30 +1,44 @@
 // Local attention part of the gradients on the bf16 MFMA units (the chain rule
 // through A_dot = softmax(scale Q K^T, causal) V of the close-reading page
-// "精读笔记：Infini-attention", section 3.1 with the mask of section 3.8 step 2).
+// "精读笔记：Infini-attention", section 3.1 with the mask of section 3.8 step 2),
+// and the retrieval's share of the query gradient (section 3.3).
 //
-//   bwd_q_mfma_kernel<D>: one workgroup (4 waves) per 128 query rows of a
-//     segment, one wave per 32 rows.  First sweep over the keys: the row's
-//     softmax maximum and sum, A_dot, then E = <dA, A_dot> and D = (1 - g) E.
-//     The retrieval (section 3.3) from M_{s-1} staged in LDS as bf16:
-//     A_mem = (colsum(M) + (sigma(q) - 1) M) / (sigma(q) z) (the column sums in
-//     fp32 keep sigma(q) ~ 1 from costing bf16 precision), the gate's share of
-//     dbeta, rs = g / den and dden.  Second sweep: dS = P ((1 - g) dP - D) and
-//     dq += scale dS K; then the retrieval's dq = (M (rs dA) + dden z) sigma'(q).  Scores are
-//     computed transposed (keys x queries), so every register operand is already
-//     in the accumulator layout of the product that consumes it.
-//   bwd_kv_mfma_kernel<D>: one workgroup per 128 keys, one wave per 32 keys,
-//     the wave's keys and values held as operands in registers; for every chunk
-//     of 64 later queries: S, dP, P, dS, then dv += (1 - g) P^T dA and
-//     dk += scale dS^T Q.
+//   bwd_retr_q_kernel<D>: one workgroup (4 waves) per 128 queries of a segment,
+//     M_{s-1} staged in LDS as bf16.  Per query: A_mem = (colsum(M) +
+//     (sigma(q) - 1) M) / (sigma(q) z) (the column sums in fp32 keep sigma(q) ~ 1
+//     from costing bf16 precision), <dA, A_mem>, rs = g / den, dden, the
+//     retrieval's dq = (M (rs dA) + dden z) sigma'(q) (written to dq_acc) and
+//     the gate's A_mem share of dbeta.
+//   bwd_q2_kernel<D>: query-stationary.  One workgroup (8 waves, two per SIMD)
+//     per pair of 256-query tiles of one segment (tile t and NT-1-t, so that the
+//     causal work is equal), one wave per 32 queries.  First sweep over the
+//     keys: softmax statistics (log2 normaliser) and A_dot, then E = <dA, A_dot>,
+//     D = (1 - g) E and the gate's A_dot share of dbeta.  Second sweep:
+//     dS = P ((1 - g) dP - D) and dq += scale dS K (added to dq_acc).
+//   bwd_kv2_kernel<D>: key-stationary.  One workgroup (8 waves) per pair of
+//     256-key tiles, one wave per 32 keys; the tile's keys sit in LDS, the
+//     wave's values in registers.  For every 32 later queries: S, dP, P, dS,
+//     then dv += (1 - g) P^T dA and dk += scale dS^T Q.
 //
-// Operands (v_mfma_f32_32x32x16_bf16): a row-major LDS tile X is read either by
-// rows (row_op: lane l gets X[r0 + l % 32][k0 + 8 (l / 32) + 0..7]) or, for a
-// contraction over its rows, with the transposing LDS read (tr_op: lane l gets
-// X[r0 + 4 h + e][c0 + l % 32] and X[r0 + 8 + 4 h + e][...], h = l / 32), whose
-// row order matches a 32 x 32 accumulator used as the other operand (lane l
-// holds rows 8 (r / 4) + 4 h + r % 4 of column l % 32).  Chunks of K, V (or Q,
-// dA) are staged through two LDS buffers, the next chunk's global loads issued
-// before the current chunk's products.
+// Scores are computed with the stationary rows as accumulator columns (keys x
+// queries in the query kernel, queries x keys in the key kernel), so the
+// probabilities and dS feed the next product straight from the accumulators:
+// a row-major LDS tile X is read either by rows (lane l gets
+// X[r0 + l % 32][k0 + 8 (l / 32) + 0..7]) or, for a contraction over its rows,
+// with the transposing LDS read (lane l gets X[r0 + 4 h + e][c0 + l % 32] and
+// X[r0 + 8 + 4 h + e][...], h = l / 32), whose row order matches a 32 x 32
+// accumulator used as the other operand (lane l holds rows 8 (r / 4) + 4 h +
+// r % 4 of column l % 32).
+//
+// The streamed operand (K and V, or Q, dA and the rows' statistics) moves
+// HBM -> LDS in 64-row steps with buffer_load ... lds (no staging registers)
+// through a ring of LDS slots, each slot an array of its own so that the
+// compiler never waits on loads into another slot.  Both read patterns hit
+// every tile, so one XOR swizzle of the 16-byte chunks serves both: rows
+// r % 4 and (r / 4) % 4 (D = 128) or (r / 2) % 2 and (r / 4) % 4 (D = 64) pick
+// the chunk permutation, which makes 16 consecutive rows of one logical chunk
+// and 4 consecutive rows x 4 consecutive chunks each hit 16 distinct bank
+// groups.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_ops.h"
@@ -34,8 +48,8 @@ namespace infini {
 namespace {
 
 constexpr int kBwdWaves = 4;
-constexpr int kBwdBlock = 32 * kBwdWaves;   // rows (queries or keys) per workgroup
-constexpr int kChunk = 64;                  // rows of the streamed operand per step
+constexpr int kBwdBlock = 32 * kBwdWaves;   // rows per workgroup of the 4-wave kernels
+constexpr int kChunk = 64;                  // tokens per step of the Gram kernel
 
 __device__ __forceinline__ bf16x8 row_op(const bf16* X, int pitch, int r0, int k0, int lane) {
   return lds_read8(X + (r0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
@@ -71,135 +85,154 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row of accumulator element r for lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Loads a 64-row chunk of two row-major [rows][D] bf16 tensors into registers
-// (16 bytes per piece) and stores it into LDS tiles of pitch D + 8.
+// ------------------------------------------- streamed tiles of the attention kernels
+constexpr int kBw = 8;                  // waves per workgroup
+constexpr int kBwRows = 32 * kBw;       // stationary rows per tile
+constexpr int kBwStep = 64;             // streamed rows per step
+
 template <int D>
-struct ChunkPair {
-  static constexpr int P = D + 8;
-  static constexpr int PIECES = kChunk * D / 8 / (64 * kBwdWaves);
-  bf16x8 x[PIECES], y[PIECES];
-  __device__ __forceinline__ void load(const bf16* X, const bf16* Y, int64_t row0) {
+struct BwL {
+  static constexpr int KS = D / 16;                  // 16-column steps of a row
+  static constexpr int DB = D / 32;                  // 32-column blocks of a row
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;                // rows per 1 KB wave-wide load
+  static constexpr int NIN = kBwStep / RPI / kBw;    // loads per wave per streamed tile
+  static constexpr int TILE = kBwStep * D;           // elements per streamed tile
+  static_assert(NIN >= 1 && NIN * RPI * kBw == kBwStep, "a step's rows split evenly over the waves");
+};
+
+// Physical-chunk XOR of row r (the same map takes logical to physical and back).
+template <int D>
+__device__ __forceinline__ int bw_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Buffer resource over `bytes` bytes at `base`; wave-uniform (scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+#endif
+
+// Per-lane offsets into swizzled [rows x D] tiles.
+template <int D>
+struct BwOfs {
+  using L = BwL<D>;
+  int dma[L::NIN];   // bytes: this lane's 16-byte piece of the wave's loads of a 64-row tile
+  int row[4];        // elements: row reads at r0 = 0, 16-column steps 0..3
+  int rowd;          // D = 128: steps 4..7 sit at row[i] + rowd
+  int tr[L::DB];     // elements: transposing reads at r0 = 0, first 4-row group, per 32-column block
+  int trd;           // the second 4-row group (8 rows further)
+  __device__ __forceinline__ void init(int lane, int wave) {
 #pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-      const int p = threadIdx.x + 64 * kBwdWaves * i, r = p / (D / 8), c8 = p % (D / 8);
-      x[i] = *reinterpret_cast<const bf16x8*>(X + (row0 + r) * D + 8 * c8);
-      y[i] = *reinterpret_cast<const bf16x8*>(Y + (row0 + r) * D + 8 * c8);
+    for (int j = 0; j < L::NIN; ++j) {
+      const int ins = wave * L::NIN + j;
+      const int r = ins * L::RPI + lane / L::CH;
+      dma[j] = 2 * (r * D + 8 * ((lane % L::CH) ^ bw_swz<D>(r)));
     }
+    const int l32 = lane & 31, hh = lane >> 5, sw = bw_swz<D>(l32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[i] = l32 * D + 8 * ((2 * i + hh) ^ sw);
+    rowd = (sw & 8) ? -64 : 64;   // logical chunk + 8 flips bit 3 of the physical one
+    const int s = lane & 15, g1 = (lane >> 4) & 1, ra = 4 * hh + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < L::DB; ++db) {
+      const int cc = 4 * db + 2 * g1 + ((s & 3) >> 1);
+      tr[db] = ra * D + 8 * (cc ^ bw_swz<D>(ra)) + 4 * (s & 1);
+    }
+    // 8 rows further the XOR flips bit 1 of the physical chunk, which is g1 here
+    trd = 8 * D + (g1 ? -16 : 16);
   }
-  __device__ __forceinline__ void store(bf16* xs, bf16* ys) const {
+  // Called once per step: the sums of an LDS array's address and these offsets
+  // are then formed in the step (a few adds) instead of being hoisted out of the
+  // loop as one live register per array and offset (the compiler does not fold
+  // the arrays' addresses into the instructions' immediate offsets).
+  __device__ __forceinline__ void opaque() {
 #pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-      const int p = threadIdx.x + 64 * kBwdWaves * i, r = p / (D / 8), c8 = p % (D / 8);
-      *reinterpret_cast<bf16x8*>(xs + r * P + 8 * c8) = x[i];
-      *reinterpret_cast<bf16x8*>(ys + r * P + 8 * c8) = y[i];
-    }
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(row[i]));
+    asm volatile("" : "+v"(rowd));
+#pragma unroll
+    for (int db = 0; db < L::DB; ++db) asm volatile("" : "+v"(tr[db]));
+    asm volatile("" : "+v"(trd));
+  }
+  // Row operand, 16-column step c, rows r0 + [0, 32) (r0 a multiple of 32).
+  __device__ __forceinline__ int rd(int c, int r0) const {
+    return row[c & 3] + (c >= 4 ? rowd : 0) + r0 * D;
   }
 };
+
+template <int D>
+__device__ __forceinline__ bf16x8 bw_row(const bf16* X, const BwOfs<D>& of, int c, int r0) {
+  return lds_read8(X + of.rd(c, r0));
+}
+// Transposed operand of 32-column block db over rows r0 + [0, 16) (r0 a multiple of 16).
+template <int D>
+__device__ __forceinline__ bf16x8 bw_tr(const bf16* X, const BwOfs<D>& of, int db, int r0) {
+  const bf16* p = X + of.tr[db] + r0 * D;
+  const s16x4 x = lds_read_tr16(p);
+  const s16x4 y = lds_read_tr16(p + of.trd);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// This wave's share of the loads of the 64 rows at `src` (row-major, D columns)
+// into a swizzled LDS tile.
+template <int D>
+__device__ __forceinline__ void bw_dma(const bf16* src, bf16* dst, int wave, const BwOfs<D>& of) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc = bw_rsrc(src, kBwStep * D * 2);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int j = 0; j < BwL<D>::NIN; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (INFINI_LDS void*)(dst + (wv * BwL<D>::NIN + j) * 512), 16,
+                                             of.dma[j], 0, 0, 0);
+#endif
+}
+
+// Waits until at most VM of this wave's vector memory operations are in flight
+// and its LDS operations are done, then synchronises the workgroup.
+template <int VM>
+__device__ __forceinline__ void bw_wait_sync() {
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0070);
+  __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ float bw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_retr_q_kernel(BwdArgs a) {
   constexpr int P = D + 8, KS = D / 16, DB = D / 32;
   const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
   const bf16* Q = static_cast<const bf16*>(a.q);
-  const bf16* K = static_cast<const bf16*>(a.k);
-  const bf16* V = static_cast<const bf16*>(a.v);
   const bf16* DO = static_cast<const bf16*>(a.dout);
-  __shared__ __attribute__((aligned(16))) bf16 kc[2][kChunk * P];
-  __shared__ __attribute__((aligned(16))) bf16 vc[2][kChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
   __shared__ float msum[D], zsh[D], ctmp[128];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const int q0 = qb * kBwdBlock, qw0 = q0 + 32 * w;
+  const int qw0 = qb * kBwdBlock + 32 * w;
   const bool has_mem = a.seg_base + s > 0;
   const bool qvalid = qw0 < a.N;
-  const int qcol = qw0 + l32;                      // this lane's query (column of S^T)
-  const int64_t qrow = seg0 + min(qcol, a.N - 1);
+  const int64_t qrow = seg0 + min(qw0 + l32, a.N - 1);
   const float g = sigmoid_gate(a.beta[h]);
-  const float sl2 = a.scale * kLog2e;
   bf16x8 qr[KS], dr[KS];
 #pragma unroll
   for (int c = 0; c < KS; ++c) {
     qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
     dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
   }
-  const int kend = min(a.N, q0 + kBwdBlock);
   {
     const float* Mg = a.snapM + ((int64_t)bh * a.S + s) * D * D;
     for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) ms[(x / D) * P + x % D] = f2bf(Mg[x]);
     if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
     block_colsum256(Mg, D, D, msum, ctmp);
   }
-
-  // ---- first sweep: maximum, sum and A_dot^T of the wave's 32 query columns
-  f32x16 o[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) o[d] = zero16();
-  float m2 = -__builtin_inff(), l = 0.f;
-  ChunkPair<D> cp;
-  cp.load(K, V, seg0);
-  cp.store(kc[0], vc[0]);
   __syncthreads();
-  for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kChunk, buf ^= 1) {
-    const bool next = kc0 + kChunk < kend;
-    if (next) cp.load(K, V, seg0 + kc0 + kChunk);
-    // both 32-key halves of the chunk at once: four independent product chains,
-    // one rescale per 64 keys (a chunk wholly after the wave's queries is skipped)
-    if (qvalid && kc0 <= qw0 + 31) {
-      f32x16 sa[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int c = 0; c < KS; ++c)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sa[kt] = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sa[kt]);
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float v = kc0 + 32 * kt + acc_row(r, hh) <= qcol ? sa[kt][r] * sl2 : -__builtin_inff();
-          sa[kt][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m2, mx);               // finite: key 0 is in the first chunk
-      const float alpha = exp2_fast(m2 - mn);
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(sa[kt][r] - mn);
-          sa[kt][r] = p;
-          l += p;
-        }
-      m2 = mn;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        pb[kt][0] = acc_op(sa[kt], 0);
-        pb[kt][1] = acc_op(sa[kt], 1);
-      }
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          o[d] = mfma32(tr_op(vc[buf], P, 32 * kt, 32 * d, lane), pb[kt][0], o[d]);
-          o[d] = mfma32(tr_op(vc[buf], P, 32 * kt + 16, 32 * d, lane), pb[kt][1], o[d]);
-        }
-    }
-    if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
-    __syncthreads();
-  }
-  const float lt = l + __shfl_xor(l, 32);
-  const float lse2 = m2 + log2f(lt);
-  const float inv_l = 1.f / lt;
-  // A_mem^T = (colsum(M) + M^T (sigma(q) - 1)^T) / den for the lane's query
+  // q' = sigma(q) - 1 and the denominator sigma(q) z of the lane's query
   bf16x8 qm[KS];
   float den = 0.f;
 #pragma unroll
@@ -214,9 +247,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
   den += __shfl_xor(den, 32);
   const bool has = has_mem && den > 0.f;
   const float inv_den = has ? 1.f / den : 0.f;
-  // E = <dA, A_dot> and <dA, A_mem> of the lane's query: the lane holds 16 DB
-  // values of each transposed row
-  float e = 0.f, em = 0.f;
+  // <dA, A_mem> with A_mem^T = (colsum(M) + M^T q'^T) / den; the lane holds 16 DB
+  // values of its query's transposed row, in runs of four
+  float em = 0.f;
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
     f32x16 am = zero16();
@@ -225,80 +258,27 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
       for (int c = 0; c < KS; ++c) am = mfma32(tr_nat(ms, P, 16 * c, 32 * d, lane), qm[c], am);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int col = 32 * d + acc_row(r, hh);
-      const float da = bf2f(DO[qrow * D + col]);
-      e = __builtin_fmaf(da, o[d][r], e);
-      em = __builtin_fmaf(da, (msum[col] + am[r]) * inv_den, em);
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int col = 32 * d + 8 * j4 + 4 * hh;
+      const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + col);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) em = __builtin_fmaf(bf2f(da[j]), (msum[col + j] + am[4 * j4 + j]) * inv_den, em);
     }
   }
-  e = (e + __shfl_xor(e, 32)) * inv_l;
   em += __shfl_xor(em, 32);
-  const float Dv = (1.f - g) * e;
   const float rs = g * inv_den;
   const float dden = -g * em * inv_den;
   if (qvalid && hh == 0) {
-    a.lse[qrow] = lse2 * (1.f / kLog2e);
-    a.drow[qrow] = Dv;
     a.rs[qrow] = rs;
     a.dden[qrow] = dden;
   }
-  // the gate's share of dbeta for the wave's 32 queries: g (1 - g) sum (<dA, A_mem> - E)
+  // the gate's A_mem share of dbeta for the wave's 32 queries: g (1 - g) sum <dA, A_mem>
   {
-    const float bt = wave_sum(qvalid && hh == 0 ? em - e : 0.f);
+    const float bt = wave_sum(qvalid && hh == 0 ? em : 0.f);
     if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] = bt * g * (1.f - g);
   }
-
-  // ---- second sweep: dq^T += K^T dS^T
-  f32x16 dq[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) dq[d] = zero16();
-  cp.load(K, V, seg0);
-  cp.store(kc[0], vc[0]);
-  __syncthreads();
-  for (int kc0 = 0, buf = 0; kc0 < kend; kc0 += kChunk, buf ^= 1) {
-    const bool next = kc0 + kChunk < kend;
-    if (next) cp.load(K, V, seg0 + kc0 + kChunk);
-    if (qvalid && kc0 <= qw0 + 31) {
-      f32x16 sa[2] = {zero16(), zero16()}, pa[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int c = 0; c < KS; ++c)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          sa[kt] = mfma32(row_op(kc[buf], P, 32 * kt, 16 * c, lane), qr[c], sa[kt]);
-          pa[kt] = mfma32(row_op(vc[buf], P, 32 * kt, 16 * c, lane), dr[c], pa[kt]);
-        }
-      bf16x8 db[2][2];
-      const bool below = kc0 + kChunk - 1 <= qw0;   // every key of the chunk precedes every query
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (below) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sa[kt][r] = exp2_fast(sa[kt][r] * sl2 - lse2) * ((1.f - g) * pa[kt][r] - Dv);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool vis = kc0 + 32 * kt + acc_row(r, hh) <= qcol;
-            const float p = vis ? exp2_fast(sa[kt][r] * sl2 - lse2) : 0.f;
-            sa[kt][r] = p * ((1.f - g) * pa[kt][r] - Dv);
-          }
-        }
-        db[kt][0] = acc_op(sa[kt], 0);
-        db[kt][1] = acc_op(sa[kt], 1);
-      }
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt, 32 * d, lane), db[kt][0], dq[d]);
-          dq[d] = mfma32(tr_op(kc[buf], P, 32 * kt + 16, 32 * d, lane), db[kt][1], dq[d]);
-        }
-    }
-    if (next) cp.store(kc[buf ^ 1], vc[buf ^ 1]);
-    __syncthreads();
-  }
-  // the retrieval's dq^T = (M (rs dA)^T + dden z) sigma'(q): M rows from LDS,
-  // rs dA as the B operand from the dA rows already in registers
+  // the retrieval's dq^T = (M (rs dA)^T + dden z) sigma'(q): M rows from LDS, rs dA
+  // as the B operand from the dA rows in registers
   bf16x8 dn[KS];
 #pragma unroll
   for (int c = 0; c < KS; ++c)
@@ -313,138 +293,324 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_q_mfma_kernel(BwdArgs a) {
         for (int c = 0; c < KS; ++c) dm = mfma32(row_op(ms, P, 32 * d, 16 * c, lane), dn[c], dm);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int col = 32 * d + acc_row(r, hh);
-        const float x = bf2f(Q[qrow * D + col]);
-        const float sp = x > 0.f ? 1.f : exp_e(x);
-        a.dq_acc[qrow * D + col] = __builtin_fmaf(a.scale, dq[d][r], (dm[r] + dden * zsh[col]) * sp);
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int col = 32 * d + 8 * j4 + 4 * hh;
+        const bf16x4 xq = *reinterpret_cast<const bf16x4*>(Q + qrow * D + col);
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = bf2f(xq[j]);
+          const float sp = x > 0.f ? 1.f : exp_e(x);
+          o[j] = (dm[4 * j4 + j] + dden * zsh[col + j]) * sp;
+        }
+        *reinterpret_cast<f32x4*>(a.dq_acc + qrow * D + col) = o;
       }
     }
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_kv_mfma_kernel(BwdArgs a) {
-  constexpr int P = D + 8, KS = D / 16, DB = D / 32;
-  const int kb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
-  const bf16* Q = static_cast<const bf16*>(a.q);
-  const bf16* K = static_cast<const bf16*>(a.k);
-  const bf16* V = static_cast<const bf16*>(a.v);
-  const bf16* DO = static_cast<const bf16*>(a.dout);
-  __shared__ __attribute__((aligned(16))) bf16 qc[2][kChunk * P];
-  __shared__ __attribute__((aligned(16))) bf16 dc[2][kChunk * P];
-  __shared__ __attribute__((aligned(16))) float lc[2][kChunk];
-  __shared__ __attribute__((aligned(16))) float dcr[2][kChunk];
+__global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
+  using L = BwL<D>;
+  constexpr int KS = L::KS, DB = L::DB;
+  __shared__ __attribute__((aligned(1024))) bf16 ks0[L::TILE], ks1[L::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 vs0[L::TILE], vs1[L::TILE];
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int NT = (a.N + kBwRows - 1) / kBwRows, npair = (NT + 1) / 2;
+  const int id = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int pr = id % npair, sh = id / npair;    // sh = bh * S + s
+  const int s = sh % a.S, bh = sh / a.S, h = bh % a.H;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const int j0 = kb * kBwdBlock, kw0 = j0 + 32 * w;
-  const bool kvalid = kw0 < a.N;
-  const int kcol = kw0 + l32;                      // this lane's key (column of S)
-  const int64_t krow = seg0 + min(kcol, a.N - 1);
+  const bf16* Q = static_cast<const bf16*>(a.q);
+  const bf16* K = static_cast<const bf16*>(a.k) + seg0 * D;
+  const bf16* V = static_cast<const bf16*>(a.v) + seg0 * D;
+  const bf16* DO = static_cast<const bf16*>(a.dout);
   const float g = sigmoid_gate(a.beta[h]);
-  const float sl2 = a.scale * kLog2e;
-  bf16x8 kr[KS], vr[KS];
-#pragma unroll
-  for (int c = 0; c < KS; ++c) {
-    kr[c] = *reinterpret_cast<const bf16x8*>(K + krow * D + 16 * c + 8 * hh);
-    vr[c] = *reinterpret_cast<const bf16x8*>(V + krow * D + 16 * c + 8 * hh);
-  }
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) dk[d] = dv[d] = zero16();
-  ChunkPair<D> cp;
-  const int qbeg = min(j0, a.N - kChunk);          // queries before j0 see none of these keys
-  cp.load(Q, DO, seg0 + qbeg);
-  cp.store(qc[0], dc[0]);
-  if (threadIdx.x < kChunk) {
-    lc[0][threadIdx.x] = a.lse[seg0 + qbeg + threadIdx.x] * kLog2e;
-    dcr[0][threadIdx.x] = a.drow[seg0 + qbeg + threadIdx.x];
-  }
-  __syncthreads();
-  for (int qc0 = qbeg, buf = 0; qc0 < a.N; qc0 += kChunk, buf ^= 1) {
-    const bool next = qc0 + kChunk < a.N;
-    float nl = 0.f, nd = 0.f;
-    if (next) {
-      cp.load(Q, DO, seg0 + qc0 + kChunk);
-      if (threadIdx.x < kChunk) {
-        nl = a.lse[seg0 + qc0 + kChunk + threadIdx.x];
-        nd = a.drow[seg0 + qc0 + kChunk + threadIdx.x];
-      }
+  const float omg = 1.f - g, sl2 = a.scale * kLog2e;
+  BwOfs<D> of;
+  of.init(lane, w);
+  auto issue = [&](int st, bf16* kd, bf16* vd) {
+    bw_dma<D>(K + (int64_t)st * kBwStep * D, kd, w, of);
+    bw_dma<D>(V + (int64_t)st * kBwStep * D, vd, w, of);
+  };
+  // Steps 0 .. ns-1 over the segment's first ns * 64 keys: step st sits in slot
+  // st % 2; the loads of step st + 1 go out once every wave is done with step
+  // st - 1, and are the only ones in flight when step st + 1 begins.
+  auto ring = [&](int ns, auto&& compute) {
+    issue(0, ks0, vs0);
+    for (int st = 0; st < ns; st += 2) {
+      bw_wait_sync<0>();
+      if (st + 1 < ns) issue(st + 1, ks1, vs1);
+      compute(ks0, vs0, st);
+      if (st + 1 >= ns) break;
+      bw_wait_sync<0>();
+      if (st + 2 < ns) issue(st + 2, ks0, vs0);
+      compute(ks1, vs1, st + 1);
     }
-    // both 32-query halves of the chunk at once (a chunk wholly before the wave's
-    // keys is skipped)
-    if (kvalid && qc0 + kChunk - 1 >= kw0) {
-      const bool below = qc0 >= kw0 + 31;   // wave-uniform
-      f32x16 sa[2] = {zero16(), zero16()}, pa[2] = {zero16(), zero16()};
+    bw_wait_sync<0>();   // every wave is done with the slots before they are refilled
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = pass == 0 ? NT - 1 - pr : pr;   // the longer tile first
+    if (pass == 1 && t == NT - 1 - pr) break;
+    const int q0 = kBwRows * t, ns = min(a.N, q0 + kBwRows) / kBwStep;
+    const int qw0 = q0 + 32 * w;
+    const bool qvalid = qw0 < a.N;
+    const int qcol = qw0 + l32;
+    const int64_t qrow = seg0 + min(qcol, a.N - 1);
+    bf16x8 qr[KS];
 #pragma unroll
-      for (int c = 0; c < KS; ++c)
+    for (int c = 0; c < KS; ++c) qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
+
+    // ---- first sweep: statistics and A_dot^T of the wave's 32 query columns.
+    // m is a reference maximum (log2 units) raised only when a block's maximum
+    // exceeds it by more than 8, so probabilities stay below 2^8 and the rescale
+    // of O and l is rare; the result is exact for any m.
+    f32x16 o[DB];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          sa[qt] = mfma32(row_op(qc[buf], P, 32 * qt, 16 * c, lane), kr[c], sa[qt]);
-          pa[qt] = mfma32(row_op(dc[buf], P, 32 * qt, 16 * c, lane), vr[c], pa[qt]);
+    for (int d = 0; d < DB; ++d) o[d] = zero16();
+    float m = -__builtin_inff(), l = 0.f;
+    ring(ns, [&](const bf16* kt, const bf16* vt, int st) {
+      if (!qvalid) return;
+      of.opaque();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int kb = kBwStep * st + 32 * b;
+        if (kb > qw0) break;   // the wave's queries see no key of this block (nor the next)
+        f32x16 sc = zero16();
+#pragma unroll
+        for (int c = 0; c < KS; ++c) sc = mfma32(bw_row<D>(kt, of, c, 32 * b), qr[c], sc);
+        const bool diag = kb + 31 > qw0;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sc[r] * sl2;
+          if (diag && kb + acc_row(r, hh) > qcol) v = -__builtin_inff();
+          sc[r] = v;
+          mx = fmaxf(mx, v);
         }
-      // S: rows are queries qc0 + 32 qt + acc_row, the lane's column the key kcol
-      bf16x8 pb[2][2], db[2][2];
+        mx = fmaxf(mx, __shfl_xor(mx, 32));   // finite: key kb precedes every query of the wave
+        if (__ballot(mx > m + 8.f)) {
+          const float mn = fmaxf(m, mx);
+          const float al = bw_exp2(m - mn);
+          l *= al;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        // the rows' log-normalisers and D: accumulator rows come in runs of four
-        f32x4 lq[4], dq4[4];
+          for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          lq[j] = *reinterpret_cast<const f32x4*>(&lc[buf][32 * qt + 8 * j + 4 * hh]);
-          dq4[j] = *reinterpret_cast<const f32x4*>(&dcr[buf][32 * qt + 8 * j + 4 * hh]);
+            for (int r = 0; r < 16; ++r) o[d][r] *= al;
+          m = mn;
         }
-        f32x16 ds;
-        if (below) {   // every query of the chunk follows every key of the wave
+        float ps = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(sa[qt][r] * sl2 - lq[r >> 2][r & 3]);
-            sa[qt][r] = p;
-            ds[r] = p * ((1.f - g) * pa[qt][r] - dq4[r >> 2][r & 3]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int il = 32 * qt + acc_row(r, hh);
-            const bool vis = kcol <= qc0 + il;
-            const float p = vis ? exp2_fast(sa[qt][r] * sl2 - lq[r >> 2][r & 3]) : 0.f;
-            sa[qt][r] = p;
-            ds[r] = p * ((1.f - g) * pa[qt][r] - dq4[r >> 2][r & 3]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const float p = bw_exp2(sc[r] - m);
+          sc[r] = p;
+          ps += p;
         }
-        pb[qt][0] = acc_op(sa[qt], 0);
-        pb[qt][1] = acc_op(sa[qt], 1);
-        db[qt][0] = acc_op(ds, 0);
-        db[qt][1] = acc_op(ds, 1);
+        l += ps;
+        const bf16x8 p0 = acc_op(sc, 0), p1 = acc_op(sc, 1);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          o[d] = mfma32(bw_tr<D>(vt, of, d, 32 * b), p0, o[d]);
+          o[d] = mfma32(bw_tr<D>(vt, of, d, 32 * b + 16), p1, o[d]);
+        }
       }
+    });
+    const float lt = l + __shfl_xor(l, 32);
+    const float lse2 = m + __log2f(lt);
+    // E = <dA, A_dot>: the lane holds 16 DB values of its query's row of O^T, in
+    // runs of four
+    float e = 0.f;
+    if (qvalid) {
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt, 32 * d, lane), pb[qt][0], dv[d]);
-          dv[d] = mfma32(tr_op(dc[buf], P, 32 * qt + 16, 32 * d, lane), pb[qt][1], dv[d]);
-          dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt, 32 * d, lane), db[qt][0], dk[d]);
-          dk[d] = mfma32(tr_op(qc[buf], P, 32 * qt + 16, 32 * d, lane), db[qt][1], dk[d]);
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + 32 * d + 8 * j4 + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) e = __builtin_fmaf(bf2f(da[j]), o[d][4 * j4 + j], e);
         }
     }
-    if (next) {
-      cp.store(qc[buf ^ 1], dc[buf ^ 1]);
-      if (threadIdx.x < kChunk) {
-        lc[buf ^ 1][threadIdx.x] = nl * kLog2e;
-        dcr[buf ^ 1][threadIdx.x] = nd;
-      }
+    e = (e + __shfl_xor(e, 32)) / lt;
+    const float Dv = omg * e;
+    if (qvalid && hh == 0) {
+      a.lse[qrow] = lse2;
+      a.drow[qrow] = Dv;
     }
-    __syncthreads();
-  }
-  if (kvalid) {
+    {   // the gate's A_dot share of dbeta: - g (1 - g) sum E (the A_mem share is in place)
+      const float bt = wave_sum(qvalid && hh == 0 ? e : 0.f);
+      if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] -= bt * g * omg;
+    }
+
+    // ---- second sweep: dq^T += K^T dS^T
+    bf16x8 dr[KS];
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+    for (int c = 0; c < KS; ++c) dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
+    f32x16 dq[DB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t i = krow * D + 32 * d + acc_row(r, hh);
-        a.dv_acc[i] = (1.f - g) * dv[d][r];
-        a.dk_acc[i] = a.scale * dk[d][r];
+    for (int d = 0; d < DB; ++d) dq[d] = zero16();
+    ring(ns, [&](const bf16* kt, const bf16* vt, int st) {
+      if (!qvalid) return;
+      of.opaque();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int kb = kBwStep * st + 32 * b;
+        if (kb > qw0) break;
+        f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          sc = mfma32(bw_row<D>(kt, of, c, 32 * b), qr[c], sc);
+          dp = mfma32(bw_row<D>(vt, of, c, 32 * b), dr[c], dp);
+        }
+        const bool diag = kb + 31 > qw0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = bw_exp2(__builtin_fmaf(sc[r], sl2, -lse2));
+          if (diag && kb + acc_row(r, hh) > qcol) p = 0.f;
+          sc[r] = p * __builtin_fmaf(omg, dp[r], -Dv);
+        }
+        const bf16x8 d0 = acc_op(sc, 0), d1 = acc_op(sc, 1);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          dq[d] = mfma32(bw_tr<D>(kt, of, d, 32 * b), d0, dq[d]);
+          dq[d] = mfma32(bw_tr<D>(kt, of, d, 32 * b + 16), d1, dq[d]);
+        }
       }
+    });
+    if (qvalid) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          f32x4* p = reinterpret_cast<f32x4*>(a.dq_acc + qrow * D + 32 * d + 8 * j4 + 4 * hh);
+          f32x4 x = *p;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(a.scale, dq[d][4 * j4 + j], x[j]);
+          *p = x;
+        }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kBw) void bwd_kv2_kernel(BwdArgs a) {
+  using L = BwL<D>;
+  constexpr int KS = L::KS, DB = L::DB;
+  __shared__ __attribute__((aligned(1024))) bf16 qs0[L::TILE], qs1[L::TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 es0[L::TILE], es1[L::TILE];   // dA rows
+  __shared__ __attribute__((aligned(1024))) bf16 kst[kBwRows * D];              // the tile's keys
+  __shared__ __attribute__((aligned(16))) float ld0[2 * kBwStep], ld1[2 * kBwStep];   // log2 normaliser, D
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int NT = (a.N + kBwRows - 1) / kBwRows, npair = (NT + 1) / 2;
+  const int id = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int pr = id % npair, sh = id / npair;
+  const int s = sh % a.S, bh = sh / a.S, h = bh % a.H;
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  const bf16* Q = static_cast<const bf16*>(a.q) + seg0 * D;
+  const bf16* K = static_cast<const bf16*>(a.k) + seg0 * D;
+  const bf16* V = static_cast<const bf16*>(a.v);
+  const bf16* DO = static_cast<const bf16*>(a.dout) + seg0 * D;
+  const float g = sigmoid_gate(a.beta[h]);
+  const float omg = 1.f - g, sl2 = a.scale * kLog2e;
+  BwOfs<D> of;
+  of.init(lane, w);
+  // queries q0 + 64 st .. of step st; each wave also brings 16 of the 64 log2
+  // normalisers (waves 0-3) or D values (waves 4-7) with four lanes
+  auto issue = [&](int q0, bf16* qd, bf16* ed, float* ldd) {
+    bw_dma<D>(Q + (int64_t)q0 * D, qd, w, of);
+    bw_dma<D>(DO + (int64_t)q0 * D, ed, w, of);
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (lane < 4) {
+      const float* src = (w < 4 ? a.lse : a.drow) + seg0 + q0 + 16 * (w & 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bw_rsrc(src, 64), (INFINI_LDS void*)(ldd + 16 * w), 16, 16 * lane, 0,
+                                               0, 0);
+    }
+#endif
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = pass == 0 ? pr : NT - 1 - pr;   // the longer tile (more later queries) first
+    if (pass == 1 && t == pr) break;
+    const int k0 = kBwRows * t, nkeys = min(a.N - k0, kBwRows);
+    const int kw0 = k0 + 32 * w;
+    const bool kvalid = kw0 < a.N;
+    const int kcol = kw0 + l32;
+    const int64_t krow = seg0 + min(kcol, a.N - 1);
+    const int ns = (a.N - k0) / kBwStep;
+    // the tile's keys (64-row pieces) and the first step
+    for (int p = 0; p < nkeys / kBwStep; ++p) bw_dma<D>(K + (int64_t)(k0 + kBwStep * p) * D, kst + p * L::TILE, w, of);
+    issue(k0, qs0, es0, ld0);
+    bf16x8 vr[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c) vr[c] = *reinterpret_cast<const bf16x8*>(V + krow * D + 16 * c + 8 * hh);
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) dk[d] = dv[d] = zero16();
+    auto compute = [&](const bf16* qt, const bf16* et, const float* ldt, int st) {
+      if (!kvalid) return;
+      of.opaque();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int qb = k0 + kBwStep * st + 32 * b;
+        if (qb + 31 < kw0) continue;   // every query of the block precedes the wave's keys
+        f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          sc = mfma32(bw_row<D>(qt, of, c, 32 * b), bw_row<D>(kst, of, c, 32 * w), sc);
+          dp = mfma32(bw_row<D>(et, of, c, 32 * b), vr[c], dp);
+        }
+        const bool diag = qb < kw0 + 31;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 lq = *reinterpret_cast<const f32x4*>(ldt + 32 * b + 8 * j4 + 4 * hh);
+          const f32x4 dq = *reinterpret_cast<const f32x4*>(ldt + kBwStep + 32 * b + 8 * j4 + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * j4 + j;
+            float p = bw_exp2(__builtin_fmaf(sc[r], sl2, -lq[j]));
+            if (diag && kcol > qb + 8 * j4 + 4 * hh + j) p = 0.f;
+            sc[r] = p;
+            dp[r] = p * __builtin_fmaf(omg, dp[r], -dq[j]);
+          }
+        }
+        const bf16x8 p0 = acc_op(sc, 0), p1 = acc_op(sc, 1), d0 = acc_op(dp, 0), d1 = acc_op(dp, 1);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          dv[d] = mfma32(bw_tr<D>(et, of, d, 32 * b), p0, dv[d]);
+          dv[d] = mfma32(bw_tr<D>(et, of, d, 32 * b + 16), p1, dv[d]);
+          dk[d] = mfma32(bw_tr<D>(qt, of, d, 32 * b), d0, dk[d]);
+          dk[d] = mfma32(bw_tr<D>(qt, of, d, 32 * b + 16), d1, dk[d]);
+        }
+      }
+    };
+    // two slots: the loads of step st + 1 go out once every wave is done with
+    // step st - 1, and are the only ones in flight when step st + 1 begins
+    for (int st = 0; st < ns; st += 2) {
+      bw_wait_sync<0>();
+      if (st + 1 < ns) issue(k0 + kBwStep * (st + 1), qs1, es1, ld1);
+      compute(qs0, es0, ld0, st);
+      if (st + 1 >= ns) break;
+      bw_wait_sync<0>();
+      if (st + 2 < ns) issue(k0 + kBwStep * (st + 2), qs0, es0, ld0);
+      compute(qs1, es1, ld1, st + 1);
+    }
+    bw_wait_sync<0>();
+    if (kvalid) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int64_t i = krow * D + 32 * d + 8 * j4 + 4 * hh;
+          f32x4 xv, xk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xv[j] = omg * dv[d][4 * j4 + j];
+            xk[j] = a.scale * dk[d][4 * j4 + j];
+          }
+          *reinterpret_cast<f32x4*>(a.dv_acc + i) = xv;
+          *reinterpret_cast<f32x4*>(a.dk_acc + i) = xk;
+        }
+    }
   }
 }
 
@@ -737,11 +903,19 @@ int bwd_mfma_blocks(int N) { return (N + kBwdBlock - 1) / kBwdBlock; }
 
 template <int D>
 hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
-  hipLaunchKernelGGL(bwd_q_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  // the retrieval kernel writes rs, dden, the A_mem share of dbeta and the
+  // retrieval's dq, to which the query kernel adds; the key kernel reads the
+  // query kernel's statistics
+  const dim3 rgrid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
+  hipLaunchKernelGGL(bwd_retr_q_kernel<D>, rgrid, dim3(64 * kBwdWaves), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_kv_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  const int64_t npair = ((a.N + kBwRows - 1) / kBwRows + 1) / 2;
+  const int64_t nblk = npair * a.S * a.BH;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_q2_kernel<D>, dim3((unsigned)nblk), dim3(64 * kBw), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_kv2_kernel<D>, dim3((unsigned)nblk), dim3(64 * kBw), 0, stream, a);
   return hipGetLastError();
 }
 template hipError_t launch_backward_attention_mfma<64>(const BwdArgs&, hipStream_t);

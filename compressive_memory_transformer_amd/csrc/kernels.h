@@ -172,7 +172,8 @@ struct BwdArgs {
   float* dzr;            // [BH*S][dk]
   float* ez;             // [BH*S][dk]
   float* gzs;            // [BH*S][dk] dL/dz_s
-  float* lse;            // [BH*L] softmax log-normaliser of each row
+  float* lse;            // [BH*L] softmax log-normaliser of each row (natural log on the VALU
+                         // path, base 2 on the MFMA path)
   float* drow;           // [BH*L] <(1 - g) dA, A_dot>
   float* rs;             // [BH*L] g / den (0 without memory)
   float* dden;           // [BH*L]

@@ -32,8 +32,12 @@ CASES = [
     ("f32_ragged_resume", 32, 2, 1, 20, 24, 37, 3, "f32", 2),
     ("bf16_d64", 33, 1, 2, 64, 64, 128, 3, "bf16", 0),
     ("bf16_d128_resume", 34, 1, 2, 128, 128, 256, 3, "bf16", 2),
-    # N = 192: the last 128-row block of the MFMA kernels has two idle waves
+    # N = 192: the 256-row tile of the attention kernels has two idle waves
     ("bf16_d128_n192", 35, 2, 1, 128, 128, 192, 2, "bf16", 1),
+    # 256-row tiles of the attention kernels: three tiles (a pair and a lone
+    # middle one), and a pair whose second tile holds 64 rows
+    ("bf16_d128_n768", 37, 1, 2, 128, 128, 768, 2, "bf16", 1),
+    ("bf16_d64_n320", 38, 1, 2, 64, 64, 320, 3, "bf16", 0),
     # a bf16 shape without MFMA kernels (different widths, ragged N): the VALU kernels
     ("bf16_dk32_dv48_n80", 36, 1, 2, 32, 48, 80, 3, "bf16", 1),
 ]
