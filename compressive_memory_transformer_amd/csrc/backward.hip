@@ -740,64 +740,107 @@ __global__ __launch_bounds__(kThreads) void bwd_lin_update_kernel(BwdArgs a) {
 // !FWD: dMr_s replaced by dL/dM_s, dL/dM_0 to dM0.
 template <bool FWD>
 __global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
+  constexpr int kAP = 132;   // LDS pitch of A_s rows (16-byte aligned rows, 4 banks apart)
   const int cb = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  __shared__ float As[128][kP];
+  __shared__ __attribute__((aligned(16))) float As[128 * kAP];
   __shared__ float Xs[128][kColB + 1];
-  const int D = a.dk;
+  const int D = a.dk, na = D * D / (4 * kThreads);   // float4 pieces of A_s per thread (<= 16)
+  const int c = t % kColB, col = cb * kColB + c, x0 = t / kColB;   // the thread's rows: x0 + 16 r
+  const bool cok = col < a.dv;
   for (int i = t; i < 128 * kColB; i += kThreads) {
-    const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
+    const int r = i / kColB, cc = i % kColB, cl = cb * kColB + cc;
     float x = 0.f;
-    if (r < D && col < a.dv) {
-      const int64_t m = ((int64_t)bh * D + r) * a.dv + col;
+    if (r < D && cl < a.dv) {
+      const int64_t m = ((int64_t)bh * D + r) * a.dv + cl;
       x = FWD ? a.M0[m] : (a.dM ? a.dM[m] : 0.f);
     }
-    Xs[r][c] = x;
+    Xs[r][cc] = x;
   }
-  for (int k = 0; k < a.S; ++k) {
-    const int s = FWD ? k : a.S - 1 - k;
-    const bool first = is_first(a, s);
+  // The next segment's A_s and additive term are fetched into registers while
+  // the current product runs.
+  f32x4 an[16];
+  float ad[8];
+  auto seg_of = [&](int k) __attribute__((always_inline)) { return FWD ? k : a.S - 1 - k; };
+  auto fetch = [&](int k) __attribute__((always_inline)) {
+    const int s = seg_of(k);
     const int64_t seg = (int64_t)bh * a.S + s;
-    __syncthreads();
-    if (!first)
-      for (int i = t; i < D * D; i += kThreads) As[i / D][i % D] = a.Amat[seg * D * D + i];
-    float add[8];
+    if (!is_first(a, s)) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.Amat + seg * D * D);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < na) an[j] = src[t + kThreads * j];
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int i = t + kThreads * r, x = i / kColB, c = i % kColB, col = cb * kColB + c;
-      add[r] = 0.f;
-      if (x < D && col < a.dv) {
-        if (FWD) {
-          add[r] = a.dMr[seg * D * a.dv + (int64_t)col * D + x];   // C_s^T[col][x]
-          a.snapM[seg * D * a.dv + (int64_t)x * a.dv + col] = Xs[x][c];
-        } else {
-          float* p = a.dMr + seg * D * a.dv + (int64_t)x * a.dv + col;
-          add[r] = *p;
-          *p = Xs[x][c];
-        }
+      const int x = x0 + 16 * r;
+      ad[r] = 0.f;
+      if (x < D && cok)   // FWD: C_s^T[col][x]; else dMr_s[x][col]
+        ad[r] = FWD ? a.dMr[seg * D * a.dv + (int64_t)col * D + x] : a.dMr[seg * D * a.dv + (int64_t)x * a.dv + col];
+    }
+  };
+  auto put_a = [&](int k) __attribute__((always_inline)) {
+    if (is_first(a, seg_of(k))) return;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < na) {
+        const int i = t + kThreads * j, r = i / (D / 4), q = i % (D / 4);
+        *reinterpret_cast<f32x4*>(&As[r * kAP + 4 * q]) = an[j];
+      }
+  };
+  fetch(0);
+  put_a(0);
+  __syncthreads();
+  for (int k = 0; k < a.S; ++k) {
+    const int s = seg_of(k);
+    const bool first = is_first(a, s);
+    const int64_t seg = (int64_t)bh * a.S + s;
+    float add[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) add[r] = ad[r];
+    // the carried matrix at this segment: FWD the snapshot M_{s-1}, else dL/dM_s
+    // (in place of dMr_s, already read)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int x = x0 + 16 * r;
+      if (x < D && cok) {
+        float* dst = (FWD ? a.snapM : a.dMr) + seg * D * a.dv + (int64_t)x * a.dv + col;
+        *dst = Xs[x][c];
       }
     }
-    __syncthreads();
+    if (k + 1 < a.S) fetch(k + 1);
+    float acc[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+    if (!first) {
+      for (int y = 0; y < D; y += 4) {
+        const float x0v = Xs[y][c], x1v = Xs[y + 1][c], x2v = Xs[y + 2][c], x3v = Xs[y + 3][c];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          if (r < D / 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&As[(x0 + 16 * r) * kAP + y]);
+            acc[r] = __builtin_fmaf(av[0], x0v, acc[r]);
+            acc[r] = __builtin_fmaf(av[1], x1v, acc[r]);
+            acc[r] = __builtin_fmaf(av[2], x2v, acc[r]);
+            acc[r] = __builtin_fmaf(av[3], x3v, acc[r]);
+          }
+      }
+    }
     float nx[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int i = t + kThreads * r, x = i / kColB, c = i % kColB;
-      float acc = 0.f;
-      if (!first && x < D)
-        for (int y = 0; y < D; ++y) acc = __builtin_fmaf(As[x][y], Xs[y][c], acc);
-      nx[r] = Xs[x][c] - acc + add[r];
+      const int x = x0 + 16 * r;
+      nx[r] = x < D ? Xs[x][c] - acc[r] + add[r] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int i = t + kThreads * r;
-      Xs[i / kColB][i % kColB] = nx[r];
-    }
+    for (int r = 0; r < 8; ++r) Xs[x0 + 16 * r][c] = nx[r];
+    if (k + 1 < a.S) put_a(k + 1);
+    __syncthreads();
   }
-  __syncthreads();
   if (!FWD && a.dM0)
     for (int i = t; i < D * kColB; i += kThreads) {
-      const int r = i / kColB, c = i % kColB, col = cb * kColB + c;
-      if (col < a.dv) a.dM0[((int64_t)bh * D + r) * a.dv + col] = Xs[r][c];
+      const int r = i / kColB, cc = i % kColB, cl = cb * kColB + cc;
+      if (cl < a.dv) a.dM0[((int64_t)bh * D + r) * a.dv + cl] = Xs[r][cc];
     }
 }
 
