@@ -577,6 +577,51 @@ __global__ __launch_bounds__(kThreads) void bwd_ez_kernel(BwdArgs a) {
   if (half == 0 && x < a.dk) a.ez[((int64_t)bh * a.S + s) * a.dk + x] = acc + part[x];
 }
 
+// bf16 keys, d_key = D in {64, 128}: the same sums with 16-byte key loads; thread
+// t takes columns 8 (t % (D / 8)) .. + 7 of rows t / (D / 8) + G i (G row groups,
+// four rows in flight), and the groups meet in LDS.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_ez_vec_kernel(BwdArgs a) {
+  constexpr int C8 = D / 8, G = kThreads / C8;
+  const int s = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, c8 = t % C8, g = t / C8;
+  const bf16* K = static_cast<const bf16*>(a.k);
+  __shared__ float red[G * D];
+  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (!is_first(a, s)) {
+    int r = g;
+    for (; r + 3 * G < a.N; r += 4 * G) {
+      bf16x8 kx[4];
+      float dw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t row = seg0 + r + G * u;
+        kx[u] = *reinterpret_cast<const bf16x8*>(K + row * D + 8 * c8);
+        dw[u] = a.de[row];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(dw[u], sig(bf2f(kx[u][j])), acc[j]);
+    }
+    for (; r < a.N; r += G) {
+      const int64_t row = seg0 + r;
+      const bf16x8 kx = *reinterpret_cast<const bf16x8*>(K + row * D + 8 * c8);
+      const float dw = a.de[row];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(dw, sig(bf2f(kx[j])), acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[g * D + 8 * c8 + j] = acc[j];
+  __syncthreads();
+  if (t < D) {
+    float sum = 0.f;
+    for (int q = 0; q < G; ++q) sum += red[q * D + t];
+    a.ez[((int64_t)bh * a.S + s) * D + t] = sum;
+  }
+}
+
 // grid (BH), 128 threads: gzs_s = dL/dz_s; dz0 = dL/dz_0.
 __global__ __launch_bounds__(128) void bwd_zchain_kernel(BwdArgs a) {
   const int bh = blockIdx.x, x = threadIdx.x;
@@ -1023,7 +1068,12 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
                         0, stream, a);
     }
   }
-  INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+  if (delta_mfma) {
+    if (a.dk == 128) INFINI_BWD_LAUNCH(bwd_ez_vec_kernel<128>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+    else INFINI_BWD_LAUNCH(bwd_ez_vec_kernel<64>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+  } else {
+    INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+  }
   INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
   {
     const uintptr_t al = 4 * sizeof(T) - 1;

@@ -85,6 +85,41 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row of accumulator element r for lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Stages a row-major fp32 [D][D] matrix into LDS as bf16 (pitch D + 8) and its
+// column sums in fp32, by a workgroup of 256 threads: thread t loads the 16-byte
+// pieces t + 256 j (always the same four columns), keeps their partial column
+// sums, and the 256 / (D / 4) row groups meet in `red` (1024 floats).  Ends with
+// a barrier.
+template <int D>
+__device__ __forceinline__ void stage_mat(const float* X, bf16* xs, float* colsum, float* red) {
+  constexpr int P = D + 8, Q4 = D / 4, NJ = D * D / 4 / 256, G = 256 / Q4;
+  static_assert(G * D == 1024, "row groups x columns fill the reduction array");
+  const int t = threadIdx.x, c4 = t % Q4, r0 = t / Q4;
+  f32x4 v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) v[j] = reinterpret_cast<const f32x4*>(X)[t + 256 * j];
+  f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    bf16x4 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cs[e] += v[j][e];
+      b[e] = f2bf(v[j][e]);
+    }
+    *reinterpret_cast<bf16x4*>(xs + (r0 + G * j) * P + 4 * c4) = b;
+  }
+  *reinterpret_cast<f32x4*>(red + r0 * D + 4 * c4) = cs;
+  __syncthreads();
+  if (t < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) sum += red[g * D + t];
+    colsum[t] = sum;
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------- streamed tiles of the attention kernels
 constexpr int kBw = 8;                  // waves per workgroup
 constexpr int kBwRows = 32 * kBw;       // stationary rows per tile
@@ -212,7 +247,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_retr_q_kernel(BwdArgs a) {
   const bf16* Q = static_cast<const bf16*>(a.q);
   const bf16* DO = static_cast<const bf16*>(a.dout);
   __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
-  __shared__ float msum[D], zsh[D], ctmp[128];
+  __shared__ __attribute__((aligned(16))) float red[1024];
+  __shared__ float msum[D], zsh[D];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int qw0 = qb * kBwdBlock + 32 * w;
   const bool has_mem = a.seg_base + s > 0;
@@ -225,13 +261,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_retr_q_kernel(BwdArgs a) {
     qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
     dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
   }
-  {
-    const float* Mg = a.snapM + ((int64_t)bh * a.S + s) * D * D;
-    for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) ms[(x / D) * P + x % D] = f2bf(Mg[x]);
-    if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
-    block_colsum256(Mg, D, D, msum, ctmp);
-  }
-  __syncthreads();
+  if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
+  stage_mat<D>(a.snapM + ((int64_t)bh * a.S + s) * D * D, ms, msum, red);
   // q' = sigma(q) - 1 and the denominator sigma(q) z of the lane's query
   bf16x8 qm[KS];
   float den = 0.f;
@@ -625,10 +656,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(Bwd
   const bf16* K = static_cast<const bf16*>(a.k);
   const bf16* V = static_cast<const bf16*>(a.v);
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
-  __shared__ float gsum[D], ctmp[128];
-  const float* Gg = a.dMr + ((int64_t)bh * a.S + s) * D * D;
-  for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) gs[(x / D) * P + x % D] = f2bf(Gg[x]);
-  block_colsum256(Gg, D, D, gsum, ctmp);
+  __shared__ __attribute__((aligned(16))) float red[1024];
+  __shared__ float gsum[D];
+  stage_mat<D>(a.dMr + ((int64_t)bh * a.S + s) * D * D, gs, gsum, red);
   const int t0 = rb * kBwdBlock + 32 * w;           // the wave's first token in the segment
   const bool valid = t0 < a.N;
   const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
@@ -807,17 +837,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
   const bf16* V = static_cast<const bf16*>(a.v);
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
   __shared__ __attribute__((aligned(16))) bf16 msb[D * P];
-  __shared__ float gsum[D], msum[D], zsh[D], ctmp[128], ctmp2[128];
+  __shared__ __attribute__((aligned(16))) float red[1024];
+  __shared__ float gsum[D], msum[D], zsh[D];
   const int64_t seg = (int64_t)bh * a.S + s;
-  const float* Gg = a.dMr + seg * D * D;
-  const float* Mg = a.snapM + seg * D * D;
-  for (int x = threadIdx.x; x < D * D; x += 64 * kBwdWaves) {
-    gs[(x / D) * P + x % D] = f2bf(Gg[x]);
-    msb[(x / D) * P + x % D] = f2bf(Mg[x]);
-  }
   if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[seg * D + threadIdx.x];
-  block_colsum256(Gg, D, D, gsum, ctmp);
-  block_colsum256(Mg, D, D, msum, ctmp2);
+  stage_mat<D>(a.dMr + seg * D * D, gs, gsum, red);
+  stage_mat<D>(a.snapM + seg * D * D, msb, msum, red);
   const bool first = a.seg_base + s == 0;
   const int t0 = rb * kBwdBlock + 32 * w;
   const bool valid = t0 < a.N;
@@ -852,14 +877,22 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
     }
     f32x16 u, dw;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int col = 32 * d + acc_row(r, hh);
-      const float dut = du[r] + gsum[col];
-      const float R = first ? 0.f : (re[r] + msum[col]) * wt;
-      a.dv_acc[row * D + col] += dut;
-      u[r] = bf2f(V[row * D + col]) - R;
-      dw[r] = -dut * wt;
-      de = __builtin_fmaf(dut, R, de);
+    for (int j4 = 0; j4 < 4; ++j4) {   // accumulator rows come in runs of four columns
+      const int col = 32 * d + 8 * j4 + 4 * hh;
+      f32x4* dvp = reinterpret_cast<f32x4*>(a.dv_acc + row * D + col);
+      f32x4 dva = *dvp;
+      const bf16x4 vv = *reinterpret_cast<const bf16x4*>(V + row * D + col);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j4 + j;
+        const float dut = du[r] + gsum[col + j];
+        const float R = first ? 0.f : (re[r] + msum[col + j]) * wt;
+        dva[j] += dut;
+        u[r] = bf2f(vv[j]) - R;
+        dw[r] = -dut * wt;
+        de = __builtin_fmaf(dut, R, de);
+      }
+      *dvp = dva;
     }
     ub[d][0] = acc_op(u, 0);
     ub[d][1] = acc_op(u, 1);
@@ -895,7 +928,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
         if (!first) df = mfma32(ma, db[d][ks], df);
       }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) a.dfk_acc[row * D + 32 * d2 + acc_row(r, hh)] = df[r];
+    for (int j4 = 0; j4 < 4; ++j4) {
+      f32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = df[4 * j4 + j];
+      *reinterpret_cast<f32x4*>(a.dfk_acc + row * D + 32 * d2 + 8 * j4 + 4 * hh) = o;
+    }
   }
 }
 
