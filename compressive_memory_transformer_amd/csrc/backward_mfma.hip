@@ -713,24 +713,27 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
   const bf16* Y = static_cast<const bf16*>(a.dout);
   __shared__ __attribute__((aligned(16))) bf16 xs[kChunk * P];
   __shared__ __attribute__((aligned(16))) bf16 ys[kChunk * P];
-  __shared__ float zsh[D], ush[D], wsh[kChunk], dsh[kChunk];
+  __shared__ float zsh[D], ush[D], wred[kChunk];
+  __shared__ float red[kChunk * D];   // the column sums' partials, one row per token thread
   const int64_t seg = (int64_t)bh * a.S + s;
   float* out = (RETR ? a.dMr : a.Amat) + seg * D * D;
   if (!RETR && a.seg_base + s == 0) {
     for (int i = t; i < D * D; i += 64 * kBwdWaves) out[i] = 0.f;
     return;
   }
-  if (t < D) {
-    zsh[t] = RETR ? 0.f : a.snapz[seg * D + t];
-    ush[t] = 0.f;
-  }
+  if (t < D) zsh[t] = RETR ? 0.f : a.snapz[seg * D + t];
   f32x16 acc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = zero16();
-  float wsum = 0.f, upart = 0.f, zpart = 0.f;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
   const int tt = t >> 2, qq = t & 3;   // staging: token tt, quarter qq of its row
   constexpr int QW = D / 4;
+  // column sums, accumulated by each staging thread over its tokens (from the
+  // fp32 inputs for the retrieval: sum_t rs_t dA_t and sum_t dden_t sigma(q_t);
+  // from the bf16 K' of the product for A_s) and met across the threads at the end
+  float up[QW], zp[QW], wsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < QW; ++j) up[j] = zp[j] = 0.f;
   __syncthreads();
   for (int t0 = 0; t0 < a.N; t0 += kChunk) {
     const int64_t row = seg0 + t0 + tt;
@@ -747,14 +750,16 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
         if (!RETR) e = __builtin_fmaf(f + 1.f, zsh[qq * QW + 8 * i + j], e);
       }
     }
-    float wt;
+    float wt, dd = 0.f;
     if (RETR) {
       wt = a.rs[row];
+      dd = a.dden[row];
     } else {
       e += __shfl_xor(e, 1);
       e += __shfl_xor(e, 2);
       wt = e > 0.f ? 1.f / e : 0.f;
     }
+    wsum += wt;
 #pragma unroll
     for (int i = 0; i < QW / 8; ++i) {
       bf16x8 xb, yb;
@@ -762,39 +767,24 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
         const bf16x8 y = *reinterpret_cast<const bf16x8*>(Y + row * D + qq * QW + 8 * i);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+          const float yv = bf2f(y[j]);
           xb[j] = f2bf(xv[8 * i + j]);
-          yb[j] = f2bf(wt * bf2f(y[j]));
+          yb[j] = f2bf(wt * yv);
+          up[8 * i + j] = __builtin_fmaf(wt, yv, up[8 * i + j]);
+          zp[8 * i + j] = __builtin_fmaf(dd, xv[8 * i + j] + 1.f, zp[8 * i + j]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           xb[j] = f2bf(xv[8 * i + j]);
           yb[j] = f2bf(wt * xv[8 * i + j]);
+          up[8 * i + j] = __builtin_fmaf(wt, bf2f(xb[j]), up[8 * i + j]);
         }
       }
       *reinterpret_cast<bf16x8*>(xs + tt * P + qq * QW + 8 * i) = xb;
       *reinterpret_cast<bf16x8*>(ys + tt * P + qq * QW + 8 * i) = yb;
     }
-    if (qq == 0) {
-      wsh[tt] = wt;
-      if (RETR) dsh[tt] = a.dden[row];
-    }
     __syncthreads();
-    if (t < D) {
-      if (RETR) {
-        // fp32 column sums from the inputs: sum_t rs_t dA_t and sum_t dden_t sigma(q_t)
-        for (int r = 0; r < kChunk; ++r) {
-          const int64_t rr = seg0 + t0 + r;
-          upart = __builtin_fmaf(wsh[r], bf2f(Y[rr * D + t]), upart);
-          const float q = bf2f(X[rr * D + t]);
-          zpart = __builtin_fmaf(dsh[r], q > 0.f ? q + 1.f : exp_e(q), zpart);
-        }
-      } else {
-        for (int r = 0; r < kChunk; ++r) upart = __builtin_fmaf(wsh[r], bf2f(xs[r * P + t]), upart);
-      }
-    }
-    if (!RETR && t == 0)
-      for (int r = 0; r < kChunk; ++r) wsum += wsh[r];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tile = w * TPW + i, bi = tile / NT, bj = tile % NT;
@@ -804,11 +794,28 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
-  if (t < D) ush[t] = upart;
-  if (t == 0) wsh[0] = wsum;
-  if (RETR && t < D) a.dzr[seg * D + t] = zpart;
+#pragma unroll
+  for (int j = 0; j < QW; ++j) red[tt * D + qq * QW + j] = up[j];
+  if (qq == 0) wred[tt] = wsum;
   __syncthreads();
-  const float ws = wsh[0];
+  float colsum = 0.f, wtot = 0.f;
+  if (t < D)
+    for (int r = 0; r < kChunk; ++r) colsum += red[r * D + t];
+  for (int r = 0; r < kChunk; ++r) wtot += wred[r];
+  if (RETR) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < QW; ++j) red[tt * D + qq * QW + j] = zp[j];
+    __syncthreads();
+    if (t < D) {
+      float z = 0.f;
+      for (int r = 0; r < kChunk; ++r) z += red[r * D + t];
+      a.dzr[seg * D + t] = z;
+    }
+  }
+  if (t < D) ush[t] = colsum;
+  __syncthreads();
+  const float ws = wtot;
   const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
