@@ -917,10 +917,12 @@ __device__ __forceinline__ void st4(bf16* p, const float (&x)[4]) {
 __device__ __forceinline__ void st4(float* p, const float (&x)[4]) {
   *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
 }
-template <typename T, int W>
+// DIRECT (the bf16 MFMA path): dq and dv were written in their final form by the
+// query kernel and the update kernels; only dk is left.
+template <typename T, int W, bool DIRECT>
 __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdArgs a) {
   const int gk = a.dk / W, gv = a.dv / W;
-  const int64_t rows = (int64_t)a.BH * a.L, nk = rows * gk, nv = rows * gv;
+  const int64_t rows = (int64_t)a.BH * a.L, nk = rows * gk, nv = DIRECT ? 0 : rows * gv;
   const T* K = static_cast<const T*>(a.k);
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nk + nv; i += (int64_t)gridDim.x * kThreads) {
     if (i < nk) {
@@ -935,16 +937,16 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdArgs a) {
       for (int j = 0; j < W; ++j) {
         const float dfk = __builtin_fmaf(de, a.snapz[zi + j], a.dfk_acc[ri + j] + a.gzs[zi + j]);
         dk[j] = a.dk_acc[ri + j] + dfk * sig_prime(ld(K, ri + j));
-        dq[j] = a.dq_acc[ri + j];
+        dq[j] = DIRECT ? 0.f : a.dq_acc[ri + j];
       }
       if constexpr (W == 4) {
         st4(static_cast<T*>(a.dk_out) + ri, dk);
-        st4(static_cast<T*>(a.dq_out) + ri, dq);
+        if (!DIRECT) st4(static_cast<T*>(a.dq_out) + ri, dq);
       } else {
 #pragma unroll
         for (int j = 0; j < W; ++j) {
           st(static_cast<T*>(a.dk_out), ri + j, dk[j]);
-          st(static_cast<T*>(a.dq_out), ri + j, dq[j]);
+          if (!DIRECT) st(static_cast<T*>(a.dq_out), ri + j, dq[j]);
         }
       }
     } else {
@@ -1080,10 +1082,12 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     const bool vec = a.dk % 4 == 0 && a.dv % 4 == 0 &&
                      ((reinterpret_cast<uintptr_t>(a.dq_out) | reinterpret_cast<uintptr_t>(a.dk_out) |
                        reinterpret_cast<uintptr_t>(a.dv_out)) & al) == 0;
-    const int64_t n = (int64_t)a.BH * a.L * (a.dk + a.dv) / (vec ? 4 : 1);
+    // the MFMA path wrote dq and dv already (its outputs are 16-byte aligned)
+    const int64_t n = (int64_t)a.BH * a.L * (a.dk + (mfma ? 0 : a.dv)) / (vec ? 4 : 1);
     const dim3 grid((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1 << 20));
-    if (vec) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4>), grid, dim3(kThreads), 0, stream, a);
-    else INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 1>), grid, dim3(kThreads), 0, stream, a);
+    if (mfma) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4, true>), grid, dim3(kThreads), 0, stream, a);
+    else if (vec) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4, false>), grid, dim3(kThreads), 0, stream, a);
+    else INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 1, false>), grid, dim3(kThreads), 0, stream, a);
   }
   INFINI_BWD_LAUNCH(bwd_dbeta_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, stream, a);
 #undef INFINI_BWD_LAUNCH

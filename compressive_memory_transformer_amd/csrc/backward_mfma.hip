@@ -508,16 +508,17 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
         }
       }
     });
-    if (qvalid) {
+    if (qvalid) {   // the final dq: the retrieval's share plus scale * dS K, in bf16
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
-          f32x4* p = reinterpret_cast<f32x4*>(a.dq_acc + qrow * D + 32 * d + 8 * j4 + 4 * hh);
-          f32x4 x = *p;
+          const int64_t i = qrow * D + 32 * d + 8 * j4 + 4 * hh;
+          const f32x4 x = *reinterpret_cast<const f32x4*>(a.dq_acc + i);
+          bf16x4 o;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(a.scale, dq[d][4 * j4 + j], x[j]);
-          *p = x;
+          for (int j = 0; j < 4; ++j) o[j] = f2bf(__builtin_fmaf(a.scale, dq[d][4 * j4 + j], x[j]));
+          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dq_out) + i) = o;
         }
     }
   }
@@ -688,7 +689,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(Bwd
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t i = (out0 + acc_row(r, hh)) * D + col;
-      a.dv_acc[i] += gsum[col] + dv[r];
+      static_cast<bf16*>(a.dv_out)[i] = f2bf(a.dv_acc[i] + (gsum[col] + dv[r]));   // the final dv
       a.dfk_acc[i] = df[r];
     }
   }
@@ -886,20 +887,20 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {   // accumulator rows come in runs of four columns
       const int col = 32 * d + 8 * j4 + 4 * hh;
-      f32x4* dvp = reinterpret_cast<f32x4*>(a.dv_acc + row * D + col);
-      f32x4 dva = *dvp;
+      const f32x4 dvl = *reinterpret_cast<const f32x4*>(a.dv_acc + row * D + col);   // local attention's dv
+      bf16x4 dvo;
       const bf16x4 vv = *reinterpret_cast<const bf16x4*>(V + row * D + col);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * j4 + j;
         const float dut = du[r] + gsum[col + j];
         const float R = first ? 0.f : (re[r] + msum[col + j]) * wt;
-        dva[j] += dut;
+        dvo[j] = f2bf(dvl[j] + dut);
         u[r] = bf2f(vv[j]) - R;
         dw[r] = -dut * wt;
         de = __builtin_fmaf(dut, R, de);
       }
-      *dvp = dva;
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dv_out) + row * D + col) = dvo;   // the final dv
     }
     ub[d][0] = acc_op(u, 0);
     ub[d][1] = acc_op(u, 1);
