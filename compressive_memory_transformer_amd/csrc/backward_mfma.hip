@@ -3,7 +3,7 @@
 // "精读笔记：Infini-attention", section 3.1 with the mask of section 3.8 step 2),
 // and the retrieval's share of the query gradient (section 3.3).
 //
-//   bwd_retr_q_kernel<D>: one workgroup (4 waves) per 128 queries of a segment,
+//   bwd_retr_q_kernel<D>: one workgroup (8 waves) per 256 queries of a segment,
 //     M_{s-1} staged in LDS as bf16.  Per query: A_mem = (colsum(M) +
 //     (sigma(q) - 1) M) / (sigma(q) z) (the column sums in fp32 keep sigma(q) ~ 1
 //     from costing bf16 precision), <dA, A_mem>, rs = g / den, dden, the
@@ -39,6 +39,8 @@
 // the chunk permutation, which makes 16 consecutive rows of one logical chunk
 // and 4 consecutive rows x 4 consecutive chunks each hit 16 distinct bank
 // groups.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_ops.h"
@@ -47,8 +49,11 @@ namespace infini {
 
 namespace {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdBlock = 32 * kBwdWaves;   // rows per workgroup of the 4-wave kernels
+constexpr int kBwdWaves = 4;                // waves of the Gram kernel's workgroup
+constexpr int kUpdWaves = 8;                // waves of the retrieval and linear-update kernels
+constexpr int kUpdBlock = 32 * kUpdWaves;   // tokens (or queries) per workgroup of those
+constexpr int kDuWaves = 4;                 // waves of the delta-update kernel (two staged
+constexpr int kDuBlock = 32 * kDuWaves;     // matrices: two workgroups per CU at this size)
 constexpr int kChunk = 64;                  // tokens per step of the Gram kernel
 
 __device__ __forceinline__ bf16x8 row_op(const bf16* X, int pitch, int r0, int k0, int lane) {
@@ -86,18 +91,18 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // Stages a row-major fp32 [D][D] matrix into LDS as bf16 (pitch D + 8) and its
-// column sums in fp32, by a workgroup of 256 threads: thread t loads the 16-byte
-// pieces t + 256 j (always the same four columns), keeps their partial column
-// sums, and the 256 / (D / 4) row groups meet in `red` (1024 floats).  Ends with
-// a barrier.
-template <int D>
+// column sums in fp32, by a workgroup of NT threads: thread t loads the 16-byte
+// pieces t + NT j (always the same four columns), keeps their partial column
+// sums, and the NT / (D / 4) row groups meet in `red` (4 NT floats).  Ends with a
+// barrier.
+template <int D, int NT>
 __device__ __forceinline__ void stage_mat(const float* X, bf16* xs, float* colsum, float* red) {
-  constexpr int P = D + 8, Q4 = D / 4, NJ = D * D / 4 / 256, G = 256 / Q4;
-  static_assert(G * D == 1024, "row groups x columns fill the reduction array");
+  constexpr int P = D + 8, Q4 = D / 4, NJ = D * D / 4 / NT, G = NT / Q4;
+  static_assert(G * D == 4 * NT && NJ * NT * 4 == D * D, "row groups x columns fill the reduction array");
   const int t = threadIdx.x, c4 = t % Q4, r0 = t / Q4;
   f32x4 v[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) v[j] = reinterpret_cast<const f32x4*>(X)[t + 256 * j];
+  for (int j = 0; j < NJ; ++j) v[j] = reinterpret_cast<const f32x4*>(X)[t + NT * j];
   f32x4 cs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -240,17 +245,17 @@ __device__ __forceinline__ float bw_exp2(float x) { return __builtin_amdgcn_exp2
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_retr_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kUpdWaves) void bwd_retr_q_kernel(BwdArgs a) {
   constexpr int P = D + 8, KS = D / 16, DB = D / 32;
   const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
   const bf16* Q = static_cast<const bf16*>(a.q);
   const bf16* DO = static_cast<const bf16*>(a.dout);
   __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
-  __shared__ __attribute__((aligned(16))) float red[1024];
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * kUpdWaves];
   __shared__ float msum[D], zsh[D];
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const int qw0 = qb * kBwdBlock + 32 * w;
+  const int qw0 = qb * kUpdBlock + 32 * w;
   const bool has_mem = a.seg_base + s > 0;
   const bool qvalid = qw0 < a.N;
   const int64_t qrow = seg0 + min(qw0 + l32, a.N - 1);
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_retr_q_kernel(BwdArgs a) {
     dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
   }
   if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
-  stage_mat<D>(a.snapM + ((int64_t)bh * a.S + s) * D * D, ms, msum, red);
+  stage_mat<D, 64 * kUpdWaves>(a.snapM + ((int64_t)bh * a.S + s) * D * D, ms, msum, red);
   // q' = sigma(q) - 1 and the denominator sigma(q) z of the lane's query
   bf16x8 qm[KS];
   float den = 0.f;
@@ -646,21 +651,21 @@ __global__ __launch_bounds__(64 * kBw) void bwd_kv2_kernel(BwdArgs a) {
   }
 }
 
-// Linear rule, per 128 tokens of a segment (one wave per 32), given G = dL/dM_s
+// Linear rule, per 256 tokens of a segment (one wave per 32), given G = dL/dM_s
 // (fp32 [d_key][d_value], staged in LDS as bf16 with fp32 column sums):
 //   dv += sigma(K) G = colsum(G) + (sigma(K) - 1) G;   d sigma(K) = V G^T.
 template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kUpdWaves) void bwd_lin_update_mfma_kernel(BwdArgs a) {
   constexpr int P = D + 8, KS = D / 16, DB = D / 32;
   const int rb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
   const bf16* K = static_cast<const bf16*>(a.k);
   const bf16* V = static_cast<const bf16*>(a.v);
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
-  __shared__ __attribute__((aligned(16))) float red[1024];
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * kUpdWaves];
   __shared__ float gsum[D];
-  stage_mat<D>(a.dMr + ((int64_t)bh * a.S + s) * D * D, gs, gsum, red);
-  const int t0 = rb * kBwdBlock + 32 * w;           // the wave's first token in the segment
+  stage_mat<D, 64 * kUpdWaves>(a.dMr + ((int64_t)bh * a.S + s) * D * D, gs, gsum, red);
+  const int t0 = rb * kUpdBlock + 32 * w;           // the wave's first token in the segment
   const bool valid = t0 < a.N;
   const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
   bf16x8 kp[KS], vr[KS];
@@ -695,8 +700,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_lin_update_mfma_kernel(Bwd
   }
 }
 
-// A per-segment Gram product on MFMA, one workgroup per segment, 64 tokens per
-// step, both operands read transposed from LDS:
+// A per-segment Gram product on MFMA, two workgroups per segment (each half of
+// the 64-token chunks; the second writes its partial into gpart and a combining
+// pass adds it, so the sums keep a fixed order), both operands read transposed
+// from LDS:
 //   GRAM = false (delta rule): A_s = sigma(K)^T diag(w) sigma(K), w_t = 1 / (sigma(K_t) .
 //     z_{s-1}) (0 in a stream's first segment).  With sigma(K) = 1 + K' (K' rounded
 //     to bf16 for the product) A_s = (sum w) 1 1^T + 1 u^T + u 1^T + K'^T diag(w) K',
@@ -708,7 +715,7 @@ template <int D, bool RETR>
 __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
   constexpr int P = D + 8, NT = D / 32;
   constexpr int TPW = NT * NT / kBwdWaves > 0 ? NT * NT / kBwdWaves : 1;   // output tiles per wave
-  const int s = blockIdx.x, bh = blockIdx.y;
+  const int s = blockIdx.x, bh = blockIdx.y, part = blockIdx.z;   // part: which half of the token chunks
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const bf16* X = static_cast<const bf16*>(RETR ? a.q : a.k);
   const bf16* Y = static_cast<const bf16*>(a.dout);
@@ -717,7 +724,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
   __shared__ float zsh[D], ush[D], wred[kChunk];
   __shared__ float red[kChunk * D];   // the column sums' partials, one row per token thread
   const int64_t seg = (int64_t)bh * a.S + s;
-  float* out = (RETR ? a.dMr : a.Amat) + seg * D * D;
+  const int64_t nseg = (int64_t)a.BH * a.S;
+  // the first half writes the result in place, the second its partial into gpart
+  float* out = (part ? a.gpart : (RETR ? a.dMr : a.Amat)) + seg * D * D;
+  float* zout = part ? a.gpart + nseg * D * D : a.dzr;
   if (!RETR && a.seg_base + s == 0) {
     for (int i = t; i < D * D; i += 64 * kBwdWaves) out[i] = 0.f;
     return;
@@ -736,7 +746,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
 #pragma unroll
   for (int j = 0; j < QW; ++j) up[j] = zp[j] = 0.f;
   __syncthreads();
-  for (int t0 = 0; t0 < a.N; t0 += kChunk) {
+  const int nch = a.N / kChunk, chalf = (nch + 1) / 2;
+  const int c0 = part ? chalf : 0, c1 = part ? nch : chalf;
+  for (int t0 = c0 * kChunk; t0 < c1 * kChunk; t0 += kChunk) {
     const int64_t row = seg0 + t0 + tt;
     float xv[QW];
     float e = 0.f;
@@ -811,7 +823,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
     if (t < D) {
       float z = 0.f;
       for (int r = 0; r < kChunk; ++r) z += red[r * D + t];
-      a.dzr[seg * D + t] = z;
+      zout[seg * D + t] = z;
     }
   }
   if (t < D) ush[t] = colsum;
@@ -837,7 +849,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
 // Transposed products (d_value x tokens) keep every register operand in the
 // accumulator layout of the product that consumes it.
 template <int D>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kDuWaves) void bwd_delta_update_mfma_kernel(BwdArgs a) {
   constexpr int P = D + 8, KS = D / 16, DB = D / 32;
   const int rb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
@@ -845,14 +857,14 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
   const bf16* V = static_cast<const bf16*>(a.v);
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
   __shared__ __attribute__((aligned(16))) bf16 msb[D * P];
-  __shared__ __attribute__((aligned(16))) float red[1024];
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * kDuWaves];
   __shared__ float gsum[D], msum[D], zsh[D];
   const int64_t seg = (int64_t)bh * a.S + s;
   if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[seg * D + threadIdx.x];
-  stage_mat<D>(a.dMr + seg * D * D, gs, gsum, red);
-  stage_mat<D>(a.snapM + seg * D * D, msb, msum, red);
+  stage_mat<D, 64 * kDuWaves>(a.dMr + seg * D * D, gs, gsum, red);
+  stage_mat<D, 64 * kDuWaves>(a.snapM + seg * D * D, msb, msum, red);
   const bool first = a.seg_base + s == 0;
-  const int t0 = rb * kBwdBlock + 32 * w;
+  const int t0 = rb * kDuBlock + 32 * w;
   const bool valid = t0 < a.N;
   const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
   __syncthreads();
@@ -945,7 +957,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_delta_update_mfma_kernel(B
   }
 }
 
-int bwd_mfma_blocks(int N) { return (N + kBwdBlock - 1) / kBwdBlock; }
+int bwd_mfma_blocks(int N) { return (N + kUpdBlock - 1) / kUpdBlock; }
 
 template <int D>
 hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) {
@@ -953,7 +965,7 @@ hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) 
   // retrieval's dq, to which the query kernel adds; the key kernel reads the
   // query kernel's statistics
   const dim3 rgrid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
-  hipLaunchKernelGGL(bwd_retr_q_kernel<D>, rgrid, dim3(64 * kBwdWaves), 0, stream, a);
+  hipLaunchKernelGGL(bwd_retr_q_kernel<D>, rgrid, dim3(64 * kUpdWaves), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t npair = ((a.N + kBwRows - 1) / kBwRows + 1) / 2;
@@ -970,29 +982,52 @@ template hipError_t launch_backward_attention_mfma<128>(const BwdArgs&, hipStrea
 template <int D>
 hipError_t launch_backward_lin_update_mfma(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
-  hipLaunchKernelGGL(bwd_lin_update_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  hipLaunchKernelGGL(bwd_lin_update_mfma_kernel<D>, grid, dim3(64 * kUpdWaves), 0, stream, a);
   return hipGetLastError();
 }
 template hipError_t launch_backward_lin_update_mfma<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_lin_update_mfma<128>(const BwdArgs&, hipStream_t);
 
+// Adds the second halves' partials of the Gram kernel: out += part (n floats),
+// and for the retrieval zout += zpart (nz floats), four at a time.
+__global__ __launch_bounds__(256) void bwd_gram_combine_kernel(float* out, const float* part, int64_t n4,
+                                                               float* zout, const float* zpart, int64_t nz4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4 + nz4; i += (int64_t)gridDim.x * 256) {
+    f32x4* o = reinterpret_cast<f32x4*>(i < n4 ? out : zout) + (i < n4 ? i : i - n4);
+    const f32x4 p = reinterpret_cast<const f32x4*>(i < n4 ? part : zpart)[i < n4 ? i : i - n4];
+    f32x4 x = *o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] += p[e];
+    *o = x;
+  }
+}
+
+template <int D, bool RETR>
+static hipError_t launch_gram(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_gram_kernel<D, RETR>), dim3((unsigned)a.S, (unsigned)a.BH, 2u), dim3(64 * kBwdWaves), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nseg = (int64_t)a.BH * a.S, n4 = nseg * D * D / 4, nz4 = RETR ? nseg * D / 4 : 0;
+  const int64_t blocks = std::min<int64_t>((n4 + nz4 + 255) / 256, 1 << 16);
+  hipLaunchKernelGGL(bwd_gram_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     RETR ? a.dMr : a.Amat, a.gpart, n4, a.dzr, a.gpart + nseg * D * D, nz4);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_backward_delta_amat_mfma(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_gram_kernel<D, false>), dim3((unsigned)a.S, (unsigned)a.BH), dim3(64 * kBwdWaves), 0, stream,
-                     a);
-  return hipGetLastError();
+  return launch_gram<D, false>(a, stream);
 }
 template <int D>
 hipError_t launch_backward_delta_update_mfma(const BwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
-  hipLaunchKernelGGL(bwd_delta_update_mfma_kernel<D>, grid, dim3(64 * kBwdWaves), 0, stream, a);
+  const dim3 grid((unsigned)((a.N + kDuBlock - 1) / kDuBlock), (unsigned)a.S, (unsigned)a.BH);
+  hipLaunchKernelGGL(bwd_delta_update_mfma_kernel<D>, grid, dim3(64 * kDuWaves), 0, stream, a);
   return hipGetLastError();
 }
 template <int D>
 hipError_t launch_backward_retrieval_grad_mfma(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_gram_kernel<D, true>), dim3((unsigned)a.S, (unsigned)a.BH), dim3(64 * kBwdWaves), 0,
-                     stream, a);
-  return hipGetLastError();
+  return launch_gram<D, true>(a, stream);
 }
 template hipError_t launch_backward_retrieval_grad_mfma<64>(const BwdArgs&, hipStream_t);
 template hipError_t launch_backward_retrieval_grad_mfma<128>(const BwdArgs&, hipStream_t);

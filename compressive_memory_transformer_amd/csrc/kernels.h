@@ -184,6 +184,7 @@ struct BwdArgs {
   float* dfk_acc;        // [BH*L][dk] update's d sigma(K)
   float* dbeta_part;     // [BH*S][nqb]
   float* Amat;           // delta rule, bf16 path: [BH*S][dk][dk] sigma(K)^T diag(1/e) sigma(K)
+  float* gpart;          // bf16 MFMA path: [BH*S][dk][dv] + [BH*S][dk], the Gram kernels' second halves
   int B, H, BH, N, S, dk, dv, nqb;
   int64_t L, seg_base;
   int delta;
