@@ -196,10 +196,26 @@ struct ChainCfg {
   static constexpr int NT = 64 * NW;    // threads
   static constexpr int KS = D / 32;     // 32-deep steps of the product
   static constexpr int LDP = D + 4;     // row pitch of the fp32 stage of P (floats)
+  static constexpr int LDB = D + 8;     // row pitch of the bf16 planes of P (elements)
   static constexpr int TPR = NT / 16;   // threads per row of P in the snapshot pass
   static constexpr int EPR = D / TPR;   // elements per thread in the snapshot pass
   static_assert(EPR == 4, "the snapshot pass moves four elements per thread");
 };
+
+// v moved across the lanes of each row of 16 by the DPP control CTRL.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Sum over each row of 16 lanes by DPP lane moves (quad sums, then the half rows
+// and the rows by mirrors); every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_row<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_row<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_row<0x141>(x);   // row_half_mirror
+  x += dpp_row<0x140>(x);   // row_mirror
+  return x;
+}
 
 // Operands of one segment's step for one lane: row col of A_s (bf16 hi and lo,
 // k = 32 ks + 8 (l / 16) ..) and C_s^T at rows 4 (l / 16) + r, column col.
@@ -216,14 +232,16 @@ struct ChainOps {
 // One workgroup of D / 16 waves per (b, h, column block); wave w computes the
 // 16 x 16 tile (rows of the block) x (d_key columns 16 w ..) of P A on
 // v_mfma_f32_16x16x32_bf16.  Each step:
-//   P (fp32, accumulator layout in registers) -> LDS stage;
-//   snapshot of M_{s-1}: its 16 rows of M^T in bf16 with their bf16 remainders,
-//   and their sums (column sums of M over d_key), for the fused kernel;
-//   A operand P_hi, P_lo from the stage; B operands A_hi, A_lo straight from
+//   each wave writes its tile of P (fp32, accumulator layout in registers) into
+//   LDS as bf16 hi and lo planes, and its partial row sums (a 16-lane DPP sum);
+//   snapshot of M_{s-1}: its 16 rows of M^T in bf16 with their bf16 remainders
+//   straight from the planes, and their sums (column sums of M over d_key, the
+//   waves' partials added), for the fused kernel;
+//   A operand P_hi, P_lo from the planes; B operands A_hi, A_lo straight from
 //   memory (A_s is symmetric, so row n of A_s is column n);
 //   P += C_s^T - (P_hi A_hi + P_lo A_hi + P_hi A_lo).
 // The operands of the next two segments are loaded into registers ahead of
-// their step (a ring unrolled over its slots); the stage of P is double-buffered,
+// their step (a ring unrolled over its slots); the planes are double-buffered,
 // so one LDS-only barrier per step suffices.
 template <int D>
 __global__ __launch_bounds__(64 * (D / 16), 1)
@@ -231,8 +249,10 @@ void delta_chain_kernel(DeltaArgs a) {
   using C = ChainCfg<D>;
   constexpr int KS = C::KS;
   constexpr int kRing = 2;
-  __shared__ __attribute__((aligned(16))) float pl0[16 * C::LDP];
-  __shared__ __attribute__((aligned(16))) float pl1[16 * C::LDP];
+  __shared__ __attribute__((aligned(16))) float pl0[16 * C::LDP];   // P at the start and the end
+  __shared__ __attribute__((aligned(16))) bf16 ph0[16 * C::LDB], ph1[16 * C::LDB];     // P_hi per step parity
+  __shared__ __attribute__((aligned(16))) bf16 plo0[16 * C::LDB], plo1[16 * C::LDB];   // P_lo
+  __shared__ float rsum0[C::NW * 16], rsum1[C::NW * 16];   // per-wave partial row sums
   constexpr int ncb = D / 16;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   const int bh = blk / ncb, cb = blk % ncb;
@@ -270,39 +290,38 @@ void delta_chain_kernel(DeltaArgs a) {
   // snapshot pass: row t / TPR, elements 4 (t % TPR) ..
   const int srow = t / C::TPR, sk = (t % C::TPR) * C::EPR;
   auto step = [&](const ChainOps<D>& o, int s) {
-    float* pl = (s & 1) ? pl1 : pl0;
+    // P_{s-1} as bf16 hi and lo planes (each wave converts its own tile) and the
+    // wave's partial row sums (over its 16 d_key columns, exact in fp32)
+    bf16* ph_s = (s & 1) ? ph1 : ph0;
+    bf16* pl_s = (s & 1) ? plo1 : plo0;
+    float* rs_s = (s & 1) ? rsum1 : rsum0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pl[(4 * g + r) * C::LDP + col] = p[r];
+    for (int r = 0; r < 4; ++r) {
+      const bf16 hb = f2bf(p[r]);
+      ph_s[(4 * g + r) * C::LDB + col] = hb;
+      pl_s[(4 * g + r) * C::LDB + col] = f2bf(p[r] - bf2f(hb));
+      const float rr = row16_sum(p[r]);
+      if (l16 == 0) rs_s[wave * 16 + 4 * g + r] = rr;
+    }
     lds_sync();
     const int64_t shg = (int64_t)bh * S + s;
-    {
-      const f32x4 x = *(const INFINI_LDS f32x4*)(pl + srow * C::LDP + sk);
-      bf16x4 b, bl;
+    {   // snapshot of M_{s-1}: 16 rows of M^T in bf16 hi and lo, and their sums
+      const bf16x4 hv = *(const INFINI_LDS bf16x4*)(ph_s + srow * C::LDB + sk);
+      const bf16x4 lv = *(const INFINI_LDS bf16x4*)(pl_s + srow * C::LDB + sk);
+      *reinterpret_cast<bf16x4*>(a.snapM + (shg * D + 16 * cb + srow) * D + sk) = hv;
+      *reinterpret_cast<bf16x4*>(a.snapMlo + (shg * D + 16 * cb + srow) * D + sk) = lv;
+      if (t < 16) {
+        float rs = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        b[e] = f2bf(x[e]);
-        bl[e] = f2bf(x[e] - bf2f(b[e]));
+        for (int w2 = 0; w2 < C::NW; ++w2) rs += rs_s[w2 * 16 + t];
+        a.snapc[shg * D + 16 * cb + t] = rs;
       }
-      *reinterpret_cast<bf16x4*>(a.snapM + (shg * D + 16 * cb + srow) * D + sk) = b;
-      *reinterpret_cast<bf16x4*>(a.snapMlo + (shg * D + 16 * cb + srow) * D + sk) = bl;
-      float rs = (x[0] + x[1]) + (x[2] + x[3]);
-#pragma unroll
-      for (int o2 = 1; o2 < C::TPR; o2 <<= 1) rs += __shfl_xor(rs, o2);
-      if (t % C::TPR == 0) a.snapc[shg * D + 16 * cb + srow] = rs;
     }
     bf16x8 ph[KS], plo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float* src = pl + l16 * C::LDP + 32 * ks + 8 * g;
-      const f32x4 x0 = *(const INFINI_LDS f32x4*)(src);
-      const f32x4 x1 = *(const INFINI_LDS f32x4*)(src + 4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = j < 4 ? x0[j] : x1[j - 4];
-        const bf16 h = f2bf(v);
-        ph[ks][j] = h;
-        plo[ks][j] = f2bf(v - bf2f(h));
-      }
+      ph[ks] = *(const INFINI_LDS bf16x8*)(ph_s + l16 * C::LDB + 32 * ks + 8 * g);
+      plo[ks] = *(const INFINI_LDS bf16x8*)(pl_s + l16 * C::LDB + 32 * ks + 8 * g);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
