@@ -40,6 +40,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTok = 64;      // token chunk of the state kernels
 constexpr int kColB = 16;     // columns of M per chain / snapshot workgroup
+constexpr int kChainCB = 4;   // columns of M per workgroup of the bf16 path's delta chains
 constexpr int kQB = 32;       // query rows per query-block workgroup
 constexpr int kKC = 64;       // key chunk
 constexpr int kKB = 32;       // keys per key-block workgroup
@@ -781,19 +782,20 @@ __global__ __launch_bounds__(kThreads) void bwd_lin_update_kernel(BwdArgs a) {
 // (C_s = sigma(K)^T V) and its gradient dL/dM_{s-1} = (I - A_s) dL/dM_s + dMr_s
 // (A_s is symmetric).  A_s and C_s come from parallel kernels; the two chains
 // below carry only a d_key x d_key x 16 product per segment.
-// grid (column blocks of 16, BH).  FWD: M_{s-1} snapshots from C_s^T (in dMr).
+// grid (column blocks of CB, BH).  FWD: M_{s-1} snapshots from C_s^T (in dMr).
 // !FWD: dMr_s replaced by dL/dM_s, dL/dM_0 to dM0.
-template <bool FWD>
+template <bool FWD, int CB>
 __global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
+  constexpr int RPT = 128 * CB / kThreads, RS = kThreads / CB;   // rows per thread, row stride
   constexpr int kAP = 132;   // LDS pitch of A_s rows (16-byte aligned rows, 4 banks apart)
   const int cb = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   __shared__ __attribute__((aligned(16))) float As[128 * kAP];
-  __shared__ float Xs[128][kColB + 1];
+  __shared__ float Xs[128][CB + 1];
   const int D = a.dk, na = D * D / (4 * kThreads);   // float4 pieces of A_s per thread (<= 16)
-  const int c = t % kColB, col = cb * kColB + c, x0 = t / kColB;   // the thread's rows: x0 + 16 r
+  const int c = t % CB, col = cb * CB + c, x0 = t / CB;   // the thread's rows: x0 + RS r
   const bool cok = col < a.dv;
-  for (int i = t; i < 128 * kColB; i += kThreads) {
-    const int r = i / kColB, cc = i % kColB, cl = cb * kColB + cc;
+  for (int i = t; i < 128 * CB; i += kThreads) {
+    const int r = i / CB, cc = i % CB, cl = cb * CB + cc;
     float x = 0.f;
     if (r < D && cl < a.dv) {
       const int64_t m = ((int64_t)bh * D + r) * a.dv + cl;
@@ -804,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
   // The next segment's A_s and additive term are fetched into registers while
   // the current product runs.
   f32x4 an[16];
-  float ad[8];
+  float ad[RPT];
   auto seg_of = [&](int k) __attribute__((always_inline)) { return FWD ? k : a.S - 1 - k; };
   auto fetch = [&](int k) __attribute__((always_inline)) {
     const int s = seg_of(k);
@@ -816,8 +818,8 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
         if (j < na) an[j] = src[t + kThreads * j];
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int x = x0 + 16 * r;
+    for (int r = 0; r < RPT; ++r) {
+      const int x = x0 + RS * r;
       ad[r] = 0.f;
       if (x < D && cok)   // FWD: C_s^T[col][x]; else dMr_s[x][col]
         ad[r] = FWD ? a.dMr[seg * D * a.dv + (int64_t)col * D + x] : a.dMr[seg * D * a.dv + (int64_t)x * a.dv + col];
@@ -839,30 +841,30 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
     const int s = seg_of(k);
     const bool first = is_first(a, s);
     const int64_t seg = (int64_t)bh * a.S + s;
-    float add[8];
+    float add[RPT];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) add[r] = ad[r];
+    for (int r = 0; r < RPT; ++r) add[r] = ad[r];
     // the carried matrix at this segment: FWD the snapshot M_{s-1}, else dL/dM_s
     // (in place of dMr_s, already read)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int x = x0 + 16 * r;
+    for (int r = 0; r < RPT; ++r) {
+      const int x = x0 + RS * r;
       if (x < D && cok) {
         float* dst = (FWD ? a.snapM : a.dMr) + seg * D * a.dv + (int64_t)x * a.dv + col;
         *dst = Xs[x][c];
       }
     }
     if (k + 1 < a.S) fetch(k + 1);
-    float acc[8];
+    float acc[RPT];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+    for (int r = 0; r < RPT; ++r) acc[r] = 0.f;
     if (!first) {
       for (int y = 0; y < D; y += 4) {
         const float x0v = Xs[y][c], x1v = Xs[y + 1][c], x2v = Xs[y + 2][c], x3v = Xs[y + 3][c];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-          if (r < D / 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(&As[(x0 + 16 * r) * kAP + y]);
+        for (int r = 0; r < RPT; ++r)
+          if (x0 + RS * r < D) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&As[(x0 + RS * r) * kAP + y]);
             acc[r] = __builtin_fmaf(av[0], x0v, acc[r]);
             acc[r] = __builtin_fmaf(av[1], x1v, acc[r]);
             acc[r] = __builtin_fmaf(av[2], x2v, acc[r]);
@@ -870,21 +872,21 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_chain_kernel(BwdArgs a) {
           }
       }
     }
-    float nx[8];
+    float nx[RPT];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int x = x0 + 16 * r;
+    for (int r = 0; r < RPT; ++r) {
+      const int x = x0 + RS * r;
       nx[r] = x < D ? Xs[x][c] - acc[r] + add[r] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 8; ++r) Xs[x0 + 16 * r][c] = nx[r];
+    for (int r = 0; r < RPT; ++r) Xs[x0 + RS * r][c] = nx[r];
     if (k + 1 < a.S) put_a(k + 1);
     __syncthreads();
   }
   if (!FWD && a.dM0)
-    for (int i = t; i < D * kColB; i += kThreads) {
-      const int r = i / kColB, cc = i % kColB, cl = cb * kColB + cc;
+    for (int i = t; i < D * CB; i += kThreads) {
+      const int r = i / CB, cc = i % CB, cl = cb * CB + cc;
       if (cl < a.dv) a.dM0[((int64_t)bh * D + r) * a.dv + cl] = Xs[r][cc];
     }
 }
@@ -1004,6 +1006,7 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e; \
   } while (0)
   const unsigned ncb32 = (unsigned)((a.dv + 31) / 32);
+  const unsigned ncb_chain = (unsigned)((a.dv + kChainCB - 1) / kChainCB);
   const bool delta_mfma = mfma && a.delta;
   if (a.delta && !mfma) {
     INFINI_BWD_LAUNCH(bwd_snap_kernel<T>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
@@ -1024,7 +1027,7 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
         e = a.dk == 128 ? launch_backward_delta_amat_mfma<128>(a, stream)
                         : launch_backward_delta_amat_mfma<64>(a, stream);
         if (e != hipSuccess) return e;
-        INFINI_BWD_LAUNCH(bwd_delta_chain_kernel<true>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+        INFINI_BWD_LAUNCH((bwd_delta_chain_kernel<true, kChainCB>), dim3(ncb_chain, BH), dim3(kThreads), 0, stream, a);
       } else {
         INFINI_BWD_LAUNCH((bwd_scan_kernel<false, true>), sg, dim3(kThreads), 0, stream, a);
       }
@@ -1049,7 +1052,7 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     INFINI_BWD_LAUNCH((bwd_tall_kernel<T, 1>), dim3(ncb32, S, BH), dim3(kThreads), 0, stream, a);
   }
   if (delta_mfma) {
-    INFINI_BWD_LAUNCH(bwd_delta_chain_kernel<false>, dim3(ncb, BH), dim3(kThreads), 0, stream, a);
+    INFINI_BWD_LAUNCH((bwd_delta_chain_kernel<false, kChainCB>), dim3(ncb_chain, BH), dim3(kThreads), 0, stream, a);
     e = a.dk == 128 ? launch_backward_delta_update_mfma<128>(a, stream)
                     : launch_backward_delta_update_mfma<64>(a, stream);
     if (e != hipSuccess) return e;
