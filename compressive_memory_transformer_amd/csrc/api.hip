@@ -288,7 +288,9 @@ bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w)
   take(&w->rs, rows);
   take(&w->dden, rows);
   take(&w->de, rows);
-  take(&w->dq, rk);
+  // bf16 MFMA path: the query kernel writes dq in one piece (no fp32 accumulator)
+  const bool mfma = st->dtype == INFINI_BF16 && mfma_shape(st->d_key, st->d_value, st->segment_len);
+  take(&w->dq, mfma ? 0 : rk);
   take(&w->dk, rk);
   take(&w->dv, rv);
   take(&w->dfk, rk);
@@ -297,7 +299,6 @@ bool backward_layout(const infini_attn_state* st, int64_t seq_len, BwdLayout* w)
   const bool amat = st->rule == INFINI_RULE_DELTA && st->dtype == INFINI_BF16;
   take(&w->amat, amat ? segs * dk * dk : 0);
   // bf16 MFMA path: the second halves of the per-segment Gram products
-  const bool mfma = st->dtype == INFINI_BF16 && mfma_shape(st->d_key, st->d_value, st->segment_len);
   take(&w->gpart, mfma ? mm + segs * dk : 0);
   w->total = off;
   return true;
@@ -543,7 +544,7 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dbeta = dbeta; a.dM0 = dM0; a.dz0 = dz0;
   a.snapM = f(w.snapM); a.snapz = f(w.snapz); a.dMr = f(w.dMr); a.dzr = f(w.dzr); a.ez = f(w.ez); a.gzs = f(w.gzs);
   a.lse = f(w.lse); a.drow = f(w.drow); a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
-  a.dq_acc = f(w.dq); a.dk_acc = f(w.dk); a.dv_acc = f(w.dv); a.dfk_acc = f(w.dfk); a.dbeta_part = f(w.dbp);
+  a.dq_acc = mfma_path(st) ? nullptr : f(w.dq); a.dk_acc = f(w.dk); a.dv_acc = f(w.dv); a.dfk_acc = f(w.dfk); a.dbeta_part = f(w.dbp);
   a.Amat = f(w.amat);
   a.gpart = f(w.gpart);
   a.B = st->batch; a.H = st->heads; a.BH = (int)BH; a.N = st->segment_len; a.S = (int)S64;

@@ -3,18 +3,16 @@
 // "精读笔记：Infini-attention", section 3.1 with the mask of section 3.8 step 2),
 // and the retrieval's share of the query gradient (section 3.3).
 //
-//   bwd_retr_q_kernel<D>: one workgroup (8 waves) per 256 queries of a segment,
-//     M_{s-1} staged in LDS as bf16.  Per query: A_mem = (colsum(M) +
-//     (sigma(q) - 1) M) / (sigma(q) z) (the column sums in fp32 keep sigma(q) ~ 1
-//     from costing bf16 precision), <dA, A_mem>, rs = g / den, dden, the
-//     retrieval's dq = (M (rs dA) + dden z) sigma'(q) (written to dq_acc) and
-//     the gate's A_mem share of dbeta.
 //   bwd_q2_kernel<D>: query-stationary.  One workgroup (8 waves, two per SIMD)
 //     per pair of 256-query tiles of one segment (tile t and NT-1-t, so that the
 //     causal work is equal), one wave per 32 queries.  First sweep over the
-//     keys: softmax statistics (log2 normaliser) and A_dot, then E = <dA, A_dot>,
-//     D = (1 - g) E and the gate's A_dot share of dbeta.  Second sweep:
-//     dS = P ((1 - g) dP - D) and dq += scale dS K (added to dq_acc).
+//     keys: softmax statistics (log2 normaliser) and A_dot, then E = <dA, A_dot>
+//     and D = (1 - g) E.  Second sweep: dS = P ((1 - g) dP - D) and
+//     dq = scale dS K.  Then the retrieval, with M_{s-1} staged once per
+//     workgroup in LDS as bf16: A_mem = (colsum(M) + (sigma(q) - 1) M) /
+//     (sigma(q) z) (the column sums in fp32 keep sigma(q) ~ 1 from costing bf16
+//     precision), <dA, A_mem>, rs = g / den, dden, the gate's share of dbeta,
+//     and dq += (M (rs dA) + dden z) sigma'(q), written once in bf16.
 //   bwd_kv2_kernel<D>: key-stationary.  One workgroup (8 waves) per pair of
 //     256-key tiles, one wave per 32 keys; the tile's keys sit in LDS, the
 //     wave's values in registers.  For every 32 later queries: S, dP, P, dS,
@@ -50,8 +48,8 @@ namespace infini {
 namespace {
 
 constexpr int kBwdWaves = 4;                // waves of the Gram kernel's workgroup
-constexpr int kUpdWaves = 8;                // waves of the retrieval and linear-update kernels
-constexpr int kUpdBlock = 32 * kUpdWaves;   // tokens (or queries) per workgroup of those
+constexpr int kUpdWaves = 8;                // waves of the linear-update kernel
+constexpr int kUpdBlock = 32 * kUpdWaves;   // tokens per workgroup of that kernel
 constexpr int kDuWaves = 4;                 // waves of the delta-update kernel (two staged
 constexpr int kDuBlock = 32 * kDuWaves;     // matrices: two workgroups per CU at this size)
 constexpr int kChunk = 64;                  // tokens per step of the Gram kernel
@@ -245,112 +243,15 @@ __device__ __forceinline__ float bw_exp2(float x) { return __builtin_amdgcn_exp2
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(64 * kUpdWaves) void bwd_retr_q_kernel(BwdArgs a) {
-  constexpr int P = D + 8, KS = D / 16, DB = D / 32;
-  const int qb = blockIdx.x, s = blockIdx.y, bh = blockIdx.z, h = bh % a.H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, hh = lane >> 5;
-  const bf16* Q = static_cast<const bf16*>(a.q);
-  const bf16* DO = static_cast<const bf16*>(a.dout);
-  __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * kUpdWaves];
-  __shared__ float msum[D], zsh[D];
-  const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-  const int qw0 = qb * kUpdBlock + 32 * w;
-  const bool has_mem = a.seg_base + s > 0;
-  const bool qvalid = qw0 < a.N;
-  const int64_t qrow = seg0 + min(qw0 + l32, a.N - 1);
-  const float g = sigmoid_gate(a.beta[h]);
-  bf16x8 qr[KS], dr[KS];
-#pragma unroll
-  for (int c = 0; c < KS; ++c) {
-    qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
-    dr[c] = *reinterpret_cast<const bf16x8*>(DO + qrow * D + 16 * c + 8 * hh);
-  }
-  if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[((int64_t)bh * a.S + s) * D + threadIdx.x];
-  stage_mat<D, 64 * kUpdWaves>(a.snapM + ((int64_t)bh * a.S + s) * D * D, ms, msum, red);
-  // q' = sigma(q) - 1 and the denominator sigma(q) z of the lane's query
-  bf16x8 qm[KS];
-  float den = 0.f;
-#pragma unroll
-  for (int c = 0; c < KS; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = bf2f(qr[c][j]);
-      const float f = x > 0.f ? x : exp_e(x) - 1.f;
-      qm[c][j] = f2bf(f);
-      den = __builtin_fmaf(f + 1.f, zsh[16 * c + 8 * hh + j], den);
-    }
-  den += __shfl_xor(den, 32);
-  const bool has = has_mem && den > 0.f;
-  const float inv_den = has ? 1.f / den : 0.f;
-  // <dA, A_mem> with A_mem^T = (colsum(M) + M^T q'^T) / den; the lane holds 16 DB
-  // values of its query's transposed row, in runs of four
-  float em = 0.f;
-#pragma unroll
-  for (int d = 0; d < DB; ++d) {
-    f32x16 am = zero16();
-    if (has_mem) {
-#pragma unroll
-      for (int c = 0; c < KS; ++c) am = mfma32(tr_nat(ms, P, 16 * c, 32 * d, lane), qm[c], am);
-    }
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const int col = 32 * d + 8 * j4 + 4 * hh;
-      const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + col);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) em = __builtin_fmaf(bf2f(da[j]), (msum[col + j] + am[4 * j4 + j]) * inv_den, em);
-    }
-  }
-  em += __shfl_xor(em, 32);
-  const float rs = g * inv_den;
-  const float dden = -g * em * inv_den;
-  if (qvalid && hh == 0) {
-    a.rs[qrow] = rs;
-    a.dden[qrow] = dden;
-  }
-  // the gate's A_mem share of dbeta for the wave's 32 queries: g (1 - g) sum <dA, A_mem>
-  {
-    const float bt = wave_sum(qvalid && hh == 0 ? em : 0.f);
-    if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] = bt * g * (1.f - g);
-  }
-  // the retrieval's dq^T = (M (rs dA)^T + dden z) sigma'(q): M rows from LDS, rs dA
-  // as the B operand from the dA rows in registers
-  bf16x8 dn[KS];
-#pragma unroll
-  for (int c = 0; c < KS; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dn[c][j] = f2bf(rs * bf2f(dr[c][j]));
-  if (qvalid) {
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      f32x16 dm = zero16();
-      if (has_mem) {   // wave-uniform; rows without memory have rs = dden = 0
-#pragma unroll
-        for (int c = 0; c < KS; ++c) dm = mfma32(row_op(ms, P, 32 * d, 16 * c, lane), dn[c], dm);
-      }
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int col = 32 * d + 8 * j4 + 4 * hh;
-        const bf16x4 xq = *reinterpret_cast<const bf16x4*>(Q + qrow * D + col);
-        f32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x = bf2f(xq[j]);
-          const float sp = x > 0.f ? 1.f : exp_e(x);
-          o[j] = (dm[4 * j4 + j] + dden * zsh[col + j]) * sp;
-        }
-        *reinterpret_cast<f32x4*>(a.dq_acc + qrow * D + col) = o;
-      }
-    }
-  }
-}
-
-template <int D>
 __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
   using L = BwL<D>;
   constexpr int KS = L::KS, DB = L::DB;
+  constexpr int P = D + 8;
   __shared__ __attribute__((aligned(1024))) bf16 ks0[L::TILE], ks1[L::TILE];
   __shared__ __attribute__((aligned(1024))) bf16 vs0[L::TILE], vs1[L::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 ms[D * P];   // M_{s-1} [d_key][d_value] in bf16
+  __shared__ float msum[D], zsh[D];                         // its column sums, z_{s-1}
+  static_assert(4 * 64 * kBw * sizeof(float) <= sizeof(ks0), "the staging reduction fits a streamed tile");
   const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int NT = (a.N + kBwRows - 1) / kBwRows, npair = (NT + 1) / 2;
@@ -358,12 +259,18 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
   const int pr = id % npair, sh = id / npair;    // sh = bh * S + s
   const int s = sh % a.S, bh = sh / a.S, h = bh % a.H;
   const int64_t seg0 = (int64_t)bh * a.L + (int64_t)s * a.N;
+  const bool has_mem = a.seg_base + s > 0;
   const bf16* Q = static_cast<const bf16*>(a.q);
   const bf16* K = static_cast<const bf16*>(a.k) + seg0 * D;
   const bf16* V = static_cast<const bf16*>(a.v) + seg0 * D;
   const bf16* DO = static_cast<const bf16*>(a.dout);
   const float g = sigmoid_gate(a.beta[h]);
   const float omg = 1.f - g, sl2 = a.scale * kLog2e;
+  // the memory the segment's queries read, staged once for both tiles (the first
+  // streamed slot holds the reduction of its column sums; the staging ends with
+  // a barrier before any load into that slot)
+  if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[(int64_t)sh * D + threadIdx.x];
+  stage_mat<D, 64 * kBw>(a.snapM + (int64_t)sh * D * D, ms, msum, reinterpret_cast<float*>(ks0));
   BwOfs<D> of;
   of.init(lane, w);
   auto issue = [&](int st, bf16* kd, bf16* vd) {
@@ -473,9 +380,55 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
       a.lse[qrow] = lse2;
       a.drow[qrow] = Dv;
     }
-    {   // the gate's A_dot share of dbeta: - g (1 - g) sum E (the A_mem share is in place)
-      const float bt = wave_sum(qvalid && hh == 0 ? e : 0.f);
-      if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] -= bt * g * omg;
+
+    // ---- the retrieval's statistics of the wave's queries.  The lane's LDS
+    // addresses are formed here, not hoisted to the kernel's entry where they
+    // would stay live through the sweeps.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lh = ln >> 5;
+    // q' = sigma(q) - 1 and the denominator sigma(q) z of the lane's query
+    float den = 0.f;
+    bf16x8 qm[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = bf2f(qr[c][j]);
+        const float f = x > 0.f ? x : exp_e(x) - 1.f;
+        qm[c][j] = f2bf(f);
+        den = __builtin_fmaf(f + 1.f, zsh[16 * c + 8 * lh + j], den);
+      }
+    den += __shfl_xor(den, 32);
+    const float inv_den = has_mem && den > 0.f ? 1.f / den : 0.f;
+    // <dA, A_mem> with A_mem^T = (colsum(M) + M^T q'^T) / den; the lane holds 16 DB
+    // values of its query's transposed row, in runs of four
+    float em = 0.f;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      f32x16 am = zero16();
+      if (has_mem) {
+#pragma unroll
+        for (int c = 0; c < KS; ++c) am = mfma32(tr_nat(ms, P, 16 * c, 32 * d, ln), qm[c], am);
+      }
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int col = 32 * d + 8 * j4 + 4 * lh;
+        const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + col);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) em = __builtin_fmaf(bf2f(da[j]), (msum[col + j] + am[4 * j4 + j]) * inv_den, em);
+      }
+    }
+    em += __shfl_xor(em, 32);
+    const float rs = g * inv_den;
+    const float dden = -g * em * inv_den;
+    if (qvalid && hh == 0) {
+      a.rs[qrow] = rs;
+      a.dden[qrow] = dden;
+    }
+    {   // the gate's share of dbeta for the wave's 32 queries: g (1 - g) sum (<dA, A_mem> - E)
+      const float bt = wave_sum(qvalid && hh == 0 ? em - e : 0.f);
+      if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] = bt * g * omg;
     }
 
     // ---- second sweep: dq^T += K^T dS^T
@@ -513,18 +466,35 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
         }
       }
     });
-    if (qvalid) {   // the final dq: the retrieval's share plus scale * dS K, in bf16
+    // ---- the final dq = (M (rs dA)^T + dden z) sigma'(q) + scale dS K, in bf16:
+    // M rows from LDS, rs dA (in place of dA) as the B operand
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int d = 0; d < DB; ++d)
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dr[c][j] = f2bf(rs * bf2f(dr[c][j]));
+    if (qvalid) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        f32x16 dm = zero16();
+        if (has_mem) {   // wave-uniform; rows without memory have rs = dden = 0
+#pragma unroll
+          for (int c = 0; c < KS; ++c) dm = mfma32(row_op(ms, P, 32 * d, 16 * c, ln), dr[c], dm);
+        }
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
-          const int64_t i = qrow * D + 32 * d + 8 * j4 + 4 * hh;
-          const f32x4 x = *reinterpret_cast<const f32x4*>(a.dq_acc + i);
+          const int col = 32 * d + 8 * j4 + 4 * lh;
+          const bf16x4 xq = *reinterpret_cast<const bf16x4*>(Q + qrow * D + col);
           bf16x4 o;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = f2bf(__builtin_fmaf(a.scale, dq[d][4 * j4 + j], x[j]));
-          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dq_out) + i) = o;
+          for (int j = 0; j < 4; ++j) {
+            const float x = bf2f(xq[j]);
+            const float sp = x > 0.f ? 1.f : exp_e(x);
+            o[j] = f2bf(__builtin_fmaf(a.scale, dq[d][4 * j4 + j], (dm[4 * j4 + j] + dden * zsh[col + j]) * sp));
+          }
+          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dq_out) + qrow * D + col) = o;
         }
+      }
     }
   }
 }
@@ -961,13 +931,9 @@ int bwd_mfma_blocks(int N) { return (N + kUpdBlock - 1) / kUpdBlock; }
 
 template <int D>
 hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) {
-  // the retrieval kernel writes rs, dden, the A_mem share of dbeta and the
-  // retrieval's dq, to which the query kernel adds; the key kernel reads the
-  // query kernel's statistics
-  const dim3 rgrid((unsigned)bwd_mfma_blocks(a.N), (unsigned)a.S, (unsigned)a.BH);
-  hipLaunchKernelGGL(bwd_retr_q_kernel<D>, rgrid, dim3(64 * kUpdWaves), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // the query kernel writes dq, rs, dden, dbeta's shares and the softmax
+  // statistics the key kernel reads
+  hipError_t e;
   const int64_t npair = ((a.N + kBwRows - 1) / kBwRows + 1) / 2;
   const int64_t nblk = npair * a.S * a.BH;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;

@@ -178,7 +178,7 @@ struct BwdArgs {
   float* rs;             // [BH*L] g / den (0 without memory)
   float* dden;           // [BH*L]
   float* de;             // [BH*L] delta rule: gradient of sigma(K_t) . z_{s-1}
-  float* dq_acc;         // [BH*L][dk] (MFMA path: the retrieval's share; the query kernel writes dq_out)
+  float* dq_acc;         // [BH*L][dk] (null on the MFMA path: its query kernel writes dq_out whole)
   float* dk_acc;         // [BH*L][dk] local attention's dk
   float* dv_acc;         // [BH*L][dv] (MFMA path: local attention's; the update kernels write dv_out)
   float* dfk_acc;        // [BH*L][dk] update's d sigma(K)

@@ -227,10 +227,10 @@ def test_backward_workspace_bytes():
     L = S * N
     mm, seg, rows = BH * S * D * D, BH * S * D, BH * L
     # snapshots, retrieval gradients of M and (delta, bf16) A_s; four per-segment d_key vectors, five per-row
-    # scalars, four per-row accumulators, the dbeta shares (64 query blocks per segment), and on the bf16
-    # MFMA path the Gram kernels' second-half partials (one d_key x d_value matrix and one d_key vector per
-    # segment)
-    want = 4 * (3 * mm + 4 * seg + 5 * rows + 4 * rows * D + BH * S * 64 + mm + seg)
+    # scalars, three per-row accumulators (the bf16 MFMA path writes dq without one), the dbeta shares (64
+    # query blocks per segment), and on that path the Gram kernels' second-half partials (one d_key x d_value
+    # matrix and one d_key vector per segment)
+    want = 4 * (3 * mm + 4 * seg + 5 * rows + 3 * rows * D + BH * S * 64 + mm + seg)
     assert ia.backward_workspace_bytes(st, L) == want
     assert ia.backward_workspace_bytes(st, L + 1) == 0
     assert ia.backward_workspace_bytes(_state(batch=0), L) == 0
