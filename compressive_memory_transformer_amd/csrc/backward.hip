@@ -631,7 +631,7 @@ __global__ __launch_bounds__(128) void bwd_zchain_kernel(BwdArgs a) {
   for (int s = a.S - 1; s >= 0; --s) {
     const int64_t i = ((int64_t)bh * a.S + s) * a.dk + x;
     a.gzs[i] = gz;
-    gz += a.dzr[i] + a.ez[i];
+    gz += a.dzr[i] + (a.delta ? a.ez[i] : 0.f);
   }
   if (a.dz0) a.dz0[(int64_t)bh * a.dk + x] = gz;
 }
@@ -1066,6 +1066,9 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
     INFINI_BWD_LAUNCH((bwd_scan_kernel<true, false>), dim3((unsigned)((n + kThreads - 1) / kThreads)),
                       dim3(kThreads), 0, stream, a);
     if (mfma) {
+      // the z chain needs only the retrieval's gradient of z here, and the update
+      // kernel finishes dk and dv with it
+      INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
       e = a.dk == 128 ? launch_backward_lin_update_mfma<128>(a, stream) : launch_backward_lin_update_mfma<64>(a, stream);
       if (e != hipSuccess) return e;
     } else {
@@ -1073,24 +1076,26 @@ static hipError_t launch_all(const BwdArgs& a, bool mfma, hipStream_t stream) {
                         0, stream, a);
     }
   }
-  if (delta_mfma) {
-    if (a.dk == 128) INFINI_BWD_LAUNCH(bwd_ez_vec_kernel<128>, dim3(S, BH), dim3(kThreads), 0, stream, a);
-    else INFINI_BWD_LAUNCH(bwd_ez_vec_kernel<64>, dim3(S, BH), dim3(kThreads), 0, stream, a);
-  } else {
-    INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
-  }
-  INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
-  {
-    const uintptr_t al = 4 * sizeof(T) - 1;
-    const bool vec = a.dk % 4 == 0 && a.dv % 4 == 0 &&
-                     ((reinterpret_cast<uintptr_t>(a.dq_out) | reinterpret_cast<uintptr_t>(a.dk_out) |
-                       reinterpret_cast<uintptr_t>(a.dv_out)) & al) == 0;
-    // the MFMA path wrote dq and dv already (its outputs are 16-byte aligned)
-    const int64_t n = (int64_t)a.BH * a.L * (a.dk + (mfma ? 0 : a.dv)) / (vec ? 4 : 1);
-    const dim3 grid((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1 << 20));
-    if (mfma) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4, true>), grid, dim3(kThreads), 0, stream, a);
-    else if (vec) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4, false>), grid, dim3(kThreads), 0, stream, a);
-    else INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 1, false>), grid, dim3(kThreads), 0, stream, a);
+  if (!(mfma && !a.delta)) {   // (the linear rule's MFMA update kernel finished dk and dv)
+    if (delta_mfma) {
+      if (a.dk == 128) INFINI_BWD_LAUNCH(bwd_ez_vec_kernel<128>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+      else INFINI_BWD_LAUNCH(bwd_ez_vec_kernel<64>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+    } else {
+      INFINI_BWD_LAUNCH(bwd_ez_kernel<T>, dim3(S, BH), dim3(kThreads), 0, stream, a);
+    }
+    INFINI_BWD_LAUNCH(bwd_zchain_kernel, dim3(BH), dim3(128), 0, stream, a);
+    {
+      const uintptr_t al = 4 * sizeof(T) - 1;
+      const bool vec = a.dk % 4 == 0 && a.dv % 4 == 0 &&
+                       ((reinterpret_cast<uintptr_t>(a.dq_out) | reinterpret_cast<uintptr_t>(a.dk_out) |
+                         reinterpret_cast<uintptr_t>(a.dv_out)) & al) == 0;
+      // the MFMA path wrote dq and dv already (its outputs are 16-byte aligned)
+      const int64_t n = (int64_t)a.BH * a.L * (a.dk + (mfma ? 0 : a.dv)) / (vec ? 4 : 1);
+      const dim3 grid((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1 << 20));
+      if (mfma) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4, true>), grid, dim3(kThreads), 0, stream, a);
+      else if (vec) INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 4, false>), grid, dim3(kThreads), 0, stream, a);
+      else INFINI_BWD_LAUNCH((bwd_finish_kernel<T, 1, false>), grid, dim3(kThreads), 0, stream, a);
+    }
   }
   INFINI_BWD_LAUNCH(bwd_dbeta_kernel, dim3((unsigned)a.H), dim3(kThreads), 0, stream, a);
 #undef INFINI_BWD_LAUNCH

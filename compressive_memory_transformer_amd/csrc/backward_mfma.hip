@@ -50,6 +50,7 @@ namespace {
 constexpr int kBwdWaves = 4;                // waves of the Gram kernel's workgroup
 constexpr int kUpdWaves = 8;                // waves of the linear-update kernel
 constexpr int kUpdBlock = 32 * kUpdWaves;   // tokens per workgroup of that kernel
+constexpr int kXtP = 36;                    // row pitch (floats) of its transposing tiles
 constexpr int kDuWaves = 4;                 // waves of the delta-update kernel (two staged
 constexpr int kDuBlock = 32 * kDuWaves;     // matrices: two workgroups per CU at this size)
 constexpr int kChunk = 64;                  // tokens per step of the Gram kernel
@@ -622,8 +623,10 @@ __global__ __launch_bounds__(64 * kBw) void bwd_kv2_kernel(BwdArgs a) {
 }
 
 // Linear rule, per 256 tokens of a segment (one wave per 32), given G = dL/dM_s
-// (fp32 [d_key][d_value], staged in LDS as bf16 with fp32 column sums):
-//   dv += sigma(K) G = colsum(G) + (sigma(K) - 1) G;   d sigma(K) = V G^T.
+// (fp32 [d_key][d_value], staged in LDS as bf16 with fp32 column sums) and
+// dL/dz_s: the final dv and dk in bf16,
+//   dv = dv_acc + sigma(K) G = dv_acc + colsum(G) + (sigma(K) - 1) G,
+//   dk = dk_acc + (V G^T + dL/dz_s) sigma'(K).
 template <int D>
 __global__ __launch_bounds__(64 * kUpdWaves) void bwd_lin_update_mfma_kernel(BwdArgs a) {
   constexpr int P = D + 8, KS = D / 16, DB = D / 32;
@@ -634,11 +637,68 @@ __global__ __launch_bounds__(64 * kUpdWaves) void bwd_lin_update_mfma_kernel(Bwd
   __shared__ __attribute__((aligned(16))) bf16 gs[D * P];
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * kUpdWaves];
   __shared__ float gsum[D];
+  __shared__ __attribute__((aligned(16))) float xt[kUpdWaves][32 * kXtP];   // each wave's transposing tile
   stage_mat<D, 64 * kUpdWaves>(a.dMr + ((int64_t)bh * a.S + s) * D * D, gs, gsum, red);
   const int t0 = rb * kUpdBlock + 32 * w;           // the wave's first token in the segment
-  const bool valid = t0 < a.N;
-  const int64_t row = (int64_t)bh * a.L + (int64_t)s * a.N + min(t0 + l32, a.N - 1);
-  bf16x8 kp[KS], vr[KS];
+  if (t0 >= a.N) return;                            // (after the staging's barriers)
+  // a valid wave's 32 tokens all lie in the segment
+  const int64_t out0 = (int64_t)bh * a.L + (int64_t)s * a.N + t0;
+  const int64_t row = out0 + l32;
+  const float* gz = a.gzs + ((int64_t)bh * a.S + s) * D;   // dL/dz_s, which every sigma(k) of the segment adds to
+  // The products leave token (acc_row(r, hh)) x column (l32) in the accumulators;
+  // the wave's own LDS tile turns a 32 x 32 block around so that the lane takes
+  // rows tr + 8 it, columns tc .. tc + 3 (eight lanes per 128-byte row piece).
+  // The epilogue's loads of block d + 1 go out before the stores of block d.
+  float* xw = xt[w];
+  const int tr = lane >> 3, tc = 4 * (lane & 7);
+  auto turn = [&](const f32x16& acc, f32x4* out) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xw[acc_row(r, hh) * kXtP + l32] = acc[r];
+    __builtin_amdgcn_wave_barrier();   // (a wave's LDS operations complete in order)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) out[it] = *reinterpret_cast<const f32x4*>(xw + (tr + 8 * it) * kXtP + tc);
+    __builtin_amdgcn_wave_barrier();
+  };
+  // dk = dk_acc + (V G^T + dL/dz_s) sigma'(K)
+  {
+    bf16x8 vr[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c) vr[c] = *reinterpret_cast<const bf16x8*>(V + row * D + 16 * c + 8 * hh);
+    f32x4 xa[2][4];
+    bf16x4 xk[2][4];
+    auto load = [&](int d, f32x4* pa, bf16x4* pk) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int64_t i = (out0 + tr + 8 * it) * D + 32 * d + tc;
+        pa[it] = *reinterpret_cast<const f32x4*>(a.dk_acc + i);
+        pk[it] = *reinterpret_cast<const bf16x4*>(K + i);
+      }
+    };
+    load(0, xa[0], xk[0]);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      f32x16 df = zero16();
+#pragma unroll
+      for (int c = 0; c < KS; ++c) df = mfma32(vr[c], row_op(gs, P, 32 * d, 16 * c, lane), df);
+      f32x4 dt[4];
+      turn(df, dt);
+      if (d + 1 < DB) load(d + 1, xa[(d + 1) & 1], xk[(d + 1) & 1]);
+      const f32x4 gzc = *reinterpret_cast<const f32x4*>(gz + 32 * d + tc);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        bf16x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = bf2f(xk[d & 1][it][j]);
+          const float sp = x > 0.f ? 1.f : exp_e(x);
+          o[j] = f2bf(__builtin_fmaf(dt[it][j] + gzc[j], sp, xa[d & 1][it][j]));
+        }
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dk_out) + (out0 + tr + 8 * it) * D + 32 * d + tc) = o;
+      }
+    }
+  }
+  // dv = dv_acc + sigma(K) G = dv_acc + colsum(G) + (sigma(K) - 1) G
+  bf16x8 kp[KS];
 #pragma unroll
   for (int c = 0; c < KS; ++c) {
     const bf16x8 kx = *reinterpret_cast<const bf16x8*>(K + row * D + 16 * c + 8 * hh);
@@ -647,25 +707,27 @@ __global__ __launch_bounds__(64 * kUpdWaves) void bwd_lin_update_mfma_kernel(Bwd
       const float x = bf2f(kx[j]);
       kp[c][j] = f2bf(x > 0.f ? x : exp_e(x) - 1.f);
     }
-    vr[c] = *reinterpret_cast<const bf16x8*>(V + row * D + 16 * c + 8 * hh);
   }
-  __syncthreads();
-  if (!valid) return;
-  const int64_t out0 = (int64_t)bh * a.L + (int64_t)s * a.N + t0;
+  f32x4 xa[2][4];
+  auto load = [&](int d, f32x4* pa) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) pa[it] = *reinterpret_cast<const f32x4*>(a.dv_acc + (out0 + tr + 8 * it) * D + 32 * d + tc);
+  };
+  load(0, xa[0]);
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
-    f32x16 dv = zero16(), df = zero16();
+    f32x16 dv = zero16();
 #pragma unroll
-    for (int c = 0; c < KS; ++c) {
-      dv = mfma32(kp[c], tr_nat(gs, P, 16 * c, 32 * d, lane), dv);
-      df = mfma32(vr[c], row_op(gs, P, 32 * d, 16 * c, lane), df);
-    }
-    const int col = 32 * d + l32;
+    for (int c = 0; c < KS; ++c) dv = mfma32(kp[c], tr_nat(gs, P, 16 * c, 32 * d, lane), dv);
+    f32x4 dt[4];
+    turn(dv, dt);
+    if (d + 1 < DB) load(d + 1, xa[(d + 1) & 1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t i = (out0 + acc_row(r, hh)) * D + col;
-      static_cast<bf16*>(a.dv_out)[i] = f2bf(a.dv_acc[i] + (gsum[col] + dv[r]));   // the final dv
-      a.dfk_acc[i] = df[r];
+    for (int it = 0; it < 4; ++it) {
+      bf16x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = f2bf(xa[d & 1][it][j] + (gsum[32 * d + tc + j] + dt[it][j]));
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dv_out) + (out0 + tr + 8 * it) * D + 32 * d + tc) = o;
     }
   }
 }

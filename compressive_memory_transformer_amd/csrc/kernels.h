@@ -181,7 +181,7 @@ struct BwdArgs {
   float* dq_acc;         // [BH*L][dk] (null on the MFMA path: its query kernel writes dq_out whole)
   float* dk_acc;         // [BH*L][dk] local attention's dk
   float* dv_acc;         // [BH*L][dv] (MFMA path: local attention's; the update kernels write dv_out)
-  float* dfk_acc;        // [BH*L][dk] update's d sigma(K)
+  float* dfk_acc;        // [BH*L][dk] update's d sigma(K) (unused by the linear rule's MFMA path)
   float* dbeta_part;     // [BH*S][nqb]
   float* Amat;           // delta rule, bf16 path: [BH*S][dk][dk] sigma(K)^T diag(1/e) sigma(K)
   float* gpart;          // bf16 MFMA path: [BH*S][dk][dv] + [BH*S][dk], the Gram kernels' second halves
