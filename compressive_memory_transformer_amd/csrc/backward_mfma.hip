@@ -51,8 +51,8 @@ constexpr int kBwdWaves = 4;                // waves of the Gram kernel's workgr
 constexpr int kUpdWaves = 8;                // waves of the linear-update kernel
 constexpr int kUpdBlock = 32 * kUpdWaves;   // tokens per workgroup of that kernel
 constexpr int kXtP = 36;                    // row pitch (floats) of its transposing tiles
-constexpr int kDuWaves = 4;                 // waves of the delta-update kernel (two staged
-constexpr int kDuBlock = 32 * kDuWaves;     // matrices: two workgroups per CU at this size)
+constexpr int kDuWaves = 8;                 // waves of the delta-update kernel (two staged
+constexpr int kDuBlock = 32 * kDuWaves;     // matrices shared by 256 tokens)
 constexpr int kChunk = 64;                  // tokens per step of the Gram kernel
 
 __device__ __forceinline__ bf16x8 row_op(const bf16* X, int pitch, int r0, int k0, int lane) {
@@ -240,6 +240,41 @@ __device__ __forceinline__ void bw_wait_sync() {
 }
 
 __device__ __forceinline__ float bw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Four-element accesses within a wave's 32 rows of D elements at the
+// wave-uniform `base`: the lane's byte offset `vb` in a vector register, a
+// compile-time constant one `sb` in a scalar register, so that the accesses of
+// a 32 x 32 block need no 64-bit address each.
+template <int D>
+__device__ __forceinline__ f32x4 wv_ld4(const float* base, int vb, int sb) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(bw_rsrc(base, 32 * D * 4), vb, sb, 0));
+#else
+  return f32x4{};
+#endif
+}
+template <int D>
+__device__ __forceinline__ bf16x4 wv_ld4(const bf16* base, int vb, int sb) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(bw_rsrc(base, 32 * D * 2), vb, sb, 0));
+#else
+  return bf16x4{};
+#endif
+}
+template <int D>
+__device__ __forceinline__ void wv_st4(float* base, int vb, int sb, f32x4 x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using u4 = __attribute__((ext_vector_type(4))) unsigned int;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), bw_rsrc(base, 32 * D * 4), vb, sb, 0);
+#endif
+}
+template <int D>
+__device__ __forceinline__ void wv_st4(bf16* base, int vb, int sb, bf16x4 x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using u2 = __attribute__((ext_vector_type(2))) unsigned int;
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, x), bw_rsrc(base, 32 * D * 2), vb, sb, 0);
+#endif
+}
 
 }  // namespace
 
@@ -873,7 +908,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_gram_kernel(BwdArgs a) {
   }
 }
 
-// Delta rule, per 128 tokens of a segment (one wave per 32, lanes = tokens),
+// Delta rule, per 256 tokens of a segment (one wave per 32, lanes = tokens),
 // given G = dL/dM_s (in dMr after the backward chain), M_{s-1}, z_{s-1}:
 //   dU = sigma(K) G,  R = sigma(K) M_{s-1} / e (0 in the first segment),
 //   U = V - R;  dv += dU;  d sigma(K) = U G^T - M_{s-1} (dU / e)^T;
@@ -891,6 +926,7 @@ __global__ __launch_bounds__(64 * kDuWaves) void bwd_delta_update_mfma_kernel(Bw
   __shared__ __attribute__((aligned(16))) bf16 msb[D * P];
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * kDuWaves];
   __shared__ float gsum[D], msum[D], zsh[D];
+  __shared__ __attribute__((aligned(16))) float xt[kDuWaves][32 * kXtP];   // each wave's transposing tile
   const int64_t seg = (int64_t)bh * a.S + s;
   if (threadIdx.x < D) zsh[threadIdx.x] = a.snapz[seg * D + threadIdx.x];
   stage_mat<D, 64 * kDuWaves>(a.dMr + seg * D * D, gs, gsum, red);
@@ -916,6 +952,47 @@ __global__ __launch_bounds__(64 * kDuWaves) void bwd_delta_update_mfma_kernel(Bw
   e += __shfl_xor(e, 32);
   const float wt = (!first && e > 0.f) ? 1.f / e : 0.f;
   if (!valid) return;
+  // A valid wave's 32 tokens all lie in the segment.  The products hold token
+  // l32 and columns 8 j4 + 4 hh + 0..3 of a 32-column block per lane; global
+  // memory is read and written in row pieces (token tr + 8 it, columns tc ..
+  // tc + 3: eight lanes per 128-byte row piece), turned around in the wave's own
+  // LDS tile.  The loads of block d + 1 go out before the stores of block d.
+  const int64_t out0 = row - l32;
+  const int tr = lane >> 3, tc = 4 * (lane & 7);
+  float* xw = xt[w];
+  auto to_acc = [&](const f32x4* piece, f32x4* run) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) *reinterpret_cast<f32x4*>(xw + (tr + 8 * it) * kXtP + tc) = piece[it];
+    __builtin_amdgcn_wave_barrier();   // (a wave's LDS operations complete in order)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) run[j4] = *reinterpret_cast<const f32x4*>(xw + l32 * kXtP + 8 * j4 + 4 * hh);
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto to_rows = [&](const f32x4* run, f32x4* piece) {
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) *reinterpret_cast<f32x4*>(xw + l32 * kXtP + 8 * j4 + 4 * hh) = run[j4];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) piece[it] = *reinterpret_cast<const f32x4*>(xw + (tr + 8 * it) * kXtP + tc);
+    __builtin_amdgcn_wave_barrier();
+  };
+  f32x4 pa[4];   // local attention's dv
+  bf16x4 pv[4];  // V
+  // element (tr + 8 it, 32 d + tc) of the wave's rows: lane part ve, constant part
+  const int ve = tr * D + tc;
+  const float* dva = a.dv_acc + out0 * D;
+  const bf16* vw = V + out0 * D;
+  bf16* dvo = static_cast<bf16*>(a.dv_out) + out0 * D;
+  float* dfo = a.dfk_acc + out0 * D;
+  auto load = [&](int d, f32x4* a4, bf16x4* v4) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int se = 8 * it * D + 32 * d;
+      a4[it] = wv_ld4<D>(dva, 4 * ve, 4 * se);
+      v4[it] = wv_ld4<D>(vw, 2 * ve, 2 * se);
+    }
+  };
+  load(0, pa, pv);
   // dU^T, R^T, U^T per 32-row tile of d_value; B operands for d sigma(K)^T
   bf16x8 ub[DB][2], db[DB][2];
   float de = 0.f;
@@ -927,29 +1004,41 @@ __global__ __launch_bounds__(64 * kDuWaves) void bwd_delta_update_mfma_kernel(Bw
       du = mfma32(tr_nat(gs, P, 16 * c, 32 * d, lane), kp[c], du);
       if (!first) re = mfma32(tr_nat(msb, P, 16 * c, 32 * d, lane), kp[c], re);
     }
+    f32x4 dvl[4], vvf[4], tmp[4];
+    to_acc(pa, dvl);
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmp[it][j] = bf2f(pv[it][j]);
+    to_acc(tmp, vvf);
+    if (d + 1 < DB) load(d + 1, pa, pv);
     f32x16 u, dw;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {   // accumulator rows come in runs of four columns
       const int col = 32 * d + 8 * j4 + 4 * hh;
-      const f32x4 dvl = *reinterpret_cast<const f32x4*>(a.dv_acc + row * D + col);   // local attention's dv
-      bf16x4 dvo;
-      const bf16x4 vv = *reinterpret_cast<const bf16x4*>(V + row * D + col);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * j4 + j;
         const float dut = du[r] + gsum[col + j];
         const float R = first ? 0.f : (re[r] + msum[col + j]) * wt;
-        dvo[j] = f2bf(dvl[j] + dut);
-        u[r] = bf2f(vv[j]) - R;
+        tmp[j4][j] = dvl[j4][j] + dut;
+        u[r] = vvf[j4][j] - R;
         dw[r] = -dut * wt;
         de = __builtin_fmaf(dut, R, de);
       }
-      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.dv_out) + row * D + col) = dvo;   // the final dv
     }
     ub[d][0] = acc_op(u, 0);
     ub[d][1] = acc_op(u, 1);
     db[d][0] = acc_op(dw, 0);
     db[d][1] = acc_op(dw, 1);
+    to_rows(tmp, dvl);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {   // the final dv
+      bf16x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = f2bf(dvl[it][j]);
+      wv_st4<D>(dvo, 2 * ve, 2 * (8 * it * D + 32 * d), o);
+    }
   }
   de = (de + __shfl_xor(de, 32)) * wt;
   if (hh == 0) a.de[row] = de;
@@ -979,13 +1068,14 @@ __global__ __launch_bounds__(64 * kDuWaves) void bwd_delta_update_mfma_kernel(Bw
         df = mfma32(ga, ub[d][ks], df);
         if (!first) df = mfma32(ma, db[d][ks], df);
       }
+    f32x4 run[4], piece[4];
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      f32x4 o;
+    for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = df[4 * j4 + j];
-      *reinterpret_cast<f32x4*>(a.dfk_acc + row * D + 32 * d2 + 8 * j4 + 4 * hh) = o;
-    }
+      for (int j = 0; j < 4; ++j) run[j4][j] = df[4 * j4 + j];
+    to_rows(run, piece);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) wv_st4<D>(dfo, 4 * ve, 4 * (8 * it * D + 32 * d2), piece[it]);
   }
 }
 
