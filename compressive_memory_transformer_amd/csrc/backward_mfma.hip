@@ -276,6 +276,27 @@ __device__ __forceinline__ void wv_st4(bf16* base, int vb, int sb, bf16x4 x) {
 #endif
 }
 
+// Turns f times a 32 x 32 accumulator block (lane ln holds column ln % 32, rows
+// 8 j4 + 4 (ln / 32) + 0..3 at elements 4 j4 ..) into row pieces: piece[it] =
+// row ln / 8 + 8 it, columns 4 (ln % 8) .. + 3 of the block's transpose, i.e.
+// the lane's column-major element runs become eight-lanes-per-row pieces.  `xw`
+// is the wave's own 4 KB LDS tile; its 16-byte chunk c of row r sits at
+// c ^ (r % 8).
+__device__ __forceinline__ void turn32(float* xw, const f32x16& acc, float f, int ln, f32x4* piece) {
+  const int r32 = ln & 31, h2 = ln >> 5, tr = (ln >> 3) & 7, c8 = ln & 7;
+#pragma unroll
+  for (int j4 = 0; j4 < 4; ++j4) {
+    f32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = f * acc[4 * j4 + j];
+    *reinterpret_cast<f32x4*>(xw + 32 * r32 + 4 * ((2 * j4 + h2) ^ (r32 & 7))) = x;
+  }
+  __builtin_amdgcn_wave_barrier();   // (a wave's LDS operations complete in order)
+#pragma unroll
+  for (int it = 0; it < 4; ++it) piece[it] = *reinterpret_cast<const f32x4*>(xw + 32 * (tr + 8 * it) + 4 * (c8 ^ tr));
+  __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace
 
 template <int D>
@@ -509,7 +530,45 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
     for (int c = 0; c < KS; ++c)
 #pragma unroll
       for (int j = 0; j < 8; ++j) dr[c][j] = f2bf(rs * bf2f(dr[c][j]));
-    if (qvalid) {
+    if (qvalid && D == 128) {
+      // through a 4 KB tile per wave in the second ring slots (no load goes
+      // there before the next sweep's first barrier): (M (rs dA)^T + dden z) and
+      // scale dS K turned into row pieces (query tr + 8 it, columns 4 c8 ..
+      // 4 c8 + 3), then sigma'(q) from the matching piece of Q
+      float* xw = reinterpret_cast<float*>(w < 4 ? ks1 : vs1) + 1024 * (w & 3);
+      const int vb = 2 * ((ln >> 3) * D + 4 * (ln & 7));
+      const bf16* qw = Q + (seg0 + qw0) * D;
+      bf16* dqw = static_cast<bf16*>(a.dq_out) + (seg0 + qw0) * D;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        bf16x4 xq[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) xq[it] = wv_ld4<D>(qw, vb, 2 * (8 * it * D + 32 * d));
+        f32x16 dm = zero16();
+        if (has_mem) {   // wave-uniform; rows without memory have rs = dden = 0
+#pragma unroll
+          for (int c = 0; c < KS; ++c) dm = mfma32(row_op(ms, P, 32 * d, 16 * c, ln), dr[c], dm);
+        }
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dm[4 * j4 + j] += dden * zsh[32 * d + 8 * j4 + 4 * lh + j];
+        f32x4 tm[4], ta[4];
+        turn32(xw, dm, 1.f, ln, tm);
+        turn32(xw, dq[d], a.scale, ln, ta);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          bf16x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = bf2f(xq[it][j]);
+            const float sp = x > 0.f ? 1.f : exp_e(x);
+            o[j] = f2bf(__builtin_fmaf(tm[it][j], sp, ta[it][j]));
+          }
+          wv_st4<D>(dqw, vb, 2 * (8 * it * D + 32 * d), o);
+        }
+      }
+    } else if (qvalid) {
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
         f32x16 dm = zero16();
@@ -638,7 +697,31 @@ __global__ __launch_bounds__(64 * kBw) void bwd_kv2_kernel(BwdArgs a) {
       compute(qs1, es1, ld1, st + 1);
     }
     bw_wait_sync<0>();
-    if (kvalid) {
+    if (!kvalid) continue;
+    if constexpr (D == 128) {
+      // The accumulators hold key l32 and columns 8 j4 + 4 hh + 0..3 of each
+      // 32-column block; a 4 KB tile per wave in the second ring slots (no load
+      // goes there before the next pass's first barrier) turns each block into
+      // row pieces (key tr + 8 it, columns 4 c8 .. 4 c8 + 3: eight lanes per
+      // 128-byte row piece).  The lane's offsets are formed here, not hoisted
+      // into the sweep.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      float* xw = reinterpret_cast<float*>(w < 4 ? qs1 : es1) + 1024 * (w & 3);
+      const int vb = 4 * ((ln >> 3) * D + 4 * (ln & 7));
+      float* dvw = a.dv_acc + (seg0 + kw0) * D;
+      float* dkw = a.dk_acc + (seg0 + kw0) * D;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        f32x4 x[4];
+        turn32(xw, dv[d], omg, ln, x);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) wv_st4<D>(dvw, vb, 4 * (8 * it * D + 32 * d), x[it]);
+        turn32(xw, dk[d], a.scale, ln, x);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) wv_st4<D>(dkw, vb, 4 * (8 * it * D + 32 * d), x[it]);
+      }
+    } else {
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
