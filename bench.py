@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="time infini_attn_backward_sequence over the workload (gradients of a forward from an "
                         "empty memory); prints its own JSON line")
+    p.add_argument("--saved", action="store_true",
+                   help="with --backward: time infini_attn_backward_sequence_saved, given the output and the "
+                        "softmax log-normalisers of an (untimed) infini_attn_forward_sequence_train call")
     p.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
                    help="time infini_attn_layer_forward (QKV projection, stream, output projection) with model "
                         "width D_MODEL (0: off); prints its own JSON line")
@@ -320,9 +323,20 @@ def bench_backward(args):
     dbeta = torch.empty(w.heads, dtype=torch.float32, device="cuda")
     dM0, dz0 = torch.empty_like(M0), torch.empty_like(z0)
     sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    saved = None
+    if args.saved:
+        # the training forward from the same (empty) starting state keeps what the
+        # backward then reads instead of recomputing the softmax statistics
+        eng.reset()
+        saved = eng.forward_sequence_train(q, k, v, beta)
+        torch.cuda.synchronize()
 
     def step():
-        ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, need, sh)
+        if saved is None:
+            ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, need, sh)
+        else:
+            ia.backward_sequence_saved(st, q, k, v, L, beta, saved[0], saved[1], dout, dM, dz, dq, dk, dv, dbeta,
+                                       dM0, dz0, ws, need, sh)
 
     for _ in range(args.warmup):
         step()
@@ -340,7 +354,8 @@ def bench_backward(args):
     tf = fl / gpu_s / 1e12
     cpu = backward_cpu_baseline(w, rule, args.cpu_seconds) if args.cpu_seconds > 0 else None
     line = {
-        "metric": "Infini-attention backward tokens/sec on 1 MI355X (gradients of forward_sequence)",
+        "metric": ("Infini-attention backward tokens/sec on 1 MI355X (gradients of forward_sequence"
+                   + (", given the training forward's output and softmax log-normalisers)" if saved else ")")),
         "value": w.tokens * args.steps / wall,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -352,9 +367,9 @@ def bench_backward(args):
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"backward/{w.name}", "batch": w.batch, "heads": w.heads,
-                   "segment_len": w.segment_len, "segments": w.segments, "d_key": w.d_key, "d_value": w.d_value,
-                   "rule": rule, "parallelism": "single GPU"},
+        "config": {"workload": f"backward{'_saved' if saved else ''}/{w.name}", "batch": w.batch,
+                   "heads": w.heads, "segment_len": w.segment_len, "segments": w.segments, "d_key": w.d_key,
+                   "d_value": w.d_value, "rule": rule, "parallelism": "single GPU"},
         "roofline": ({"bound": "mfma", "kernel": "whole backward (all launches of one call)", "achieved": tf,
                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
                       "traffic": None, "flops_per_step": fl, "avg_step_ms_on_stream": gpu_s * 1e3}

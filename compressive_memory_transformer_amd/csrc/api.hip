@@ -143,7 +143,7 @@ int record(void* const* events, int i, hipStream_t stream) {
 template <int D>
 int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t L, int S,
              const float* beta, void* out, char* ws, const WsLayout& w, hipStream_t stream,
-             void* const* events) {
+             void* const* events, float* lse = nullptr) {
   int rc;
   if ((rc = record(events, 0, stream)) != INFINI_OK) return rc;
   using infini::bf16;
@@ -169,7 +169,7 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
   infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,
                    snapM, snapMlo, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, 0,
-                   st->segments_done, (float)((double)st->scale * 1.4426950408889634)};
+                   st->segments_done, (float)((double)st->scale * 1.4426950408889634), lse};
   if ((e = infini::launch_fa_fwd<D>(f, stream)) != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return record(events, 2, stream);
 }
@@ -387,7 +387,7 @@ size_t infini_attn_workspace_bytes(const infini_attn_state* st, int64_t seq_len)
 
 static int forward_impl(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t seq_len,
                         const float* beta, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                        void* const* events) {
+                        void* const* events, float* lse = nullptr) {
   int rc = check_state(st);
   if (rc != INFINI_OK) return rc;
   if (!q || !k || !v || !beta || !out) return fail(INFINI_EINVAL, "q, k, v, beta and out must be non-NULL");
@@ -424,6 +424,18 @@ static int forward_impl(infini_attn_state* st, const void* q, const void* k, con
   if (overlaps(workspace, w.total, out, out_bytes) || overlaps(workspace, w.total, st->M, m_bytes) ||
       overlaps(workspace, w.total, st->z, z_bytes))
     return fail(INFINI_EWORKSPACE, "workspace must not alias out or the state");
+  if (lse) {
+    if (!mfma_path(st))
+      return fail(INFINI_EUNSUPPORTED, "the log-normalisers are kept on the bf16 MFMA path only "
+                  "(d_key = d_value in {64, 128}, segment_len a multiple of 64)");
+    if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(INFINI_EINVAL, "lse must be 4-byte aligned");
+    const size_t lb = (size_t)rows * 4;
+    if (overlaps(lse, lb, out, out_bytes) || overlaps(lse, lb, q, (size_t)nqk * esz) ||
+        overlaps(lse, lb, k, (size_t)nqk * esz) || overlaps(lse, lb, v, (size_t)nvo * esz) ||
+        overlaps(lse, lb, st->M, m_bytes) || overlaps(lse, lb, st->z, z_bytes) ||
+        overlaps(lse, lb, workspace, w.total) || overlaps(lse, lb, beta, (size_t)st->heads * 4))
+      return fail(INFINI_EINVAL, "lse must not alias out, the inputs, the state or the workspace");
+  }
   if (mfma_path(st)) {
     const int64_t fa_blocks = infini::fa_fwd_blocks(BH * S64, st->segment_len);
     if (fa_blocks > 0x7fffffff) return fail(INFINI_EUNSUPPORTED, "launch grid too large; split the call");
@@ -432,8 +444,8 @@ static int forward_impl(infini_attn_state* st, const void* q, const void* k, con
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (mfma_path(st)) {
-    rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events)
-                          : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events);
+    rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events, lse)
+                          : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events, lse);
   } else {
     rc = run_f32(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events);
   }
@@ -446,6 +458,13 @@ int infini_attn_forward_sequence(infini_attn_state* st, const void* q, const voi
                                  int64_t seq_len, const float* beta, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   return forward_impl(st, q, k, v, seq_len, beta, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int infini_attn_forward_sequence_train(infini_attn_state* st, const void* q, const void* k, const void* v,
+                                       int64_t seq_len, const float* beta, void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!lse) return fail(INFINI_EINVAL, "lse must be non-NULL");
+  return forward_impl(st, q, k, v, seq_len, beta, out, workspace, workspace_bytes, stream, nullptr, lse);
 }
 
 int infini_attn_forward_sequence_noalloc(infini_attn_state* st, const void* q, const void* k, const void* v,
@@ -483,12 +502,17 @@ size_t infini_attn_backward_workspace_bytes(const infini_attn_state* st, int64_t
   return w.total;
 }
 
-int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, const void* k, const void* v,
-                                  int64_t seq_len, const float* beta, const void* dout, const float* dM,
-                                  const float* dz, void* dq, void* dk, void* dv, float* dbeta, float* dM0,
-                                  float* dz0, void* workspace, size_t workspace_bytes, void* stream) {
+static int backward_impl(const infini_attn_state* st, const void* q, const void* k, const void* v,
+                         int64_t seq_len, const float* beta, const void* out_fw, const float* lse_fw,
+                         const void* dout, const float* dM, const float* dz, void* dq, void* dk, void* dv,
+                         float* dbeta, float* dM0, float* dz0, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   int rc = check_state(st);
   if (rc != INFINI_OK) return rc;
+  const bool saved = out_fw != nullptr;
+  if (saved && !mfma_path(st))
+    return fail(INFINI_EUNSUPPORTED, "the saved-statistics backward runs on the bf16 MFMA path only "
+                "(d_key = d_value in {64, 128}, segment_len a multiple of 64)");
   if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta)
     return fail(INFINI_EINVAL, "q, k, v, beta, dout, dq, dk, dv and dbeta must be non-NULL");
   if (seq_len <= 0 || seq_len % st->segment_len != 0)
@@ -511,8 +535,11 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
     if (reinterpret_cast<uintptr_t>(p) % align != 0)
       return fail(INFINI_EINVAL, "q, k, v, dout, dq, dk and dv must be %d-byte aligned", (int)align);
   for (const void* p : {static_cast<const void*>(beta), static_cast<const void*>(dM), static_cast<const void*>(dz),
-                        static_cast<const void*>(dbeta), static_cast<const void*>(dM0), static_cast<const void*>(dz0)})
+                        static_cast<const void*>(dbeta), static_cast<const void*>(dM0), static_cast<const void*>(dz0),
+                        static_cast<const void*>(lse_fw)})
     if (reinterpret_cast<uintptr_t>(p) % 4 != 0) return fail(INFINI_EINVAL, "fp32 arguments must be 4-byte aligned");
+  if (saved && reinterpret_cast<uintptr_t>(out_fw) % align != 0)
+    return fail(INFINI_EINVAL, "out must be %d-byte aligned", (int)align);
   const size_t qkb = (size_t)nqk * esz, vb = (size_t)nvo * esz;
   const size_t mb = (size_t)BH * st->d_key * st->d_value * 4, zb = (size_t)BH * st->d_key * 4;
   BwdLayout w;
@@ -526,7 +553,8 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   const Buf outs[] = {{dq, qkb}, {dk, qkb}, {dv, vb}, {dbeta, (size_t)st->heads * 4}, {dM0, dM0 ? mb : 0},
                       {dz0, dz0 ? zb : 0}, {workspace, w.total}};
   const Buf ins[] = {{q, qkb}, {k, qkb}, {v, vb}, {dout, vb}, {beta, (size_t)st->heads * 4}, {dM, dM ? mb : 0},
-                     {dz, dz ? zb : 0}, {st->M, mb}, {st->z, zb}};
+                     {dz, dz ? zb : 0}, {st->M, mb}, {st->z, zb}, {out_fw, saved ? vb : 0},
+                     {lse_fw, saved ? (size_t)rows * 4 : 0}};
   for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
     if (!outs[i].n) continue;
     for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
@@ -543,7 +571,7 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.beta = beta; a.M0 = st->M; a.z0 = st->z; a.dM = dM; a.dz = dz;
   a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dbeta = dbeta; a.dM0 = dM0; a.dz0 = dz0;
   a.snapM = f(w.snapM); a.snapz = f(w.snapz); a.dMr = f(w.dMr); a.dzr = f(w.dzr); a.ez = f(w.ez); a.gzs = f(w.gzs);
-  a.lse = f(w.lse); a.drow = f(w.drow); a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
+  a.lse = saved ? const_cast<float*>(lse_fw) : f(w.lse); a.drow = f(w.drow); a.out_fw = out_fw; a.rs = f(w.rs); a.dden = f(w.dden); a.de = f(w.de);
   a.dq_acc = mfma_path(st) ? nullptr : f(w.dq); a.dk_acc = f(w.dk); a.dv_acc = f(w.dv); a.dfk_acc = f(w.dfk); a.dbeta_part = f(w.dbp);
   a.Amat = f(w.amat);
   a.gpart = f(w.gpart);
@@ -553,6 +581,24 @@ int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, co
   const hipError_t e = infini::launch_backward(a, st->dtype == INFINI_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
+}
+
+int infini_attn_backward_sequence(const infini_attn_state* st, const void* q, const void* k, const void* v,
+                                  int64_t seq_len, const float* beta, const void* dout, const float* dM,
+                                  const float* dz, void* dq, void* dk, void* dv, float* dbeta, float* dM0,
+                                  float* dz0, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(st, q, k, v, seq_len, beta, nullptr, nullptr, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0,
+                       workspace, workspace_bytes, stream);
+}
+
+int infini_attn_backward_sequence_saved(const infini_attn_state* st, const void* q, const void* k, const void* v,
+                                        int64_t seq_len, const float* beta, const void* out, const float* lse,
+                                        const void* dout, const float* dM, const float* dz, void* dq, void* dk,
+                                        void* dv, float* dbeta, float* dM0, float* dz0, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!out || !lse) return fail(INFINI_EINVAL, "out and lse must be non-NULL");
+  return backward_impl(st, q, k, v, seq_len, beta, out, lse, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, workspace,
+                       workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------ layer

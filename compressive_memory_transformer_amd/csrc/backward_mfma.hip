@@ -299,7 +299,7 @@ __device__ __forceinline__ void turn32(float* xw, const f32x16& acc, float f, in
 
 }  // namespace
 
-template <int D>
+template <int D, bool SAVED>
 __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
   using L = BwL<D>;
   constexpr int KS = L::KS, DB = L::DB;
@@ -362,80 +362,86 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < KS; ++c) qr[c] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + 16 * c + 8 * hh);
 
-    // ---- first sweep: statistics and A_dot^T of the wave's 32 query columns.
-    // m is a reference maximum (log2 units) raised only when a block's maximum
-    // exceeds it by more than 8, so probabilities stay below 2^8 and the rescale
-    // of O and l is rare; the result is exact for any m.
-    f32x16 o[DB];
+    // With the forward's output and log-normalisers (SAVED) the first sweep is
+    // not needed: D = (1 - g) <dA, A_dot> = <dA, A> - g <dA, A_mem>, and <dA, A_mem>
+    // comes with the retrieval below.
+    float lse2 = 0.f, Dv = 0.f;
+    if constexpr (!SAVED) {
+      // ---- first sweep: statistics and A_dot^T of the wave's 32 query columns.
+      // m is a reference maximum (log2 units) raised only when a block's maximum
+      // exceeds it by more than 8, so probabilities stay below 2^8 and the rescale
+      // of O and l is rare; the result is exact for any m.
+      f32x16 o[DB];
 #pragma unroll
-    for (int d = 0; d < DB; ++d) o[d] = zero16();
-    float m = -__builtin_inff(), l = 0.f;
-    ring(ns, [&](const bf16* kt, const bf16* vt, int st) {
-      if (!qvalid) return;
-      of.opaque();
+      for (int d = 0; d < DB; ++d) o[d] = zero16();
+      float m = -__builtin_inff(), l = 0.f;
+      ring(ns, [&](const bf16* kt, const bf16* vt, int st) {
+        if (!qvalid) return;
+        of.opaque();
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int kb = kBwStep * st + 32 * b;
-        if (kb > qw0) break;   // the wave's queries see no key of this block (nor the next)
-        f32x16 sc = zero16();
+        for (int b = 0; b < 2; ++b) {
+          const int kb = kBwStep * st + 32 * b;
+          if (kb > qw0) break;   // the wave's queries see no key of this block (nor the next)
+          f32x16 sc = zero16();
 #pragma unroll
-        for (int c = 0; c < KS; ++c) sc = mfma32(bw_row<D>(kt, of, c, 32 * b), qr[c], sc);
-        const bool diag = kb + 31 > qw0;
-        float mx = -__builtin_inff();
+          for (int c = 0; c < KS; ++c) sc = mfma32(bw_row<D>(kt, of, c, 32 * b), qr[c], sc);
+          const bool diag = kb + 31 > qw0;
+          float mx = -__builtin_inff();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sc[r] * sl2;
-          if (diag && kb + acc_row(r, hh) > qcol) v = -__builtin_inff();
-          sc[r] = v;
-          mx = fmaxf(mx, v);
+          for (int r = 0; r < 16; ++r) {
+            float v = sc[r] * sl2;
+            if (diag && kb + acc_row(r, hh) > qcol) v = -__builtin_inff();
+            sc[r] = v;
+            mx = fmaxf(mx, v);
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 32));   // finite: key kb precedes every query of the wave
+          if (__ballot(mx > m + 8.f)) {
+            const float mn = fmaxf(m, mx);
+            const float al = bw_exp2(m - mn);
+            l *= al;
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[d][r] *= al;
+            m = mn;
+          }
+          float ps = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = bw_exp2(sc[r] - m);
+            sc[r] = p;
+            ps += p;
+          }
+          l += ps;
+          const bf16x8 p0 = acc_op(sc, 0), p1 = acc_op(sc, 1);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            o[d] = mfma32(bw_tr<D>(vt, of, d, 32 * b), p0, o[d]);
+            o[d] = mfma32(bw_tr<D>(vt, of, d, 32 * b + 16), p1, o[d]);
+          }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));   // finite: key kb precedes every query of the wave
-        if (__ballot(mx > m + 8.f)) {
-          const float mn = fmaxf(m, mx);
-          const float al = bw_exp2(m - mn);
-          l *= al;
+      });
+      const float lt = l + __shfl_xor(l, 32);
+      const float lse2s = m + __log2f(lt);
+      // E = <dA, A_dot>: the lane holds 16 DB values of its query's row of O^T, in
+      // runs of four
+      float e = 0.f;
+      if (qvalid) {
 #pragma unroll
-          for (int d = 0; d < DB; ++d)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[d][r] *= al;
-          m = mn;
-        }
-        float ps = 0.f;
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + 32 * d + 8 * j4 + 4 * hh);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = bw_exp2(sc[r] - m);
-          sc[r] = p;
-          ps += p;
-        }
-        l += ps;
-        const bf16x8 p0 = acc_op(sc, 0), p1 = acc_op(sc, 1);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          o[d] = mfma32(bw_tr<D>(vt, of, d, 32 * b), p0, o[d]);
-          o[d] = mfma32(bw_tr<D>(vt, of, d, 32 * b + 16), p1, o[d]);
-        }
+            for (int j = 0; j < 4; ++j) e = __builtin_fmaf(bf2f(da[j]), o[d][4 * j4 + j], e);
+          }
       }
-    });
-    const float lt = l + __shfl_xor(l, 32);
-    const float lse2 = m + __log2f(lt);
-    // E = <dA, A_dot>: the lane holds 16 DB values of its query's row of O^T, in
-    // runs of four
-    float e = 0.f;
-    if (qvalid) {
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + 32 * d + 8 * j4 + 4 * hh);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) e = __builtin_fmaf(bf2f(da[j]), o[d][4 * j4 + j], e);
-        }
-    }
-    e = (e + __shfl_xor(e, 32)) / lt;
-    const float Dv = omg * e;
-    if (qvalid && hh == 0) {
-      a.lse[qrow] = lse2;
-      a.drow[qrow] = Dv;
+      e = (e + __shfl_xor(e, 32)) / lt;
+      Dv = omg * e;
+      lse2 = lse2s;
+      if (qvalid && hh == 0) a.lse[qrow] = lse2;
+    } else {
+      lse2 = a.lse[qrow];
     }
 
     // ---- the retrieval's statistics of the wave's queries.  The lane's LDS
@@ -460,7 +466,7 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
     const float inv_den = has_mem && den > 0.f ? 1.f / den : 0.f;
     // <dA, A_mem> with A_mem^T = (colsum(M) + M^T q'^T) / den; the lane holds 16 DB
     // values of its query's transposed row, in runs of four
-    float em = 0.f;
+    float em = 0.f, ea = 0.f;   // <dA, A_mem>, and (SAVED) <dA, A>
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
       f32x16 am = zero16();
@@ -474,18 +480,26 @@ __global__ __launch_bounds__(64 * kBw) void bwd_q2_kernel(BwdArgs a) {
         const bf16x4 da = *reinterpret_cast<const bf16x4*>(DO + qrow * D + col);
 #pragma unroll
         for (int j = 0; j < 4; ++j) em = __builtin_fmaf(bf2f(da[j]), (msum[col + j] + am[4 * j4 + j]) * inv_den, em);
+        if constexpr (SAVED) {
+          const bf16x4 ao = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.out_fw) + qrow * D + col);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ea = __builtin_fmaf(bf2f(da[j]), bf2f(ao[j]), ea);
+        }
       }
     }
     em += __shfl_xor(em, 32);
+    if constexpr (SAVED) Dv = (ea + __shfl_xor(ea, 32)) - g * em;
     const float rs = g * inv_den;
     const float dden = -g * em * inv_den;
     if (qvalid && hh == 0) {
       a.rs[qrow] = rs;
       a.dden[qrow] = dden;
+      a.drow[qrow] = Dv;
     }
-    {   // the gate's share of dbeta for the wave's 32 queries: g (1 - g) sum (<dA, A_mem> - E)
-      const float bt = wave_sum(qvalid && hh == 0 ? em - e : 0.f);
-      if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] = bt * g * omg;
+    {   // the gate's share of dbeta for the wave's 32 queries:
+        // g (1 - g) sum (<dA, A_mem> - <dA, A_dot>) = g sum ((1 - g) <dA, A_mem> - D)
+      const float bt = wave_sum(qvalid && hh == 0 ? omg * em - Dv : 0.f);
+      if (qvalid && lane == 0) a.dbeta_part[((int64_t)bh * a.S + s) * a.nqb + qw0 / 32] = bt * g;
     }
 
     // ---- second sweep: dq^T += K^T dS^T
@@ -1172,7 +1186,8 @@ hipError_t launch_backward_attention_mfma(const BwdArgs& a, hipStream_t stream) 
   const int64_t npair = ((a.N + kBwRows - 1) / kBwRows + 1) / 2;
   const int64_t nblk = npair * a.S * a.BH;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_q2_kernel<D>, dim3((unsigned)nblk), dim3(64 * kBw), 0, stream, a);
+  if (a.out_fw) hipLaunchKernelGGL((bwd_q2_kernel<D, true>), dim3((unsigned)nblk), dim3(64 * kBw), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_q2_kernel<D, false>), dim3((unsigned)nblk), dim3(64 * kBw), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_kv2_kernel<D>, dim3((unsigned)nblk), dim3(64 * kBw), 0, stream, a);
   return hipGetLastError();

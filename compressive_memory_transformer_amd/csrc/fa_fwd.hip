@@ -516,7 +516,8 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
                                              const float* __restrict__ zs, const float* __restrict__ cs,
                                              const LdsAddr<D>& ad, bool has_memory, float beta, float inv_sc,
                                              bf16* __restrict__ ob, bf16* __restrict__ stages, int wave,
-                                             const bf16* __restrict__ qg, const bf16* __restrict__ mlo) {
+                                             const bf16* __restrict__ qg, const bf16* __restrict__ mlo,
+                                             float* __restrict__ lrow) {
   // The lane index is computed here (from the exec mask, with an opaque base) so
   // that it and the per-lane addresses below are not hoisted to the kernel start
   // and kept live (spilled) across the tile loop: the reload of a spill here
@@ -534,6 +535,7 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
   const int l32 = lane & 31, hi = lane >> 5;
   const float l_tot = X.l + __shfl_xor(X.l, 32);
   const float inv_l = 1.f / l_tot;
+  if (lrow && hi == 0) lrow[l32] = X.m + __log2f(l_tot);   // the row's log-normaliser, when kept
   bf16x8 qp[D / 16];                   // q' = sigma(q) - 1 (bf16), the B operand of M^T q'
   bf16x8 ql[D / 16];                   // precise path: q' - qp (bf16)
   const bool precise = X.big;
@@ -653,6 +655,7 @@ struct FaCtx {
   const bf16* snapMlo;     // its bf16 remainder
   const float* snapz;
   const float* snapc;
+  float* lb;               // the segment's log-normalisers, or null
   uint32_t seg_bytes;
   int N, nk, wave;
   bool has_memory;
@@ -777,7 +780,7 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf1
   if (act && __any(X.bad)) recompute_block<D>(X, r0, cx.kseg, cx.vseg);
 
   if (act) finish_block<D>(X, k0s, zc, zc + 256, ad, cx.has_memory, cx.beta, 1.f / cx.sc, cx.ob + (int64_t)r0 * D,
-                           stg, cx.wave, cx.qb + (int64_t)r0 * D, cx.snapMlo);
+                           stg, cx.wave, cx.qb + (int64_t)r0 * D, cx.snapMlo, cx.lb ? cx.lb + r0 : nullptr);
   // the snapshot in k0s is no longer read (the output stores stay in flight)
   if (next) wait_lds_and_sync();
 }
@@ -811,6 +814,7 @@ void fa_fwd_kernel(FaArgs a) {
   cx.snapMlo = a.snapMlo + (int64_t)sh * D * D;
   cx.snapz = a.snapz + (int64_t)sh * D;
   cx.snapc = a.snapc + (int64_t)sh * D;
+  cx.lb = a.lse ? a.lse + tok0 : nullptr;
   cx.seg_bytes = (uint32_t)a.N * D * 2;
   cx.N = a.N;
   cx.nk = (a.N + kBN - 1) / kBN;

@@ -26,6 +26,8 @@ struct FaArgs {
   int nq;                // query tiles per segment (set by the launcher)
   int64_t seg_base;      // segments folded into the state before this call
   float sc_log2;         // softmax scale * log2(e)
+  float* lse;            // [B*H*L] or null: log2 of each query row's local softmax denominator
+                         // over the base-2 scores sc_log2 q.k (reference maximum included)
 };
 template <int D> hipError_t launch_fa_fwd(const FaArgs& a, hipStream_t stream);
 // Workgroups of one fused-kernel launch over seg_heads (b, h, segment) tiles.
@@ -173,7 +175,7 @@ struct BwdArgs {
   float* ez;             // [BH*S][dk]
   float* gzs;            // [BH*S][dk] dL/dz_s
   float* lse;            // [BH*L] softmax log-normaliser of each row (natural log on the VALU
-                         // path, base 2 on the MFMA path)
+                         // path, base 2 on the MFMA path; the forward's, read only, when out_fw is set)
   float* drow;           // [BH*L] <(1 - g) dA, A_dot>
   float* rs;             // [BH*L] g / den (0 without memory)
   float* dden;           // [BH*L]
@@ -185,6 +187,8 @@ struct BwdArgs {
   float* dbeta_part;     // [BH*S][nqb]
   float* Amat;           // delta rule, bf16 path: [BH*S][dk][dk] sigma(K)^T diag(1/e) sigma(K)
   float* gpart;          // bf16 MFMA path: [BH*S][dk][dv] + [BH*S][dk], the Gram kernels' second halves
+  const void* out_fw;    // bf16 MFMA path, or null: the forward's output A [BH*L][dv], with its
+                         // log-normalisers in lse (the softmax statistics are then not recomputed)
   int B, H, BH, N, S, dk, dv, nqb;
   int64_t L, seg_base;
   int delta;

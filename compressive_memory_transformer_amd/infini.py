@@ -112,6 +112,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.infini_attn_backward_sequence.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                   vp, sz, vp]
     lib.infini_attn_backward_sequence.restype = ctypes.c_int
+    lib.infini_attn_forward_sequence_train.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.infini_attn_forward_sequence_train.restype = ctypes.c_int
+    lib.infini_attn_backward_sequence_saved.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                        vp, vp, vp, vp, sz, vp]
+    lib.infini_attn_backward_sequence_saved.restype = ctypes.c_int
     lib.infini_attn_layer_workspace_bytes.argtypes = [sp, i32, i64]
     lib.infini_attn_layer_workspace_bytes.restype = sz
     lib.infini_attn_layer_forward.argtypes = [sp, vp, i32, vp, vp, i64, vp, vp, vp, sz, vp]
@@ -231,6 +236,26 @@ def backward_sequence(st: State, q, k, v, seq_len, beta, dout, dM, dz, dq, dk, d
     return _check(rc) if check else rc
 
 
+def forward_sequence_train(st: State, q, k, v, seq_len, beta, out, lse, workspace, ws_bytes, stream=None,
+                           check=True) -> int:
+    """forward_sequence that also writes each query row's base-2 softmax
+    log-normaliser into lse (fp32 [B, H, seq_len]) for backward_sequence_saved."""
+    rc = load_library().infini_attn_forward_sequence_train(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len,
+                                                           _ptr(beta), _ptr(out), _ptr(lse), _ptr(workspace),
+                                                           ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
+def backward_sequence_saved(st: State, q, k, v, seq_len, beta, out, lse, dout, dM, dz, dq, dk, dv, dbeta, dM0,
+                            dz0, workspace, ws_bytes, stream=None, check=True) -> int:
+    """backward_sequence given the output and lse of a forward_sequence_train call."""
+    rc = load_library().infini_attn_backward_sequence_saved(
+        ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v), seq_len, _ptr(beta), _ptr(out), _ptr(lse), _ptr(dout),
+        _ptr(dM), _ptr(dz), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(workspace),
+        ws_bytes, stream)
+    return _check(rc) if check else rc
+
+
 def layer_workspace_bytes(st: State, d_model: int, seq_len: int) -> int:
     return load_library().infini_attn_layer_workspace_bytes(ctypes.byref(st), d_model, seq_len)
 
@@ -307,6 +332,19 @@ class InfiniAttention:
         forward_sequence(self.state, q, k, v, seq_len, beta, out, ws, nbytes, _stream_handle(self.torch, stream))
         return out
 
+    def forward_sequence_train(self, q, k, v, beta, out=None, lse=None, stream=None):
+        """forward_sequence that also returns each query row's base-2 softmax
+        log-normaliser (fp32 [B, H, L]) for backward_sequence(..., saved=(out, lse))."""
+        seq_len = q.shape[2]
+        if out is None:
+            out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
+        if lse is None:
+            lse = self.torch.empty(q.shape[:3], dtype=self.torch.float32, device=q.device)
+        ws, nbytes = self.workspace(seq_len)
+        forward_sequence_train(self.state, q, k, v, seq_len, beta, out, lse, ws, nbytes,
+                               _stream_handle(self.torch, stream))
+        return out, lse
+
     def forward_segment(self, q, k, v, beta, out=None, stream=None):
         if out is None:
             out = self.torch.empty((*q.shape[:3], v.shape[3]), dtype=q.dtype, device=q.device)
@@ -381,11 +419,14 @@ class InfiniAttention:
                       _stream_handle(torch, stream))
         return y
 
-    def backward_sequence(self, q, k, v, beta, dout, M0, z0, segments_done, dM=None, dz=None, stream=None):
+    def backward_sequence(self, q, k, v, beta, dout, M0, z0, segments_done, dM=None, dz=None, stream=None,
+                          saved=None):
         """Gradients of a forward_sequence call over q, k, v, beta that started
         from the state (M0, z0, segments_done), for the output gradient dout and
-        the final-state gradients dM, dz (None for zero).  Returns a dict with dq,
-        dk, dv (input dtype), dbeta [H], dM0 and dz0 (fp32)."""
+        the final-state gradients dM, dz (None for zero).  With saved = (out, lse)
+        from forward_sequence_train over the same call, the softmax statistics are
+        not recomputed.  Returns a dict with dq, dk, dv (input dtype), dbeta [H],
+        dM0 and dz0 (fp32)."""
         torch = self.torch
         st = State.from_buffer_copy(self.state)
         st.M, st.z, st.segments_done = _ptr(M0), _ptr(z0), int(segments_done)
@@ -399,7 +440,12 @@ class InfiniAttention:
         out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
                "dbeta": torch.empty(self.state.heads, dtype=torch.float32, device=self.device),
                "dM0": torch.empty_like(M0), "dz0": torch.empty_like(z0)}
-        backward_sequence(st, q, k, v, seq_len, beta, dout, dM, dz, out["dq"], out["dk"], out["dv"], out["dbeta"],
-                          out["dM0"], out["dz0"], ws, need, _stream_handle(torch, stream))
+        if saved is None:
+            backward_sequence(st, q, k, v, seq_len, beta, dout, dM, dz, out["dq"], out["dk"], out["dv"],
+                              out["dbeta"], out["dM0"], out["dz0"], ws, need, _stream_handle(torch, stream))
+        else:
+            backward_sequence_saved(st, q, k, v, seq_len, beta, saved[0], saved[1], dout, dM, dz, out["dq"],
+                                    out["dk"], out["dv"], out["dbeta"], out["dM0"], out["dz0"], ws, need,
+                                    _stream_handle(torch, stream))
         out["_workspace"] = raw   # kept alive until the caller synchronises
         return out

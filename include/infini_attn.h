@@ -243,6 +243,37 @@ int infini_attn_backward_sequence(const infini_attn_state *st, const void *q, co
                                   void *dk, void *dv, float *dbeta, float *dM0, float *dz0,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* Training pair: a forward that keeps the local attention's softmax statistics,
+ * and a backward that uses them with the forward's output instead of
+ * recomputing the first of its two sweeps over the keys (the same derivatives
+ * as infini_attn_backward_sequence; section 3.1 of the page "精读笔记：
+ * Infini-attention" for the causal softmax, 3.3-3.5 for the memory and gate).
+ * bf16 MFMA path only (d_key = d_value in {64, 128}, segment_len a multiple of
+ * 64): INFINI_EUNSUPPORTED otherwise.
+ *
+ * forward_sequence_train: forward_sequence (the same arguments, the same out and
+ * state, bitwise) that also writes lse, fp32 [B, H, seq_len] (4-byte aligned,
+ * caller-owned, overlapping nothing else): per query row t, log2 of
+ * sum over the causal keys j <= t of 2^(scale q_t.k_j log2 e), i.e. the
+ * row's softmax log-normaliser in base 2 of the scores scale q.k log2 e.
+ *
+ * backward_sequence_saved: backward_sequence given out (the forward's output A,
+ * bf16 [B, H, seq_len, d_value], 16-byte aligned) and lse from a
+ * forward_sequence_train call over the same inputs and starting state; both are
+ * read only and may not overlap an output or the workspace.  Workspace size
+ * from infini_attn_backward_workspace_bytes.  Other arguments, results and
+ * errors as backward_sequence. */
+int infini_attn_forward_sequence_train(infini_attn_state *st, const void *q, const void *k,
+                                       const void *v, int64_t seq_len, const float *beta, void *out,
+                                       float *lse, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+int infini_attn_backward_sequence_saved(const infini_attn_state *st, const void *q, const void *k,
+                                        const void *v, int64_t seq_len, const float *beta,
+                                        const void *out, const float *lse, const void *dout,
+                                        const float *dM, const float *dz, void *dq, void *dk, void *dv,
+                                        float *dbeta, float *dM0, float *dz0, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * The layer: the projections on either side of the segment stream
  * (section 3.1 of the page "精读笔记：Infini-attention": Q = X W_Q, K = X W_K,

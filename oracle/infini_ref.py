@@ -40,6 +40,9 @@ reason in the design notes of the repository):
   same M_{s-1} and z_{s-1}; z is updated exactly as in the linear rule;
 * the gate is g * A_mem + (1 - g) * A_dot with g = sigmoid(beta_h), one beta per
   head shared over the batch, applied in every segment including the first;
+* the local softmax's log-normaliser (``local_log_normaliser``, what a training
+  forward keeps for the backward) is reported in base 2: log2 of the causal
+  denominator of section 3.1, so the probabilities are 2^(scale q.k log2 e - lse);
 * streaming (the pages' "streaming inference", abstract of the close-reading
   page and point 4 of the key-idea list of the CSDN page): a token that arrives
   before its segment is complete attends causally to the tokens of its segment
@@ -108,6 +111,36 @@ def local_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: f
     p = np.exp(scores - row_max)
     p = p / p.sum(axis=1, keepdims=True)
     return p @ v
+
+
+def local_log_normaliser(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """Per query row i of one segment, the base-2 logarithm of the causal softmax
+    denominator of A_dot: log2 of the sum over keys j <= i of exp(scale q_i.k_j)
+    (close-reading page, section 3.1, with the causal mask of section 3.8 step 2).
+    In base 2 the row's probabilities are 2^(scale q_i.k_j log2(e) - lse_i).
+    q, k: [n, d_key]; returns [n], float64."""
+    n = q.shape[0]
+    scores = scale * (q @ k.T)
+    scores = np.where(causal_mask(n), scores, -np.inf)
+    row_max = scores.max(axis=1)
+    natural = row_max + np.log(np.exp(scores - row_max[:, None]).sum(axis=1))
+    return natural / math.log(2.0)
+
+
+def log_normalisers(q, k, segment_len: int, scale=None) -> np.ndarray:
+    """local_log_normaliser of every query row of a stream, segment by segment
+    (each segment attends only to itself): q, k [B, H, L, d_key] -> [B, H, L]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, L, dk = q.shape
+    sc = default_scale(dk, scale)
+    out = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            for s0 in range(0, L, segment_len):
+                rows = slice(s0, s0 + segment_len)
+                out[b, h, rows] = local_log_normaliser(q[b, h, rows], k[b, h, rows], sc)
+    return out
 
 
 def prefix_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, offset: int,

@@ -396,4 +396,46 @@ def pin_delta_matrix_form(o):
         assert np.allclose(got, (np.eye(dk) - A) @ M + fk.T @ v, rtol=1e-12, atol=1e-12)
         assert np.allclose(gz, z + fk.sum(axis=0))
 
+def pin_log_normaliser_of_equal_keys(o):
+    """Every key equal: row i sees i + 1 equal scores s, so the base-2
+    log-normaliser is s log2(e) + log2(i + 1)."""
+    n, d = 9, 4
+    q = _randn(61, n, d)
+    k = np.tile(_randn(62, 1, d), (n, 1))
+    scale = 0.37
+    s = scale * (q @ k[0])
+    want = s / math.log(2.0) + np.log2(np.arange(1, n + 1))
+    got = o.local_log_normaliser(q, k, scale)
+    assert np.allclose(got, want, rtol=0, atol=1e-12), (got, want)
+
+
+def pin_log_normaliser_is_scipy_logsumexp(o):
+    """Against scipy's logsumexp over each row's visible keys, in base 2."""
+    from scipy.special import logsumexp
+    n, d = 12, 5
+    q, k = _randn(63, n, d, scale=2.0), _randn(64, n, d, scale=2.0)
+    scale = 0.6
+    got = o.local_log_normaliser(q, k, scale)
+    for i in range(n):
+        want = logsumexp(scale * (q[i] @ k[: i + 1].T)) / math.log(2.0)
+        assert abs(got[i] - want) < 1e-12, (i, got[i], want)
+
+
+def pin_log_normaliser_normalises_the_attention(o):
+    """The probabilities 2^(scale q.k log2 e - lse) over the visible keys give
+    torch's causal SDPA output when applied to V (the default scale of the
+    attention), across the segments of a stream."""
+    B, H, N, S, d = 1, 2, 6, 2, 4
+    q, k, v = (_randn(65 + i, B, H, N * S, d) for i in range(3))
+    lse = o.log_normalisers(q, k, N)
+    scale = 1.0 / math.sqrt(d)
+    for h in range(H):
+        for s0 in range(0, N * S, N):
+            rows = slice(s0, s0 + N)
+            qs, ks, vs = q[0, h, rows], k[0, h, rows], v[0, h, rows]
+            p = np.exp2(scale * (qs @ ks.T) / math.log(2.0) - lse[0, h, rows][:, None])
+            p = np.where(np.tril(np.ones((N, N), bool)), p, 0.0)
+            assert np.allclose(p @ vs, _sdpa(qs * math.sqrt(d) * scale, ks, vs), atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -31,7 +31,7 @@ def _snapshot(st):
 def test_exports_every_declared_function():
     lib = ia.load_library()
     names = ia.header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ia.LIB_PATH], capture_output=True, text=True).stdout
@@ -273,6 +273,70 @@ def test_backward_rejects_bad_arguments(case):
     before = _snapshot(st)
     rc = ia.backward_sequence(st, q, k, v, L, beta, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws, nbytes, None,
                               check=False)
+    assert rc == expect, (case, ia.last_error())
+    assert ia.last_error()
+    assert _snapshot(st) == before
+
+
+@pytest.mark.parametrize("case", ["null_lse", "f32", "misaligned_lse", "alias_lse_out", "alias_lse_ws",
+                                  "small_ws"])
+def test_forward_train_rejects_bad_arguments(case):
+    st = _state()
+    L = 2 * 2048
+    need = ia.workspace_bytes(st, L)
+    q, k, v, beta, out, lse, ws, nbytes = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8, FAKE * 9, FAKE * 10, need
+    expect = ia.EINVAL
+    if case == "null_lse":
+        lse = None
+    elif case == "f32":
+        st = _state(dtype=ia.F32, d_key=32, d_value=32, segment_len=64)
+        L, nbytes, expect = 128, ia.workspace_bytes(st, 128), ia.EUNSUPPORTED
+    elif case == "misaligned_lse":
+        lse = FAKE * 9 + 2
+    elif case == "alias_lse_out":
+        lse = out + 1024
+    elif case == "alias_lse_ws":
+        lse = ws + 4096
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    before = _snapshot(st)
+    rc = ia.forward_sequence_train(st, q, k, v, L, beta, out, lse, ws, nbytes, None, check=False)
+    assert rc == expect, (case, ia.last_error())
+    assert ia.last_error()
+    assert _snapshot(st) == before
+
+
+@pytest.mark.parametrize("case", ["null_out", "null_lse", "f32", "misaligned_out", "misaligned_lse",
+                                  "alias_dq_out", "alias_ws_lse", "small_ws"])
+def test_backward_saved_rejects_bad_arguments(case):
+    st = _state()
+    L = 2 * 2048
+    need = ia.backward_workspace_bytes(st, L)
+    q, k, v, beta, dout = FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, FAKE * 8
+    dq, dk, dv, dbeta, dM0, dz0 = FAKE * 9, FAKE * 10, FAKE * 11, FAKE * 12, FAKE * 13, FAKE * 14
+    out, lse = FAKE * 16, FAKE * 17
+    dM, dz, ws, nbytes = None, None, FAKE * 15, need
+    expect = ia.EINVAL
+    if case == "null_out":
+        out = None
+    elif case == "null_lse":
+        lse = None
+    elif case == "f32":
+        st = _state(dtype=ia.F32, d_key=32, d_value=32, segment_len=64)
+        L, nbytes, expect = 128, ia.backward_workspace_bytes(st, 128), ia.EUNSUPPORTED
+    elif case == "misaligned_out":
+        out = FAKE * 16 + 8
+    elif case == "misaligned_lse":
+        lse = FAKE * 17 + 2
+    elif case == "alias_dq_out":
+        dq = out + 64
+    elif case == "alias_ws_lse":
+        lse = ws + 4096
+    elif case == "small_ws":
+        nbytes, expect = need - 1, ia.EWORKSPACE
+    before = _snapshot(st)
+    rc = ia.backward_sequence_saved(st, q, k, v, L, beta, out, lse, dout, dM, dz, dq, dk, dv, dbeta, dM0, dz0, ws,
+                                    nbytes, None, check=False)
     assert rc == expect, (case, ia.last_error())
     assert ia.last_error()
     assert _snapshot(st) == before

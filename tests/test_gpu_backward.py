@@ -71,6 +71,10 @@ def test_backward_matches_oracle(case, rule):
                               dz=torch.from_numpy(dz).cuda())
     torch.cuda.synchronize()
     want = og.backward_sequence(qn, kn, vn, beta, rule, N, don, dM=dM, dz=dz, M0=M0, z0=z0, segments_done=done)
+    _check_grads(g, want, name, rule, dtype, B, H, S, N)
+
+
+def _check_grads(g, want, name, rule, dtype, B, H, S, N):
     tol = gh.tol(dtype)
     worst = {}
     for key in ("dq", "dk", "dv"):
@@ -96,23 +100,79 @@ def test_backward_matches_oracle(case, rule):
     assert e <= tol, f"{name}/{rule} dbeta: error {e:.3e} ({gb} vs {want['dbeta']})"
 
 
+# the saved-statistics pair runs on the MFMA shapes only
+SAVED_CASES = [c for c in CASES if c[8] == "bf16" and c[4] == c[5] and c[4] in (64, 128) and c[6] % 64 == 0]
+
+
 @pytest.mark.parametrize("rule", ["linear", "delta"])
-def test_full_size_sampled_head(rule):
+@pytest.mark.parametrize("case", SAVED_CASES, ids=[c[0] for c in SAVED_CASES])
+def test_backward_saved_matches_oracle(case, rule):
+    """forward_sequence_train writes the output of forward_sequence bitwise and the
+    rows' base-2 log-normalisers (against the oracle's); backward_sequence_saved
+    on them gives the oracle's gradients."""
+    from compressive_memory_transformer_amd import infini as ia
+    from oracle import infini_ref as ref
+    torch = gh.torch_mod()
+    name, seed, B, H, dk, dv, N, S, dtype, done = case
+    gh.log(f"backward saved {name} rule={rule}")
+    w = _workload(name, seed, B, H, dk, dv, N, S, dtype)
+    qn, kn, vn, don = (syn.full_tensor(w, i) for i in (syn.Q_ID, syn.K_ID, syn.V_ID, syn.DOUT_ID))
+    beta = syn.betas(w)
+    dM, dz = syn.state_grads(w)
+    if done:
+        M0, z0 = syn.initial_state(w, done)
+    else:
+        M0, z0 = np.zeros((B, H, dk, dv), np.float32), np.zeros((B, H, dk), np.float32)
+    q, k, v, dout = (_device(torch, x, dtype) for x in (qn, kn, vn, don))
+    beta_t, M0t, z0t = (torch.from_numpy(x).cuda() for x in (beta, M0, z0))
+    eng = ia.InfiniAttention(B, H, dk, dv, N, dtype, rule)
+
+    def start():
+        eng.M.copy_(M0t)
+        eng.z.copy_(z0t)
+        eng.state.segments_done = done
+
+    start()
+    out_plain = eng.forward_sequence(q, k, v, beta_t)
+    start()
+    out, lse = eng.forward_sequence_train(q, k, v, beta_t)
+    torch.cuda.synchronize()
+    assert eng.segments_done == done + S
+    assert torch.equal(out, out_plain), f"{name}/{rule}: the training forward's output differs"
+    e = float(np.abs(gh.to_host(lse) - ref.log_normalisers(qn, kn, N)).max())
+    gh.log(f"  lse max abs error {e:.2e} (log2 units)")
+    assert e <= gh.tol(dtype), f"{name}/{rule} lse: error {e:.3e}"
+    g = eng.backward_sequence(q, k, v, beta_t, dout, M0t, z0t, done, dM=torch.from_numpy(dM).cuda(),
+                              dz=torch.from_numpy(dz).cuda(), saved=(out, lse))
+    torch.cuda.synchronize()
+    want = og.backward_sequence(qn, kn, vn, beta, rule, N, don, dM=dM, dz=dz, M0=M0, z0=z0, segments_done=done)
+    _check_grads(g, want, name + "/saved", rule, dtype, B, H, S, N)
+
+
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_full_size_sampled_head(rule, saved):
     """The 32K-token single-layer stream at its full size (the shape bench.py times):
     one head's gradients over all 16 segments against the oracle (heads are
-    independent; with one batch row dbeta of that head is that head's alone)."""
+    independent; with one batch row dbeta of that head is that head's alone), from
+    the backward that recomputes the softmax statistics and from the one given the
+    training forward's output and log-normalisers."""
     from compressive_memory_transformer_amd import infini as ia
     torch = gh.torch_mod()
     w = syn.WORKLOADS["layer_32k_linear"]
     h = 3
-    gh.log(f"backward full size {w.name} rule={rule}, head {h}")
+    gh.log(f"backward full size {w.name} rule={rule}, head {h}, saved={saved}")
     q, k, v, beta = gh.device_inputs(w)
     dout = gh.upload(w, syn.DOUT_ID)
     dM, dz = syn.state_grads(w)
     eng = ia.InfiniAttention(w.batch, w.heads, w.d_key, w.d_value, w.segment_len, "bf16", rule)
     zM, zz = torch.zeros_like(eng.M), torch.zeros_like(eng.z)
+    keep = None
+    if saved:
+        eng.reset()
+        keep = eng.forward_sequence_train(q, k, v, beta)
     g = eng.backward_sequence(q, k, v, beta, dout, zM, zz, 0, dM=torch.from_numpy(dM).cuda(),
-                              dz=torch.from_numpy(dz).cuda())
+                              dz=torch.from_numpy(dz).cuda(), saved=keep)
     torch.cuda.synchronize()
     qn, kn, vn, don = (syn.full_tensor(w, i, heads=[h]) for i in (syn.Q_ID, syn.K_ID, syn.V_ID, syn.DOUT_ID))
     want = og.backward_sequence(qn, kn, vn, syn.betas(w)[[h]], rule, w.segment_len, don, dM=dM[:, [h]],

@@ -128,6 +128,22 @@ def _stream_commits_every_call(q, k, v, beta, rule, segment_len, M0=None, z0=Non
     return res
 
 
+def _log_normaliser_natural(q, k, scale):
+    return _real_lse(q, k, scale) * math.log(2.0)
+
+
+def _log_normaliser_unscaled(q, k, scale):
+    return _real_lse(q, k, 1.0)
+
+
+def _log_normaliser_shifted_row(q, k, scale):
+    x = _real_lse(q, k, scale)
+    return np.concatenate([x[:1], x[:-1]])
+
+
+_real_lse = o.local_log_normaliser
+
+
 MUTANTS = {
     "prefix_mask_excludes_diagonal": ("prefix_causal_attention", _prefix_mask_excludes_diagonal),
     "prefix_offset_ignored": ("prefix_causal_attention", _prefix_offset_ignored),
@@ -146,6 +162,9 @@ MUTANTS = {
     "gate_weights_swapped": ("gate", _gate_swapped),
     "softmax_normalised_before_mask": ("local_causal_attention", _softmax_over_all_keys),
     "memory_written_before_read": ("segment_forward", _write_before_read),
+    "log_normaliser_in_natural_log": ("local_log_normaliser", _log_normaliser_natural),
+    "log_normaliser_without_scale": ("local_log_normaliser", _log_normaliser_unscaled),
+    "log_normaliser_of_previous_row": ("local_log_normaliser", _log_normaliser_shifted_row),
 }
 
 
