@@ -140,10 +140,74 @@ int record(void* const* events, int i, hipStream_t stream) {
   return e == hipSuccess ? INFINI_OK : hip_fail(e, "hipEventRecord");
 }
 
+// ------------------------------------------------------------------ delta pipeline
+// The delta rule's chain is sequential over the segments and keeps few CUs busy.
+// On the pipelined path it runs on a side stream in kPipeChunks ranges of
+// segments, and the fused attention of each range follows on the caller's stream
+// once that range is chained, beside the chain of the later ranges.  One side
+// stream (default priority) and kPipeChunks + 1 events per device, created on
+// first use and kept until the process ends; a call's records and waits are
+// enqueued under g_pipe_mu so that calls from several host threads do not
+// interleave them (a wait binds to the event's latest record when it is enqueued).
+constexpr int kPipeChunks = 8;
+constexpr int kPipeDevices = 64;
+struct Pipe {
+  hipStream_t side = nullptr;
+  hipEvent_t ev[kPipeChunks + 1] = {};
+  bool ready = false;
+  int cus = 0;   // compute units of the device
+};
+std::mutex g_pipe_mu;
+Pipe g_pipe[kPipeDevices];
+
+// The current device's entry (g_pipe_mu held), with its compute-unit count.
+int pipe_device(Pipe** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kPipeDevices) return fail(INFINI_EUNSUPPORTED, "device index %d out of range", dev);
+  Pipe& p = g_pipe[dev];
+  if (p.cus <= 0 && (e = hipDeviceGetAttribute(&p.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) {
+    p.cus = 0;
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  *out = &p;
+  return INFINI_OK;
+}
+
+// Number of ranges for the pipelined delta path, or 0 when it does not pay: the
+// chain's workgroups must leave at least half of the compute units to the fused
+// kernel (they hold whole CUs), and each range's fused launch must still fill
+// the device twice over.
+int pipe_ranges(const Pipe& p, int64_t chain_wgs, int64_t fa_wgs_total, int S) {
+  if (p.cus <= 0 || 2 * chain_wgs > p.cus) return 0;
+  const int64_t by_fill = fa_wgs_total / (2 * (int64_t)p.cus);
+  const int nc = (int)std::min<int64_t>(std::min<int64_t>(kPipeChunks, S), by_fill);
+  return nc >= 2 ? nc : 0;
+}
+
+// Creates the device's side stream and events on first use (g_pipe_mu held).
+int pipe_ready(Pipe& p) {
+  hipError_t e;
+  if (!p.ready) {
+    if (!p.side && (e = hipStreamCreateWithFlags(&p.side, hipStreamNonBlocking)) != hipSuccess) {
+      p.side = nullptr;
+      return hip_fail(e, "hipStreamCreateWithFlags");
+    }
+    for (hipEvent_t& ev : p.ev)
+      if (!ev && (e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+        ev = nullptr;
+        return hip_fail(e, "hipEventCreateWithFlags");
+      }
+    p.ready = true;
+  }
+  return INFINI_OK;
+}
+
 template <int D>
 int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t L, int S,
              const float* beta, void* out, char* ws, const WsLayout& w, hipStream_t stream,
-             void* const* events, float* lse = nullptr) {
+             void* const* events, float* lse = nullptr, bool pipeline = false) {
   int rc;
   if ((rc = record(events, 0, stream)) != INFINI_OK) return rc;
   using infini::bf16;
@@ -164,6 +228,39 @@ int run_bf16(infini_attn_state* st, const void* q, const void* k, const void* v,
     infini::DeltaArgs d{static_cast<const bf16*>(k), static_cast<const bf16*>(v), st->M, st->z, snapM, snapMlo,
                         snapz, snapc, reinterpret_cast<float*>(ws + w.cM), reinterpret_cast<float*>(ws + w.cz),
                         reinterpret_cast<bf16*>(ws + w.amat), B * H, S, N, L, st->segments_done};
+    // the pipelined path where it pays (the lock is held while its launches are enqueued)
+    std::unique_lock<std::mutex> lock(g_pipe_mu, std::defer_lock);
+    Pipe* pp = nullptr;
+    int nc = 0;
+    if (pipeline && !events && S >= 2) {
+      lock.lock();
+      if ((rc = pipe_device(&pp)) != INFINI_OK) return rc;
+      nc = pipe_ranges(*pp, (int64_t)B * H * (D / 16), infini::fa_fwd_blocks((int64_t)B * H * S, N), S);
+      if (nc == 0) lock.unlock();
+    }
+    if (nc > 0) {
+      infini::FaArgs f{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), beta,
+                       snapM, snapMlo, snapz, snapc, static_cast<bf16*>(out), B, H, S, N, L, 0,
+                       st->segments_done, (float)((double)st->scale * 1.4426950408889634), lse};
+      if ((rc = pipe_ready(*pp)) != INFINI_OK) return rc;
+      if ((e = infini::launch_delta_prep<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta state launch");
+      if ((e = hipEventRecord(pp->ev[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipStreamWaitEvent(pp->side, pp->ev[0], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+      const int per = (S + nc - 1) / nc;
+      for (int c = 0; c < nc && c * per < S; ++c) {
+        d.s0 = c * per;
+        d.sn = std::min(per, S - d.s0);
+        if ((e = infini::launch_delta_chain<D>(d, pp->side)) != hipSuccess) return hip_fail(e, "delta chain launch");
+        if ((e = hipEventRecord(pp->ev[1 + c], pp->side)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      }
+      for (int c = 0; c < nc && c * per < S; ++c) {
+        if ((e = hipStreamWaitEvent(stream, pp->ev[1 + c], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        f.s0 = c * per;
+        f.sn = std::min(per, S - f.s0);
+        if ((e = infini::launch_fa_fwd<D>(f, stream)) != hipSuccess) return hip_fail(e, "fa_fwd launch");
+      }
+      return INFINI_OK;
+    }
     if ((e = infini::launch_delta_state<D>(d, stream)) != hipSuccess) return hip_fail(e, "delta state launch");
   }
   if ((rc = record(events, 1, stream)) != INFINI_OK) return rc;
@@ -387,7 +484,7 @@ size_t infini_attn_workspace_bytes(const infini_attn_state* st, int64_t seq_len)
 
 static int forward_impl(infini_attn_state* st, const void* q, const void* k, const void* v, int64_t seq_len,
                         const float* beta, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                        void* const* events, float* lse = nullptr) {
+                        void* const* events, float* lse = nullptr, bool pipeline = true) {
   int rc = check_state(st);
   if (rc != INFINI_OK) return rc;
   if (!q || !k || !v || !beta || !out) return fail(INFINI_EINVAL, "q, k, v, beta and out must be non-NULL");
@@ -444,8 +541,8 @@ static int forward_impl(infini_attn_state* st, const void* q, const void* k, con
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (mfma_path(st)) {
-    rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events, lse)
-                          : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events, lse);
+    rc = st->d_key == 128 ? run_bf16<128>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events, lse, pipeline)
+                          : run_bf16<64>(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events, lse, pipeline);
   } else {
     rc = run_f32(st, q, k, v, seq_len, S, beta, out, ws, w, strm, events);
   }
@@ -482,7 +579,8 @@ int infini_attn_forward_sequence_noalloc(infini_attn_state* st, const void* q, c
                 w.total, kScratchBytes);
   void* ws = nullptr;
   if ((rc = scratch_address(&ws)) != INFINI_OK) return rc;
-  return forward_impl(st, q, k, v, seq_len, beta, out, ws, kScratchBytes, stream, nullptr);
+  // (not pipelined: the side stream and its events are resources created on first use)
+  return forward_impl(st, q, k, v, seq_len, beta, out, ws, kScratchBytes, stream, nullptr, nullptr, false);
 }
 
 int infini_attn_forward_sequence_profiled(infini_attn_state* st, const void* q, const void* k, const void* v,
@@ -690,8 +788,8 @@ int infini_attn_layer_forward(infini_attn_state* st, const void* x, int32_t d_mo
   hipError_t e = infini::launch_gemm_bf16(g1, strm);
   if (e != hipSuccess) return hip_fail(e, "QKV projection launch");
   infini_attn_state s = *st;
-  rc = s.d_key == 128 ? run_bf16<128>(&s, q, k, v, seq_len, (int)S64, beta, a, ws + fo, fw, strm, nullptr)
-                      : run_bf16<64>(&s, q, k, v, seq_len, (int)S64, beta, a, ws + fo, fw, strm, nullptr);
+  rc = s.d_key == 128 ? run_bf16<128>(&s, q, k, v, seq_len, (int)S64, beta, a, ws + fo, fw, strm, nullptr, nullptr, true)
+                      : run_bf16<64>(&s, q, k, v, seq_len, (int)S64, beta, a, ws + fo, fw, strm, nullptr, nullptr, true);
   if (rc != INFINI_OK) return rc;
   infini::GemmArgs g2{a, static_cast<const bf*>(w_o), static_cast<bf*>(y), nullptr, nullptr, nullptr,
                       (int)M, d_model, st->heads * st->d_value, 1, 0, (int)seq_len, st->heads, st->d_key,

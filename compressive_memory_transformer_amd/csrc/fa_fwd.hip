@@ -798,10 +798,12 @@ void fa_fwd_kernel(FaArgs a) {
 
   const int npair = (a.nq + 1) / 2;
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int sh = blk / npair;            // (b*H + h) * S + s
+  const int sn = a.sn > 0 ? a.sn : a.S;  // the launch covers segments s0 .. s0 + sn - 1 of every head
+  const int shl = blk / npair;
   const int pair = blk % npair;
-  const int bh = sh / a.S;
-  const int s = sh % a.S;
+  const int bh = shl / sn;
+  const int s = a.s0 + shl % sn;
+  const int sh = bh * a.S + s;           // (b*H + h) * S + s
   const int h = bh % a.H;
   const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
 
@@ -861,7 +863,9 @@ template <int D>
 hipError_t launch_fa_fwd(const FaArgs& args, hipStream_t stream) {
   FaArgs a = args;
   a.nq = (a.N + kBM - 1) / kBM;
-  const int64_t blocks = fa_fwd_blocks((int64_t)a.B * a.H * a.S, a.N);
+  const int sn = a.sn > 0 ? a.sn : a.S;
+  if (a.s0 < 0 || a.s0 + sn > a.S) return hipErrorInvalidValue;
+  const int64_t blocks = fa_fwd_blocks((int64_t)a.B * a.H * sn, a.N);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fa_fwd_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

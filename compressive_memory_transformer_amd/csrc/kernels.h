@@ -28,6 +28,7 @@ struct FaArgs {
   float sc_log2;         // softmax scale * log2(e)
   float* lse;            // [B*H*L] or null: log2 of each query row's local softmax denominator
                          // over the base-2 scores sc_log2 q.k (reference maximum included)
+  int s0, sn;            // segments s0 .. s0 + sn - 1 of every head (sn = 0: all S)
 };
 template <int D> hipError_t launch_fa_fwd(const FaArgs& a, hipStream_t stream);
 // Workgroups of one fused-kernel launch over seg_heads (b, h, segment) tiles.
@@ -81,8 +82,16 @@ struct DeltaArgs {
   int BH, S, N;
   int64_t L;
   int64_t seg_base;
+  int s0, sn;            // the chain's segments s0 .. s0 + sn - 1 (sn = 0: all S), from M, z
 };
+// The whole state stage: launch_delta_prep, then the chain over every segment.
 template <int D> hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream);
+// Its parallel part: C_s, c_s, the z prefix (snapshots of z) and A_s of every segment.
+template <int D> hipError_t launch_delta_prep(const DeltaArgs& a, hipStream_t stream);
+// Its sequential part over a.s0 .. a.s0 + a.sn - 1 (after launch_delta_prep): from
+// the state M (M_{s0-1}), the snapshots of M_{s-1} for those segments; the state
+// ends as M_{s0+sn-1}.  Consecutive ranges on one stream chain exactly.
+template <int D> hipError_t launch_delta_chain(const DeltaArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------------ VALU path
 // fp32 states and the bf16 shapes without MFMA kernels.  One segment per launch;

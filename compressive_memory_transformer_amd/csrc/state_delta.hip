@@ -272,9 +272,10 @@ void delta_chain_kernel(DeltaArgs a) {
   for (int r = 0; r < 4; ++r) p[r] = pl0[(4 * g + r) * C::LDP + col];
   __syncthreads();
 
-  const bf16* Abase = a.amat + (int64_t)bh * a.S * 2 * D * D + (int64_t)col * D + 8 * g;
-  const float* Cbase = a.cM + (int64_t)bh * a.S * D * D + (int64_t)(16 * cb + 4 * g) * D + col;
-  const int S = a.S;
+  // segments s0 .. s0 + S - 1 of the head (a range of the stream, or all of it)
+  const int s0 = a.s0, S = a.sn > 0 ? a.sn : a.S;
+  const bf16* Abase = a.amat + ((int64_t)bh * a.S + s0) * 2 * D * D + (int64_t)col * D + 8 * g;
+  const float* Cbase = a.cM + ((int64_t)bh * a.S + s0) * D * D + (int64_t)(16 * cb + 4 * g) * D + col;
   auto fetch = [&](ChainOps<D>& o, int s) {   // clamped: a load past the last segment is unused
     const int ss = s < S ? s : S - 1;
     const bf16* A0 = Abase + (int64_t)ss * 2 * D * D;
@@ -304,7 +305,7 @@ void delta_chain_kernel(DeltaArgs a) {
       if (l16 == 0) rs_s[wave * 16 + 4 * g + r] = rr;
     }
     lds_sync();
-    const int64_t shg = (int64_t)bh * S + s;
+    const int64_t shg = (int64_t)bh * a.S + s0 + s;
     {   // snapshot of M_{s-1}: 16 rows of M^T in bf16 hi and lo, and their sums
       const bf16x4 hv = *(const INFINI_LDS bf16x4*)(ph_s + srow * C::LDB + sk);
       const bf16x4 lv = *(const INFINI_LDS bf16x4*)(pl_s + srow * C::LDB + sk);
@@ -361,7 +362,7 @@ void delta_chain_kernel(DeltaArgs a) {
 
 // ------------------------------------------------------------------ launchers
 template <int D>
-hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream) {
+hipError_t launch_delta_prep(const DeltaArgs& a, hipStream_t stream) {
   const int64_t seg_heads = (int64_t)a.BH * a.S;
   if (seg_heads <= 0) return hipSuccess;
   if (seg_heads > 0x7fffffff || a.N % kAmT != 0) return hipErrorInvalidValue;
@@ -372,12 +373,33 @@ hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(delta_zscan_kernel<D>, dim3((unsigned)a.BH), dim3(D), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(delta_amat_kernel<D>, dim3((unsigned)seg_heads), dim3(kAmThreads), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_delta_chain(const DeltaArgs& a, hipStream_t stream) {
+  const int sn = a.sn > 0 ? a.sn : a.S;
+  if ((int64_t)a.BH * a.S <= 0 || sn <= 0) return hipSuccess;
+  if (a.s0 < 0 || a.s0 + sn > a.S) return hipErrorInvalidValue;
   hipLaunchKernelGGL(delta_chain_kernel<D>, dim3((unsigned)(a.BH * (D / 16))), dim3(64 * (D / 16)), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_delta_state(const DeltaArgs& a, hipStream_t stream) {
+  hipError_t e = launch_delta_prep<D>(a, stream);
+  if (e != hipSuccess) return e;
+  DeltaArgs all = a;
+  all.s0 = 0;
+  all.sn = a.S;
+  return launch_delta_chain<D>(all, stream);
+}
+
 template hipError_t launch_delta_state<64>(const DeltaArgs&, hipStream_t);
 template hipError_t launch_delta_state<128>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_prep<64>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_prep<128>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_chain<64>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_chain<128>(const DeltaArgs&, hipStream_t);
 
 }  // namespace infini

@@ -131,7 +131,12 @@ size_t infini_attn_workspace_bytes(const infini_attn_state *st, int64_t seq_len)
  * Errors: EINVAL (NULL pointers, seq_len not a positive multiple of N,
  * misalignment, out aliasing an input or the state), EWORKSPACE (workspace
  * missing, too small, misaligned or aliasing), EUNSUPPORTED (a launch grid above
- * 2^31 workgroups: split the call), EHIP (a launch failed). */
+ * 2^31 workgroups: split the call), EHIP (a launch failed).
+ * On the bf16 delta path a long stream with few heads runs its sequential memory
+ * chain on a side stream of the library's (one per device, default priority,
+ * created on the first such call and kept until the process ends) beside the
+ * attention on `stream`; the call's work is still ordered on `stream` (it waits
+ * for the side stream before its last kernel) and the results are the same. */
 int infini_attn_forward_sequence(infini_attn_state *st, const void *q, const void *k,
                                  const void *v, int64_t seq_len, const float *beta,
                                  void *out, void *workspace, size_t workspace_bytes,
@@ -170,7 +175,11 @@ int infini_attn_forward_sequence_profiled(infini_attn_state *st, const void *q, 
  * per-segment recurrence of section 3.4 of "精读笔记：Infini-attention": the
  * state carries M_{s-1}, z_{s-1} from one call to the next).  A stream fed
  * segment by segment gives bitwise the same results as one forward_sequence
- * call over the whole stream.  Arguments and errors as forward_sequence. */
+ * call over the whole stream, except at d_key = 128 when that call holds at least
+ * as many (b, h, segment) tiles as the device has compute units: its per-segment
+ * sums sigma(K)^T V and sum sigma(K) are then formed in another order, and the
+ * results agree up to that fp32 rounding.  Arguments and errors as
+ * forward_sequence. */
 int infini_attn_forward_segment(infini_attn_state *st, const void *q, const void *k,
                                 const void *v, const float *beta, void *out,
                                 void *workspace, size_t workspace_bytes, void *stream);

@@ -4,7 +4,8 @@ Small shapes (several query/key tiles, a ragged last query tile, both rules,
 both head widths), the tiny fp32 workload and the full 32K-token single-layer
 workload, plus the diagnostics: pure-memory and pure-local gates, a stress input
 with widely spread scores, segment-by-segment streaming == one sequence call
-(bitwise), reset, determinism and a NaN-poisoned workspace.
+(bitwise, also on the pipelined delta path), reset, determinism and a
+NaN-poisoned workspace.
 """
 
 import math
@@ -121,6 +122,38 @@ def test_segments_equal_sequence_bitwise(rule, dtype):
     assert torch.equal(out1, out2)
     assert torch.equal(e1.M, e2.M) and torch.equal(e1.z, e2.z)
     assert e1.segments_done == e2.segments_done == w.segments
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_delta_pipeline_bitwise(d):
+    """A delta stream whose chain leaves most compute units free (8 heads, 8 x
+    CUs / 8 segments of 128 tokens) takes the pipelined path: the chain in ranges
+    of segments on a side stream, the fused kernel of each range on the caller's
+    stream as soon as the range is chained.  Its output and final state equal,
+    bitwise, those of the same stream fed in calls of CUs / 8 segments, which are
+    not pipelined but tile the contributions the same way (as many (b, h,
+    segment) tiles per call as compute units); and the oracle's at the bf16
+    tolerance."""
+    from compressive_memory_transformer_amd import infini as ia
+    torch = gh.torch_mod()
+    H = 8
+    per_call = torch.cuda.get_device_properties(0).multi_processor_count // H
+    S, N = 8 * per_call, 128
+    w = syn.custom("pipeline_case", 43, 1, H, d, N, S, rules=("delta",))
+    gh.log(f"delta pipeline d={d}, {S} segments, reference calls of {per_call}")
+    q, k, v, beta = gh.device_inputs(w)
+    out1, e1 = gh.run(w, "delta", q, k, v, beta, mode="sequence")
+    e2 = ia.InfiniAttention(1, H, d, d, N, "bf16", "delta")
+    out2 = torch.empty_like(out1)
+    for c in range(0, S, per_call):
+        rows = slice(c * N, (c + per_call) * N)
+        out2[:, :, rows] = e2.forward_sequence(q[:, :, rows].contiguous(), k[:, :, rows].contiguous(),
+                                               v[:, :, rows].contiguous(), beta)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(e1.M, e2.M) and torch.equal(e1.z, e2.z)
+    res = gh.oracle_full(w, "delta")
+    gh.compare_full(w, "delta", out1, e1, res, label=f"pipeline d={d}")
 
 
 @pytest.mark.parametrize("rule", ["linear", "delta"])
