@@ -380,9 +380,14 @@ __device__ __forceinline__ void tile_pipe(QBlock<D>& X, const bf16* __restrict__
 #pragma unroll
   for (int c = 0; c < KS; ++c) ko[c] = lds_read8(kt + 32 * D + ad.kofs(c));
   INFINI_FENCE();
+  // On a diagonal tile the blocks right of the wave's diagonal block jd hold
+  // masked keys only: the loop leaves after jd, and the skipped blocks' share of
+  // the next load item is issued after it.
+  const int jd = MASK ? __builtin_amdgcn_readfirstlane((r0 - k0) >> 5) : kKB - 1;
 #pragma unroll
   for (int j = 0; j < kKB; ++j) {
-    const bool more = j + 1 < kKB;
+    if (MASK && j > jd) break;
+    const bool more = j + 1 < kKB;   // (on a diagonal tile, computed also for the block after jd)
     if (MASK) mask_scores(s, k0 + 32 * j, r0);
     f32x16 ns;
     bf16x8 p[2];
@@ -433,6 +438,19 @@ __device__ __forceinline__ void tile_pipe(QBlock<D>& X, const bf16* __restrict__
       INFINI_FENCE();
     }
     if (more) s = ns;
+  }
+  // the skipped blocks' shares of the next load item
+  if (MASK) {
+#pragma unroll
+    for (int j = 1; j < kDmaBlocks; ++j)
+      if (j > jd) {
+#pragma unroll
+        for (int w = 0; w < DPB; ++w) {
+          const int u = DPB * j + w;   // instruction u of this wave's K then V loads
+          if (u < NI) issue_part<D, false, 1>(u, pf.kb, pf.kbytes, pf.kn, pf.wave, *pf.dof);
+          else issue_part<D, true, 1>(u - NI, pf.vb, pf.vbytes, pf.vn, pf.wave, *pf.dof);
+        }
+      }
   }
 }
 
@@ -530,6 +548,7 @@ __device__ __forceinline__ void finish_block(const QBlock<D>& X, const bf16* __r
   // Likewise the gate is computed here from beta (a scalar register): a vector
   // copy kept from the kernel start is spilled, and its reload here would wait
   // for the next pass's Q loads in flight.
+  beta = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, beta)));
   asm volatile("" : "+s"(beta));
   const float g = sigmoid_gate(beta);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -667,22 +686,31 @@ struct FaCtx {
 // so that a wave reads its 32 rows as it reads a 32-key block of K.  Rows past
 // the segment end load zeros (their results are never used).
 template <int D>
-__device__ __forceinline__ void issue_q(const FaCtx<D>& cx, int qt, bf16* k1s, bf16* v1s, const DmaOfs<D>& dof) {
+__device__ __forceinline__ void issue_q(const bf16* qb, int N, int wave, int qt, bf16* k1s, bf16* v1s,
+                                        const DmaOfs<D>& dof) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int r = qt * kBM + half * kBN;
-    const bool in = r < cx.N;
-    issue_tile<D, false>(cx.qb + (in ? (int64_t)r * D : 0), in ? (uint32_t)(cx.N - r) * D * 2 : 0u,
-                         half ? v1s : k1s, cx.wave, dof);
+    const bool in = r < N;
+    issue_tile<D, false>(qb + (in ? (int64_t)r * D : 0), in ? (uint32_t)(N - r) * D * 2 : 0u,
+                         half ? v1s : k1s, wave, dof);
   }
 }
+
+// The pass after the current one: its query tile (qt < 0: none) and the Q rows
+// and V tensor of its (b, h, segment), which may be another item's.
+struct NextPass {
+  const bf16* qb;
+  const bf16* vseg;
+  int qt;
+};
 
 // The load item after step t of a pass with nsteps steps: tile t+1 (zeros past
 // the segment), or after the last step the snapshot of M^T (K part) together
 // with the V part of the next pass's tile 0 (zeros when there is none).
 template <int D>
-__device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int nsteps, bool next, bf16* kn,
-                                                bf16* vn, const DmaOfs<D>& dof) {
+__device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int nsteps, const NextPass& np,
+                                                bf16* kn, bf16* vn, const DmaOfs<D>& dof) {
   Prefetch<D> pf;
   pf.kn = kn;
   pf.vn = vn;
@@ -697,8 +725,8 @@ __device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int 
   } else {
     pf.kb = cx.snapM;
     pf.kbytes = cx.has_memory ? (uint32_t)(D * D * 2) : 0u;
-    pf.vb = cx.vseg;
-    pf.vbytes = next ? cx.seg_bytes : 0u;
+    pf.vb = np.qt >= 0 ? np.vseg : cx.vseg;
+    pf.vbytes = np.qt >= 0 ? cx.seg_bytes : 0u;
   }
   return pf;
 }
@@ -706,15 +734,15 @@ __device__ __forceinline__ Prefetch<D> next_item(const FaCtx<D>& cx, int t, int 
 // One query tile (pass) of the workgroup.  Tile t of the pass sits in slot t % 2
 // (k0s/v0s, k1s/v1s); every pass has an even number of steps, so the last one
 // uses slot 1 and brings the snapshot of M^T into k0s (with z and colsum into
-// zc) and, with a next pass (query tile qn >= 0), the V part of its tile 0 into
-// v0s; the Q rows of that pass go into slot 1 during the epilogue.  On entry
-// tile 0 is in slot 0 and the pass's Q rows in slot 1 (waited for and
-// synchronised).
+// zc) and, with a next pass (np.qt >= 0, of this or another (b, h, segment)),
+// the V part of its tile 0 into v0s; the Q rows of that pass go into slot 1
+// during the epilogue.  On entry tile 0 is in slot 0 and the pass's Q rows in
+// slot 1 (waited for and synchronised).
 template <int D>
-__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf16* k0s, bf16* v0s, bf16* k1s,
-                                         bf16* v1s, float* zc, bf16* stg, const LdsAddr<D>& ad,
+__device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, const NextPass& np, bf16* k0s, bf16* v0s,
+                                         bf16* k1s, bf16* v1s, float* zc, bf16* stg, const LdsAddr<D>& ad,
                                          const DmaOfs<D>& dof) {
-  const bool next = qn >= 0;
+  const bool next = np.qt >= 0;
   const int q0 = qt * kBM;
   const int r0 = q0 + 32 * cx.wave;          // first row of this wave's query block
   const bool act = r0 < cx.N;
@@ -754,7 +782,7 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf1
 #define INFINI_FA_STEP(T, KC, VC, KN, VN)                                                        \
   {                                                                                              \
     const int t_ = (T);                                                                          \
-    const Prefetch<D> pf_ = next_item<D>(cx, t_, nsteps, next, KN, VN, dof);                     \
+    const Prefetch<D> pf_ = next_item<D>(cx, t_, nsteps, np, KN, VN, dof);                     \
     if (t_ + 1 == nsteps && cx.has_memory && cx.wave == 0) {                                     \
       issue_row(cx.snapz, D * 4, zc);                                                            \
       issue_row(cx.snapc, D * 4, zc + 256);                                                      \
@@ -776,7 +804,7 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf1
 
   // slot 1 is free after the last step: the next pass's Q rows load during the
   // epilogue
-  if (next) issue_q<D>(cx, qn, k1s, v1s, dof);
+  if (next) issue_q<D>(np.qb, cx.N, cx.wave, np.qt, k1s, v1s, dof);
   if (act && __any(X.bad)) recompute_block<D>(X, r0, cx.kseg, cx.vseg);
 
   if (act) finish_block<D>(X, k0s, zc, zc + 256, ad, cx.has_memory, cx.beta, 1.f / cx.sc, cx.ob + (int64_t)r0 * D,
@@ -785,28 +813,23 @@ __device__ __forceinline__ void run_pass(const FaCtx<D>& cx, int qt, int qn, bf1
   if (next) wait_lds_and_sync();
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 1)
-void fa_fwd_kernel(FaArgs a) {
-  using L = FaLayout<D>;
-  __shared__ __attribute__((aligned(1024))) bf16 k0s[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 v0s[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 k1s[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 v1s[L::TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) float zc[512];   // z at [0, D), colsum(M) at [256, 256 + D)
-  __shared__ __attribute__((aligned(1024))) bf16 stg[kWaves * kStageElems];   // output stages
+// First token (in units of rows of q, k, v, out) of the (b, h, segment) of item it.
+__device__ __forceinline__ int64_t item_tok0(const FaArgs& a, int it, int npair, int sn) {
+  const int shl = it / npair;
+  const int bh = shl / sn;
+  const int s = a.s0 + shl % sn;
+  return (int64_t)bh * a.L + (int64_t)s * a.N;
+}
 
-  const int npair = (a.nq + 1) / 2;
-  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int sn = a.sn > 0 ? a.sn : a.S;  // the launch covers segments s0 .. s0 + sn - 1 of every head
-  const int shl = blk / npair;
-  const int pair = blk % npair;
+// Context of the (b, h, segment) of item it.
+template <int D>
+__device__ __forceinline__ FaCtx<D> item_ctx(const FaArgs& a, int it, int npair, int sn, int wave) {
+  const int shl = it / npair;
   const int bh = shl / sn;
   const int s = a.s0 + shl % sn;
   const int sh = bh * a.S + s;           // (b*H + h) * S + s
   const int h = bh % a.H;
   const int64_t tok0 = (int64_t)bh * a.L + (int64_t)s * a.N;
-
   FaCtx<D> cx;
   cx.qb = a.q + tok0 * D;
   cx.ob = a.out + tok0 * D;
@@ -820,37 +843,98 @@ void fa_fwd_kernel(FaArgs a) {
   cx.seg_bytes = (uint32_t)a.N * D * 2;
   cx.N = a.N;
   cx.nk = (a.N + kBN - 1) / kBN;
-  cx.wave = threadIdx.x >> 6;
+  cx.wave = wave;
   cx.has_memory = (a.seg_base + s) > 0;
   cx.beta = a.beta[h];
   cx.sc = a.sc_log2;
+  return cx;
+}
 
+template <int D>
+__global__ __launch_bounds__(kThreads, 1)
+void fa_fwd_kernel(FaArgs a) {
+  using L = FaLayout<D>;
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[L::TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) float zc[512];   // z at [0, D), colsum(M) at [256, 256 + D)
+  __shared__ __attribute__((aligned(1024))) bf16 stg[kWaves * kStageElems];   // output stages
+
+  // Items: (b, h, segment) tile x pair of query tiles, the pair fastest.  With G
+  // workgroups (G a multiple of the 8 XCDs), XCD x (hardware id % 8) owns the
+  // items [x n / 8, (x + 1) n / 8) and its G / 8 workgroups take them in turn, so
+  // the workgroups of one XCD work on consecutive items (the pairs of a segment
+  // together, sharing its K/V tiles in that XCD's L2).  With G = n each workgroup
+  // does one item; with G = the number of compute units the kernel is persistent
+  // and the next item's Q rows and tile 0 load during the current epilogue.
+  const int npair = (a.nq + 1) / 2;
+  const int sn = a.sn > 0 ? a.sn : a.S;  // the launch covers segments s0 .. s0 + sn - 1 of every head
+  const int nitems = a.B * a.H * sn * npair;
+  const int G = gridDim.x, g = blockIdx.x;
+  int it, it_end, it_step;
+  if (G % 8 == 0) {
+    const int x = g % 8;
+    it = (int)((int64_t)x * nitems / 8) + g / 8;
+    it_end = (int)((int64_t)(x + 1) * nitems / 8);
+    it_step = G / 8;
+  } else {
+    it = g;
+    it_end = nitems;
+    it_step = G;
+  }
+  if (it >= it_end) return;   // uniform over the workgroup, before any barrier
+
+  const int wave = threadIdx.x >> 6;
+  FaCtx<D> cx = item_ctx<D>(a, it, npair, sn, wave);
   LdsAddr<D> ad;
   ad.init(threadIdx.x & 63);
+  DmaOfs<D> dof;
+  dof.init(threadIdx.x & 63);
 
   // the longer query tile first: the workgroups of one (b, h, segment) then
   // stream the same K/V tiles at about the same time (L2 reuse)
-  const int qt0 = a.nq - 1 - pair;
-  const int qt1 = pair;
-  const bool two = qt1 != qt0;
-
-  DmaOfs<D> dof;
-  dof.init(threadIdx.x & 63);
-  issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
-  issue_tile<D, true>(cx.vseg, cx.seg_bytes, v0s, cx.wave, dof);
-  issue_q<D>(cx, qt0, k1s, v1s, dof);
+  int pair = it % npair;
+  issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, wave, dof);
+  issue_tile<D, true>(cx.vseg, cx.seg_bytes, v0s, wave, dof);
+  issue_q<D>(cx.qb, cx.N, wave, a.nq - 1 - pair, k1s, v1s, dof);
   wait_loads_and_sync();
-  // One copy of the pass code serves both passes (the loop is not unrolled).
-  // Between them, the K part of tile 0 goes into k0s (free once the snapshot has
-  // been used); its V part is already in v0s and the Q rows in slot 1.
-  const int npass = two ? 2 : 1;
+  // One copy of the pass code serves every pass (the loop is not unrolled).
+  // Between passes, the K part of the next pass's tile 0 goes into k0s (free
+  // once the snapshot has been used); its V part is already in v0s and its Q
+  // rows in slot 1.
+  bool second = false;
 #pragma unroll 1
-  for (int p = 0; p < npass; ++p) {
-    run_pass<D>(cx, p == 0 ? qt0 : qt1, p + 1 < npass ? qt1 : -1, k0s, v0s, k1s, v1s, zc, stg, ad, dof);
-    if (p + 1 < npass) {
-      issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, cx.wave, dof);
-      wait_loads_and_sync();
+  for (;;) {
+    const int qt = second ? pair : a.nq - 1 - pair;
+    const bool same_item = !second && pair != a.nq - 1 - pair;   // the pair's second tile follows
+    NextPass np;
+    if (same_item) {
+      np.qb = cx.qb;
+      np.vseg = cx.vseg;
+      np.qt = pair;
+    } else if (it + it_step < it_end) {
+      const int64_t t0 = item_tok0(a, it + it_step, npair, sn);
+      np.qb = a.q + t0 * D;
+      np.vseg = a.v + t0 * D;
+      np.qt = a.nq - 1 - (it + it_step) % npair;
+    } else {
+      np.qb = cx.qb;
+      np.vseg = cx.vseg;
+      np.qt = -1;
     }
+    run_pass<D>(cx, qt, np, k0s, v0s, k1s, v1s, zc, stg, ad, dof);
+    if (np.qt < 0) break;
+    if (same_item) {
+      second = true;
+    } else {
+      it += it_step;
+      pair = it % npair;
+      second = false;
+      cx = item_ctx<D>(a, it, npair, sn, wave);
+    }
+    issue_tile<D, false>(cx.kseg, cx.seg_bytes, k0s, wave, dof);
+    wait_loads_and_sync();
   }
 }
 
@@ -868,7 +952,21 @@ hipError_t launch_fa_fwd(const FaArgs& args, hipStream_t stream) {
   const int64_t blocks = fa_fwd_blocks((int64_t)a.B * a.H * sn, a.N);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fa_fwd_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  // A launch over whole streams runs persistent, one workgroup per compute unit
+  // (the kernel's LDS admits one per CU).  A launch over a range of segments
+  // runs one workgroup per item: it shares the device with the delta chain,
+  // which holds some CUs, and a persistent grid would leave the share of the
+  // workgroups waiting for those CUs to the end.
+  int64_t grid = blocks;
+  if (args.sn <= 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t slots = cus >= 8 ? cus / 8 * 8 : cus;
+    if (slots > 0 && grid > slots) grid = slots;
+  }
+  hipLaunchKernelGGL(fa_fwd_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
