@@ -103,9 +103,15 @@ void delta_amat_kernel(DeltaArgs a) {
   if (t < D) zs[t] = a.snapz[(int64_t)sh * D + t];
   __syncthreads();
   const int tok = t / C::TPT, part = t % C::TPT;
+  // Thread (tok, part) holds the logical 16-byte chunks TPT c + part, c < CPT, of
+  // its token: the TPT threads of a token read one contiguous piece per load, and
+  // the 16 lanes of an LDS write (four tokens x four parts) land on 16 distinct
+  // bank groups under the XOR swizzle of the X layout.
   float zr[C::EPT];
 #pragma unroll
-  for (int e = 0; e < C::EPT; ++e) zr[e] = zs[part * C::EPT + e];
+  for (int c = 0; c < C::CPT; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zr[8 * c + j] = zs[8 * (C::TPT * c + part) + j];
   const bf16* kseg = a.k + ((int64_t)bh * a.L + (int64_t)s * a.N) * D;
   const int nst = a.N / kAmT;
 
@@ -124,9 +130,9 @@ void delta_amat_kernel(DeltaArgs a) {
   bf16x8 raw[C::CPT];
   auto load = [&](int q) {   // stage q's K chunks of this thread (clamped: a load past the end is unused)
     const int qq = q < nst ? q : nst - 1;
-    const bf16* p = kseg + ((int64_t)qq * kAmT + tok) * D + part * C::EPT;
+    const bf16* p = kseg + ((int64_t)qq * kAmT + tok) * D + 8 * part;
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) raw[c] = *reinterpret_cast<const bf16x8*>(p + 8 * c);
+    for (int c = 0; c < C::CPT; ++c) raw[c] = *reinterpret_cast<const bf16x8*>(p + 8 * C::TPT * c);
   };
   auto convert = [&](bf16* X) {   // row tok of X from the raw K chunks
     float f[C::EPT];
@@ -148,7 +154,7 @@ void delta_amat_kernel(DeltaArgs a) {
       bf16x8 o;
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = f2bf(sw * f[8 * c + j]);
-      const int phys = trt_chunk<D>(tok, part * C::CPT + c);
+      const int phys = trt_chunk<D>(tok, C::TPT * c + part);
       *(INFINI_LDS bf16x8*)(X + tok * D + 8 * phys) = o;
     }
   };
