@@ -363,10 +363,13 @@ void lin_contrib_seg_kernel(LinContribArgs a) {
   const int total = ((items - lw + G - 1) / G) * nst;   // stream positions of this workgroup
 
   const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
-  const int dvb = wave & 3, dkq = 2 * (wave >> 2);
-  const int vofs = lc_tr_offset<D>(lane, dvb);
-  const int kofs0 = lc_tr_offset<D>(lane, dkq);
-  const int kofs1 = lc_tr_offset<D>(lane, dkq + 1);
+  // wave: C^T tiles (d_value block dv0, d_key block dkb) and (dv0 + 1, dkb), so a
+  // 16-token step reads two V operands and one hi / lo pair of sigma(K) operands
+  // (a tile pair along d_key would read one V operand and two pairs)
+  const int dv0 = 2 * (wave & 1), dkb = wave >> 1;
+  const int vofs0 = lc_tr_offset<D>(lane, dv0);
+  const int vofs1 = lc_tr_offset<D>(lane, dv0 + 1);
+  const int kofs = lc_tr_offset<D>(lane, dkb);
   // sigma(K) pass: row th / 16 of the stage, logical chunk th % 16, at its
   // physical position (the loads placed it there)
   const int srow = th >> 4, sch = th & 15;
@@ -435,9 +438,9 @@ void lin_contrib_seg_kernel(LinContribArgs a) {
     const int hi = ln >> 5, l32 = ln & 31;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int dv = 32 * dvb + 8 * (r >> 2) + 4 * hi + (r & 3);
-      cm[dv * D + 32 * dkq + l32] = acc0[r];
-      cm[dv * D + 32 * dkq + 32 + l32] = acc1[r];
+      const int dv = 32 * dv0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      cm[dv * D + 32 * dkb + l32] = acc0[r];
+      cm[(dv + 32) * D + 32 * dkb + l32] = acc1[r];
     }
     // barrier after this wave's LDS writes only: an LDS fence would also wait for
     // the ring's direct-to-LDS loads in flight
@@ -491,22 +494,21 @@ void lin_contrib_seg_kernel(LinContribArgs a) {
       }                                                                                         \
       /* all operand reads of the stage first: one LDS latency per stage */                     \
       const bf16x8 kx_ = *(const INFINI_LDS bf16x8*)(KN + sdst);                                \
-      bf16x8 va_[2], k0_[2], l0_[2], k1_[2], l1_[2];                                            \
+      bf16x8 v0_[2], v1_[2], kh_[2], kl_[2];                                                    \
       _Pragma("unroll")                                                                         \
       for (int st = 0; st < 2; ++st) {                                                          \
-        va_[st] = lc_read_tr<D>(VC, 16 * st * D + vofs);                                        \
-        k0_[st] = lc_read_tr<D>(KC, 16 * st * D + kofs0);                                       \
-        l0_[st] = lc_read_tr<D>(KLC, 16 * st * D + kofs0);                                      \
-        k1_[st] = lc_read_tr<D>(KC, 16 * st * D + kofs1);                                       \
-        l1_[st] = lc_read_tr<D>(KLC, 16 * st * D + kofs1);                                      \
+        v0_[st] = lc_read_tr<D>(VC, 16 * st * D + vofs0);                                       \
+        v1_[st] = lc_read_tr<D>(VC, 16 * st * D + vofs1);                                       \
+        kh_[st] = lc_read_tr<D>(KC, 16 * st * D + kofs);                                        \
+        kl_[st] = lc_read_tr<D>(KLC, 16 * st * D + kofs);                                       \
       }                                                                                         \
       bf16x8 h8_, l8_;                                                                          \
       _Pragma("unroll")                                                                         \
       for (int st = 0; st < 2; ++st) {                                                          \
-        acc0 = mfma32(va_[st], k0_[st], acc0);                                                  \
-        acc0 = mfma32(va_[st], l0_[st], acc0);                                                  \
-        acc1 = mfma32(va_[st], k1_[st], acc1);                                                  \
-        acc1 = mfma32(va_[st], l1_[st], acc1);                                                  \
+        acc0 = mfma32(v0_[st], kh_[st], acc0);                                                  \
+        acc0 = mfma32(v0_[st], kl_[st], acc0);                                                  \
+        acc1 = mfma32(v1_[st], kh_[st], acc1);                                                  \
+        acc1 = mfma32(v1_[st], kl_[st], acc1);                                                  \
         if (more_) sigma_part(kx_, h8_, l8_, 4 * st, 4);                                        \
       }                                                                                         \
       if (more_) {                                                                              \
