@@ -4,8 +4,9 @@ Small shapes (several query/key tiles, a ragged last query tile, both rules,
 both head widths), the tiny fp32 workload and the full 32K-token single-layer
 workload, plus the diagnostics: pure-memory and pure-local gates, a stress input
 with widely spread scores, segment-by-segment streaming == one sequence call
-(bitwise, also on the pipelined delta path), reset, determinism and a
-NaN-poisoned workspace.
+(bitwise, also on the pipelined delta path), the persistent fused-kernel grid
+with an odd number of query tiles and a ragged last tile, reset, determinism
+and a NaN-poisoned workspace.
 """
 
 import math
@@ -154,6 +155,44 @@ def test_delta_pipeline_bitwise(d):
     assert torch.equal(e1.M, e2.M) and torch.equal(e1.z, e2.z)
     res = gh.oracle_full(w, "delta")
     gh.compare_full(w, "delta", out1, e1, res, label=f"pipeline d={d}")
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_persistent_grid_odd_tiles(rule, d):
+    """A call with more (b, h, segment) x query-tile-pair items than compute units
+    runs the fused kernel persistent (one workgroup per CU walking its XCD's items,
+    passes chained across items).  Segments of 1216 tokens give five query tiles:
+    pairs (4, 0) and (3, 1) and a middle pair with a single tile (2), the last
+    tile ragged (192 rows: two waves idle), and 4 x 80 x 3 = 960 items, which the
+    8 XCD ranges do not split evenly.  At d = 64 the output and final state equal,
+    bitwise, those of the same stream fed one segment per call (12 items: one
+    workgroup each); at both widths every tile of two heads matches the oracle."""
+    torch = gh.torch_mod()
+    H, N, S = 4, 1216, 80
+    w = syn.custom(f"persistent_odd_d{d}", 47, 1, H, d, N, S)
+    gh.log(f"persistent grid d={d} rule={rule}: {H * S * 3} items")
+    q, k, v, beta = gh.device_inputs(w)
+    out1, e1 = gh.run(w, rule, q, k, v, beta, mode="sequence")
+    if d == 64:
+        out2, e2 = gh.run(w, rule, q, k, v, beta, mode="segments")
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out2)
+        assert torch.equal(e1.M, e2.M) and torch.equal(e1.z, e2.z)
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    res = gh.oracle_full(w, rule, heads=heads)
+    got = gh.to_host(out1)[:, heads]
+    worst = 0.0
+    for j, h in enumerate(heads):
+        for s in range(S):
+            sl = slice(s * N, (s + 1) * N)
+            e = gh.metric(got[0, j, sl], res["A"][0, j, sl], "bf16")
+            worst = max(worst, e)
+            assert e <= gh.tol("bf16"), f"head {h} segment {s}: error {e:.3e}"
+    eM = gh.metric(gh.to_host(e1.M)[:, heads], res["M"], "bf16")
+    gh.log(f"  persistent d={d}/{rule}: worst tile {worst:.3e}, final M {eM:.3e}")
+    assert eM <= gh.tol("bf16")
 
 
 @pytest.mark.parametrize("rule", ["linear", "delta"])
