@@ -7,9 +7,12 @@
 // section 3.3; the gate of section 3.5.  The N x N score matrix never leaves
 // registers (chapter-24 page, section 24.1.2).
 //
-// Work decomposition.  One workgroup (8 waves, two per SIMD, one workgroup per
-// CU) handles a pair of 256-row query tiles of one (b, h, segment): tile w and
-// tile NQ-1-w, so that every workgroup does the same causal work.  Wave w owns
+// Work decomposition.  An item is a pair of 256-row query tiles of one (b, h,
+// segment): tile w and tile NQ-1-w, so that every item holds the same causal
+// work.  One workgroup (8 waves, two per SIMD) per CU walks the items of its
+// XCD in turn (a persistent grid; a launch over a range of segments runs one
+// workgroup per item instead), each pass overlapping the next one's first
+// loads whether or not it belongs to the same item.  Wave w owns
 // the 32-row query block 32 w + [0, 32) of a tile.  The two waves of a SIMD
 // interleave in hardware: while one runs its softmax (VALU) or waits for LDS,
 // the other keeps the matrix pipe busy.  Per 32-key block of a 128-key tile:
