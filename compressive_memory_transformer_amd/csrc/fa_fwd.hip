@@ -962,10 +962,7 @@ hipError_t launch_fa_fwd(const FaArgs& args, hipStream_t stream) {
   // workgroups waiting for those CUs to the end.
   int64_t grid = blocks;
   if (args.sn <= 0) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
+    const int cus = device_compute_units();
     const int64_t slots = cus >= 8 ? cus / 8 * 8 : cus;
     if (slots > 0 && grid > slots) grid = slots;
   }
